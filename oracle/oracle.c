@@ -1,0 +1,356 @@
+/*
+ * CPU oracle for the BitNet b1.58 BitLinear hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test-suite, the entry point's smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header, table or
+ * constant with the HIP library.
+ *
+ * It is the plain, slow, literal reading of what the pages define.  Pages
+ * (cited by title and section):
+ *   [NOTES]  "BitNet 1.5技术解析：2比特量化在神经网络中的应用与挑战"
+ *            (intelliparadigm.com) -- 2.1 weight quantization, 2.2 activation
+ *            quantization, 3.1 the BitLinear layer, 5.2 hardware needs.
+ *   [ENG]    "BitNet 三元权重量化训练工程：直通估计器与梯度裁剪实践"
+ *            (blog.hotdry.top, 2025-10-04) -- section on the straight-through
+ *            estimator for ternary weights; section on gradient clipping.
+ *   [WALL]   "1.58-bit量化技术突破AI算力与内存墙限制" (intelliparadigm.com)
+ *            -- 2.2 ternary quantization, 3.1 add/subtract matmul,
+ *            3.2 the STE, 4.1 memory layout.
+ *
+ * Precision.  The pages' code is PyTorch in float32, so every step that
+ * decides an integer (the ternary code, the int8 activation) is evaluated in
+ * IEEE binary32 with round-to-nearest-even, one rounding per operation, no
+ * fused multiply-add (built with -ffp-contract=off) and denormals kept.  The
+ * integer GEMM is exact (int64 accumulation, checked to fit int32).  The
+ * dequantized output and the STE gradients, which decide nothing, are
+ * computed in float64 as references for the tolerance checks.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes):
+ *   - summation order: the canonical pairwise tree tree_sum() below;
+ *   - RMSNorm: mean of squares over the row, eps inside the square root,
+ *     multiply by the correctly rounded reciprocal of the root, unit gain;
+ *   - weight codes: divide by gamma (the memory-wall page's form), not
+ *     multiply by 1/gamma;
+ *   - packing: code of column k in bits 2*(k%4)..2*(k%4)+1 of byte k/4 of
+ *     its row, rows stored one after another.
+ *
+ * Every entry point returns 0 on success and a negative value on a bad
+ * argument (null pointer, non-positive size) or an int32 overflow.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_EPS_FLOOR 1e-5f /* clamp(min=1e-5) on the scale denominators */
+
+/* ---------------------------------------------------------------- threads */
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_get_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------- O1: tree sum
+ * The pages only say "mean" / "sum".  To make the codes reproducible a
+ * single order is fixed: pad v to P = 2^ceil(log2 n) entries with +0.0 and
+ * add as a perfect binary tree in index order,
+ *   T(v[lo, lo+P)) = T(v[lo, lo+P/2)) + T(v[lo+P/2, lo+P)).
+ * Entries at or beyond n are +0.0. */
+static float tree_rec(const float *v, int64_t lo, int64_t P, int64_t n) {
+    if (lo >= n) return 0.0f;
+    if (P == 1) return v[lo];
+    int64_t h = P / 2;
+    float a = tree_rec(v, lo, h, n);
+    float b = tree_rec(v, lo + h, h, n);
+    return a + b;
+}
+
+static int64_t pow2_ceil(int64_t n) {
+    int64_t P = 1;
+    while (P < n) P *= 2;
+    return P;
+}
+
+float oracle_tree_sum_f32(const float *v, int64_t n) {
+    if (!v || n <= 0) return 0.0f;
+    return tree_rec(v, 0, pow2_ceil(n), n);
+}
+
+/* bf16 -> fp32 is exact: the 16 bits are the top half of the binary32. */
+static float bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* dtype 0 = fp32, 1 = bf16 (stored as its 16 raw bits) */
+static float load_elem(const void *p, int dtype, int64_t i) {
+    if (dtype == 1) return bf16_to_f32(((const uint16_t *)p)[i]);
+    return ((const float *)p)[i];
+}
+
+/* ------------------------------------ O2: RMSNorm + per-token absmax int8
+ * [NOTES 3.1]: the layer normalizes x with RMSNorm, then quantizes.
+ * [NOTES 2.2], [ENG STE section]: per token (row), scale = 127 / max|x| with
+ * the max clamped below at 1e-5, q = clamp(round(x*scale), -128, 127).
+ * [ENG STE section] fixes eps = 1e-5 inside the square root.  Unit gain. */
+int oracle_act_quant(const void *x, int x_dtype, int64_t M, int64_t K, float eps,
+                     int8_t *q, float *scale_x) {
+    if (!x || !q || !scale_x || M <= 0 || K <= 0) return -1;
+    if (x_dtype != 0 && x_dtype != 1) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; m++) {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+        float *sq = (float *)malloc((size_t)K * sizeof(float));
+        if (!row || !sq) { bad |= 1; free(row); free(sq); continue; }
+        for (int64_t k = 0; k < K; k++) {
+            row[k] = load_elem(x, x_dtype, m * K + k);
+            sq[k] = row[k] * row[k];
+        }
+        float ss = oracle_tree_sum_f32(sq, K);     /* sum of squares        */
+        float ms = ss / (float)K;                  /* mean of squares       */
+        float d = sqrtf(ms + eps);                 /* root, eps inside      */
+        float inv = 1.0f / d;                      /* reciprocal            */
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; k++) {
+            row[k] = row[k] * inv;                 /* normalized value      */
+            float a = fabsf(row[k]);
+            if (a > amax) amax = a;
+        }
+        float den = amax > ORACLE_EPS_FLOOR ? amax : ORACLE_EPS_FLOOR;
+        float s = 127.0f / den;
+        scale_x[m] = s;
+        for (int64_t k = 0; k < K; k++) {
+            float r = rintf(row[k] * s);           /* round half to even    */
+            if (r < -128.0f) r = -128.0f;
+            if (r > 127.0f) r = 127.0f;
+            q[m * K + k] = (int8_t)r;
+        }
+        free(row);
+        free(sq);
+    }
+    return bad ? -2 : 0;
+}
+
+/* ----------------------------------------- O3: absmean ternary weights
+ * [NOTES 2.1], [WALL 2.2], [ENG STE section]: gamma = mean|W| over the whole
+ * matrix (clamped below at 1e-5), code = clamp(round(W / gamma), -1, 1).
+ * The mean is the tree sum of the per-row tree sums, divided by N*K. */
+int oracle_weight_quant(const void *w, int w_dtype, int64_t N, int64_t K,
+                        int8_t *codes, float *gamma_out) {
+    if (!w || !codes || !gamma_out || N <= 0 || K <= 0) return -1;
+    if (w_dtype != 0 && w_dtype != 1) return -1;
+    float *rows = (float *)malloc((size_t)N * sizeof(float));
+    if (!rows) return -2;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++) {
+        float *a = (float *)malloc((size_t)K * sizeof(float));
+        if (!a) { bad |= 1; continue; }
+        for (int64_t k = 0; k < K; k++) a[k] = fabsf(load_elem(w, w_dtype, n * K + k));
+        rows[n] = oracle_tree_sum_f32(a, K);
+        free(a);
+    }
+    if (bad) { free(rows); return -2; }
+    float total = oracle_tree_sum_f32(rows, N);
+    free(rows);
+    float mean = total / (float)(N * K);
+    float g = mean > ORACLE_EPS_FLOOR ? mean : ORACLE_EPS_FLOOR;
+    *gamma_out = g;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            float r = rintf(load_elem(w, w_dtype, n * K + k) / g);
+            if (r < -1.0f) r = -1.0f;
+            if (r > 1.0f) r = 1.0f;
+            codes[n * K + k] = (int8_t)r;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------ D1: 2-bit packing
+ * [WALL 4.1]: 00 -> 0, 01 -> +1, 10 -> -1, 11 reserved.  Bit order in the
+ * byte and row layout are this build's reading (see file header). */
+int oracle_pack(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed) {
+    if (!codes || !packed || N <= 0 || K <= 0 || K % 4 != 0) return -1;
+    int64_t KB = K / 4;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t b = 0; b < KB; b++) {
+            unsigned byte = 0;
+            for (int j = 0; j < 4; j++) {
+                int8_t c = codes[n * K + 4 * b + j];
+                unsigned bits;
+                if (c == 0) bits = 0u;
+                else if (c == 1) bits = 1u;
+                else if (c == -1) bits = 2u;
+                else return -3; /* not a ternary code */
+                byte |= bits << (2 * j);
+            }
+            packed[n * KB + b] = (uint8_t)byte;
+        }
+    }
+    return 0;
+}
+
+int oracle_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *codes) {
+    if (!codes || !packed || N <= 0 || K <= 0 || K % 4 != 0) return -1;
+    int64_t KB = K / 4;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            unsigned bits = (packed[n * KB + k / 4] >> (2 * (k % 4))) & 3u;
+            if (bits == 0u) codes[n * K + k] = 0;
+            else if (bits == 1u) codes[n * K + k] = 1;
+            else if (bits == 2u) codes[n * K + k] = -1;
+            else return -3; /* reserved pattern */
+        }
+    }
+    return 0;
+}
+
+/* ----------------------------------------------- O4: integer GEMM
+ * acc[m,n] = sum_k q[m,k] * c[n,k]: the linear layer of [NOTES 3.1] on the
+ * integer operands, with the wide accumulator of [NOTES 5.2].  Accumulated
+ * in int64 and required to fit int32. */
+int oracle_gemm_i32(const int8_t *q, const int8_t *codes, int64_t M, int64_t N, int64_t K,
+                    int32_t *acc) {
+    if (!q || !codes || !acc || M <= 0 || N <= 0 || K <= 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; k++) s += (int64_t)q[m * K + k] * (int64_t)codes[n * K + k];
+            if (s > INT32_MAX || s < INT32_MIN) bad |= 1;
+            acc[m * N + n] = (int32_t)s;
+        }
+    }
+    return bad ? -4 : 0;
+}
+
+/* The same sum for a list of (m, n) pairs only. */
+int oracle_gemm_i32_at(const int8_t *q, const int8_t *codes, int64_t K, const int64_t *ms,
+                       const int64_t *ns, int64_t count, int32_t *out) {
+    if (!q || !codes || !ms || !ns || !out || K <= 0 || count < 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t i = 0; i < count; i++) {
+        int64_t s = 0;
+        for (int64_t k = 0; k < K; k++) s += (int64_t)q[ms[i] * K + k] * (int64_t)codes[ns[i] * K + k];
+        if (s > INT32_MAX || s < INT32_MIN) bad |= 1;
+        out[i] = (int32_t)s;
+    }
+    return bad ? -4 : 0;
+}
+
+/* ------------------------------------------------------ O5: dequant
+ * [NOTES 3.1] multiplies the linear output back by the scale; with integer
+ * operands that is y = acc * gamma / scale_x[m].  float64 reference. */
+int oracle_dequant(const int32_t *acc, const float *scale_x, float gamma, int64_t M, int64_t N,
+                   double *y) {
+    if (!acc || !scale_x || !y || M <= 0 || N <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++)
+            y[m * N + n] = (double)acc[m * N + n] * (double)gamma / (double)scale_x[m];
+    return 0;
+}
+
+/* ------------------------------------------------- O6: STE backward
+ * [NOTES 2.1, 2.2] (detach trick), [WALL 3.2] (backward returns the incoming
+ * gradient): both quantizers pass the gradient through unchanged, so the
+ * layer's gradients are those of a plain linear map evaluated at the
+ * dequantized operands W_deq = gamma * c and X_deq = q / scale_x:
+ *   grad_x[m,k] = sum_n gy[m,n] * W_deq[n,k]
+ *   grad_W[n,k] = sum_m gy[m,n] * X_deq[m,k]
+ * gy is fp32 or bf16 (dtype flag as above); sums in float64. */
+int oracle_ste_grad_x(const void *gy, int gy_dtype, const int8_t *codes, float gamma,
+                      int64_t M, int64_t N, int64_t K, double *gx) {
+    if (!gy || !codes || !gx || M <= 0 || N <= 0 || K <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t k = 0; k < K; k++) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; n++) {
+                double wdeq = (double)gamma * (double)codes[n * K + k];
+                s += (double)load_elem(gy, gy_dtype, m * N + n) * wdeq;
+            }
+            gx[m * K + k] = s;
+        }
+    }
+    return 0;
+}
+
+int oracle_ste_grad_w(const void *gy, int gy_dtype, const int8_t *q, const float *scale_x,
+                      int64_t M, int64_t N, int64_t K, double *gw) {
+    if (!gy || !q || !scale_x || !gw || M <= 0 || N <= 0 || K <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            double s = 0.0;
+            for (int64_t m = 0; m < M; m++) {
+                double xdeq = (double)q[m * K + k] / (double)scale_x[m];
+                s += (double)load_elem(gy, gy_dtype, m * N + n) * xdeq;
+            }
+            gw[n * K + k] = s;
+        }
+    }
+    return 0;
+}
+
+/* Sampled forms: grad_x at (m, k) pairs, grad_W at (n, k) pairs. */
+int oracle_ste_grad_x_at(const void *gy, int gy_dtype, const int8_t *codes, float gamma,
+                         int64_t M, int64_t N, int64_t K, const int64_t *ms, const int64_t *ks,
+                         int64_t count, double *out) {
+    if (!gy || !codes || !ms || !ks || !out || M <= 0 || N <= 0 || K <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; i++) {
+        double s = 0.0;
+        for (int64_t n = 0; n < N; n++) {
+            double wdeq = (double)gamma * (double)codes[n * K + ks[i]];
+            s += (double)load_elem(gy, gy_dtype, ms[i] * N + n) * wdeq;
+        }
+        out[i] = s;
+    }
+    return 0;
+}
+
+int oracle_ste_grad_w_at(const void *gy, int gy_dtype, const int8_t *q, const float *scale_x,
+                         int64_t M, int64_t N, int64_t K, const int64_t *ns, const int64_t *ks,
+                         int64_t count, double *out) {
+    if (!gy || !q || !scale_x || !ns || !ks || !out || M <= 0 || N <= 0 || K <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; i++) {
+        double s = 0.0;
+        for (int64_t m = 0; m < M; m++) {
+            double xdeq = (double)q[m * K + ks[i]] / (double)scale_x[m];
+            s += (double)load_elem(gy, gy_dtype, m * N + ns[i]) * xdeq;
+        }
+        out[i] = s;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------- build-flag probe
+ * Returns a*b + c as this file's build evaluates it.  With contraction off
+ * it is fl(fl(a*b) + c), never fma(a, b, c); a test pins that. */
+float oracle_mul_add_probe(float a, float b, float c) { return a * b + c; }
