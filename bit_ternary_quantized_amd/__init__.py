@@ -1,0 +1,207 @@
+"""Python binding of the gfx950 BitLinear library (libbitnet_amd.so).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels.  Each function has the name of the C entry point it wraps
+(include/bitnet.h has the full contract); torch supplies device memory and
+the current stream.  Outputs not passed in are allocated here with torch.
+
+There is no fallback: if the library is missing or a call fails, an error
+is raised.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitnet_amd.so")
+
+BITNET_OK = 0
+BITNET_F32, BITNET_BF16 = 0, 1
+BITNET_OP_WEIGHT_QUANT, BITNET_OP_LINEAR_BWD_STE, BITNET_OP_LINEAR_FWD = 0, 1, 2
+GEMV_MAX_M = 16  # linear_fwd runs the packed GEMV up to this many tokens
+
+EXPORTS = (
+    "bitnet_weight_quant", "bitnet_act_quant", "bitnet_linear_fwd", "bitnet_linear_bwd_ste",
+    "bitnet_pack_ternary", "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
+)
+
+
+class BitnetError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: status {status} ({text})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libbitnet_amd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} not found: build it with `python bit_ternary_quantized_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    i64, p, c_int, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sigs = {
+        "bitnet_weight_quant": (c_int, [p, c_int, i64, i64, p, p, p, sz, p]),
+        "bitnet_act_quant": (c_int, [p, c_int, i64, i64, ctypes.c_float, p, p, p]),
+        "bitnet_linear_fwd": (c_int, [p, p, p, p, i64, i64, i64, p, p, p]),
+        "bitnet_linear_bwd_ste": (c_int, [p, c_int, p, p, p, p, i64, i64, i64, p, c_int, p, p, sz, p]),
+        "bitnet_pack_ternary": (c_int, [p, i64, i64, p, p]),
+        "bitnet_workspace_bytes": (sz, [c_int, i64, i64, i64]),
+        "bitnet_status_str": (ctypes.c_char_p, [c_int]),
+        "bitnet_version": (c_int, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != BITNET_OK:
+        raise BitnetError(fn, status, bitnet_status_str(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return BITNET_F32
+    if t.dtype == torch.bfloat16:
+        return BITNET_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def bitnet_status_str(status: int) -> str:
+    return load_library().bitnet_status_str(int(status)).decode()
+
+
+def bitnet_version() -> int:
+    return int(load_library().bitnet_version())
+
+
+def bitnet_workspace_bytes(op: int, M: int, N: int, K: int) -> int:
+    return int(load_library().bitnet_workspace_bytes(int(op), int(M), int(N), int(K)))
+
+
+def bitnet_weight_quant(W: torch.Tensor, W_packed=None, gamma=None, workspace=None, stream=None):
+    """Absmean ternary codes, 2-bit packed -> (W_packed uint8 [N,K/4], gamma f32 [1])."""
+    lib = load_library()
+    _need(W, "W")
+    N, K = W.shape
+    dev = W.device
+    if W_packed is None:
+        W_packed = torch.empty(N, K // 4, dtype=torch.uint8, device=dev)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=dev)
+    need = bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT, 0, N, K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check("bitnet_weight_quant", lib.bitnet_weight_quant(
+        _ptr(W), _dtype_code(W), N, K, _ptr(W_packed), _ptr(gamma), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return W_packed, gamma
+
+
+def bitnet_act_quant(X: torch.Tensor, eps: float = 1e-5, Xq=None, scale_x=None, stream=None):
+    """RMSNorm + per-token absmax int8 -> (Xq int8 [M,K], scale_x f32 [M])."""
+    lib = load_library()
+    _need(X, "X")
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty(M, K, dtype=torch.int8, device=X.device)
+    if scale_x is None:
+        scale_x = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check("bitnet_act_quant", lib.bitnet_act_quant(
+        _ptr(X), _dtype_code(X), M, K, ctypes.c_float(eps), _ptr(Xq), _ptr(scale_x), _stream(stream)))
+    return Xq, scale_x
+
+
+def bitnet_linear_fwd(Xq, scale_x, W_packed, gamma, Y=None, acc=None, want_acc=False, stream=None):
+    """y = (Xq . codes^T) * gamma / scale_x -> (Y f32 [M,N], acc int32 [M,N] or None)."""
+    lib = load_library()
+    for t, n in ((Xq, "Xq"), (scale_x, "scale_x"), (W_packed, "W_packed"), (gamma, "gamma")):
+        _need(t, n)
+    M, K = Xq.shape
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K:
+        raise ValueError("W_packed must be [N, K/4]")
+    if Y is None:
+        Y = torch.empty(M, N, dtype=torch.float32, device=Xq.device)
+    if acc is None and want_acc:
+        acc = torch.empty(M, N, dtype=torch.int32, device=Xq.device)
+    _check("bitnet_linear_fwd", lib.bitnet_linear_fwd(
+        _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(gamma), M, N, K, _ptr(Y), _ptr(acc),
+        _stream(stream)))
+    return Y, acc
+
+
+def bitnet_linear_bwd_ste(grad_y, Xq, scale_x, W_packed, gamma, want_grad_x=True, want_grad_W=True,
+                          gx_dtype=torch.float32, grad_x=None, grad_W=None, workspace=None,
+                          stream=None):
+    """STE backward -> (grad_x [M,K] f32/bf16 or None, grad_W f32 [N,K] or None)."""
+    lib = load_library()
+    for t, n in ((grad_y, "grad_y"), (Xq, "Xq"), (scale_x, "scale_x"), (W_packed, "W_packed"),
+                 (gamma, "gamma")):
+        _need(t, n)
+    M, K = Xq.shape
+    N = W_packed.shape[0]
+    dev = Xq.device
+    if grad_x is None and want_grad_x:
+        grad_x = torch.empty(M, K, dtype=gx_dtype, device=dev)
+    if grad_W is None and want_grad_W:
+        grad_W = torch.empty(N, K, dtype=torch.float32, device=dev)
+    need = bitnet_workspace_bytes(BITNET_OP_LINEAR_BWD_STE, M, N, K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    gx_code = _dtype_code(grad_x) if grad_x is not None else BITNET_F32
+    _check("bitnet_linear_bwd_ste", lib.bitnet_linear_bwd_ste(
+        _ptr(grad_y), _dtype_code(grad_y), _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(gamma),
+        M, N, K, _ptr(grad_x), gx_code, _ptr(grad_W), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return grad_x, grad_W
+
+
+def bitnet_pack_ternary(codes: torch.Tensor, W_packed=None, stream=None):
+    """int8 codes [N,K] -> packed uint8 [N,K/4]."""
+    lib = load_library()
+    _need(codes, "codes")
+    N, K = codes.shape
+    if W_packed is None:
+        W_packed = torch.empty(N, K // 4, dtype=torch.uint8, device=codes.device)
+    _check("bitnet_pack_ternary", lib.bitnet_pack_ternary(
+        _ptr(codes), N, K, _ptr(W_packed), _stream(stream)))
+    return W_packed
+
+
+def bitlinear_forward(X, W, eps: float = 1e-5, want_acc=False, stream=None):
+    """The whole forward of one layer on the device: act quant, weight quant, linear.
+
+    Returns a dict with Xq, scale_x, W_packed, gamma, Y (and acc when asked).
+    """
+    Xq, scale_x = bitnet_act_quant(X, eps, stream=stream)
+    W_packed, gamma = bitnet_weight_quant(W, stream=stream)
+    Y, acc = bitnet_linear_fwd(Xq, scale_x, W_packed, gamma, want_acc=want_acc, stream=stream)
+    return {"Xq": Xq, "scale_x": scale_x, "W_packed": W_packed, "gamma": gamma, "Y": Y, "acc": acc}

@@ -1,0 +1,116 @@
+// C ABI of the BitLinear library: host-side argument checks, then kernel
+// launches on the caller's stream.  Declarations and the full contract of
+// each call are in include/bitnet.h.
+#include "../../include/bitnet.h"
+#include "common.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+int hip_status(hipError_t e) { return e == hipSuccess ? BITNET_OK : BITNET_E_HIP; }
+bool float_dtype(int d) { return d == BITNET_F32 || d == BITNET_BF16; }
+
+// int8 GEMM / GEMV path limits: |acc| <= 128*K must fit int32.
+constexpr int64_t kMaxK = (int64_t)1 << 24;
+constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;  // kernels index rows with int
+
+}  // namespace
+
+extern "C" {
+
+int bitnet_version(void) { return kVersion; }
+
+const char* bitnet_status_str(int status) {
+    switch (status) {
+        case BITNET_OK: return "ok";
+        case BITNET_E_ARG: return "null required pointer or bad flag";
+        case BITNET_E_SHAPE: return "size out of range (M, N, K >= 1; K % 4 or K % 16 as required)";
+        case BITNET_E_DTYPE: return "unsupported dtype";
+        case BITNET_E_ALIGN: return "pointer not 16-byte aligned";
+        case BITNET_E_WORKSPACE: return "workspace missing or too small";
+        case BITNET_E_HIP: return "HIP launch or runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t bitnet_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return 0;
+    switch (op) {
+        case BITNET_OP_WEIGHT_QUANT: return bitnet::weight_quant_ws_bytes(N);
+        case BITNET_OP_LINEAR_BWD_STE: return bitnet::bwd_ws_bytes(M, N, K);
+        default: return 0;
+    }
+}
+
+int bitnet_weight_quant(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* W_packed,
+                        float* gamma, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!W || !W_packed || !gamma) return BITNET_E_ARG;
+    if (!float_dtype(w_dtype)) return BITNET_E_DTYPE;
+    if (N < 1 || K < 1 || K % 4 != 0 || N > kMaxDim || K > kMaxDim) return BITNET_E_SHAPE;
+    if (!aligned16(W) || !aligned16(W_packed) || !aligned4(gamma)) return BITNET_E_ALIGN;
+    if (!workspace || workspace_bytes < bitnet::weight_quant_ws_bytes(N)) return BITNET_E_WORKSPACE;
+    if (!aligned16(workspace)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_weight_quant(W, w_dtype == BITNET_BF16, N, K, W_packed, gamma,
+                                                  workspace, as_stream(stream)));
+}
+
+int bitnet_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, float eps, int8_t* Xq,
+                     float* scale_x, void* stream) {
+    if (!X || !Xq || !scale_x) return BITNET_E_ARG;
+    if (!float_dtype(x_dtype)) return BITNET_E_DTYPE;
+    if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim) return BITNET_E_SHAPE;
+    if (!(eps >= 0.0f)) return BITNET_E_ARG;
+    if (!aligned16(X) || !aligned16(Xq) || !aligned4(scale_x)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_act_quant(X, x_dtype == BITNET_BF16, M, K, eps, Xq, scale_x,
+                                               as_stream(stream)));
+}
+
+int bitnet_linear_fwd(const int8_t* Xq, const float* scale_x, const uint8_t* W_packed,
+                      const float* gamma, int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc,
+                      void* stream) {
+    if (!Xq || !scale_x || !W_packed || !gamma || !Y) return BITNET_E_ARG;
+    if (M < 1 || N < 1 || K < 1 || K % 16 != 0 || K >= kMaxK || M > kMaxDim || N > kMaxDim)
+        return BITNET_E_SHAPE;
+    if (!aligned16(Xq) || !aligned16(W_packed) || !aligned16(Y) || !aligned4(scale_x) ||
+        !aligned4(gamma) || (acc && !aligned16(acc)))
+        return BITNET_E_ALIGN;
+    if (M <= bitnet::kGemvMaxM && K <= 16384)
+        return hip_status(bitnet::launch_gemv_t2(Xq, scale_x, W_packed, gamma, M, N, K, Y, acc,
+                                                 as_stream(stream)));
+    return hip_status(bitnet::launch_gemm_i8t2(Xq, scale_x, W_packed, gamma, M, N, K, Y, acc,
+                                               as_stream(stream)));
+}
+
+int bitnet_linear_bwd_ste(const void* grad_y, int gy_dtype, const int8_t* Xq, const float* scale_x,
+                          const uint8_t* W_packed, const float* gamma, int64_t M, int64_t N,
+                          int64_t K, void* grad_x, int gx_dtype, float* grad_W, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (!grad_y || !Xq || !scale_x || !W_packed || !gamma) return BITNET_E_ARG;
+    if (!grad_x && !grad_W) return BITNET_E_ARG;
+    if (gy_dtype != BITNET_BF16 || !float_dtype(gx_dtype)) return BITNET_E_DTYPE;
+    if (M < 1 || N < 1 || K < 1 || K % 16 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return BITNET_E_SHAPE;
+    if (!aligned16(grad_y) || !aligned16(Xq) || !aligned16(W_packed) || !aligned4(scale_x) ||
+        !aligned4(gamma) || (grad_x && !aligned16(grad_x)) || (grad_W && !aligned16(grad_W)))
+        return BITNET_E_ALIGN;
+    if (!workspace || workspace_bytes < bitnet::bwd_ws_bytes(M, N, K)) return BITNET_E_WORKSPACE;
+    if (!aligned16(workspace)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_bwd_ste(static_cast<const uint16_t*>(grad_y), Xq, scale_x,
+                                             W_packed, gamma, M, N, K, grad_x,
+                                             gx_dtype == BITNET_BF16, grad_W, workspace,
+                                             as_stream(stream)));
+}
+
+int bitnet_pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* W_packed,
+                        void* stream) {
+    if (!codes || !W_packed) return BITNET_E_ARG;
+    if (N < 1 || K < 1 || K % 4 != 0 || N > kMaxDim || K > kMaxDim) return BITNET_E_SHAPE;
+    if (!aligned16(codes) || !aligned16(W_packed)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_pack_ternary(codes, N, K, W_packed, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+// Internal helpers shared by the gfx950 kernels of the BitLinear library.
+// Not part of the public ABI (include/bitnet.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// ------------------------------------------------------------ element loads
+// bf16 -> fp32 is exact: the 16 bits are the high half of the binary32.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+    return __uint_as_float(b16 << 16);
+}
+
+// 16 bytes of a row as floats: 4 fp32 or 8 bf16 elements.
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+    static constexpr int E = 4;
+    __device__ __forceinline__ static void load(const float* p, float (&v)[4]) {
+        const float4 q = *reinterpret_cast<const float4*>(p);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+};
+template <> struct Vec16<uint16_t> {  // bf16 stored as raw bits
+    static constexpr int E = 8;
+    __device__ __forceinline__ static void load(const uint16_t* p, float (&v)[8]) {
+        const uint4 q = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+
+__device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const uint16_t* p, int64_t i) {
+    return bf16_bits_to_f32(p[i]);
+}
+
+// ---------------------------------------------------- canonical tree sums
+// The library's summation order: pad to a power of two with +0 and add as a
+// perfect binary tree in index order.  Aligned power-of-two blocks may be
+// summed independently and then combined as a tree; both helpers below keep
+// that structure exactly.
+
+// In-lane tree over E (power of two) consecutive values.
+template <int E>
+__device__ __forceinline__ float lane_tree(const float (&v)[E]) {
+    float t[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) t[i] = v[i];
+#pragma unroll
+    for (int w = 1; w < E; w *= 2) {
+#pragma unroll
+        for (int i = 0; i < E; i += 2 * w) t[i] = t[i] + t[i + w];
+    }
+    return t[0];
+}
+
+// xor butterfly over the 64 lanes: lane l and lane l^m add the same two
+// partial sums (commutative, so bit-identical), which is the tree over the
+// lanes in lane order.  Every lane ends with the total.
+__device__ __forceinline__ float wave_tree_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < kWave; m *= 2) v = v + __shfl_xor(v, m, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 1; m < kWave; m *= 2) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+// Pairwise combination of a stream of equal-size, consecutive, aligned
+// blocks (a binary counter): after pushing leaves 0..n-1, total() is the
+// tree over them zero-padded to a power of two.  The leaf count must be
+// uniform across the wave so that every branch is uniform.
+struct PairwiseStack {
+    static constexpr int kLevels = 26;
+    float part[kLevels];
+    uint32_t n = 0;
+    __device__ __forceinline__ void push(float s) {
+        bool done = false;
+#pragma unroll
+        for (int l = 0; l < kLevels; ++l) {
+            if (!done) {
+                if ((n >> l) & 1u) {
+                    s = part[l] + s;
+                } else {
+                    part[l] = s;
+                    done = true;
+                }
+            }
+        }
+        ++n;
+    }
+    __device__ __forceinline__ float total() const {
+        float acc = 0.0f;
+        bool have = false;
+#pragma unroll
+        for (int l = 0; l < kLevels; ++l) {
+            if ((n >> l) & 1u) {
+                acc = have ? part[l] + acc : part[l];
+                have = true;
+            }
+        }
+        return acc;
+    }
+};
+
+// ------------------------------------------------------------ 2-bit codes
+// Packed layout: code of column k in bits 2(k%4)..2(k%4)+1 of byte k/4;
+// 00 = 0, 01 = +1, 10 = -1.
+//
+// unpack16: one packed dword (16 codes, columns c0..c0+15) -> 16 int8 in
+// four dwords.  Dword j holds the codes of columns c0+j, c0+4+j, c0+8+j,
+// c0+12+j in bytes 0..3 (a 4x4 byte transpose of the natural order); the
+// other matrix-core operand is brought into the same order with
+// transpose4x4_bytes() so that every dot product pairs equal columns.
+__device__ __forceinline__ void unpack16(uint32_t w, uint32_t (&out)[4]) {
+    // byte LUT indexed by the 2-bit code: 0 -> 0x00, 1 -> 0x01, 2 -> 0xff
+    constexpr uint32_t kLut = 0x00ff0100u;
+    out[0] = __builtin_amdgcn_perm(0u, kLut, w & 0x03030303u);
+    out[1] = __builtin_amdgcn_perm(0u, kLut, (w >> 2) & 0x03030303u);
+    out[2] = __builtin_amdgcn_perm(0u, kLut, (w >> 4) & 0x03030303u);
+    out[3] = __builtin_amdgcn_perm(0u, kLut, (w >> 6) & 0x03030303u);
+}
+
+// a[j] byte b -> out[b] byte j.
+__device__ __forceinline__ void transpose4x4_bytes(const uint32_t (&a)[4], uint32_t (&o)[4]) {
+    // perm(S0, S1, sel): selector byte 0..3 picks S1 bytes, 4..7 picks S0.
+    const uint32_t t0 = __builtin_amdgcn_perm(a[1], a[0], 0x06020400u);  // a0.0 a1.0 a0.2 a1.2
+    const uint32_t t1 = __builtin_amdgcn_perm(a[1], a[0], 0x07030501u);  // a0.1 a1.1 a0.3 a1.3
+    const uint32_t t2 = __builtin_amdgcn_perm(a[3], a[2], 0x06020400u);  // a2.0 a3.0 a2.2 a3.2
+    const uint32_t t3 = __builtin_amdgcn_perm(a[3], a[2], 0x07030501u);  // a2.1 a3.1 a2.3 a3.3
+    o[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+    o[2] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+    o[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// ------------------------------------------------------------- launchers
+// Host-side launchers, one per kernel family; arguments are validated by the
+// ABI layer before these run.  Each returns hipSuccess or the launch error.
+hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, float eps,
+                            int8_t* Xq, float* scale_x, hipStream_t s);
+hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
+                               uint8_t* W_packed, float* gamma, void* ws, hipStream_t s);
+size_t weight_quant_ws_bytes(int64_t N);
+hipError_t launch_pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* W_packed,
+                               hipStream_t s);
+hipError_t launch_gemm_i8t2(const int8_t* Xq, const float* scale_x, const uint8_t* Wp,
+                            const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
+                            int32_t* acc, hipStream_t s);
+hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t* Wp,
+                          const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
+                          int32_t* acc, hipStream_t s);
+constexpr int64_t kGemvMaxM = 16;
+hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* scale_x,
+                          const uint8_t* Wp, const float* gamma, int64_t M, int64_t N, int64_t K,
+                          void* grad_x, bool gx_bf16, float* grad_W, void* ws, hipStream_t s);
+size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K);
+
+}  // namespace bitnet

@@ -1,0 +1,389 @@
+// Quantizers of the BitLinear hot path for gfx950.
+//
+//   act_quant    RMSNorm (unit gain) + per-token absmax int8
+//                ("BitNet 1.5技术解析" 2.2 and 3.1; "BitNet 三元权重量化训练工程",
+//                straight-through-estimator section: eps = 1e-5, 127/max|x|)
+//   weight_quant absmean ternary codes + 2-bit packing
+//                ("BitNet 1.5技术解析" 2.1; "1.58-bit量化技术突破AI算力与内存墙限制"
+//                2.2 and 4.1)
+//   pack_ternary pre-quantized codes -> 2-bit packing (same page, 4.1)
+//
+// All three are HBM-bound streams.  Every operation that decides an integer
+// is a single correctly rounded binary32 operation (built with contraction
+// off), and every sum uses the library's canonical tree order, so the int8
+// activations, the codes, gamma and scale_x are reproducible bit for bit.
+#include "common.h"
+
+namespace bitnet {
+
+// ===================================================================== K2
+// One wave per token row.  Block b of the row is the 64*E elements
+// [b*64E, (b+1)*64E); lane l holds elements b*64E + l*E .. +E-1 (one 16-byte
+// load, so each wave load is a fully coalesced 1 KiB).  The sum of squares is
+// the tree over the row: in-lane tree over E, butterfly over the lanes, then
+// the tree over blocks.  NB > 0: the row (at most NB blocks) stays in
+// registers between the two passes.  NB == 0: any length; the row is
+// streamed twice.
+
+constexpr int kAqWaves = 4;
+
+template <typename T, int NB>
+__global__ __launch_bounds__(kAqWaves * kWave) void act_quant_kernel(
+    const T* __restrict__ X, int64_t M, int64_t K, float eps, int8_t* __restrict__ Q,
+    float* __restrict__ S) {
+    constexpr int E = Vec16<T>::E;
+    constexpr int BLK = kWave * E;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row = (int64_t)blockIdx.x * kAqWaves + (threadIdx.x >> 6);
+    if (row >= M) return;  // uniform per wave
+    const T* x = X + row * K;
+    int8_t* q = Q + row * K;
+    const int64_t nblk = (K + BLK - 1) / BLK;
+    const bool vec_ok = (K % E) == 0;  // rows start 16-byte aligned
+
+    auto load_block = [&](int64_t b, float (&v)[E]) {
+        const int64_t k0 = b * BLK + (int64_t)lane * E;
+        if (vec_ok && k0 + E <= K) {
+            Vec16<T>::load(x + k0, v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = (k0 + e < K) ? load_elem(x, k0 + e) : 0.0f;
+        }
+    };
+    auto block_sq_sum = [&](const float (&v)[E]) {
+        float sq[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) sq[e] = v[e] * v[e];
+        return wave_tree_sum(lane_tree<E>(sq));
+    };
+
+    float amax = 0.0f;
+    float ss;
+    float cache[NB > 0 ? NB : 1][E];
+    if constexpr (NB > 0) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b < nblk) load_block(b, cache[b]);
+        }
+        float bs[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b < nblk) {
+                bs[b] = block_sq_sum(cache[b]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(cache[b][e]));
+            } else {
+                bs[b] = 0.0f;
+            }
+        }
+        ss = lane_tree<NB>(bs);  // blocks beyond the row are +0 (exact padding)
+    } else {
+        PairwiseStack st;
+        for (int64_t b = 0; b < nblk; ++b) {
+            float v[E];
+            load_block(b, v);
+            st.push(block_sq_sum(v));
+#pragma unroll
+            for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
+        }
+        ss = st.total();
+    }
+    amax = wave_max(amax);
+
+    const float ms = ss / (float)K;
+    const float d = sqrtf(ms + eps);
+    const float inv = 1.0f / d;
+    // max|x * inv| == max|x| * inv: rounding is monotone, inv > 0
+    const float a = amax * inv;
+    const float scale = 127.0f / fmaxf(a, 1e-5f);
+    if (lane == 0) S[row] = scale;
+
+    auto quant_store = [&](int64_t b, const float (&v)[E]) {
+        const int64_t k0 = b * BLK + (int64_t)lane * E;
+        int8_t qv[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float n = v[e] * inv;
+            float r = rintf(n * scale);
+            r = fminf(fmaxf(r, -128.0f), 127.0f);
+            qv[e] = (int8_t)(int)r;
+        }
+        if (vec_ok && k0 + E <= K) {
+            if constexpr (E == 8) {
+                uint2 pk;
+                pk.x = (uint32_t)(uint8_t)qv[0] | ((uint32_t)(uint8_t)qv[1] << 8) |
+                       ((uint32_t)(uint8_t)qv[2] << 16) | ((uint32_t)(uint8_t)qv[3] << 24);
+                pk.y = (uint32_t)(uint8_t)qv[4] | ((uint32_t)(uint8_t)qv[5] << 8) |
+                       ((uint32_t)(uint8_t)qv[6] << 16) | ((uint32_t)(uint8_t)qv[7] << 24);
+                if ((K % 8) == 0) {
+                    *reinterpret_cast<uint2*>(q + k0) = pk;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) q[k0 + e] = qv[e];
+                }
+            } else {
+                const uint32_t pk = (uint32_t)(uint8_t)qv[0] | ((uint32_t)(uint8_t)qv[1] << 8) |
+                                    ((uint32_t)(uint8_t)qv[2] << 16) |
+                                    ((uint32_t)(uint8_t)qv[3] << 24);
+                *reinterpret_cast<uint32_t*>(q + k0) = pk;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (k0 + e < K) q[k0 + e] = qv[e];
+        }
+    };
+
+    if constexpr (NB > 0) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (b < nblk) quant_store(b, cache[b]);
+    } else {
+        for (int64_t b = 0; b < nblk; ++b) {
+            float v[E];
+            load_block(b, v);
+            quant_store(b, v);
+        }
+    }
+}
+
+template <typename T>
+static hipError_t act_quant_dispatch(const T* X, int64_t M, int64_t K, float eps, int8_t* Q,
+                                     float* S, hipStream_t s) {
+    constexpr int E = Vec16<T>::E;
+    const int64_t nblk = (K + kWave * E - 1) / (kWave * E);
+    const dim3 grid((unsigned)((M + kAqWaves - 1) / kAqWaves)), block(kAqWaves * kWave);
+    if (nblk <= 1)
+        act_quant_kernel<T, 1><<<grid, block, 0, s>>>(X, M, K, eps, Q, S);
+    else if (nblk <= 2)
+        act_quant_kernel<T, 2><<<grid, block, 0, s>>>(X, M, K, eps, Q, S);
+    else if (nblk <= 4)
+        act_quant_kernel<T, 4><<<grid, block, 0, s>>>(X, M, K, eps, Q, S);
+    else if (nblk <= 8)
+        act_quant_kernel<T, 8><<<grid, block, 0, s>>>(X, M, K, eps, Q, S);
+    else if (nblk <= 16)
+        act_quant_kernel<T, 16><<<grid, block, 0, s>>>(X, M, K, eps, Q, S);
+    else
+        act_quant_kernel<T, 0><<<grid, block, 0, s>>>(X, M, K, eps, Q, S);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, float eps,
+                            int8_t* Xq, float* scale_x, hipStream_t s) {
+    if (x_bf16)
+        return act_quant_dispatch(static_cast<const uint16_t*>(X), M, K, eps, Xq, scale_x, s);
+    return act_quant_dispatch(static_cast<const float*>(X), M, K, eps, Xq, scale_x, s);
+}
+
+// ===================================================================== K1
+// Pass 1: one wave per weight row -> tree sum of |w| over the row.
+// Pass 2: one workgroup -> tree over the row sums, gamma = max(S/(N*K), 1e-5),
+//         and the code threshold (below).
+// Pass 3: each thread turns kPackU groups of 4 weights into packed bytes.
+//
+// Code decision without a per-element division.  code != 0 exactly when
+// rint(fl(|w| / gamma)) >= 1, i.e. when fl(|w| / gamma) > 0.5.  With a
+// correctly rounded quotient that holds iff |w| / gamma > 0.5 + 2^-25 (the
+// rounding boundary above 0.5; a quotient exactly on it rounds to the even
+// neighbour 0.5), i.e. iff |w| > t with t = gamma * (0.5 + 2^-25).  t has at
+// most 49 significant bits, so it is exact in binary64, and for a binary32
+// |w| the test |w| > t equals |w| >= thr, thr = the least float above t.
+
+constexpr int kWqWaves = 4;
+
+template <typename T>
+__global__ __launch_bounds__(kWqWaves * kWave) void wq_row_abs_sum_kernel(
+    const T* __restrict__ W, int64_t N, int64_t K, float* __restrict__ row_sums) {
+    constexpr int E = Vec16<T>::E;
+    constexpr int BLK = kWave * E;
+    constexpr int G = 8;  // loads in flight per lane
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row = (int64_t)blockIdx.x * kWqWaves + (threadIdx.x >> 6);
+    if (row >= N) return;
+    const T* w = W + row * K;
+    const int64_t nblk = (K + BLK - 1) / BLK;
+    const bool vec_ok = (K % E) == 0;
+    PairwiseStack st;
+    for (int64_t b0 = 0; b0 < nblk; b0 += G) {
+        float v[G][E];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int64_t k0 = (b0 + g) * BLK + (int64_t)lane * E;
+            if (b0 + g < nblk && vec_ok && k0 + E <= K) {
+                Vec16<T>::load(w + k0, v[g]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    v[g][e] = (b0 + g < nblk && k0 + e < K) ? load_elem(w, k0 + e) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (b0 + g < nblk) {
+                float a[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) a[e] = fabsf(v[g][e]);
+                st.push(wave_tree_sum(lane_tree<E>(a)));
+            }
+        }
+    }
+    if (lane == 0) row_sums[row] = st.total();
+}
+
+// Pass 2 uses 16 waves: with P = N rounded up to a power of two and
+// L = max(256, P/16), wave w sums the aligned range [w*L, (w+1)*L) as a tree
+// and thread 0 combines the 16 partial sums as a tree (ranges beyond N are
+// +0), which is the tree over all N row sums.
+constexpr int kGammaWaves = 16;
+
+__global__ __launch_bounds__(kGammaWaves * kWave) void wq_gamma_kernel(
+    const float* __restrict__ row_sums, int64_t N, int64_t K, float* __restrict__ gamma,
+    float* __restrict__ thr_out) {
+    __shared__ float part[kGammaWaves];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x >> 6;
+    constexpr int E = 4;
+    constexpr int BLK = kWave * E;
+    int64_t P = 1;
+    while (P < N) P *= 2;
+    const int64_t L = P / kGammaWaves > BLK ? P / kGammaWaves : BLK;
+    const int64_t lo = (int64_t)wv * L;
+    const int64_t nblk = L / BLK;
+    PairwiseStack st;
+    for (int64_t b0 = 0; b0 < nblk; b0 += 8) {
+        float v[8][E];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int64_t k0 = lo + (b0 + g) * BLK + (int64_t)lane * E;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                v[g][e] = (b0 + g < nblk && k0 + e < N) ? row_sums[k0 + e] : 0.0f;
+        }
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+            if (b0 + g < nblk) st.push(wave_tree_sum(lane_tree<E>(v[g])));
+    }
+    if (lane == 0) part[wv] = st.total();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float p16[kGammaWaves];
+#pragma unroll
+        for (int i = 0; i < kGammaWaves; ++i) p16[i] = part[i];
+        const float total = lane_tree<kGammaWaves>(p16);
+        const float mean = total / (float)(N * K);
+        const float g = fmaxf(mean, 1e-5f);
+        const double t = (double)g * (0.5 + 0x1p-25);
+        float thr = (float)t;
+        if ((double)thr <= t) thr = __uint_as_float(__float_as_uint(thr) + 1u);
+        gamma[0] = g;
+        thr_out[0] = thr;
+    }
+}
+
+__device__ __forceinline__ uint32_t code_bits(float w, float thr) {
+    // 01 = +1, 10 = -1, 00 = 0
+    return fabsf(w) >= thr ? (w > 0.0f ? 1u : 2u) : 0u;
+}
+
+constexpr int kPackU = 4;  // groups of 4 weights per thread (loads in flight)
+
+template <typename T>
+__global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, int64_t total4,
+                                                      const float* __restrict__ thr_p,
+                                                      uint8_t* __restrict__ out) {
+    const float thr = *thr_p;
+    const int64_t base = (int64_t)blockIdx.x * (256 * kPackU) + threadIdx.x;
+    float v[kPackU][4];
+#pragma unroll
+    for (int u = 0; u < kPackU; ++u) {
+        const int64_t i = base + u * 256;
+        if (i < total4) {
+            if constexpr (sizeof(T) == 4) {
+                const float4 q = reinterpret_cast<const float4*>(W)[i];
+                v[u][0] = q.x; v[u][1] = q.y; v[u][2] = q.z; v[u][3] = q.w;
+            } else {
+                const uint2 q = reinterpret_cast<const uint2*>(W)[i];
+                v[u][0] = __uint_as_float(q.x << 16);
+                v[u][1] = __uint_as_float(q.x & 0xffff0000u);
+                v[u][2] = __uint_as_float(q.y << 16);
+                v[u][3] = __uint_as_float(q.y & 0xffff0000u);
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kPackU; ++u) {
+        const int64_t i = base + u * 256;
+        if (i < total4) {
+            uint32_t byte = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) byte |= code_bits(v[u][j], thr) << (2 * j);
+            out[i] = (uint8_t)byte;
+        }
+    }
+}
+
+size_t weight_quant_ws_bytes(int64_t N) {
+    // row sums, then the threshold float, 256-byte aligned
+    return (size_t)(((N * 4 + 255) / 256) * 256 + 256);
+}
+
+static unsigned stream_grid(int64_t work_items, int per_block) {
+    int64_t g = (work_items + per_block - 1) / per_block;
+    const int64_t cap = 256 * 32;  // enough resident waves to saturate HBM
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
+
+hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
+                               uint8_t* W_packed, float* gamma, void* ws, hipStream_t s) {
+    float* row_sums = static_cast<float*>(ws);
+    float* thr = reinterpret_cast<float*>(static_cast<char*>(ws) + ((N * 4 + 255) / 256) * 256);
+    const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
+    if (w_bf16)
+        wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K,
+                                                           row_sums);
+    else
+        wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K,
+                                                        row_sums);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    wq_gamma_kernel<<<1, kGammaWaves * kWave, 0, s>>>(row_sums, N, K, gamma, thr);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total4 = N * K / 4;
+    const unsigned g3 = (unsigned)((total4 + 256 * kPackU - 1) / (256 * kPackU));
+    if (w_bf16)
+        wq_pack_kernel<uint16_t><<<g3, 256, 0, s>>>(static_cast<const uint16_t*>(W), total4, thr,
+                                                     W_packed);
+    else
+        wq_pack_kernel<float><<<g3, 256, 0, s>>>(static_cast<const float*>(W), total4, thr,
+                                                  W_packed);
+    return hipGetLastError();
+}
+
+// ============================================================ pack helper
+__global__ __launch_bounds__(256) void pack_codes_kernel(const int8_t* __restrict__ codes,
+                                                         int64_t total4,
+                                                         uint8_t* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total4; i += stride) {
+        const uint32_t c4 = reinterpret_cast<const uint32_t*>(codes)[i];
+        uint32_t byte = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int8_t c = (int8_t)(c4 >> (8 * j));
+            byte |= (c > 0 ? 1u : (c < 0 ? 2u : 0u)) << (2 * j);
+        }
+        out[i] = (uint8_t)byte;
+    }
+}
+
+hipError_t launch_pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* W_packed,
+                               hipStream_t s) {
+    const int64_t total4 = N * K / 4;
+    pack_codes_kernel<<<stream_grid(total4, 256), 256, 0, s>>>(codes, total4, W_packed);
+    return hipGetLastError();
+}
+
+}  // namespace bitnet

@@ -1,0 +1,181 @@
+/*
+ * bitnet.h -- C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear hot path.
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [NOTES] "BitNet 1.5技术解析：2比特量化在神经网络中的应用与挑战"
+ *           (intelliparadigm.com): 2.1 weight quantization, 2.2 activation
+ *           quantization, 3.1 the BitLinear layer, 5.2 hardware needs.
+ *   [ENG]   "BitNet 三元权重量化训练工程：直通估计器与梯度裁剪实践"
+ *           (blog.hotdry.top, 2025-10-04): section on the straight-through
+ *           estimator for ternary weights (absmean, absmax per token,
+ *           eps = 1e-5); section on gradient clipping (bf16 forward, fp32
+ *           gradients).
+ *   [WALL]  "1.58-bit量化技术突破AI算力与内存墙限制" (intelliparadigm.com):
+ *           2.2 ternary quantization, 3.1 add/subtract matmul, 3.2 the STE,
+ *           4.1 2-bit memory layout.
+ *
+ * Conventions shared by every call
+ *   - Tensors are row-major and contiguous.  Every tensor pointer is a
+ *     DEVICE pointer on the current HIP device unless a comment says
+ *     otherwise; gamma and scale_x stay on the device (no call copies to
+ *     the host).  Pointers must be 16-byte aligned.
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     never allocates device memory, keeps no pointer after returning and
+ *     has no mutable global state.
+ *   - Asynchrony: a call validates its arguments on the host, enqueues its
+ *     kernels on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream) and returns.  Outputs are valid once the stream reaches that
+ *     point.  Calls on one stream run in order.
+ *   - Errors: every argument check runs before any launch; on failure the
+ *     call returns a negative bitnet_status and enqueues nothing.  A failed
+ *     launch returns BITNET_E_HIP.  No C++ exception crosses the ABI.
+ *     NaN or Inf inputs give unspecified (but memory-safe) results.
+ *   - Determinism: the same inputs give the same output bits (no floating
+ *     point atomics; every reduction has a fixed order).
+ *   - Sizes: M tokens, K input features, N output features; 1 <= M, N, K
+ *     < 2^31.  K % 4 == 0 for the quantizer and packing calls (whole packed
+ *     bytes); K % 16 == 0 for the linear calls (whole packed dwords).
+ *   - Built for gfx950 only; on any other device a launch fails and the call
+ *     returns BITNET_E_HIP.
+ *
+ * Packed ternary weights ([WALL 4.1]): 2 bits per weight, 00 = 0,
+ * 01 = +1, 10 = -1 (11 never written).  Row n of W occupies K/4 bytes
+ * starting at byte n*K/4; the code of column k sits in bits 2*(k%4) and
+ * 2*(k%4)+1 of byte k/4 of its row.  The bit order is this library's choice
+ * (the page fixes only the codes).
+ */
+#ifndef BITNET_H_
+#define BITNET_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BITNET_OK = 0,
+    BITNET_E_ARG = -1,       /* null required pointer or bad flag          */
+    BITNET_E_SHAPE = -2,     /* M, N or K out of range or K not a multiple  */
+    BITNET_E_DTYPE = -3,     /* unknown or unsupported dtype code           */
+    BITNET_E_ALIGN = -4,     /* a pointer is not 16-byte aligned            */
+    BITNET_E_WORKSPACE = -5, /* workspace missing or smaller than required  */
+    BITNET_E_HIP = -6        /* a HIP launch or runtime call failed         */
+} bitnet_status;
+
+typedef enum { BITNET_F32 = 0, BITNET_BF16 = 1 } bitnet_dtype;
+
+typedef enum {
+    BITNET_OP_WEIGHT_QUANT = 0,
+    BITNET_OP_LINEAR_BWD_STE = 1,
+    BITNET_OP_LINEAR_FWD = 2
+} bitnet_op;
+
+/*
+ * Absmean ternary weight quantization and 2-bit packing.
+ * [NOTES 2.1], [WALL 2.2], [ENG STE section]:
+ *   gamma = max(mean|W|, 1e-5) over the WHOLE matrix,
+ *   code  = clamp(round(W / gamma), -1, 1), round = half to even.
+ * The mean is evaluated in binary32 in one fixed order: per row a pairwise
+ * tree over the row (zero-padded to a power of two), then a pairwise tree
+ * over the N row sums, then one division by the binary32 value of N*K.
+ * W / gamma is the correctly rounded binary32 quotient.
+ *   W        [N][K] fp32 or bf16 (w_dtype)
+ *   W_packed [N][K/4] bytes, written
+ *   gamma    1 float, written (device)
+ *   workspace >= bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT, 0, N, K)
+ *            bytes of device scratch (row sums); contents on entry ignored.
+ * Errors: BITNET_E_ARG, BITNET_E_SHAPE (K % 4), BITNET_E_DTYPE,
+ * BITNET_E_ALIGN, BITNET_E_WORKSPACE, BITNET_E_HIP.
+ */
+int bitnet_weight_quant(const void *W, int w_dtype, int64_t N, int64_t K,
+                        uint8_t *W_packed, float *gamma,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * RMSNorm (unit gain) followed by per-token absmax int8 quantization.
+ * [NOTES 3.1] (RMSNorm before the quantizer), [NOTES 2.2] and [ENG STE
+ * section] (per-row scale 127 / max|x|, max clamped at 1e-5, eps = 1e-5):
+ *   d       = sqrt(sum_k x^2 / K + eps)     (pairwise tree over the row)
+ *   n_k     = x_k * (1 / d)
+ *   scale_x = 127 / max(max_k |n_k|, 1e-5)
+ *   q_k     = clamp(round(n_k * scale_x), -128, 127), round half to even
+ * every operation a single correctly rounded binary32 operation.
+ *   X       [M][K] fp32 or bf16 (x_dtype)
+ *   Xq      [M][K] int8, written
+ *   scale_x [M] fp32, written
+ * Errors: BITNET_E_ARG, BITNET_E_SHAPE, BITNET_E_DTYPE, BITNET_E_ALIGN,
+ * BITNET_E_HIP.
+ */
+int bitnet_act_quant(const void *X, int x_dtype, int64_t M, int64_t K, float eps,
+                     int8_t *Xq, float *scale_x, void *stream);
+
+/*
+ * BitLinear forward from the quantized operands.
+ * [NOTES 3.1] (linear layer, then multiply back by the scale), [NOTES 5.2]
+ * (wide accumulator), [WALL 3.1] (+1 adds, -1 subtracts, 0 skips):
+ *   acc[m][n] = sum_k Xq[m][k] * code[n][k]      (exact int32)
+ *   Y[m][n]   = acc[m][n] * gamma / scale_x[m]   (fp32)
+ * M <= 16 takes the bandwidth-bound packed GEMV, larger M the int8 MFMA
+ * GEMM.
+ *   Xq       [M][K] int8;  scale_x [M] fp32;  W_packed [N][K/4];  gamma 1 fp32
+ *   Y        [M][N] fp32, written
+ *   acc      [M][N] int32, written when non-NULL (for exact checks)
+ * |acc| <= 128*K must fit int32, so K < 2^24; K % 16 == 0.
+ * Errors: BITNET_E_ARG, BITNET_E_SHAPE, BITNET_E_ALIGN, BITNET_E_HIP.
+ */
+int bitnet_linear_fwd(const int8_t *Xq, const float *scale_x, const uint8_t *W_packed,
+                      const float *gamma, int64_t M, int64_t N, int64_t K,
+                      float *Y, int32_t *acc, void *stream);
+
+/*
+ * Straight-through-estimator backward of the BitLinear forward above.
+ * [NOTES 2.1, 2.2] (the detach trick), [WALL 3.2] (the backward passes the
+ * incoming gradient through): both quantizers act as the identity, so with
+ * W_deq = gamma * code and X_deq = Xq / scale_x
+ *   grad_x[m][k] = sum_n grad_y[m][n] * W_deq[n][k]
+ *   grad_W[n][k] = sum_m grad_y[m][n] * X_deq[m][k]
+ * computed on bf16 matrix cores with fp32 accumulation ([ENG clipping
+ * section]: bf16 forward, fp32 gradients).  grad_x is the gradient with
+ * respect to the quantizer input (the RMSNorm output).
+ *   grad_y  [M][N] bf16 (gy_dtype must be BITNET_BF16)
+ *   Xq [M][K] int8, scale_x [M] fp32, W_packed [N][K/4], gamma 1 fp32
+ *   grad_x  [M][K] fp32 or bf16 (gx_dtype), written when non-NULL
+ *   grad_W  [N][K] fp32, written when non-NULL
+ *   workspace >= bitnet_workspace_bytes(BITNET_OP_LINEAR_BWD_STE, M, N, K)
+ *            device scratch: bf16 copies of codes^T, grad_y^T and X_deq^T
+ *            (2*(K*N + N*M + K*M) bytes); contents on entry ignored.
+ * K % 16 == 0.
+ * Errors: BITNET_E_ARG (both outputs NULL), BITNET_E_SHAPE, BITNET_E_DTYPE,
+ * BITNET_E_ALIGN, BITNET_E_WORKSPACE, BITNET_E_HIP.
+ */
+int bitnet_linear_bwd_ste(const void *grad_y, int gy_dtype, const int8_t *Xq,
+                          const float *scale_x, const uint8_t *W_packed, const float *gamma,
+                          int64_t M, int64_t N, int64_t K,
+                          void *grad_x, int gx_dtype, float *grad_W,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Pack pre-quantized ternary codes ([WALL 4.1] code table).
+ *   codes    [N][K] int8; a value > 0 packs as +1, < 0 as -1, 0 as 0
+ *   W_packed [N][K/4] bytes, written
+ * Errors: BITNET_E_ARG, BITNET_E_SHAPE (K % 4), BITNET_E_ALIGN, BITNET_E_HIP.
+ */
+int bitnet_pack_ternary(const int8_t *codes, int64_t N, int64_t K, uint8_t *W_packed,
+                        void *stream);
+
+/* Device scratch bytes `op` needs for these sizes (0 = none). */
+size_t bitnet_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+/* Static, human-readable text for a status code. */
+const char *bitnet_status_str(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int bitnet_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_H_ */

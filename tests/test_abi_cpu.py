@@ -1,0 +1,118 @@
+"""The C-ABI library loads on a host without a GPU, exports every entry point
+include/bitnet.h declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_ternary_quantized_amd as bt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitnet.h")
+
+# Fake, 16-byte-aligned device addresses: every call below fails its host
+# checks first, so nothing is ever dereferenced or launched.
+P = ctypes.c_void_p(1 << 20)
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitnet_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = declared_functions()
+    for n in ("bitnet_weight_quant", "bitnet_act_quant", "bitnet_linear_fwd", "bitnet_linear_bwd_ste"):
+        assert n in names
+    assert set(names) == set(bt.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bt.load_library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    raw = ctypes.CDLL(bt.LIB_PATH)
+    for n in declared_functions():
+        getattr(raw, n)  # raises AttributeError when missing
+
+
+def test_status_strings_and_version():
+    assert bt.bitnet_status_str(0) == "ok"
+    for s in range(-6, 0):
+        assert bt.bitnet_status_str(s) not in ("ok", "unknown status")
+    assert bt.bitnet_status_str(-99) == "unknown status"
+    assert bt.bitnet_version() >= 10000
+
+
+def test_workspace_sizes():
+    assert bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_FWD, 8, 8, 16) == 0
+    wq = bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, 0, 28672, 8192)
+    assert wq >= 28672 * 4 + 4 and wq % 256 == 0
+    M, N, K = 4096, 28672, 8192
+    bw = bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, M, N, K)
+    assert bw >= 2 * (K * N + N * M + K * M)
+    assert bt.bitnet_workspace_bytes(7, 1, 1, 4) == 0
+    assert bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, -1, 4, 4) == 0
+
+
+def test_weight_quant_rejects_bad_arguments():
+    lib = bt.load_library()
+    ws = 1 << 20
+    assert lib.bitnet_weight_quant(NULL, 0, 4, 4, P, P, P, ws, NULL) == -1
+    assert lib.bitnet_weight_quant(P, 7, 4, 4, P, P, P, ws, NULL) == -3
+    assert lib.bitnet_weight_quant(P, 0, 0, 4, P, P, P, ws, NULL) == -2
+    assert lib.bitnet_weight_quant(P, 0, 4, 6, P, P, P, ws, NULL) == -2       # K % 4
+    assert lib.bitnet_weight_quant(P, 0, 4, 4, ctypes.c_void_p((1 << 20) + 2), P, P, ws, NULL) == -4
+    assert lib.bitnet_weight_quant(P, 0, 4, 4, P, P, P, 16, NULL) == -5      # workspace too small
+    assert lib.bitnet_weight_quant(P, 0, 4, 4, P, P, NULL, ws, NULL) == -5
+
+
+def test_act_quant_rejects_bad_arguments():
+    lib = bt.load_library()
+    e = ctypes.c_float(1e-5)
+    assert lib.bitnet_act_quant(NULL, 0, 4, 4, e, P, P, NULL) == -1
+    assert lib.bitnet_act_quant(P, 2, 4, 4, e, P, P, NULL) == -3
+    assert lib.bitnet_act_quant(P, 0, 0, 4, e, P, P, NULL) == -2
+    assert lib.bitnet_act_quant(P, 0, 4, -1, e, P, P, NULL) == -2
+    assert lib.bitnet_act_quant(P, 0, 4, 4, ctypes.c_float(-1.0), P, P, NULL) == -1
+    assert lib.bitnet_act_quant(ctypes.c_void_p((1 << 20) + 8), 0, 4, 4, e, P, P, NULL) == -4
+
+
+def test_linear_fwd_rejects_bad_arguments():
+    lib = bt.load_library()
+    assert lib.bitnet_linear_fwd(P, P, P, P, 4, 4, 16, NULL, NULL, NULL) == -1
+    assert lib.bitnet_linear_fwd(P, P, P, P, 4, 4, 8, P, NULL, NULL) == -2     # K % 16
+    assert lib.bitnet_linear_fwd(P, P, P, P, 4, 0, 16, P, NULL, NULL) == -2
+    assert lib.bitnet_linear_fwd(P, P, P, P, 4, 4, 1 << 24, P, NULL, NULL) == -2
+    assert lib.bitnet_linear_fwd(P, P, P, P, 4, 4, 16, P, ctypes.c_void_p((1 << 20) + 4), NULL) == -4
+
+
+def test_linear_bwd_rejects_bad_arguments():
+    lib = bt.load_library()
+    ws = 1 << 30
+    assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 4, 4, 16, NULL, 0, NULL, P, ws, NULL) == -1
+    assert lib.bitnet_linear_bwd_ste(P, 0, P, P, P, P, 4, 4, 16, P, 0, P, P, ws, NULL) == -3   # fp32 gy
+    assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 4, 4, 16, P, 5, P, P, ws, NULL) == -3
+    assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 4, 4, 12, P, 0, P, P, ws, NULL) == -2
+    assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 4, 4, 16, P, 0, P, P, 64, NULL) == -5
+
+
+def test_pack_rejects_bad_arguments():
+    lib = bt.load_library()
+    assert lib.bitnet_pack_ternary(NULL, 4, 4, P, NULL) == -1
+    assert lib.bitnet_pack_ternary(P, 4, 5, P, NULL) == -2
+    assert lib.bitnet_pack_ternary(P, 4, 4, ctypes.c_void_p((1 << 20) + 1), NULL) == -4
+
+
+def test_binding_has_no_silent_fallback(tmp_path):
+    # a missing library is an error, never a CPU path
+    with pytest.raises(ImportError):
+        bt._lib_saved = bt._lib
+        try:
+            bt._lib = None
+            bt.load_library(str(tmp_path / "missing.so"))
+        finally:
+            bt._lib = bt._lib_saved

@@ -1,0 +1,126 @@
+"""GPU parity of the BitLinear forward (int8 MFMA GEMM and packed GEMV) and
+the STE backward (bf16 MFMA GEMMs) against the CPU oracle.
+
+Forward: int32 accumulators bit-exact, Y within relative 1e-3 of the
+float64 reference.  Backward: within 2e-2 (elementwise against |r| + RMS(r)
+and as a relative Frobenius error) of the float64 reference.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_ternary_quantized_amd as bt
+import oracle
+import workloads
+from gpu_util import assert_grad_close, assert_y_close, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _quantized_operands(M, N, K, seed, p_zero=0.35):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randint(-127, 128, (M, K), generator=g, dtype=torch.int64).to(torch.int8)
+    codes = workloads.ternary_codes(N, K, p_zero, seed=seed + 1)
+    scale_x = (20.0 + 30.0 * torch.rand(M, generator=g, dtype=torch.float64)).to(torch.float32)
+    gamma = torch.tensor([0.0123], dtype=torch.float32)
+    return q, codes, scale_x, gamma
+
+
+FWD_SHAPES = [
+    # GEMV path (M <= 16)
+    (1, 16, 16), (1, 300, 256), (2, 33, 1040), (5, 257, 4096), (16, 1000, 512),
+    (16, 64, 16384), (3, 17, 48),
+    # GEMM path: several tiles plus ragged edges in M, N and K
+    (17, 16, 16), (100, 300, 256), (256, 256, 64), (300, 513, 1040),
+    (513, 257, 4096), (1000, 40, 48),
+]
+
+
+@pytest.mark.parametrize("M,N,K", FWD_SHAPES)
+def test_linear_fwd_exact_acc(M, N, K):
+    print(f"linear_fwd M={M} N={N} K={K}", flush=True)
+    q, codes, scale_x, gamma = _quantized_operands(M, N, K, seed=M * 31 + N * 7 + K)
+    wp = oracle.pack(codes.numpy())
+    Y, acc = bt.bitnet_linear_fwd(to_dev(q), to_dev(scale_x), to_dev(torch.from_numpy(wp)),
+                                  to_dev(gamma), want_acc=True)
+    torch.cuda.synchronize()
+    acc_ref, y_ref = oracle.linear_fwd(q.numpy(), scale_x.numpy(), codes.numpy(), float(gamma[0]))
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert_y_close(Y.cpu().numpy(), y_ref)
+
+
+def test_linear_fwd_extreme_values():
+    # |acc| = 128*K at the int8 extremes: int32 accumulation must not wrap
+    M, N, K = 20, 32, 4096
+    q = torch.full((M, K), -128, dtype=torch.int8)
+    q[::2] = 127
+    codes = torch.full((N, K), -1, dtype=torch.int8)
+    codes[::3] = 1
+    scale_x = torch.full((M,), 3.0)
+    gamma = torch.tensor([0.5])
+    wp = oracle.pack(codes.numpy())
+    for m in (M, 4):  # GEMM and GEMV paths
+        Y, acc = bt.bitnet_linear_fwd(to_dev(q[:m]), to_dev(scale_x[:m]), to_dev(torch.from_numpy(wp)),
+                                      to_dev(gamma), want_acc=True)
+        acc_ref, y_ref = oracle.linear_fwd(q[:m].numpy(), scale_x[:m].numpy(), codes.numpy(), 0.5)
+        assert np.array_equal(acc.cpu().numpy(), acc_ref)
+        assert_y_close(Y.cpu().numpy(), y_ref)
+
+
+def test_linear_fwd_all_zero_codes_give_zero():
+    M, N, K = 40, 48, 256
+    q, _, scale_x, gamma = _quantized_operands(M, N, K, seed=5)
+    wp = torch.zeros(N, K // 4, dtype=torch.uint8)
+    Y, acc = bt.bitnet_linear_fwd(to_dev(q), to_dev(scale_x), to_dev(wp), to_dev(gamma), want_acc=True)
+    assert not acc.any().item() and not Y.any().item()
+
+
+BWD_SHAPES = [(1, 16, 16), (17, 33, 64), (300, 257, 272), (256, 256, 256), (600, 100, 48), (64, 1376, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", BWD_SHAPES)
+@pytest.mark.parametrize("gx_dtype", [torch.float32, torch.bfloat16])
+def test_linear_bwd_ste(M, N, K, gx_dtype):
+    print(f"linear_bwd M={M} N={N} K={K} {gx_dtype}", flush=True)
+    q, codes, scale_x, gamma = _quantized_operands(M, N, K, seed=M + 3 * N + 5 * K)
+    gy = workloads.normal((M, N), 1e-3, seed=M + N, dtype="bf16")
+    wp = oracle.pack(codes.numpy())
+    gx, gw = bt.bitnet_linear_bwd_ste(to_dev(gy), to_dev(q), to_dev(scale_x), to_dev(torch.from_numpy(wp)),
+                                      to_dev(gamma), gx_dtype=gx_dtype)
+    torch.cuda.synchronize()
+    gx_ref = oracle.ste_grad_x(host(gy), codes.numpy(), float(gamma[0]))
+    gw_ref = oracle.ste_grad_w(host(gy), q.numpy(), scale_x.numpy())
+    assert_grad_close(gx.float().cpu().numpy(), gx_ref, "grad_x")
+    assert_grad_close(gw.cpu().numpy(), gw_ref, "grad_W")
+
+
+def test_linear_bwd_single_outputs():
+    M, N, K = 70, 90, 128
+    q, codes, scale_x, gamma = _quantized_operands(M, N, K, seed=9)
+    gy = workloads.normal((M, N), 1e-3, seed=10, dtype="bf16")
+    wp = to_dev(torch.from_numpy(oracle.pack(codes.numpy())))
+    gx, gw = bt.bitnet_linear_bwd_ste(to_dev(gy), to_dev(q), to_dev(scale_x), wp, to_dev(gamma),
+                                      want_grad_W=False)
+    assert gw is None
+    assert_grad_close(gx.cpu().numpy(), oracle.ste_grad_x(host(gy), codes.numpy(), float(gamma[0])), "grad_x")
+    gx, gw = bt.bitnet_linear_bwd_ste(to_dev(gy), to_dev(q), to_dev(scale_x), wp, to_dev(gamma),
+                                      want_grad_x=False)
+    assert gx is None
+    assert_grad_close(gw.cpu().numpy(), oracle.ste_grad_w(host(gy), q.numpy(), scale_x.numpy()), "grad_W")
+
+
+def test_end_to_end_small_layer():
+    # RMSNorm + act quant, weight quant, forward, STE backward: every stage
+    # against the oracle on the same seeded inputs
+    d = workloads.linear_inputs(96, 200, 320, x_dtype="bf16", w_dtype="f32", seed=21)
+    out = bt.bitlinear_forward(to_dev(d["x"]), to_dev(d["w"]), want_acc=True)
+    q_ref, s_ref = oracle.act_quant(host(d["x"]))
+    c_ref, g_ref = oracle.weight_quant(host(d["w"]))
+    assert np.array_equal(out["Xq"].cpu().numpy(), q_ref)
+    assert np.array_equal(out["W_packed"].cpu().numpy(), oracle.pack(c_ref))
+    acc_ref, y_ref = oracle.linear_fwd(q_ref, s_ref, c_ref, g_ref)
+    assert np.array_equal(out["acc"].cpu().numpy(), acc_ref)
+    assert_y_close(out["Y"].cpu().numpy(), y_ref)
+    gx, gw = bt.bitnet_linear_bwd_ste(to_dev(d["gy"]), out["Xq"], out["scale_x"], out["W_packed"], out["gamma"])
+    assert_grad_close(gx.cpu().numpy(), oracle.ste_grad_x(host(d["gy"]), c_ref, g_ref), "grad_x")
+    assert_grad_close(gw.cpu().numpy(), oracle.ste_grad_w(host(d["gy"]), q_ref, s_ref), "grad_W")

@@ -1,0 +1,126 @@
+"""GPU parity of the quantizers against the CPU oracle: bit-exact int8
+activations, scale_x bits, ternary codes (packed bytes) and gamma bits."""
+import numpy as np
+import pytest
+import torch
+
+import bit_ternary_quantized_amd as bt
+import oracle
+import workloads
+from gpu_util import DEV, f32_bits_equal, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _act_case(M, K, dtype, seed, special=None):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, K, generator=g)
+    if special == "zero_rows":
+        x[::3] = 0.0
+    elif special == "outliers":
+        x[:, ::97] *= 40.0
+    elif special == "tiny":
+        x *= 1e-3
+    elif special == "single":
+        x.zero_()
+        x[:, K // 2] = -2.5
+    return x.to(dtype)
+
+
+@pytest.mark.parametrize("M,K,dtype,special", [
+    (32, 256, torch.float32, None),          # the tiny workload's shape
+    (1, 4, torch.float32, None),
+    (3, 12, torch.float32, None),            # K not a multiple of the 16-byte vector (bf16)
+    (17, 100, torch.bfloat16, None),
+    (5, 1000, torch.float32, None),
+    (64, 512, torch.bfloat16, "zero_rows"),
+    (33, 4096, torch.bfloat16, "outliers"),
+    (9, 8192, torch.bfloat16, None),
+    (9, 4096, torch.float32, "tiny"),
+    (4, 520, torch.float32, "single"),
+    (3, 20000, torch.bfloat16, None),        # streamed (row beyond the register cache)
+    (2, 12345, torch.float32, None),
+])
+def test_act_quant_bit_exact(M, K, dtype, special):
+    print(f"act_quant M={M} K={K} {dtype} {special}", flush=True)
+    x = _act_case(M, K, dtype, seed=M * 1000 + K, special=special)
+    q, s = bt.bitnet_act_quant(to_dev(x))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.act_quant(host(x))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert f32_bits_equal(s.cpu().numpy(), s_ref)
+
+
+def _weight_case(N, K, dtype, seed, special=None):
+    if special == "zero":
+        return torch.zeros(N, K, dtype=dtype)
+    w = workloads.normal((N, K), 0.02, seed=seed, dtype="f32")
+    if special == "heavy":
+        w[:, :3] *= 50.0
+    return w.to(dtype)
+
+
+@pytest.mark.parametrize("N,K,dtype,special", [
+    (256, 256, torch.float32, None),
+    (1, 4, torch.float32, None),
+    (5, 12, torch.float32, None),
+    (37, 100, torch.bfloat16, None),
+    (300, 512, torch.float32, None),
+    (129, 1028, torch.bfloat16, "heavy"),
+    (1376, 512, torch.float32, None),
+    (64, 8192, torch.float32, None),
+    (7, 64, torch.float32, "zero"),
+    (4099, 64, torch.bfloat16, None),        # many rows: second-level tree over > 4096 sums
+])
+def test_weight_quant_bit_exact(N, K, dtype, special):
+    print(f"weight_quant N={N} K={K} {dtype} {special}", flush=True)
+    w = _weight_case(N, K, dtype, seed=N * 7 + K, special=special)
+    wp, gamma = bt.bitnet_weight_quant(to_dev(w))
+    torch.cuda.synchronize()
+    c_ref, g_ref = oracle.weight_quant(host(w))
+    assert f32_bits_equal(gamma.cpu().numpy(), np.array([g_ref], np.float32))
+    assert np.array_equal(wp.cpu().numpy(), oracle.pack(c_ref))
+
+
+@pytest.mark.parametrize("j", [25, 31, 41, 47, 97, 127])
+def test_weight_quant_near_tie_matches_division(j):
+    # gamma = j*2^-8 exactly and entries one ulp above gamma/2: the decision
+    # must follow the correctly rounded quotient (oracle), not a reciprocal
+    from test_oracle_pins import near_tie_matrix
+    W, g = near_tie_matrix(j)
+    W = np.tile(W, (4, 2))  # 4 x 16: same mean
+    wp, gamma = bt.bitnet_weight_quant(to_dev(torch.from_numpy(W)))
+    c_ref, g_ref = oracle.weight_quant(W)
+    assert g_ref == g
+    assert f32_bits_equal(gamma.cpu().numpy(), np.array([g_ref], np.float32))
+    assert np.array_equal(wp.cpu().numpy(), oracle.pack(c_ref))
+
+
+def test_weight_quant_exact_half_ties():
+    # every W/gamma is an exact half-integer: round-half-to-even decides
+    from test_oracle_pins import exact_half_tie_matrix
+    _, W = exact_half_tie_matrix()
+    wp, gamma = bt.bitnet_weight_quant(to_dev(torch.from_numpy(W)))
+    c_ref, g_ref = oracle.weight_quant(W)
+    assert f32_bits_equal(gamma.cpu().numpy(), np.array([g_ref], np.float32))
+    assert np.array_equal(wp.cpu().numpy(), oracle.pack(c_ref))
+
+
+@pytest.mark.parametrize("N,K", [(1, 4), (37, 96), (11008, 4096)])
+def test_pack_ternary_matches_oracle(N, K):
+    c = workloads.ternary_codes(N, K, 0.35, seed=N + K)
+    wp = bt.bitnet_pack_ternary(to_dev(c))
+    torch.cuda.synchronize()
+    assert np.array_equal(wp.cpu().numpy(), oracle.pack(c.numpy()))
+
+
+def test_quantizers_are_deterministic():
+    x = _act_case(64, 4096, torch.bfloat16, seed=3)
+    w = _weight_case(512, 4096, torch.float32, seed=4)
+    xd, wd = to_dev(x), to_dev(w)
+    q1, s1 = bt.bitnet_act_quant(xd)
+    q2, s2 = bt.bitnet_act_quant(xd)
+    p1, g1 = bt.bitnet_weight_quant(wd)
+    p2, g2 = bt.bitnet_weight_quant(wd)
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+    assert torch.equal(p1, p2) and torch.equal(g1, g2)

@@ -161,11 +161,13 @@ def test_weight_quant_all_zero():
     assert not c.any()
 
 
-def test_weight_quant_exact_half_ties():
-    # Integer matrix A with sum|A| = 512 scaled by 2^-6 over 256 entries:
-    # gamma = 2^-5 exactly and every W/gamma = A/2 is an exact half-integer,
-    # so round-half-to-even decides: |A| <= 1 -> 0, else sign(A).
-    rng = np.random.default_rng(8)
+def exact_half_tie_matrix(seed: int = 8):
+    """Integer matrix A (8x32, |A| <= 6) with sum|A| = 512, and W = A * 2^-6.
+
+    mean|W| = 512 * 2^-6 / 256 = 2^-5 exactly, so every W/gamma = A/2 is an
+    exact half-integer and round-half-to-even decides each code.
+    """
+    rng = np.random.default_rng(seed)
     A = rng.integers(-6, 7, size=(8, 32)).astype(np.int64)
     deficit = 512 - int(np.abs(A).sum())
     i = 0
@@ -178,7 +180,12 @@ def test_weight_quant_exact_half_ties():
             deficit -= step
         i += 1
     assert np.abs(A).sum() == 512
-    W = (A.astype(np.float64) * 2.0 ** -6).astype(np.float32)
+    return A, (A.astype(np.float64) * 2.0 ** -6).astype(np.float32)
+
+
+def test_weight_quant_exact_half_ties():
+    # |A| <= 1 -> |W/gamma| <= 0.5 -> 0 (0.5 is a tie to even); else sign(A)
+    A, W = exact_half_tie_matrix()
     c, g = oracle.weight_quant(W)
     assert g == np.float32(2.0 ** -5)
     expect = np.where(np.abs(A) <= 1, 0, np.sign(A))
