@@ -1,0 +1,337 @@
+"""Benchmark of the BitLinear hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+RMSNorm + per-token int8 activation quantization, absmean ternary weight
+quantization + packing, the ternary x int8 forward with dequantization,
+and the STE backward (grad_x and grad_W).  Inputs are generated once on the
+host (seeded, see workloads.py), copied to HBM before timing, and every
+output buffer is preallocated, so the timed region is device work only.
+
+Default workload: small_llama (M=8192 tokens, K=512, N=1376: the MLP
+up-projection of the ~15M-parameter LLaMA-shaped model), the forward plus
+STE backward configuration.  Other workloads (--workload) are for
+profiling: tiny, prefill_7b (forward only), decode_7b (packed GEMV only,
+pre-quantized operands, weight copies rotated so every launch streams its
+weights from HBM) and qat_70b_mlp (full step).
+
+Prints ONE JSON line.  `value` is the step's algorithmic operation rate:
+(2MNK int8 forward + 2MNK bf16 grad_x + 2MNK bf16 grad_W) / step time,
+in TOPS (forward-only workloads count 2MNK; decode reports GB/s of the
+bytes the GEMV must move).  `roofline` is the dominant single-kernel call
+of the step, timed with HIP events on the stream it runs on; `kernels`
+breaks the step down per call; `cpu_baseline` is the CPU oracle timed on
+this host (a bounded sample of the same workload).
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import bit_ternary_quantized_amd as bt  # noqa: E402
+import workloads  # noqa: E402
+
+METRIC = "BitLinear fwd int8 TOPS & packed-GEMV GB/s (fraction of MI355X roofline)"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0    # dense int8 MFMA
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="small_llama",
+                    choices=["small_llama", "tiny", "prefill_7b", "decode_7b", "qat_70b_mlp"])
+    ap.add_argument("--decode-m", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events around each ABI call of a step, on the call's stream."""
+
+    def __init__(self, names, steps):
+        self.names = names
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+                   for _ in range(steps)]
+
+    def mark(self, step, i):
+        self.ev[step][i].record(torch.cuda.current_stream())
+
+    def mean_ms(self):
+        out = {}
+        for i, n in enumerate(self.names):
+            out[n] = statistics.fmean(e[i].elapsed_time(e[i + 1]) for e in self.ev)
+        return out
+
+
+# --------------------------------------------------------------- workloads
+
+def setup_layer(name):
+    d = workloads.workload(name)
+    M, N, K = d["M"], d["N"], d["K"]
+    dev = "cuda:0"
+    x, w = d["x"].to(dev), d["w"].to(dev)
+    gy = d["gy"].to(dev) if "gy" in d else None
+    buf = {
+        "Xq": torch.empty(M, K, dtype=torch.int8, device=dev),
+        "scale_x": torch.empty(M, dtype=torch.float32, device=dev),
+        "W_packed": torch.empty(N, K // 4, dtype=torch.uint8, device=dev),
+        "gamma": torch.empty(1, dtype=torch.float32, device=dev),
+        "ws_wq": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, M, N, K),
+                             dtype=torch.uint8, device=dev),
+        "Y": torch.empty(M, N, dtype=torch.float32, device=dev),
+    }
+    if gy is not None:
+        buf["grad_x"] = torch.empty(M, K, dtype=torch.float32, device=dev)
+        buf["grad_W"] = torch.empty(N, K, dtype=torch.float32, device=dev)
+        buf["ws_bwd"] = torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, M, N, K),
+                                    dtype=torch.uint8, device=dev)
+    return d, x, w, gy, buf
+
+
+def layer_counts(M, N, K, x_bytes, w_bytes, gy):
+    """Algorithmic work of each call (bytes moved once, or ops)."""
+    c = {
+        "act_quant": {"bytes": M * K * x_bytes + M * K + 4 * M, "bound": "hbm"},
+        # two reads of W: gamma needs the full reduction before any code exists
+        "weight_quant": {"bytes": 2 * N * K * w_bytes + N * K // 4 + 4, "bound": "hbm"},
+        "linear_fwd": {"ops": 2 * M * N * K, "bytes": M * K + N * K // 4 + 4 * M + 4 * M * N,
+                       "peak_ops": INT8_PEAK_TOPS},
+    }
+    if gy:
+        c["linear_bwd_ste"] = {"ops": 4 * M * N * K,
+                               "bytes": 2 * M * N + M * K + N * K // 4 + 4 * M + 4 * M * K + 4 * N * K,
+                               "peak_ops": BF16_PEAK_TFLOPS}
+    for v in c.values():
+        if "ops" in v:
+            ridge = v["peak_ops"] * 1e12 / (HBM_PEAK_GBS * 1e9)
+            v["bound"] = "mfma" if v["ops"] / v["bytes"] > ridge else "hbm"
+    return c
+
+
+def rate(entry, ms):
+    s = ms * 1e-3
+    if entry["bound"] == "hbm":
+        a = entry["bytes"] / s / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a / HBM_PEAK_GBS}
+    a = entry["ops"] / s / 1e12
+    return {"bound": "mfma", "achieved": a, "peak": entry["peak_ops"], "unit": "TFLOP/s",
+            "frac": a / entry["peak_ops"]}
+
+
+def cpu_baseline_layer(d, gy_present, budget_s=12.0):
+    """The oracle on this host, on the first S tokens of the same layer: act
+    quant of those S rows, weight quant of the whole W (a step needs it
+    whatever the token count), forward and STE backward over the S tokens.
+    S is sized from a short calibration run so that one sample takes about
+    half the budget; the sample repeats until the budget is spent (at most
+    three times) and the median counts.  Rate = the GPU's algorithmic ops
+    for S tokens / seconds."""
+    import oracle
+    M, N, K = d["M"], d["N"], d["K"]
+    xh = workloads.host_array(d["x"])
+    wh = workloads.host_array(d["w"])
+    gyh = workloads.host_array(d["gy"]) if gy_present else None
+
+    def run(S):
+        t0 = time.perf_counter()
+        q, s = oracle.act_quant(xh[:S])
+        c, g = oracle.weight_quant(wh)
+        oracle.gemm_i32(q, c)
+        if gyh is not None:
+            oracle.ste_grad_x(gyh[:S], c, g)
+            oracle.ste_grad_w(gyh[:S], q, s)
+        return time.perf_counter() - t0
+
+    S = min(M, 64)
+    t = run(S)
+    S = int(max(1, min(M, S * (budget_s / 2) / max(t, 1e-9))))
+    times = []
+    t_start = time.perf_counter()
+    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 3):
+        times.append(run(S))
+    ops = (2 + (4 if gy_present else 0)) * S * N * K
+    sec = statistics.median(times)
+    return {"value": ops / sec / 1e12, "unit": "TOPS", "cores": oracle.get_threads(), "kind": "oracle",
+            "sample": f"first {S} of {M} tokens: act quant of those rows, weight quant of all of W, "
+                      f"forward{' and STE backward' if gy_present else ''}; median of {len(times)} run(s) "
+                      f"of {sec:.2f} s",
+            "seconds": sec}
+
+
+def capture(fn):
+    """Capture the kernels one call enqueues into a HIP graph (torch stream
+    capture; the library launches on the current stream and allocates
+    nothing when every buffer is passed in)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # one eager run on the capture stream before capturing
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+SLEEP_CYCLES = 50_000_000  # bounded spin that lets the host enqueue ahead
+REPS = 8                   # launches of one call per timed graph
+
+
+def bench_layer(args, name):
+    d, x, w, gy, b = setup_layer(name)
+    M, N, K = d["M"], d["N"], d["K"]
+    calls = {
+        "act_quant": lambda: bt.bitnet_act_quant(x, 1e-5, Xq=b["Xq"], scale_x=b["scale_x"]),
+        "weight_quant": lambda: bt.bitnet_weight_quant(w, W_packed=b["W_packed"], gamma=b["gamma"],
+                                                       workspace=b["ws_wq"]),
+        "linear_fwd": lambda: bt.bitnet_linear_fwd(b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], Y=b["Y"]),
+    }
+    if gy is not None:
+        calls["linear_bwd_ste"] = lambda: bt.bitnet_linear_bwd_ste(
+            gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], grad_x=b["grad_x"], grad_W=b["grad_W"],
+            workspace=b["ws_bwd"])
+    names = list(calls)
+
+    def step():
+        for n in names:
+            calls[n]()
+
+    g_step = capture(step)
+    for _ in range(args.warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, one graph launch each
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        g_step.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    dev_ms = start.elapsed_time(end) / args.steps
+
+    # per-call device time: each call captured REPS times back to back in
+    # one graph; K replays of each, bracketed by HIP events on the stream
+    # they run on.  A bounded spin first lets the host enqueue the whole loop,
+    # so no host gap sits between two events.
+    g_rep = {n: capture(lambda n=n: [calls[n]() for _ in range(REPS)]) for n in names}
+    timer = Timer(names, args.steps)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SLEEP_CYCLES)
+    for i in range(args.steps):
+        for j, n in enumerate(names):
+            timer.mark(i, j)
+            g_rep[n].replay()
+        timer.mark(i, len(names))
+    torch.cuda.synchronize()
+    per = {n: v / REPS for n, v in timer.mean_ms().items()}
+
+    counts = layer_counts(M, N, K, d["x"].element_size(), d["w"].element_size(), gy is not None)
+    kernels = {n: {"ms": per[n], **rate(counts[n], per[n])} for n in names}
+    fwd_bwd = 2 + (4 if gy is not None else 0)
+    value = fwd_bwd * M * N * K / (ms * 1e-3) / 1e12
+    # the forward GEMM is the step's single-kernel hot call; the backward
+    # call launches several kernels and is reported in `kernels`
+    dom = "linear_fwd"
+    roof = dict(rate(counts[dom], per[dom]))
+    roof["kernel"] = "gemm_i8t2_kernel (bitnet_linear_fwd)"
+    roof["traffic"] = None
+    out = {
+        "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "device_ms_per_step": dev_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8+bf16" if gy is not None else "i8",
+        "data": "synthetic",
+        "config": {"workload": name, "M": M, "N": N, "K": K, "x_dtype": str(d["x"].dtype).split(".")[-1],
+                   "w_dtype": str(d["w"].dtype).split(".")[-1],
+                   "step": "+".join(names), "launch": "one HIP graph per step"},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_layer(d, gy is not None)
+    return out
+
+
+def bench_decode(args):
+    """Packed GEMV at decode shape; weights rotated over enough copies that
+    every launch reads its 2-bit weights from HBM, not the 256 MB cache."""
+    M = args.decode_m
+    d = workloads.workload("decode_7b", M=M)
+    N, K = d["N"], d["K"]
+    dev = "cuda:0"
+    q, s, gm = d["q"].to(dev), d["scale_x"].to(dev), d["gamma"].to(dev)
+    wp0 = bt.bitnet_pack_ternary(d["codes"].to(dev))
+    copies = max(2, (512 << 20) // wp0.numel() + 1)  # > 2x the Infinity Cache
+    wps = [wp0] + [wp0.clone() for _ in range(copies - 1)]
+    Y = torch.empty(M, N, dtype=torch.float32, device=dev)
+    # one graph = one launch per weight copy, back to back; each replay
+    # streams every copy once
+    g = capture(lambda: [bt.bitnet_linear_fwd(q, s, wp, gm, Y=Y) for wp in wps])
+    for _ in range(max(1, args.warmup // copies)):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // copies)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda._sleep(SLEEP_CYCLES)
+    t0 = time.perf_counter()
+    for i in range(reps):
+        ev[i].record()
+        g.replay()
+    ev[-1].record()
+    torch.cuda.synchronize()
+    ms = statistics.fmean(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / copies
+    nbytes = N * K // 4 + M * K + 4 * M + 4 + 4 * M * N
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": "decode_7b", "M": M, "N": N, "K": K, "weight_copies": copies,
+                   "launches_timed": reps * copies},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "gemv_t2_kernel"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        qh, ch = d["q"].numpy(), d["codes"].numpy()
+        t = time.perf_counter()
+        oracle.gemm_i32(qh, ch)
+        sec = time.perf_counter() - t
+        out["cpu_baseline"] = {"value": nbytes / sec / 1e9, "unit": "GB/s", "cores": oracle.get_threads(),
+                               "kind": "oracle", "sample": f"whole GEMV (M={M}) once, {sec:.2f} s"}
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    bt.load_library()
+    if args.workload == "decode_7b":
+        out = bench_decode(args)
+    else:
+        out = bench_layer(args, args.workload)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

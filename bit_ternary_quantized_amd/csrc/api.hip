@@ -78,7 +78,7 @@ int bitnet_linear_fwd(const int8_t* Xq, const float* scale_x, const uint8_t* W_p
     if (!aligned16(Xq) || !aligned16(W_packed) || !aligned16(Y) || !aligned4(scale_x) ||
         !aligned4(gamma) || (acc && !aligned16(acc)))
         return BITNET_E_ALIGN;
-    if (M <= bitnet::kGemvMaxM && K <= 16384)
+    if (bitnet::gemv_supported(M, K))
         return hip_status(bitnet::launch_gemv_t2(Xq, scale_x, W_packed, gamma, M, N, K, Y, acc,
                                                  as_stream(stream)));
     return hip_status(bitnet::launch_gemm_i8t2(Xq, scale_x, W_packed, gamma, M, N, K, Y, acc,
@@ -97,8 +97,9 @@ int bitnet_linear_bwd_ste(const void* grad_y, int gy_dtype, const int8_t* Xq, co
     if (!aligned16(grad_y) || !aligned16(Xq) || !aligned16(W_packed) || !aligned4(scale_x) ||
         !aligned4(gamma) || (grad_x && !aligned16(grad_x)) || (grad_W && !aligned16(grad_W)))
         return BITNET_E_ALIGN;
-    if (!workspace || workspace_bytes < bitnet::bwd_ws_bytes(M, N, K)) return BITNET_E_WORKSPACE;
-    if (!aligned16(workspace)) return BITNET_E_ALIGN;
+    const size_t need = grad_W ? bitnet::bwd_ws_bytes(M, N, K) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return BITNET_E_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return BITNET_E_ALIGN;
     return hip_status(bitnet::launch_bwd_ste(static_cast<const uint16_t*>(grad_y), Xq, scale_x,
                                              W_packed, gamma, M, N, K, grad_x,
                                              gx_dtype == BITNET_BF16, grad_W, workspace,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace bitnet {
 
 constexpr int kWave = 64;  // CDNA wavefront width
@@ -162,6 +164,7 @@ hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t*
                           const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
                           int32_t* acc, hipStream_t s);
 constexpr int64_t kGemvMaxM = 16;
+bool gemv_supported(int64_t M, int64_t K);  // M <= 16 and the activations fit LDS
 hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* scale_x,
                           const uint8_t* Wp, const float* gamma, int64_t M, int64_t N, int64_t K,
                           void* grad_x, bool gx_bf16, float* grad_W, void* ws, hipStream_t s);

@@ -6,119 +6,158 @@
 // Decode is bound by streaming the 2-bit weights from HBM once (the memory
 // wall of "1.58-bit量化技术突破AI算力与内存墙限制", section 1); the
 // add / subtract / skip of its 3.1 is computed as an exact int8 dot product.
-// Unpacking codes costs VALU work per weight regardless of M, so the
-// products run on v_mfma_i32_16x16x64_i8 with the tokens padded to 16: the
-// matrix-core time is then independent of M as well.
+// Unpacking codes costs VALU work per weight whatever M is, so the products
+// run on v_mfma_i32_16x16x64_i8 with the tokens padded to 16 and the
+// matrix-core time is independent of M as well.
 //
-// One 256-thread workgroup owns 16 weight rows; its 4 waves split K into
-// quarters.  Inside a wave, lane group g = lane/16 owns a contiguous quarter
-// of the wave's K range, and MFMA step s takes the s-th 16-column chunk of
-// every group's range, so each lane streams one contiguous run of packed
-// bytes of its weight row (the sum over k is order-free, and activations are
-// gathered with the same mapping).  Partial int32 tiles meet in LDS.
+// Data flow.  One 1024-thread workgroup per CU (16 waves).  Weight rows come
+// in groups of 16 (one MFMA N block); workgroup w owns groups w, w+G, ...
+// Every packed weight byte the workgroup needs is requested first, with no
+// branch in front of the loads, so the whole matrix is in flight at once.
+// The activations (16 x K int8, tokens >= M zero) are staged once in LDS,
+// each 16-byte chunk byte-transposed 4 x 4 to match the column order
+// unpack16 produces.  The 16 waves split K: wave v owns columns
+// [v*Kw, (v+1)*Kw), its lane group g = lane/16 the contiguous quarter
+// [v*Kw + g*Kw/4, ...), and MFMA step s the s-th 16-column chunk of every
+// quarter (the sum over k is exact and order-free).  The 16 partial int32
+// tiles meet in LDS.
 #include "common.h"
 
 namespace bitnet {
 
 namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
-constexpr int kRows = 16;    // weight rows per workgroup (MFMA N)
-constexpr int kWaves = 4;    // K split
-constexpr int kMaxSteps = 64;  // MFMA steps per wave handled by the template
+constexpr int kWaves = 16;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxKLds = 8192;            // activation tile K bound (LDS)
+constexpr int kAStride = kMaxKLds + 16;   // bytes per token row in LDS (+pad)
+constexpr int kMaxGroups = 8;             // row groups prefetched per pass
 }  // namespace
 
-// STEPS: MFMA k-steps (64 columns each) per wave; lane group range = 16*STEPS.
-template <int STEPS>
-__global__ __launch_bounds__(kWaves * 64) void gemv_t2_kernel(
+// S: MFMA steps (64 columns) per wave, Kw = 64*S; FULL: K == 16*Kw, so every
+// lane's column range lies inside the row and loads are 16-byte vectors.
+template <int S, bool FULL>
+__global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ scale_x,
     const uint8_t* __restrict__ Wp, const float* __restrict__ gamma_p, int M, int N, int K,
     float* __restrict__ Y, int32_t* __restrict__ acc_out) {
-    __shared__ int red[kWaves][kRows * 16];
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int n0 = blockIdx.x * kRows;
-    const int col = lane & 15;  // weight row inside the tile / token for A
-    const int g = lane >> 4;    // lane group
-    constexpr int GR = 16 * STEPS;                     // columns per lane group
-    const int kbase = wave * (4 * GR) + g * GR;        // first column of this lane
+    __shared__ __align__(16) uint8_t As[16 * kAStride];
+    __shared__ int red[kWaves][256];
+    constexpr int Kw = 64 * S;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int kb = wave * Kw + g * (Kw / 4);  // first column of this lane
     const int KB = K / 4;
-    const bool vec = (KB % 16) == 0;  // packed rows 16-byte aligned
+    const int ngroups = (N + 15) / 16;
 
-    // weights: row n0+col, columns [kbase, kbase + GR): GR/4 packed bytes
-    uint32_t wq[STEPS];
-    {
-        const int n = n0 + col;
-        const uint8_t* src = Wp + (int64_t)n * KB + kbase / 4;
+    for (int base = blockIdx.x; base < ngroups; base += gridDim.x * kMaxGroups) {
+        // ---- weights for up to kMaxGroups row groups, all loads first
+        uint32_t wq[kMaxGroups][S];
 #pragma unroll
-        for (int s = 0; s < STEPS; s += 4) {
-            // 16 bytes = 4 steps when fully inside the row
-            if (vec && n < N && kbase + 16 * (s + 4) <= K) {
-                const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * s);
-                wq[s] = v.x; wq[s + 1] = v.y; wq[s + 2] = v.z; wq[s + 3] = v.w;
+        for (int r = 0; r < kMaxGroups; ++r) {
+            const int grp = base + r * gridDim.x;
+            const int n = grp * 16 + col;
+            const bool nv = grp < ngroups && n < N;
+            const int nc = nv ? n : 0;  // clamped address, value dropped below
+            const uint8_t* src = Wp + (int64_t)nc * KB + kb / 4;
+            if constexpr (FULL && S % 4 == 0) {
+#pragma unroll
+                for (int s = 0; s < S; s += 4) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * s);
+                    wq[r][s] = nv ? v.x : 0u;
+                    wq[r][s + 1] = nv ? v.y : 0u;
+                    wq[r][s + 2] = nv ? v.z : 0u;
+                    wq[r][s + 3] = nv ? v.w : 0u;
+                }
             } else {
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    wq[s + u] = (n < N && kbase + 16 * (s + u) < K)
-                                    ? *reinterpret_cast<const uint32_t*>(src + 4 * (s + u))
-                                    : 0u;
+                for (int s = 0; s < S; ++s) {
+                    const bool kv = kb + 16 * s < K;
+                    const uint32_t v = *reinterpret_cast<const uint32_t*>(
+                        Wp + (int64_t)nc * KB + (kv ? (kb + 16 * s) / 4 : 0));
+                    wq[r][s] = (nv && kv) ? v : 0u;
+                }
             }
         }
-    }
 
-    v4i acc = {0, 0, 0, 0};
-    const int tok = col;
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        const int k = kbase + 16 * s;
-        uint32_t a4[4] = {0u, 0u, 0u, 0u};
-        if (tok < M && k < K) {
-            const uint4 v = *reinterpret_cast<const uint4*>(Xq + (int64_t)tok * K + k);
-            a4[0] = v.x; a4[1] = v.y; a4[2] = v.z; a4[3] = v.w;
+        // ---- activations -> LDS (first pass only; they do not change)
+        if (base == (int)blockIdx.x) {
+            const int kch = K / 16;  // 16-byte chunks per token row
+            for (int c = t; c < 16 * kch; c += kThreads) {
+                const int tok = c / kch, kc = c - tok * kch;
+                const bool tv = tok < M;
+                const uint4 v = *reinterpret_cast<const uint4*>(Xq + (int64_t)(tv ? tok : 0) * K + 16 * kc);
+                const uint32_t a[4] = {tv ? v.x : 0u, tv ? v.y : 0u, tv ? v.z : 0u, tv ? v.w : 0u};
+                uint32_t o[4];
+                transpose4x4_bytes(a, o);
+                *reinterpret_cast<uint4*>(As + tok * kAStride + 16 * kc) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+            __syncthreads();
         }
-        uint32_t at[4], b[4];
-        transpose4x4_bytes(a4, at);
-        unpack16(wq[s], b);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-            v4i{(int)at[0], (int)at[1], (int)at[2], (int)at[3]},
-            v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]}, acc, 0, 0, 0);
-    }
-    // 16x16 output layout: lane holds column lane%16 (weight row) and rows
-    // (tokens) 4*(lane/16) + r.
+
+        // ---- products, one row group at a time
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][(4 * g + r) * 16 + col] = acc[r];
-    __syncthreads();
-    {
-        const int tk = t >> 4, nn = t & 15;  // 256 threads = 16 tokens x 16 rows
-        const int sum = red[0][t] + red[1][t] + red[2][t] + red[3][t];
-        if (tk < M && n0 + nn < N) {
-            const float rs = *gamma_p / scale_x[tk];
-            Y[(int64_t)tk * N + n0 + nn] = (float)sum * rs;
-            if (acc_out) acc_out[(int64_t)tk * N + n0 + nn] = sum;
+        for (int r = 0; r < kMaxGroups; ++r) {
+            const int grp = base + r * gridDim.x;
+            if (grp >= ngroups) break;  // uniform over the workgroup
+            v4i acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int k = kb + 16 * s;
+                uint4 av = make_uint4(0, 0, 0, 0);
+                if (FULL || k < K) av = *reinterpret_cast<const uint4*>(As + col * kAStride + k);
+                uint32_t b[4];
+                unpack16(wq[r][s], b);
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                    v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w},
+                    v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]}, acc, 0, 0, 0);
+            }
+            // 16x16 layout: lane holds weight row lane%16, tokens 4*(lane/16)+i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][(4 * g + i) * 16 + col] = acc[i];
+            __syncthreads();
+            if (t < 256) {
+                const int tk = t >> 4, nn = grp * 16 + (t & 15);
+                int sum = 0;
+#pragma unroll
+                for (int v = 0; v < kWaves; ++v) sum += red[v][t];
+                if (tk < M && nn < N) {
+                    const float rs = *gamma_p / scale_x[tk];
+                    Y[(int64_t)tk * N + nn] = (float)sum * rs;
+                    if (acc_out) acc_out[(int64_t)tk * N + nn] = sum;
+                }
+            }
+            __syncthreads();
         }
     }
 }
 
+bool gemv_supported(int64_t M, int64_t K) { return M <= kGemvMaxM && K <= kMaxKLds; }
+
 hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t* Wp,
                           const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
                           int32_t* acc, hipStream_t s) {
-    // steps per wave: K / (4 waves * 4 groups * 16 columns), rounded up to 4
-    int64_t steps = (K + 255) / 256;
-    steps = (steps + 3) / 4 * 4;
-    const dim3 grid((unsigned)((N + kRows - 1) / kRows)), block(kWaves * 64);
-#define BITNET_GEMV_CASE(S)                                                                    \
-    if (steps <= S) {                                                                          \
-        gemv_t2_kernel<S><<<grid, block, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N,       \
-                                                 (int)K, Y, acc);                              \
+    if (!gemv_supported(M, K)) return hipErrorInvalidValue;
+    const int64_t ngroups = (N + 15) / 16;
+    const unsigned grid = (unsigned)std::min<int64_t>(ngroups, 256);
+    const int64_t steps = (K + 16 * 64 - 1) / (16 * 64);  // MFMA steps per wave
+    const bool full = K % (16 * 64) == 0;
+#define BITNET_GEMV_CASE(S_)                                                                   \
+    if (steps <= S_) {                                                                         \
+        if (full && steps == S_)                                                               \
+            gemv_t2_kernel<S_, true><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, \
+                                                              (int)N, (int)K, Y, acc);         \
+        else                                                                                   \
+            gemv_t2_kernel<S_, false><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M,\
+                                                               (int)N, (int)K, Y, acc);        \
         return hipGetLastError();                                                              \
     }
+    BITNET_GEMV_CASE(1)
+    BITNET_GEMV_CASE(2)
     BITNET_GEMV_CASE(4)
     BITNET_GEMV_CASE(8)
-    BITNET_GEMV_CASE(16)
-    BITNET_GEMV_CASE(32)
-    BITNET_GEMV_CASE(64)
 #undef BITNET_GEMV_CASE
-    (void)kMaxSteps;
-    return hipErrorInvalidValue;  // K beyond 16384: the ABI routes it to the GEMM
+    return hipErrorInvalidValue;
 }
 
 }  // namespace bitnet

@@ -117,8 +117,8 @@ int bitnet_act_quant(const void *X, int x_dtype, int64_t M, int64_t K, float eps
  * (wide accumulator), [WALL 3.1] (+1 adds, -1 subtracts, 0 skips):
  *   acc[m][n] = sum_k Xq[m][k] * code[n][k]      (exact int32)
  *   Y[m][n]   = acc[m][n] * gamma / scale_x[m]   (fp32)
- * M <= 16 takes the bandwidth-bound packed GEMV, larger M the int8 MFMA
- * GEMM.
+ * M <= 16 (with K <= 8192) takes the bandwidth-bound packed GEMV, other
+ * shapes the int8 MFMA GEMM.
  *   Xq       [M][K] int8;  scale_x [M] fp32;  W_packed [N][K/4];  gamma 1 fp32
  *   Y        [M][N] fp32, written
  *   acc      [M][N] int32, written when non-NULL (for exact checks)
@@ -144,8 +144,10 @@ int bitnet_linear_fwd(const int8_t *Xq, const float *scale_x, const uint8_t *W_p
  *   grad_x  [M][K] fp32 or bf16 (gx_dtype), written when non-NULL
  *   grad_W  [N][K] fp32, written when non-NULL
  *   workspace >= bitnet_workspace_bytes(BITNET_OP_LINEAR_BWD_STE, M, N, K)
- *            device scratch: bf16 copies of codes^T, grad_y^T and X_deq^T
- *            (2*(K*N + N*M + K*M) bytes); contents on entry ignored.
+ *            device scratch for fp32 partial tiles of grad_W when its
+ *            output is too small to fill the GPU and the token range is
+ *            split (splits*N*K*4 bytes; 0 otherwise, then NULL is allowed);
+ *            contents on entry ignored.
  * K % 16 == 0.
  * Errors: BITNET_E_ARG (both outputs NULL), BITNET_E_SHAPE, BITNET_E_DTYPE,
  * BITNET_E_ALIGN, BITNET_E_WORKSPACE, BITNET_E_HIP.

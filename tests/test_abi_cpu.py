@@ -51,9 +51,11 @@ def test_workspace_sizes():
     assert bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_FWD, 8, 8, 16) == 0
     wq = bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, 0, 28672, 8192)
     assert wq >= 28672 * 4 + 4 and wq % 256 == 0
-    M, N, K = 4096, 28672, 8192
-    bw = bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, M, N, K)
-    assert bw >= 2 * (K * N + N * M + K * M)
+    # grad_W of a large layer fills the GPU without splitting its tokens
+    assert bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, 4096, 28672, 8192) == 0
+    # a small one (N*K = 1376*512) splits 8192 tokens: fp32 partial tiles
+    bw = bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, 8192, 1376, 512)
+    assert bw >= 2 * 1376 * 512 * 4 and bw % 256 == 0
     assert bt.bitnet_workspace_bytes(7, 1, 1, 4) == 0
     assert bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, -1, 4, 4) == 0
 
@@ -97,7 +99,9 @@ def test_linear_bwd_rejects_bad_arguments():
     assert lib.bitnet_linear_bwd_ste(P, 0, P, P, P, P, 4, 4, 16, P, 0, P, P, ws, NULL) == -3   # fp32 gy
     assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 4, 4, 16, P, 5, P, P, ws, NULL) == -3
     assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 4, 4, 12, P, 0, P, P, ws, NULL) == -2
-    assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 4, 4, 16, P, 0, P, P, 64, NULL) == -5
+    ws_need = bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, 8192, 1376, 512)
+    assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 8192, 1376, 512, P, 0, P, P, ws_need - 256, NULL) == -5
+    assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 8192, 1376, 512, P, 0, P, NULL, ws_need, NULL) == -5
 
 
 def test_pack_rejects_bad_arguments():
