@@ -13,11 +13,12 @@
 // rounded to bf16 once (Xq times the correctly rounded 1/scale_x).
 //
 // Each matrix-core operand wants its contraction index contiguous per lane.
-// grad_x reads gy rows as they are; the codes are unpacked from 2 bits
-// straight into a [k][n] LDS tile (pairs of rows n, n+1 per 32-bit write).
-// grad_W contracts over tokens, so both its tiles are transposed on the way
-// into LDS ([n][m] from gy rows, [k][m] from Xq rows, pairs of tokens per
-// write).  No operand is copied through HBM.
+// grad_x reads gy rows as they are; the codes are unpacked from 2 bits into
+// a natural [n][k] LDS tile.  grad_W contracts over tokens, so both of its
+// tiles ([m][n] from gy, [m][k] from Xq) are natural too.  Tiles stored with
+// the contraction index as their row are read transposed by gfx950's
+// ds_read_b64_tr_b16, so every LDS write is a 16-byte store.  No operand is
+// copied through HBM.
 //
 // Tiles are 256 x 256 (512 threads, 2 x 4 waves of 128 x 64) when the output
 // has enough of them, else 128 x 128 (256 threads, 2 x 2 waves of 64 x 64);
@@ -31,24 +32,53 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-constexpr int BK = 32;       // contraction per step (bf16)
-constexpr int STRIDE = 80;   // LDS bytes per tile row: 64 data + 16 pad
+constexpr int BK = 64;  // contraction per step: 4 MFMA sub-steps of 16
 
-// 16-byte chunk c of tile row r, XOR-swizzled by bits [S, S+2) of the row so
-// that 32-bit writes to rows 8 (S = 3) or 16 (S = 4) apart use distinct banks;
-// consecutive rows stay conflict-free for 16-byte reads through the pad.
-template <int S>
-__device__ __forceinline__ int chunk_off(int r, int c) {
-    return r * STRIDE + ((c ^ ((r >> S) & 3)) << 4);
+// LDS tiles come in two layouts.
+//  "rows": one row per output index, its 64 contraction values contiguous
+//          (128 B + 16 pad); MFMA operands are plain 16-byte reads.
+//  "cols": one row per contraction index, the output indices contiguous
+//          (pitch = 2*width + 64 B, i.e. 64 B mod 256, so that the transposing
+//          reads below hit 64 distinct banks); written with 16-byte stores
+//          straight from the source rows, read transposed with
+//          ds_read_b64_tr_b16.
+constexpr int ROWS_STRIDE = 144;
+template <int W>
+constexpr int cols_pitch() { return 2 * W + 64; }
+
+// Transposing read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane group,
+// lane j supplies the address of 4 consecutive bf16; output lane 4a+b then
+// holds element b of the chunks of lanes a, 4+a, 8+a, 12+a.  So if lane
+// j = 4e + a points at contraction row c0+e, columns x0+4a..x0+4a+3, output
+// lane i holds column x0+i at rows c0..c0+3.
+__device__ __forceinline__ v4s lds_read_tr16(const uint8_t* tile, int byte_off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s*)((__attribute__((address_space(3))) const char*)tile + byte_off));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    v2bf v;
-    v[0] = (__bf16)lo;
-    v[1] = (__bf16)hi;
-    return __builtin_bit_cast(uint32_t, v);
+// Matrix-core operand (8 contraction values for output index x0 + lane%32)
+// from a "cols" tile: two transposing reads give contraction rows
+// c0 + 8*(lane/32) + 0..3 and + 4..7.
+template <int PITCH>
+__device__ __forceinline__ v8bf cols_operand(const uint8_t* tile, int c0, int x0, int lane) {
+    const int G = lane >> 4, j = lane & 15, e = j >> 2, a = j & 3;
+    const int row = c0 + 8 * (G >> 1) + e, col = x0 + 16 * (G & 1) + 4 * a;
+    const v4s lo = lds_read_tr16(tile, row * PITCH + 2 * col);
+    const v4s hi = lds_read_tr16(tile, (row + 4) * PITCH + 2 * col);
+    v8bf r;
+    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
+    r = __builtin_bit_cast(v8bf, make_uint4(l.x, l.y, h.x, h.y));
+    return r;
+}
+
+// Matrix-core operand from a "rows" tile: contraction values
+// c0 + 8*(lane/32) + 0..7 of output row x0 + lane%32.
+__device__ __forceinline__ v8bf rows_operand(const uint8_t* tile, int c0, int x0, int lane) {
+    return *reinterpret_cast<const v8bf*>(tile + (x0 + (lane & 31)) * ROWS_STRIDE +
+                                          2 * (c0 + 8 * (lane >> 5)));
 }
 
 template <int BM>
@@ -60,7 +90,7 @@ struct Cfg {
     static constexpr int WAVES_N = BM == 256 ? 4 : 2;
     static constexpr int WTM = BM / 2, WTN = BN / WAVES_N;
     static constexpr int IM = WTM / 32, JN = WTN / 32;
-    static constexpr int TILE = BM * STRIDE;  // A and B tiles have equal rows here
+    static constexpr int MFMAS = IM * JN * 4;  // per wave and step
 };
 
 // Workgroup id -> (tile m, tile n, split), regrouped so that each XCD (ids
@@ -77,27 +107,15 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int sp
     tn = id % tiles_n;
 }
 
-// One 32-deep step of the wave's MFMA blocks from the LDS tiles.
-template <int BM, int BN, int SA, int SB>
-__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs,
-                                         v16f (&acc)[Cfg<BM, BN>::IM][Cfg<BM, BN>::JN], int wm,
-                                         int wn, int lane) {
-    using C = Cfg<BM, BN>;
-    const int g = lane >> 5, l32 = lane & 31;
+// Interleave hint for one step: each MFMA followed by a few VALU and LDS ops.
+template <int N_MFMA>
+__device__ __forceinline__ void interleave_hint() {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-        v8bf a[C::IM], b[C::JN];
-#pragma unroll
-        for (int i = 0; i < C::IM; ++i)
-            a[i] = *reinterpret_cast<const v8bf*>(As + chunk_off<SA>(wm * C::WTM + i * 32 + l32, 2 * g + kh));
-#pragma unroll
-        for (int j = 0; j < C::JN; ++j)
-            b[j] = *reinterpret_cast<const v8bf*>(Bs + chunk_off<SB>(wn * C::WTN + j * 32 + l32, 2 * g + kh));
-#pragma unroll
-        for (int i = 0; i < C::IM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::JN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < N_MFMA; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // up to two LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // up to one LDS write
     }
 }
 
@@ -118,17 +136,62 @@ __device__ __forceinline__ void for_each_out(const v16f (&acc)[Cfg<BM, BN>::IM][
                   acc[i][j][r]);
 }
 
+// 8 bf16 of row `r` from column `c` (zero past `cols` or past `rows`);
+// branch-free: out-of-range reads go to a clamped, valid address.
+__device__ __forceinline__ uint4 load8_bf16(const uint16_t* P, int rows, int cols, int r, int c,
+                                            bool vec) {
+    const bool rv = r < rows;
+    const uint16_t* p = P + (int64_t)(rv ? r : 0) * cols;
+    if (vec) {
+        const bool v = rv && c < cols;
+        const uint4 x = *reinterpret_cast<const uint4*>(p + (v ? c : 0));
+        return v ? x : make_uint4(0, 0, 0, 0);
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bool v0 = rv && c + 2 * e < cols, v1 = rv && c + 2 * e + 1 < cols;
+        const uint32_t lo = p[v0 ? c + 2 * e : 0], hi = p[v1 ? c + 2 * e + 1 : 0];
+        w[e] = (v0 ? lo : 0u) | ((v1 ? hi : 0u) << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// 16 ternary codes (one packed dword, columns k..k+15) -> 16 bf16 in natural
+// column order (8 dwords, two codes each).  bf16 of a code: low byte 0x80 if
+// nonzero, high byte 0x3f (+1) or 0xbf (-1).
+__device__ __forceinline__ void codes16_to_bf16(uint32_t w, uint32_t (&o)[8]) {
+    constexpr uint32_t kHi = 0x00bf3f00u, kLo = 0x00808000u;
+    const uint32_t ev = w & 0x33333333u;          // codes 0,2 of every byte (bits 0-1, 4-5)
+    const uint32_t od = (w >> 2) & 0x33333333u;   // codes 1,3 of every byte
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        // [ev.b, ev.b, od.b, od.b]: codes 4b (low nibble) and 4b+1, then 4b+2 and 4b+3 (high)
+        const uint32_t pb = __builtin_amdgcn_perm(od, ev, (uint32_t)(b | b << 8 | (b + 4) << 16 | (b + 4) << 24));
+        const uint32_t s0 = (pb & 0x03030303u) + 0x00040004u;
+        const uint32_t s1 = ((pb >> 4) & 0x03030303u) + 0x00040004u;
+        o[2 * b] = __builtin_amdgcn_perm(kLo, kHi, s0);
+        o[2 * b + 1] = __builtin_amdgcn_perm(kLo, kHi, s1);
+    }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ grad_x
 // out[m][k] = gamma * sum_n gy[m][n] * code[n][k]; tile BM (m) x BN (k).
+// A tile ("rows"): gy rows m as they are.  B tile ("cols"): codes of rows n
+// unpacked to bf16 in natural order ([n][k]), read transposed.
 template <int BM, int BN, bool OUT_BF16>
 __global__ __launch_bounds__(kThreadsFor<BM>) void gradx_kernel(
     const uint16_t* __restrict__ gy, const uint8_t* __restrict__ Wp,
     const float* __restrict__ gamma_p, int M, int N, int K, void* __restrict__ out) {
     using C = Cfg<BM, BN>;
-    constexpr int SA = 3, SB = 4;
-    __shared__ __align__(16) uint8_t smem[2][2 * C::TILE];
+    constexpr int A_BYTES = BM * ROWS_STRIDE;
+    constexpr int BP = cols_pitch<BN>();
+    constexpr int B_BYTES = BK * BP;
+    constexpr int kAPer = BM * 8 / C::T;             // 16-byte A chunks per thread
+    constexpr int kBPer = BK * (BN / 16) / C::T;     // 16-code B items per thread
+    __shared__ __align__(16) uint8_t smem[2][A_BYTES + B_BYTES];
     int tm, tn, sp;
     tile_of(blockIdx.x, (M + BM - 1) / BM, (K + BN - 1) / BN, 1, tm, tn, sp);
     const int m0 = tm * BM, k0 = tn * BN;
@@ -137,62 +200,44 @@ __global__ __launch_bounds__(kThreadsFor<BM>) void gradx_kernel(
     const int KB = K / 4;
     const bool vec = (N % 8) == 0;
     const int nsteps = (N + BK - 1) / BK;
+    constexpr int kcN = BN / 16;
 
-    // A: gy rows, 4 chunks of 8 bf16 per row -> 4*BM chunks, 2 per thread.
-    // B: thread t < BN: row pair p = t%16 (n = 2p, 2p+1), 16 codes kc = t/16.
-    uint4 pa[2];
-    uint32_t pb[2];
-    auto load = [&](int st) {
+    struct Stage {
+        uint4 a[kAPer];
+        uint32_t b[kBPer];
+    };
+    auto load = [&](int st, Stage& f) {
         const int n0 = st * BK;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < kAPer; ++u) {
             const int c = t + u * C::T;
-            const int row = c >> 2, ch = c & 3;
-            const int m = m0 + row, n = n0 + ch * 8;
-            pa[u] = make_uint4(0, 0, 0, 0);
-            if (m < M && n < N) {
-                const uint16_t* p = gy + (int64_t)m * N + n;
-                if (vec) {
-                    pa[u] = *reinterpret_cast<const uint4*>(p);
-                } else {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        w[e] = (n + 2 * e < N ? p[2 * e] : 0u) | ((n + 2 * e + 1 < N ? (uint32_t)p[2 * e + 1] : 0u) << 16);
-                    pa[u] = make_uint4(w[0], w[1], w[2], w[3]);
-                }
-            }
+            f.a[u] = load8_bf16(gy, M, N, m0 + c / 8, n0 + 8 * (c % 8), vec);
         }
-        if (t < BN) {
-            const int p = t & 15, kc = t >> 4;
-            const int k = k0 + 16 * kc;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int n = n0 + 2 * p + h;
-                pb[h] = (n < N && k < K) ? *reinterpret_cast<const uint32_t*>(Wp + (int64_t)n * KB + k / 4) : 0u;
-            }
+        for (int u = 0; u < kBPer; ++u) {  // item: row n0 + e / kcN, codes 16*(e % kcN)
+            const int e = t + u * C::T;
+            const int n = n0 + e / kcN, k = k0 + 16 * (e % kcN);
+            const bool v = n < N && k < K;
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(Wp + (int64_t)(v ? n : 0) * KB + (v ? k / 4 : 0));
+            f.b[u] = v ? w : 0u;
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](int buf, const Stage& f) {
         uint8_t* As = smem[buf];
-        uint8_t* Bs = smem[buf] + C::TILE;
+        uint8_t* Bs = smem[buf] + A_BYTES;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < kAPer; ++u) {
             const int c = t + u * C::T;
-            *reinterpret_cast<uint4*>(As + chunk_off<SA>(c >> 2, c & 3)) = pa[u];
+            *reinterpret_cast<uint4*>(As + (c / 8) * ROWS_STRIDE + 16 * (c % 8)) = f.a[u];
         }
-        if (t < BN) {
-            const int p = t & 15, kc = t >> 4;
-            // bf16 of a code: lo byte 0x80 if nonzero, hi byte 0x3f / 0xbf
-            constexpr uint32_t kHi = 0x00bf3f00u, kLo = 0x00808000u;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t c0 = (pb[0] >> (2 * j)) & 3u, c1 = (pb[1] >> (2 * j)) & 3u;
-                const uint32_t sel = (c0 | (c1 << 16)) * 0x101u + 0x00040004u;
-                const uint32_t v = __builtin_amdgcn_perm(kLo, kHi, sel);
-                const int row = 16 * kc + j;
-                *reinterpret_cast<uint32_t*>(Bs + chunk_off<SB>(row, p >> 2) + 4 * (p & 3)) = v;
-            }
+        for (int u = 0; u < kBPer; ++u) {
+            const int e = t + u * C::T;
+            uint32_t o[8];
+            codes16_to_bf16(f.b[u], o);
+            uint4* d = reinterpret_cast<uint4*>(Bs + (e / kcN) * BP + 32 * (e % kcN));
+            d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            d[1] = make_uint4(o[4], o[5], o[6], o[7]);
         }
     };
 
@@ -204,15 +249,36 @@ __global__ __launch_bounds__(kThreadsFor<BM>) void gradx_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    load(0);
-    store(0);
+    // two steps of global loads in flight; past the end of N the loads are
+    // zero-filled from clamped addresses, so the step body has no branch
+    Stage s0, nxt;
+    load(0, s0);
+    load(1, nxt);
+    store(0, s0);
     __syncthreads();
     for (int st = 0; st < nsteps; ++st) {
         const int buf = st & 1;
-        if (st + 1 < nsteps) load(st + 1);
-        mma_step<BM, BN, SA, SB>(smem[buf], smem[buf] + C::TILE, acc, wm, wn, lane);
-        if (st + 1 < nsteps) store(buf ^ 1);
+        Stage cur;
+        load(st + 2, cur);
+        const uint8_t* As = smem[buf];
+        const uint8_t* Bs = smem[buf] + A_BYTES;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v8bf a[C::IM], b[C::JN];
+#pragma unroll
+            for (int i = 0; i < C::IM; ++i) a[i] = rows_operand(As, 16 * q, wm * C::WTM + i * 32, lane);
+#pragma unroll
+            for (int j = 0; j < C::JN; ++j) b[j] = cols_operand<BP>(Bs, 16 * q, wn * C::WTN + j * 32, lane);
+#pragma unroll
+            for (int i = 0; i < C::IM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::JN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        store(buf ^ 1, nxt);
+        interleave_hint<C::MFMAS>();
         __syncthreads();
+        nxt = cur;
     }
 
     const float gam = *gamma_p;
@@ -231,15 +297,20 @@ __global__ __launch_bounds__(kThreadsFor<BM>) void gradx_kernel(
 // ------------------------------------------------------------------ grad_W
 // out[n][k] = sum_m gy[m][n] * X_deq[m][k]; tile BM (n) x BN (k); token range
 // of split sp: [sp*mper, min(M, (sp+1)*mper)).  With splits > 1 the tile goes
-// to part[sp][n][k] (fp32) for the ordered reduction.
+// to part[sp][n][k] (fp32) for the ordered reduction.  Both tiles are "cols"
+// tiles: gy rows m as they are, and Xq rows m converted to bf16(Xq / s[m]);
+// both are read transposed.
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreadsFor<BM>) void gradw_kernel(
     const uint16_t* __restrict__ gy, const int8_t* __restrict__ Xq,
     const float* __restrict__ scale_x, int M, int N, int K, int splits, int mper,
     float* __restrict__ out) {
     using C = Cfg<BM, BN>;
-    constexpr int SA = 3, SB = 3;
-    __shared__ __align__(16) uint8_t smem[2][2 * C::TILE];
+    constexpr int AP = cols_pitch<BM>(), BP = cols_pitch<BN>();
+    constexpr int A_BYTES = BK * AP, B_BYTES = BK * BP;
+    constexpr int kAPer = BK * (BM / 8) / C::T;  // 8-wide gy pieces per thread
+    constexpr int kBPer = BK * (BN / 8) / C::T;  // 8-wide Xq pieces per thread
+    __shared__ __align__(16) uint8_t smem[2][A_BYTES + B_BYTES];
     int tm, tn, sp;
     tile_of(blockIdx.x, (N + BM - 1) / BM, (K + BN - 1) / BN, splits, tm, tn, sp);
     const int n0 = tm * BM, k0 = tn * BN;
@@ -249,62 +320,55 @@ __global__ __launch_bounds__(kThreadsFor<BM>) void gradw_kernel(
     const bool vec = (N % 8) == 0;
     const int nsteps = (mhi - mlo + BK - 1) / BK;
 
-    // thread -> token pair p = t%16 (m = 2p, 2p+1 of the step), chunk t/16:
-    // A: 8 consecutive n of gy rows m, m+1;  B: 8 consecutive k of Xq rows.
-    // Threads t < 2*BM load A; threads t < 2*BN load B (here BM == BN).
-    const int p = t & 15, ch = t >> 4;
-    uint4 ga[2];
-    uint2 qb[2];
-    float rs[2];
-    auto load = [&](int st) {
+    struct Stage {
+        uint4 a[kAPer];
+        uint2 b[kBPer];
+        float rs[kBPer];
+    };
+    auto load = [&](int st, Stage& f) {
         const int mb = mlo + st * BK;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int m = mb + 2 * p + h;
-            const bool mv = m < mhi;
-            const int n = n0 + 8 * ch;
-            ga[h] = make_uint4(0, 0, 0, 0);
-            if (mv && n < N) {
-                const uint16_t* src = gy + (int64_t)m * N + n;
-                if (vec) {
-                    ga[h] = *reinterpret_cast<const uint4*>(src);
-                } else {
-                    uint32_t w[4];
+        for (int u = 0; u < kAPer; ++u) {  // piece: token mb + c / (BM/8), n 8*(c % (BM/8))
+            const int c = t + u * C::T;
+            const int m = mb + c / (BM / 8);
+            f.a[u] = load8_bf16(gy, m < mhi ? M : 0, N, m, n0 + 8 * (c % (BM / 8)), vec);
+        }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        w[e] = (n + 2 * e < N ? src[2 * e] : 0u) |
-                               ((n + 2 * e + 1 < N ? (uint32_t)src[2 * e + 1] : 0u) << 16);
-                    ga[h] = make_uint4(w[0], w[1], w[2], w[3]);
-                }
-            }
-            const int k = k0 + 8 * ch;
-            qb[h] = (mv && k < K) ? *reinterpret_cast<const uint2*>(Xq + (int64_t)m * K + k) : make_uint2(0, 0);
-            rs[h] = mv ? 1.0f / scale_x[m] : 0.0f;
+        for (int u = 0; u < kBPer; ++u) {
+            const int c = t + u * C::T;
+            const int m = mb + c / (BN / 8), k = k0 + 8 * (c % (BN / 8));
+            const bool mv = m < mhi, v = mv && k < K;
+            const uint2 q = *reinterpret_cast<const uint2*>(Xq + (int64_t)(v ? m : 0) * K + (v ? k : 0));
+            f.b[u] = v ? q : make_uint2(0, 0);
+            const float sx = scale_x[mv ? m : 0];
+            f.rs[u] = mv ? 1.0f / sx : 0.0f;
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](int buf, const Stage& f) {
         uint8_t* As = smem[buf];
-        uint8_t* Bs = smem[buf] + C::TILE;
-        const int cp = p >> 2, off = 4 * (p & 3);
-        {   // A: pairs (gy[m][n+i], gy[m+1][n+i]) -> row n+i
-            const uint32_t a0[4] = {ga[0].x, ga[0].y, ga[0].z, ga[0].w};
-            const uint32_t a1[4] = {ga[1].x, ga[1].y, ga[1].z, ga[1].w};
+        uint8_t* Bs = smem[buf] + A_BYTES;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t v = (i & 1) ? __builtin_amdgcn_perm(a1[i >> 1], a0[i >> 1], 0x07060302u)
-                                           : __builtin_amdgcn_perm(a1[i >> 1], a0[i >> 1], 0x05040100u);
-                *reinterpret_cast<uint32_t*>(As + chunk_off<SA>(8 * ch + i, cp) + off) = v;
-            }
+        for (int u = 0; u < kAPer; ++u) {
+            const int c = t + u * C::T;
+            *reinterpret_cast<uint4*>(As + (c / (BM / 8)) * AP + 16 * (c % (BM / 8))) = f.a[u];
         }
-        {   // B: pairs (Xq[m][k+j]/s[m], Xq[m+1][k+j]/s[m+1]) -> row k+j
-            const uint32_t q0[2] = {qb[0].x, qb[0].y};
-            const uint32_t q1[2] = {qb[1].x, qb[1].y};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float f0 = (float)(int8_t)(q0[j >> 2] >> (8 * (j & 3))) * rs[0];
-                const float f1 = (float)(int8_t)(q1[j >> 2] >> (8 * (j & 3))) * rs[1];
-                *reinterpret_cast<uint32_t*>(Bs + chunk_off<SB>(8 * ch + j, cp) + off) = pack_bf16x2(f0, f1);
+        for (int u = 0; u < kBPer; ++u) {
+            const int c = t + u * C::T;
+            const uint32_t q[2] = {f.b[u].x, f.b[u].y};
+            uint32_t o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x0 = (float)(int8_t)(q[j >> 1] >> (16 * (j & 1))) * f.rs[u];
+                const float x1 = (float)(int8_t)(q[j >> 1] >> (16 * (j & 1) + 8)) * f.rs[u];
+                typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+                v2bf pr;
+                pr[0] = (__bf16)x0;
+                pr[1] = (__bf16)x1;
+                o[j] = __builtin_bit_cast(uint32_t, pr);
             }
+            *reinterpret_cast<uint4*>(Bs + (c / (BN / 8)) * BP + 16 * (c % (BN / 8))) =
+                make_uint4(o[0], o[1], o[2], o[3]);
         }
     };
 
@@ -316,17 +380,34 @@ __global__ __launch_bounds__(kThreadsFor<BM>) void gradw_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    if (nsteps > 0) {
-        load(0);
-        store(0);
-    }
+    Stage s0, nxt;
+    load(0, s0);
+    load(1, nxt);
+    store(0, s0);
     __syncthreads();
     for (int st = 0; st < nsteps; ++st) {
         const int buf = st & 1;
-        if (st + 1 < nsteps) load(st + 1);
-        mma_step<BM, BN, SA, SB>(smem[buf], smem[buf] + C::TILE, acc, wm, wn, lane);
-        if (st + 1 < nsteps) store(buf ^ 1);
+        Stage cur;
+        load(st + 2, cur);
+        const uint8_t* As = smem[buf];
+        const uint8_t* Bs = smem[buf] + A_BYTES;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v8bf a[C::IM], b[C::JN];
+#pragma unroll
+            for (int i = 0; i < C::IM; ++i) a[i] = cols_operand<AP>(As, 16 * q, wm * C::WTM + i * 32, lane);
+#pragma unroll
+            for (int j = 0; j < C::JN; ++j) b[j] = cols_operand<BP>(Bs, 16 * q, wn * C::WTN + j * 32, lane);
+#pragma unroll
+            for (int i = 0; i < C::IM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::JN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        store(buf ^ 1, nxt);
+        interleave_hint<C::MFMAS>();
         __syncthreads();
+        nxt = cur;
     }
 
     float* dst = splits > 1 ? out + (int64_t)sp * N * K : out;

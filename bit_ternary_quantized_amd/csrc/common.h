@@ -44,6 +44,31 @@ __device__ __forceinline__ float load_elem(const uint16_t* p, int64_t i) {
     return bf16_bits_to_f32(p[i]);
 }
 
+// ------------------------------------------------------------ buffer loads
+// Raw buffer loads through a resource descriptor (gfx9 layout).  The
+// hardware checks every offset against the descriptor's size: an offset at
+// or past it reads zeros and touches no memory.  Tile loads use this for
+// their tails (offset kBufOOB) instead of a branch or a clamped address, and
+// the loads can neither be predicated away nor moved under a branch by the
+// compiler.  Valid offsets stay below 2^31 (the callers bound their sizes).
+constexpr uint32_t kBufOOB = 0x80000000u;
+constexpr int kBufMaxBytes = 0x7fffffff;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void* base) {
+    // word 3 = 0x00020000: 32-bit data format, no swizzle, no added thread id
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kBufMaxBytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 // ---------------------------------------------------- canonical tree sums
 // The library's summation order: pad to a power of two with +0 and add as a
 // perfect binary tree in index order.  Aligned power-of-two blocks may be

@@ -9,15 +9,27 @@
 // "1.58-bit量化技术突破AI算力与内存墙限制" (3.1), evaluated here as an exact
 // int8 dot product on v_mfma_i32_32x32x32_i8.
 //
-// Tiling: a 256 x 256 output tile per 512-thread workgroup, 8 waves as 2 (M)
-// x 4 (N), each wave 128 x 64 = 4 x 2 MFMA blocks of 32 x 32.  K advances 64
-// per step.  The activation tile (256 x 64 B) is staged in LDS with each
-// 16-byte chunk byte-transposed 4 x 4; the weight tile stays 2-bit packed in
+// Tiling: a 256 x 256 output tile per 512-thread workgroup; 8 waves as
+// 2 (M) x 4 (N), each owning 128 x 64 (4 x 2 MFMA blocks of 32 x 32, 128
+// int32 accumulators).  K advances 64 per step.  Activation chunks are
+// staged in LDS byte-transposed 4 x 4; the weight tile stays 2-bit packed in
 // LDS (256 x 16 B, a quarter of the int8 bytes) and each wave unpacks its
-// operand in registers right before the MFMA (unpack16 yields the same
-// transposed column order, so every product pairs equal columns; the sum over
-// k is exact and order-free).  Two LDS buffers; the next step's global loads
-// are in flight while the current step computes.
+// operands in registers (unpack16 yields the same transposed column order,
+// so every product pairs equal columns; the sum over k is exact and
+// order-free).
+//
+// Schedule: ping-pong of two wave groups.  Waves 0-3 (tile rows 0-127) and
+// waves 4-7 (rows 128-255) put one wave on each SIMD and run the same loop
+// one barrier apart, so on every SIMD one wave issues its 16 MFMAs while the
+// other does its memory phase: write the next tile into LDS, issue the
+// global loads of the tile after it, read and unpack its operands of the
+// current tile into registers.  Each group stages its own activation half
+// and its own copy of the weight tile (double-buffered, 64 KB in all), so
+// the groups share no LDS data and a barrier only orders the phases.  Global
+// loads are buffer loads whose tails (rows past M or N, columns past K) read
+// zeros, so the loop has no branch.
+#include <type_traits>
+
 #include "common.h"
 
 namespace bitnet {
@@ -29,11 +41,28 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 512;
-constexpr int A_STRIDE = 80;  // 64 data bytes + 16 pad: conflict-free b128 reads
-constexpr int B_STRIDE = 24;  // 16 packed bytes + 8 pad: conflict-free b64 reads
-constexpr int A_BYTES = BM * A_STRIDE;
-constexpr int B_BYTES = BN * B_STRIDE;
-constexpr int BUF_BYTES = A_BYTES + B_BYTES;
+constexpr int kGroupThreads = 256;  // one wave group: 4 waves, one per SIMD
+constexpr int HM = BM / 2;          // tile rows per group
+constexpr int JN = 2;               // 32-column blocks per wave
+// Activation tile of one group and step: 128 rows x 64 B.  Weight codes come
+// in blocks of 4 steps: 256 rows x 64 B (4 slices of 16 B = 64 codes), so a
+// row's load is one 64-byte piece taken by 4 adjacent lanes; each step loads
+// a quarter (64 rows) of the block after next.
+constexpr int ROW_BYTES = 64;
+constexpr int A_BYTES = HM * ROW_BYTES;
+constexpr int B_BYTES = BN * ROW_BYTES;
+constexpr int kStepsPerBlock = 4;
+constexpr int kQuarterRows = BN / kStepsPerBlock;
+constexpr int kAPer = HM * (ROW_BYTES / 16) / kGroupThreads;  // 16-byte activation chunks per thread
+// LDS rows are unpadded and XOR-swizzled so that the 16-byte writes of the
+// staging threads and the operand reads of the waves both hit distinct banks
+// in every 16-lane group: 16-byte chunk c of row r sits at slot
+// c ^ ((r >> 2) & 3); inside a weight slice, 8-byte half h at
+// h ^ ((r >> 4) & 1) ^ ((r >> 5) & 1).  The row-bit-5 term keeps the two
+// reads of rows r and r + 32 (which the compiler may merge into one
+// ds_read2_b64) on different banks.
+__device__ __forceinline__ int row_slot(int r, int c) { return r * ROW_BYTES + 16 * (c ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int half_swap(int r) { return ((r >> 4) ^ (r >> 5)) & 1; }
 
 // Workgroup id -> tile, XCD-aware: consecutive ids go round-robin over the
 // 8 XCDs, so ids are regrouped to give each XCD a contiguous run of tiles
@@ -43,31 +72,39 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& t
     const int q = G / 8, r = G % 8;
     const int x = wg % 8, local = wg / 8;
     const int id = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
-    tm = id / tiles_n;
-    tn = id % tiles_n;
+    // uniform values; readfirstlane keeps them (and the addresses built
+    // from them) in scalar registers after the division's VALU expansion
+    tm = __builtin_amdgcn_readfirstlane(id / tiles_n);
+    tn = __builtin_amdgcn_readfirstlane(id % tiles_n);
 }
 
-struct Prefetch {
-    uint4 a[2];      // two 16-byte activation chunks
-    uint32_t b[2];   // two packed weight dwords
+struct Stage {
+    uint4 a[kAPer];  // 16-byte activation chunks of the group's half (tile t)
+    uint4 b;         // one 16-byte weight slice (quarter t + 3), halves in slot order
 };
 
 }  // namespace
 
+// VECB: K % 64 == 0, so a step's 16 bytes of a packed weight row are all in
+// or all out of range (else dword granularity).
+template <bool VECB>
 __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ scale_x,
     const uint8_t* __restrict__ Wp, const float* __restrict__ gamma_p, int M, int N, int K,
     float* __restrict__ Y, int32_t* __restrict__ acc_out) {
-    __shared__ __align__(16) uint8_t smem[2 * BUF_BYTES];
+    __shared__ __align__(16) uint8_t smem_a[2][2][A_BYTES];  // [group][buffer]
+    __shared__ __align__(16) uint8_t smem_b[2][2][B_BYTES];  // [group][block buffer]
     __shared__ float row_scale[BM];
 
     int tm, tn;
     tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves
-    const int KB = K / 4;                     // packed bytes per weight row
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform in the wave
+    const int wm = wave >> 2, wn = wave & 3;                   // wm: the wave group
+    const int tg = t & (kGroupThreads - 1);                    // thread inside the group
+    const int KB = K / 4;                                      // packed bytes per weight row
     const int nk = (K + BK - 1) / BK;
 
     {
@@ -75,105 +112,230 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
         if (t < BM) row_scale[t] = (m0 + t < M) ? g / scale_x[m0 + t] : 0.0f;
     }
 
-    auto load_global = [&](int it, Prefetch& p) {
-        const int k0 = it * BK;
+    // Activations: thread tg stages chunks tg + 256 u (row c / 4, chunk c % 4)
+    // of the group's 128 rows; offsets relative to the step's base address.
+    const int mh = m0 + wm * HM;  // first row of the group's half
+    uint32_t aoff[kAPer];
+    int acol[kAPer];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int c = t + u * kThreads;  // 0..1023: 256 rows x 4 chunks
-            const int row = c >> 2, ch = c & 3;
-            const int k = k0 + ch * 16;
-            if (m0 + row < M && k < K)
-                p.a[u] = *reinterpret_cast<const uint4*>(Xq + (int64_t)(m0 + row) * K + k);
-            else
-                p.a[u] = make_uint4(0, 0, 0, 0);
-            if (n0 + row < N && k < K)
-                p.b[u] = *reinterpret_cast<const uint32_t*>(Wp + (int64_t)(n0 + row) * KB + k / 4);
-            else
-                p.b[u] = 0u;
+    for (int u = 0; u < kAPer; ++u) {
+        const int c = tg + u * kGroupThreads;
+        const int row = c >> 2;
+        acol[u] = (c & 3) * 16;
+        aoff[u] = mh + row < M ? (uint32_t)(row * K + acol[u]) : kBufOOB;
+    }
+    const int8_t* Xt = Xq + (int64_t)mh * K;
+    // Weights: in a quarter, thread tg stages slice bc = tg % 4 of row
+    // bq = tg / 4 (+ 64 per quarter), both 8-byte halves in slot order.
+    const int bq = tg >> 2, bc = tg & 3, bsw = half_swap(bq);
+    const uint32_t boff = (uint32_t)(bq * KB + 16 * bc);
+    const uint8_t* Wt = Wp + (int64_t)n0 * KB;
+
+    auto load_a = [&](int it, uint4 (&a)[kAPer]) {
+        const int k0 = it * BK;
+        const __amdgpu_buffer_rsrc_t ra = make_buf(Xt + k0);
+#pragma unroll
+        for (int u = 0; u < kAPer; ++u) a[u] = buf_load16(ra, k0 + acol[u] < K ? aoff[u] : kBufOOB);
+    };
+    auto load_b = [&](int qi, uint4& b) {  // quarter qi: block qi / 4, rows 64 (qi % 4) + bq
+        const int blk = qi >> 2, part = qi & 3;
+        const int kb0 = blk * kStepsPerBlock * BK;  // first column of the block
+        const __amdgpu_buffer_rsrc_t rb = make_buf(Wt + (int64_t)part * kQuarterRows * KB + blk * ROW_BYTES);
+        const bool rv = n0 + part * kQuarterRows + bq < N;
+        const int kc = kb0 + bc * BK;  // first column of the slice
+        if constexpr (VECB) {
+            const bool v = rv && kc < K;
+            const uint2 lo = buf_load8(rb, v ? boff + 8 * bsw : kBufOOB);
+            const uint2 hi = buf_load8(rb, v ? boff + 8 * (bsw ^ 1) : kBufOOB);
+            b = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {  // dword d of the slice covers columns kc + 16 d .. + 15
+            const int d0 = 2 * bsw, d1 = 2 * (bsw ^ 1);
+            b.x = buf_load4(rb, rv && kc + 16 * d0 < K ? boff + 4 * d0 : kBufOOB);
+            b.y = buf_load4(rb, rv && kc + 16 * d0 + 16 < K ? boff + 4 * d0 + 4 : kBufOOB);
+            b.z = buf_load4(rb, rv && kc + 16 * d1 < K ? boff + 4 * d1 : kBufOOB);
+            b.w = buf_load4(rb, rv && kc + 16 * d1 + 16 < K ? boff + 4 * d1 + 4 : kBufOOB);
         }
     };
-    auto store_lds = [&](int buf, const Prefetch& p) {
-        uint8_t* As = smem + buf * BUF_BYTES;
-        uint8_t* Bs = As + A_BYTES;
+    // staged activation chunks are byte-transposed in registers (in a
+    // compute phase, where the VALU is otherwise idle) and stored as they are
+    auto transpose_a = [&](uint4 (&a)[kAPer]) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int c = t + u * kThreads;
-            const int row = c >> 2, ch = c & 3;
-            const uint32_t in[4] = {p.a[u].x, p.a[u].y, p.a[u].z, p.a[u].w};
+        for (int u = 0; u < kAPer; ++u) {
+            const uint32_t in[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
             uint32_t o[4];
             transpose4x4_bytes(in, o);
-            *reinterpret_cast<uint4*>(As + row * A_STRIDE + ch * 16) = make_uint4(o[0], o[1], o[2], o[3]);
-            *reinterpret_cast<uint32_t*>(Bs + row * B_STRIDE + ch * 4) = p.b[u];
+            a[u] = make_uint4(o[0], o[1], o[2], o[3]);
         }
     };
+    auto store_a = [&](int buf, const uint4 (&a)[kAPer]) {
+        uint8_t* As = smem_a[wm][buf];
+#pragma unroll
+        for (int u = 0; u < kAPer; ++u) {
+            const int c = tg + u * kGroupThreads;
+            *reinterpret_cast<uint4*>(As + row_slot(c >> 2, c & 3)) = a[u];
+        }
+    };
+    auto store_b = [&](int qi, const uint4& b) {
+        uint8_t* Bs = smem_b[wm][(qi >> 2) & 1];
+        *reinterpret_cast<uint4*>(Bs + row_slot((qi & 3) * kQuarterRows + bq, bc)) = b;
+    };
+    // tile t of the activations and quarter t + 3 of the weights
+    auto load_global = [&](int it, Stage& p) {
+        load_a(it, p.a);
+        load_b(it + 3, p.b);
+    };
+    auto store_lds = [&](int it, const Stage& p) {
+        store_a(it & 1, p.a);
+        store_b(it + 3, p.b);
+    };
 
-    v16i acc[4][2];
+    v16i acc[4][JN];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < JN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    Prefetch pf;
-    load_global(0, pf);
-    store_lds(0, pf);
-    __syncthreads();
-
     const int g = lane >> 5;    // lane group: k chunks 2g, 2g+1 of the step
     const int l32 = lane & 31;  // row (A) / column (B) inside a 32-block
-    for (int it = 0; it < nk; ++it) {
-        const int buf = it & 1;
-        if (it + 1 < nk) load_global(it + 1, pf);
-        const uint8_t* As = smem + buf * BUF_BYTES;
-        const uint8_t* Bs = As + A_BYTES;
-        uint2 bp[2];
+
+    // Operands of one step: MFMA half kh pairs activation chunk 2g+kh with
+    // the same chunk of the codes (one packed dword per half).
+    v4i a[2][4], b[2][JN];
+    uint2 bp[JN];
+    auto read_codes = [&](int it) {
+        const uint8_t* Bs = smem_b[wm][(it >> 2) & 1];
+        const int c = it & 3;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            bp[j] = *reinterpret_cast<const uint2*>(Bs + (wn * 64 + j * 32 + l32) * B_STRIDE + 8 * g);
+        for (int j = 0; j < JN; ++j) {
+            const int r = wn * 64 + j * 32 + l32;
+            bp[j] = *reinterpret_cast<const uint2*>(Bs + row_slot(r, c) + 8 * (g ^ half_swap(r)));
+        }
+    };
+    auto read_acts = [&](int buf) {
+        const uint8_t* As = smem_a[wm][buf];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            v4i a[4], b[2];
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint4 v = *reinterpret_cast<const uint4*>(
-                    As + (wm * 128 + i * 32 + l32) * A_STRIDE + 32 * g + 16 * kh);
-                a[i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                const uint4 v = *reinterpret_cast<const uint4*>(As + row_slot(i * 32 + l32, 2 * g + kh));
+                a[kh][i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
             }
+    };
+    auto unpack_codes = [&] {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                uint32_t u[4];
-                unpack16(kh ? bp[j].y : bp[j].x, u);
-                b[j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
-            }
+        for (int j = 0; j < JN; ++j) {
+            uint32_t u[4];
+            unpack16(bp[j].x, u);
+            b[0][j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
+            unpack16(bp[j].y, u);
+            b[1][j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
+        }
+    };
+    auto barrier = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // One step.  Memory phase: operands of step it (packed codes first, then
+    // activations); activation tile it + 1 and weight quarter it + 4 (loaded
+    // two steps ago into `st`, transposed since) into LDS; then the loads of
+    // tile it + 3 / quarter it + 6 into the freed `st`.  Compute phase: the
+    // 16 MFMAs, with the VALU work of the step between them: unpacking the
+    // codes just read and byte-transposing the activations of `nx` (loaded a
+    // step ago, stored next step).
+    //   Buffers: activation tile t in buffer t % 2; weight block t / 4 (steps
+    //   4 (t/4) .. + 3) in buffer (t / 4) % 2, written a quarter per step
+    //   during the four steps before it is read.  Every buffer is rewritten
+    //   only two barriers after its last read.
+    auto step = [&](int it, Stage& st, Stage& nx) {
+        read_codes(it);
+        read_acts(it & 1);
+        store_lds(it + 1, st);
+        load_global(it + 3, st);
+        barrier();
+        __builtin_amdgcn_s_setprio(1);
+        unpack_codes();
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        if (it + 1 < nk) store_lds(buf ^ 1, pf);
-        __syncthreads();
-    }
+                for (int j = 0; j < JN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[kh][i], b[kh][j], acc[i][j], 0, 0, 0);
+        transpose_a(nx.a);
+        __builtin_amdgcn_s_setprio(0);
+        barrier();
+    };
 
+    // Prologue: activation tile 0 and weight block 0 (quarters 0-3) in LDS;
+    // tiles 1, 2 and quarters 4, 5 loading.  Group 1 then waits one extra
+    // barrier, which puts it a phase behind group 0.
+    {
+        uint4 q0, q1, q2;
+        load_b(0, q0);
+        load_b(1, q1);
+        load_b(2, q2);
+        Stage p0;
+        load_global(0, p0);  // tile 0, quarter 3
+        transpose_a(p0.a);
+        store_a(0, p0.a);
+        store_b(0, q0);
+        store_b(1, q1);
+        store_b(2, q2);
+        store_b(3, p0.b);
+    }
+    Stage s0, s1;
+    load_global(1, s1);
+    load_global(2, s0);
+    transpose_a(s1.a);
+    barrier();
+    if (wm == 1) barrier();
+
+    // Unrolled by two so that the staging sets alternate by name (no copy);
+    // with nk odd the last step runs on zero tiles (loads past K read
+    // zeros), which adds nothing to the sums.
+    for (int it = 0; it < nk; it += 2) {
+        step(it, s1, s0);
+        step(it + 1, s0, s1);
+    }
     // Epilogue.  32x32 block layout: lane holds column l32 and rows
-    // 8*(r/4) + 4*g + r%4 for r = 0..15.
+    // 8*(r/4) + 4*g + r%4 for r = 0..15.  Stores address a uniform tile base
+    // with 32-bit offsets (a tile spans < 2^31 bytes).
+    float* Yt = Y + (int64_t)m0 * N + n0;
+    const int mlim = M - m0, nlim = N - n0;
+    const int rbase = wm * 128 + 4 * g, cbase = wn * 64 + l32;
+    // Interior tiles store without per-element conditions: a branch per
+    // store would let the compiler pull all 256 accumulators into VGPRs at
+    // once.  Edge tiles take the guarded loop.
+    auto store_tile = [&](auto guarded_tag, auto out, auto value) {
+        constexpr bool GUARD = decltype(guarded_tag)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + l32;
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int rloc = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                const int row = m0 + rloc;
-                if (row < M && col < N) {
-                    const int v = acc[i][j][r];
-                    Y[(int64_t)row * N + col] = (float)v * row_scale[rloc];
-                    if (acc_out) acc_out[(int64_t)row * N + col] = v;
+                const int rloc = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+                const int roff = rloc * N;
+                const float rs = row_scale[rloc];
+#pragma unroll
+                for (int j = 0; j < JN; ++j) {
+                    const int cloc = cbase + j * 32;
+                    if (!GUARD || (rloc < mlim && cloc < nlim)) out[roff + cloc] = value(acc[i][j][r], rs);
                 }
             }
+            // keep the scheduler from pulling later accumulators forward
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    auto yval = [](int v, float rs) { return (float)v * rs; };
+    auto aval = [](int v, float) { return v; };
+    if (mlim >= BM && nlim >= BN) store_tile(std::false_type{}, Yt, yval);
+    else store_tile(std::true_type{}, Yt, yval);
+    if (acc_out) {
+        int32_t* At = acc_out + (int64_t)m0 * N + n0;
+        store_tile(std::true_type{}, At, aval);
     }
 }
 
@@ -181,8 +343,12 @@ hipError_t launch_gemm_i8t2(const int8_t* Xq, const float* scale_x, const uint8_
                             const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
                             int32_t* acc, hipStream_t s) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    gemm_i8t2_kernel<<<(unsigned)tiles, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N,
-                                                          (int)K, Y, acc);
+    if (K % BK == 0)
+        gemm_i8t2_kernel<true><<<(unsigned)tiles, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M,
+                                                                    (int)N, (int)K, Y, acc);
+    else
+        gemm_i8t2_kernel<false><<<(unsigned)tiles, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M,
+                                                                     (int)N, (int)K, Y, acc);
     return hipGetLastError();
 }
 
