@@ -16,6 +16,7 @@ bool float_dtype(int d) { return d == BITNET_F32 || d == BITNET_BF16; }
 
 // int8 GEMM / GEMV path limits: |acc| <= 128*K must fit int32.
 constexpr int64_t kMaxK = (int64_t)1 << 24;
+constexpr int64_t kMaxFwdN = (int64_t)1 << 23;  // GEMM tile: 256 rows x N, 32-bit offsets
 constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;  // kernels index rows with int
 
 }  // namespace
@@ -73,7 +74,7 @@ int bitnet_linear_fwd(const int8_t* Xq, const float* scale_x, const uint8_t* W_p
                       const float* gamma, int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc,
                       void* stream) {
     if (!Xq || !scale_x || !W_packed || !gamma || !Y) return BITNET_E_ARG;
-    if (M < 1 || N < 1 || K < 1 || K % 16 != 0 || K >= kMaxK || M > kMaxDim || N > kMaxDim)
+    if (M < 1 || N < 1 || K < 1 || K % 16 != 0 || K >= kMaxK || M > kMaxDim || N >= kMaxFwdN)
         return BITNET_E_SHAPE;
     if (!aligned16(Xq) || !aligned16(W_packed) || !aligned16(Y) || !aligned4(scale_x) ||
         !aligned4(gamma) || (acc && !aligned16(acc)))

@@ -117,12 +117,13 @@ int bitnet_act_quant(const void *X, int x_dtype, int64_t M, int64_t K, float eps
  * (wide accumulator), [WALL 3.1] (+1 adds, -1 subtracts, 0 skips):
  *   acc[m][n] = sum_k Xq[m][k] * code[n][k]      (exact int32)
  *   Y[m][n]   = acc[m][n] * gamma / scale_x[m]   (fp32)
- * M <= 16 (with K <= 8192) takes the bandwidth-bound packed GEMV, other
+ * M <= 16 (with K <= 16384) takes the bandwidth-bound packed GEMV, other
  * shapes the int8 MFMA GEMM.
  *   Xq       [M][K] int8;  scale_x [M] fp32;  W_packed [N][K/4];  gamma 1 fp32
  *   Y        [M][N] fp32, written
  *   acc      [M][N] int32, written when non-NULL (for exact checks)
- * |acc| <= 128*K must fit int32, so K < 2^24; K % 16 == 0.
+ * |acc| <= 128*K must fit int32, so K < 2^24; K % 16 == 0.  N < 2^23 (the
+ * GEMM addresses a 256-row output tile with 32-bit offsets).
  * Errors: BITNET_E_ARG, BITNET_E_SHAPE, BITNET_E_ALIGN, BITNET_E_HIP.
  */
 int bitnet_linear_fwd(const int8_t *Xq, const float *scale_x, const uint8_t *W_packed,

@@ -89,6 +89,7 @@ def test_linear_fwd_rejects_bad_arguments():
     assert lib.bitnet_linear_fwd(P, P, P, P, 4, 4, 8, P, NULL, NULL) == -2     # K % 16
     assert lib.bitnet_linear_fwd(P, P, P, P, 4, 0, 16, P, NULL, NULL) == -2
     assert lib.bitnet_linear_fwd(P, P, P, P, 4, 4, 1 << 24, P, NULL, NULL) == -2
+    assert lib.bitnet_linear_fwd(P, P, P, P, 4, 1 << 23, 16, P, NULL, NULL) == -2  # N limit
     assert lib.bitnet_linear_fwd(P, P, P, P, 4, 4, 16, P, ctypes.c_void_p((1 << 20) + 4), NULL) == -4
 
 
