@@ -16,7 +16,7 @@ bool float_dtype(int d) { return d == BITNET_F32 || d == BITNET_BF16; }
 
 // int8 GEMM / GEMV path limits: |acc| <= 128*K must fit int32.
 constexpr int64_t kMaxK = (int64_t)1 << 24;
-constexpr int64_t kMaxFwdN = (int64_t)1 << 23;  // GEMM tile: 256 rows x N, 32-bit offsets
+constexpr int64_t kMaxFwdN = (int64_t)1 << 23;  // tile loads and stores use 32-bit offsets
 constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;  // kernels index rows with int
 
 }  // namespace
@@ -93,7 +93,7 @@ int bitnet_linear_bwd_ste(const void* grad_y, int gy_dtype, const int8_t* Xq, co
     if (!grad_y || !Xq || !scale_x || !W_packed || !gamma) return BITNET_E_ARG;
     if (!grad_x && !grad_W) return BITNET_E_ARG;
     if (gy_dtype != BITNET_BF16 || !float_dtype(gx_dtype)) return BITNET_E_DTYPE;
-    if (M < 1 || N < 1 || K < 1 || K % 16 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    if (M < 1 || N < 1 || K < 1 || K % 16 != 0 || M > kMaxDim || N >= kMaxFwdN || K >= kMaxK)
         return BITNET_E_SHAPE;
     if (!aligned16(grad_y) || !aligned16(Xq) || !aligned16(W_packed) || !aligned4(scale_x) ||
         !aligned4(gamma) || (grad_x && !aligned16(grad_x)) || (grad_W && !aligned16(grad_W)))

@@ -10,20 +10,31 @@
 // "BitNet 三元权重量化训练工程" (gradient-clipping section) pairs a bf16
 // forward with fp32 gradients: both products run on v_mfma_f32_32x32x16_bf16
 // with fp32 accumulation.  gy and the codes are exact in bf16; X_deq is
-// rounded to bf16 once (Xq times the correctly rounded 1/scale_x).
+// rounded to bf16 once (Xq times 1/scale_x).
 //
-// Each matrix-core operand wants its contraction index contiguous per lane.
-// grad_x reads gy rows as they are; the codes are unpacked from 2 bits into
-// a natural [n][k] LDS tile.  grad_W contracts over tokens, so both of its
-// tiles ([m][n] from gy, [m][k] from Xq) are natural too.  Tiles stored with
-// the contraction index as their row are read transposed by gfx950's
-// ds_read_b64_tr_b16, so every LDS write is a 16-byte store.  No operand is
-// copied through HBM.
+// One kernel template serves both products.  Output tile BM x BN per
+// 512-thread workgroup, BK of the contraction per step.  Two wave groups
+// (waves 0-3: tile rows 0 .. BM/2-1, waves 4-7: the rest) put one wave on
+// each SIMD and run the same loop one barrier apart (ping-pong): while one
+// wave per SIMD issues its MFMAs, the other does its memory phase (operand
+// reads, LDS writes of the next tile, global loads two steps ahead).
 //
-// Tiles are 256 x 256 (512 threads, 2 x 4 waves of 128 x 64) when the output
-// has enough of them, else 128 x 128 (256 threads, 2 x 2 waves of 64 x 64);
-// when even those are too few, grad_W splits its token range and a second
-// kernel adds the fp32 partial tiles in split order (deterministic).
+// Operands.  A matrix-core operand wants 8 contraction values per lane.
+//   grad_x: A = gy rows as they are ("rows" tile, 16-byte reads); B = the
+//     codes, unpacked from 2 bits to bf16 +-1/0 in their natural [n][k]
+//     order ("cols" tile).
+//   grad_W: A = gy [m][n] and B = X_deq [m][k], both "cols" tiles.
+// A "cols" tile has the contraction index as its row; gfx950's transposing
+// read ds_read_b64_tr_b16 turns four rows x four columns per lane group into
+// the operand layout, so every LDS write is a 16-byte store of loaded (or
+// converted) data.  The A tile is private to its group; the B tile is shared:
+// each group fills half of it.  The ping-pong barrier order makes that safe:
+// a tile written in a group's memory phase of step s is read in memory phases
+// s + 1 of both groups, and its buffer is rewritten only at step s + 2.
+//
+// Small outputs (fewer than 256 large tiles) use 128 x 128 tiles; grad_W
+// then also splits its token range, and a second kernel adds the fp32
+// partial tiles in split order (deterministic).
 #include "common.h"
 
 namespace bitnet {
@@ -32,389 +43,412 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-constexpr int BK = 64;  // contraction per step: 4 MFMA sub-steps of 16
+enum { kGradX = 0, kGradW = 1 };
+constexpr int kThreads = 512;
+constexpr int kGroupThreads = 256;
 
-// LDS tiles come in two layouts.
-//  "rows": one row per output index, its 64 contraction values contiguous
-//          (128 B + 16 pad); MFMA operands are plain 16-byte reads.
-//  "cols": one row per contraction index, the output indices contiguous
-//          (pitch = 2*width + 64 B, i.e. 64 B mod 256, so that the transposing
-//          reads below hit 64 distinct banks); written with 16-byte stores
-//          straight from the source rows, read transposed with
-//          ds_read_b64_tr_b16.
-constexpr int ROWS_STRIDE = 144;
-template <int W>
-constexpr int cols_pitch() { return 2 * W + 64; }
+template <int BM_, int BN_, int BK_>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int HM = BM / 2;   // output rows per group
+    static constexpr int WTN = BN / 4;  // output columns per wave
+    static constexpr int IM = HM / 32, JN = WTN / 32;
+    static constexpr int KQ = BK / 16;  // MFMA k-steps per step
+    // "rows" tile: HM rows x BK bf16 (2*BK bytes), 16-byte chunks swizzled
+    static constexpr int CPR = 2 * BK / 16;
+    static constexpr int ROWS_BYTES = HM * 2 * BK;
+    // "cols" tile of width W: BK rows, pitch 2W + 64 bytes (64 or 192 mod
+    // 256, so the 32 8-byte pieces of each transposing read hit 32 distinct
+    // bank pairs)
+    static constexpr int pitch(int W) { return 2 * W + 64; }
+    static constexpr int cols_bytes(int W) { return BK * pitch(W); }
+};
+using TileL = Tile<256, 256, 32>;
+using TileS = Tile<128, 128, 64>;
+
+// Chunk c of row r of a "rows" tile: each 256-byte bank window holds 16/CPR
+// rows; XOR-ing the chunk index with the window index gives every 16-lane
+// group (16 rows, same chunk; or 16/CPR rows, all chunks) distinct banks.
+template <class T>
+__device__ __forceinline__ int rows_slot(int r, int c) {
+    constexpr int RPW = 16 / T::CPR;  // rows per 256-byte window
+    return r * (2 * T::BK) + 16 * (c ^ ((r / RPW) % T::CPR));
+}
 
 // Transposing read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane group,
 // lane j supplies the address of 4 consecutive bf16; output lane 4a+b then
 // holds element b of the chunks of lanes a, 4+a, 8+a, 12+a.  So if lane
 // j = 4e + a points at contraction row c0+e, columns x0+4a..x0+4a+3, output
 // lane i holds column x0+i at rows c0..c0+3.
-__device__ __forceinline__ v4s lds_read_tr16(const uint8_t* tile, int byte_off) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* tile, int byte_off) {
+    const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_v4s*)((__attribute__((address_space(3))) const char*)tile + byte_off));
+    return __builtin_bit_cast(uint2, v);
 }
 
-// Matrix-core operand (8 contraction values for output index x0 + lane%32)
-// from a "cols" tile: two transposing reads give contraction rows
-// c0 + 8*(lane/32) + 0..3 and + 4..7.
+// Operand (8 contraction values c0 + 8*(lane/32) + 0..7 for output index
+// x0 + lane%32) from a "cols" tile: two transposing reads, rows +0..3, +4..7.
 template <int PITCH>
 __device__ __forceinline__ v8bf cols_operand(const uint8_t* tile, int c0, int x0, int lane) {
     const int G = lane >> 4, j = lane & 15, e = j >> 2, a = j & 3;
     const int row = c0 + 8 * (G >> 1) + e, col = x0 + 16 * (G & 1) + 4 * a;
-    const v4s lo = lds_read_tr16(tile, row * PITCH + 2 * col);
-    const v4s hi = lds_read_tr16(tile, (row + 4) * PITCH + 2 * col);
-    v8bf r;
-    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
-    r = __builtin_bit_cast(v8bf, make_uint4(l.x, l.y, h.x, h.y));
-    return r;
+    const uint2 lo = lds_read_tr16(tile, row * PITCH + 2 * col);
+    const uint2 hi = lds_read_tr16(tile, (row + 4) * PITCH + 2 * col);
+    return __builtin_bit_cast(v8bf, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// Matrix-core operand from a "rows" tile: contraction values
-// c0 + 8*(lane/32) + 0..7 of output row x0 + lane%32.
-__device__ __forceinline__ v8bf rows_operand(const uint8_t* tile, int c0, int x0, int lane) {
-    return *reinterpret_cast<const v8bf*>(tile + (x0 + (lane & 31)) * ROWS_STRIDE +
-                                          2 * (c0 + 8 * (lane >> 5)));
+// Operand from a "rows" tile: contraction values 16*kq + 8*(lane/32) + 0..7
+// of row x0 + lane%32.
+template <class T>
+__device__ __forceinline__ v8bf rows_operand(const uint8_t* tile, int kq, int x0, int lane) {
+    return *reinterpret_cast<const v8bf*>(tile + rows_slot<T>(x0 + (lane & 31), 2 * kq + (lane >> 5)));
 }
 
-template <int BM>
-constexpr int kThreadsFor = BM == 256 ? 512 : 256;
+// 16 ternary codes (one packed dword, columns k..k+15) -> 16 bf16 in natural
+// column order (8 dwords, two codes each).  bf16 of a code: low byte 0x80 if
+// nonzero, high byte 0x3f (+1) or 0xbf (-1).
+__device__ __forceinline__ void codes16_to_bf16(uint32_t w, uint4 (&o)[2]) {
+    constexpr uint32_t kHi = 0x00bf3f00u, kLo = 0x00808000u;
+    const uint32_t ev = w & 0x33333333u;         // codes 0, 2 of every byte
+    const uint32_t od = (w >> 2) & 0x33333333u;  // codes 1, 3 of every byte
+    uint32_t r[8];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        // [ev.b, ev.b, od.b, od.b]: codes 4b, 4b+2 (low / high nibble of ev.b), 4b+1, 4b+3
+        const uint32_t pb = __builtin_amdgcn_perm(od, ev, (uint32_t)(b | b << 8 | (b + 4) << 16 | (b + 4) << 24));
+        const uint32_t s0 = (pb & 0x03030303u) + 0x00040004u;
+        const uint32_t s1 = ((pb >> 4) & 0x03030303u) + 0x00040004u;
+        r[2 * b] = __builtin_amdgcn_perm(kLo, kHi, s0);
+        r[2 * b + 1] = __builtin_amdgcn_perm(kLo, kHi, s1);
+    }
+    o[0] = make_uint4(r[0], r[1], r[2], r[3]);
+    o[1] = make_uint4(r[4], r[5], r[6], r[7]);
+}
 
-template <int BM, int BN>
-struct Cfg {
-    static constexpr int T = kThreadsFor<BM>;
-    static constexpr int WAVES_N = BM == 256 ? 4 : 2;
-    static constexpr int WTM = BM / 2, WTN = BN / WAVES_N;
-    static constexpr int IM = WTM / 32, JN = WTN / 32;
-    static constexpr int MFMAS = IM * JN * 4;  // per wave and step
-};
+// 16 int8 (4 dwords) times rs -> 16 bf16 (8 dwords)
+__device__ __forceinline__ void int8x16_to_bf16(uint4 q, float rs, uint4 (&o)[2]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t r[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v2bf p;
+            p[0] = (__bf16)((float)(int8_t)(w[d] >> (16 * h)) * rs);
+            p[1] = (__bf16)((float)(int8_t)(w[d] >> (16 * h + 8)) * rs);
+            r[2 * d + h] = __builtin_bit_cast(uint32_t, p);
+        }
+    }
+    o[0] = make_uint4(r[0], r[1], r[2], r[3]);
+    o[1] = make_uint4(r[4], r[5], r[6], r[7]);
+}
 
-// Workgroup id -> (tile m, tile n, split), regrouped so that each XCD (ids
-// are dealt round-robin over the 8 XCDs) works on a contiguous run.
+// Workgroup id -> (tile row, tile column, split), regrouped so that each XCD
+// (ids are dealt round-robin over the 8 XCDs) works on a contiguous run.
 __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int splits, int& tm,
                                         int& tn, int& sp) {
     const int G = tiles_m * tiles_n * splits;
     const int q = G / 8, r = G % 8;
     const int x = wg % 8, local = wg / 8;
     int id = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
-    sp = id % splits;
+    sp = __builtin_amdgcn_readfirstlane(id % splits);
     id /= splits;
-    tm = id / tiles_n;
-    tn = id % tiles_n;
+    tm = __builtin_amdgcn_readfirstlane(id / tiles_n);
+    tn = __builtin_amdgcn_readfirstlane(id % tiles_n);
 }
 
-// Interleave hint for one step: each MFMA followed by a few VALU and LDS ops.
-template <int N_MFMA>
-__device__ __forceinline__ void interleave_hint() {
-#pragma unroll
-    for (int q = 0; q < N_MFMA; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // up to two LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // up to one LDS write
-    }
-}
-
-// Output of one wave: 32x32 block layout, lane holds column l32 and rows
-// 8*(r/4) + 4*g + r%4.
-template <int BM, int BN, typename F>
-__device__ __forceinline__ void for_each_out(const v16f (&acc)[Cfg<BM, BN>::IM][Cfg<BM, BN>::JN],
-                                             int wm, int wn, int lane, F&& f) {
-    using C = Cfg<BM, BN>;
-    const int g = lane >> 5, l32 = lane & 31;
-#pragma unroll
-    for (int i = 0; i < C::IM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::JN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                f(wm * C::WTM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3), wn * C::WTN + j * 32 + l32,
-                  acc[i][j][r]);
-}
-
-// 8 bf16 of row `r` from column `c` (zero past `cols` or past `rows`);
-// branch-free: out-of-range reads go to a clamped, valid address.
-__device__ __forceinline__ uint4 load8_bf16(const uint16_t* P, int rows, int cols, int r, int c,
-                                            bool vec) {
-    const bool rv = r < rows;
-    const uint16_t* p = P + (int64_t)(rv ? r : 0) * cols;
-    if (vec) {
-        const bool v = rv && c < cols;
-        const uint4 x = *reinterpret_cast<const uint4*>(p + (v ? c : 0));
-        return v ? x : make_uint4(0, 0, 0, 0);
-    }
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const bool v0 = rv && c + 2 * e < cols, v1 = rv && c + 2 * e + 1 < cols;
-        const uint32_t lo = p[v0 ? c + 2 * e : 0], hi = p[v1 ? c + 2 * e + 1 : 0];
-        w[e] = (v0 ? lo : 0u) | ((v1 ? hi : 0u) << 16);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// 16 ternary codes (one packed dword, columns k..k+15) -> 16 bf16 in natural
-// column order (8 dwords, two codes each).  bf16 of a code: low byte 0x80 if
-// nonzero, high byte 0x3f (+1) or 0xbf (-1).
-__device__ __forceinline__ void codes16_to_bf16(uint32_t w, uint32_t (&o)[8]) {
-    constexpr uint32_t kHi = 0x00bf3f00u, kLo = 0x00808000u;
-    const uint32_t ev = w & 0x33333333u;          // codes 0,2 of every byte (bits 0-1, 4-5)
-    const uint32_t od = (w >> 2) & 0x33333333u;   // codes 1,3 of every byte
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        // [ev.b, ev.b, od.b, od.b]: codes 4b (low nibble) and 4b+1, then 4b+2 and 4b+3 (high)
-        const uint32_t pb = __builtin_amdgcn_perm(od, ev, (uint32_t)(b | b << 8 | (b + 4) << 16 | (b + 4) << 24));
-        const uint32_t s0 = (pb & 0x03030303u) + 0x00040004u;
-        const uint32_t s1 = ((pb >> 4) & 0x03030303u) + 0x00040004u;
-        o[2 * b] = __builtin_amdgcn_perm(kLo, kHi, s0);
-        o[2 * b + 1] = __builtin_amdgcn_perm(kLo, kHi, s1);
-    }
-}
+// Staged data of one step (per thread): two 16-byte A chunks as loaded; the
+// B item as loaded (braw: a packed code dword, or 16 int8 with their row's
+// 1/scale_x) and converted to 16 bf16 (bcv) in a compute phase.
+template <int MODE>
+struct Stage;
+template <>
+struct Stage<kGradX> {
+    uint4 a[2];
+    uint32_t braw;
+    uint4 bcv[2];
+};
+template <>
+struct Stage<kGradW> {
+    uint4 a[2];
+    uint4 braw;
+    float rs;
+    uint4 bcv[2];
+};
 
 }  // namespace
 
-// ------------------------------------------------------------------ grad_x
-// out[m][k] = gamma * sum_n gy[m][n] * code[n][k]; tile BM (m) x BN (k).
-// A tile ("rows"): gy rows m as they are.  B tile ("cols"): codes of rows n
-// unpacked to bf16 in natural order ([n][k]), read transposed.
-template <int BM, int BN, bool OUT_BF16>
-__global__ __launch_bounds__(kThreadsFor<BM>) void gradx_kernel(
-    const uint16_t* __restrict__ gy, const uint8_t* __restrict__ Wp,
-    const float* __restrict__ gamma_p, int M, int N, int K, void* __restrict__ out) {
-    using C = Cfg<BM, BN>;
-    constexpr int A_BYTES = BM * ROWS_STRIDE;
-    constexpr int BP = cols_pitch<BN>();
-    constexpr int B_BYTES = BK * BP;
-    constexpr int kAPer = BM * 8 / C::T;             // 16-byte A chunks per thread
-    constexpr int kBPer = BK * (BN / 16) / C::T;     // 16-code B items per thread
-    __shared__ __align__(16) uint8_t smem[2][A_BYTES + B_BYTES];
+// MODE kGradX: out [M][K] (fp32, or bf16 if OUT_BF16) = gamma * gy . codes,
+//   rows m, columns k, contraction n.  `second` = packed codes, `aux` = gamma.
+// MODE kGradW: out [N][K] fp32 = gy^T . X_deq, rows n, columns k, contraction
+//   m over the split's token range; with splits > 1 the tile goes to
+//   out + sp*N*K (partials).  `second` = Xq, `aux` = scale_x.
+// VEC: N % 8 == 0 (gy rows 16-byte aligned, 8-element chunks all in or out);
+// otherwise gy is read element by element.
+template <int MODE, class T, bool VEC, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void bwd_kernel(
+    const uint16_t* __restrict__ gy, const void* __restrict__ second, const float* __restrict__ aux,
+    int M, int N, int K, int splits, int kper, void* __restrict__ out) {
+    constexpr int BK = T::BK, HM = T::HM, IM = T::IM, JN = T::JN, KQ = T::KQ;
+    constexpr int PB = T::pitch(T::BN);  // shared B tile
+    constexpr int PA = T::pitch(HM);     // grad_W A tile
+    constexpr int A_BYTES = MODE == kGradX ? T::ROWS_BYTES : T::cols_bytes(HM);
+    constexpr int B_BYTES = T::cols_bytes(T::BN);
+    constexpr int CPA = HM / 8;          // grad_W: 8-element gy chunks per A row
+    __shared__ __align__(16) uint8_t smem_a[2][2][A_BYTES];  // [group][buffer]
+    __shared__ __align__(16) uint8_t smem_b[2][B_BYTES];     // [buffer]
+
+    // grad_W A chunk c -> (token row, 8-column chunk).  Rows of 16 chunks:
+    // 16 lanes per row.  Rows of 8 chunks (pitch 192): each 16-lane group
+    // takes chunks 0-3 or 4-7 of four consecutive rows, whose 16-byte slots
+    // (row offsets 0, 12, 8, 4 slots mod 16) are then all distinct.
+    auto a_chunk = [](int c, int& row, int& ch) {
+        if constexpr (CPA >= 16) {
+            row = c / CPA;
+            ch = c % CPA;
+        } else {
+            static_assert(CPA == 8, "grad_W A rows of 8 or 16 chunks");
+            const int q = c >> 4, l = c & 15;
+            row = 4 * (q >> 1) + (l >> 2);
+            ch = 4 * (q & 1) + (l & 3);
+        }
+    };
+    const int R = MODE == kGradX ? M : N;  // output rows
+    const int C = K;                        // output columns
+    const int KC = MODE == kGradX ? N : M;  // contraction length
     int tm, tn, sp;
-    tile_of(blockIdx.x, (M + BM - 1) / BM, (K + BN - 1) / BN, 1, tm, tn, sp);
-    const int m0 = tm * BM, k0 = tn * BN;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    tile_of(blockIdx.x, (R + T::BM - 1) / T::BM, (C + T::BN - 1) / T::BN, splits, tm, tn, sp);
+    const int r0 = tm * T::BM, c0 = tn * T::BN;
+    const int klo = sp * kper, khi = min(KC, klo + kper);
+    const int nsteps = (khi - klo + BK - 1) / BK;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 2, wn = wave & 3;  // wm: the wave group
+    const int tg = t & (kGroupThreads - 1);
     const int KB = K / 4;
-    const bool vec = (N % 8) == 0;
-    const int nsteps = (N + BK - 1) / BK;
-    constexpr int kcN = BN / 16;
+    const int rg = r0 + wm * HM;           // first output row of the group
+    const int cb = c0 + wm * (T::BN / 2);  // first column of the group's B half
 
-    struct Stage {
-        uint4 a[kAPer];
-        uint32_t b[kBPer];
+    // ---- per-thread staging geometry; offsets are relative to the step's
+    // base address (which moves by BK along the contraction)
+    // A chunks u = 0, 1 (c = tg + 256 u): 8 consecutive gy elements.
+    //   grad_x: row rg + c / CPR, contraction 8 * (c % CPR) of the step
+    //   grad_W: token c / CPA of the step, columns rg + 8 * (c % CPA)
+    uint32_t aoff[2];
+    int a_k[2];    // contraction index of the chunk's first element (in the step)
+    int a_lim[2];  // grad_x: row valid; grad_W: columns left in the row
+    bool a_ok[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int c = tg + u * kGroupThreads;
+        if constexpr (MODE == kGradX) {
+            const int row = c / T::CPR, ch = c % T::CPR;
+            a_k[u] = 8 * ch;
+            a_ok[u] = rg + row < R;
+            a_lim[u] = 8;
+            aoff[u] = (uint32_t)((row * N + 8 * ch) * 2);
+        } else {
+            int row, ch;
+            a_chunk(c, row, ch);
+            a_k[u] = row;
+            a_lim[u] = R - (rg + 8 * ch);  // columns of this chunk inside the row
+            a_ok[u] = a_lim[u] > 0;
+            aoff[u] = (uint32_t)((row * N + 8 * ch) * 2);
+        }
+    }
+    // B: one item per thread, 16 output columns of one contraction row.
+    //   grad_x: packed dword j of row bk (codes of 16 columns)
+    //   grad_W: 16 int8 of token bk
+    constexpr int IPR = T::BN / 32;  // items per row of the group's half
+    const int bk = tg / IPR, bj = tg % IPR;
+    const int bcol = wm * (T::BN / 2) + 16 * bj;  // first output column in the tile
+    const bool b_ok = cb + 16 * bj < C;
+    const uint32_t boff = MODE == kGradX ? (uint32_t)(bk * KB + 4 * bj) : (uint32_t)(bk * K + 16 * bj);
+
+    auto load_a = [&](int kb, const __amdgpu_buffer_rsrc_t& ra, int u) -> uint4 {
+        // kb: contraction base of the step
+        if constexpr (VEC) {
+            const bool v = a_ok[u] && kb + a_k[u] < khi;
+            return buf_load16(ra, v ? aoff[u] : kBufOOB);
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bool v0, v1;
+                if constexpr (MODE == kGradX) {
+                    v0 = a_ok[u] && kb + a_k[u] + 2 * e < khi;
+                    v1 = a_ok[u] && kb + a_k[u] + 2 * e + 1 < khi;
+                } else {
+                    v0 = kb + a_k[u] < khi && 2 * e < a_lim[u];
+                    v1 = kb + a_k[u] < khi && 2 * e + 1 < a_lim[u];
+                }
+                const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(ra, v0 ? aoff[u] + 4 * e : kBufOOB, 0, 0);
+                const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(ra, v1 ? aoff[u] + 4 * e + 2 : kBufOOB, 0, 0);
+                w[e] = (lo & 0xffffu) | (hi << 16);
+            }
+            return make_uint4(w[0], w[1], w[2], w[3]);
+        }
     };
-    auto load = [&](int st, Stage& f) {
-        const int n0 = st * BK;
-#pragma unroll
-        for (int u = 0; u < kAPer; ++u) {
-            const int c = t + u * C::T;
-            f.a[u] = load8_bf16(gy, M, N, m0 + c / 8, n0 + 8 * (c % 8), vec);
-        }
-#pragma unroll
-        for (int u = 0; u < kBPer; ++u) {  // item: row n0 + e / kcN, codes 16*(e % kcN)
-            const int e = t + u * C::T;
-            const int n = n0 + e / kcN, k = k0 + 16 * (e % kcN);
-            const bool v = n < N && k < K;
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(Wp + (int64_t)(v ? n : 0) * KB + (v ? k / 4 : 0));
-            f.b[u] = v ? w : 0u;
+    auto load_global = [&](int st, Stage<MODE>& p) {
+        const int kb = klo + st * BK;
+        const bool bv = b_ok && kb + bk < khi;
+        if constexpr (MODE == kGradX) {
+            const __amdgpu_buffer_rsrc_t ra = make_buf(gy + (int64_t)rg * N + kb);
+            p.a[0] = load_a(kb, ra, 0);
+            p.a[1] = load_a(kb, ra, 1);
+            const __amdgpu_buffer_rsrc_t rb =
+                make_buf(static_cast<const uint8_t*>(second) + (int64_t)kb * KB + cb / 4);
+            p.braw = buf_load4(rb, bv ? boff : kBufOOB);
+        } else {
+            const __amdgpu_buffer_rsrc_t ra = make_buf(gy + (int64_t)kb * N + rg);
+            p.a[0] = load_a(kb, ra, 0);
+            p.a[1] = load_a(kb, ra, 1);
+            const __amdgpu_buffer_rsrc_t rb =
+                make_buf(static_cast<const int8_t*>(second) + (int64_t)kb * K + cb);
+            p.braw = buf_load16(rb, bv ? boff : kBufOOB);
+            const bool tv = kb + bk < khi;
+            const float sx = aux[tv ? kb + bk : 0];
+            p.rs = tv ? __builtin_amdgcn_rcpf(sx) : 0.0f;
         }
     };
-    auto store = [&](int buf, const Stage& f) {
-        uint8_t* As = smem[buf];
-        uint8_t* Bs = smem[buf] + A_BYTES;
+    // Conversion to the B tile's bf16 form.  With the pitch (64 B mod 256)
+    // rows bk and bk + 1 of the items' 32-byte slots fall on the same banks;
+    // odd rows therefore store their two halves in swapped order, so each
+    // 16-byte store instruction covers distinct banks.
+    auto convert = [&](Stage<MODE>& p) {
+        uint4 o[2];
+        if constexpr (MODE == kGradX) codes16_to_bf16(p.braw, o);
+        else int8x16_to_bf16(p.braw, p.rs, o);
+        const bool sw = bk & 1;  // per-component selects (no indexed array)
+        p.bcv[0] = make_uint4(sw ? o[1].x : o[0].x, sw ? o[1].y : o[0].y, sw ? o[1].z : o[0].z,
+                              sw ? o[1].w : o[0].w);
+        p.bcv[1] = make_uint4(sw ? o[0].x : o[1].x, sw ? o[0].y : o[1].y, sw ? o[0].z : o[1].z,
+                              sw ? o[0].w : o[1].w);
+    };
+    auto store_lds = [&](int st, const Stage<MODE>& p) {
+        uint8_t* As = smem_a[wm][st & 1];
+        uint8_t* Bs = smem_b[st & 1];
 #pragma unroll
-        for (int u = 0; u < kAPer; ++u) {
-            const int c = t + u * C::T;
-            *reinterpret_cast<uint4*>(As + (c / 8) * ROWS_STRIDE + 16 * (c % 8)) = f.a[u];
+        for (int u = 0; u < 2; ++u) {
+            const int c = tg + u * kGroupThreads;
+            if constexpr (MODE == kGradX)
+                *reinterpret_cast<uint4*>(As + rows_slot<T>(c / T::CPR, c % T::CPR)) = p.a[u];
+            else {
+                int row, ch;
+                a_chunk(c, row, ch);
+                *reinterpret_cast<uint4*>(As + row * PA + 16 * ch) = p.a[u];
+            }
         }
-#pragma unroll
-        for (int u = 0; u < kBPer; ++u) {
-            const int e = t + u * C::T;
-            uint32_t o[8];
-            codes16_to_bf16(f.b[u], o);
-            uint4* d = reinterpret_cast<uint4*>(Bs + (e / kcN) * BP + 32 * (e % kcN));
-            d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-            d[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        }
+        // the item's two 16-byte halves, odd rows in swapped order (see convert)
+        uint8_t* d = Bs + bk * PB + 2 * bcol;
+        *reinterpret_cast<uint4*>(d + 16 * (bk & 1)) = p.bcv[0];
+        *reinterpret_cast<uint4*>(d + 16 * ((bk & 1) ^ 1)) = p.bcv[1];
     };
 
-    v16f acc[C::IM][C::JN];
+    v16f acc[IM][JN];
 #pragma unroll
-    for (int i = 0; i < C::IM; ++i)
+    for (int i = 0; i < IM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::JN; ++j)
+        for (int j = 0; j < JN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // two steps of global loads in flight; past the end of N the loads are
-    // zero-filled from clamped addresses, so the step body has no branch
-    Stage s0, nxt;
-    load(0, s0);
-    load(1, nxt);
-    store(0, s0);
-    __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
-        Stage cur;
-        load(st + 2, cur);
-        const uint8_t* As = smem[buf];
-        const uint8_t* Bs = smem[buf] + A_BYTES;
+    v8bf a[KQ][IM], b[KQ][JN];
+    auto read_operands = [&](int st) {
+        const uint8_t* As = smem_a[wm][st & 1];
+        const uint8_t* Bs = smem_b[st & 1];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            v8bf a[C::IM], b[C::JN];
+        for (int kq = 0; kq < KQ; ++kq) {
 #pragma unroll
-            for (int i = 0; i < C::IM; ++i) a[i] = rows_operand(As, 16 * q, wm * C::WTM + i * 32, lane);
+            for (int j = 0; j < JN; ++j) b[kq][j] = cols_operand<PB>(Bs, 16 * kq, wn * T::WTN + j * 32, lane);
 #pragma unroll
-            for (int j = 0; j < C::JN; ++j) b[j] = cols_operand<BP>(Bs, 16 * q, wn * C::WTN + j * 32, lane);
-#pragma unroll
-            for (int i = 0; i < C::IM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::JN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        store(buf ^ 1, nxt);
-        interleave_hint<C::MFMAS>();
-        __syncthreads();
-        nxt = cur;
-    }
-
-    const float gam = *gamma_p;
-    for_each_out<BM, BN>(acc, wm, wn, lane, [&](int r, int c, float v) {
-        const int m = m0 + r, k = k0 + c;
-        if (m < M && k < K) {
-            if constexpr (OUT_BF16) {
-                static_cast<__bf16*>(out)[(int64_t)m * K + k] = (__bf16)(v * gam);
-            } else {
-                static_cast<float*>(out)[(int64_t)m * K + k] = v * gam;
+            for (int i = 0; i < IM; ++i) {
+                if constexpr (MODE == kGradX) a[kq][i] = rows_operand<T>(As, kq, i * 32, lane);
+                else a[kq][i] = cols_operand<PA>(As, 16 * kq, i * 32, lane);
             }
         }
-    });
-}
-
-// ------------------------------------------------------------------ grad_W
-// out[n][k] = sum_m gy[m][n] * X_deq[m][k]; tile BM (n) x BN (k); token range
-// of split sp: [sp*mper, min(M, (sp+1)*mper)).  With splits > 1 the tile goes
-// to part[sp][n][k] (fp32) for the ordered reduction.  Both tiles are "cols"
-// tiles: gy rows m as they are, and Xq rows m converted to bf16(Xq / s[m]);
-// both are read transposed.
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreadsFor<BM>) void gradw_kernel(
-    const uint16_t* __restrict__ gy, const int8_t* __restrict__ Xq,
-    const float* __restrict__ scale_x, int M, int N, int K, int splits, int mper,
-    float* __restrict__ out) {
-    using C = Cfg<BM, BN>;
-    constexpr int AP = cols_pitch<BM>(), BP = cols_pitch<BN>();
-    constexpr int A_BYTES = BK * AP, B_BYTES = BK * BP;
-    constexpr int kAPer = BK * (BM / 8) / C::T;  // 8-wide gy pieces per thread
-    constexpr int kBPer = BK * (BN / 8) / C::T;  // 8-wide Xq pieces per thread
-    __shared__ __align__(16) uint8_t smem[2][A_BYTES + B_BYTES];
-    int tm, tn, sp;
-    tile_of(blockIdx.x, (N + BM - 1) / BM, (K + BN - 1) / BN, splits, tm, tn, sp);
-    const int n0 = tm * BM, k0 = tn * BN;
-    const int mlo = sp * mper, mhi = min(M, mlo + mper);
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const bool vec = (N % 8) == 0;
-    const int nsteps = (mhi - mlo + BK - 1) / BK;
-
-    struct Stage {
-        uint4 a[kAPer];
-        uint2 b[kBPer];
-        float rs[kBPer];
     };
-    auto load = [&](int st, Stage& f) {
-        const int mb = mlo + st * BK;
-#pragma unroll
-        for (int u = 0; u < kAPer; ++u) {  // piece: token mb + c / (BM/8), n 8*(c % (BM/8))
-            const int c = t + u * C::T;
-            const int m = mb + c / (BM / 8);
-            f.a[u] = load8_bf16(gy, m < mhi ? M : 0, N, m, n0 + 8 * (c % (BM / 8)), vec);
-        }
-#pragma unroll
-        for (int u = 0; u < kBPer; ++u) {
-            const int c = t + u * C::T;
-            const int m = mb + c / (BN / 8), k = k0 + 8 * (c % (BN / 8));
-            const bool mv = m < mhi, v = mv && k < K;
-            const uint2 q = *reinterpret_cast<const uint2*>(Xq + (int64_t)(v ? m : 0) * K + (v ? k : 0));
-            f.b[u] = v ? q : make_uint2(0, 0);
-            const float sx = scale_x[mv ? m : 0];
-            f.rs[u] = mv ? 1.0f / sx : 0.0f;
-        }
-    };
-    auto store = [&](int buf, const Stage& f) {
-        uint8_t* As = smem[buf];
-        uint8_t* Bs = smem[buf] + A_BYTES;
-#pragma unroll
-        for (int u = 0; u < kAPer; ++u) {
-            const int c = t + u * C::T;
-            *reinterpret_cast<uint4*>(As + (c / (BM / 8)) * AP + 16 * (c % (BM / 8))) = f.a[u];
-        }
-#pragma unroll
-        for (int u = 0; u < kBPer; ++u) {
-            const int c = t + u * C::T;
-            const uint32_t q[2] = {f.b[u].x, f.b[u].y};
-            uint32_t o[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float x0 = (float)(int8_t)(q[j >> 1] >> (16 * (j & 1))) * f.rs[u];
-                const float x1 = (float)(int8_t)(q[j >> 1] >> (16 * (j & 1) + 8)) * f.rs[u];
-                typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-                v2bf pr;
-                pr[0] = (__bf16)x0;
-                pr[1] = (__bf16)x1;
-                o[j] = __builtin_bit_cast(uint32_t, pr);
-            }
-            *reinterpret_cast<uint4*>(Bs + (c / (BN / 8)) * BP + 16 * (c % (BN / 8))) =
-                make_uint4(o[0], o[1], o[2], o[3]);
-        }
-    };
-
-    v16f acc[C::IM][C::JN];
-#pragma unroll
-    for (int i = 0; i < C::IM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::JN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    Stage s0, nxt;
-    load(0, s0);
-    load(1, nxt);
-    store(0, s0);
-    __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
-        Stage cur;
-        load(st + 2, cur);
-        const uint8_t* As = smem[buf];
-        const uint8_t* Bs = smem[buf] + A_BYTES;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            v8bf a[C::IM], b[C::JN];
-#pragma unroll
-            for (int i = 0; i < C::IM; ++i) a[i] = cols_operand<AP>(As, 16 * q, wm * C::WTM + i * 32, lane);
-#pragma unroll
-            for (int j = 0; j < C::JN; ++j) b[j] = cols_operand<BP>(Bs, 16 * q, wn * C::WTN + j * 32, lane);
-#pragma unroll
-            for (int i = 0; i < C::IM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::JN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        store(buf ^ 1, nxt);
-        interleave_hint<C::MFMAS>();
+    auto barrier = [] {
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        nxt = cur;
-    }
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
-    float* dst = splits > 1 ? out + (int64_t)sp * N * K : out;
-    for_each_out<BM, BN>(acc, wm, wn, lane, [&](int r, int c, float v) {
-        const int n = n0 + r, k = k0 + c;
-        if (n < N && k < K) dst[(int64_t)n * K + k] = v;
-    });
+    // One step: memory phase = operands of step st, tile st + 1 (loaded two
+    // steps ago, converted since) into LDS, loads of step st + 3 into the
+    // freed staging set; compute phase = the MFMAs, with the conversion of
+    // the other staging set (stored next step) between them.
+    auto step = [&](int st, Stage<MODE>& cur, Stage<MODE>& nx) {
+        read_operands(st);
+        store_lds(st + 1, cur);
+        load_global(st + 3, cur);
+        barrier();
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+            for (int i = 0; i < IM; ++i)
+#pragma unroll
+                for (int j = 0; j < JN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kq][i], b[kq][j], acc[i][j], 0, 0, 0);
+        convert(nx);
+        __builtin_amdgcn_s_setprio(0);
+        barrier();
+    };
+
+    // Prologue: step 0 in LDS buffer 0, steps 1 and 2 loading.  Group 1 then
+    // waits one extra barrier, which puts it a phase behind group 0.
+    Stage<MODE> s0, s1;
+    {
+        Stage<MODE> p0;
+        load_global(0, p0);
+        convert(p0);
+        store_lds(0, p0);
+    }
+    load_global(1, s1);
+    load_global(2, s0);
+    convert(s1);
+    barrier();
+    if (wm == 1) barrier();
+    // unrolled by two (staging sets alternate by name); with nsteps odd the
+    // last step runs on zero tiles (loads past the range read zeros)
+    for (int st = 0; st < nsteps; st += 2) {
+        step(st, s1, s0);
+        step(st + 1, s0, s1);
+    }
+    if (wm == 0) barrier();  // every wave passes the same number of barriers
+
+    // ---- epilogue: 32x32 block layout, lane holds column l32 and rows
+    // 8*(r/4) + 4*g + r%4
+    const int g = lane >> 5, l32 = lane & 31;
+    const float scale = MODE == kGradX ? *aux : 1.0f;
+    float* outf = static_cast<float*>(out);
+    if constexpr (MODE == kGradW) outf += (int64_t)sp * N * K;
+#pragma unroll
+    for (int i = 0; i < IM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = rg + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (row < R) {
+#pragma unroll
+                for (int j = 0; j < JN; ++j) {
+                    const int col = c0 + wn * T::WTN + j * 32 + l32;
+                    if (col < C) {
+                        const float v = acc[i][j][r] * scale;
+                        if constexpr (MODE == kGradX && OUT_BF16)
+                            static_cast<__bf16*>(out)[(int64_t)row * C + col] = (__bf16)v;
+                        else
+                            outf[(int64_t)row * C + col] = v;
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // out[i] = sum over s = 0..splits-1 of part[s][i], in that order.
@@ -442,34 +476,47 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 // ------------------------------------------------------------------ plans
 namespace {
 
-struct Plan {
-    bool big;     // 256 x 256 tiles
-    int splits;   // token splits (grad_W only)
-    int mper;     // tokens per split (multiple of BK)
-    int64_t tiles;
-};
-
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Enough workgroups to cover the 256 CUs at least twice, else smaller tiles,
-// else (grad_W) split the token range.
+struct Plan {
+    bool big;       // TileL, else TileS
+    int splits;     // contraction splits (grad_W only)
+    int kper;       // contraction per split (multiple of the step)
+    int64_t tiles;  // output tiles
+};
+
+// Large tiles when they give at least one workgroup per CU, else small tiles;
+// grad_W (allow_split) then splits its token range so that about two
+// workgroups per CU are in flight, each with at least 8 steps.
 Plan plan_for(int64_t rows, int64_t cols, int64_t depth, bool allow_split) {
-    Plan p{true, 1, (int)depth, ceil_div(rows, 256) * ceil_div(cols, 256)};
-    if (p.tiles >= 512) return p;
+    Plan p{true, 1, (int)depth, ceil_div(rows, TileL::BM) * ceil_div(cols, TileL::BN)};
+    if (p.tiles >= 256) return p;
     p.big = false;
-    p.tiles = ceil_div(rows, 128) * ceil_div(cols, 128);
+    p.tiles = ceil_div(rows, TileS::BM) * ceil_div(cols, TileS::BN);
     if (!allow_split || p.tiles >= 256) return p;
     int64_t s = ceil_div(512, p.tiles);
-    const int64_t max_s = std::max<int64_t>(1, depth / (4 * BK));  // >= 4 steps per split
+    const int64_t max_s = std::max<int64_t>(1, depth / (8 * TileS::BK));
     s = std::min(s, max_s);
-    int64_t mper = ceil_div(ceil_div(depth, s), BK) * BK;
-    s = ceil_div(depth, mper);
-    p.splits = (int)s;
-    p.mper = (int)mper;
+    const int64_t kper = ceil_div(ceil_div(depth, s), TileS::BK) * TileS::BK;
+    p.splits = (int)ceil_div(depth, kper);
+    p.kper = (int)kper;
     return p;
 }
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+template <int MODE, class T, bool OUT_BF16>
+hipError_t launch_one(const uint16_t* gy, const void* second, const float* aux, int M, int N, int K,
+                      const Plan& p, void* out, hipStream_t s) {
+    const unsigned grid = (unsigned)(p.tiles * p.splits);
+    if (N % 8 == 0)
+        bwd_kernel<MODE, T, true, OUT_BF16><<<grid, kThreads, 0, s>>>(gy, second, aux, M, N, K, p.splits,
+                                                                     p.kper, out);
+    else
+        bwd_kernel<MODE, T, false, OUT_BF16><<<grid, kThreads, 0, s>>>(gy, second, aux, M, N, K, p.splits,
+                                                                      p.kper, out);
+    return hipGetLastError();
+}
 
 }  // namespace
 
@@ -484,25 +531,20 @@ hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* sca
     const int m = (int)M, n = (int)N, k = (int)K;
     if (grad_x) {
         const Plan p = plan_for(M, K, N, false);
-        if (p.big) {
-            if (gx_bf16) gradx_kernel<256, 256, true><<<(unsigned)p.tiles, 512, 0, s>>>(gy, Wp, gamma, m, n, k, grad_x);
-            else gradx_kernel<256, 256, false><<<(unsigned)p.tiles, 512, 0, s>>>(gy, Wp, gamma, m, n, k, grad_x);
-        } else {
-            if (gx_bf16) gradx_kernel<128, 128, true><<<(unsigned)p.tiles, 256, 0, s>>>(gy, Wp, gamma, m, n, k, grad_x);
-            else gradx_kernel<128, 128, false><<<(unsigned)p.tiles, 256, 0, s>>>(gy, Wp, gamma, m, n, k, grad_x);
-        }
-        const hipError_t e = hipGetLastError();
+        hipError_t e;
+        if (p.big)
+            e = gx_bf16 ? launch_one<kGradX, TileL, true>(gy, Wp, gamma, m, n, k, p, grad_x, s)
+                        : launch_one<kGradX, TileL, false>(gy, Wp, gamma, m, n, k, p, grad_x, s);
+        else
+            e = gx_bf16 ? launch_one<kGradX, TileS, true>(gy, Wp, gamma, m, n, k, p, grad_x, s)
+                        : launch_one<kGradX, TileS, false>(gy, Wp, gamma, m, n, k, p, grad_x, s);
         if (e != hipSuccess) return e;
     }
     if (grad_W) {
         const Plan p = plan_for(N, K, M, true);
-        float* dst = p.splits > 1 ? static_cast<float*>(ws) : grad_W;
-        const unsigned grid = (unsigned)(p.tiles * p.splits);
-        if (p.big)
-            gradw_kernel<256, 256><<<grid, 512, 0, s>>>(gy, Xq, scale_x, m, n, k, p.splits, p.mper, dst);
-        else
-            gradw_kernel<128, 128><<<grid, 256, 0, s>>>(gy, Xq, scale_x, m, n, k, p.splits, p.mper, dst);
-        hipError_t e = hipGetLastError();
+        void* dst = p.splits > 1 ? ws : static_cast<void*>(grad_W);
+        hipError_t e = p.big ? launch_one<kGradW, TileL, false>(gy, Xq, scale_x, m, n, k, p, dst, s)
+                             : launch_one<kGradW, TileS, false>(gy, Xq, scale_x, m, n, k, p, dst, s);
         if (e != hipSuccess) return e;
         if (p.splits > 1) {
             const int64_t count = N * K;

@@ -149,7 +149,7 @@ int bitnet_linear_fwd(const int8_t *Xq, const float *scale_x, const uint8_t *W_p
  *            output is too small to fill the GPU and the token range is
  *            split (splits*N*K*4 bytes; 0 otherwise, then NULL is allowed);
  *            contents on entry ignored.
- * K % 16 == 0.
+ * K % 16 == 0, K < 2^24, N < 2^23 (tile loads use 32-bit offsets).
  * Errors: BITNET_E_ARG (both outputs NULL), BITNET_E_SHAPE, BITNET_E_DTYPE,
  * BITNET_E_ALIGN, BITNET_E_WORKSPACE, BITNET_E_HIP.
  */

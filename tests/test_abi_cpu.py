@@ -100,6 +100,8 @@ def test_linear_bwd_rejects_bad_arguments():
     assert lib.bitnet_linear_bwd_ste(P, 0, P, P, P, P, 4, 4, 16, P, 0, P, P, ws, NULL) == -3   # fp32 gy
     assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 4, 4, 16, P, 5, P, P, ws, NULL) == -3
     assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 4, 4, 12, P, 0, P, P, ws, NULL) == -2
+    assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 4, 1 << 23, 16, P, 0, P, P, ws, NULL) == -2
+    assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 4, 4, 1 << 24, P, 0, P, P, ws, NULL) == -2
     ws_need = bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, 8192, 1376, 512)
     assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 8192, 1376, 512, P, 0, P, P, ws_need - 256, NULL) == -5
     assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 8192, 1376, 512, P, 0, P, NULL, ws_need, NULL) == -5
