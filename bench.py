@@ -14,15 +14,20 @@ up-projection of the ~15M-parameter LLaMA-shaped model), the forward plus
 STE backward configuration.  Other workloads (--workload) are for
 profiling: tiny, prefill_7b (forward only), decode_7b (packed GEMV only,
 pre-quantized operands, weight copies rotated so every launch streams its
-weights from HBM) and qat_70b_mlp (full step).
+weights from HBM), qat_70b_mlp (full step) and copy (a 1 GiB device copy,
+the calibration kernel for the HBM byte counters).
 
 Prints ONE JSON line.  `value` is the step's algorithmic operation rate:
 (2MNK int8 forward + 2MNK bf16 grad_x + 2MNK bf16 grad_W) / step time,
 in TOPS (forward-only workloads count 2MNK; decode reports GB/s of the
-bytes the GEMV must move).  `roofline` is the dominant single-kernel call
-of the step, timed with HIP events on the stream it runs on; `kernels`
-breaks the step down per call; `cpu_baseline` is the CPU oracle timed on
-this host (a bounded sample of the same workload).
+bytes the GEMV must move).  `roofline` is the longest single product of
+the step (the backward call counts as its grad_x and grad_W products), its
+algorithmic work per launch over its per-launch time from HIP events on the
+stream it runs on; its `traffic` is the HBM bytes per launch from rocprofv3
+FETCH_SIZE + WRITE_SIZE recorded under profiles/ (null once the kernel
+sources differ from the profiled ones).  `kernels` breaks the step down per
+call; `cpu_baseline` is the CPU oracle timed on this host (a bounded sample
+of the same workload).
 """
 import argparse
 import json
@@ -51,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="small_llama",
-                    choices=["small_llama", "tiny", "prefill_7b", "decode_7b", "qat_70b_mlp"])
+                    choices=["small_llama", "tiny", "prefill_7b", "decode_7b", "qat_70b_mlp", "copy"])
     ap.add_argument("--decode-m", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -113,11 +118,57 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
         c["linear_bwd_ste"] = {"ops": 4 * M * N * K,
                                "bytes": 2 * M * N + M * K + N * K // 4 + 4 * M + 4 * M * K + 4 * N * K,
                                "peak_ops": BF16_PEAK_TFLOPS}
+        c["bwd_grad_x"] = {"ops": 2 * M * N * K, "bytes": 2 * M * N + N * K // 4 + 4 + 4 * M * K,
+                           "peak_ops": BF16_PEAK_TFLOPS}
+        c["bwd_grad_W"] = {"ops": 2 * M * N * K, "bytes": 2 * M * N + M * K + 4 * M + 4 * N * K,
+                           "peak_ops": BF16_PEAK_TFLOPS}
     for v in c.values():
         if "ops" in v:
             ridge = v["peak_ops"] * 1e12 / (HBM_PEAK_GBS * 1e9)
             v["bound"] = "mfma" if v["ops"] / v["bytes"] > ridge else "hbm"
     return c
+
+
+KERNEL_OF = {
+    "act_quant": "act_quant_kernel",
+    "weight_quant": "wq_row_abs_sum_kernel + wq_gamma_kernel + wq_pack_kernel",
+    "linear_fwd": "gemm_i8t2_kernel",
+    "bwd_grad_x": "bwd_kernel<grad_x>",
+    "bwd_grad_W": "bwd_kernel<grad_W> (+ split_reduce_kernel when split)",
+}
+# sources each call's kernels are built from: the HBM traffic recorded under
+# profiles/ is used only while these files are unchanged
+SOURCES_OF = {
+    "act_quant": ["bit_ternary_quantized_amd/csrc/quant.hip"],
+    "weight_quant": ["bit_ternary_quantized_amd/csrc/quant.hip"],
+    "linear_fwd": ["bit_ternary_quantized_amd/csrc/gemm_i8.hip", "bit_ternary_quantized_amd/csrc/gemv.hip"],
+    "bwd_grad_x": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
+    "bwd_grad_W": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest(call):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in SOURCES_OF.get(call, []) + ["bit_ternary_quantized_amd/csrc/common.h"]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(call, workload):
+    """HBM bytes per launch of `call` from rocprofv3 FETCH_SIZE + WRITE_SIZE
+    (scaled by the copy calibration), as recorded under profiles/; None when
+    absent or when the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(f"{call}@{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_digest(call):
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
 
 
 def rate(entry, ms):
@@ -204,6 +255,16 @@ def bench_layer(args, name):
             gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], grad_x=b["grad_x"], grad_W=b["grad_W"],
             workspace=b["ws_bwd"])
     names = list(calls)
+    # the backward call's two products, each timed on its own (not part of
+    # the step): grad_x is one kernel, grad_W one kernel plus the ordered
+    # split reduction when its token range is split
+    parts = {}
+    if gy is not None:
+        parts["bwd_grad_x"] = lambda: bt.bitnet_linear_bwd_ste(
+            gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], want_grad_W=False, grad_x=b["grad_x"])
+        parts["bwd_grad_W"] = lambda: bt.bitnet_linear_bwd_ste(
+            gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], want_grad_x=False, grad_W=b["grad_W"],
+            workspace=b["ws_bwd"])
 
     def step():
         for n in names:
@@ -231,28 +292,31 @@ def bench_layer(args, name):
     # one graph; K replays of each, bracketed by HIP events on the stream
     # they run on.  A bounded spin first lets the host enqueue the whole loop,
     # so no host gap sits between two events.
-    g_rep = {n: capture(lambda n=n: [calls[n]() for _ in range(REPS)]) for n in names}
-    timer = Timer(names, args.steps)
+    allc = dict(calls, **parts)
+    timed = list(allc)
+    g_rep = {n: capture(lambda n=n: [allc[n]() for _ in range(REPS)]) for n in timed}
+    timer = Timer(timed, args.steps)
     torch.cuda.synchronize()
     torch.cuda._sleep(SLEEP_CYCLES)
     for i in range(args.steps):
-        for j, n in enumerate(names):
+        for j, n in enumerate(timed):
             timer.mark(i, j)
             g_rep[n].replay()
-        timer.mark(i, len(names))
+        timer.mark(i, len(timed))
     torch.cuda.synchronize()
     per = {n: v / REPS for n, v in timer.mean_ms().items()}
 
     counts = layer_counts(M, N, K, d["x"].element_size(), d["w"].element_size(), gy is not None)
-    kernels = {n: {"ms": per[n], **rate(counts[n], per[n])} for n in names}
+    kernels = {n: {"ms": per[n], **rate(counts[n], per[n])} for n in timed}
     fwd_bwd = 2 + (4 if gy is not None else 0)
     value = fwd_bwd * M * N * K / (ms * 1e-3) / 1e12
-    # the forward GEMM is the step's single-kernel hot call; the backward
-    # call launches several kernels and is reported in `kernels`
-    dom = "linear_fwd"
+    # roofline: the longest single product of the step (the backward call
+    # counts as its two products)
+    cands = [n for n in timed if n != "linear_bwd_ste"]
+    dom = max(cands, key=lambda n: per[n])
     roof = dict(rate(counts[dom], per[dom]))
-    roof["kernel"] = "gemm_i8t2_kernel (bitnet_linear_fwd)"
-    roof["traffic"] = None
+    roof["kernel"] = KERNEL_OF[dom] + f" ({dom})"
+    roof["traffic"] = measured_traffic(dom, name)
     out = {
         "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "device_ms_per_step": dev_ms, "higher_is_better": True,
@@ -319,6 +383,31 @@ def bench_decode(args):
     return out
 
 
+def bench_copy(args):
+    """Device-to-device copy of a known size (1 GiB, four times the Infinity
+    Cache): the calibration kernel for the HBM byte counters."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(max(1, args.warmup)):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        b.copy_(a)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    return {"metric": "HBM copy GB/s (counter calibration)", "value": gbs, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "copy", "bytes_read": n, "bytes_written": n},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "device copy"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -328,6 +417,8 @@ def main():
     bt.load_library()
     if args.workload == "decode_7b":
         out = bench_decode(args)
+    elif args.workload == "copy":
+        out = bench_copy(args)
     else:
         out = bench_layer(args, args.workload)
     print(json.dumps(out))

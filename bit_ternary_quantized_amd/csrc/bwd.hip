@@ -486,15 +486,16 @@ struct Plan {
 };
 
 // Large tiles when they give at least one workgroup per CU, else small tiles;
-// grad_W (allow_split) then splits its token range so that about two
-// workgroups per CU are in flight, each with at least 8 steps.
+// grad_W (allow_split) then splits its token range so that the grid fills
+// the 256 CUs in one wave of workgroups (one workgroup fits per CU), each
+// split keeping at least 8 steps.
 Plan plan_for(int64_t rows, int64_t cols, int64_t depth, bool allow_split) {
     Plan p{true, 1, (int)depth, ceil_div(rows, TileL::BM) * ceil_div(cols, TileL::BN)};
     if (p.tiles >= 256) return p;
     p.big = false;
     p.tiles = ceil_div(rows, TileS::BM) * ceil_div(cols, TileS::BN);
     if (!allow_split || p.tiles >= 256) return p;
-    int64_t s = ceil_div(512, p.tiles);
+    int64_t s = std::max<int64_t>(1, 256 / p.tiles);
     const int64_t max_s = std::max<int64_t>(1, depth / (8 * TileS::BK));
     s = std::min(s, max_s);
     const int64_t kper = ceil_div(ceil_div(depth, s), TileS::BK) * TileS::BK;
