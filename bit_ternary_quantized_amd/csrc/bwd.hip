@@ -148,17 +148,20 @@ __device__ __forceinline__ void int8x16_to_bf16(uint4 q, float rs, uint4 (&o)[2]
 }
 
 // Workgroup id -> (tile row, tile column, split), regrouped so that each XCD
-// (ids are dealt round-robin over the 8 XCDs) works on a contiguous run.
+// (ids are dealt round-robin over the 8 XCDs) works on a contiguous run, with
+// the tile column fastest: consecutive workgroups share their A operand
+// (the same gy rows, or the same token range and gy columns), which then
+// comes from that XCD's L2.
 __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int splits, int& tm,
                                         int& tn, int& sp) {
     const int G = tiles_m * tiles_n * splits;
     const int q = G / 8, r = G % 8;
     const int x = wg % 8, local = wg / 8;
     int id = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
-    sp = __builtin_amdgcn_readfirstlane(id % splits);
-    id /= splits;
-    tm = __builtin_amdgcn_readfirstlane(id / tiles_n);
     tn = __builtin_amdgcn_readfirstlane(id % tiles_n);
+    id /= tiles_n;
+    sp = __builtin_amdgcn_readfirstlane(id % splits);
+    tm = __builtin_amdgcn_readfirstlane(id / splits);
 }
 
 // Staged data of one step (per thread): two 16-byte A chunks as loaded; the
