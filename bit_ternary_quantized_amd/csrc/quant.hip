@@ -177,8 +177,9 @@ hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, fl
 
 // ===================================================================== K1
 // Pass 1: one wave per weight row -> tree sum of |w| over the row.
-// Pass 2: one workgroup -> tree over the row sums, gamma = max(S/(N*K), 1e-5),
-//         and the code threshold (below).
+// Pass 2: the tree over the row sums, gamma = max(S/(N*K), 1e-5), and the
+//         code threshold (below): one workgroup for large N, else every
+//         workgroup of pass 3 redundantly (one launch fewer).
 // Pass 3: each thread turns kPackU groups of 4 weights into packed bytes.
 //
 // Code decision without a per-element division.  code != 0 exactly when
@@ -230,51 +231,60 @@ __global__ __launch_bounds__(kWqWaves * kWave) void wq_row_abs_sum_kernel(
     if (lane == 0) row_sums[row] = st.total();
 }
 
-// Pass 2 uses 16 waves: with P = N rounded up to a power of two and
-// L = max(256, P/16), wave w sums the aligned range [w*L, (w+1)*L) as a tree
-// and thread 0 combines the 16 partial sums as a tree (ranges beyond N are
-// +0), which is the tree over all N row sums.
-constexpr int kGammaWaves = 16;
-
-__global__ __launch_bounds__(kGammaWaves * kWave) void wq_gamma_kernel(
-    const float* __restrict__ row_sums, int64_t N, int64_t K, float* __restrict__ gamma,
-    float* __restrict__ thr_out) {
-    __shared__ float part[kGammaWaves];
+// Pass 2: the tree over the N row sums.  With P = N rounded up to a power of
+// two and L = max(256, P/W), wave w of W sums the aligned range [w*L,
+// (w+1)*L) as a tree and the W partial sums are combined as a tree (ranges
+// beyond N are +0).  Every W gives the same bits: it is the canonical tree
+// over the row sums padded with zeros, and extra zero padding adds exact
+// zeros.
+template <int W>
+__device__ __forceinline__ void gamma_and_thr(const float* __restrict__ row_sums, int64_t N,
+                                              int64_t K, float* part, float& g, float& thr) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x >> 6;
     constexpr int E = 4;
     constexpr int BLK = kWave * E;
     int64_t P = 1;
     while (P < N) P *= 2;
-    const int64_t L = P / kGammaWaves > BLK ? P / kGammaWaves : BLK;
+    const int64_t L = P / W > BLK ? P / W : BLK;
     const int64_t lo = (int64_t)wv * L;
     const int64_t nblk = L / BLK;
     PairwiseStack st;
     for (int64_t b0 = 0; b0 < nblk; b0 += 8) {
         float v[8][E];
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            const int64_t k0 = lo + (b0 + g) * BLK + (int64_t)lane * E;
+        for (int gi = 0; gi < 8; ++gi) {
+            const int64_t k0 = lo + (b0 + gi) * BLK + (int64_t)lane * E;
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                v[g][e] = (b0 + g < nblk && k0 + e < N) ? row_sums[k0 + e] : 0.0f;
+                v[gi][e] = (b0 + gi < nblk && k0 + e < N) ? row_sums[k0 + e] : 0.0f;
         }
 #pragma unroll
-        for (int g = 0; g < 8; ++g)
-            if (b0 + g < nblk) st.push(wave_tree_sum(lane_tree<E>(v[g])));
+        for (int gi = 0; gi < 8; ++gi)
+            if (b0 + gi < nblk) st.push(wave_tree_sum(lane_tree<E>(v[gi])));
     }
     if (lane == 0) part[wv] = st.total();
     __syncthreads();
-    if (threadIdx.x == 0) {
-        float p16[kGammaWaves];
+    float pw[W];
 #pragma unroll
-        for (int i = 0; i < kGammaWaves; ++i) p16[i] = part[i];
-        const float total = lane_tree<kGammaWaves>(p16);
-        const float mean = total / (float)(N * K);
-        const float g = fmaxf(mean, 1e-5f);
-        const double t = (double)g * (0.5 + 0x1p-25);
-        float thr = (float)t;
-        if ((double)thr <= t) thr = __uint_as_float(__float_as_uint(thr) + 1u);
+    for (int i = 0; i < W; ++i) pw[i] = part[i];
+    const float total = lane_tree<W>(pw);
+    const float mean = total / (float)(N * K);
+    g = fmaxf(mean, 1e-5f);
+    const double t = (double)g * (0.5 + 0x1p-25);
+    thr = (float)t;
+    if ((double)thr <= t) thr = __uint_as_float(__float_as_uint(thr) + 1u);
+}
+
+constexpr int kGammaWaves = 16;
+
+__global__ __launch_bounds__(kGammaWaves * kWave) void wq_gamma_kernel(
+    const float* __restrict__ row_sums, int64_t N, int64_t K, float* __restrict__ gamma,
+    float* __restrict__ thr_out) {
+    __shared__ float part[kGammaWaves];
+    float g, thr;
+    gamma_and_thr<kGammaWaves>(row_sums, N, K, part, g, thr);
+    if (threadIdx.x == 0) {
         gamma[0] = g;
         thr_out[0] = thr;
     }
@@ -286,12 +296,19 @@ __device__ __forceinline__ uint32_t code_bits(float w, float thr) {
 }
 
 constexpr int kPackU = 4;  // groups of 4 weights per thread (loads in flight)
+// Up to this many rows, every pack workgroup evaluates gamma and the
+// threshold itself from the row sums (one launch fewer); above it a single
+// workgroup does and the pack kernel reads the threshold.
+constexpr int64_t kFusedGammaMaxN = 8192;
 
-template <typename T>
+// FUSED: the threshold is computed here from the row sums (block 0 also
+// writes gamma); otherwise it is read from thr_p.
+template <typename T, bool FUSED>
 __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, int64_t total4,
                                                       const float* __restrict__ thr_p,
+                                                      const float* __restrict__ row_sums,
+                                                      int64_t N, int64_t K, float* __restrict__ gamma,
                                                       uint8_t* __restrict__ out) {
-    const float thr = *thr_p;
     const int64_t base = (int64_t)blockIdx.x * (256 * kPackU) + threadIdx.x;
     float v[kPackU][4];
 #pragma unroll
@@ -309,6 +326,15 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, i
                 v[u][3] = __uint_as_float(q.y & 0xffff0000u);
             }
         }
+    }
+    float thr;
+    if constexpr (FUSED) {
+        __shared__ float part[4];
+        float g;
+        gamma_and_thr<4>(row_sums, N, K, part, g, thr);
+        if (blockIdx.x == 0 && threadIdx.x == 0) gamma[0] = g;
+    } else {
+        thr = *thr_p;
     }
 #pragma unroll
     for (int u = 0; u < kPackU; ++u) {
@@ -348,17 +374,24 @@ hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
                                                         row_sums);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int64_t total4 = N * K / 4;
+    const unsigned g3 = (unsigned)((total4 + 256 * kPackU - 1) / (256 * kPackU));
+    const uint16_t* Wb = static_cast<const uint16_t*>(W);
+    const float* Wf = static_cast<const float*>(W);
+    if (N <= kFusedGammaMaxN) {
+        if (w_bf16)
+            wq_pack_kernel<uint16_t, true><<<g3, 256, 0, s>>>(Wb, total4, thr, row_sums, N, K, gamma, W_packed);
+        else
+            wq_pack_kernel<float, true><<<g3, 256, 0, s>>>(Wf, total4, thr, row_sums, N, K, gamma, W_packed);
+        return hipGetLastError();
+    }
     wq_gamma_kernel<<<1, kGammaWaves * kWave, 0, s>>>(row_sums, N, K, gamma, thr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t total4 = N * K / 4;
-    const unsigned g3 = (unsigned)((total4 + 256 * kPackU - 1) / (256 * kPackU));
     if (w_bf16)
-        wq_pack_kernel<uint16_t><<<g3, 256, 0, s>>>(static_cast<const uint16_t*>(W), total4, thr,
-                                                     W_packed);
+        wq_pack_kernel<uint16_t, false><<<g3, 256, 0, s>>>(Wb, total4, thr, row_sums, N, K, gamma, W_packed);
     else
-        wq_pack_kernel<float><<<g3, 256, 0, s>>>(static_cast<const float*>(W), total4, thr,
-                                                  W_packed);
+        wq_pack_kernel<float, false><<<g3, 256, 0, s>>>(Wf, total4, thr, row_sums, N, K, gamma, W_packed);
     return hipGetLastError();
 }
 
