@@ -108,16 +108,16 @@ __device__ __forceinline__ v8bf rows_operand(const uint8_t* tile, int kq, int x0
     return *reinterpret_cast<const v8bf*>(tile + rows_slot<T>(x0 + (lane & 31), 2 * kq + (lane >> 5)));
 }
 
-// 16 ternary codes (one packed dword, columns k..k+15) -> 16 bf16 in natural
-// column order (8 dwords, two codes each).  bf16 of a code: low byte 0x80 if
+// 8 ternary codes (the low 16 bits of w: columns k..k+7) -> 8 bf16 in natural
+// column order (4 dwords, two codes each).  bf16 of a code: low byte 0x80 if
 // nonzero, high byte 0x3f (+1) or 0xbf (-1).
-__device__ __forceinline__ void codes16_to_bf16(uint32_t w, uint4 (&o)[2]) {
+__device__ __forceinline__ uint4 codes8_to_bf16(uint32_t w) {
     constexpr uint32_t kHi = 0x00bf3f00u, kLo = 0x00808000u;
     const uint32_t ev = w & 0x33333333u;         // codes 0, 2 of every byte
     const uint32_t od = (w >> 2) & 0x33333333u;  // codes 1, 3 of every byte
-    uint32_t r[8];
+    uint32_t r[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < 2; ++b) {
         // [ev.b, ev.b, od.b, od.b]: codes 4b, 4b+2 (low / high nibble of ev.b), 4b+1, 4b+3
         const uint32_t pb = __builtin_amdgcn_perm(od, ev, (uint32_t)(b | b << 8 | (b + 4) << 16 | (b + 4) << 24));
         const uint32_t s0 = (pb & 0x03030303u) + 0x00040004u;
@@ -125,16 +125,15 @@ __device__ __forceinline__ void codes16_to_bf16(uint32_t w, uint4 (&o)[2]) {
         r[2 * b] = __builtin_amdgcn_perm(kLo, kHi, s0);
         r[2 * b + 1] = __builtin_amdgcn_perm(kLo, kHi, s1);
     }
-    o[0] = make_uint4(r[0], r[1], r[2], r[3]);
-    o[1] = make_uint4(r[4], r[5], r[6], r[7]);
+    return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
-// 16 int8 (4 dwords) times rs -> 16 bf16 (8 dwords)
-__device__ __forceinline__ void int8x16_to_bf16(uint4 q, float rs, uint4 (&o)[2]) {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    uint32_t r[8];
+// 8 int8 (2 dwords) times rs -> 8 bf16 (4 dwords)
+__device__ __forceinline__ uint4 int8x8_to_bf16(uint2 q, float rs) {
+    const uint32_t w[2] = {q.x, q.y};
+    uint32_t r[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < 2; ++d) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             v2bf p;
@@ -143,8 +142,7 @@ __device__ __forceinline__ void int8x16_to_bf16(uint4 q, float rs, uint4 (&o)[2]
             r[2 * d + h] = __builtin_bit_cast(uint32_t, p);
         }
     }
-    o[0] = make_uint4(r[0], r[1], r[2], r[3]);
-    o[1] = make_uint4(r[4], r[5], r[6], r[7]);
+    return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 // Workgroup id -> (tile row, tile column, split), regrouped so that each XCD
@@ -164,22 +162,23 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int sp
     tm = __builtin_amdgcn_readfirstlane(id / splits);
 }
 
-// Staged data of one step (per thread): two 16-byte A chunks as loaded; the
-// B item as loaded (braw: a packed code dword, or 16 int8 with their row's
-// 1/scale_x) and converted to 16 bf16 (bcv) in a compute phase.
+// Staged data of one step (per thread): two 16-byte A chunks as loaded; two
+// B items (8 output columns of one contraction row each) as loaded (braw: 8
+// packed codes, or 8 int8 with their row's 1/scale_x) and converted to 8
+// bf16 (bcv) in a compute phase.
 template <int MODE>
 struct Stage;
 template <>
 struct Stage<kGradX> {
     uint4 a[2];
-    uint32_t braw;
+    uint32_t braw[2];
     uint4 bcv[2];
 };
 template <>
 struct Stage<kGradW> {
     uint4 a[2];
-    uint4 braw;
-    float rs;
+    uint2 braw[2];
+    float rs[2];
     uint4 bcv[2];
 };
 
@@ -263,14 +262,18 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
             aoff[u] = (uint32_t)((row * N + 8 * ch) * 2);
         }
     }
-    // B: one item per thread, 16 output columns of one contraction row.
-    //   grad_x: packed dword j of row bk (codes of 16 columns)
-    //   grad_W: 16 int8 of token bk
-    constexpr int IPR = T::BN / 32;  // items per row of the group's half
-    const int bk = tg / IPR, bj = tg % IPR;
-    const int bcol = wm * (T::BN / 2) + 16 * bj;  // first output column in the tile
-    const bool b_ok = cb + 16 * bj < C;
-    const uint32_t boff = MODE == kGradX ? (uint32_t)(bk * KB + 4 * bj) : (uint32_t)(bk * K + 16 * bj);
+    // B: two items per thread, 8 output columns of one contraction row each;
+    // consecutive lanes take consecutive 8-column pieces of a row, so every
+    // 16-byte LDS store instruction writes contiguous runs (no bank conflict).
+    //   grad_x: 8 packed codes (2 bytes) of row bk;  grad_W: 8 int8 of token bk
+    constexpr int IPR = T::BN / 16;              // items per row of the group's half
+    constexpr int RPP = kGroupThreads / IPR;     // rows per pass over the group
+    static_assert(BK == 2 * RPP, "two B items per thread");
+    const int bk = tg / IPR, bj = tg % IPR;      // rows bk and bk + RPP
+    const int bcol = wm * (T::BN / 2) + 8 * bj;  // first output column in the tile
+    const bool b_ok = cb + 8 * bj < C;
+    const uint32_t boff = MODE == kGradX ? (uint32_t)(bk * KB + 2 * bj) : (uint32_t)(bk * K + 8 * bj);
+    const uint32_t bstep = MODE == kGradX ? (uint32_t)(RPP * KB) : (uint32_t)(RPP * K);
 
     auto load_a = [&](int kb, const __amdgpu_buffer_rsrc_t& ra, int u) -> uint4 {
         // kb: contraction base of the step
@@ -298,39 +301,38 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     };
     auto load_global = [&](int st, Stage<MODE>& p) {
         const int kb = klo + st * BK;
-        const bool bv = b_ok && kb + bk < khi;
         if constexpr (MODE == kGradX) {
             const __amdgpu_buffer_rsrc_t ra = make_buf(gy + (int64_t)rg * N + kb);
             p.a[0] = load_a(kb, ra, 0);
             p.a[1] = load_a(kb, ra, 1);
             const __amdgpu_buffer_rsrc_t rb =
                 make_buf(static_cast<const uint8_t*>(second) + (int64_t)kb * KB + cb / 4);
-            p.braw = buf_load4(rb, bv ? boff : kBufOOB);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool bv = b_ok && kb + bk + h * RPP < khi;
+                p.braw[h] = __builtin_amdgcn_raw_buffer_load_b16(rb, bv ? boff + h * bstep : kBufOOB, 0, 0);
+            }
         } else {
             const __amdgpu_buffer_rsrc_t ra = make_buf(gy + (int64_t)kb * N + rg);
             p.a[0] = load_a(kb, ra, 0);
             p.a[1] = load_a(kb, ra, 1);
             const __amdgpu_buffer_rsrc_t rb =
                 make_buf(static_cast<const int8_t*>(second) + (int64_t)kb * K + cb);
-            p.braw = buf_load16(rb, bv ? boff : kBufOOB);
-            const bool tv = kb + bk < khi;
-            const float sx = aux[tv ? kb + bk : 0];
-            p.rs = tv ? __builtin_amdgcn_rcpf(sx) : 0.0f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool tv = kb + bk + h * RPP < khi;
+                p.braw[h] = buf_load8(rb, b_ok && tv ? boff + h * bstep : kBufOOB);
+                const float sx = aux[tv ? kb + bk + h * RPP : 0];
+                p.rs[h] = tv ? __builtin_amdgcn_rcpf(sx) : 0.0f;
+            }
         }
     };
-    // Conversion to the B tile's bf16 form.  With the pitch (64 B mod 256)
-    // rows bk and bk + 1 of the items' 32-byte slots fall on the same banks;
-    // odd rows therefore store their two halves in swapped order, so each
-    // 16-byte store instruction covers distinct banks.
     auto convert = [&](Stage<MODE>& p) {
-        uint4 o[2];
-        if constexpr (MODE == kGradX) codes16_to_bf16(p.braw, o);
-        else int8x16_to_bf16(p.braw, p.rs, o);
-        const bool sw = bk & 1;  // per-component selects (no indexed array)
-        p.bcv[0] = make_uint4(sw ? o[1].x : o[0].x, sw ? o[1].y : o[0].y, sw ? o[1].z : o[0].z,
-                              sw ? o[1].w : o[0].w);
-        p.bcv[1] = make_uint4(sw ? o[0].x : o[1].x, sw ? o[0].y : o[1].y, sw ? o[0].z : o[1].z,
-                              sw ? o[0].w : o[1].w);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if constexpr (MODE == kGradX) p.bcv[h] = codes8_to_bf16(p.braw[h]);
+            else p.bcv[h] = int8x8_to_bf16(p.braw[h], p.rs[h]);
+        }
     };
     auto store_lds = [&](int st, const Stage<MODE>& p) {
         uint8_t* As = smem_a[wm][st & 1];
@@ -346,10 +348,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
                 *reinterpret_cast<uint4*>(As + row * PA + 16 * ch) = p.a[u];
             }
         }
-        // the item's two 16-byte halves, odd rows in swapped order (see convert)
-        uint8_t* d = Bs + bk * PB + 2 * bcol;
-        *reinterpret_cast<uint4*>(d + 16 * (bk & 1)) = p.bcv[0];
-        *reinterpret_cast<uint4*>(d + 16 * ((bk & 1) ^ 1)) = p.bcv[1];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<uint4*>(Bs + (bk + h * RPP) * PB + 2 * bcol) = p.bcv[h];
     };
 
     v16f acc[IM][JN];
