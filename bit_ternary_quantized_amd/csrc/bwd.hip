@@ -32,8 +32,9 @@
 // a tile written in a group's memory phase of step s is read in memory phases
 // s + 1 of both groups, and its buffer is rewritten only at step s + 2.
 //
-// Small outputs (fewer than 256 large tiles) use 128 x 128 tiles; grad_W
-// then also splits its token range, and a second kernel adds the fp32
+// Small outputs (fewer than 256 large tiles) use 128 x 128 tiles (grad_W with
+// the contraction split between the wave groups, see Tile); grad_W then also
+// splits its token range over workgroups, and a second kernel adds the fp32
 // partial tiles in split order (deterministic).
 #include "common.h"
 
@@ -51,24 +52,41 @@ enum { kGradX = 0, kGradW = 1 };
 constexpr int kThreads = 512;
 constexpr int kGroupThreads = 256;
 
-template <int BM_, int BN_, int BK_>
+// Tile shapes.  The workgroup's two wave groups either split the output
+// rows (each group: BM/2 rows, its four waves side by side along the
+// columns; the B tile is shared, each group staging half of it), or, with
+// KSPLIT, split the contraction: group g takes every other step, covers the
+// whole BM x BN tile with its four waves as 2 x 2, stages its own tiles, and
+// the two partial tiles are added once at the end.  The latter gives each
+// wave a square 64 x 64 accumulator block, which needs a quarter fewer LDS
+// bytes per MFMA than a 64 x 32 one.
+template <int BM_, int BN_, int BK_, bool KSPLIT_>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
-    static constexpr int HM = BM / 2;   // output rows per group
-    static constexpr int WTN = BN / 4;  // output columns per wave
-    static constexpr int IM = HM / 32, JN = WTN / 32;
+    static constexpr bool KSPLIT = KSPLIT_;
+    static constexpr int GROWS = KSPLIT ? BM : BM / 2;   // output rows of a group
+    static constexpr int GBCOLS = KSPLIT ? BN : BN / 2;  // B columns a group stages
+    static constexpr int WAVES_M = KSPLIT ? 2 : 1, WAVES_N = 4 / WAVES_M;
+    static constexpr int WTM = GROWS / WAVES_M;          // wave tile rows
+    static constexpr int WTN = BN / WAVES_N;             // wave tile columns
+    static constexpr int IM = WTM / 32, JN = WTN / 32;
     static constexpr int KQ = BK / 16;  // MFMA k-steps per step
-    // "rows" tile: HM rows x BK bf16 (2*BK bytes), 16-byte chunks swizzled
+    static constexpr int MFMAS = IM * JN * KQ;
+    // "rows" tile: GROWS rows x BK bf16 (2*BK bytes), 16-byte chunks swizzled
     static constexpr int CPR = 2 * BK / 16;
-    static constexpr int ROWS_BYTES = HM * 2 * BK;
+    static constexpr int ROWS_BYTES = GROWS * 2 * BK;
+    // staged per thread and step: A chunks (8 elements) and B items (8 columns)
+    static constexpr int NA = GROWS * BK / 8 / 256;
+    static constexpr int NB = BK * (GBCOLS / 8) / 256;
     // "cols" tile of width W: BK rows, pitch 2W + 64 bytes (64 or 192 mod
     // 256, so the 32 8-byte pieces of each transposing read hit 32 distinct
     // bank pairs)
     static constexpr int pitch(int W) { return 2 * W + 64; }
     static constexpr int cols_bytes(int W) { return BK * pitch(W); }
 };
-using TileL = Tile<256, 256, 32>;
-using TileS = Tile<128, 128, 64>;
+using TileL = Tile<256, 256, 32, false>;
+using TileS = Tile<128, 128, 64, false>;   // small outputs, grad_x
+using TileSK = Tile<128, 128, 64, true>;  // small outputs, grad_W (measured faster)
 
 // Chunk c of row r of a "rows" tile: each 256-byte bank window holds 16/CPR
 // rows; XOR-ing the chunk index with the window index gives every 16-lane
@@ -162,24 +180,24 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int sp
     tm = __builtin_amdgcn_readfirstlane(id / splits);
 }
 
-// Staged data of one step (per thread): two 16-byte A chunks as loaded; two
+// Staged data of one step (per thread): NA 16-byte A chunks as loaded; NB
 // B items (8 output columns of one contraction row each) as loaded (braw: 8
 // packed codes, or 8 int8 with their row's 1/scale_x) and converted to 8
 // bf16 (bcv) in a compute phase.
-template <int MODE>
+template <int MODE, int NA, int NB>
 struct Stage;
-template <>
-struct Stage<kGradX> {
-    uint4 a[2];
-    uint32_t braw[2];
-    uint4 bcv[2];
+template <int NA, int NB>
+struct Stage<kGradX, NA, NB> {
+    uint4 a[NA];
+    uint32_t braw[NB];
+    uint4 bcv[NB];
 };
-template <>
-struct Stage<kGradW> {
-    uint4 a[2];
-    uint2 braw[2];
-    float rs[2];
-    uint4 bcv[2];
+template <int NA, int NB>
+struct Stage<kGradW, NA, NB> {
+    uint4 a[NA];
+    uint2 braw[NB];
+    float rs[NB];
+    uint4 bcv[NB];
 };
 
 }  // namespace
@@ -195,14 +213,17 @@ template <int MODE, class T, bool VEC, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(
     const uint16_t* __restrict__ gy, const void* __restrict__ second, const float* __restrict__ aux,
     int M, int N, int K, int splits, int kper, void* __restrict__ out) {
-    constexpr int BK = T::BK, HM = T::HM, IM = T::IM, JN = T::JN, KQ = T::KQ;
-    constexpr int PB = T::pitch(T::BN);  // shared B tile
-    constexpr int PA = T::pitch(HM);     // grad_W A tile
-    constexpr int A_BYTES = MODE == kGradX ? T::ROWS_BYTES : T::cols_bytes(HM);
+    constexpr int BK = T::BK, GROWS = T::GROWS, IM = T::IM, JN = T::JN, KQ = T::KQ;
+    constexpr int NA = T::NA, NB = T::NB;
+    constexpr bool KS = T::KSPLIT;
+    constexpr int PB = T::pitch(T::BN);  // B tile
+    constexpr int PA = T::pitch(GROWS);  // grad_W A tile
+    constexpr int A_BYTES = MODE == kGradX ? T::ROWS_BYTES : T::cols_bytes(GROWS);
     constexpr int B_BYTES = T::cols_bytes(T::BN);
-    constexpr int CPA = HM / 8;          // grad_W: 8-element gy chunks per A row
-    __shared__ __align__(16) uint8_t smem_a[2][2][A_BYTES];  // [group][buffer]
-    __shared__ __align__(16) uint8_t smem_b[2][B_BYTES];     // [buffer]
+    constexpr int CPA = GROWS / 8;       // grad_W: 8-element gy chunks per A row
+    constexpr int NBUF_B = KS ? 2 : 1;   // B tiles per buffer: per group, or one shared
+    __shared__ __align__(16) uint8_t smem_a[2][2][A_BYTES];       // [group][buffer]
+    __shared__ __align__(16) uint8_t smem_b[NBUF_B][2][B_BYTES];  // [group or 0][buffer]
 
     // grad_W A chunk c -> (token row, 8-column chunk).  Rows of 16 chunks:
     // 16 lanes per row.  Rows of 8 chunks (pitch 192): each 16-lane group
@@ -232,20 +253,27 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     const int wm = wave >> 2, wn = wave & 3;  // wm: the wave group
     const int tg = t & (kGroupThreads - 1);
     const int KB = K / 4;
-    const int rg = r0 + wm * HM;           // first output row of the group
-    const int cb = c0 + wm * (T::BN / 2);  // first column of the group's B half
+    const int rg = r0 + (KS ? 0 : wm * GROWS);    // first output row of the group
+    const int cb = c0 + (KS ? 0 : wm * T::GBCOLS);  // first column the group stages
+    const int wr = KS ? (wn >> 1) * T::WTM : 0;     // wave tile origin in the group
+    const int wc = (KS ? (wn & 1) : wn) * T::WTN;
+    // the group's steps: all of them, or (KSPLIT) every other one
+    const int nsteps_g = KS ? (nsteps + 1 - wm) / 2 : nsteps;
+    auto kstep = [&](int i) { return KS ? 2 * i + wm : i; };
+    uint8_t* const smem_bg = &smem_b[KS ? wm : 0][0][0];
+    auto bbuf = [&](int i) { return smem_bg + (i & 1) * B_BYTES; };
 
     // ---- per-thread staging geometry; offsets are relative to the step's
     // base address (which moves by BK along the contraction)
-    // A chunks u = 0, 1 (c = tg + 256 u): 8 consecutive gy elements.
+    // A chunks u (c = tg + 256 u): 8 consecutive gy elements.
     //   grad_x: row rg + c / CPR, contraction 8 * (c % CPR) of the step
-    //   grad_W: token c / CPA of the step, columns rg + 8 * (c % CPA)
-    uint32_t aoff[2];
-    int a_k[2];    // contraction index of the chunk's first element (in the step)
-    int a_lim[2];  // grad_x: row valid; grad_W: columns left in the row
-    bool a_ok[2];
+    //   grad_W: token row of the step, columns rg + 8 * ch (a_chunk)
+    uint32_t aoff[NA];
+    int a_k[NA];    // contraction index of the chunk's first element (in the step)
+    int a_lim[NA];  // grad_W: columns left in the row
+    bool a_ok[NA];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NA; ++u) {
         const int c = tg + u * kGroupThreads;
         if constexpr (MODE == kGradX) {
             const int row = c / T::CPR, ch = c % T::CPR;
@@ -262,15 +290,15 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
             aoff[u] = (uint32_t)((row * N + 8 * ch) * 2);
         }
     }
-    // B: two items per thread, 8 output columns of one contraction row each;
+    // B: NB items per thread, 8 output columns of one contraction row each;
     // consecutive lanes take consecutive 8-column pieces of a row, so every
     // 16-byte LDS store instruction writes contiguous runs (no bank conflict).
     //   grad_x: 8 packed codes (2 bytes) of row bk;  grad_W: 8 int8 of token bk
-    constexpr int IPR = T::BN / 16;              // items per row of the group's half
-    constexpr int RPP = kGroupThreads / IPR;     // rows per pass over the group
-    static_assert(BK == 2 * RPP, "two B items per thread");
-    const int bk = tg / IPR, bj = tg % IPR;      // rows bk and bk + RPP
-    const int bcol = wm * (T::BN / 2) + 8 * bj;  // first output column in the tile
+    constexpr int IPR = T::GBCOLS / 8;            // items per staged row
+    constexpr int RPP = kGroupThreads / IPR;      // rows per pass over the group
+    static_assert(BK == NB * RPP, "B items cover the step");
+    const int bk = tg / IPR, bj = tg % IPR;       // rows bk + h * RPP
+    const int bcol = (cb - c0) + 8 * bj;          // first output column in the tile
     const bool b_ok = cb + 8 * bj < C;
     const uint32_t boff = MODE == kGradX ? (uint32_t)(bk * KB + 2 * bj) : (uint32_t)(bk * K + 8 * bj);
     const uint32_t bstep = MODE == kGradX ? (uint32_t)(RPP * KB) : (uint32_t)(RPP * K);
@@ -299,27 +327,29 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
             return make_uint4(w[0], w[1], w[2], w[3]);
         }
     };
-    auto load_global = [&](int st, Stage<MODE>& p) {
-        const int kb = klo + st * BK;
+    using StageT = Stage<MODE, NA, NB>;
+    // i: the group's step index
+    auto load_global = [&](int i, StageT& p) {
+        const int kb = klo + kstep(i) * BK;
         if constexpr (MODE == kGradX) {
             const __amdgpu_buffer_rsrc_t ra = make_buf(gy + (int64_t)rg * N + kb);
-            p.a[0] = load_a(kb, ra, 0);
-            p.a[1] = load_a(kb, ra, 1);
+#pragma unroll
+            for (int u = 0; u < NA; ++u) p.a[u] = load_a(kb, ra, u);
             const __amdgpu_buffer_rsrc_t rb =
                 make_buf(static_cast<const uint8_t*>(second) + (int64_t)kb * KB + cb / 4);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < NB; ++h) {
                 const bool bv = b_ok && kb + bk + h * RPP < khi;
                 p.braw[h] = __builtin_amdgcn_raw_buffer_load_b16(rb, bv ? boff + h * bstep : kBufOOB, 0, 0);
             }
         } else {
             const __amdgpu_buffer_rsrc_t ra = make_buf(gy + (int64_t)kb * N + rg);
-            p.a[0] = load_a(kb, ra, 0);
-            p.a[1] = load_a(kb, ra, 1);
+#pragma unroll
+            for (int u = 0; u < NA; ++u) p.a[u] = load_a(kb, ra, u);
             const __amdgpu_buffer_rsrc_t rb =
                 make_buf(static_cast<const int8_t*>(second) + (int64_t)kb * K + cb);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < NB; ++h) {
                 const bool tv = kb + bk + h * RPP < khi;
                 p.braw[h] = buf_load8(rb, b_ok && tv ? boff + h * bstep : kBufOOB);
                 const float sx = aux[tv ? kb + bk + h * RPP : 0];
@@ -327,18 +357,18 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
             }
         }
     };
-    auto convert = [&](Stage<MODE>& p) {
+    auto convert = [&](StageT& p) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < NB; ++h) {
             if constexpr (MODE == kGradX) p.bcv[h] = codes8_to_bf16(p.braw[h]);
             else p.bcv[h] = int8x8_to_bf16(p.braw[h], p.rs[h]);
         }
     };
-    auto store_lds = [&](int st, const Stage<MODE>& p) {
-        uint8_t* As = smem_a[wm][st & 1];
-        uint8_t* Bs = smem_b[st & 1];
+    auto store_lds = [&](int i, const StageT& p) {
+        uint8_t* As = smem_a[wm][i & 1];
+        uint8_t* Bs = bbuf(i);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < NA; ++u) {
             const int c = tg + u * kGroupThreads;
             if constexpr (MODE == kGradX)
                 *reinterpret_cast<uint4*>(As + rows_slot<T>(c / T::CPR, c % T::CPR)) = p.a[u];
@@ -349,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
             }
         }
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NB; ++h)
             *reinterpret_cast<uint4*>(Bs + (bk + h * RPP) * PB + 2 * bcol) = p.bcv[h];
     };
 
@@ -362,17 +392,17 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     v8bf a[KQ][IM], b[KQ][JN];
-    auto read_operands = [&](int st) {
-        const uint8_t* As = smem_a[wm][st & 1];
-        const uint8_t* Bs = smem_b[st & 1];
+    auto read_operands = [&](int i) {
+        const uint8_t* As = smem_a[wm][i & 1];
+        const uint8_t* Bs = bbuf(i);
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
 #pragma unroll
-            for (int j = 0; j < JN; ++j) b[kq][j] = cols_operand<PB>(Bs, 16 * kq, wn * T::WTN + j * 32, lane);
+            for (int j = 0; j < JN; ++j) b[kq][j] = cols_operand<PB>(Bs, 16 * kq, wc + j * 32, lane);
 #pragma unroll
-            for (int i = 0; i < IM; ++i) {
-                if constexpr (MODE == kGradX) a[kq][i] = rows_operand<T>(As, kq, i * 32, lane);
-                else a[kq][i] = cols_operand<PA>(As, 16 * kq, i * 32, lane);
+            for (int ii = 0; ii < IM; ++ii) {
+                if constexpr (MODE == kGradX) a[kq][ii] = rows_operand<T>(As, kq, wr + ii * 32, lane);
+                else a[kq][ii] = cols_operand<PA>(As, 16 * kq, wr + ii * 32, lane);
             }
         }
     };
@@ -382,33 +412,38 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // One step: memory phase = operands of step st, tile st + 1 (loaded two
-    // steps ago, converted since) into LDS, loads of step st + 3 into the
-    // freed staging set; compute phase = the MFMAs, with the conversion of
-    // the other staging set (stored next step) between them.
-    auto step = [&](int st, Stage<MODE>& cur, Stage<MODE>& nx) {
-        read_operands(st);
-        store_lds(st + 1, cur);
-        load_global(st + 3, cur);
+    // One step of the group (its i-th): memory phase = operands of step i,
+    // step i + 1 (loaded two steps ago, converted since) into LDS, loads of
+    // step i + 3 into the freed staging set; compute phase = the MFMAs, with
+    // the conversion of the other staging set (stored next step) between
+    // them.  Past the group's last step the loads read zeros, which add
+    // nothing.
+    auto step = [&](int i, StageT& cur, StageT& nx) {
+        read_operands(i);
+        store_lds(i + 1, cur);
+        load_global(i + 3, cur);
         barrier();
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq)
 #pragma unroll
-            for (int i = 0; i < IM; ++i)
+            for (int ii = 0; ii < IM; ++ii)
 #pragma unroll
                 for (int j = 0; j < JN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kq][i], b[kq][j], acc[i][j], 0, 0, 0);
+                    acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kq][ii], b[kq][j], acc[ii][j], 0, 0, 0);
         convert(nx);
         __builtin_amdgcn_s_setprio(0);
         barrier();
     };
 
-    // Prologue: step 0 in LDS buffer 0, steps 1 and 2 loading.  Group 1 then
-    // waits one extra barrier, which puts it a phase behind group 0.
-    Stage<MODE> s0, s1;
+    // Prologue: the group's step 0 in LDS buffer 0, steps 1 and 2 loading.
+    // Group 1 then waits one extra barrier, which puts it a phase behind
+    // group 0.  Both groups run the same number of loop steps (a group with
+    // fewer real steps runs zero tiles), so every wave passes the same number
+    // of barriers.
+    StageT s0, s1;
     {
-        Stage<MODE> p0;
+        StageT p0;
         load_global(0, p0);
         convert(p0);
         store_lds(0, p0);
@@ -418,31 +453,56 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     convert(s1);
     barrier();
     if (wm == 1) barrier();
-    // unrolled by two (staging sets alternate by name); with nsteps odd the
-    // last step runs on zero tiles (loads past the range read zeros)
-    for (int st = 0; st < nsteps; st += 2) {
-        step(st, s1, s0);
-        step(st + 1, s0, s1);
+    const int nloop = KS ? (nsteps + 1) / 2 : nsteps;  // the larger group's step count
+    (void)nsteps_g;
+    for (int i = 0; i < nloop; i += 2) {
+        step(i, s1, s0);
+        step(i + 1, s0, s1);
     }
-    if (wm == 0) barrier();  // every wave passes the same number of barriers
+    if (wm == 0) barrier();
+
+    // ---- KSPLIT: group 1 hands its partial tile to group 0 through LDS
+    // (the A buffers, no longer read), lane-contiguous so the accesses are
+    // conflict-free; group 0 adds (fixed order: own + other).
+    const int g = lane >> 5, l32 = lane & 31;
+    if constexpr (KS) {
+        static_assert(IM * JN * 16 * 64 * 4 * 4 <= sizeof(smem_a), "partial tiles fit the A buffers");
+        float* xfer = reinterpret_cast<float*>(&smem_a[0][0][0]);
+        float* mine = xfer + wn * (IM * JN * 16 * 64);
+        if (wm == 1) {
+#pragma unroll
+            for (int ii = 0; ii < IM; ++ii)
+#pragma unroll
+                for (int j = 0; j < JN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mine[((ii * JN + j) * 16 + r) * 64 + lane] = acc[ii][j][r];
+        }
+        barrier();
+        if (wm == 1) return;  // uniform per wave; no barrier follows
+#pragma unroll
+        for (int ii = 0; ii < IM; ++ii)
+#pragma unroll
+            for (int j = 0; j < JN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[ii][j][r] += mine[((ii * JN + j) * 16 + r) * 64 + lane];
+    }
 
     // ---- epilogue: 32x32 block layout, lane holds column l32 and rows
     // 8*(r/4) + 4*g + r%4
-    const int g = lane >> 5, l32 = lane & 31;
     const float scale = MODE == kGradX ? *aux : 1.0f;
     float* outf = static_cast<float*>(out);
     if constexpr (MODE == kGradW) outf += (int64_t)sp * N * K;
 #pragma unroll
-    for (int i = 0; i < IM; ++i) {
+    for (int ii = 0; ii < IM; ++ii) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = rg + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const int row = rg + wr + ii * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
             if (row < R) {
 #pragma unroll
                 for (int j = 0; j < JN; ++j) {
-                    const int col = c0 + wn * T::WTN + j * 32 + l32;
+                    const int col = c0 + wc + j * 32 + l32;
                     if (col < C) {
-                        const float v = acc[i][j][r] * scale;
+                        const float v = acc[ii][j][r] * scale;
                         if constexpr (MODE == kGradX && OUT_BF16)
                             static_cast<__bf16*>(out)[(int64_t)row * C + col] = (__bf16)v;
                         else
@@ -549,7 +609,7 @@ hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* sca
         const Plan p = plan_for(N, K, M, true);
         void* dst = p.splits > 1 ? ws : static_cast<void*>(grad_W);
         hipError_t e = p.big ? launch_one<kGradW, TileL, false>(gy, Xq, scale_x, m, n, k, p, dst, s)
-                             : launch_one<kGradW, TileS, false>(gy, Xq, scale_x, m, n, k, p, dst, s);
+                             : launch_one<kGradW, TileSK, false>(gy, Xq, scale_x, m, n, k, p, dst, s);
         if (e != hipSuccess) return e;
         if (p.splits > 1) {
             const int64_t count = N * K;
