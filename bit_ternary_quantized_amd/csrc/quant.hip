@@ -57,21 +57,55 @@ __global__ __launch_bounds__(kAqWaves * kWave) void act_quant_kernel(
         return wave_tree_sum(lane_tree<E>(sq));
     };
 
+    // The row cache holds the 16 loaded bytes per block as they are (8 bf16
+    // in 4 registers rather than 8 floats), widened to float where used, so
+    // twice as many waves fit when the input is bf16.
+    auto load_raw = [&](int64_t b) -> uint4 {
+        const int64_t k0 = b * BLK + (int64_t)lane * E;
+        if (vec_ok && k0 + E <= K) return *reinterpret_cast<const uint4*>(x + k0);
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (k0 + e < K) w[e] = __float_as_uint(load_elem(x, k0 + e));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (k0 + e < K) w[e / 2] |= (uint32_t)x[k0 + e] << (16 * (e % 2));
+        }
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    };
+    auto widen = [](const uint4& r, float (&v)[E]) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __uint_as_float(w[i] << 16);
+                v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            }
+        }
+    };
+
     float amax = 0.0f;
     float ss;
-    float cache[NB > 0 ? NB : 1][E];
+    uint4 cache[NB > 0 ? NB : 1];
     if constexpr (NB > 0) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            if (b < nblk) load_block(b, cache[b]);
+            if (b < nblk) cache[b] = load_raw(b);
         }
         float bs[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             if (b < nblk) {
-                bs[b] = block_sq_sum(cache[b]);
+                float v[E];
+                widen(cache[b], v);
+                bs[b] = block_sq_sum(v);
 #pragma unroll
-                for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(cache[b][e]));
+                for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
             } else {
                 bs[b] = 0.0f;
             }
@@ -136,8 +170,16 @@ __global__ __launch_bounds__(kAqWaves * kWave) void act_quant_kernel(
 
     if constexpr (NB > 0) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            if (b < nblk) quant_store(b, cache[b]);
+        for (int b = 0; b < NB; ++b) {
+            // an empty register constraint: the compiler cannot reuse the
+            // floats widened for the sums (which would keep all of them live)
+            asm volatile("" : "+v"(cache[b].x), "+v"(cache[b].y), "+v"(cache[b].z), "+v"(cache[b].w));
+            if (b < nblk) {
+                float v[E];
+                widen(cache[b], v);
+                quant_store(b, v);
+            }
+        }
     } else {
         for (int64_t b = 0; b < nblk; ++b) {
             float v[E];
@@ -296,10 +338,11 @@ __device__ __forceinline__ uint32_t code_bits(float w, float thr) {
 }
 
 constexpr int kPackU = 4;  // groups of 4 weights per thread (loads in flight)
-// Up to this many rows, every pack workgroup evaluates gamma and the
-// threshold itself from the row sums (one launch fewer); above it a single
-// workgroup does and the pack kernel reads the threshold.
-constexpr int64_t kFusedGammaMaxN = 8192;
+// When (rows x pack workgroups) is at most this, every pack workgroup
+// evaluates gamma and the threshold itself from the row sums (one launch
+// fewer, for small matrices); otherwise a single workgroup does and the pack
+// kernel reads the threshold.
+constexpr int64_t kFusedGammaMaxWork = (int64_t)1 << 22;
 
 // FUSED: the threshold is computed here from the row sums (block 0 also
 // writes gamma); otherwise it is read from thr_p.
@@ -378,7 +421,7 @@ hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
     const unsigned g3 = (unsigned)((total4 + 256 * kPackU - 1) / (256 * kPackU));
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
     const float* Wf = static_cast<const float*>(W);
-    if (N <= kFusedGammaMaxN) {
+    if (N * (int64_t)g3 <= kFusedGammaMaxWork) {
         if (w_bf16)
             wq_pack_kernel<uint16_t, true><<<g3, 256, 0, s>>>(Wb, total4, thr, row_sums, N, K, gamma, W_packed);
         else
