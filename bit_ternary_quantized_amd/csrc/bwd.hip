@@ -502,11 +502,12 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
                 for (int j = 0; j < JN; ++j) {
                     const int col = c0 + wc + j * 32 + l32;
                     if (col < C) {
+                        // streaming (non-temporal) stores: the output is not read again here
                         const float v = acc[ii][j][r] * scale;
                         if constexpr (MODE == kGradX && OUT_BF16)
-                            static_cast<__bf16*>(out)[(int64_t)row * C + col] = (__bf16)v;
+                            __builtin_nontemporal_store((__bf16)v, &static_cast<__bf16*>(out)[(int64_t)row * C + col]);
                         else
-                            outf[(int64_t)row * C + col] = v;
+                            __builtin_nontemporal_store(v, &outf[(int64_t)row * C + col]);
                     }
                 }
             }

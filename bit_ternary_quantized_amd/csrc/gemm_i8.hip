@@ -322,7 +322,9 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
 #pragma unroll
                 for (int j = 0; j < JN; ++j) {
                     const int cloc = cbase + j * 32;
-                    if (!GUARD || (rloc < mlim && cloc < nlim)) out[roff + cloc] = value(acc[i][j][r], rs);
+                    // streaming (non-temporal) stores: the output is not read again here
+                    if (!GUARD || (rloc < mlim && cloc < nlim))
+                        __builtin_nontemporal_store(value(acc[i][j][r], rs), &out[roff + cloc]);
                 }
             }
             // keep the scheduler from pulling later accumulators forward
