@@ -37,7 +37,7 @@ constexpr int kMaxGroups = 4;  // row groups per pass when S <= 4
 // S: MFMA steps (64 columns) per wave, Kw = 64*S; FULL: K == 16*Kw, so every
 // lane's column range lies inside the row and loads are 16-byte vectors.
 // STAGE: the activations come in with coalesced 16-byte loads through an LDS
-// tile (M > 4: 16 token rows would otherwise be fetched as scattered pieces
+// tile (M > 8: 16 token rows would otherwise be fetched as scattered pieces
 // by every lane); without it each lane loads its own chunks (few tokens).
 constexpr int kStageMaxK = 4096;  // LDS activation tile bound
 constexpr int kStageStride = kStageMaxK + 16;
@@ -194,7 +194,7 @@ hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t*
     const unsigned grid = (unsigned)std::min<int64_t>(ngroups, 256);
     const int64_t steps = (K + 16 * 64 - 1) / (16 * 64);  // MFMA steps per wave
     const bool full = K % (16 * 64) == 0;
-    const bool stage = M > 4 && K <= kStageMaxK;
+    const bool stage = M > 8 && K <= kStageMaxK;  // measured: direct loads win up to 8 tokens
 #define BITNET_GEMV_LAUNCH(S_, F_, G_)                                                          \
     gemv_t2_kernel<S_, F_, G_><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, \
                                                         (int)K, Y, acc)
