@@ -182,8 +182,9 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int sp
 
 // Staged data of one step (per thread): NA 16-byte A chunks as loaded; NB
 // B items (8 output columns of one contraction row each) as loaded (braw: 8
-// packed codes, or 8 int8 with their row's 1/scale_x) and converted to 8
-// bf16 (bcv) in a compute phase.
+// packed codes, or 8 int8 with their row's scale_x, 0 past the token range)
+// and converted to 8 bf16 (bcv) in a compute phase.  Nothing loaded is used
+// in the phase that loads it (1/scale_x included), so no wait there.
 template <int MODE, int NA, int NB>
 struct Stage;
 template <int NA, int NB>
@@ -196,7 +197,7 @@ template <int NA, int NB>
 struct Stage<kGradW, NA, NB> {
     uint4 a[NA];
     uint2 braw[NB];
-    float rs[NB];
+    float sx[NB];
     uint4 bcv[NB];
 };
 
@@ -348,12 +349,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
             for (int u = 0; u < NA; ++u) p.a[u] = load_a(kb, ra, u);
             const __amdgpu_buffer_rsrc_t rb =
                 make_buf(static_cast<const int8_t*>(second) + (int64_t)kb * K + cb);
+            const __amdgpu_buffer_rsrc_t rs = make_buf(aux + kb);
 #pragma unroll
             for (int h = 0; h < NB; ++h) {
                 const bool tv = kb + bk + h * RPP < khi;
                 p.braw[h] = buf_load8(rb, b_ok && tv ? boff + h * bstep : kBufOOB);
-                const float sx = aux[tv ? kb + bk + h * RPP : 0];
-                p.rs[h] = tv ? __builtin_amdgcn_rcpf(sx) : 0.0f;
+                p.sx[h] = __builtin_bit_cast(
+                    float, buf_load4(rs, tv ? (uint32_t)(4 * (bk + h * RPP)) : kBufOOB));
             }
         }
     };
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
 #pragma unroll
         for (int h = 0; h < NB; ++h) {
             if constexpr (MODE == kGradX) p.bcv[h] = codes8_to_bf16(p.braw[h]);
-            else p.bcv[h] = int8x8_to_bf16(p.braw[h], p.rs[h]);
+            else p.bcv[h] = int8x8_to_bf16(p.braw[h], p.sx[h] > 0.0f ? __builtin_amdgcn_rcpf(p.sx[h]) : 0.0f);
         }
     };
     auto store_lds = [&](int i, const StageT& p) {
