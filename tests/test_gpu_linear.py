@@ -94,6 +94,39 @@ def test_linear_bwd_ste(M, N, K, gx_dtype):
     assert_grad_close(gw.cpu().numpy(), gw_ref, "grad_W")
 
 
+# grad_W of these splits its token range over workgroups (fewer than 256
+# output tiles, at least 1024 tokens): 4 even splits, 2 with a ragged last
+# split and ragged tile edges, 5 with a short last split.  The workspace
+# starts as 0xff bytes (its contents on entry must not matter), and grad_W
+# is also computed alone.
+SPLIT_SHAPES = [(2048, 100, 48), (1100, 257, 272), (3000, 130, 144)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_linear_bwd_token_split(M, N, K):
+    print(f"linear_bwd token split M={M} N={N} K={K}", flush=True)
+    q, codes, scale_x, gamma = _quantized_operands(M, N, K, seed=M + 7 * N + K)
+    gy = workloads.normal((M, N), 1e-3, seed=M + 2 * N, dtype="bf16")
+    wp = to_dev(torch.from_numpy(oracle.pack(codes.numpy())))
+    nws = bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, M, N, K)
+    assert nws > 0
+    ws = torch.full((nws,), 255, dtype=torch.uint8, device="cuda")
+    args = (to_dev(gy), to_dev(q), to_dev(scale_x), wp, to_dev(gamma))
+    gw_ref = oracle.ste_grad_w(host(gy), q.numpy(), scale_x.numpy())
+    gx, gw = bt.bitnet_linear_bwd_ste(*args, workspace=ws)
+    torch.cuda.synchronize()
+    assert_grad_close(gx.cpu().numpy(), oracle.ste_grad_x(host(gy), codes.numpy(), float(gamma[0])), "grad_x")
+    assert_grad_close(gw.cpu().numpy(), gw_ref, "grad_W")
+    first = gw.cpu().numpy()
+    ws.fill_(255)
+    _, gw2 = bt.bitnet_linear_bwd_ste(*args, want_grad_x=False, workspace=ws)
+    _, gw3 = bt.bitnet_linear_bwd_ste(*args, want_grad_x=False, workspace=ws)
+    torch.cuda.synchronize()
+    # the split partials are added in split order: identical bits every call
+    assert np.array_equal(gw2.cpu().numpy(), first)
+    assert np.array_equal(gw3.cpu().numpy(), first)
+
+
 def test_linear_bwd_single_outputs():
     M, N, K = 70, 90, 128
     q, codes, scale_x, gamma = _quantized_operands(M, N, K, seed=9)
