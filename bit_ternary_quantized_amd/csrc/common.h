@@ -89,19 +89,42 @@ __device__ __forceinline__ float lane_tree(const float (&v)[E]) {
     return t[0];
 }
 
-// xor butterfly over the 64 lanes: lane l and lane l^m add the same two
-// partial sums (commutative, so bit-identical), which is the tree over the
-// lanes in lane order.  Every lane ends with the total.
+// The tree over the 64 lanes in lane order; every lane ends with the total.
+// Level m adds each lane's subtree sum to its sibling's (lane l ^ m), so the
+// two lanes of a pair add the same two values (commutative: identical bits).
+// Levels 1 and 2 read the sibling with a DPP quad permutation.  Levels 4 and
+// 8: every lane of an aligned group of m already holds that group's sum, so
+// any lane of the sibling group will do, and the row half-mirror (lane i of
+// 8 reads 7 - i) and row mirror (i of 16 reads 15 - i) reach one.  The last
+// two levels add the four 16-lane sums read from lanes 0, 16, 32, 48.
+// Every lane must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_read(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+__device__ __forceinline__ float lane_read(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 __device__ __forceinline__ float wave_tree_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < kWave; m *= 2) v = v + __shfl_xor(v, m, kWave);
-    return v;
+    v = v + dpp_read<kDppXor1>(v);
+    v = v + dpp_read<kDppXor2>(v);
+    v = v + dpp_read<kDppHalfMirror>(v);
+    v = v + dpp_read<kDppMirror>(v);
+    return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 1; m < kWave; m *= 2) v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
+    v = fmaxf(v, dpp_read<kDppXor1>(v));
+    v = fmaxf(v, dpp_read<kDppXor2>(v));
+    v = fmaxf(v, dpp_read<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_read<kDppMirror>(v));
+    return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
 }
 
 // Pairwise combination of a stream of equal-size, consecutive, aligned
