@@ -130,7 +130,7 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
 
 
 KERNEL_OF = {
-    "act_quant": "act_quant_kernel",
+    "act_quant": "act_quant_rows_kernel (rows of whole 16-byte blocks), else act_quant_kernel",
     "weight_quant": "wq_row_abs_sum_kernel + wq_gamma_kernel + wq_pack_kernel",
     "linear_fwd": "gemm_i8t2_kernel",
     "bwd_grad_x": "bwd_kernel<grad_x>",
