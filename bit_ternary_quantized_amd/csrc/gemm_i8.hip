@@ -96,248 +96,262 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
     __shared__ __align__(16) uint8_t smem_b[2][2][B_BYTES];  // [group][block buffer]
     __shared__ float row_scale[BM];
 
-    int tm, tn;
-    tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform in the wave
-    const int wm = wave >> 2, wn = wave & 3;                   // wm: the wave group
-    const int tg = t & (kGroupThreads - 1);                    // thread inside the group
-    const int KB = K / 4;                                      // packed bytes per weight row
-    const int nk = (K + BK - 1) / BK;
+    // Persistent: workgroup b takes tiles b, b + grid, ...  (the grid is at
+    // most one workgroup per CU), so the y stores of one tile drain while
+    // the next tile's loads and MFMAs run instead of ending every round of
+    // workgroups with a write burst.  Tile v maps as workgroup v would in a
+    // one-tile-per-workgroup launch (same XCD when the grid is a multiple
+    // of 8).
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    for (int tile = blockIdx.x; tile < tiles_m * tiles_n; tile += gridDim.x) {
+        int tm, tn;
+        tile_of(tile, tiles_m, tiles_n, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int t = threadIdx.x;
+        const int lane = t & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform in the wave
+        const int wm = wave >> 2, wn = wave & 3;                   // wm: the wave group
+        const int tg = t & (kGroupThreads - 1);                    // thread inside the group
+        const int KB = K / 4;                                      // packed bytes per weight row
+        const int nk = (K + BK - 1) / BK;
 
-    {
-        const float g = *gamma_p;
-        if (t < BM) row_scale[t] = (m0 + t < M) ? g / scale_x[m0 + t] : 0.0f;
-    }
-
-    // Activations: thread tg stages chunks tg + 256 u (row c / 4, chunk c % 4)
-    // of the group's 128 rows; offsets relative to the step's base address.
-    const int mh = m0 + wm * HM;  // first row of the group's half
-    uint32_t aoff[kAPer];
-    int acol[kAPer];
-#pragma unroll
-    for (int u = 0; u < kAPer; ++u) {
-        const int c = tg + u * kGroupThreads;
-        const int row = c >> 2;
-        acol[u] = (c & 3) * 16;
-        aoff[u] = mh + row < M ? (uint32_t)(row * K + acol[u]) : kBufOOB;
-    }
-    const int8_t* Xt = Xq + (int64_t)mh * K;
-    // Weights: in a quarter, thread tg stages slice bc = tg % 4 of row
-    // bq = tg / 4 (+ 64 per quarter), both 8-byte halves in slot order.
-    const int bq = tg >> 2, bc = tg & 3, bsw = half_swap(bq);
-    const uint32_t boff = (uint32_t)(bq * KB + 16 * bc);
-    const uint8_t* Wt = Wp + (int64_t)n0 * KB;
-
-    auto load_a = [&](int it, uint4 (&a)[kAPer]) {
-        const int k0 = it * BK;
-        const __amdgpu_buffer_rsrc_t ra = make_buf(Xt + k0);
-#pragma unroll
-        for (int u = 0; u < kAPer; ++u) a[u] = buf_load16(ra, k0 + acol[u] < K ? aoff[u] : kBufOOB);
-    };
-    auto load_b = [&](int qi, uint4& b) {  // quarter qi: block qi / 4, rows 64 (qi % 4) + bq
-        const int blk = qi >> 2, part = qi & 3;
-        const int kb0 = blk * kStepsPerBlock * BK;  // first column of the block
-        const __amdgpu_buffer_rsrc_t rb = make_buf(Wt + (int64_t)part * kQuarterRows * KB + blk * ROW_BYTES);
-        const bool rv = n0 + part * kQuarterRows + bq < N;
-        const int kc = kb0 + bc * BK;  // first column of the slice
-        if constexpr (VECB) {
-            const bool v = rv && kc < K;
-            const uint2 lo = buf_load8(rb, v ? boff + 8 * bsw : kBufOOB);
-            const uint2 hi = buf_load8(rb, v ? boff + 8 * (bsw ^ 1) : kBufOOB);
-            b = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        } else {  // dword d of the slice covers columns kc + 16 d .. + 15
-            const int d0 = 2 * bsw, d1 = 2 * (bsw ^ 1);
-            b.x = buf_load4(rb, rv && kc + 16 * d0 < K ? boff + 4 * d0 : kBufOOB);
-            b.y = buf_load4(rb, rv && kc + 16 * d0 + 16 < K ? boff + 4 * d0 + 4 : kBufOOB);
-            b.z = buf_load4(rb, rv && kc + 16 * d1 < K ? boff + 4 * d1 : kBufOOB);
-            b.w = buf_load4(rb, rv && kc + 16 * d1 + 16 < K ? boff + 4 * d1 + 4 : kBufOOB);
+        {
+            const float g = *gamma_p;
+            if (t < BM) row_scale[t] = (m0 + t < M) ? g / scale_x[m0 + t] : 0.0f;
         }
-    };
-    // staged activation chunks are byte-transposed in registers (in a
-    // compute phase, where the VALU is otherwise idle) and stored as they are
-    auto transpose_a = [&](uint4 (&a)[kAPer]) {
-#pragma unroll
-        for (int u = 0; u < kAPer; ++u) {
-            const uint32_t in[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
-            uint32_t o[4];
-            transpose4x4_bytes(in, o);
-            a[u] = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-    };
-    auto store_a = [&](int buf, const uint4 (&a)[kAPer]) {
-        uint8_t* As = smem_a[wm][buf];
-#pragma unroll
+
+        // Activations: thread tg stages chunks tg + 256 u (row c / 4, chunk c % 4)
+        // of the group's 128 rows; offsets relative to the step's base address.
+        const int mh = m0 + wm * HM;  // first row of the group's half
+        uint32_t aoff[kAPer];
+        int acol[kAPer];
+    #pragma unroll
         for (int u = 0; u < kAPer; ++u) {
             const int c = tg + u * kGroupThreads;
-            *reinterpret_cast<uint4*>(As + row_slot(c >> 2, c & 3)) = a[u];
+            const int row = c >> 2;
+            acol[u] = (c & 3) * 16;
+            aoff[u] = mh + row < M ? (uint32_t)(row * K + acol[u]) : kBufOOB;
         }
-    };
-    auto store_b = [&](int qi, const uint4& b) {
-        uint8_t* Bs = smem_b[wm][(qi >> 2) & 1];
-        *reinterpret_cast<uint4*>(Bs + row_slot((qi & 3) * kQuarterRows + bq, bc)) = b;
-    };
-    // tile t of the activations and quarter t + 3 of the weights
-    auto load_global = [&](int it, Stage& p) {
-        load_a(it, p.a);
-        load_b(it + 3, p.b);
-    };
-    auto store_lds = [&](int it, const Stage& p) {
-        store_a(it & 1, p.a);
-        store_b(it + 3, p.b);
-    };
+        const int8_t* Xt = Xq + (int64_t)mh * K;
+        // Weights: in a quarter, thread tg stages slice bc = tg % 4 of row
+        // bq = tg / 4 (+ 64 per quarter), both 8-byte halves in slot order.
+        const int bq = tg >> 2, bc = tg & 3, bsw = half_swap(bq);
+        const uint32_t boff = (uint32_t)(bq * KB + 16 * bc);
+        const uint8_t* Wt = Wp + (int64_t)n0 * KB;
 
-    v16i acc[4][JN];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < JN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
-
-    const int g = lane >> 5;    // lane group: k chunks 2g, 2g+1 of the step
-    const int l32 = lane & 31;  // row (A) / column (B) inside a 32-block
-
-    // Operands of one step: MFMA half kh pairs activation chunk 2g+kh with
-    // the same chunk of the codes (one packed dword per half).
-    v4i a[2][4], b[2][JN];
-    uint2 bp[JN];
-    auto read_codes = [&](int it) {
-        const uint8_t* Bs = smem_b[wm][(it >> 2) & 1];
-        const int c = it & 3;
-#pragma unroll
-        for (int j = 0; j < JN; ++j) {
-            const int r = wn * 64 + j * 32 + l32;
-            bp[j] = *reinterpret_cast<const uint2*>(Bs + row_slot(r, c) + 8 * (g ^ half_swap(r)));
-        }
-    };
-    auto read_acts = [&](int buf) {
-        const uint8_t* As = smem_a[wm][buf];
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 v = *reinterpret_cast<const uint4*>(As + row_slot(i * 32 + l32, 2 * g + kh));
-                a[kh][i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+        auto load_a = [&](int it, uint4 (&a)[kAPer]) {
+            const int k0 = it * BK;
+            const __amdgpu_buffer_rsrc_t ra = make_buf(Xt + k0);
+    #pragma unroll
+            for (int u = 0; u < kAPer; ++u) a[u] = buf_load16(ra, k0 + acol[u] < K ? aoff[u] : kBufOOB);
+        };
+        auto load_b = [&](int qi, uint4& b) {  // quarter qi: block qi / 4, rows 64 (qi % 4) + bq
+            const int blk = qi >> 2, part = qi & 3;
+            const int kb0 = blk * kStepsPerBlock * BK;  // first column of the block
+            const __amdgpu_buffer_rsrc_t rb = make_buf(Wt + (int64_t)part * kQuarterRows * KB + blk * ROW_BYTES);
+            const bool rv = n0 + part * kQuarterRows + bq < N;
+            const int kc = kb0 + bc * BK;  // first column of the slice
+            if constexpr (VECB) {
+                const bool v = rv && kc < K;
+                const uint2 lo = buf_load8(rb, v ? boff + 8 * bsw : kBufOOB);
+                const uint2 hi = buf_load8(rb, v ? boff + 8 * (bsw ^ 1) : kBufOOB);
+                b = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            } else {  // dword d of the slice covers columns kc + 16 d .. + 15
+                const int d0 = 2 * bsw, d1 = 2 * (bsw ^ 1);
+                b.x = buf_load4(rb, rv && kc + 16 * d0 < K ? boff + 4 * d0 : kBufOOB);
+                b.y = buf_load4(rb, rv && kc + 16 * d0 + 16 < K ? boff + 4 * d0 + 4 : kBufOOB);
+                b.z = buf_load4(rb, rv && kc + 16 * d1 < K ? boff + 4 * d1 : kBufOOB);
+                b.w = buf_load4(rb, rv && kc + 16 * d1 + 16 < K ? boff + 4 * d1 + 4 : kBufOOB);
             }
-    };
-    auto unpack_codes = [&] {
-#pragma unroll
-        for (int j = 0; j < JN; ++j) {
-            uint32_t u[4];
-            unpack16(bp[j].x, u);
-            b[0][j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
-            unpack16(bp[j].y, u);
-            b[1][j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
-        }
-    };
-    auto barrier = [] {
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-    };
+        };
+        // staged activation chunks are byte-transposed in registers (in a
+        // compute phase, where the VALU is otherwise idle) and stored as they are
+        auto transpose_a = [&](uint4 (&a)[kAPer]) {
+    #pragma unroll
+            for (int u = 0; u < kAPer; ++u) {
+                const uint32_t in[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
+                uint32_t o[4];
+                transpose4x4_bytes(in, o);
+                a[u] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        };
+        auto store_a = [&](int buf, const uint4 (&a)[kAPer]) {
+            uint8_t* As = smem_a[wm][buf];
+    #pragma unroll
+            for (int u = 0; u < kAPer; ++u) {
+                const int c = tg + u * kGroupThreads;
+                *reinterpret_cast<uint4*>(As + row_slot(c >> 2, c & 3)) = a[u];
+            }
+        };
+        auto store_b = [&](int qi, const uint4& b) {
+            uint8_t* Bs = smem_b[wm][(qi >> 2) & 1];
+            *reinterpret_cast<uint4*>(Bs + row_slot((qi & 3) * kQuarterRows + bq, bc)) = b;
+        };
+        // tile t of the activations and quarter t + 3 of the weights
+        auto load_global = [&](int it, Stage& p) {
+            load_a(it, p.a);
+            load_b(it + 3, p.b);
+        };
+        auto store_lds = [&](int it, const Stage& p) {
+            store_a(it & 1, p.a);
+            store_b(it + 3, p.b);
+        };
 
-    // One step.  Memory phase: operands of step it (packed codes first, then
-    // activations); activation tile it + 1 and weight quarter it + 4 (loaded
-    // two steps ago into `st`, transposed since) into LDS; then the loads of
-    // tile it + 3 / quarter it + 6 into the freed `st`.  Compute phase: the
-    // 16 MFMAs, with the VALU work of the step between them: unpacking the
-    // codes just read and byte-transposing the activations of `nx` (loaded a
-    // step ago, stored next step).
-    //   Buffers: activation tile t in buffer t % 2; weight block t / 4 (steps
-    //   4 (t/4) .. + 3) in buffer (t / 4) % 2, written a quarter per step
-    //   during the four steps before it is read.  Every buffer is rewritten
-    //   only two barriers after its last read.
-    auto step = [&](int it, Stage& st, Stage& nx) {
-        read_codes(it);
-        read_acts(it & 1);
-        store_lds(it + 1, st);
-        load_global(it + 3, st);
-        barrier();
-        __builtin_amdgcn_s_setprio(1);
-        unpack_codes();
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < JN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[kh][i], b[kh][j], acc[i][j], 0, 0, 0);
-        transpose_a(nx.a);
-        __builtin_amdgcn_s_setprio(0);
-        barrier();
-    };
+        v16i acc[4][JN];
+    #pragma unroll
+        for (int i = 0; i < 4; ++i)
+    #pragma unroll
+            for (int j = 0; j < JN; ++j)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    // Prologue: activation tile 0 and weight block 0 (quarters 0-3) in LDS;
-    // tiles 1, 2 and quarters 4, 5 loading.  Group 1 then waits one extra
-    // barrier, which puts it a phase behind group 0.
-    {
-        uint4 q0, q1, q2;
-        load_b(0, q0);
-        load_b(1, q1);
-        load_b(2, q2);
-        Stage p0;
-        load_global(0, p0);  // tile 0, quarter 3
-        transpose_a(p0.a);
-        store_a(0, p0.a);
-        store_b(0, q0);
-        store_b(1, q1);
-        store_b(2, q2);
-        store_b(3, p0.b);
-    }
-    Stage s0, s1;
-    load_global(1, s1);
-    load_global(2, s0);
-    transpose_a(s1.a);
-    barrier();
-    if (wm == 1) barrier();
+        const int g = lane >> 5;    // lane group: k chunks 2g, 2g+1 of the step
+        const int l32 = lane & 31;  // row (A) / column (B) inside a 32-block
 
-    // Unrolled by two so that the staging sets alternate by name (no copy);
-    // with nk odd the last step runs on zero tiles (loads past K read
-    // zeros), which adds nothing to the sums.
-    for (int it = 0; it < nk; it += 2) {
-        step(it, s1, s0);
-        step(it + 1, s0, s1);
-    }
-    // Epilogue.  32x32 block layout: lane holds column l32 and rows
-    // 8*(r/4) + 4*g + r%4 for r = 0..15.  Stores address a uniform tile base
-    // with 32-bit offsets (a tile spans < 2^31 bytes).
-    float* Yt = Y + (int64_t)m0 * N + n0;
-    const int mlim = M - m0, nlim = N - n0;
-    const int rbase = wm * 128 + 4 * g, cbase = wn * 64 + l32;
-    // Interior tiles store without per-element conditions: a branch per
-    // store would let the compiler pull all 256 accumulators into VGPRs at
-    // once.  Edge tiles take the guarded loop.
-    auto store_tile = [&](auto guarded_tag, auto out, auto value) {
-        constexpr bool GUARD = decltype(guarded_tag)::value;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rloc = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
-                const int roff = rloc * N;
-                const float rs = row_scale[rloc];
-#pragma unroll
-                for (int j = 0; j < JN; ++j) {
-                    const int cloc = cbase + j * 32;
-                    // streaming (non-temporal) stores: the output is not read again here
-                    if (!GUARD || (rloc < mlim && cloc < nlim))
-                        __builtin_nontemporal_store(value(acc[i][j][r], rs), &out[roff + cloc]);
+        // Operands of one step: MFMA half kh pairs activation chunk 2g+kh with
+        // the same chunk of the codes (one packed dword per half).
+        v4i a[2][4], b[2][JN];
+        uint2 bp[JN];
+        auto read_codes = [&](int it) {
+            const uint8_t* Bs = smem_b[wm][(it >> 2) & 1];
+            const int c = it & 3;
+    #pragma unroll
+            for (int j = 0; j < JN; ++j) {
+                const int r = wn * 64 + j * 32 + l32;
+                bp[j] = *reinterpret_cast<const uint2*>(Bs + row_slot(r, c) + 8 * (g ^ half_swap(r)));
+            }
+        };
+        auto read_acts = [&](int buf) {
+            const uint8_t* As = smem_a[wm][buf];
+    #pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(As + row_slot(i * 32 + l32, 2 * g + kh));
+                    a[kh][i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
                 }
+        };
+        auto unpack_codes = [&] {
+    #pragma unroll
+            for (int j = 0; j < JN; ++j) {
+                uint32_t u[4];
+                unpack16(bp[j].x, u);
+                b[0][j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
+                unpack16(bp[j].y, u);
+                b[1][j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
             }
-            // keep the scheduler from pulling later accumulators forward
+        };
+        auto barrier = [] {
             __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        // One step.  Memory phase: operands of step it (packed codes first, then
+        // activations); activation tile it + 1 and weight quarter it + 4 (loaded
+        // two steps ago into `st`, transposed since) into LDS; then the loads of
+        // tile it + 3 / quarter it + 6 into the freed `st`.  Compute phase: the
+        // 16 MFMAs, with the VALU work of the step between them: unpacking the
+        // codes just read and byte-transposing the activations of `nx` (loaded a
+        // step ago, stored next step).
+        //   Buffers: activation tile t in buffer t % 2; weight block t / 4 (steps
+        //   4 (t/4) .. + 3) in buffer (t / 4) % 2, written a quarter per step
+        //   during the four steps before it is read.  Every buffer is rewritten
+        //   only two barriers after its last read.
+        auto step = [&](int it, Stage& st, Stage& nx) {
+            read_codes(it);
+            read_acts(it & 1);
+            store_lds(it + 1, st);
+            load_global(it + 3, st);
+            barrier();
+            __builtin_amdgcn_s_setprio(1);
+            unpack_codes();
+    #pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i)
+    #pragma unroll
+                    for (int j = 0; j < JN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[kh][i], b[kh][j], acc[i][j], 0, 0, 0);
+            transpose_a(nx.a);
+            __builtin_amdgcn_s_setprio(0);
+            barrier();
+        };
+
+        // Prologue: activation tile 0 and weight block 0 (quarters 0-3) in LDS;
+        // tiles 1, 2 and quarters 4, 5 loading.  Group 1 then waits one extra
+        // barrier, which puts it a phase behind group 0.
+        {
+            uint4 q0, q1, q2;
+            load_b(0, q0);
+            load_b(1, q1);
+            load_b(2, q2);
+            Stage p0;
+            load_global(0, p0);  // tile 0, quarter 3
+            transpose_a(p0.a);
+            store_a(0, p0.a);
+            store_b(0, q0);
+            store_b(1, q1);
+            store_b(2, q2);
+            store_b(3, p0.b);
         }
-    };
-    auto yval = [](int v, float rs) { return (float)v * rs; };
-    auto aval = [](int v, float) { return v; };
-    if (mlim >= BM && nlim >= BN) store_tile(std::false_type{}, Yt, yval);
-    else store_tile(std::true_type{}, Yt, yval);
-    if (acc_out) {
-        int32_t* At = acc_out + (int64_t)m0 * N + n0;
-        store_tile(std::true_type{}, At, aval);
+        Stage s0, s1;
+        load_global(1, s1);
+        load_global(2, s0);
+        transpose_a(s1.a);
+        barrier();
+        if (wm == 1) barrier();
+
+        // Unrolled by two so that the staging sets alternate by name (no copy);
+        // with nk odd the last step runs on zero tiles (loads past K read
+        // zeros), which adds nothing to the sums.
+        for (int it = 0; it < nk; it += 2) {
+            step(it, s1, s0);
+            step(it + 1, s0, s1);
+        }
+        // Group 0 closes with the barrier group 1 took at the start: both
+        // groups pass the same barriers in every tile.
+        if (wm == 0) barrier();
+        // Epilogue.  32x32 block layout: lane holds column l32 and rows
+        // 8*(r/4) + 4*g + r%4 for r = 0..15.  Stores address a uniform tile base
+        // with 32-bit offsets (a tile spans < 2^31 bytes).
+        float* Yt = Y + (int64_t)m0 * N + n0;
+        const int mlim = M - m0, nlim = N - n0;
+        const int rbase = wm * 128 + 4 * g, cbase = wn * 64 + l32;
+        // Interior tiles store without per-element conditions: a branch per
+        // store would let the compiler pull all 256 accumulators into VGPRs at
+        // once.  Edge tiles take the guarded loop.
+        auto store_tile = [&](auto guarded_tag, auto out, auto value) {
+            constexpr bool GUARD = decltype(guarded_tag)::value;
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rloc = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
+                    const int roff = rloc * N;
+                    const float rs = row_scale[rloc];
+    #pragma unroll
+                    for (int j = 0; j < JN; ++j) {
+                        const int cloc = cbase + j * 32;
+                        // streaming (non-temporal) stores: the output is not read again here
+                        if (!GUARD || (rloc < mlim && cloc < nlim))
+                            __builtin_nontemporal_store(value(acc[i][j][r], rs), &out[roff + cloc]);
+                    }
+                }
+                // keep the scheduler from pulling later accumulators forward
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto yval = [](int v, float rs) { return (float)v * rs; };
+        auto aval = [](int v, float) { return v; };
+        if (mlim >= BM && nlim >= BN) store_tile(std::false_type{}, Yt, yval);
+        else store_tile(std::true_type{}, Yt, yval);
+        if (acc_out) {
+            int32_t* At = acc_out + (int64_t)m0 * N + n0;
+            store_tile(std::true_type{}, At, aval);
+        }
+        // row_scale and the LDS tiles are rewritten by the next tile
+        __syncthreads();
     }
 }
 
@@ -345,12 +359,19 @@ hipError_t launch_gemm_i8t2(const int8_t* Xq, const float* scale_x, const uint8_
                             const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
                             int32_t* acc, hipStream_t s) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+    // one workgroup per CU at most (its LDS allows one), each walking tiles
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)std::min<int64_t>(tiles, std::max(cus, 1));
     if (K % BK == 0)
-        gemm_i8t2_kernel<true><<<(unsigned)tiles, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M,
-                                                                    (int)N, (int)K, Y, acc);
+        gemm_i8t2_kernel<true><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, (int)K,
+                                                         Y, acc);
     else
-        gemm_i8t2_kernel<false><<<(unsigned)tiles, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M,
-                                                                     (int)N, (int)K, Y, acc);
+        gemm_i8t2_kernel<false><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, (int)K,
+                                                          Y, acc);
     return hipGetLastError();
 }
 

@@ -33,6 +33,9 @@ FWD_SHAPES = [
     # GEMM path: several tiles plus ragged edges in M, N and K
     (17, 16, 16), (100, 300, 256), (256, 256, 64), (300, 513, 1040),
     (513, 257, 4096), (1000, 40, 48),
+    # more 256 x 256 tiles than CUs: workgroups walk several tiles (ragged
+    # edges; K a multiple of the step, and not)
+    (4200, 4100, 64), (4196, 4132, 48),
 ]
 
 
