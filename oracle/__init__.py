@@ -54,6 +54,7 @@ def _load():
                                                 _p, _p, _i64, _p]),
         "oracle_ste_grad_w_at": (ctypes.c_int, [_p, ctypes.c_int, _p, _p, _i64, _i64, _i64,
                                                 _p, _p, _i64, _p]),
+        "oracle_rmsnorm_bwd": (ctypes.c_int, [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, ctypes.c_float, _p]),
         "oracle_mul_add_probe": (ctypes.c_float, [ctypes.c_float, ctypes.c_float, ctypes.c_float]),
     }
     for name, (res, args) in sig.items():
@@ -228,6 +229,19 @@ def ste_grad_w_at(gy, q, scale_x, ns, ks):
     out = np.empty(ns.size, np.float64)
     _check(_load().oracle_ste_grad_w_at(_ptr(gy), dt, _ptr(q), _ptr(scale_x), M, N, K,
                                         _ptr(ns), _ptr(ks), ns.size, _ptr(out)), "ste_grad_w_at")
+    return out
+
+
+def rmsnorm_bwd(x, g, eps: float = 1e-5):
+    """Gradient w.r.t. the RMSNorm input x given g = dL/d(RMSNorm output)
+    (unit gain, eps inside the root), float64."""
+    x, xt = _float_input(x)
+    g, gt = _float_input(g)
+    assert x.shape == g.shape and x.ndim == 2
+    M, K = x.shape
+    out = np.empty((M, K), np.float64)
+    _check(_load().oracle_rmsnorm_bwd(_ptr(x), xt, _ptr(g), gt, M, K, ctypes.c_float(eps), _ptr(out)),
+           "rmsnorm_bwd")
     return out
 
 

@@ -350,6 +350,37 @@ int oracle_ste_grad_w_at(const void *gy, int gy_dtype, const int8_t *q, const fl
     return 0;
 }
 
+/* -------------------------------------- N1: RMSNorm backward (unit gain)
+ * [NOTES 3.1] puts an RMSNorm in front of the activation quantizer; the
+ * pages derive no backward for it, so this is the exact derivative of the
+ * forward reading above (mean of squares over the row, eps inside the root,
+ * unit gain).  Per row, with r = 1/sqrt(sum_k x_k^2 / K + eps) and n = x * r:
+ *   dL/dx_j = r * (g_j - n_j * (sum_k g_k * n_k) / K)
+ * where g = dL/dn (the STE backward's grad_x).  Everything in float64 (a
+ * reference: it decides no integer).  x and g are fp32 or bf16 (dtype flags
+ * as above). */
+int oracle_rmsnorm_bwd(const void *x, int x_dtype, const void *g, int g_dtype, int64_t M,
+                       int64_t K, float eps, double *dx) {
+    if (!x || !g || !dx || M <= 0 || K <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            const double v = (double)load_elem(x, x_dtype, m * K + k);
+            ss += v * v;
+        }
+        const double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+        double dot = 0.0;
+        for (int64_t k = 0; k < K; k++)
+            dot += (double)load_elem(g, g_dtype, m * K + k) * ((double)load_elem(x, x_dtype, m * K + k) * r);
+        for (int64_t k = 0; k < K; k++) {
+            const double n = (double)load_elem(x, x_dtype, m * K + k) * r;
+            dx[m * K + k] = r * ((double)load_elem(g, g_dtype, m * K + k) - n * dot / (double)K);
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------- build-flag probe
  * Returns a*b + c as this file's build evaluates it.  With contraction off
  * it is fl(fl(a*b) + c), never fma(a, b, c); a test pins that. */

@@ -456,6 +456,77 @@ def test_ste_sampled_forms_and_bf16_grad():
 
 # ------------------------------------------------------------ build rule
 
+# ------------------------------------------------------ RMSNorm backward
+# [NOTES] 3.1 puts an RMSNorm (unit gain) in front of the quantizer; its
+# backward is the exact derivative of the forward reading (eps inside the
+# root).  Pinned by finite differences of that forward, by torch autograd of
+# the forward written out directly, and by closed forms.
+
+def _rms_forward64(x, eps):
+    # eps as the binary32 value the oracle receives
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + float(np.float32(eps)))
+
+
+def test_rmsnorm_bwd_matches_finite_differences():
+    rng = np.random.default_rng(40)
+    M, K, eps = 3, 7, 1e-5
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    g = rng.standard_normal((M, K)).astype(np.float32)
+    dx = oracle.rmsnorm_bwd(x, g, eps)
+    h = 1e-6
+    for m in range(M):
+        for k in range(K):
+            xp = x.astype(np.float64).copy()
+            xm = xp.copy()
+            xp[m, k] += h
+            xm[m, k] -= h
+            num = (np.sum(g * _rms_forward64(xp, eps)) - np.sum(g * _rms_forward64(xm, eps))) / (2 * h)
+            assert abs(num - dx[m, k]) <= 1e-6 * (1 + abs(dx[m, k])), (m, k, num, dx[m, k])
+
+
+def test_rmsnorm_bwd_equals_autograd_of_forward():
+    rng = np.random.default_rng(41)
+    M, K, eps = 5, 96, 1e-5
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    g = rng.standard_normal((M, K)).astype(np.float32)
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    n = xt * torch.rsqrt(xt.pow(2).mean(dim=1, keepdim=True) + float(np.float32(eps)))
+    n.backward(torch.tensor(g, dtype=torch.float64))
+    np.testing.assert_allclose(oracle.rmsnorm_bwd(x, g, eps), xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_rmsnorm_bwd_closed_forms():
+    rng = np.random.default_rng(42)
+    # K = 1: n = x / sqrt(x^2 + eps), dn/dx = eps / (x^2 + eps)^(3/2)
+    eps = 0.25
+    x = np.array([[0.5], [-2.0], [0.0]], np.float32)
+    g = np.array([[1.0], [3.0], [-2.0]], np.float32)
+    want = g.astype(np.float64) * eps / (x.astype(np.float64) ** 2 + eps) ** 1.5
+    np.testing.assert_allclose(oracle.rmsnorm_bwd(x, g, eps), want, rtol=1e-6)
+    # x . dx = (sum_k g_k n_k) * eps / (mean x^2 + eps): zero when eps = 0
+    M, K = 4, 33
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    g = rng.standard_normal((M, K)).astype(np.float32)
+    for eps in (1e-5, 0.5):
+        dx = oracle.rmsnorm_bwd(x, g, eps)
+        x64 = x.astype(np.float64)
+        ms = np.mean(x64 * x64, axis=1)
+        dot = np.sum(g * _rms_forward64(x, eps), axis=1)
+        e32 = float(np.float32(eps))
+        np.testing.assert_allclose(np.sum(x64 * dx, axis=1), dot * e32 / (ms + e32), rtol=1e-9, atol=1e-12)
+    # eps = 0: the forward is scale invariant, so dx(a x) = dx(x) / a
+    dx1 = oracle.rmsnorm_bwd(x, g, 0.0)
+    dx2 = oracle.rmsnorm_bwd((4.0 * x).astype(np.float32), g, 0.0)
+    np.testing.assert_allclose(dx2, dx1 / 4.0, rtol=1e-12, atol=1e-14)
+    # bf16 inputs widen exactly
+    xb = workloads.bf16_bits(torch.tensor(x).to(torch.bfloat16))
+    gb = workloads.bf16_bits(torch.tensor(g).to(torch.bfloat16))
+    xw = (xb.astype(np.uint32) << 16).view(np.float32)
+    gw = (gb.astype(np.uint32) << 16).view(np.float32)
+    np.testing.assert_array_equal(oracle.rmsnorm_bwd(xb, gb, 1e-5), oracle.rmsnorm_bwd(xw, gw, 1e-5))
+
+
 def test_oracle_does_not_contract_multiply_add():
     # a*b = 1 + 2^-11 + 2^-24 rounds to 1 + 2^-11 (tie to even), so the
     # unfused result is 0 while fma(a, b, c) would be 2^-24.
