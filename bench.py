@@ -102,6 +102,7 @@ def setup_layer(name):
         buf["grad_W"] = torch.empty(N, K, dtype=torch.float32, device=dev)
         buf["ws_bwd"] = torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, M, N, K),
                                     dtype=torch.uint8, device=dev)
+        buf["grad_X"] = torch.empty(M, K, dtype=torch.float32, device=dev)
     return d, x, w, gy, buf
 
 
@@ -122,6 +123,8 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
                            "peak_ops": BF16_PEAK_TFLOPS}
         c["bwd_grad_W"] = {"ops": 2 * M * N * K, "bytes": 2 * M * N + M * K + 4 * M + 4 * N * K,
                            "peak_ops": BF16_PEAK_TFLOPS}
+        # RMSNorm backward (after the STE backward): x and fp32 grad_x read, fp32 grad_X written
+        c["rmsnorm_bwd"] = {"bytes": M * K * x_bytes + 4 * M * K + 4 * M * K, "bound": "hbm"}
     for v in c.values():
         if "ops" in v:
             ridge = v["peak_ops"] * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -135,6 +138,7 @@ KERNEL_OF = {
     "linear_fwd": "gemm_i8t2_kernel",
     "bwd_grad_x": "bwd_kernel<grad_x>",
     "bwd_grad_W": "bwd_kernel<grad_W> (+ split_reduce_kernel when split)",
+    "rmsnorm_bwd": "rmsnorm_bwd_kernel",
 }
 # sources each call's kernels are built from: the HBM traffic recorded under
 # profiles/ is used only while these files are unchanged
@@ -144,6 +148,7 @@ SOURCES_OF = {
     "linear_fwd": ["bit_ternary_quantized_amd/csrc/gemm_i8.hip", "bit_ternary_quantized_amd/csrc/gemv.hip"],
     "bwd_grad_x": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
     "bwd_grad_W": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
+    "rmsnorm_bwd": ["bit_ternary_quantized_amd/csrc/norm_bwd.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -265,6 +270,9 @@ def bench_layer(args, name):
         parts["bwd_grad_W"] = lambda: bt.bitnet_linear_bwd_ste(
             gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], want_grad_x=False, grad_W=b["grad_W"],
             workspace=b["ws_bwd"])
+        # the gradient through the RMSNorm in front of the quantizer, from the
+        # step's grad_x (timed on its own; not part of the step)
+        parts["rmsnorm_bwd"] = lambda: bt.bitnet_rmsnorm_bwd(x, b["grad_x"], 1e-5, grad_X=b["grad_X"])
 
     def step():
         for n in names:
@@ -312,7 +320,7 @@ def bench_layer(args, name):
     value = fwd_bwd * M * N * K / (ms * 1e-3) / 1e12
     # roofline: the longest single product of the step (the backward call
     # counts as its two products)
-    cands = [n for n in timed if n != "linear_bwd_ste"]
+    cands = [n for n in timed if n not in ("linear_bwd_ste", "rmsnorm_bwd")]
     dom = max(cands, key=lambda n: per[n])
     roof = dict(rate(counts[dom], per[dom]))
     roof["kernel"] = KERNEL_OF[dom] + f" ({dom})"

@@ -23,7 +23,8 @@ GEMV_MAX_M = 16  # linear_fwd runs the packed GEMV up to this many tokens
 
 EXPORTS = (
     "bitnet_weight_quant", "bitnet_act_quant", "bitnet_linear_fwd", "bitnet_linear_bwd_ste",
-    "bitnet_pack_ternary", "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
+    "bitnet_pack_ternary", "bitnet_rmsnorm_bwd", "bitnet_workspace_bytes", "bitnet_status_str",
+    "bitnet_version",
 )
 
 
@@ -52,6 +53,7 @@ def load_library(path: str = LIB_PATH):
         "bitnet_linear_fwd": (c_int, [p, p, p, p, i64, i64, i64, p, p, p]),
         "bitnet_linear_bwd_ste": (c_int, [p, c_int, p, p, p, p, i64, i64, i64, p, c_int, p, p, sz, p]),
         "bitnet_pack_ternary": (c_int, [p, i64, i64, p, p]),
+        "bitnet_rmsnorm_bwd": (c_int, [p, c_int, p, c_int, i64, i64, ctypes.c_float, p, c_int, p]),
         "bitnet_workspace_bytes": (sz, [c_int, i64, i64, i64]),
         "bitnet_status_str": (ctypes.c_char_p, [c_int]),
         "bitnet_version": (c_int, []),
@@ -182,6 +184,23 @@ def bitnet_linear_bwd_ste(grad_y, Xq, scale_x, W_packed, gamma, want_grad_x=True
         M, N, K, _ptr(grad_x), gx_code, _ptr(grad_W), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return grad_x, grad_W
+
+
+def bitnet_rmsnorm_bwd(X, grad_n, eps: float = 1e-5, out_dtype=torch.float32, grad_X=None, stream=None):
+    """Backward of the unit-gain RMSNorm: grad w.r.t. its input X given grad_n
+    (w.r.t. its output) -> grad_X [M,K] f32/bf16."""
+    lib = load_library()
+    _need(X, "X")
+    _need(grad_n, "grad_n")
+    M, K = X.shape
+    if tuple(grad_n.shape) != (M, K):
+        raise ValueError("grad_n must have X's shape")
+    if grad_X is None:
+        grad_X = torch.empty(M, K, dtype=out_dtype, device=X.device)
+    _check("bitnet_rmsnorm_bwd", lib.bitnet_rmsnorm_bwd(
+        _ptr(X), _dtype_code(X), _ptr(grad_n), _dtype_code(grad_n), M, K, ctypes.c_float(eps),
+        _ptr(grad_X), _dtype_code(grad_X), _stream(stream)))
+    return grad_X
 
 
 def bitnet_pack_ternary(codes: torch.Tensor, W_packed=None, stream=None):

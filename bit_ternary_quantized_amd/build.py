@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(HERE, "libbitnet_amd.so")
-SOURCES = ["api.hip", "quant.hip", "gemm_i8.hip", "gemv.hip", "bwd.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm_i8.hip", "gemv.hip", "bwd.hip", "norm_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

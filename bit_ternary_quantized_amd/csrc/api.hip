@@ -107,6 +107,18 @@ int bitnet_linear_bwd_ste(const void* grad_y, int gy_dtype, const int8_t* Xq, co
                                              as_stream(stream)));
 }
 
+int bitnet_rmsnorm_bwd(const void* X, int x_dtype, const void* grad_n, int g_dtype, int64_t M,
+                       int64_t K, float eps, void* grad_X, int out_dtype, void* stream) {
+    if (!X || !grad_n || !grad_X) return BITNET_E_ARG;
+    if (!float_dtype(x_dtype) || !float_dtype(g_dtype) || !float_dtype(out_dtype)) return BITNET_E_DTYPE;
+    if (M < 1 || K < 1 || K % 8 != 0 || M > kMaxDim || K > kMaxDim) return BITNET_E_SHAPE;
+    if (!(eps >= 0.0f)) return BITNET_E_ARG;
+    if (!aligned16(X) || !aligned16(grad_n) || !aligned16(grad_X)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_rmsnorm_bwd(X, x_dtype == BITNET_BF16, grad_n, g_dtype == BITNET_BF16,
+                                                 M, K, eps, grad_X, out_dtype == BITNET_BF16,
+                                                 as_stream(stream)));
+}
+
 int bitnet_pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* W_packed,
                         void* stream) {
     if (!codes || !W_packed) return BITNET_E_ARG;

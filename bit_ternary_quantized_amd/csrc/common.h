@@ -217,5 +217,7 @@ hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* sca
                           const uint8_t* Wp, const float* gamma, int64_t M, int64_t N, int64_t K,
                           void* grad_x, bool gx_bf16, float* grad_W, void* ws, hipStream_t s);
 size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_rmsnorm_bwd(const void* X, bool x_bf16, const void* G, bool g_bf16, int64_t M,
+                              int64_t K, float eps, void* Out, bool out_bf16, hipStream_t s);
 
 }  // namespace bitnet

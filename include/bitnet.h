@@ -160,6 +160,28 @@ int bitnet_linear_bwd_ste(const void *grad_y, int gy_dtype, const int8_t *Xq,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Backward of the unit-gain RMSNorm in front of the activation quantizer
+ * ([NOTES 3.1] places it there; no page derives its backward, so this is the
+ * exact derivative of the forward defined under bitnet_act_quant).  Per row,
+ * with r = 1/sqrt(sum_k x_k^2 / K + eps) and n = x * r:
+ *   grad_X[m][j] = r * (grad_n[m][j] - n_j * (sum_k grad_n[m][k] * n_k) / K)
+ * computed in fp32 (a gradient; checked against a float64 reference).
+ * grad_n is the gradient w.r.t. the RMSNorm output, i.e. grad_x of
+ * bitnet_linear_bwd_ste; composing the two gives the BitLinear input
+ * gradient of one QAT step.
+ *   X       [M][K] fp32 or bf16 (x_dtype): the forward's RMSNorm input
+ *   grad_n  [M][K] fp32 or bf16 (g_dtype)
+ *   grad_X  [M][K] fp32 or bf16 (out_dtype, round to nearest even), written
+ *   eps     the forward's eps (>= 0)
+ * K % 8 == 0.  grad_X must not alias X or grad_n.
+ * Errors: BITNET_E_ARG, BITNET_E_SHAPE, BITNET_E_DTYPE, BITNET_E_ALIGN,
+ * BITNET_E_HIP.
+ */
+int bitnet_rmsnorm_bwd(const void *X, int x_dtype, const void *grad_n, int g_dtype,
+                       int64_t M, int64_t K, float eps, void *grad_X, int out_dtype,
+                       void *stream);
+
+/*
  * Pack pre-quantized ternary codes ([WALL 4.1] code table).
  *   codes    [N][K] int8; a value > 0 packs as +1, < 0 as -1, 0 as 0
  *   W_packed [N][K/4] bytes, written

@@ -107,6 +107,19 @@ def test_linear_bwd_rejects_bad_arguments():
     assert lib.bitnet_linear_bwd_ste(P, 1, P, P, P, P, 8192, 1376, 512, P, 0, P, NULL, ws_need, NULL) == -5
 
 
+def test_rmsnorm_bwd_rejects_bad_arguments():
+    lib = bt.load_library()
+    e = ctypes.c_float(1e-5)
+    assert lib.bitnet_rmsnorm_bwd(NULL, 1, P, 0, 4, 8, e, P, 0, NULL) == -1
+    assert lib.bitnet_rmsnorm_bwd(P, 1, P, 0, 4, 8, e, NULL, 0, NULL) == -1
+    assert lib.bitnet_rmsnorm_bwd(P, 2, P, 0, 4, 8, e, P, 0, NULL) == -3
+    assert lib.bitnet_rmsnorm_bwd(P, 1, P, 0, 4, 8, e, P, 9, NULL) == -3
+    assert lib.bitnet_rmsnorm_bwd(P, 1, P, 0, 0, 8, e, P, 0, NULL) == -2
+    assert lib.bitnet_rmsnorm_bwd(P, 1, P, 0, 4, 12, e, P, 0, NULL) == -2      # K % 8
+    assert lib.bitnet_rmsnorm_bwd(P, 1, P, 0, 4, 8, ctypes.c_float(-1.0), P, 0, NULL) == -1
+    assert lib.bitnet_rmsnorm_bwd(P, 1, ctypes.c_void_p((1 << 20) + 4), 0, 4, 8, e, P, 0, NULL) == -4
+
+
 def test_pack_rejects_bad_arguments():
     lib = bt.load_library()
     assert lib.bitnet_pack_ternary(NULL, 4, 4, P, NULL) == -1
