@@ -13,8 +13,9 @@
 // HBM-bound: x, g read once (a second time from cache for long rows), dx
 // written once.  One wave per row; lane l holds 8 consecutive elements of
 // every 512-element block, so each load is a coalesced 16-byte (bf16) or
-// 2 x 16-byte (fp32) piece.  Rows of at most 4 blocks stay in registers
-// between the passes; longer rows are read twice.
+// 2 x 16-byte (fp32) piece.  Rows of at most 16 blocks (8 with fp32 x and g)
+// stay in registers between the passes, as the raw loaded bytes; longer
+// rows are read twice.
 #include "common.h"
 
 namespace bitnet {
@@ -25,23 +26,31 @@ constexpr int kNbWaves = 4;
 constexpr int kNbChunk = 8;                 // elements per lane and block
 constexpr int kNbBlock = kWave * kNbChunk;  // 512
 
-// 8 elements at byte offset `off` (kBufOOB: zeros)
-__device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, uint32_t off, const float*, float (&v)[8]) {
-    const uint4 a = buf_load16(r, off);
-    const uint4 b = buf_load16(r, off == kBufOOB ? kBufOOB : off + 16);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+// 16-byte pieces holding 8 elements of T
+template <typename T>
+constexpr int kPieces = (int)sizeof(T) / 2;
+// raw bytes of 8 elements at byte offset `off` (kBufOOB: zeros)
+template <typename T>
+__device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 (&p)[kPieces<T>]) {
+#pragma unroll
+    for (int i = 0; i < kPieces<T>; ++i) p[i] = buf_load16(r, off == kBufOOB ? kBufOOB : off + 16 * i);
+}
+__device__ __forceinline__ void widen(const uint4 (&p)[2], float (&v)[8]) {  // fp32
+    const uint32_t w[8] = {p[0].x, p[0].y, p[0].z, p[0].w, p[1].x, p[1].y, p[1].z, p[1].w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
 }
-__device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint16_t*, float (&v)[8]) {
-    const uint4 a = buf_load16(r, off);
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+__device__ __forceinline__ void widen(const uint4 (&p)[1], float (&v)[8]) {  // bf16
+    const uint32_t w[4] = {p[0].x, p[0].y, p[0].z, p[0].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         v[2 * i] = __uint_as_float(w[i] << 16);
         v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
 }
+// rows of NB blocks fit the register cache (at most 192 registers of raw bytes)
+template <typename TX, typename TG>
+constexpr bool cache_fits(int nb) { return nb * (kPieces<TX> + kPieces<TG>) * 4 <= 192; }
 
 __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
     reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -77,9 +86,18 @@ __global__ __launch_bounds__(kNbWaves * kWave) void rmsnorm_bwd_kernel(
     auto offset = [&](int64_t b, int elem_bytes) -> uint32_t {
         return first(b) < K ? (uint32_t)(first(b) * elem_bytes) : kBufOOB;
     };
+    using RawX = uint4[kPieces<TX>];
+    using RawG = uint4[kPieces<TG>];
+    auto load_pair_raw = [&](int64_t b, RawX& x, RawG& g) {
+        load_raw<TX>(rx, offset(b, (int)sizeof(TX)), x);
+        load_raw<TG>(rg, offset(b, (int)sizeof(TG)), g);
+    };
     auto load_pair = [&](int64_t b, float (&x)[8], float (&g)[8]) {
-        load8(rx, offset(b, (int)sizeof(TX)), X, x);
-        load8(rg, offset(b, (int)sizeof(TG)), G, g);
+        RawX xr;
+        RawG gr;
+        load_pair_raw(b, xr, gr);
+        widen(xr, x);
+        widen(gr, g);
     };
     float sq = 0.0f, gx = 0.0f;
     auto accumulate = [&](const float (&x)[8], const float (&g)[8]) {
@@ -106,14 +124,32 @@ __global__ __launch_bounds__(kNbWaves * kWave) void rmsnorm_bwd_kernel(
     };
 
     if constexpr (NB > 0) {
-        float xs[NB][8], gs[NB][8];
+        static_assert(cache_fits<TX, TG>(NB), "row cache exceeds the register budget");
+        RawX xr[NB];
+        RawG gr[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) load_pair(b, xs[b], gs[b]);
+        for (int b = 0; b < NB; ++b) load_pair_raw(b, xr[b], gr[b]);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) accumulate(xs[b], gs[b]);
+        for (int b = 0; b < NB; ++b) {
+            float x[8], g[8];
+            widen(xr[b], x);
+            widen(gr[b], g);
+            accumulate(x, g);
+        }
         finish_sums();
 #pragma unroll
-        for (int b = 0; b < NB; ++b) write(b, xs[b], gs[b]);
+        for (int b = 0; b < NB; ++b) {
+            // an empty register constraint: the floats widened for the sums
+            // are not kept live until here
+#pragma unroll
+            for (int i = 0; i < kPieces<TX>; ++i) asm volatile("" : "+v"(xr[b][i].x), "+v"(xr[b][i].y), "+v"(xr[b][i].z), "+v"(xr[b][i].w));
+#pragma unroll
+            for (int i = 0; i < kPieces<TG>; ++i) asm volatile("" : "+v"(gr[b][i].x), "+v"(gr[b][i].y), "+v"(gr[b][i].z), "+v"(gr[b][i].w));
+            float x[8], g[8];
+            widen(xr[b], x);
+            widen(gr[b], g);
+            write(b, x, g);
+        }
     } else {
         constexpr int kInFlight = 2;  // blocks loaded per round
         for (int64_t b0 = 0; b0 < nblk; b0 += kInFlight) {
@@ -148,6 +184,10 @@ hipError_t rmsnorm_bwd_dispatch(const TX* X, const TG* G, int64_t M, int64_t K, 
         rmsnorm_bwd_kernel<TX, TG, TO, 2><<<grid, block, 0, s>>>(X, G, M, K, eps, Out);
     else if (nblk <= 4)
         rmsnorm_bwd_kernel<TX, TG, TO, 4><<<grid, block, 0, s>>>(X, G, M, K, eps, Out);
+    else if (nblk <= 8)
+        rmsnorm_bwd_kernel<TX, TG, TO, 8><<<grid, block, 0, s>>>(X, G, M, K, eps, Out);
+    else if (nblk <= 16 && cache_fits<TX, TG>(16))
+        rmsnorm_bwd_kernel<TX, TG, TO, cache_fits<TX, TG>(16) ? 16 : 0><<<grid, block, 0, s>>>(X, G, M, K, eps, Out);
     else
         rmsnorm_bwd_kernel<TX, TG, TO, 0><<<grid, block, 0, s>>>(X, G, M, K, eps, Out);
     return hipGetLastError();
