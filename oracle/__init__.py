@@ -55,6 +55,8 @@ def _load():
         "oracle_ste_grad_w_at": (ctypes.c_int, [_p, ctypes.c_int, _p, _p, _i64, _i64, _i64,
                                                 _p, _p, _i64, _p]),
         "oracle_rmsnorm_bwd": (ctypes.c_int, [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, ctypes.c_float, _p]),
+        "oracle_ste_gate": (ctypes.c_int, [_p, _p, ctypes.c_int, _i64, _i64, ctypes.c_float, ctypes.c_float, _p]),
+        "oracle_weight_clamp": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_float, ctypes.c_float, _p]),
         "oracle_mul_add_probe": (ctypes.c_float, [ctypes.c_float, ctypes.c_float, ctypes.c_float]),
     }
     for name, (res, args) in sig.items():
@@ -242,6 +244,29 @@ def rmsnorm_bwd(x, g, eps: float = 1e-5):
     out = np.empty((M, K), np.float64)
     _check(_load().oracle_rmsnorm_bwd(_ptr(x), xt, _ptr(g), gt, M, K, ctypes.c_float(eps), _ptr(out)),
            "rmsnorm_bwd")
+    return out
+
+
+def ste_gate(grad, w, lo: float = -1.0, hi: float = 1.0):
+    """grad (float64 [N,K]) where lo <= w <= hi (the master weights), else 0."""
+    grad = np.ascontiguousarray(grad, dtype=np.float64)
+    w, wt = _float_input(w)
+    assert grad.shape == w.shape and w.ndim == 2
+    N, K = w.shape
+    out = np.empty((N, K), np.float64)
+    _check(_load().oracle_ste_gate(_ptr(grad), _ptr(w), wt, N, K, ctypes.c_float(lo), ctypes.c_float(hi),
+                                   _ptr(out)), "ste_gate")
+    return out
+
+
+def weight_clamp(w, lo: float = -1.0, hi: float = 1.0):
+    """Master weights clamped to [lo, hi], same dtype (bf16 as uint16 bits)."""
+    w, wt = _float_input(w)
+    assert w.ndim == 2
+    N, K = w.shape
+    out = np.empty_like(w)
+    _check(_load().oracle_weight_clamp(_ptr(w), wt, N, K, ctypes.c_float(lo), ctypes.c_float(hi), _ptr(out)),
+           "weight_clamp")
     return out
 
 

@@ -381,6 +381,49 @@ int oracle_rmsnorm_bwd(const void *x, int x_dtype, const void *g, int g_dtype, i
     return 0;
 }
 
+/* ---------------------------- N3: range-gated STE and the weight clamp
+ * A variant of the STE above for the master weights ("BitNet量化感知训练中的
+ * 梯度传播优化" (blog.hotdry.top), section on the straight-through estimator:
+ * the gradient handed to the full-precision weight is masked by
+ * |w_full| <= 1; the STE comparison table (section 7) of the zyxy.net STE
+ * lecture: the gradient passes where a <= w <= b, else 0).  Both bounds
+ * are inclusive; comparisons on the binary32 value of w (exact for fp32 and
+ * bf16 weights).  grad and out are float64 [N][K]; out may alias grad. */
+int oracle_ste_gate(const double *grad, const void *w, int w_dtype, int64_t N, int64_t K, float lo,
+                    float hi, double *out) {
+    if (!grad || !w || !out || N <= 0 || K <= 0) return -1;
+    for (int64_t i = 0; i < N * K; i++) {
+        const float v = load_elem(w, w_dtype, i);
+        out[i] = (lo <= v && v <= hi) ? grad[i] : 0.0;
+    }
+    return 0;
+}
+
+/* The clamp of the master weights after an update (same blog, section on
+ * the BitLinear implementation: weight.data.clamp_(-1, 1)): w < lo -> lo,
+ * w > hi -> hi, else w (a NaN stays NaN).  out has w's dtype; for bf16 the
+ * result is rounded to nearest even (it changes only a bound that bf16
+ * cannot hold).  out may alias w. */
+static uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u); /* quiet NaN */
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+int oracle_weight_clamp(const void *w, int w_dtype, int64_t N, int64_t K, float lo, float hi,
+                        void *out) {
+    if (!w || !out || N <= 0 || K <= 0) return -1;
+    for (int64_t i = 0; i < N * K; i++) {
+        const float v = load_elem(w, w_dtype, i);
+        const float c = v < lo ? lo : (v > hi ? hi : v);
+        if (w_dtype == 1) ((uint16_t *)out)[i] = f32_to_bf16_rne(c);
+        else ((float *)out)[i] = c;
+    }
+    return 0;
+}
+
 /* ------------------------------------------------- build-flag probe
  * Returns a*b + c as this file's build evaluates it.  With contraction off
  * it is fl(fl(a*b) + c), never fma(a, b, c); a test pins that. */

@@ -527,6 +527,76 @@ def test_rmsnorm_bwd_closed_forms():
     np.testing.assert_array_equal(oracle.rmsnorm_bwd(xb, gb, 1e-5), oracle.rmsnorm_bwd(xw, gw, 1e-5))
 
 
+# ------------------------------------------- range-gated STE, weight clamp
+def _golden_gate_cases():
+    cases = []
+    for line in open(os.path.join(GOLDEN, "ste_gate_cases.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        fields = [f.split() for f in line.split("|")]
+        kind, dt, lo, hi = fields[0]
+        vals = [[float.fromhex(v) if "0x" in v else float(v) for v in f] for f in fields[1:]]
+        cases.append((kind, dt, float(lo), float(hi), vals))
+    return cases
+
+
+def _as_dtype(vals, dt):
+    a = np.array(vals, np.float32)
+    if dt == "bf16":
+        b = workloads.bf16_bits(torch.tensor(a).to(torch.bfloat16))
+        assert np.array_equal((b.astype(np.uint32) << 16).view(np.float32), a), "fixture value not bf16"
+        return b[None, :]
+    return a[None, :]
+
+
+def test_ste_gate_and_clamp_golden_cases():
+    cases = _golden_gate_cases()
+    assert len(cases) >= 7
+    for kind, dt, lo, hi, vals in cases:
+        w = _as_dtype(vals[0], dt)
+        if kind == "gate":
+            got = oracle.ste_gate(np.array([vals[1]], np.float64), w, lo, hi)
+            assert np.array_equal(got, np.array([vals[2]], np.float64)), (dt, lo, hi, got)
+        else:
+            got = oracle.weight_clamp(w, lo, hi)
+            want = _as_dtype(vals[1], dt)
+            assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (dt, lo, hi, got)
+
+
+def test_ste_gate_equals_autograd_through_clamp():
+    # torch's clamp passes its gradient where lo <= w <= hi (inclusive), so
+    # the gated STE is the gradient through clamp(W) of the plain STE layer
+    rng = np.random.default_rng(50)
+    N, K, M = 6, 40, 9
+    w = (rng.standard_normal((N, K)) * 0.8).astype(np.float32)
+    w[0, :4] = [-1.0, 1.0, -0.5, 0.25]  # bounds hit exactly
+    gy = rng.standard_normal((M, N)).astype(np.float32)
+    xd = rng.standard_normal((M, K))
+    for lo, hi in ((-1.0, 1.0), (-0.5, 0.25)):
+        wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+        y = torch.nn.functional.linear(torch.tensor(xd), torch.clamp(wt, lo, hi))
+        y.backward(torch.tensor(gy, dtype=torch.float64))
+        plain = gy.astype(np.float64).T @ xd  # the STE gradient without the gate
+        np.testing.assert_allclose(oracle.ste_gate(plain, w, lo, hi), wt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    # an unbounded range is the plain STE, an empty one blocks everything
+    g = rng.standard_normal((N, K))
+    assert np.array_equal(oracle.ste_gate(g, w, -np.inf, np.inf), g)
+    assert not oracle.ste_gate(g, w, 1.0, -1.0).any()
+
+
+def test_weight_clamp_equals_torch_clamp():
+    rng = np.random.default_rng(51)
+    w = (rng.standard_normal((7, 64)) * 2).astype(np.float32)
+    for lo, hi in ((-1.0, 1.0), (-0.3, 0.7)):
+        np.testing.assert_array_equal(oracle.weight_clamp(w, lo, hi), torch.clamp(torch.tensor(w), lo, hi).numpy())
+        wb = torch.tensor(w).to(torch.bfloat16)
+        want = torch.clamp(wb.float(), lo, hi).to(torch.bfloat16)
+        np.testing.assert_array_equal(oracle.weight_clamp(workloads.bf16_bits(wb), lo, hi), workloads.bf16_bits(want))
+    c = oracle.weight_clamp(w)
+    assert np.array_equal(oracle.weight_clamp(c), c)  # idempotent
+
+
 def test_oracle_does_not_contract_multiply_add():
     # a*b = 1 + 2^-11 + 2^-24 rounds to 1 + 2^-11 (tie to even), so the
     # unfused result is 0 while fma(a, b, c) would be 2^-24.
