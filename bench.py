@@ -103,6 +103,7 @@ def setup_layer(name):
         buf["ws_bwd"] = torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, M, N, K),
                                     dtype=torch.uint8, device=dev)
         buf["grad_X"] = torch.empty(M, K, dtype=torch.float32, device=dev)
+        buf["w_clamp"] = w.clone()  # the clamp runs in place on a copy
     return d, x, w, gy, buf
 
 
@@ -125,6 +126,12 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
                            "peak_ops": BF16_PEAK_TFLOPS}
         # RMSNorm backward (after the STE backward): x and fp32 grad_x read, fp32 grad_X written
         c["rmsnorm_bwd"] = {"bytes": M * K * x_bytes + 4 * M * K + 4 * M * K, "bound": "hbm"}
+        # grad_W with the master-weight range gate: the master weights read as well
+        c["bwd_grad_W_gated"] = {"ops": 2 * M * N * K,
+                                 "bytes": 2 * M * N + M * K + 4 * M + 4 * N * K + w_bytes * N * K,
+                                 "peak_ops": BF16_PEAK_TFLOPS}
+        # the master-weight clamp: read and written in place
+        c["weight_clamp"] = {"bytes": 2 * N * K * w_bytes, "bound": "hbm"}
     for v in c.values():
         if "ops" in v:
             ridge = v["peak_ops"] * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -139,6 +146,8 @@ KERNEL_OF = {
     "bwd_grad_x": "bwd_kernel<grad_x>",
     "bwd_grad_W": "bwd_kernel<grad_W> (+ split_reduce_kernel when split)",
     "rmsnorm_bwd": "rmsnorm_bwd_kernel",
+    "bwd_grad_W_gated": "bwd_kernel<grad_W> with the range gate (+ split_reduce_kernel when split)",
+    "weight_clamp": "weight_clamp_kernel",
 }
 # sources each call's kernels are built from: the HBM traffic recorded under
 # profiles/ is used only while these files are unchanged
@@ -149,6 +158,8 @@ SOURCES_OF = {
     "bwd_grad_x": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
     "bwd_grad_W": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
     "rmsnorm_bwd": ["bit_ternary_quantized_amd/csrc/norm_bwd.hip"],
+    "bwd_grad_W_gated": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
+    "weight_clamp": ["bit_ternary_quantized_amd/csrc/quant.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -273,6 +284,12 @@ def bench_layer(args, name):
         # the gradient through the RMSNorm in front of the quantizer, from the
         # step's grad_x (timed on its own; not part of the step)
         parts["rmsnorm_bwd"] = lambda: bt.bitnet_rmsnorm_bwd(x, b["grad_x"], 1e-5, grad_X=b["grad_X"])
+        # the STE variants: grad_W gated by the master weights in [-1, 1], and
+        # the clamp of the master weights after an update
+        parts["bwd_grad_W_gated"] = lambda: bt.bitnet_linear_bwd_ste_gated(
+            gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], w, -1.0, 1.0, want_grad_x=False,
+            grad_W=b["grad_W"], workspace=b["ws_bwd"])
+        parts["weight_clamp"] = lambda: bt.bitnet_weight_clamp(b["w_clamp"], -1.0, 1.0)
 
     def step():
         for n in names:
@@ -320,7 +337,7 @@ def bench_layer(args, name):
     value = fwd_bwd * M * N * K / (ms * 1e-3) / 1e12
     # roofline: the longest single product of the step (the backward call
     # counts as its two products)
-    cands = [n for n in timed if n not in ("linear_bwd_ste", "rmsnorm_bwd")]
+    cands = [n for n in timed if n not in ("linear_bwd_ste", "rmsnorm_bwd", "bwd_grad_W_gated", "weight_clamp")]
     dom = max(cands, key=lambda n: per[n])
     roof = dict(rate(counts[dom], per[dom]))
     roof["kernel"] = KERNEL_OF[dom] + f" ({dom})"

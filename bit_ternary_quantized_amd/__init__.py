@@ -23,8 +23,8 @@ GEMV_MAX_M = 16  # linear_fwd runs the packed GEMV up to this many tokens
 
 EXPORTS = (
     "bitnet_weight_quant", "bitnet_act_quant", "bitnet_linear_fwd", "bitnet_linear_bwd_ste",
-    "bitnet_pack_ternary", "bitnet_rmsnorm_bwd", "bitnet_workspace_bytes", "bitnet_status_str",
-    "bitnet_version",
+    "bitnet_pack_ternary", "bitnet_rmsnorm_bwd", "bitnet_linear_bwd_ste_gated", "bitnet_weight_clamp",
+    "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
 )
 
 
@@ -54,6 +54,9 @@ def load_library(path: str = LIB_PATH):
         "bitnet_linear_bwd_ste": (c_int, [p, c_int, p, p, p, p, i64, i64, i64, p, c_int, p, p, sz, p]),
         "bitnet_pack_ternary": (c_int, [p, i64, i64, p, p]),
         "bitnet_rmsnorm_bwd": (c_int, [p, c_int, p, c_int, i64, i64, ctypes.c_float, p, c_int, p]),
+        "bitnet_linear_bwd_ste_gated": (c_int, [p, c_int, p, p, p, p, p, c_int, ctypes.c_float, ctypes.c_float,
+                                                i64, i64, i64, p, c_int, p, p, sz, p]),
+        "bitnet_weight_clamp": (c_int, [p, c_int, i64, i64, ctypes.c_float, ctypes.c_float, p]),
         "bitnet_workspace_bytes": (sz, [c_int, i64, i64, i64]),
         "bitnet_status_str": (ctypes.c_char_p, [c_int]),
         "bitnet_version": (c_int, []),
@@ -201,6 +204,45 @@ def bitnet_rmsnorm_bwd(X, grad_n, eps: float = 1e-5, out_dtype=torch.float32, gr
         _ptr(X), _dtype_code(X), _ptr(grad_n), _dtype_code(grad_n), M, K, ctypes.c_float(eps),
         _ptr(grad_X), _dtype_code(grad_X), _stream(stream)))
     return grad_X
+
+
+def bitnet_linear_bwd_ste_gated(grad_y, Xq, scale_x, W_packed, gamma, W, w_lo=-1.0, w_hi=1.0,
+                                want_grad_x=True, want_grad_W=True, gx_dtype=torch.float32, grad_x=None,
+                                grad_W=None, workspace=None, stream=None):
+    """STE backward with grad_W zeroed where the master weight W lies outside
+    [w_lo, w_hi] -> (grad_x or None, grad_W or None)."""
+    lib = load_library()
+    for t, n in ((grad_y, "grad_y"), (Xq, "Xq"), (scale_x, "scale_x"), (W_packed, "W_packed"),
+                 (gamma, "gamma"), (W, "W")):
+        _need(t, n)
+    M, K = Xq.shape
+    N = W_packed.shape[0]
+    if tuple(W.shape) != (N, K):
+        raise ValueError("W must be [N, K]")
+    dev = Xq.device
+    if grad_x is None and want_grad_x:
+        grad_x = torch.empty(M, K, dtype=gx_dtype, device=dev)
+    if grad_W is None and want_grad_W:
+        grad_W = torch.empty(N, K, dtype=torch.float32, device=dev)
+    need = bitnet_workspace_bytes(BITNET_OP_LINEAR_BWD_STE, M, N, K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    gx_code = _dtype_code(grad_x) if grad_x is not None else BITNET_F32
+    _check("bitnet_linear_bwd_ste_gated", lib.bitnet_linear_bwd_ste_gated(
+        _ptr(grad_y), _dtype_code(grad_y), _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(gamma),
+        _ptr(W), _dtype_code(W), ctypes.c_float(w_lo), ctypes.c_float(w_hi), M, N, K, _ptr(grad_x), gx_code,
+        _ptr(grad_W), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return grad_x, grad_W
+
+
+def bitnet_weight_clamp(W, lo=-1.0, hi=1.0, stream=None):
+    """Clamp the master weights in place to [lo, hi]; returns W."""
+    lib = load_library()
+    _need(W, "W")
+    N, K = W.shape
+    _check("bitnet_weight_clamp", lib.bitnet_weight_clamp(
+        _ptr(W), _dtype_code(W), N, K, ctypes.c_float(lo), ctypes.c_float(hi), _stream(stream)))
+    return W
 
 
 def bitnet_pack_ternary(codes: torch.Tensor, W_packed=None, stream=None):

@@ -107,6 +107,46 @@ int bitnet_linear_bwd_ste(const void* grad_y, int gy_dtype, const int8_t* Xq, co
                                              as_stream(stream)));
 }
 
+int bitnet_linear_bwd_ste_gated(const void* grad_y, int gy_dtype, const int8_t* Xq, const float* scale_x,
+                                const uint8_t* W_packed, const float* gamma, const void* W, int w_dtype,
+                                float w_lo, float w_hi, int64_t M, int64_t N, int64_t K, void* grad_x,
+                                int gx_dtype, float* grad_W, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    if (!W) return BITNET_E_ARG;
+    if (!float_dtype(w_dtype)) return BITNET_E_DTYPE;
+    if (w_lo != w_lo || w_hi != w_hi) return BITNET_E_ARG;  // NaN bounds
+    if (!aligned16(W)) return BITNET_E_ALIGN;
+    if (!grad_y || !Xq || !scale_x || !W_packed || !gamma) return BITNET_E_ARG;
+    if (!grad_x && !grad_W) return BITNET_E_ARG;
+    if (gy_dtype != BITNET_BF16 || !float_dtype(gx_dtype)) return BITNET_E_DTYPE;
+    if (M < 1 || N < 1 || K < 1 || K % 16 != 0 || M > kMaxDim || N >= kMaxFwdN || K >= kMaxK)
+        return BITNET_E_SHAPE;
+    if (!aligned16(grad_y) || !aligned16(Xq) || !aligned16(W_packed) || !aligned4(scale_x) ||
+        !aligned4(gamma) || (grad_x && !aligned16(grad_x)) || (grad_W && !aligned16(grad_W)))
+        return BITNET_E_ALIGN;
+    const size_t need = grad_W ? bitnet::bwd_ws_bytes(M, N, K) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return BITNET_E_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return BITNET_E_ALIGN;
+    bitnet::SteGate gate;
+    gate.w = W;
+    gate.bf16 = w_dtype == BITNET_BF16;
+    gate.lo = w_lo;
+    gate.hi = w_hi;
+    return hip_status(bitnet::launch_bwd_ste(static_cast<const uint16_t*>(grad_y), Xq, scale_x,
+                                             W_packed, gamma, M, N, K, grad_x,
+                                             gx_dtype == BITNET_BF16, grad_W, workspace,
+                                             as_stream(stream), gate));
+}
+
+int bitnet_weight_clamp(void* W, int w_dtype, int64_t N, int64_t K, float lo, float hi, void* stream) {
+    if (!W) return BITNET_E_ARG;
+    if (!float_dtype(w_dtype)) return BITNET_E_DTYPE;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return BITNET_E_SHAPE;
+    if (!(lo <= hi)) return BITNET_E_ARG;  // also rejects NaN bounds
+    if (!aligned16(W)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_weight_clamp(W, w_dtype == BITNET_BF16, N * K, lo, hi, as_stream(stream)));
+}
+
 int bitnet_rmsnorm_bwd(const void* X, int x_dtype, const void* grad_n, int g_dtype, int64_t M,
                        int64_t K, float eps, void* grad_X, int out_dtype, void* stream) {
     if (!X || !grad_n || !grad_X) return BITNET_E_ARG;

@@ -36,6 +36,8 @@
 // the contraction split between the wave groups, see Tile); grad_W then also
 // splits its token range over workgroups, and a second kernel adds the fp32
 // partial tiles in split order (deterministic).
+#include <type_traits>
+
 #include "common.h"
 
 namespace bitnet {
@@ -209,11 +211,12 @@ struct Stage<kGradW, NA, NB> {
 //   m over the split's token range; with splits > 1 the tile goes to
 //   out + sp*N*K (partials).  `second` = Xq, `aux` = scale_x.
 // VEC: N % 8 == 0 (gy rows 16-byte aligned, 8-element chunks all in or out);
-// otherwise gy is read element by element.
-template <int MODE, class T, bool VEC, bool OUT_BF16>
+// otherwise gy is read element by element.  GATED (grad_W, one split only):
+// the master-weight range gate `gate` applied as the tile is written.
+template <int MODE, class T, bool VEC, bool OUT_BF16, bool GATED = false>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(
     const uint16_t* __restrict__ gy, const void* __restrict__ second, const float* __restrict__ aux,
-    int M, int N, int K, int splits, int kper, void* __restrict__ out) {
+    int M, int N, int K, int splits, int kper, void* __restrict__ out, SteGate gate) {
     constexpr int BK = T::BK, GROWS = T::GROWS, IM = T::IM, JN = T::JN, KQ = T::KQ;
     constexpr int NA = T::NA, NB = T::NB;
     constexpr bool KS = T::KSPLIT;
@@ -496,6 +499,21 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     if constexpr (MODE == kGradW) outf += (int64_t)sp * N * K;
 #pragma unroll
     for (int ii = 0; ii < IM; ++ii) {
+        // gated: the master weights of this 32-row block first (clamped
+        // indices, so every load is unconditional and they all fly together)
+        float wv[GATED ? 16 : 1][GATED ? JN : 1];
+        if constexpr (GATED) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = min(rg + wr + ii * 32 + 8 * (r >> 2) + 4 * g + (r & 3), R - 1);
+#pragma unroll
+                for (int j = 0; j < JN; ++j) {
+                    const int64_t idx = (int64_t)row * C + min(c0 + wc + j * 32 + l32, C - 1);
+                    wv[r][j] = gate.bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(gate.w)[idx])
+                                         : static_cast<const float*>(gate.w)[idx];
+                }
+            }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = rg + wr + ii * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -504,12 +522,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
                 for (int j = 0; j < JN; ++j) {
                     const int col = c0 + wc + j * 32 + l32;
                     if (col < C) {
+                        const int64_t idx = (int64_t)row * C + col;
+                        float v = acc[ii][j][r] * scale;
+                        if constexpr (GATED) v = (gate.lo <= wv[r][j] && wv[r][j] <= gate.hi) ? v : 0.0f;
                         // streaming (non-temporal) stores: the output is not read again here
-                        const float v = acc[ii][j][r] * scale;
                         if constexpr (MODE == kGradX && OUT_BF16)
-                            __builtin_nontemporal_store((__bf16)v, &static_cast<__bf16*>(out)[(int64_t)row * C + col]);
+                            __builtin_nontemporal_store((__bf16)v, &static_cast<__bf16*>(out)[idx]);
                         else
-                            __builtin_nontemporal_store(v, &outf[(int64_t)row * C + col]);
+                            __builtin_nontemporal_store(v, &outf[idx]);
                     }
                 }
             }
@@ -518,24 +538,35 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     }
 }
 
-// out[i] = sum over s = 0..splits-1 of part[s][i], in that order.
+// out[i] = sum over s = 0..splits-1 of part[s][i], in that order (then the
+// master-weight range gate when gate.w is set).
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
                                                            int splits, int64_t count,
-                                                           float* __restrict__ out) {
+                                                           float* __restrict__ out, SteGate gate) {
     const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i4 >= count) return;
+    auto gated = [&](int64_t i, float v) {
+        if (gate.w == nullptr) return v;
+        const float w = gate.bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(gate.w)[i])
+                                  : static_cast<const float*>(gate.w)[i];
+        return (gate.lo <= w && w <= gate.hi) ? v : 0.0f;
+    };
     if (i4 + 4 <= count && (count % 4) == 0) {
         float4 s = reinterpret_cast<const float4*>(part + i4)[0];
         for (int p = 1; p < splits; ++p) {
             const float4 v = reinterpret_cast<const float4*>(part + (int64_t)p * count + i4)[0];
             s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
         }
+        s.x = gated(i4, s.x);
+        s.y = gated(i4 + 1, s.y);
+        s.z = gated(i4 + 2, s.z);
+        s.w = gated(i4 + 3, s.w);
         reinterpret_cast<float4*>(out + i4)[0] = s;
     } else {
         for (int64_t i = i4; i < i4 + 4 && i < count; ++i) {
             float s = part[i];
             for (int p = 1; p < splits; ++p) s += part[(int64_t)p * count + i];
-            out[i] = s;
+            out[i] = gated(i, s);
         }
     }
 }
@@ -575,14 +606,24 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 template <int MODE, class T, bool OUT_BF16>
 hipError_t launch_one(const uint16_t* gy, const void* second, const float* aux, int M, int N, int K,
-                      const Plan& p, void* out, hipStream_t s) {
+                      const Plan& p, void* out, hipStream_t s, const SteGate& gate = SteGate{}) {
     const unsigned grid = (unsigned)(p.tiles * p.splits);
-    if (N % 8 == 0)
-        bwd_kernel<MODE, T, true, OUT_BF16><<<grid, kThreads, 0, s>>>(gy, second, aux, M, N, K, p.splits,
-                                                                     p.kper, out);
-    else
-        bwd_kernel<MODE, T, false, OUT_BF16><<<grid, kThreads, 0, s>>>(gy, second, aux, M, N, K, p.splits,
-                                                                      p.kper, out);
+    // the gate rides in the tile epilogue only without a token split (with
+    // one, split_reduce_kernel applies it)
+    const bool gated = MODE == kGradW && gate.w != nullptr && p.splits == 1;
+#define BITNET_BWD_LAUNCH(V_, G_)                                                                \
+    bwd_kernel<MODE, T, V_, OUT_BF16, G_><<<grid, kThreads, 0, s>>>(gy, second, aux, M, N, K,   \
+                                                                   p.splits, p.kper, out, gate)
+    if constexpr (MODE == kGradW) {
+        if (gated) {
+            if (N % 8 == 0) BITNET_BWD_LAUNCH(true, true);
+            else BITNET_BWD_LAUNCH(false, true);
+            return hipGetLastError();
+        }
+    }
+    if (N % 8 == 0) BITNET_BWD_LAUNCH(true, false);
+    else BITNET_BWD_LAUNCH(false, false);
+#undef BITNET_BWD_LAUNCH
     return hipGetLastError();
 }
 
@@ -595,7 +636,8 @@ size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* scale_x,
                           const uint8_t* Wp, const float* gamma, int64_t M, int64_t N, int64_t K,
-                          void* grad_x, bool gx_bf16, float* grad_W, void* ws, hipStream_t s) {
+                          void* grad_x, bool gx_bf16, float* grad_W, void* ws, hipStream_t s,
+                          const SteGate& gate) {
     const int m = (int)M, n = (int)N, k = (int)K;
     if (grad_x) {
         const Plan p = plan_for(M, K, N, false);
@@ -611,13 +653,13 @@ hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* sca
     if (grad_W) {
         const Plan p = plan_for(N, K, M, true);
         void* dst = p.splits > 1 ? ws : static_cast<void*>(grad_W);
-        hipError_t e = p.big ? launch_one<kGradW, TileL, false>(gy, Xq, scale_x, m, n, k, p, dst, s)
-                             : launch_one<kGradW, TileSK, false>(gy, Xq, scale_x, m, n, k, p, dst, s);
+        hipError_t e = p.big ? launch_one<kGradW, TileL, false>(gy, Xq, scale_x, m, n, k, p, dst, s, gate)
+                             : launch_one<kGradW, TileSK, false>(gy, Xq, scale_x, m, n, k, p, dst, s, gate);
         if (e != hipSuccess) return e;
         if (p.splits > 1) {
             const int64_t count = N * K;
             split_reduce_kernel<<<(unsigned)ceil_div(ceil_div(count, 4), 256), 256, 0, s>>>(
-                static_cast<const float*>(ws), p.splits, count, grad_W);
+                static_cast<const float*>(ws), p.splits, count, grad_W, gate);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

@@ -213,9 +213,18 @@ hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t*
                           int32_t* acc, hipStream_t s);
 constexpr int64_t kGemvMaxM = 16;
 bool gemv_supported(int64_t M, int64_t K);  // M <= 16 and the activations fit LDS
+// Range gate of the master-weight gradient: grad_W[n][k] is kept where
+// lo <= W[n][k] <= hi and set to 0 elsewhere; w == nullptr: no gate.
+struct SteGate {
+    const void* w = nullptr;
+    int bf16 = 0;  // W is bf16 (else fp32)
+    float lo = 0.0f, hi = 0.0f;
+};
 hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* scale_x,
                           const uint8_t* Wp, const float* gamma, int64_t M, int64_t N, int64_t K,
-                          void* grad_x, bool gx_bf16, float* grad_W, void* ws, hipStream_t s);
+                          void* grad_x, bool gx_bf16, float* grad_W, void* ws, hipStream_t s,
+                          const SteGate& gate = SteGate{});
+hipError_t launch_weight_clamp(void* W, bool w_bf16, int64_t count, float lo, float hi, hipStream_t s);
 size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_rmsnorm_bwd(const void* X, bool x_bf16, const void* G, bool g_bf16, int64_t M,
                               int64_t K, float eps, void* Out, bool out_bf16, hipStream_t s);

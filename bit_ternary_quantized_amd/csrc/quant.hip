@@ -518,6 +518,66 @@ static unsigned stream_grid(int64_t work_items, int per_block) {
     return (unsigned)g;
 }
 
+// ============================================================ weight clamp
+// The clamp of the master weights after an update to [lo, hi]
+// ("BitNet量化感知训练中的梯度传播优化", section on the BitLinear
+// implementation: weight.data.clamp_(-1, 1)).  In place, 16 bytes per thread
+// and step; an unclamped weight keeps its bits, a bound bf16 cannot hold is
+// rounded to nearest even.
+template <typename T>
+__global__ __launch_bounds__(256) void weight_clamp_kernel(T* __restrict__ W, int64_t count, float lo,
+                                                           float hi) {
+    constexpr int E = 16 / (int)sizeof(T);
+    const int64_t nvec = count / E;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    auto clamp_bits = [&](uint32_t bits) -> uint32_t {  // one element's bits
+        if constexpr (sizeof(T) == 4) {
+            const float v = __uint_as_float(bits);
+            return v < lo ? __float_as_uint(lo) : v > hi ? __float_as_uint(hi) : bits;
+        } else {
+            const float v = bf16_bits_to_f32(bits);
+            if (v < lo) return __builtin_bit_cast(uint16_t, (__bf16)lo);
+            if (v > hi) return __builtin_bit_cast(uint16_t, (__bf16)hi);
+            return bits;
+        }
+    };
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride) {
+        uint4 v = reinterpret_cast<const uint4*>(W)[i];
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            if constexpr (sizeof(T) == 4) {
+                w[d] = clamp_bits(w[d]);
+            } else {
+                w[d] = clamp_bits(w[d] & 0xffffu) | (clamp_bits(w[d] >> 16) << 16);
+            }
+        }
+        reinterpret_cast<uint4*>(W)[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    // the last count % E elements
+    if (blockIdx.x == 0 && threadIdx.x < count - nvec * E) {
+        const int64_t i = nvec * E + threadIdx.x;
+        if constexpr (sizeof(T) == 4) {
+            uint32_t* p = reinterpret_cast<uint32_t*>(W) + i;
+            *p = clamp_bits(*p);
+        } else {
+            uint16_t* p = reinterpret_cast<uint16_t*>(W) + i;
+            *p = (uint16_t)clamp_bits(*p);
+        }
+    }
+}
+
+hipError_t launch_weight_clamp(void* W, bool w_bf16, int64_t count, float lo, float hi, hipStream_t s) {
+    const int64_t per = w_bf16 ? 8 : 4;
+    const unsigned grid = stream_grid((count / per + 1), 256);
+    if (w_bf16)
+        weight_clamp_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<uint16_t*>(W), count, lo, hi);
+    else
+        weight_clamp_kernel<float><<<grid, 256, 0, s>>>(static_cast<float*>(W), count, lo, hi);
+    return hipGetLastError();
+}
+
+
 hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
                                uint8_t* W_packed, float* gamma, void* ws, hipStream_t s) {
     float* row_sums = static_cast<float*>(ws);

@@ -160,6 +160,38 @@ int bitnet_linear_bwd_ste(const void *grad_y, int gy_dtype, const int8_t *Xq,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Range-gated STE for the master weights: bitnet_linear_bwd_ste, except that
+ * grad_W[n][k] is 0 wherever the master weight W[n][k] lies outside
+ * [w_lo, w_hi] (both bounds inclusive, decided on the binary32 value of W).
+ * "BitNet量化感知训练中的梯度传播优化" (blog.hotdry.top), section on the
+ * straight-through estimator: the gradient handed to the full-precision
+ * weight is masked by |w| <= 1 (w_lo = -1, w_hi = 1); zyxy.net lecture on
+ * STE design, section 7: a quantizer over [a, b] passes the gradient where
+ * a <= w <= b.  grad_x is unchanged.
+ *   W  [N][K] fp32 or bf16 (w_dtype): the master weights the codes came from
+ * Other arguments, sizes, workspace and errors as bitnet_linear_bwd_ste;
+ * also BITNET_E_ARG for W NULL or a NaN bound.
+ */
+int bitnet_linear_bwd_ste_gated(const void *grad_y, int gy_dtype, const int8_t *Xq,
+                                const float *scale_x, const uint8_t *W_packed,
+                                const float *gamma, const void *W, int w_dtype, float w_lo,
+                                float w_hi, int64_t M, int64_t N, int64_t K, void *grad_x,
+                                int gx_dtype, float *grad_W, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
+ * Clamp the master weights in place to [lo, hi] after an update (same blog,
+ * section on the BitLinear implementation: the weights are kept in [-1, 1]).
+ * w < lo -> lo, w > hi -> hi, any other value (NaN included) keeps its bits;
+ * for bf16 W a bound that bf16 cannot hold is rounded to nearest even.
+ *   W  [N][K] fp32 or bf16 (w_dtype), read and written
+ * Errors: BITNET_E_ARG (W NULL, lo > hi or a NaN bound), BITNET_E_SHAPE,
+ * BITNET_E_DTYPE, BITNET_E_ALIGN, BITNET_E_HIP.
+ */
+int bitnet_weight_clamp(void *W, int w_dtype, int64_t N, int64_t K, float lo, float hi,
+                        void *stream);
+
+/*
  * Backward of the unit-gain RMSNorm in front of the activation quantizer
  * ([NOTES 3.1] places it there; no page derives its backward, so this is the
  * exact derivative of the forward defined under bitnet_act_quant).  Per row,

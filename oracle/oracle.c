@@ -401,9 +401,9 @@ int oracle_ste_gate(const double *grad, const void *w, int w_dtype, int64_t N, i
 
 /* The clamp of the master weights after an update (same blog, section on
  * the BitLinear implementation: weight.data.clamp_(-1, 1)): w < lo -> lo,
- * w > hi -> hi, else w (a NaN stays NaN).  out has w's dtype; for bf16 the
- * result is rounded to nearest even (it changes only a bound that bf16
- * cannot hold).  out may alias w. */
+ * w > hi -> hi, else w unchanged, bit for bit (a NaN stays as it is).  out
+ * has w's dtype; a bound that bf16 cannot hold is rounded to nearest even.
+ * out may alias w. */
 static uint16_t f32_to_bf16_rne(float f) {
     uint32_t u;
     memcpy(&u, &f, 4);
@@ -417,9 +417,14 @@ int oracle_weight_clamp(const void *w, int w_dtype, int64_t N, int64_t K, float 
     if (!w || !out || N <= 0 || K <= 0) return -1;
     for (int64_t i = 0; i < N * K; i++) {
         const float v = load_elem(w, w_dtype, i);
-        const float c = v < lo ? lo : (v > hi ? hi : v);
-        if (w_dtype == 1) ((uint16_t *)out)[i] = f32_to_bf16_rne(c);
-        else ((float *)out)[i] = c;
+        const int below = v < lo, above = v > hi;
+        if (w_dtype == 1) {
+            /* an unclamped weight keeps its 16 bits */
+            ((uint16_t *)out)[i] = below ? f32_to_bf16_rne(lo) : above ? f32_to_bf16_rne(hi)
+                                                                    : ((const uint16_t *)w)[i];
+        } else {
+            ((float *)out)[i] = below ? lo : above ? hi : v;
+        }
     }
     return 0;
 }

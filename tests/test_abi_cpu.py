@@ -120,6 +120,31 @@ def test_rmsnorm_bwd_rejects_bad_arguments():
     assert lib.bitnet_rmsnorm_bwd(P, 1, ctypes.c_void_p((1 << 20) + 4), 0, 4, 8, e, P, 0, NULL) == -4
 
 
+def test_gated_bwd_and_clamp_reject_bad_arguments():
+    lib = bt.load_library()
+    ws = 1 << 30
+    f = ctypes.c_float
+    ok = (f(-1.0), f(1.0))
+    # W missing, W dtype, NaN bound, W misaligned, then the plain call's checks
+    assert lib.bitnet_linear_bwd_ste_gated(P, 1, P, P, P, P, NULL, 0, *ok, 4, 4, 16, P, 0, P, P, ws, NULL) == -1
+    assert lib.bitnet_linear_bwd_ste_gated(P, 1, P, P, P, P, P, 4, *ok, 4, 4, 16, P, 0, P, P, ws, NULL) == -3
+    assert lib.bitnet_linear_bwd_ste_gated(P, 1, P, P, P, P, P, 0, f(float("nan")), f(1.0), 4, 4, 16, P, 0, P, P,
+                                           ws, NULL) == -1
+    assert lib.bitnet_linear_bwd_ste_gated(P, 1, P, P, P, P, ctypes.c_void_p((1 << 20) + 4), 0, *ok, 4, 4, 16, P, 0,
+                                           P, P, ws, NULL) == -4
+    assert lib.bitnet_linear_bwd_ste_gated(P, 1, P, P, P, P, P, 0, *ok, 4, 4, 12, P, 0, P, P, ws, NULL) == -2
+    assert lib.bitnet_linear_bwd_ste_gated(P, 0, P, P, P, P, P, 0, *ok, 4, 4, 16, P, 0, P, P, ws, NULL) == -3
+    ws_need = bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, 8192, 1376, 512)
+    assert lib.bitnet_linear_bwd_ste_gated(P, 1, P, P, P, P, P, 0, *ok, 8192, 1376, 512, P, 0, P, P, ws_need - 256,
+                                           NULL) == -5
+    assert lib.bitnet_weight_clamp(NULL, 0, 4, 4, *ok, NULL) == -1
+    assert lib.bitnet_weight_clamp(P, 3, 4, 4, *ok, NULL) == -3
+    assert lib.bitnet_weight_clamp(P, 0, 0, 4, *ok, NULL) == -2
+    assert lib.bitnet_weight_clamp(P, 0, 4, 4, f(1.0), f(-1.0), NULL) == -1   # lo > hi
+    assert lib.bitnet_weight_clamp(P, 0, 4, 4, f(float("nan")), f(1.0), NULL) == -1
+    assert lib.bitnet_weight_clamp(ctypes.c_void_p((1 << 20) + 2), 1, 4, 4, *ok, NULL) == -4
+
+
 def test_pack_rejects_bad_arguments():
     lib = bt.load_library()
     assert lib.bitnet_pack_ternary(NULL, 4, 4, P, NULL) == -1
