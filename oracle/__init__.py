@@ -57,6 +57,7 @@ def _load():
         "oracle_rmsnorm_bwd": (ctypes.c_int, [_p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, ctypes.c_float, _p]),
         "oracle_ste_gate": (ctypes.c_int, [_p, _p, ctypes.c_int, _i64, _i64, ctypes.c_float, ctypes.c_float, _p]),
         "oracle_weight_clamp": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_float, ctypes.c_float, _p]),
+        "oracle_code_counts": (ctypes.c_int, [_p, _i64, _i64, _p]),
         "oracle_mul_add_probe": (ctypes.c_float, [ctypes.c_float, ctypes.c_float, ctypes.c_float]),
     }
     for name, (res, args) in sig.items():
@@ -267,6 +268,16 @@ def weight_clamp(w, lo: float = -1.0, hi: float = 1.0):
     out = np.empty_like(w)
     _check(_load().oracle_weight_clamp(_ptr(w), wt, N, K, ctypes.c_float(lo), ctypes.c_float(hi), _ptr(out)),
            "weight_clamp")
+    return out
+
+
+def code_counts(packed, K: int):
+    """Counts of the codes in packed weights [N, K/4]: (zeros, +1, -1, unused 11)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    assert packed.shape[1] * 4 == K
+    out = np.zeros(4, np.uint64)
+    _check(_load().oracle_code_counts(_ptr(packed), N, K, _ptr(out)), "code_counts")
     return out
 
 

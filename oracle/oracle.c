@@ -429,6 +429,29 @@ int oracle_weight_clamp(const void *w, int w_dtype, int64_t N, int64_t K, float 
     return 0;
 }
 
+/* ------------------------------------------- N4: code counts (monitoring)
+ * The monitoring the pages ask for on the quantized weights: the share of
+ * zero codes ("BitNet 1.5技术解析" 6, practice notes, item 3: watch the
+ * ratio of zeros) and the balance of +1 against -1 ("BitNet量化感知训练中的
+ * 梯度传播优化", section on convergence monitoring: over-sparse weights,
+ * polarity imbalance).  Counts the codes of packed weights ([WALL 4.1]
+ * table: 00 = 0, 01 = +1, 10 = -1, 11 unused) by unpacking them one by one:
+ * counts[0] zeros, [1] +1, [2] -1, [3] the unused pattern 11. */
+int oracle_code_counts(const uint8_t *packed, int64_t N, int64_t K, uint64_t *counts) {
+    if (!packed || !counts || N <= 0 || K <= 0 || K % 4 != 0) return -1;
+    counts[0] = counts[1] = counts[2] = counts[3] = 0;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            const unsigned bits = (packed[n * (K / 4) + k / 4] >> (2 * (k % 4))) & 3u;
+            if (bits == 0u) counts[0]++;
+            else if (bits == 1u) counts[1]++;
+            else if (bits == 2u) counts[2]++;
+            else counts[3]++;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------- build-flag probe
  * Returns a*b + c as this file's build evaluates it.  With contraction off
  * it is fl(fl(a*b) + c), never fma(a, b, c); a test pins that. */

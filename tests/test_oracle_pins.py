@@ -597,6 +597,27 @@ def test_weight_clamp_equals_torch_clamp():
     assert np.array_equal(oracle.weight_clamp(c), c)  # idempotent
 
 
+# ------------------------------------------------------------ code counts
+def test_code_counts_hand_packed_bytes():
+    # byte 0b10_01_00_01: columns 0..3 = +1, 0, +1, -1 ([WALL] 4.1 table, the
+    # code of column k in bits 2k..2k+1); 0xff: four unused 11 patterns
+    packed = np.array([[0b10010001, 0x00], [0xFF, 0b01010101]], np.uint8)
+    np.testing.assert_array_equal(oracle.code_counts(packed, 8), [1 + 4, 2 + 4, 1, 4])
+
+
+def test_code_counts_match_the_codes():
+    rng = np.random.default_rng(60)
+    w = (rng.standard_normal((37, 64)) * 0.02).astype(np.float32)
+    codes, _ = oracle.weight_quant(w)
+    cnt = oracle.code_counts(oracle.pack(codes), 64)
+    assert int(cnt.sum()) == codes.size and cnt[3] == 0
+    assert (int(cnt[0]), int(cnt[1]), int(cnt[2])) == (int((codes == 0).sum()), int((codes == 1).sum()),
+                                                       int((codes == -1).sum()))
+    # -W swaps the +1 and -1 counts
+    c2 = oracle.code_counts(oracle.pack(oracle.weight_quant(-w)[0]), 64)
+    assert (c2[0], c2[1], c2[2]) == (cnt[0], cnt[2], cnt[1])
+
+
 def test_oracle_does_not_contract_multiply_add():
     # a*b = 1 + 2^-11 + 2^-24 rounds to 1 + 2^-11 (tie to even), so the
     # unfused result is 0 while fma(a, b, c) would be 2^-24.
