@@ -96,6 +96,9 @@ def setup_layer(name):
         "ws_wq": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, M, N, K),
                              dtype=torch.uint8, device=dev),
         "Y": torch.empty(M, N, dtype=torch.float32, device=dev),
+        "counts": torch.empty(4, dtype=torch.int64, device=dev),
+        "ws_cc": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_CODE_COUNTS, 0, N, K), dtype=torch.uint8,
+                             device=dev),
     }
     if gy is not None:
         buf["grad_x"] = torch.empty(M, K, dtype=torch.float32, device=dev)
@@ -115,6 +118,8 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
         "weight_quant": {"bytes": 2 * N * K * w_bytes + N * K // 4 + 4, "bound": "hbm"},
         "linear_fwd": {"ops": 2 * M * N * K, "bytes": M * K + N * K // 4 + 4 * M + 4 * M * N,
                        "peak_ops": INT8_PEAK_TOPS},
+        # zero / +1 / -1 counts of the packed codes (monitoring): the codes read once
+        "code_counts": {"bytes": N * K // 4 + 32, "bound": "hbm"},
     }
     if gy:
         c["linear_bwd_ste"] = {"ops": 4 * M * N * K,
@@ -148,6 +153,7 @@ KERNEL_OF = {
     "rmsnorm_bwd": "rmsnorm_bwd_kernel",
     "bwd_grad_W_gated": "bwd_kernel<grad_W> with the range gate (+ split_reduce_kernel when split)",
     "weight_clamp": "weight_clamp_kernel",
+    "code_counts": "code_counts_kernel + code_counts_final_kernel",
 }
 # sources each call's kernels are built from: the HBM traffic recorded under
 # profiles/ is used only while these files are unchanged
@@ -160,6 +166,7 @@ SOURCES_OF = {
     "rmsnorm_bwd": ["bit_ternary_quantized_amd/csrc/norm_bwd.hip"],
     "bwd_grad_W_gated": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
     "weight_clamp": ["bit_ternary_quantized_amd/csrc/quant.hip"],
+    "code_counts": ["bit_ternary_quantized_amd/csrc/quant.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -274,7 +281,7 @@ def bench_layer(args, name):
     # the backward call's two products, each timed on its own (not part of
     # the step): grad_x is one kernel, grad_W one kernel plus the ordered
     # split reduction when its token range is split
-    parts = {}
+    parts = {"code_counts": lambda: bt.bitnet_code_counts(b["W_packed"], K, counts=b["counts"], workspace=b["ws_cc"])}
     if gy is not None:
         parts["bwd_grad_x"] = lambda: bt.bitnet_linear_bwd_ste(
             gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], want_grad_W=False, grad_x=b["grad_x"])
@@ -337,7 +344,8 @@ def bench_layer(args, name):
     value = fwd_bwd * M * N * K / (ms * 1e-3) / 1e12
     # roofline: the longest single product of the step (the backward call
     # counts as its two products)
-    cands = [n for n in timed if n not in ("linear_bwd_ste", "rmsnorm_bwd", "bwd_grad_W_gated", "weight_clamp")]
+    cands = [n for n in timed if n not in ("linear_bwd_ste", "rmsnorm_bwd", "bwd_grad_W_gated", "weight_clamp",
+                                           "code_counts")]
     dom = max(cands, key=lambda n: per[n])
     roof = dict(rate(counts[dom], per[dom]))
     roof["kernel"] = KERNEL_OF[dom] + f" ({dom})"

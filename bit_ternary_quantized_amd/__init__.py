@@ -18,12 +18,13 @@ LIB_PATH = os.path.join(_HERE, "libbitnet_amd.so")
 
 BITNET_OK = 0
 BITNET_F32, BITNET_BF16 = 0, 1
-BITNET_OP_WEIGHT_QUANT, BITNET_OP_LINEAR_BWD_STE, BITNET_OP_LINEAR_FWD = 0, 1, 2
+BITNET_OP_WEIGHT_QUANT, BITNET_OP_LINEAR_BWD_STE, BITNET_OP_LINEAR_FWD, BITNET_OP_CODE_COUNTS = 0, 1, 2, 3
 GEMV_MAX_M = 16  # linear_fwd runs the packed GEMV up to this many tokens
 
 EXPORTS = (
     "bitnet_weight_quant", "bitnet_act_quant", "bitnet_linear_fwd", "bitnet_linear_bwd_ste",
     "bitnet_pack_ternary", "bitnet_rmsnorm_bwd", "bitnet_linear_bwd_ste_gated", "bitnet_weight_clamp",
+    "bitnet_code_counts",
     "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
 )
 
@@ -57,6 +58,7 @@ def load_library(path: str = LIB_PATH):
         "bitnet_linear_bwd_ste_gated": (c_int, [p, c_int, p, p, p, p, p, c_int, ctypes.c_float, ctypes.c_float,
                                                 i64, i64, i64, p, c_int, p, p, sz, p]),
         "bitnet_weight_clamp": (c_int, [p, c_int, i64, i64, ctypes.c_float, ctypes.c_float, p]),
+        "bitnet_code_counts": (c_int, [p, i64, i64, p, p, sz, p]),
         "bitnet_workspace_bytes": (sz, [c_int, i64, i64, i64]),
         "bitnet_status_str": (ctypes.c_char_p, [c_int]),
         "bitnet_version": (c_int, []),
@@ -243,6 +245,24 @@ def bitnet_weight_clamp(W, lo=-1.0, hi=1.0, stream=None):
     _check("bitnet_weight_clamp", lib.bitnet_weight_clamp(
         _ptr(W), _dtype_code(W), N, K, ctypes.c_float(lo), ctypes.c_float(hi), _stream(stream)))
     return W
+
+
+def bitnet_code_counts(W_packed, K: int, counts=None, workspace=None, stream=None):
+    """Counts of the packed codes -> int64 device tensor [zeros, +1, -1, unused 11]."""
+    lib = load_library()
+    _need(W_packed, "W_packed")
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K:
+        raise ValueError("W_packed must be [N, K/4]")
+    if counts is None:
+        counts = torch.empty(4, dtype=torch.int64, device=W_packed.device)
+    if workspace is None:
+        workspace = torch.empty(bitnet_workspace_bytes(BITNET_OP_CODE_COUNTS, 0, N, K), dtype=torch.uint8,
+                                device=W_packed.device)
+    _check("bitnet_code_counts", lib.bitnet_code_counts(
+        _ptr(W_packed), N, K, _ptr(counts), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return counts
 
 
 def bitnet_pack_ternary(codes: torch.Tensor, W_packed=None, stream=None):

@@ -43,6 +43,7 @@ size_t bitnet_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
     switch (op) {
         case BITNET_OP_WEIGHT_QUANT: return bitnet::weight_quant_ws_bytes(N);
         case BITNET_OP_LINEAR_BWD_STE: return bitnet::bwd_ws_bytes(M, N, K);
+        case BITNET_OP_CODE_COUNTS: return bitnet::code_counts_ws_bytes();
         default: return 0;
     }
 }
@@ -145,6 +146,16 @@ int bitnet_weight_clamp(void* W, int w_dtype, int64_t N, int64_t K, float lo, fl
     if (!(lo <= hi)) return BITNET_E_ARG;  // also rejects NaN bounds
     if (!aligned16(W)) return BITNET_E_ALIGN;
     return hip_status(bitnet::launch_weight_clamp(W, w_dtype == BITNET_BF16, N * K, lo, hi, as_stream(stream)));
+}
+
+int bitnet_code_counts(const uint8_t* W_packed, int64_t N, int64_t K, uint64_t* counts, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (!W_packed || !counts) return BITNET_E_ARG;
+    if (N < 1 || K < 1 || K % 4 != 0 || N > kMaxDim || K > kMaxDim) return BITNET_E_SHAPE;
+    if (!aligned16(W_packed) || (reinterpret_cast<uintptr_t>(counts) & 7u) != 0) return BITNET_E_ALIGN;
+    if (!workspace || workspace_bytes < bitnet::code_counts_ws_bytes()) return BITNET_E_WORKSPACE;
+    if (!aligned16(workspace)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_code_counts(W_packed, N * (K / 4), counts, workspace, as_stream(stream)));
 }
 
 int bitnet_rmsnorm_bwd(const void* X, int x_dtype, const void* grad_n, int g_dtype, int64_t M,

@@ -225,6 +225,9 @@ hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* sca
                           void* grad_x, bool gx_bf16, float* grad_W, void* ws, hipStream_t s,
                           const SteGate& gate = SteGate{});
 hipError_t launch_weight_clamp(void* W, bool w_bf16, int64_t count, float lo, float hi, hipStream_t s);
+hipError_t launch_code_counts(const uint8_t* W_packed, int64_t nbytes, uint64_t* counts, void* ws,
+                              hipStream_t s);
+size_t code_counts_ws_bytes();
 size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_rmsnorm_bwd(const void* X, bool x_bf16, const void* G, bool g_bf16, int64_t M,
                               int64_t K, float eps, void* Out, bool out_bf16, hipStream_t s);

@@ -518,6 +518,90 @@ static unsigned stream_grid(int64_t work_items, int per_block) {
     return (unsigned)g;
 }
 
+// ============================================================ code counts
+// Counts of the packed codes (00 = 0, 01 = +1, 10 = -1, 11 unused) for the
+// zero-ratio and polarity monitoring of the quantized weights
+// ("BitNet 1.5技术解析" 6, item 3; "BitNet量化感知训练中的梯度传播优化",
+// section on convergence monitoring).  Pass 1: a bounded grid; each thread
+// counts 16-byte chunks with population counts over the low and high bit of
+// every 2-bit field, each workgroup sums its threads and writes its four
+// partial counts.  Pass 2: one workgroup adds the partials in workgroup
+// order.  Integers throughout, no atomics: exact and deterministic.
+constexpr int kCountGroups = 1024;  // pass-1 workgroups at most
+
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* red) {  // 256 threads
+#pragma unroll
+    for (int m = 1; m < kWave; m *= 2) v += __shfl_xor(v, m, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const uint32_t t = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    return t;
+}
+
+__global__ __launch_bounds__(256) void code_counts_kernel(const uint8_t* __restrict__ P, int64_t nbytes,
+                                                          uint32_t* __restrict__ partial) {
+    __shared__ uint32_t red[4];
+    uint32_t c[4] = {0u, 0u, 0u, 0u};  // zeros, +1, -1, 11
+    auto count_fields = [&](uint32_t w, uint32_t field_mask) {  // one bit per 2-bit field
+        const uint32_t lo = w & field_mask, hi = (w >> 1) & field_mask;
+        c[0] += __builtin_popcount(~(lo | hi) & field_mask);
+        c[1] += __builtin_popcount(lo & ~hi);
+        c[2] += __builtin_popcount(hi & ~lo);
+        c[3] += __builtin_popcount(lo & hi);
+    };
+    const int64_t nvec = nbytes / 16;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * 256) {
+        const uint4 v = reinterpret_cast<const uint4*>(P)[i];
+        count_fields(v.x, 0x55555555u);
+        count_fields(v.y, 0x55555555u);
+        count_fields(v.z, 0x55555555u);
+        count_fields(v.w, 0x55555555u);
+    }
+    if (blockIdx.x == 0 && threadIdx.x < nbytes - nvec * 16) count_fields(P[nvec * 16 + threadIdx.x], 0x55u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t t = block_sum_u32(c[j], red);
+        if (threadIdx.x == 0) partial[4 * blockIdx.x + j] = t;
+    }
+}
+
+__global__ __launch_bounds__(256) void code_counts_final_kernel(const uint32_t* __restrict__ partial,
+                                                                int groups,
+                                                                unsigned long long* __restrict__ counts) {
+    __shared__ unsigned long long red[4][4];
+    unsigned long long c[4] = {0ull, 0ull, 0ull, 0ull};
+    for (int b = threadIdx.x; b < groups; b += 256)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] += partial[4 * b + j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        unsigned long long v = c[j];
+#pragma unroll
+        for (int m = 1; m < kWave; m *= 2) v += __shfl_xor(v, m, kWave);
+        if ((threadIdx.x & (kWave - 1)) == 0) red[j][threadIdx.x >> 6] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < 4) {
+        const int j = threadIdx.x;
+        counts[j] = red[j][0] + red[j][1] + red[j][2] + red[j][3];
+    }
+}
+
+size_t code_counts_ws_bytes() { return (size_t)kCountGroups * 4 * sizeof(uint32_t); }
+
+hipError_t launch_code_counts(const uint8_t* W_packed, int64_t nbytes, uint64_t* counts, void* ws,
+                              hipStream_t s) {
+    const int64_t need = (nbytes / 16 + 255) / 256;
+    const int groups = (int)std::max<int64_t>(1, std::min<int64_t>(need, kCountGroups));
+    uint32_t* partial = static_cast<uint32_t*>(ws);
+    code_counts_kernel<<<groups, 256, 0, s>>>(W_packed, nbytes, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    code_counts_final_kernel<<<1, 256, 0, s>>>(partial, groups, reinterpret_cast<unsigned long long*>(counts));
+    return hipGetLastError();
+}
+
 // ============================================================ weight clamp
 // The clamp of the master weights after an update to [lo, hi]
 // ("BitNet量化感知训练中的梯度传播优化", section on the BitLinear

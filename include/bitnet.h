@@ -69,7 +69,8 @@ typedef enum { BITNET_F32 = 0, BITNET_BF16 = 1 } bitnet_dtype;
 typedef enum {
     BITNET_OP_WEIGHT_QUANT = 0,
     BITNET_OP_LINEAR_BWD_STE = 1,
-    BITNET_OP_LINEAR_FWD = 2
+    BITNET_OP_LINEAR_FWD = 2,
+    BITNET_OP_CODE_COUNTS = 3
 } bitnet_op;
 
 /*
@@ -190,6 +191,25 @@ int bitnet_linear_bwd_ste_gated(const void *grad_y, int gy_dtype, const int8_t *
  */
 int bitnet_weight_clamp(void *W, int w_dtype, int64_t N, int64_t K, float lo, float hi,
                         void *stream);
+
+/*
+ * Counts of the codes in packed ternary weights, for the monitoring the
+ * pages ask for: the share of zero codes ([NOTES 6], practice notes, item 3)
+ * and the balance of +1 against -1 ("BitNet量化感知训练中的梯度传播优化",
+ * section on convergence monitoring: over-sparse weights, polarity
+ * imbalance).  Exact integers:
+ *   counts[0] = zeros, counts[1] = +1, counts[2] = -1, counts[3] = fields
+ *   holding the unused pattern 11 (0 for anything this library packed)
+ *   W_packed [N][K/4] bytes ([WALL 4.1] layout above); K % 4 == 0
+ *   counts   4 uint64, DEVICE memory, 8-byte aligned, written
+ *   workspace >= bitnet_workspace_bytes(BITNET_OP_CODE_COUNTS, 0, N, K) bytes
+ *            of device scratch (per-workgroup partial counts; no atomics,
+ *            so the counts need no clearing); contents on entry ignored.
+ * Errors: BITNET_E_ARG, BITNET_E_SHAPE, BITNET_E_ALIGN, BITNET_E_WORKSPACE,
+ * BITNET_E_HIP.
+ */
+int bitnet_code_counts(const uint8_t *W_packed, int64_t N, int64_t K, uint64_t *counts,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Backward of the unit-gain RMSNorm in front of the activation quantizer

@@ -145,6 +145,20 @@ def test_gated_bwd_and_clamp_reject_bad_arguments():
     assert lib.bitnet_weight_clamp(ctypes.c_void_p((1 << 20) + 2), 1, 4, 4, *ok, NULL) == -4
 
 
+def test_code_counts_reject_bad_arguments():
+    lib = bt.load_library()
+    ws = bt.bitnet_workspace_bytes(bt.BITNET_OP_CODE_COUNTS, 0, 4, 4)
+    assert ws > 0 and ws % 16 == 0
+    assert lib.bitnet_code_counts(NULL, 4, 4, P, P, ws, NULL) == -1
+    assert lib.bitnet_code_counts(P, 4, 4, NULL, P, ws, NULL) == -1
+    assert lib.bitnet_code_counts(P, 4, 6, P, P, ws, NULL) == -2
+    assert lib.bitnet_code_counts(P, 0, 4, P, P, ws, NULL) == -2
+    assert lib.bitnet_code_counts(ctypes.c_void_p((1 << 20) + 4), 4, 4, P, P, ws, NULL) == -4
+    assert lib.bitnet_code_counts(P, 4, 4, ctypes.c_void_p((1 << 20) + 4), P, ws, NULL) == -4
+    assert lib.bitnet_code_counts(P, 4, 4, P, P, ws - 16, NULL) == -5
+    assert lib.bitnet_code_counts(P, 4, 4, P, NULL, ws, NULL) == -5
+
+
 def test_pack_rejects_bad_arguments():
     lib = bt.load_library()
     assert lib.bitnet_pack_ternary(NULL, 4, 4, P, NULL) == -1
