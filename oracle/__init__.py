@@ -58,6 +58,9 @@ def _load():
         "oracle_ste_gate": (ctypes.c_int, [_p, _p, ctypes.c_int, _i64, _i64, ctypes.c_float, ctypes.c_float, _p]),
         "oracle_weight_clamp": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, ctypes.c_float, ctypes.c_float, _p]),
         "oracle_code_counts": (ctypes.c_int, [_p, _i64, _i64, _p]),
+        "oracle_weight_quant_rows": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _p, _p]),
+        "oracle_dequant_channel": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _p]),
+        "oracle_ste_grad_x_channel": (ctypes.c_int, [_p, ctypes.c_int, _p, _p, _i64, _i64, _i64, _p]),
         "oracle_mul_add_probe": (ctypes.c_float, [ctypes.c_float, ctypes.c_float, ctypes.c_float]),
     }
     for name, (res, args) in sig.items():
@@ -278,6 +281,41 @@ def code_counts(packed, K: int):
     assert packed.shape[1] * 4 == K
     out = np.zeros(4, np.uint64)
     _check(_load().oracle_code_counts(_ptr(packed), N, K, _ptr(out)), "code_counts")
+    return out
+
+
+def weight_quant_rows(w):
+    """Per-output-channel absmean codes -> (int8 codes [N,K], float32 gamma [N])."""
+    w, wt = _float_input(w)
+    N, K = w.shape
+    codes = np.empty((N, K), np.int8)
+    gamma = np.empty(N, np.float32)
+    _check(_load().oracle_weight_quant_rows(_ptr(w), wt, N, K, _ptr(codes), _ptr(gamma)), "weight_quant_rows")
+    return codes, gamma
+
+
+def linear_fwd_channel(q, scale_x, codes, s):
+    """(exact int32 acc, float64 y = acc * s[n] / scale_x[m])."""
+    acc = gemm_i32(q, codes)
+    scale_x = np.ascontiguousarray(scale_x, dtype=np.float32)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    M, N = acc.shape
+    assert scale_x.shape == (M,) and s.shape == (N,)
+    y = np.empty((M, N), np.float64)
+    _check(_load().oracle_dequant_channel(_ptr(acc), _ptr(scale_x), _ptr(s), M, N, _ptr(y)), "dequant_channel")
+    return acc, y
+
+
+def ste_grad_x_channel(gy, codes, s):
+    gy, dt = _float_input(gy)
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    M, N = gy.shape
+    K = codes.shape[1]
+    assert codes.shape[0] == N and s.shape == (N,)
+    out = np.empty((M, K), np.float64)
+    _check(_load().oracle_ste_grad_x_channel(_ptr(gy), dt, _ptr(codes), _ptr(s), M, N, K, _ptr(out)),
+           "ste_grad_x_channel")
     return out
 
 

@@ -452,6 +452,66 @@ int oracle_code_counts(const uint8_t *packed, int64_t N, int64_t K, uint64_t *co
     return 0;
 }
 
+/* ------------------------------ N4b: per-output-channel weight scales
+ * The variant with one scale per output row instead of one per matrix:
+ * "BitNet量化感知训练中的梯度传播优化" (blog.hotdry.top), section on the
+ * BitLinear implementation, 1 (weight scaling): output = (sign(W) . s) x
+ * with s in R^{d_out}, one scale per row; the zyxy.net STE lecture takes
+ * the mean of |w| along each row.  Reading: the absmean rule of O3 applied
+ * to each row on its own,
+ *   gamma_n = max(T(|w_n|) / K, 1e-5),  c = clamp(rint(w / gamma_n), -1, 1),
+ * the forward y[m,n] = acc[m,n] * s_n / scale_x[m] for any per-row s (gamma
+ * or a learned scale), and the STE backward with W_deq[n,k] = s_n * c[n,k]:
+ *   grad_x[m,k] = sum_n gy[m,n] * s_n * c[n,k]   (grad_W is unchanged). */
+int oracle_weight_quant_rows(const void *w, int w_dtype, int64_t N, int64_t K, int8_t *codes,
+                             float *gamma) {
+    if (!w || !codes || !gamma || N <= 0 || K <= 0) return -1;
+    if (w_dtype != 0 && w_dtype != 1) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++) {
+        float *a = (float *)malloc((size_t)K * sizeof(float));
+        if (!a) { bad |= 1; continue; }
+        for (int64_t k = 0; k < K; k++) a[k] = fabsf(load_elem(w, w_dtype, n * K + k));
+        const float mean = oracle_tree_sum_f32(a, K) / (float)K;
+        free(a);
+        const float g = mean > ORACLE_EPS_FLOOR ? mean : ORACLE_EPS_FLOOR;
+        gamma[n] = g;
+        for (int64_t k = 0; k < K; k++) {
+            float r = rintf(load_elem(w, w_dtype, n * K + k) / g);
+            if (r < -1.0f) r = -1.0f;
+            if (r > 1.0f) r = 1.0f;
+            codes[n * K + k] = (int8_t)r;
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+int oracle_dequant_channel(const int32_t *acc, const float *scale_x, const float *s, int64_t M, int64_t N,
+                           double *y) {
+    if (!acc || !scale_x || !s || !y || M <= 0 || N <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++)
+            y[m * N + n] = (double)acc[m * N + n] * (double)s[n] / (double)scale_x[m];
+    return 0;
+}
+
+int oracle_ste_grad_x_channel(const void *gy, int gy_dtype, const int8_t *codes, const float *s,
+                              int64_t M, int64_t N, int64_t K, double *gx) {
+    if (!gy || !codes || !s || !gx || M <= 0 || N <= 0 || K <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t k = 0; k < K; k++) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; n++)
+                acc += (double)load_elem(gy, gy_dtype, m * N + n) * ((double)s[n] * (double)codes[n * K + k]);
+            gx[m * K + k] = acc;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------- build-flag probe
  * Returns a*b + c as this file's build evaluates it.  With contraction off
  * it is fl(fl(a*b) + c), never fma(a, b, c); a test pins that. */

@@ -618,6 +618,44 @@ def test_code_counts_match_the_codes():
     assert (c2[0], c2[1], c2[2]) == (cnt[0], cnt[2], cnt[1])
 
 
+# ------------------------------------------- per-output-channel scales
+def test_weight_quant_rows_is_the_matrix_rule_per_row():
+    rng = np.random.default_rng(80)
+    w = (rng.standard_normal((9, 40)) * 0.02).astype(np.float32)
+    w[3] = 0.0                       # an all-zero row: gamma floor, all codes 0
+    w[5] *= 100.0                    # rows on different scales get their own gamma
+    codes, gamma = oracle.weight_quant_rows(w)
+    for n in range(w.shape[0]):
+        c1, g1 = oracle.weight_quant(w[n:n + 1])
+        assert np.array_equal(codes[n:n + 1], c1) and gamma[n] == np.float32(g1)
+    assert gamma[3] == np.float32(1e-5) and not codes[3].any()
+    # worked case: rows [1,7,0,0] and [3,5,0,0] both have gamma 2
+    c, g = oracle.weight_quant_rows(np.array([[1, 7, 0, 0], [3, 5, 0, 0]], np.float32))
+    assert g.tolist() == [2.0, 2.0] and c.tolist() == [[0, 1, 0, 0], [1, 1, 0, 0]]
+
+
+def test_channel_forward_and_grad_x():
+    rng = np.random.default_rng(81)
+    M, N, K = 6, 10, 32
+    q = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    codes = rng.integers(-1, 2, (N, K), dtype=np.int8)
+    sx = rng.uniform(20, 40, M).astype(np.float32)
+    # one scale for every channel reduces to the per-matrix forward
+    acc, y = oracle.linear_fwd_channel(q, sx, codes, np.full(N, 0.0125, np.float32))
+    acc0, y0 = oracle.linear_fwd(q, sx, codes, 0.0125)
+    assert np.array_equal(acc, acc0)
+    np.testing.assert_allclose(y, y0, rtol=1e-15)
+    # per-channel scales: autograd of the linear map at W_deq = s_n * c
+    s = rng.uniform(0.01, 0.05, N).astype(np.float32)
+    gy = rng.standard_normal((M, N)).astype(np.float32)
+    xt = torch.tensor(q.astype(np.float64) / sx[:, None], requires_grad=True)
+    wdeq = torch.tensor(s.astype(np.float64)[:, None] * codes.astype(np.float64))
+    torch.nn.functional.linear(xt, wdeq).backward(torch.tensor(gy, dtype=torch.float64))
+    np.testing.assert_allclose(oracle.ste_grad_x_channel(gy, codes, s), xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    _, y = oracle.linear_fwd_channel(q, sx, codes, s)
+    np.testing.assert_allclose(y, (xt.detach().numpy() @ wdeq.numpy().T), rtol=1e-12)
+
+
 def test_oracle_does_not_contract_multiply_add():
     # a*b = 1 + 2^-11 + 2^-24 rounds to 1 + 2^-11 (tie to even), so the
     # unfused result is 0 while fma(a, b, c) would be 2^-24.
