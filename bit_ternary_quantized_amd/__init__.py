@@ -18,13 +18,15 @@ LIB_PATH = os.path.join(_HERE, "libbitnet_amd.so")
 
 BITNET_OK = 0
 BITNET_F32, BITNET_BF16 = 0, 1
-BITNET_OP_WEIGHT_QUANT, BITNET_OP_LINEAR_BWD_STE, BITNET_OP_LINEAR_FWD, BITNET_OP_CODE_COUNTS = 0, 1, 2, 3
+(BITNET_OP_WEIGHT_QUANT, BITNET_OP_LINEAR_BWD_STE, BITNET_OP_LINEAR_FWD, BITNET_OP_CODE_COUNTS,
+ BITNET_OP_WEIGHT_QUANT_ROWS) = 0, 1, 2, 3, 4
 GEMV_MAX_M = 16  # linear_fwd runs the packed GEMV up to this many tokens
 
 EXPORTS = (
     "bitnet_weight_quant", "bitnet_act_quant", "bitnet_linear_fwd", "bitnet_linear_bwd_ste",
     "bitnet_pack_ternary", "bitnet_rmsnorm_bwd", "bitnet_linear_bwd_ste_gated", "bitnet_weight_clamp",
-    "bitnet_code_counts",
+    "bitnet_code_counts", "bitnet_weight_quant_rows", "bitnet_linear_fwd_channel",
+    "bitnet_linear_bwd_ste_channel",
     "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
 )
 
@@ -59,6 +61,9 @@ def load_library(path: str = LIB_PATH):
                                                 i64, i64, i64, p, c_int, p, p, sz, p]),
         "bitnet_weight_clamp": (c_int, [p, c_int, i64, i64, ctypes.c_float, ctypes.c_float, p]),
         "bitnet_code_counts": (c_int, [p, i64, i64, p, p, sz, p]),
+        "bitnet_weight_quant_rows": (c_int, [p, c_int, i64, i64, p, p, p, sz, p]),
+        "bitnet_linear_fwd_channel": (c_int, [p, p, p, p, i64, i64, i64, p, p, p]),
+        "bitnet_linear_bwd_ste_channel": (c_int, [p, c_int, p, p, p, p, i64, i64, i64, p, c_int, p, p, sz, p]),
         "bitnet_workspace_bytes": (sz, [c_int, i64, i64, i64]),
         "bitnet_status_str": (ctypes.c_char_p, [c_int]),
         "bitnet_version": (c_int, []),
@@ -245,6 +250,69 @@ def bitnet_weight_clamp(W, lo=-1.0, hi=1.0, stream=None):
     _check("bitnet_weight_clamp", lib.bitnet_weight_clamp(
         _ptr(W), _dtype_code(W), N, K, ctypes.c_float(lo), ctypes.c_float(hi), _stream(stream)))
     return W
+
+
+def bitnet_weight_quant_rows(W: torch.Tensor, W_packed=None, gamma=None, workspace=None, stream=None):
+    """Per-output-channel absmean codes -> (W_packed uint8 [N,K/4], gamma f32 [N])."""
+    lib = load_library()
+    _need(W, "W")
+    N, K = W.shape
+    dev = W.device
+    if W_packed is None:
+        W_packed = torch.empty(N, K // 4, dtype=torch.uint8, device=dev)
+    if gamma is None:
+        gamma = torch.empty(N, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT_ROWS, 0, N, K), dtype=torch.uint8,
+                                device=dev)
+    _check("bitnet_weight_quant_rows", lib.bitnet_weight_quant_rows(
+        _ptr(W), _dtype_code(W), N, K, _ptr(W_packed), _ptr(gamma), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return W_packed, gamma
+
+
+def bitnet_linear_fwd_channel(Xq, scale_x, W_packed, s, Y=None, acc=None, want_acc=False, stream=None):
+    """y = (Xq . codes^T) * s[n] / scale_x[m] -> (Y f32 [M,N], acc int32 or None)."""
+    lib = load_library()
+    for t, n in ((Xq, "Xq"), (scale_x, "scale_x"), (W_packed, "W_packed"), (s, "s")):
+        _need(t, n)
+    M, K = Xq.shape
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K or s.numel() != N:
+        raise ValueError("W_packed must be [N, K/4] and s [N]")
+    if Y is None:
+        Y = torch.empty(M, N, dtype=torch.float32, device=Xq.device)
+    if acc is None and want_acc:
+        acc = torch.empty(M, N, dtype=torch.int32, device=Xq.device)
+    _check("bitnet_linear_fwd_channel", lib.bitnet_linear_fwd_channel(
+        _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(s), M, N, K, _ptr(Y), _ptr(acc), _stream(stream)))
+    return Y, acc
+
+
+def bitnet_linear_bwd_ste_channel(grad_y, Xq, scale_x, W_packed, s, want_grad_x=True, want_grad_W=True,
+                                  gx_dtype=torch.float32, grad_x=None, grad_W=None, workspace=None, stream=None):
+    """STE backward at W_deq = s[n] * code -> (grad_x or None, grad_W or None)."""
+    lib = load_library()
+    for t, n in ((grad_y, "grad_y"), (Xq, "Xq"), (scale_x, "scale_x"), (W_packed, "W_packed"), (s, "s")):
+        _need(t, n)
+    M, K = Xq.shape
+    N = W_packed.shape[0]
+    if s.numel() != N:
+        raise ValueError("s must be [N]")
+    dev = Xq.device
+    if grad_x is None and want_grad_x:
+        grad_x = torch.empty(M, K, dtype=gx_dtype, device=dev)
+    if grad_W is None and want_grad_W:
+        grad_W = torch.empty(N, K, dtype=torch.float32, device=dev)
+    need = bitnet_workspace_bytes(BITNET_OP_LINEAR_BWD_STE, M, N, K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    gx_code = _dtype_code(grad_x) if grad_x is not None else BITNET_F32
+    _check("bitnet_linear_bwd_ste_channel", lib.bitnet_linear_bwd_ste_channel(
+        _ptr(grad_y), _dtype_code(grad_y), _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(s), M, N, K,
+        _ptr(grad_x), gx_code, _ptr(grad_W), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return grad_x, grad_W
 
 
 def bitnet_code_counts(W_packed, K: int, counts=None, workspace=None, stream=None):

@@ -44,6 +44,7 @@ size_t bitnet_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
         case BITNET_OP_WEIGHT_QUANT: return bitnet::weight_quant_ws_bytes(N);
         case BITNET_OP_LINEAR_BWD_STE: return bitnet::bwd_ws_bytes(M, N, K);
         case BITNET_OP_CODE_COUNTS: return bitnet::code_counts_ws_bytes();
+        case BITNET_OP_WEIGHT_QUANT_ROWS: return bitnet::weight_quant_rows_ws_bytes(N);
         default: return 0;
     }
 }
@@ -71,9 +72,12 @@ int bitnet_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, float eps
                                                as_stream(stream)));
 }
 
-int bitnet_linear_fwd(const int8_t* Xq, const float* scale_x, const uint8_t* W_packed,
-                      const float* gamma, int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+int linear_fwd(const int8_t* Xq, const float* scale_x, const uint8_t* W_packed, const float* gamma,
+               int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* stream, bool channel) {
     if (!Xq || !scale_x || !W_packed || !gamma || !Y) return BITNET_E_ARG;
     if (M < 1 || N < 1 || K < 1 || K % 16 != 0 || K >= kMaxK || M > kMaxDim || N >= kMaxFwdN)
         return BITNET_E_SHAPE;
@@ -82,15 +86,46 @@ int bitnet_linear_fwd(const int8_t* Xq, const float* scale_x, const uint8_t* W_p
         return BITNET_E_ALIGN;
     if (bitnet::gemv_supported(M, K))
         return hip_status(bitnet::launch_gemv_t2(Xq, scale_x, W_packed, gamma, M, N, K, Y, acc,
-                                                 as_stream(stream)));
+                                                 as_stream(stream), channel));
     return hip_status(bitnet::launch_gemm_i8t2(Xq, scale_x, W_packed, gamma, M, N, K, Y, acc,
-                                               as_stream(stream)));
+                                               as_stream(stream), channel));
 }
 
-int bitnet_linear_bwd_ste(const void* grad_y, int gy_dtype, const int8_t* Xq, const float* scale_x,
-                          const uint8_t* W_packed, const float* gamma, int64_t M, int64_t N,
-                          int64_t K, void* grad_x, int gx_dtype, float* grad_W, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+}  // namespace
+
+extern "C" {
+
+int bitnet_linear_fwd(const int8_t* Xq, const float* scale_x, const uint8_t* W_packed,
+                      const float* gamma, int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc,
+                      void* stream) {
+    return linear_fwd(Xq, scale_x, W_packed, gamma, M, N, K, Y, acc, stream, false);
+}
+
+int bitnet_linear_fwd_channel(const int8_t* Xq, const float* scale_x, const uint8_t* W_packed,
+                              const float* s, int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc,
+                              void* stream) {
+    return linear_fwd(Xq, scale_x, W_packed, s, M, N, K, Y, acc, stream, true);
+}
+
+int bitnet_weight_quant_rows(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* W_packed,
+                             float* gamma, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!W || !W_packed || !gamma) return BITNET_E_ARG;
+    if (!float_dtype(w_dtype)) return BITNET_E_DTYPE;
+    if (N < 1 || K < 1 || K % 4 != 0 || N > kMaxDim || K > kMaxDim) return BITNET_E_SHAPE;
+    if (!aligned16(W) || !aligned16(W_packed) || !aligned4(gamma)) return BITNET_E_ALIGN;
+    if (!workspace || workspace_bytes < bitnet::weight_quant_rows_ws_bytes(N)) return BITNET_E_WORKSPACE;
+    if (!aligned16(workspace)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_weight_quant_rows(W, w_dtype == BITNET_BF16, N, K, W_packed, gamma,
+                                                       workspace, as_stream(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+int linear_bwd(const void* grad_y, int gy_dtype, const int8_t* Xq, const float* scale_x,
+               const uint8_t* W_packed, const float* gamma, int64_t M, int64_t N, int64_t K, void* grad_x,
+               int gx_dtype, float* grad_W, void* workspace, size_t workspace_bytes, void* stream, bool channel) {
     if (!grad_y || !Xq || !scale_x || !W_packed || !gamma) return BITNET_E_ARG;
     if (!grad_x && !grad_W) return BITNET_E_ARG;
     if (gy_dtype != BITNET_BF16 || !float_dtype(gx_dtype)) return BITNET_E_DTYPE;
@@ -105,7 +140,27 @@ int bitnet_linear_bwd_ste(const void* grad_y, int gy_dtype, const int8_t* Xq, co
     return hip_status(bitnet::launch_bwd_ste(static_cast<const uint16_t*>(grad_y), Xq, scale_x,
                                              W_packed, gamma, M, N, K, grad_x,
                                              gx_dtype == BITNET_BF16, grad_W, workspace,
-                                             as_stream(stream)));
+                                             as_stream(stream), bitnet::SteGate{}, channel));
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitnet_linear_bwd_ste(const void* grad_y, int gy_dtype, const int8_t* Xq, const float* scale_x,
+                          const uint8_t* W_packed, const float* gamma, int64_t M, int64_t N,
+                          int64_t K, void* grad_x, int gx_dtype, float* grad_W, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    return linear_bwd(grad_y, gy_dtype, Xq, scale_x, W_packed, gamma, M, N, K, grad_x, gx_dtype, grad_W,
+                      workspace, workspace_bytes, stream, false);
+}
+
+int bitnet_linear_bwd_ste_channel(const void* grad_y, int gy_dtype, const int8_t* Xq, const float* scale_x,
+                                  const uint8_t* W_packed, const float* s, int64_t M, int64_t N, int64_t K,
+                                  void* grad_x, int gx_dtype, float* grad_W, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    return linear_bwd(grad_y, gy_dtype, Xq, scale_x, W_packed, s, M, N, K, grad_x, gx_dtype, grad_W,
+                      workspace, workspace_bytes, stream, true);
 }
 
 int bitnet_linear_bwd_ste_gated(const void* grad_y, int gy_dtype, const int8_t* Xq, const float* scale_x,

@@ -131,8 +131,10 @@ __device__ __forceinline__ v8bf rows_operand(const uint8_t* tile, int kq, int x0
 // 8 ternary codes (the low 16 bits of w: columns k..k+7) -> 8 bf16 in natural
 // column order (4 dwords, two codes each).  bf16 of a code: low byte 0x80 if
 // nonzero, high byte 0x3f (+1) or 0xbf (-1).
-__device__ __forceinline__ uint4 codes8_to_bf16(uint32_t w) {
-    constexpr uint32_t kHi = 0x00bf3f00u, kLo = 0x00808000u;
+// kHi / kLo: high / low byte of the bf16 value of code 0, +1, -1 in bytes
+// 0, 1, 2 (the defaults give 0, +1.0, -1.0).
+__device__ __forceinline__ uint4 codes8_to_bf16(uint32_t w, uint32_t kHi = 0x00bf3f00u,
+                                                uint32_t kLo = 0x00808000u) {
     const uint32_t ev = w & 0x33333333u;         // codes 0, 2 of every byte
     const uint32_t od = (w >> 2) & 0x33333333u;  // codes 1, 3 of every byte
     uint32_t r[4];
@@ -146,6 +148,14 @@ __device__ __forceinline__ uint4 codes8_to_bf16(uint32_t w) {
         r[2 * b + 1] = __builtin_amdgcn_perm(kLo, kHi, s1);
     }
     return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+// 8 ternary codes times a per-row scale s: codes -> 0, +bf16(s), -bf16(s)
+// (s rounded to bf16 once, to nearest even)
+__device__ __forceinline__ uint4 codes8_to_bf16_scaled(uint32_t w, float s) {
+    const uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)s);
+    const uint32_t hi = b >> 8, lo = b & 0xffu;
+    return codes8_to_bf16(w, ((hi ^ 0x80u) << 16) | (hi << 8), (lo << 16) | (lo << 8));
 }
 
 // 8 int8 (2 dwords) times rs -> 8 bf16 (4 dwords)
@@ -193,6 +203,7 @@ template <int NA, int NB>
 struct Stage<kGradX, NA, NB> {
     uint4 a[NA];
     uint32_t braw[NB];
+    float sn[NB];  // per-channel scale of the item's row (channel variant only)
     uint4 bcv[NB];
 };
 template <int NA, int NB>
@@ -213,7 +224,9 @@ struct Stage<kGradW, NA, NB> {
 // VEC: N % 8 == 0 (gy rows 16-byte aligned, 8-element chunks all in or out);
 // otherwise gy is read element by element.  GATED (grad_W, one split only):
 // the master-weight range gate `gate` applied as the tile is written.
-template <int MODE, class T, bool VEC, bool OUT_BF16, bool GATED = false>
+// CH (grad_x): `aux` holds one scale per output channel n (W_deq[n][k] =
+// aux[n] * code), folded into the bf16 codes; else aux is the one gamma.
+template <int MODE, class T, bool VEC, bool OUT_BF16, bool GATED = false, bool CH = false>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(
     const uint16_t* __restrict__ gy, const void* __restrict__ second, const float* __restrict__ aux,
     int M, int N, int K, int splits, int kper, void* __restrict__ out, SteGate gate) {
@@ -346,6 +359,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
                 const bool bv = b_ok && kb + bk + h * RPP < khi;
                 p.braw[h] = __builtin_amdgcn_raw_buffer_load_b16(rb, bv ? boff + h * bstep : kBufOOB, 0, 0);
             }
+            if constexpr (CH) {
+                const __amdgpu_buffer_rsrc_t rsn = make_buf(aux + kb);
+#pragma unroll
+                for (int h = 0; h < NB; ++h) {
+                    const bool tv = kb + bk + h * RPP < khi;
+                    p.sn[h] = __builtin_bit_cast(float, buf_load4(rsn, tv ? (uint32_t)(4 * (bk + h * RPP)) : kBufOOB));
+                }
+            }
         } else {
             const __amdgpu_buffer_rsrc_t ra = make_buf(gy + (int64_t)kb * N + rg);
 #pragma unroll
@@ -365,7 +386,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     auto convert = [&](StageT& p) {
 #pragma unroll
         for (int h = 0; h < NB; ++h) {
-            if constexpr (MODE == kGradX) p.bcv[h] = codes8_to_bf16(p.braw[h]);
+            if constexpr (MODE == kGradX && CH) p.bcv[h] = codes8_to_bf16_scaled(p.braw[h], p.sn[h]);
+            else if constexpr (MODE == kGradX) p.bcv[h] = codes8_to_bf16(p.braw[h]);
             else p.bcv[h] = int8x8_to_bf16(p.braw[h], p.sx[h] > 0.0f ? __builtin_amdgcn_rcpf(p.sx[h]) : 0.0f);
         }
     };
@@ -494,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
 
     // ---- epilogue: 32x32 block layout, lane holds column l32 and rows
     // 8*(r/4) + 4*g + r%4
-    const float scale = MODE == kGradX ? *aux : 1.0f;
+    const float scale = MODE == kGradX && !CH ? *aux : 1.0f;
     float* outf = static_cast<float*>(out);
     if constexpr (MODE == kGradW) outf += (int64_t)sp * N * K;
 #pragma unroll
@@ -606,7 +628,8 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 template <int MODE, class T, bool OUT_BF16>
 hipError_t launch_one(const uint16_t* gy, const void* second, const float* aux, int M, int N, int K,
-                      const Plan& p, void* out, hipStream_t s, const SteGate& gate = SteGate{}) {
+                      const Plan& p, void* out, hipStream_t s, const SteGate& gate = SteGate{},
+                      bool channel = false) {
     const unsigned grid = (unsigned)(p.tiles * p.splits);
     // the gate rides in the tile epilogue only without a token split (with
     // one, split_reduce_kernel applies it)
@@ -618,6 +641,16 @@ hipError_t launch_one(const uint16_t* gy, const void* second, const float* aux, 
         if (gated) {
             if (N % 8 == 0) BITNET_BWD_LAUNCH(true, true);
             else BITNET_BWD_LAUNCH(false, true);
+            return hipGetLastError();
+        }
+    } else {
+        if (channel) {
+            if (N % 8 == 0)
+                bwd_kernel<MODE, T, true, OUT_BF16, false, true><<<grid, kThreads, 0, s>>>(
+                    gy, second, aux, M, N, K, p.splits, p.kper, out, gate);
+            else
+                bwd_kernel<MODE, T, false, OUT_BF16, false, true><<<grid, kThreads, 0, s>>>(
+                    gy, second, aux, M, N, K, p.splits, p.kper, out, gate);
             return hipGetLastError();
         }
     }
@@ -637,17 +670,17 @@ size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* scale_x,
                           const uint8_t* Wp, const float* gamma, int64_t M, int64_t N, int64_t K,
                           void* grad_x, bool gx_bf16, float* grad_W, void* ws, hipStream_t s,
-                          const SteGate& gate) {
+                          const SteGate& gate, bool channel) {
     const int m = (int)M, n = (int)N, k = (int)K;
     if (grad_x) {
         const Plan p = plan_for(M, K, N, false);
         hipError_t e;
         if (p.big)
-            e = gx_bf16 ? launch_one<kGradX, TileL, true>(gy, Wp, gamma, m, n, k, p, grad_x, s)
-                        : launch_one<kGradX, TileL, false>(gy, Wp, gamma, m, n, k, p, grad_x, s);
+            e = gx_bf16 ? launch_one<kGradX, TileL, true>(gy, Wp, gamma, m, n, k, p, grad_x, s, SteGate{}, channel)
+                        : launch_one<kGradX, TileL, false>(gy, Wp, gamma, m, n, k, p, grad_x, s, SteGate{}, channel);
         else
-            e = gx_bf16 ? launch_one<kGradX, TileS, true>(gy, Wp, gamma, m, n, k, p, grad_x, s)
-                        : launch_one<kGradX, TileS, false>(gy, Wp, gamma, m, n, k, p, grad_x, s);
+            e = gx_bf16 ? launch_one<kGradX, TileS, true>(gy, Wp, gamma, m, n, k, p, grad_x, s, SteGate{}, channel)
+                        : launch_one<kGradX, TileS, false>(gy, Wp, gamma, m, n, k, p, grad_x, s, SteGate{}, channel);
         if (e != hipSuccess) return e;
     }
     if (grad_W) {

@@ -203,14 +203,18 @@ hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, fl
 hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
                                uint8_t* W_packed, float* gamma, void* ws, hipStream_t s);
 size_t weight_quant_ws_bytes(int64_t N);
+hipError_t launch_weight_quant_rows(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* W_packed,
+                                    float* gamma, void* ws, hipStream_t s);
+size_t weight_quant_rows_ws_bytes(int64_t N);
 hipError_t launch_pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* W_packed,
                                hipStream_t s);
+// channel: gamma holds one scale per output channel [N] (else one scalar)
 hipError_t launch_gemm_i8t2(const int8_t* Xq, const float* scale_x, const uint8_t* Wp,
                             const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
-                            int32_t* acc, hipStream_t s);
+                            int32_t* acc, hipStream_t s, bool channel = false);
 hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t* Wp,
                           const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
-                          int32_t* acc, hipStream_t s);
+                          int32_t* acc, hipStream_t s, bool channel = false);
 constexpr int64_t kGemvMaxM = 16;
 bool gemv_supported(int64_t M, int64_t K);  // M <= 16 and the activations fit LDS
 // Range gate of the master-weight gradient: grad_W[n][k] is kept where
@@ -220,10 +224,11 @@ struct SteGate {
     int bf16 = 0;  // W is bf16 (else fp32)
     float lo = 0.0f, hi = 0.0f;
 };
+// channel: gamma holds one scale per output channel [N] (grad_x only uses it)
 hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* scale_x,
                           const uint8_t* Wp, const float* gamma, int64_t M, int64_t N, int64_t K,
                           void* grad_x, bool gx_bf16, float* grad_W, void* ws, hipStream_t s,
-                          const SteGate& gate = SteGate{});
+                          const SteGate& gate = SteGate{}, bool channel = false);
 hipError_t launch_weight_clamp(void* W, bool w_bf16, int64_t count, float lo, float hi, hipStream_t s);
 hipError_t launch_code_counts(const uint8_t* W_packed, int64_t nbytes, uint64_t* counts, void* ws,
                               hipStream_t s);

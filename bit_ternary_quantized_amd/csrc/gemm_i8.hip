@@ -86,8 +86,10 @@ struct Stage {
 }  // namespace
 
 // VECB: K % 64 == 0, so a step's 16 bytes of a packed weight row are all in
-// or all out of range (else dword granularity).
-template <bool VECB>
+// or all out of range (else dword granularity).  CH: one scale per output
+// channel, gamma_p[n] (y = acc * (1/scale_x[m]) * gamma_p[n]); else the one
+// gamma of the matrix (y = acc * (gamma/scale_x[m])).
+template <bool VECB, bool CH = false>
 __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ scale_x,
     const uint8_t* __restrict__ Wp, const float* __restrict__ gamma_p, int M, int N, int K,
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
         const int nk = (K + BK - 1) / BK;
 
         {
-            const float g = *gamma_p;
+            const float g = CH ? 1.0f : *gamma_p;
             if (t < BM) row_scale[t] = (m0 + t < M) ? g / scale_x[m0 + t] : 0.0f;
         }
 
@@ -335,15 +337,26 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
                         const int cloc = cbase + j * 32;
                         // streaming (non-temporal) stores: the output is not read again here
                         if (!GUARD || (rloc < mlim && cloc < nlim))
-                            __builtin_nontemporal_store(value(acc[i][j][r], rs), &out[roff + cloc]);
+                            __builtin_nontemporal_store(value(acc[i][j][r], rs, j), &out[roff + cloc]);
                     }
                 }
                 // keep the scheduler from pulling later accumulators forward
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        auto yval = [](int v, float rs) { return (float)v * rs; };
-        auto aval = [](int v, float) { return v; };
+        // per-channel scales of this lane's JN columns (clamped index: the
+        // load is unconditional; columns past N are not stored)
+        float sc[CH ? JN : 1];
+        if constexpr (CH) {
+    #pragma unroll
+            for (int j = 0; j < JN; ++j) sc[j] = gamma_p[min(n0 + cbase + j * 32, N - 1)];
+        }
+        auto yval = [&](int v, float rs, int j) {
+            const float y = (float)v * rs;
+            if constexpr (CH) return y * sc[j];
+            else return y;
+        };
+        auto aval = [](int v, float, int) { return v; };
         if (mlim >= BM && nlim >= BN) store_tile(std::false_type{}, Yt, yval);
         else store_tile(std::true_type{}, Yt, yval);
         if (acc_out) {
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
 
 hipError_t launch_gemm_i8t2(const int8_t* Xq, const float* scale_x, const uint8_t* Wp,
                             const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
-                            int32_t* acc, hipStream_t s) {
+                            int32_t* acc, hipStream_t s, bool channel) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     if (tiles > INT32_MAX) return hipErrorInvalidValue;
     // one workgroup per CU at most (its LDS allows one), each walking tiles
@@ -366,12 +379,17 @@ hipError_t launch_gemm_i8t2(const int8_t* Xq, const float* scale_x, const uint8_
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)std::min<int64_t>(tiles, std::max(cus, 1));
-    if (K % BK == 0)
-        gemm_i8t2_kernel<true><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, (int)K,
-                                                         Y, acc);
-    else
-        gemm_i8t2_kernel<false><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, (int)K,
-                                                          Y, acc);
+#define BITNET_GEMM_LAUNCH(V_, C_)                                                                  \
+    gemm_i8t2_kernel<V_, C_><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, (int)K, Y, \
+                                                       acc)
+    if (K % BK == 0) {
+        if (channel) BITNET_GEMM_LAUNCH(true, true);
+        else BITNET_GEMM_LAUNCH(true, false);
+    } else {
+        if (channel) BITNET_GEMM_LAUNCH(false, true);
+        else BITNET_GEMM_LAUNCH(false, false);
+    }
+#undef BITNET_GEMM_LAUNCH
     return hipGetLastError();
 }
 

@@ -42,7 +42,8 @@ constexpr int kMaxGroups = 4;  // row groups per pass when S <= 4
 constexpr int kStageMaxK = 4096;  // LDS activation tile bound
 constexpr int kStageStride = kStageMaxK + 16;
 
-template <int S, bool FULL, bool STAGE>
+// CH: gamma_p holds one scale per output channel (see the GEMM).
+template <int S, bool FULL, bool STAGE, bool CH>
 __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ scale_x,
     const uint8_t* __restrict__ Wp, const float* __restrict__ gamma_p, int M, int N, int K,
@@ -175,8 +176,13 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
 #pragma unroll
             for (int v = 0; v < kWaves; ++v) sum += red[r][v][e];
             if (tk < M && nn < N) {
-                const float rs = *gamma_p / scale_x[tk];
-                Y[(int64_t)tk * N + nn] = (float)sum * rs;
+                if constexpr (CH) {
+                    const float rs = 1.0f / scale_x[tk];
+                    Y[(int64_t)tk * N + nn] = ((float)sum * rs) * gamma_p[nn];
+                } else {
+                    const float rs = *gamma_p / scale_x[tk];
+                    Y[(int64_t)tk * N + nn] = (float)sum * rs;
+                }
                 if (acc_out) acc_out[(int64_t)tk * N + nn] = sum;
             }
         }
@@ -188,7 +194,7 @@ bool gemv_supported(int64_t M, int64_t K) { return M <= kGemvMaxM && K <= 16 * 6
 
 hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t* Wp,
                           const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
-                          int32_t* acc, hipStream_t s) {
+                          int32_t* acc, hipStream_t s, bool channel) {
     if (!gemv_supported(M, K)) return hipErrorInvalidValue;
     const int64_t ngroups = (N + 15) / 16;
     const unsigned grid = (unsigned)std::min<int64_t>(ngroups, 256);
@@ -196,8 +202,14 @@ hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t*
     const bool full = K % (16 * 64) == 0;
     const bool stage = M > 8 && K <= kStageMaxK;  // measured: direct loads win up to 8 tokens
 #define BITNET_GEMV_LAUNCH(S_, F_, G_)                                                          \
-    gemv_t2_kernel<S_, F_, G_><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, \
-                                                        (int)K, Y, acc)
+    do {                                                                                       \
+        if (channel)                                                                           \
+            gemv_t2_kernel<S_, F_, G_, true><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, \
+                                                                     (int)N, (int)K, Y, acc);  \
+        else                                                                                   \
+            gemv_t2_kernel<S_, F_, G_, false><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, \
+                                                                      (int)N, (int)K, Y, acc); \
+    } while (0)
 #define BITNET_GEMV_CASE(S_)                                                                   \
     if (steps <= S_) {                                                                         \
         const bool f = full && steps == S_;                                                    \

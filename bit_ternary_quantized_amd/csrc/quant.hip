@@ -505,6 +505,89 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, i
     }
 }
 
+// ===================================================== per-row weight quant
+// The per-output-channel variant ("BitNet量化感知训练中的梯度传播优化",
+// section on the BitLinear implementation, 1: one scale per output row; the
+// zyxy.net STE lecture: the mean of |w| along each row): gamma_n =
+// max(T(|w_n|) / K, 1e-5) from the per-row tree sums of pass 1, each row's
+// code threshold from its own gamma (the rule above), and the pack with the
+// threshold of the row a byte belongs to.
+__device__ __forceinline__ float code_threshold(float g) {
+    const double t = (double)g * (0.5 + 0x1p-25);
+    float thr = (float)t;
+    if ((double)thr <= t) thr = __uint_as_float(__float_as_uint(thr) + 1u);
+    return thr;
+}
+
+__global__ __launch_bounds__(256) void wq_rows_gamma_kernel(const float* __restrict__ row_sums, int64_t N,
+                                                            int64_t K, float* __restrict__ gamma,
+                                                            float* __restrict__ thr) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    const float mean = row_sums[n] / (float)K;
+    const float g = fmaxf(mean, 1e-5f);
+    gamma[n] = g;
+    thr[n] = code_threshold(g);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void wq_pack_rows_kernel(const T* __restrict__ W, int64_t total4, int64_t KB,
+                                                           const float* __restrict__ thr,
+                                                           uint8_t* __restrict__ out) {
+    const int64_t base = (int64_t)blockIdx.x * (256 * kPackU) + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kPackU; ++u) {
+        const int64_t i = base + u * 256;  // packed byte: 4 weights of row i / KB
+        if (i < total4) {
+            float v[4];
+            if constexpr (sizeof(T) == 4) {
+                const float4 q = reinterpret_cast<const float4*>(W)[i];
+                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+            } else {
+                const uint2 q = reinterpret_cast<const uint2*>(W)[i];
+                v[0] = __uint_as_float(q.x << 16);
+                v[1] = __uint_as_float(q.x & 0xffff0000u);
+                v[2] = __uint_as_float(q.y << 16);
+                v[3] = __uint_as_float(q.y & 0xffff0000u);
+            }
+            const float t = thr[i / KB];
+            uint32_t byte = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) byte |= code_bits(v[j], t) << (2 * j);
+            out[i] = (uint8_t)byte;
+        }
+    }
+}
+
+size_t weight_quant_rows_ws_bytes(int64_t N) {
+    // row sums, then the row thresholds, each 256-byte aligned
+    return (size_t)(2 * ((N * 4 + 255) / 256) * 256);
+}
+
+hipError_t launch_weight_quant_rows(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* W_packed,
+                                    float* gamma, void* ws, hipStream_t s) {
+    float* row_sums = static_cast<float*>(ws);
+    float* thr = reinterpret_cast<float*>(static_cast<char*>(ws) + ((N * 4 + 255) / 256) * 256);
+    const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
+    if (w_bf16)
+        wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K, row_sums);
+    else
+        wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K, row_sums);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    wq_rows_gamma_kernel<<<(unsigned)((N + 255) / 256), 256, 0, s>>>(row_sums, N, K, gamma, thr);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total4 = N * K / 4;
+    const unsigned g3 = (unsigned)((total4 + 256 * kPackU - 1) / (256 * kPackU));
+    if (w_bf16)
+        wq_pack_rows_kernel<uint16_t><<<g3, 256, 0, s>>>(static_cast<const uint16_t*>(W), total4, K / 4, thr,
+                                                         W_packed);
+    else
+        wq_pack_rows_kernel<float><<<g3, 256, 0, s>>>(static_cast<const float*>(W), total4, K / 4, thr, W_packed);
+    return hipGetLastError();
+}
+
 size_t weight_quant_ws_bytes(int64_t N) {
     // row sums, then the threshold float, 256-byte aligned
     return (size_t)(((N * 4 + 255) / 256) * 256 + 256);

@@ -70,7 +70,8 @@ typedef enum {
     BITNET_OP_WEIGHT_QUANT = 0,
     BITNET_OP_LINEAR_BWD_STE = 1,
     BITNET_OP_LINEAR_FWD = 2,
-    BITNET_OP_CODE_COUNTS = 3
+    BITNET_OP_CODE_COUNTS = 3,
+    BITNET_OP_WEIGHT_QUANT_ROWS = 4
 } bitnet_op;
 
 /*
@@ -191,6 +192,43 @@ int bitnet_linear_bwd_ste_gated(const void *grad_y, int gy_dtype, const int8_t *
  */
 int bitnet_weight_clamp(void *W, int w_dtype, int64_t N, int64_t K, float lo, float hi,
                         void *stream);
+
+/*
+ * Per-output-channel weight scales: one scale per output row instead of one
+ * per matrix ("BitNet量化感知训练中的梯度传播优化" (blog.hotdry.top), section
+ * on the BitLinear implementation, 1: output = (sign(W) . s) x with
+ * s in R^{d_out}; zyxy.net STE lecture: the mean of |w| along each row).
+ *
+ * bitnet_weight_quant_rows: the absmean rule of bitnet_weight_quant applied
+ * to every row on its own,
+ *   gamma[n] = max(T(|W[n][:]|) / K, 1e-5)  (T: the row's pairwise tree),
+ *   code     = clamp(round(W[n][k] / gamma[n]), -1, 1), half to even,
+ * bit-exact like the per-matrix call.  gamma [N] fp32 (device), written;
+ * workspace >= bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT_ROWS, 0, N, K).
+ * Errors as bitnet_weight_quant.
+ *
+ * bitnet_linear_fwd_channel: bitnet_linear_fwd with a scale per output
+ * channel s[N] (the gamma of bitnet_weight_quant_rows, or a learned scale):
+ *   y[m][n] = (acc[m][n] * (1 / scale_x[m])) * s[n]   (fp32)
+ * Arguments, limits and errors as bitnet_linear_fwd.
+ *
+ * bitnet_linear_bwd_ste_channel: the STE backward at W_deq[n][k] =
+ * s[n] * code[n][k]: grad_x[m][k] = sum_n grad_y[m][n] * s[n] * code[n][k]
+ * (s rounded to bf16 once for the bf16 matrix cores); grad_W as
+ * bitnet_linear_bwd_ste.  Arguments, workspace and errors as
+ * bitnet_linear_bwd_ste with s [N] fp32 (device) in place of gamma.
+ */
+int bitnet_weight_quant_rows(const void *W, int w_dtype, int64_t N, int64_t K,
+                             uint8_t *W_packed, float *gamma, void *workspace,
+                             size_t workspace_bytes, void *stream);
+int bitnet_linear_fwd_channel(const int8_t *Xq, const float *scale_x, const uint8_t *W_packed,
+                              const float *s, int64_t M, int64_t N, int64_t K, float *Y,
+                              int32_t *acc, void *stream);
+int bitnet_linear_bwd_ste_channel(const void *grad_y, int gy_dtype, const int8_t *Xq,
+                                  const float *scale_x, const uint8_t *W_packed, const float *s,
+                                  int64_t M, int64_t N, int64_t K, void *grad_x, int gx_dtype,
+                                  float *grad_W, void *workspace, size_t workspace_bytes,
+                                  void *stream);
 
 /*
  * Counts of the codes in packed ternary weights, for the monitoring the

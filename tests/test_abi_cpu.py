@@ -159,6 +159,20 @@ def test_code_counts_reject_bad_arguments():
     assert lib.bitnet_code_counts(P, 4, 4, P, NULL, ws, NULL) == -5
 
 
+def test_channel_calls_reject_bad_arguments():
+    lib = bt.load_library()
+    ws = bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT_ROWS, 0, 4, 4)
+    assert ws >= 2 * 4 * 4 and ws % 256 == 0
+    assert lib.bitnet_weight_quant_rows(NULL, 0, 4, 4, P, P, P, ws, NULL) == -1
+    assert lib.bitnet_weight_quant_rows(P, 5, 4, 4, P, P, P, ws, NULL) == -3
+    assert lib.bitnet_weight_quant_rows(P, 0, 4, 6, P, P, P, ws, NULL) == -2
+    assert lib.bitnet_weight_quant_rows(P, 0, 4, 4, P, P, P, 16, NULL) == -5
+    assert lib.bitnet_linear_fwd_channel(P, P, P, NULL, 4, 4, 16, P, NULL, NULL) == -1
+    assert lib.bitnet_linear_fwd_channel(P, P, P, P, 4, 4, 8, P, NULL, NULL) == -2
+    assert lib.bitnet_linear_bwd_ste_channel(P, 1, P, P, P, NULL, 4, 4, 16, P, 0, NULL, NULL, 0, NULL) == -1
+    assert lib.bitnet_linear_bwd_ste_channel(P, 0, P, P, P, P, 4, 4, 16, P, 0, NULL, NULL, 0, NULL) == -3
+
+
 def test_pack_rejects_bad_arguments():
     lib = bt.load_library()
     assert lib.bitnet_pack_ternary(NULL, 4, 4, P, NULL) == -1
