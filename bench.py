@@ -99,6 +99,10 @@ def setup_layer(name):
         "counts": torch.empty(4, dtype=torch.int64, device=dev),
         "ws_cc": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_CODE_COUNTS, 0, N, K), dtype=torch.uint8,
                              device=dev),
+        "W_packed_rows": torch.empty(N, K // 4, dtype=torch.uint8, device=dev),
+        "gamma_rows": torch.empty(N, dtype=torch.float32, device=dev),
+        "ws_wqr": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT_ROWS, 0, N, K), dtype=torch.uint8,
+                              device=dev),
     }
     if gy is not None:
         buf["grad_x"] = torch.empty(M, K, dtype=torch.float32, device=dev)
@@ -120,6 +124,11 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
                        "peak_ops": INT8_PEAK_TOPS},
         # zero / +1 / -1 counts of the packed codes (monitoring): the codes read once
         "code_counts": {"bytes": N * K // 4 + 32, "bound": "hbm"},
+        # per-output-channel variants: per-row weight quant (two reads of W),
+        # the forward with a scale per output channel
+        "weight_quant_rows": {"bytes": 2 * N * K * w_bytes + N * K // 4 + 4 * N, "bound": "hbm"},
+        "linear_fwd_channel": {"ops": 2 * M * N * K, "bytes": M * K + N * K // 4 + 4 * M + 4 * N + 4 * M * N,
+                               "peak_ops": INT8_PEAK_TOPS},
     }
     if gy:
         c["linear_bwd_ste"] = {"ops": 4 * M * N * K,
@@ -127,6 +136,8 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
                                "peak_ops": BF16_PEAK_TFLOPS}
         c["bwd_grad_x"] = {"ops": 2 * M * N * K, "bytes": 2 * M * N + N * K // 4 + 4 + 4 * M * K,
                            "peak_ops": BF16_PEAK_TFLOPS}
+        c["bwd_grad_x_channel"] = {"ops": 2 * M * N * K, "bytes": 2 * M * N + N * K // 4 + 4 * N + 4 * M * K,
+                                   "peak_ops": BF16_PEAK_TFLOPS}
         c["bwd_grad_W"] = {"ops": 2 * M * N * K, "bytes": 2 * M * N + M * K + 4 * M + 4 * N * K,
                            "peak_ops": BF16_PEAK_TFLOPS}
         # RMSNorm backward (after the STE backward): x and fp32 grad_x read, fp32 grad_X written
@@ -154,6 +165,9 @@ KERNEL_OF = {
     "bwd_grad_W_gated": "bwd_kernel<grad_W> with the range gate (+ split_reduce_kernel when split)",
     "weight_clamp": "weight_clamp_kernel",
     "code_counts": "code_counts_kernel + code_counts_final_kernel",
+    "weight_quant_rows": "wq_row_abs_sum_kernel + wq_rows_gamma_kernel + wq_pack_rows_kernel",
+    "linear_fwd_channel": "gemm_i8t2_kernel (per-channel epilogue) or gemv_t2_kernel",
+    "bwd_grad_x_channel": "bwd_kernel<grad_x> (per-channel code scales)",
 }
 # sources each call's kernels are built from: the HBM traffic recorded under
 # profiles/ is used only while these files are unchanged
@@ -167,6 +181,9 @@ SOURCES_OF = {
     "bwd_grad_W_gated": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
     "weight_clamp": ["bit_ternary_quantized_amd/csrc/quant.hip"],
     "code_counts": ["bit_ternary_quantized_amd/csrc/quant.hip"],
+    "weight_quant_rows": ["bit_ternary_quantized_amd/csrc/quant.hip"],
+    "linear_fwd_channel": ["bit_ternary_quantized_amd/csrc/gemm_i8.hip", "bit_ternary_quantized_amd/csrc/gemv.hip"],
+    "bwd_grad_x_channel": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -281,10 +298,19 @@ def bench_layer(args, name):
     # the backward call's two products, each timed on its own (not part of
     # the step): grad_x is one kernel, grad_W one kernel plus the ordered
     # split reduction when its token range is split
-    parts = {"code_counts": lambda: bt.bitnet_code_counts(b["W_packed"], K, counts=b["counts"], workspace=b["ws_cc"])}
+    parts = {
+        "code_counts": lambda: bt.bitnet_code_counts(b["W_packed"], K, counts=b["counts"], workspace=b["ws_cc"]),
+        # per-output-channel variants (own buffers; not part of the step)
+        "weight_quant_rows": lambda: bt.bitnet_weight_quant_rows(w, W_packed=b["W_packed_rows"], gamma=b["gamma_rows"],
+                                                                 workspace=b["ws_wqr"]),
+        "linear_fwd_channel": lambda: bt.bitnet_linear_fwd_channel(b["Xq"], b["scale_x"], b["W_packed_rows"],
+                                                                   b["gamma_rows"], Y=b["Y"]),
+    }
     if gy is not None:
         parts["bwd_grad_x"] = lambda: bt.bitnet_linear_bwd_ste(
             gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], want_grad_W=False, grad_x=b["grad_x"])
+        parts["bwd_grad_x_channel"] = lambda: bt.bitnet_linear_bwd_ste_channel(
+            gy, b["Xq"], b["scale_x"], b["W_packed_rows"], b["gamma_rows"], want_grad_W=False, grad_x=b["grad_x"])
         parts["bwd_grad_W"] = lambda: bt.bitnet_linear_bwd_ste(
             gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], want_grad_x=False, grad_W=b["grad_W"],
             workspace=b["ws_bwd"])
@@ -344,8 +370,8 @@ def bench_layer(args, name):
     value = fwd_bwd * M * N * K / (ms * 1e-3) / 1e12
     # roofline: the longest single product of the step (the backward call
     # counts as its two products)
-    cands = [n for n in timed if n not in ("linear_bwd_ste", "rmsnorm_bwd", "bwd_grad_W_gated", "weight_clamp",
-                                           "code_counts")]
+    # the step's own products only (the other timed calls are variants)
+    cands = [n for n in timed if n in ("act_quant", "weight_quant", "linear_fwd", "bwd_grad_x", "bwd_grad_W")]
     dom = max(cands, key=lambda n: per[n])
     roof = dict(rate(counts[dom], per[dom]))
     roof["kernel"] = KERNEL_OF[dom] + f" ({dom})"

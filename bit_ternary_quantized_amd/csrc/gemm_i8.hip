@@ -121,6 +121,14 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
             const float g = CH ? 1.0f : *gamma_p;
             if (t < BM) row_scale[t] = (m0 + t < M) ? g / scale_x[m0 + t] : 0.0f;
         }
+        // per-channel scales of this lane's JN output columns, requested now
+        // so their latency hides under the K loop (clamped index: the load is
+        // unconditional; columns past N are not stored)
+        float sc[CH ? JN : 1];
+        if constexpr (CH) {
+    #pragma unroll
+            for (int j = 0; j < JN; ++j) sc[j] = gamma_p[min(n0 + (wave & 3) * 64 + (lane & 31) + j * 32, N - 1)];
+        }
 
         // Activations: thread tg stages chunks tg + 256 u (row c / 4, chunk c % 4)
         // of the group's 128 rows; offsets relative to the step's base address.
@@ -344,13 +352,6 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        // per-channel scales of this lane's JN columns (clamped index: the
-        // load is unconditional; columns past N are not stored)
-        float sc[CH ? JN : 1];
-        if constexpr (CH) {
-    #pragma unroll
-            for (int j = 0; j < JN; ++j) sc[j] = gamma_p[min(n0 + cbase + j * 32, N - 1)];
-        }
         auto yval = [&](int v, float rs, int j) {
             const float y = (float)v * rs;
             if constexpr (CH) return y * sc[j];
