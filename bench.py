@@ -59,6 +59,8 @@ def parse():
                     choices=["small_llama", "tiny", "prefill_7b", "decode_7b", "qat_70b_mlp", "copy"])
     ap.add_argument("--decode-m", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the step's calls and its two backward products (no variant calls)")
     return ap.parse_args()
 
 
@@ -350,6 +352,8 @@ def bench_layer(args, name):
     # one graph; K replays of each, bracketed by HIP events on the stream
     # they run on.  A bounded spin first lets the host enqueue the whole loop,
     # so no host gap sits between two events.
+    if args.step_only:
+        parts = {n: f for n, f in parts.items() if n in ("bwd_grad_x", "bwd_grad_W")}
     allc = dict(calls, **parts)
     timed = list(allc)
     g_rep = {n: capture(lambda n=n: [allc[n]() for _ in range(REPS)]) for n in timed}
