@@ -438,6 +438,24 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
+    // Barrier between the phases of the loop.  With KSPLIT each group stages
+    // and reads only its own tiles, and a tile written in a memory phase is
+    // read no earlier than the group's next memory phase, two barriers later:
+    // the LDS fence is then needed only where a compute phase ends, where each
+    // wave first waits for its own LDS operations (lgkmcnt 0), long complete
+    // by then; the barrier that ends a memory phase does not wait for its LDS
+    // writes.  Without KSPLIT the groups read each other's B columns one
+    // barrier after they are written, so every barrier keeps the fence.
+    auto phase_barrier = [&](bool drain_lds) {
+        if constexpr (KS) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (drain_lds) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            barrier();
+        }
+    };
 
     // One step of the group (its i-th): memory phase = operands of step i,
     // step i + 1 (loaded two steps ago, converted since) into LDS, loads of
@@ -449,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
         read_operands(i);
         store_lds(i + 1, cur);
         load_global(i + 3, cur);
-        barrier();
+        phase_barrier(false);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq)
@@ -460,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
                     acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kq][ii], b[kq][j], acc[ii][j], 0, 0, 0);
         convert(nx);
         __builtin_amdgcn_s_setprio(0);
-        barrier();
+        phase_barrier(true);
     };
 
     // Prologue: the group's step 0 in LDS buffer 0, steps 1 and 2 loading.

@@ -10,6 +10,9 @@
 namespace bitnet {
 
 constexpr int kWave = 64;  // CDNA wavefront width
+// s_waitcnt operand (gfx9 encoding) that waits for lgkmcnt 0 only: vmcnt at
+// its maximum 63 (bits 3:0 and 15:14), expcnt at its maximum 7 (bits 6:4)
+constexpr int kWaitLgkm0 = 0xC07F;
 
 // ------------------------------------------------------------ element loads
 // bf16 -> fp32 is exact: the 16 bits are the high half of the binary32.
