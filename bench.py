@@ -426,6 +426,38 @@ def bench_decode(args):
     ms = statistics.fmean(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / copies
     nbytes = N * K // 4 + M * K + 4 * M + 4 + 4 * M * N
     gbs = nbytes / (ms * 1e-3) / 1e9
+
+    # a whole decode step from the unquantized activations, per weight copy:
+    # act_quant then the GEMV (two launches), and the fused call (one launch)
+    x = d["x"].to(dev)
+    q2, s2 = torch.empty_like(q), torch.empty_like(s)
+
+    def per_launch_ms(fn):
+        gr = capture(lambda: [fn(wp) for wp in wps])
+        for _ in range(max(1, args.warmup // copies)):
+            gr.replay()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda._sleep(SLEEP_CYCLES)
+        for i in range(reps):
+            e[i].record()
+            gr.replay()
+        e[-1].record()
+        torch.cuda.synchronize()
+        return statistics.fmean(e[i].elapsed_time(e[i + 1]) for i in range(reps)) / copies
+
+    # algorithmic bytes of a decode step: x (bf16) and the packed weights in, Y out
+    step_bytes = N * K // 4 + 2 * M * K + 4 + 4 * M * N
+
+    def entry(t_ms, nb):
+        a = nb / (t_ms * 1e-3) / 1e9
+        return {"ms": t_ms, "achieved": a, "unit": "GB/s", "frac": a / HBM_PEAK_GBS}
+
+    kernels = {"linear_fwd": entry(ms, nbytes)}
+    kernels["act_quant+linear_fwd"] = entry(per_launch_ms(lambda wp: (
+        bt.bitnet_act_quant(x, 1e-5, Xq=q2, scale_x=s2), bt.bitnet_linear_fwd(q2, s2, wp, gm, Y=Y))), step_bytes)
+    kernels["linear_fwd_decode"] = entry(
+        per_launch_ms(lambda wp: bt.bitnet_linear_fwd_decode(x, wp, gm, 1e-5, Y=Y)), step_bytes)
     out = {
         "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -434,6 +466,7 @@ def bench_decode(args):
                    "launches_timed": reps * copies},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "gemv_t2_kernel"},
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -26,7 +26,7 @@ EXPORTS = (
     "bitnet_weight_quant", "bitnet_act_quant", "bitnet_linear_fwd", "bitnet_linear_bwd_ste",
     "bitnet_pack_ternary", "bitnet_rmsnorm_bwd", "bitnet_linear_bwd_ste_gated", "bitnet_weight_clamp",
     "bitnet_code_counts", "bitnet_weight_quant_rows", "bitnet_linear_fwd_channel",
-    "bitnet_linear_bwd_ste_channel",
+    "bitnet_linear_bwd_ste_channel", "bitnet_linear_fwd_decode",
     "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
 )
 
@@ -64,6 +64,7 @@ def load_library(path: str = LIB_PATH):
         "bitnet_weight_quant_rows": (c_int, [p, c_int, i64, i64, p, p, p, sz, p]),
         "bitnet_linear_fwd_channel": (c_int, [p, p, p, p, i64, i64, i64, p, p, p]),
         "bitnet_linear_bwd_ste_channel": (c_int, [p, c_int, p, p, p, p, i64, i64, i64, p, c_int, p, p, sz, p]),
+        "bitnet_linear_fwd_decode": (c_int, [p, c_int, p, p, i64, i64, i64, ctypes.c_float, p, p, p, p]),
         "bitnet_workspace_bytes": (sz, [c_int, i64, i64, i64]),
         "bitnet_status_str": (ctypes.c_char_p, [c_int]),
         "bitnet_version": (c_int, []),
@@ -287,6 +288,29 @@ def bitnet_linear_fwd_channel(Xq, scale_x, W_packed, s, Y=None, acc=None, want_a
     _check("bitnet_linear_fwd_channel", lib.bitnet_linear_fwd_channel(
         _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(s), M, N, K, _ptr(Y), _ptr(acc), _stream(stream)))
     return Y, acc
+
+
+def bitnet_linear_fwd_decode(X, W_packed, gamma, eps: float = 1e-5, Y=None, Xq=None, scale_x=None,
+                             want_q=False, stream=None):
+    """Decode forward in one launch: act_quant(X) then the packed GEMV, M <= 16,
+    K <= 4096 -> (Y f32 [M,N], Xq int8 or None, scale_x f32 or None)."""
+    lib = load_library()
+    for t, n in ((X, "X"), (W_packed, "W_packed"), (gamma, "gamma")):
+        _need(t, n)
+    M, K = X.shape
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K:
+        raise ValueError("W_packed must be [N, K/4]")
+    if Y is None:
+        Y = torch.empty(M, N, dtype=torch.float32, device=X.device)
+    if want_q and Xq is None:
+        Xq = torch.empty(M, K, dtype=torch.int8, device=X.device)
+    if want_q and scale_x is None:
+        scale_x = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check("bitnet_linear_fwd_decode", lib.bitnet_linear_fwd_decode(
+        _ptr(X), _dtype_code(X), _ptr(W_packed), _ptr(gamma), M, N, K, ctypes.c_float(eps), _ptr(Y),
+        _ptr(Xq), _ptr(scale_x), _stream(stream)))
+    return Y, Xq, scale_x
 
 
 def bitnet_linear_bwd_ste_channel(grad_y, Xq, scale_x, W_packed, s, want_grad_x=True, want_grad_W=True,

@@ -13,6 +13,8 @@ constexpr int kWave = 64;  // CDNA wavefront width
 // s_waitcnt operand (gfx9 encoding) that waits for lgkmcnt 0 only: vmcnt at
 // its maximum 63 (bits 3:0 and 15:14), expcnt at its maximum 7 (bits 6:4)
 constexpr int kWaitLgkm0 = 0xC07F;
+// s_waitcnt operand that waits for vmcnt 0 only (expcnt 7, lgkmcnt 15)
+constexpr int kWaitVm0 = 0x0F70;
 
 // ------------------------------------------------------------ element loads
 // bf16 -> fp32 is exact: the 16 bits are the high half of the binary32.
@@ -41,6 +43,22 @@ template <> struct Vec16<uint16_t> {  // bf16 stored as raw bits
         }
     }
 };
+
+// the 16 raw bytes of a Vec16 load, widened to floats
+template <typename T>
+__device__ __forceinline__ void widen16(const uint4& r, float (&v)[Vec16<T>::E]) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    if constexpr (Vec16<T>::E == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+}
 
 __device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_elem(const uint16_t* p, int64_t i) {
@@ -220,6 +238,14 @@ hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t*
                           int32_t* acc, hipStream_t s, bool channel = false);
 constexpr int64_t kGemvMaxM = 16;
 bool gemv_supported(int64_t M, int64_t K);  // M <= 16 and the activations fit LDS
+// Fused decode: act_quant of X (fp32 or bf16) and the packed GEMV in one
+// launch; xq_out / sx_out (optional) receive q and scale_x.
+hipError_t launch_gemv_decode(const void* X, bool x_bf16, const uint8_t* Wp, const float* gamma,
+                              int64_t M, int64_t N, int64_t K, float eps, float* Y, int8_t* xq_out,
+                              float* sx_out, hipStream_t s);
+// M <= 16, K <= 4096 and M * ceil(K / (64 * elements per 16 bytes)) <= 128
+// (every bf16 shape; fp32: M * ceil(K / 256) <= 128, e.g. 8 rows of 4096)
+bool gemv_decode_fits(bool x_bf16, int64_t M, int64_t K);
 // Range gate of the master-weight gradient: grad_W[n][k] is kept where
 // lo <= W[n][k] <= hi and set to 0 elsewhere; w == nullptr: no gate.
 struct SteGate {

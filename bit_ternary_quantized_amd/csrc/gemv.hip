@@ -23,6 +23,24 @@
 // weight byte of the pass is requested with no branch in front of the loads;
 // all row groups are computed before one reduction of the 16 partial int32
 // tiles in LDS.
+//
+// Fused decode variant (TX = bf16 bits or float): the activations come in
+// unquantized and every workgroup quantizes them itself, so a decode step is
+// one launch instead of two.  The quantization is act_quant's, operation for
+// operation: act_quant's blocks (64 lanes x one 16-byte chunk, lane l holding
+// elements 64E*b + E*l .. +E-1 of block b) are the work items, shared out
+// over the 16 waves; each item's block sum of squares (in-lane tree, then the
+// lane tree) and block max go to LDS; each row's scale comes from its
+// partials in block order (the pairwise tree over blocks, missing blocks +0,
+// which leaves the value unchanged) with the same binary32 steps; then each
+// item's q goes to the LDS activation tile in natural order, byte-transposed
+// in registers as it is read.  So q and scale_x are bit-identical to
+// act_quant's and Y to act_quant followed by this GEMV.  Every workgroup
+// quantizes all M*K activations (all of K feeds its row groups), about 11
+// VALU operations per element: cheap for a few tokens, more than the
+// separate act_quant launch it saves from about 8 tokens of 4096 on.
+#include <type_traits>
+
 #include "common.h"
 
 namespace bitnet {
@@ -32,6 +50,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxGroups = 4;  // row groups per pass when S <= 4
+// fused decode: at most this many (token row, block) items per wave, so the
+// raw X chunks (4 registers each) stay in registers with no spill
+constexpr int kDecodeMaxItems = 8;
 }  // namespace
 
 // S: MFMA steps (64 columns) per wave, Kw = 64*S; FULL: K == 16*Kw, so every
@@ -43,18 +64,31 @@ constexpr int kStageMaxK = 4096;  // LDS activation tile bound
 constexpr int kStageStride = kStageMaxK + 16;
 
 // CH: gamma_p holds one scale per output channel (see the GEMM).
-template <int S, bool FULL, bool STAGE, bool CH>
+// TX: int8_t, Xin = Xq and scale_x given; uint16_t (bf16) or float, Xin = X
+// unquantized, quantized here with eps (K <= kStageMaxK), scale_x unused,
+// and workgroup 0 writes q and the scales to xq_out / sx_out when non-null.
+template <int S, bool FULL, bool STAGE, bool CH, typename TX = int8_t, int IT = 1>
 __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
-    const int8_t* __restrict__ Xq, const float* __restrict__ scale_x,
+    const void* __restrict__ Xin, const float* __restrict__ scale_x,
     const uint8_t* __restrict__ Wp, const float* __restrict__ gamma_p, int M, int N, int K,
-    float* __restrict__ Y, int32_t* __restrict__ acc_out) {
+    float* __restrict__ Y, int32_t* __restrict__ acc_out, float eps, int8_t* __restrict__ xq_out,
+    float* __restrict__ sx_out) {
+    constexpr bool QX = !std::is_same<TX, int8_t>::value;
+    const int8_t* __restrict__ Xq = static_cast<const int8_t*>(Xin);
     // row groups per pass: weight (G*S) and activation (4*S) registers stay
     // within the budget of 4 waves per SIMD
     constexpr int G = S >= 16 ? 1 : (S >= 8 ? 2 : kMaxGroups);
     __shared__ int red[G][kWaves][256];
-    __shared__ __align__(16) uint8_t As[STAGE ? 16 * kStageStride : 16];
+    __shared__ __align__(16) uint8_t As[STAGE || QX ? 16 * kStageStride : 16];
+    __shared__ float tok_scale[QX ? 16 : 1], tok_inv[QX ? 16 : 1];
+    // fused: per token row and block, the block's sum of squares and max |x|
+    constexpr int QE = Vec16<std::conditional_t<QX, TX, float>>::E;
+    constexpr int QBLK = kWave * QE;
+    constexpr int QNB = QX ? kStageMaxK / QBLK : 1;  // blocks of the longest row
+    __shared__ float blk_sq[QX ? 16 : 1][QNB], blk_max[QX ? 16 : 1][QNB];
     constexpr int Kw = 64 * S;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform in the wave
     const int col = lane & 15, g = lane >> 4;
     const int kb = wave * Kw + g * (Kw / 4);  // first column of this lane
     const int KB = K / 4;
@@ -65,7 +99,26 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
     constexpr int kAPer = STAGE ? (16 * kStageMaxK / 16) / kThreads : 1;
     uint4 ac[kAPer];  // coalesced chunks for the LDS tile (STAGE)
     const int kch = K / 16;
-    if constexpr (STAGE) {
+    // fused: work item i = (token row i / nblk, block i % nblk); wave w takes
+    // items w, w + 16, ...  Their raw X chunks are requested first, with
+    // unconditional buffer loads (offsets past the rows read zeros, as
+    // act_quant pads), so that the wait for them is not a wait for the
+    // weight stream that follows.
+    uint4 xc[QX ? IT : 1];
+    const int qnblk = (K + QBLK - 1) / QBLK;
+    if constexpr (QX) {
+        static_assert(S <= kStageMaxK / (16 * 64), "fused rows fit the LDS tile");
+        const __amdgpu_buffer_rsrc_t rx = make_buf(Xin);
+#pragma unroll
+        for (int j = 0; j < IT; ++j) {
+            const int it = wave + kWaves * j;
+            const int row = it / qnblk, blk = it - row * qnblk;
+            // K % 16 == 0: a lane's QE elements are all inside the row or all past it
+            const int k0 = blk * QBLK + lane * QE;
+            const bool v = row < M && k0 < K;
+            xc[j] = buf_load16(rx, v ? (uint32_t)(((int64_t)row * K + k0) * (int)sizeof(TX)) : kBufOOB);
+        }
+    } else if constexpr (STAGE) {
 #pragma unroll
         for (int i = 0; i < kAPer; ++i) {
             const int c = t + i * kThreads;
@@ -83,11 +136,9 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
             if (tv && (FULL || k < K)) av[s] = *reinterpret_cast<const uint4*>(Xq + (int64_t)col * K + k);
         }
     }
-    bool transposed = false;
 
-    for (int base = blockIdx.x; base < ngroups; base += gridDim.x * G) {
-        // ---- weights for up to G row groups, all loads in flight
-        uint32_t wq[G][S];
+    // ---- weights for up to G row groups of the pass at `base`, all loads in flight
+    auto load_weights = [&](int base, uint32_t (&wq)[G][S]) {
 #pragma unroll
         for (int r = 0; r < G; ++r) {
             const int grp = base + r * gridDim.x;
@@ -114,40 +165,10 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
                 }
             }
         }
-        if (!transposed) {
-            if constexpr (STAGE) {
-#pragma unroll
-                for (int i = 0; i < kAPer; ++i) {
-                    const int c = t + i * kThreads;
-                    if (c < 16 * kch) {
-                        const int tok = c / kch, kc = c - tok * kch;
-                        const uint32_t a[4] = {ac[i].x, ac[i].y, ac[i].z, ac[i].w};
-                        uint32_t o[4];
-                        transpose4x4_bytes(a, o);
-                        *reinterpret_cast<uint4*>(As + tok * kStageStride + 16 * kc) =
-                            make_uint4(o[0], o[1], o[2], o[3]);
-                    }
-                }
-                __syncthreads();
-#pragma unroll
-                for (int s = 0; s < S; ++s) {
-                    const int k = kb + 16 * s;
-                    av[s] = (FULL || k < K) ? *reinterpret_cast<const uint4*>(As + col * kStageStride + k)
-                                            : make_uint4(0, 0, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int s = 0; s < S; ++s) {
-                    const uint32_t a[4] = {av[s].x, av[s].y, av[s].z, av[s].w};
-                    uint32_t o[4];
-                    transpose4x4_bytes(a, o);
-                    av[s] = make_uint4(o[0], o[1], o[2], o[3]);
-                }
-            }
-            transposed = true;
-        }
+    };
 
-        // ---- products of every row group, then one reduction
+    // ---- products of every row group of the pass, then one reduction
+    auto products = [&](int base, const uint32_t (&wq)[G][S]) {
         int nr = 0;
 #pragma unroll
         for (int r = 0; r < G; ++r) {
@@ -176,17 +197,172 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
 #pragma unroll
             for (int v = 0; v < kWaves; ++v) sum += red[r][v][e];
             if (tk < M && nn < N) {
+                const float sx = QX ? tok_scale[tk] : scale_x[tk];
                 if constexpr (CH) {
-                    const float rs = 1.0f / scale_x[tk];
+                    const float rs = 1.0f / sx;
                     Y[(int64_t)tk * N + nn] = ((float)sum * rs) * gamma_p[nn];
                 } else {
-                    const float rs = *gamma_p / scale_x[tk];
+                    const float rs = *gamma_p / sx;
                     Y[(int64_t)tk * N + nn] = (float)sum * rs;
                 }
                 if (acc_out) acc_out[(int64_t)tk * N + nn] = sum;
             }
         }
         __syncthreads();
+    };
+
+    if constexpr (QX) {
+        // ---- fused: the first pass is peeled so that the X loads, the first
+        // weight loads and the quantization are straight-line code (a wait
+        // for X then counts only the weight loads issued after it)
+        constexpr int E = QE, BLK = QBLK, NBX = QNB;
+        using TW = std::conditional_t<QX, TX, float>;
+        int base = blockIdx.x;  // < ngroups: the grid has at most ngroups workgroups
+        // X first, alone: requested behind the weight stream it arrives late
+        // (every workgroup reads the same few lines); then the weight loads,
+        // and the quantization runs while they stream in
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t wq[G][S];
+        load_weights(base, wq);
+        // 1) per item: act_quant's block partials (in-lane tree, lane tree;
+        //    lane maxima, wave max)
+#pragma unroll
+        for (int j = 0; j < IT; ++j) {
+            const int it = wave + kWaves * j;
+            const int row = it / qnblk, blk = it - row * qnblk;
+            if (row < M) {
+                float v[E], sq[E], amax = 0.0f;
+                widen16<TW>(xc[j], v);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    sq[e] = v[e] * v[e];
+                    amax = fmaxf(amax, fabsf(v[e]));
+                }
+                const float bsum = wave_tree_sum(lane_tree<E>(sq));
+                amax = wave_max(amax);
+                if (lane == 0) {
+                    blk_sq[row][blk] = bsum;
+                    blk_max[row][blk] = amax;
+                }
+            }
+        }
+        // token rows past M are zeros in the tile
+        if (wave >= M)
+            for (int k0 = lane * 16; k0 < qnblk * BLK; k0 += kWave * 16)
+                *reinterpret_cast<uint4*>(As + wave * kStageStride + k0) = make_uint4(0, 0, 0, 0);
+        __syncthreads();
+        // 2) wave r < M: row r's 1/RMS and scale from the partials in block
+        //    order (missing blocks +0: the same tree value)
+        if (wave < M) {
+            float bs[NBX], amax = 0.0f;
+#pragma unroll
+            for (int b = 0; b < NBX; ++b) {
+                bs[b] = b < qnblk ? blk_sq[wave][b] : 0.0f;
+                amax = fmaxf(amax, b < qnblk ? blk_max[wave][b] : 0.0f);
+            }
+            const float ss = lane_tree<NBX>(bs);
+            const float ms = ss / (float)K;
+            const float d = sqrtf(ms + eps);
+            const float inv = 1.0f / d;
+            const float a = amax * inv;  // max|x * inv| == max|x| * inv
+            const float scale = 127.0f / fmaxf(a, 1e-5f);
+            if (lane == 0) {
+                tok_inv[wave] = inv;
+                tok_scale[wave] = scale;
+                if (sx_out && blockIdx.x == 0) sx_out[wave] = scale;
+            }
+        }
+        __syncthreads();
+        // 3) per item: its block of q into the tile
+#pragma unroll
+        for (int j = 0; j < IT; ++j) {
+            const int it = wave + kWaves * j;
+            const int row = it / qnblk, blk = it - row * qnblk;
+            if (row < M) {
+                const float inv = tok_inv[row], scale = tok_scale[row];
+                float v[E];
+                widen16<TW>(xc[j], v);
+                uint32_t pk[E / 4];
+#pragma unroll
+                for (int i = 0; i < E / 4; ++i) {
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float r = rintf((v[4 * i + e] * inv) * scale);
+                        r = fminf(fmaxf(r, -128.0f), 127.0f);
+                        w |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * e);
+                    }
+                    pk[i] = w;
+                }
+                const int k0 = blk * BLK + lane * E;
+                uint8_t* qp = As + row * kStageStride + k0;
+                if constexpr (E == 8) *reinterpret_cast<uint2*>(qp) = make_uint2(pk[0], pk[1]);
+                else *reinterpret_cast<uint32_t*>(qp) = pk[0];
+                if (xq_out && blockIdx.x == 0 && k0 < K) {
+                    int8_t* qo = xq_out + (int64_t)row * K + k0;
+                    if constexpr (E == 8) *reinterpret_cast<uint2*>(qo) = make_uint2(pk[0], pk[1]);
+                    else *reinterpret_cast<uint32_t*>(qo) = pk[0];
+                }
+            }
+        }
+        __syncthreads();
+        // the operand: natural-order q from the tile, byte-transposed
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int k = kb + 16 * s;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (FULL || k < K) v = *reinterpret_cast<const uint4*>(As + col * kStageStride + k);
+            const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+            uint32_t o[4];
+            transpose4x4_bytes(a, o);
+            av[s] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        products(base, wq);
+        for (base += gridDim.x * G; base < ngroups; base += gridDim.x * G) {
+            uint32_t wq2[G][S];
+            load_weights(base, wq2);
+            products(base, wq2);
+        }
+    } else {
+        bool transposed = false;
+        for (int base = blockIdx.x; base < ngroups; base += gridDim.x * G) {
+            uint32_t wq[G][S];
+            load_weights(base, wq);
+            if (!transposed) {
+                if constexpr (STAGE) {
+#pragma unroll
+                    for (int i = 0; i < kAPer; ++i) {
+                        const int c = t + i * kThreads;
+                        if (c < 16 * kch) {
+                            const int tok = c / kch, kc = c - tok * kch;
+                            const uint32_t a[4] = {ac[i].x, ac[i].y, ac[i].z, ac[i].w};
+                            uint32_t o[4];
+                            transpose4x4_bytes(a, o);
+                            *reinterpret_cast<uint4*>(As + tok * kStageStride + 16 * kc) =
+                                make_uint4(o[0], o[1], o[2], o[3]);
+                        }
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int s = 0; s < S; ++s) {
+                        const int k = kb + 16 * s;
+                        av[s] = (FULL || k < K) ? *reinterpret_cast<const uint4*>(As + col * kStageStride + k)
+                                                : make_uint4(0, 0, 0, 0);
+                    }
+                } else {
+#pragma unroll
+                    for (int s = 0; s < S; ++s) {
+                        const uint32_t a[4] = {av[s].x, av[s].y, av[s].z, av[s].w};
+                        uint32_t o[4];
+                        transpose4x4_bytes(a, o);
+                        av[s] = make_uint4(o[0], o[1], o[2], o[3]);
+                    }
+                }
+                transposed = true;
+            }
+            products(base, wq);
+        }
     }
 }
 
@@ -205,10 +381,12 @@ hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t*
     do {                                                                                       \
         if (channel)                                                                           \
             gemv_t2_kernel<S_, F_, G_, true><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, \
-                                                                     (int)N, (int)K, Y, acc);  \
+                                                                     (int)N, (int)K, Y, acc, 0.0f, \
+                                                                     nullptr, nullptr);         \
         else                                                                                   \
             gemv_t2_kernel<S_, F_, G_, false><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, \
-                                                                      (int)N, (int)K, Y, acc); \
+                                                                      (int)N, (int)K, Y, acc, 0.0f, \
+                                                                      nullptr, nullptr);         \
     } while (0)
 #define BITNET_GEMV_CASE(S_)                                                                   \
     if (steps <= S_) {                                                                         \
@@ -227,6 +405,62 @@ hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t*
 #undef BITNET_GEMV_CASE
 #undef BITNET_GEMV_LAUNCH
     return hipErrorInvalidValue;
+}
+
+namespace {
+
+template <typename TX, int IT>
+hipError_t decode_launch(const TX* X, const uint8_t* Wp, const float* gamma, int64_t M, int64_t N,
+                         int64_t K, float eps, float* Y, int8_t* xq_out, float* sx_out, hipStream_t s) {
+    const int64_t ngroups = (N + 15) / 16;
+    const unsigned grid = (unsigned)std::min<int64_t>(ngroups, 256);
+    const int64_t steps = (K + 16 * 64 - 1) / (16 * 64);
+    const bool full = K % (16 * 64) == 0;
+#define BITNET_DECODE_CASE(S_)                                                                  \
+    if (steps <= S_) {                                                                          \
+        if (full && steps == S_)                                                                \
+            gemv_t2_kernel<S_, true, false, false, TX, IT><<<grid, kThreads, 0, s>>>(           \
+                X, nullptr, Wp, gamma, (int)M, (int)N, (int)K, Y, nullptr, eps, xq_out, sx_out); \
+        else                                                                                    \
+            gemv_t2_kernel<S_, false, false, false, TX, IT><<<grid, kThreads, 0, s>>>(          \
+                X, nullptr, Wp, gamma, (int)M, (int)N, (int)K, Y, nullptr, eps, xq_out, sx_out); \
+        return hipGetLastError();                                                               \
+    }
+    BITNET_DECODE_CASE(1)
+    BITNET_DECODE_CASE(2)
+    BITNET_DECODE_CASE(4)
+#undef BITNET_DECODE_CASE
+    return hipErrorInvalidValue;
+}
+
+template <typename TX>
+hipError_t decode_dispatch(const TX* X, const uint8_t* Wp, const float* gamma, int64_t M, int64_t N,
+                           int64_t K, float eps, float* Y, int8_t* xq_out, float* sx_out, hipStream_t s) {
+    // work items (token row, block) per wave
+    constexpr int64_t blk = kWave * Vec16<TX>::E;
+    const int64_t per_wave = (M * ((K + blk - 1) / blk) + kWaves - 1) / kWaves;
+    if (per_wave <= 1) return decode_launch<TX, 1>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
+    if (per_wave <= 2) return decode_launch<TX, 2>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
+    if (per_wave <= 4) return decode_launch<TX, 4>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
+    if (per_wave <= 8) return decode_launch<TX, 8>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool gemv_decode_fits(bool x_bf16, int64_t M, int64_t K) {
+    const int64_t blk = kWave * (x_bf16 ? 8 : 4);
+    return M >= 1 && M <= kGemvMaxM && K >= 1 && K <= kStageMaxK &&
+           M * ((K + blk - 1) / blk) <= kDecodeMaxItems * kWaves;
+}
+
+hipError_t launch_gemv_decode(const void* X, bool x_bf16, const uint8_t* Wp, const float* gamma,
+                              int64_t M, int64_t N, int64_t K, float eps, float* Y, int8_t* xq_out,
+                              float* sx_out, hipStream_t s) {
+    if (!gemv_decode_fits(x_bf16, M, K) || K % 16 != 0) return hipErrorInvalidValue;
+    if (x_bf16)
+        return decode_dispatch(static_cast<const uint16_t*>(X), Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
+    return decode_dispatch(static_cast<const float*>(X), Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
 }
 
 }  // namespace bitnet

@@ -224,6 +224,32 @@ int bitnet_weight_quant_rows(const void *W, int w_dtype, int64_t N, int64_t K,
 int bitnet_linear_fwd_channel(const int8_t *Xq, const float *scale_x, const uint8_t *W_packed,
                               const float *s, int64_t M, int64_t N, int64_t K, float *Y,
                               int32_t *acc, void *stream);
+
+/*
+ * Decode forward from the unquantized activations in one launch: the
+ * activation quantizer of bitnet_act_quant fused into the packed GEMV of
+ * bitnet_linear_fwd ([NOTES 5.1]: fuse the quantize and dequantize steps with
+ * the product).  Every workgroup quantizes the M <= 16 token rows itself
+ * with bitnet_act_quant's arithmetic, operation for operation, so
+ *   Y (and Xq, scale_x when requested) are bit-identical to
+ *   bitnet_act_quant(X, ..., eps) followed by bitnet_linear_fwd.
+ *   X        [M][K] fp32 or bf16 (x_dtype);  W_packed [N][K/4];  gamma 1 fp32
+ *   Y        [M][N] fp32, written
+ *   Xq       [M][K] int8, written when non-NULL (16-byte aligned)
+ *   scale_x  [M] fp32, written when non-NULL
+ * Every workgroup quantizes all M rows itself, so this pays off for a few
+ * tokens (measured at K = 4096, N = 11008: 20% faster than the two calls at
+ * M = 1, even at M = 8, slower at M = 16).
+ * 1 <= M <= 16, K % 16 == 0, K <= 4096 (the quantized rows stay in LDS);
+ * fp32 X also M * ceil(K / 256) <= 128 (the raw rows stay in registers: up
+ * to 8 rows of 4096); N < 2^23; eps >= 0.  Other shapes: bitnet_act_quant
+ * followed by bitnet_linear_fwd.
+ * Errors: BITNET_E_ARG, BITNET_E_SHAPE, BITNET_E_DTYPE, BITNET_E_ALIGN,
+ * BITNET_E_HIP.
+ */
+int bitnet_linear_fwd_decode(const void *X, int x_dtype, const uint8_t *W_packed,
+                             const float *gamma, int64_t M, int64_t N, int64_t K, float eps,
+                             float *Y, int8_t *Xq, float *scale_x, void *stream);
 int bitnet_linear_bwd_ste_channel(const void *grad_y, int gy_dtype, const int8_t *Xq,
                                   const float *scale_x, const uint8_t *W_packed, const float *s,
                                   int64_t M, int64_t N, int64_t K, void *grad_x, int gx_dtype,

@@ -173,6 +173,28 @@ def test_channel_calls_reject_bad_arguments():
     assert lib.bitnet_linear_bwd_ste_channel(P, 0, P, P, P, P, 4, 4, 16, P, 0, NULL, NULL, 0, NULL) == -3
 
 
+def test_decode_call_rejects_bad_arguments():
+    lib = bt.load_library()
+    f = lib.bitnet_linear_fwd_decode
+    eps = ctypes.c_float(1e-5)
+    # (X, dtype, W_packed, gamma, M, N, K, eps, Y, Xq, scale_x, stream)
+    assert f(NULL, 1, P, P, 1, 16, 64, eps, P, NULL, NULL, NULL) == -1
+    assert f(P, 1, P, NULL, 1, 16, 64, eps, P, NULL, NULL, NULL) == -1
+    assert f(P, 1, P, P, 1, 16, 64, eps, NULL, NULL, NULL, NULL) == -1
+    assert f(P, 2, P, P, 1, 16, 64, eps, P, NULL, NULL, NULL) == -3
+    assert f(P, 1, P, P, 1, 16, 64, ctypes.c_float(-1.0), P, NULL, NULL, NULL) == -1
+    assert f(P, 1, P, P, 17, 16, 64, eps, P, NULL, NULL, NULL) == -2   # M > 16: two calls instead
+    assert f(P, 1, P, P, 0, 16, 64, eps, P, NULL, NULL, NULL) == -2
+    assert f(P, 1, P, P, 1, 16, 4112, eps, P, NULL, NULL, NULL) == -2  # K > 4096
+    assert f(P, 0, P, P, 9, 16, 4096, eps, P, NULL, NULL, NULL) == -2  # 9 fp32 rows of 4096: 144 blocks
+    assert f(P, 1, P, P, 1, 16, 72, eps, P, NULL, NULL, NULL) == -2    # K % 16
+    assert f(P, 1, P, P, 1, 0, 64, eps, P, NULL, NULL, NULL) == -2
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    assert f(odd, 1, P, P, 1, 16, 64, eps, P, NULL, NULL, NULL) == -4
+    assert f(P, 1, P, P, 1, 16, 64, eps, P, odd, NULL, NULL) == -4
+    assert f(P, 1, P, P, 1, 16, 64, eps, P, NULL, ctypes.c_void_p((1 << 20) + 2), NULL) == -4
+
+
 def test_pack_rejects_bad_arguments():
     lib = bt.load_library()
     assert lib.bitnet_pack_ternary(NULL, 4, 4, P, NULL) == -1

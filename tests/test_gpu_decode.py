@@ -1,0 +1,110 @@
+"""Fused decode forward (bitnet_linear_fwd_decode): the activation quantizer
+and the packed GEMV in one launch.
+
+The call promises bit-identical results to bitnet_act_quant followed by
+bitnet_linear_fwd, so q, scale_x and Y are compared bit for bit with those
+two calls; q and scale_x are also compared bit for bit with the oracle's
+act_quant, and Y with the oracle's forward within relative 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_ternary_quantized_amd as bt
+import oracle
+import workloads
+from gpu_util import assert_y_close, f32_bits_equal, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(M, N, K, dtype, seed, special=None):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, K, generator=g)
+    if special == "zero_row":
+        x[0] = 0.0
+    elif special == "outliers":
+        x[:, ::97] *= 40.0
+    elif special == "single":
+        x.zero_()
+        x[:, K // 2] = -2.5
+    codes = workloads.ternary_codes(N, K, 0.35, seed=seed + 1)
+    gamma = torch.tensor([0.0173], dtype=torch.float32)
+    return x.to(dtype), codes, gamma
+
+
+def _check(x, codes, gamma):
+    wp = to_dev(torch.from_numpy(oracle.pack(codes.numpy())))
+    xd, gd = to_dev(x), to_dev(gamma)
+    y, q, s = bt.bitnet_linear_fwd_decode(xd, wp, gd, want_q=True)
+    q2, s2 = bt.bitnet_act_quant(xd)
+    y2, _ = bt.bitnet_linear_fwd(q2, s2, wp, gd)
+    torch.cuda.synchronize()
+    # the two-call path, bit for bit
+    assert torch.equal(q, q2)
+    assert f32_bits_equal(s.cpu().numpy(), s2.cpu().numpy())
+    assert f32_bits_equal(y.cpu().numpy(), y2.cpu().numpy())
+    # the oracle
+    q_ref, s_ref = oracle.act_quant(host(x))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert f32_bits_equal(s.cpu().numpy(), s_ref)
+    _, y_ref = oracle.linear_fwd(q_ref, s_ref, codes.numpy(), float(gamma[0]))
+    assert_y_close(y.cpu().numpy(), y_ref)
+    return y
+
+
+# M: one token, a few, 8 / 9, 16; K: one MFMA step, partial 512-element
+# blocks (ragged lane chunks), whole 1024-column steps and the 4096 limit
+# (fp32: at most 128 row blocks of 256, e.g. 8 rows of 4096); N: one row
+# group, ragged groups, more groups than CUs
+DECODE_SHAPES = [
+    (1, 16, 16), (1, 300, 256), (3, 33, 1040), (8, 100, 528), (8, 257, 4096), (9, 70, 4096),
+    (16, 1000, 512), (16, 64, 4096), (5, 4200, 2048), (2, 17, 48), (4, 40, 4096),
+]
+
+
+@pytest.mark.parametrize("M,N,K", DECODE_SHAPES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_matches_two_calls_and_oracle(M, N, K, dtype):
+    print(f"linear_fwd_decode M={M} N={N} K={K} {dtype}", flush=True)
+    x, codes, gamma = _case(M, N, K, dtype, seed=M * 131 + N * 7 + K)
+    if dtype == torch.float32 and M * -(-K // 256) > 128:
+        # beyond the call's documented register budget: rejected, nothing launched
+        wp = to_dev(torch.from_numpy(oracle.pack(codes.numpy())))
+        with pytest.raises(bt.BitnetError):
+            bt.bitnet_linear_fwd_decode(to_dev(x), wp, to_dev(gamma))
+        return
+    _check(x, codes, gamma)
+
+
+@pytest.mark.parametrize("special", ["zero_row", "outliers", "single"])
+def test_decode_special_rows(special):
+    print(f"linear_fwd_decode special {special}", flush=True)
+    x, codes, gamma = _case(4, 96, 1024, torch.bfloat16, seed=7, special=special)
+    _check(x, codes, gamma)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_full_size(M):
+    # the 7B-class decode layer: K = 4096, N = 11008
+    print(f"linear_fwd_decode full size M={M}", flush=True)
+    x, codes, gamma = _case(M, 11008, 4096, torch.bfloat16, seed=M)
+    _check(x, codes, gamma)
+
+
+def test_decode_rejects_shapes_beyond_the_register_budget():
+    x, codes, gamma = _case(9, 32, 4096, torch.float32, seed=3)
+    wp = to_dev(torch.from_numpy(oracle.pack(codes.numpy())))
+    with pytest.raises(bt.BitnetError):
+        bt.bitnet_linear_fwd_decode(to_dev(x), wp, to_dev(gamma))
+
+
+def test_decode_without_q_outputs_and_repeat():
+    # Xq / scale_x not requested; two calls in a row give the same Y
+    x, codes, gamma = _case(6, 200, 768, torch.bfloat16, seed=11)
+    wp = to_dev(torch.from_numpy(oracle.pack(codes.numpy())))
+    y1, q1, s1 = bt.bitnet_linear_fwd_decode(to_dev(x), wp, to_dev(gamma))
+    y2, _, _ = bt.bitnet_linear_fwd_decode(to_dev(x), wp, to_dev(gamma))
+    torch.cuda.synchronize()
+    assert q1 is None and s1 is None
+    assert torch.equal(y1, y2)

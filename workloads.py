@@ -26,6 +26,7 @@ import math
 import torch
 
 SEED_X, SEED_W, SEED_GY, SEED_AUX = 0, 1, 2, 3
+SEED_XDEC = 4  # decode's unquantized activations
 
 WORKLOADS = {
     "tiny": dict(M=32, K=256, N=256, x_dtype="f32", w_dtype="f32", w_std=0.02, gy=False),
@@ -108,7 +109,10 @@ def decode_inputs(M: int, K: int = 4096, N: int = 11008, p_zero: float = 0.35, s
     codes = ternary_codes(N, K, p_zero, SEED_W + seed)
     scale_x = (25.0 + 20.0 * torch.rand(M, generator=_gen(SEED_AUX + seed), dtype=torch.float64)).to(torch.float32)
     gamma = torch.tensor([0.02 * math.sqrt(2.0 / math.pi)], dtype=torch.float32)
-    return {"q": q, "codes": codes, "scale_x": scale_x, "gamma": gamma, "M": M, "N": N, "K": K}
+    # the unquantized layer input of the same tokens (bf16 N(0,1)), for the
+    # fused decode call that quantizes it itself
+    x = torch.randn(M, K, generator=_gen(SEED_XDEC + seed), dtype=torch.float32).to(torch.bfloat16)
+    return {"q": q, "codes": codes, "scale_x": scale_x, "gamma": gamma, "x": x, "M": M, "N": N, "K": K}
 
 
 def workload(name: str, seed: int = 0, M: int = None) -> dict:
