@@ -451,7 +451,8 @@ def bench_decode(args):
 
     def entry(t_ms, nb):
         a = nb / (t_ms * 1e-3) / 1e9
-        return {"ms": t_ms, "achieved": a, "unit": "GB/s", "frac": a / HBM_PEAK_GBS}
+        return {"ms": t_ms, "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": a / HBM_PEAK_GBS}
 
     kernels = {"linear_fwd": entry(ms, nbytes)}
     kernels["act_quant+linear_fwd"] = entry(per_launch_ms(lambda wp: (
