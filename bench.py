@@ -4,8 +4,9 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 RMSNorm + per-token int8 activation quantization, absmean ternary weight
-quantization + packing, the ternary x int8 forward with dequantization,
-and the STE backward (grad_x and grad_W).  Inputs are generated once on the
+quantization + packing (both quantizers in one bitnet_quant_operands call),
+the ternary x int8 forward with dequantization, and the STE backward
+(grad_x and grad_W).  Inputs are generated once on the
 host (seeded, see workloads.py), copied to HBM before timing, and every
 output buffer is preallocated, so the timed region is device work only.
 
@@ -60,8 +61,9 @@ def parse():
     ap.add_argument("--decode-m", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-streams", action="store_true",
-                    help="run the two quantizers (act_quant, weight_quant) on two streams inside the "
-                         "step graph (default: every call in order on one stream)")
+                    help="run the two quantizers as two calls (act_quant, weight_quant) on two streams "
+                         "inside the step graph (default: one bitnet_quant_operands call; every call in "
+                         "order on one stream)")
     ap.add_argument("--step-only", action="store_true",
                     help="time only the step's calls and its two backward products (no variant calls)")
     return ap.parse_args()
@@ -127,6 +129,9 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
         "weight_quant": {"bytes": 2 * N * K * w_bytes + N * K // 4 + 4, "bound": "hbm"},
         "linear_fwd": {"ops": 2 * M * N * K, "bytes": M * K + N * K // 4 + 4 * M + 4 * M * N,
                        "peak_ops": INT8_PEAK_TOPS},
+        # both quantizers in one call: act_quant's bytes plus weight_quant's
+        "quant_operands": {"bytes": M * K * x_bytes + M * K + 4 * M + 2 * N * K * w_bytes + N * K // 4 + 4,
+                           "bound": "hbm"},
         # zero / +1 / -1 counts of the packed codes (monitoring): the codes read once
         "code_counts": {"bytes": N * K // 4 + 32, "bound": "hbm"},
         # per-output-channel variants: per-row weight quant (two reads of W),
@@ -170,6 +175,7 @@ KERNEL_OF = {
     "bwd_grad_W_gated": "bwd_kernel<grad_W> with the range gate (+ split_reduce_kernel when split)",
     "weight_clamp": "weight_clamp_kernel",
     "code_counts": "code_counts_kernel + code_counts_final_kernel",
+    "quant_operands": "quant_operands_kernel + wq_pack_kernel (+ wq_gamma_kernel)",
     "weight_quant_rows": "wq_row_abs_sum_kernel + wq_rows_gamma_kernel + wq_pack_rows_kernel",
     "linear_fwd_channel": "gemm_i8t2_kernel (per-channel epilogue) or gemv_t2_kernel",
     "bwd_grad_x_channel": "bwd_kernel<grad_x> (per-channel code scales)",
@@ -186,6 +192,7 @@ SOURCES_OF = {
     "bwd_grad_W_gated": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
     "weight_clamp": ["bit_ternary_quantized_amd/csrc/quant.hip"],
     "code_counts": ["bit_ternary_quantized_amd/csrc/quant.hip"],
+    "quant_operands": ["bit_ternary_quantized_amd/csrc/quant.hip"],
     "weight_quant_rows": ["bit_ternary_quantized_amd/csrc/quant.hip"],
     "linear_fwd_channel": ["bit_ternary_quantized_amd/csrc/gemm_i8.hip", "bit_ternary_quantized_amd/csrc/gemv.hip"],
     "bwd_grad_x_channel": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
@@ -305,6 +312,10 @@ def bench_layer(args, name):
     # split reduction when its token range is split
     parts = {
         "code_counts": lambda: bt.bitnet_code_counts(b["W_packed"], K, counts=b["counts"], workspace=b["ws_cc"]),
+        # both quantizers in one call (one launch fewer; same outputs)
+        "quant_operands": lambda: bt.bitnet_quant_operands(x, w, 1e-5, Xq=b["Xq"], scale_x=b["scale_x"],
+                                                           W_packed=b["W_packed"], gamma=b["gamma"],
+                                                           workspace=b["ws_wq"]),
         # per-output-channel variants (own buffers; not part of the step)
         "weight_quant_rows": lambda: bt.bitnet_weight_quant_rows(w, W_packed=b["W_packed_rows"], gamma=b["gamma_rows"],
                                                                  workspace=b["ws_wqr"]),
@@ -351,10 +362,17 @@ def bench_layer(args, name):
         main_fn()
         main.wait_event(e1)
 
+    # The step: both quantizers in one call (bitnet_quant_operands: the same
+    # outputs as act_quant + weight_quant with one launch fewer), the forward,
+    # the backward.
+    step_calls = dict(calls)
+    step_calls["quant_operands"] = parts["quant_operands"]
+    step_names = ["quant_operands", "linear_fwd"] + (["linear_bwd_ste"] if gy is not None else [])
+
     def step():
         if not args.two_streams:
-            for n in names:
-                calls[n]()
+            for n in step_names:
+                step_calls[n]()
             return
         fork_join(calls["act_quant"], calls["weight_quant"])
         calls["linear_fwd"]()
@@ -418,7 +436,8 @@ def bench_layer(args, name):
         "data": "synthetic",
         "config": {"workload": name, "M": M, "N": N, "K": K, "x_dtype": str(d["x"].dtype).split(".")[-1],
                    "w_dtype": str(d["w"].dtype).split(".")[-1],
-                   "step": "+".join(names), "launch": "one HIP graph per step",
+                   "step": "act_quant+weight_quant (two streams)+" + "+".join(step_names[1:]) if args.two_streams
+                   else "+".join(step_names), "launch": "one HIP graph per step",
                    "schedule": "two streams: act_quant || weight_quant, then linear_fwd, then linear_bwd_ste"
                    if args.two_streams else "every call in order on one stream"},
         "roofline": roof,

@@ -26,7 +26,7 @@ EXPORTS = (
     "bitnet_weight_quant", "bitnet_act_quant", "bitnet_linear_fwd", "bitnet_linear_bwd_ste",
     "bitnet_pack_ternary", "bitnet_rmsnorm_bwd", "bitnet_linear_bwd_ste_gated", "bitnet_weight_clamp",
     "bitnet_code_counts", "bitnet_weight_quant_rows", "bitnet_linear_fwd_channel",
-    "bitnet_linear_bwd_ste_channel", "bitnet_linear_fwd_decode",
+    "bitnet_linear_bwd_ste_channel", "bitnet_linear_fwd_decode", "bitnet_quant_operands",
     "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
 )
 
@@ -65,6 +65,7 @@ def load_library(path: str = LIB_PATH):
         "bitnet_linear_fwd_channel": (c_int, [p, p, p, p, i64, i64, i64, p, p, p]),
         "bitnet_linear_bwd_ste_channel": (c_int, [p, c_int, p, p, p, p, i64, i64, i64, p, c_int, p, p, sz, p]),
         "bitnet_linear_fwd_decode": (c_int, [p, c_int, p, p, i64, i64, i64, ctypes.c_float, p, p, p, p]),
+        "bitnet_quant_operands": (c_int, [p, c_int, i64, i64, ctypes.c_float, p, p, p, c_int, i64, p, p, p, sz, p]),
         "bitnet_workspace_bytes": (sz, [c_int, i64, i64, i64]),
         "bitnet_status_str": (ctypes.c_char_p, [c_int]),
         "bitnet_version": (c_int, []),
@@ -150,6 +151,34 @@ def bitnet_act_quant(X: torch.Tensor, eps: float = 1e-5, Xq=None, scale_x=None, 
     _check("bitnet_act_quant", lib.bitnet_act_quant(
         _ptr(X), _dtype_code(X), M, K, ctypes.c_float(eps), _ptr(Xq), _ptr(scale_x), _stream(stream)))
     return Xq, scale_x
+
+
+def bitnet_quant_operands(X, W, eps: float = 1e-5, Xq=None, scale_x=None, W_packed=None, gamma=None,
+                          workspace=None, stream=None):
+    """act_quant(X) and weight_quant(W) with one launch fewer -> (Xq, scale_x, W_packed, gamma)."""
+    lib = load_library()
+    _need(X, "X")
+    _need(W, "W")
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("X and W must share K")
+    dev = X.device
+    if Xq is None:
+        Xq = torch.empty(M, K, dtype=torch.int8, device=dev)
+    if scale_x is None:
+        scale_x = torch.empty(M, dtype=torch.float32, device=dev)
+    if W_packed is None:
+        W_packed = torch.empty(N, K // 4, dtype=torch.uint8, device=dev)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=dev)
+    ws_bytes = lib.bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT, 0, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    _check("bitnet_quant_operands", lib.bitnet_quant_operands(
+        _ptr(X), _dtype_code(X), M, K, ctypes.c_float(eps), _ptr(Xq), _ptr(scale_x), _ptr(W), _dtype_code(W), N,
+        _ptr(W_packed), _ptr(gamma), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return Xq, scale_x, W_packed, gamma
 
 
 def bitnet_linear_fwd(Xq, scale_x, W_packed, gamma, Y=None, acc=None, want_acc=False, stream=None):

@@ -72,6 +72,24 @@ int bitnet_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, float eps
                                                as_stream(stream)));
 }
 
+int bitnet_quant_operands(const void* X, int x_dtype, int64_t M, int64_t K, float eps, int8_t* Xq,
+                          float* scale_x, const void* W, int w_dtype, int64_t N, uint8_t* W_packed,
+                          float* gamma, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!X || !Xq || !scale_x || !W || !W_packed || !gamma) return BITNET_E_ARG;
+    if (!float_dtype(x_dtype) || !float_dtype(w_dtype)) return BITNET_E_DTYPE;
+    if (M < 1 || N < 1 || K < 1 || K % 4 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return BITNET_E_SHAPE;
+    if (!(eps >= 0.0f)) return BITNET_E_ARG;
+    if (!aligned16(X) || !aligned16(Xq) || !aligned4(scale_x) || !aligned16(W) || !aligned16(W_packed) ||
+        !aligned4(gamma))
+        return BITNET_E_ALIGN;
+    if (!workspace || workspace_bytes < bitnet::weight_quant_ws_bytes(N)) return BITNET_E_WORKSPACE;
+    if (!aligned16(workspace)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_quant_operands(X, x_dtype == BITNET_BF16, M, K, eps, Xq, scale_x, W,
+                                                    w_dtype == BITNET_BF16, N, W_packed, gamma, workspace,
+                                                    as_stream(stream)));
+}
+
 }  // extern "C"
 
 namespace {

@@ -224,6 +224,11 @@ hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, fl
 hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
                                uint8_t* W_packed, float* gamma, void* ws, hipStream_t s);
 size_t weight_quant_ws_bytes(int64_t N);
+// act_quant of X and weight_quant of W (same K) with one launch fewer;
+// outputs bit-identical to the two; ws as weight_quant's
+hipError_t launch_quant_operands(const void* X, bool x_bf16, int64_t M, int64_t K, float eps, int8_t* Xq,
+                                 float* scale_x, const void* W, bool w_bf16, int64_t N, uint8_t* W_packed,
+                                 float* gamma, void* ws, hipStream_t s);
 hipError_t launch_weight_quant_rows(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* W_packed,
                                     float* gamma, void* ws, hipStream_t s);
 size_t weight_quant_rows_ws_bytes(int64_t N);

@@ -198,16 +198,17 @@ __global__ __launch_bounds__(kAqWaves * kWave) void act_quant_kernel(
 // so no branch splits the wait counters.  Same arithmetic as above.
 constexpr int kAqMaxGroups = 1024;  // workgroups of the row-walking grid (measured: 512-2048 within 3%)
 
+// The body takes its workgroup index and the number of workgroups walking
+// the rows, so a combined launch can run it on part of its grid.
 template <typename T, int NB>
-__global__ __launch_bounds__(kAqWaves * kWave) void act_quant_rows_kernel(
-    const T* __restrict__ X, int64_t M, int64_t K, float eps, int8_t* __restrict__ Q,
-    float* __restrict__ S) {
+__device__ __forceinline__ void act_quant_rows_body(const T* __restrict__ X, int64_t M, int64_t K, float eps,
+                                                    int8_t* __restrict__ Q, float* __restrict__ S, int bid,
+                                                    int nblocks) {
     constexpr int E = Vec16<T>::E;
     constexpr int BLK = kWave * E;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave_id =
-        (int64_t)blockIdx.x * kAqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * kAqWaves;
+    const int64_t wave_id = (int64_t)bid * kAqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)nblocks * kAqWaves;
     if (wave_id >= M) return;  // uniform per wave
 
     auto load_row = [&](int64_t row, bool valid, uint4 (&c)[NB]) {
@@ -291,6 +292,13 @@ __global__ __launch_bounds__(kAqWaves * kWave) void act_quant_rows_kernel(
     }
 }
 
+template <typename T, int NB>
+__global__ __launch_bounds__(kAqWaves * kWave) void act_quant_rows_kernel(
+    const T* __restrict__ X, int64_t M, int64_t K, float eps, int8_t* __restrict__ Q,
+    float* __restrict__ S) {
+    act_quant_rows_body<T, NB>(X, M, K, eps, Q, S, blockIdx.x, gridDim.x);
+}
+
 template <typename T>
 static hipError_t act_quant_dispatch(const T* X, int64_t M, int64_t K, float eps, int8_t* Q,
                                      float* S, hipStream_t s) {
@@ -349,13 +357,13 @@ hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, fl
 constexpr int kWqWaves = 4;
 
 template <typename T>
-__global__ __launch_bounds__(kWqWaves * kWave) void wq_row_abs_sum_kernel(
-    const T* __restrict__ W, int64_t N, int64_t K, float* __restrict__ row_sums) {
+__device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int64_t N, int64_t K,
+                                                    float* __restrict__ row_sums, int bid) {
     constexpr int E = Vec16<T>::E;
     constexpr int BLK = kWave * E;
     constexpr int G = 8;  // loads in flight per lane
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t row = (int64_t)blockIdx.x * kWqWaves + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)bid * kWqWaves + (threadIdx.x >> 6);
     if (row >= N) return;
     const T* w = W + row * K;
     const int64_t nblk = (K + BLK - 1) / BLK;
@@ -385,6 +393,12 @@ __global__ __launch_bounds__(kWqWaves * kWave) void wq_row_abs_sum_kernel(
         }
     }
     if (lane == 0) row_sums[row] = st.total();
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWqWaves * kWave) void wq_row_abs_sum_kernel(
+    const T* __restrict__ W, int64_t N, int64_t K, float* __restrict__ row_sums) {
+    wq_row_abs_sum_body<T>(W, N, K, row_sums, blockIdx.x);
 }
 
 // Pass 2: the tree over the N row sums.  With P = N rounded up to a power of
@@ -745,19 +759,12 @@ hipError_t launch_weight_clamp(void* W, bool w_bf16, int64_t count, float lo, fl
 }
 
 
-hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
-                               uint8_t* W_packed, float* gamma, void* ws, hipStream_t s) {
+// Passes 2 and 3 (gamma, threshold, packing) from the row sums in ws.
+static hipError_t weight_quant_pack(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* W_packed,
+                                    float* gamma, void* ws, hipStream_t s) {
     float* row_sums = static_cast<float*>(ws);
     float* thr = reinterpret_cast<float*>(static_cast<char*>(ws) + ((N * 4 + 255) / 256) * 256);
-    const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
-    if (w_bf16)
-        wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K,
-                                                           row_sums);
-    else
-        wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K,
-                                                        row_sums);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
     const int64_t total4 = N * K / 4;
     const unsigned g3 = (unsigned)((total4 + 256 * kPackU - 1) / (256 * kPackU));
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
@@ -777,6 +784,84 @@ hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
     else
         wq_pack_kernel<float, false><<<g3, 256, 0, s>>>(Wf, total4, thr, row_sums, N, K, gamma, W_packed);
     return hipGetLastError();
+}
+
+hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
+                               uint8_t* W_packed, float* gamma, void* ws, hipStream_t s) {
+    float* row_sums = static_cast<float*>(ws);
+    const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
+    if (w_bf16)
+        wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K,
+                                                           row_sums);
+    else
+        wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K,
+                                                        row_sums);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s);
+}
+
+// ============================================= both quantizers, one launch fewer
+// Launch 1 runs act_quant's row-walking kernel on workgroups [0, A) and the
+// weight row sums on [A, A + ceil(N/4)): two independent streams of HBM
+// reads in one grid, with no launch boundary between them.  Launch 2 (and
+// the gamma kernel for large N) is weight_quant's.  Same bodies, same
+// arithmetic: the outputs are bit-identical to the two separate calls.
+template <typename TX, int NB, typename TW>
+__global__ __launch_bounds__(kAqWaves * kWave) void quant_operands_kernel(
+    const TX* __restrict__ X, int64_t M, int64_t K, float eps, int8_t* __restrict__ Q, float* __restrict__ S,
+    int act_blocks, const TW* __restrict__ W, int64_t N, float* __restrict__ row_sums) {
+    static_assert(kAqWaves == kWqWaves, "one workgroup shape for both bodies");
+    const int b = blockIdx.x;  // uniform
+    if (b < act_blocks) act_quant_rows_body<TX, NB>(X, M, K, eps, Q, S, b, act_blocks);
+    else wq_row_abs_sum_body<TW>(W, N, K, row_sums, b - act_blocks);
+}
+
+namespace {
+template <typename TX, typename TW>
+hipError_t quant_operands_pass1(const TX* X, int64_t M, int64_t K, float eps, int8_t* Q, float* S, const TW* W,
+                                int64_t N, float* row_sums, int nblk, hipStream_t s) {
+    const int64_t groups = (M + kAqWaves - 1) / kAqWaves;
+    const int act_blocks = (int)std::min<int64_t>(groups, kAqMaxGroups);
+    const int64_t wq_blocks = (N + kWqWaves - 1) / kWqWaves;
+    const dim3 grid((unsigned)(act_blocks + wq_blocks)), block(kAqWaves * kWave);
+    switch (nblk) {
+        case 1: quant_operands_kernel<TX, 1, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums); break;
+        case 2: quant_operands_kernel<TX, 2, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums); break;
+        case 4: quant_operands_kernel<TX, 4, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums); break;
+        case 8: quant_operands_kernel<TX, 8, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums); break;
+        case 16: quant_operands_kernel<TX, 16, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+template <typename TX>
+hipError_t quant_operands_w(const TX* X, int64_t M, int64_t K, float eps, int8_t* Q, float* S, const void* W,
+                            bool w_bf16, int64_t N, float* row_sums, int nblk, hipStream_t s) {
+    if (w_bf16) return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const uint16_t*>(W), N, row_sums, nblk, s);
+    return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const float*>(W), N, row_sums, nblk, s);
+}
+}  // namespace
+
+hipError_t launch_quant_operands(const void* X, bool x_bf16, int64_t M, int64_t K, float eps, int8_t* Xq,
+                                 float* scale_x, const void* W, bool w_bf16, int64_t N, uint8_t* W_packed,
+                                 float* gamma, void* ws, hipStream_t s) {
+    const int64_t E = x_bf16 ? 8 : 4;
+    const int64_t nblk = (K + kWave * E - 1) / (kWave * E);
+    const bool rows = K == nblk * kWave * E && (nblk == 1 || nblk == 2 || nblk == 4 || nblk == 8 || nblk == 16);
+    hipError_t e;
+    if (!rows) {  // act_quant's general kernel: the two calls' launches in order
+        e = launch_act_quant(X, x_bf16, M, K, eps, Xq, scale_x, s);
+        if (e != hipSuccess) return e;
+        return launch_weight_quant(W, w_bf16, N, K, W_packed, gamma, ws, s);
+    }
+    float* row_sums = static_cast<float*>(ws);
+    e = x_bf16 ? quant_operands_w(static_cast<const uint16_t*>(X), M, K, eps, Xq, scale_x, W, w_bf16, N, row_sums,
+                                  (int)nblk, s)
+               : quant_operands_w(static_cast<const float*>(X), M, K, eps, Xq, scale_x, W, w_bf16, N, row_sums,
+                                  (int)nblk, s);
+    if (e != hipSuccess) return e;
+    return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s);
 }
 
 // ============================================================ pack helper

@@ -114,6 +114,24 @@ int bitnet_act_quant(const void *X, int x_dtype, int64_t M, int64_t K, float eps
                      int8_t *Xq, float *scale_x, void *stream);
 
 /*
+ * Both quantizers of a BitLinear layer in one call: bitnet_act_quant of X and
+ * bitnet_weight_quant of W, with one kernel launch fewer ([NOTES 5.1]: fuse
+ * the quantization steps).  The first launch reads X and W side by side
+ * (activation rows and weight row sums on separate workgroups of one grid);
+ * the outputs are bit-identical to the two calls.
+ *   X [M][K], W [N][K] fp32 or bf16 (x_dtype, w_dtype; same K)
+ *   Xq, scale_x as bitnet_act_quant;  W_packed, gamma as bitnet_weight_quant
+ *   workspace >= bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT, 0, N, K)
+ * K % 4 == 0.  Errors: the union of the two calls' (BITNET_E_ARG,
+ * BITNET_E_SHAPE, BITNET_E_DTYPE, BITNET_E_ALIGN, BITNET_E_WORKSPACE,
+ * BITNET_E_HIP).
+ */
+int bitnet_quant_operands(const void *X, int x_dtype, int64_t M, int64_t K, float eps, int8_t *Xq,
+                          float *scale_x, const void *W, int w_dtype, int64_t N,
+                          uint8_t *W_packed, float *gamma, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
  * BitLinear forward from the quantized operands.
  * [NOTES 3.1] (linear layer, then multiply back by the scale), [NOTES 5.2]
  * (wide accumulator), [WALL 3.1] (+1 adds, -1 subtracts, 0 skips):

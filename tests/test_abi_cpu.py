@@ -195,6 +195,25 @@ def test_decode_call_rejects_bad_arguments():
     assert f(P, 1, P, P, 1, 16, 64, eps, P, NULL, ctypes.c_void_p((1 << 20) + 2), NULL) == -4
 
 
+def test_quant_operands_rejects_bad_arguments():
+    lib = bt.load_library()
+    f = lib.bitnet_quant_operands
+    eps = ctypes.c_float(1e-5)
+    ws = bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, 0, 8, 16)
+    # (X, xdt, M, K, eps, Xq, scale_x, W, wdt, N, W_packed, gamma, ws, ws_bytes, stream)
+    assert f(NULL, 1, 4, 16, eps, P, P, P, 0, 8, P, P, P, ws, NULL) == -1
+    assert f(P, 1, 4, 16, eps, P, P, NULL, 0, 8, P, P, P, ws, NULL) == -1
+    assert f(P, 1, 4, 16, eps, P, P, P, 0, 8, P, NULL, P, ws, NULL) == -1
+    assert f(P, 3, 4, 16, eps, P, P, P, 0, 8, P, P, P, ws, NULL) == -3
+    assert f(P, 1, 4, 16, eps, P, P, P, 7, 8, P, P, P, ws, NULL) == -3
+    assert f(P, 1, 4, 18, eps, P, P, P, 0, 8, P, P, P, ws, NULL) == -2
+    assert f(P, 1, 0, 16, eps, P, P, P, 0, 8, P, P, P, ws, NULL) == -2
+    assert f(P, 1, 4, 16, ctypes.c_float(-1.0), P, P, P, 0, 8, P, P, P, ws, NULL) == -1
+    assert f(P, 1, 4, 16, eps, P, P, ctypes.c_void_p((1 << 20) + 4), 0, 8, P, P, P, ws, NULL) == -4
+    assert f(P, 1, 4, 16, eps, P, P, P, 0, 8, P, P, P, ws - 16, NULL) == -5
+    assert f(P, 1, 4, 16, eps, P, P, P, 0, 8, P, P, NULL, ws, NULL) == -5
+
+
 def test_pack_rejects_bad_arguments():
     lib = bt.load_library()
     assert lib.bitnet_pack_ternary(NULL, 4, 4, P, NULL) == -1

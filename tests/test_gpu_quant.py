@@ -124,3 +124,35 @@ def test_quantizers_are_deterministic():
     p2, g2 = bt.bitnet_weight_quant(wd)
     assert torch.equal(q1, q2) and torch.equal(s1, s2)
     assert torch.equal(p1, p2) and torch.equal(g1, g2)
+
+
+# both quantizers in one call (bitnet_quant_operands): the row-walking
+# activation kernel shares its launch with the weight row sums when K is
+# 1, 2, 4, 8 or 16 whole blocks (512 bf16 / 256 fp32 elements), else the two
+# calls' kernels run in order; either way the outputs must equal the two
+# calls' bit for bit
+@pytest.mark.parametrize("M,N,K,xdt,wdt", [
+    (300, 257, 512, torch.bfloat16, torch.float32),    # one bf16 block
+    (1000, 64, 256, torch.float32, torch.bfloat16),    # one fp32 block
+    (64, 300, 4096, torch.bfloat16, torch.bfloat16),   # 8 blocks
+    (9, 1376, 8192, torch.bfloat16, torch.float32),    # 16 blocks
+    (17, 33, 100, torch.bfloat16, torch.float32),      # ragged K: the general activation kernel
+    (5000, 8, 1024, torch.float32, torch.float32),     # more rows than the row-walking grid
+])
+def test_quant_operands_matches_the_two_calls(M, N, K, xdt, wdt):
+    print(f"quant_operands M={M} N={N} K={K} {xdt} {wdt}", flush=True)
+    x = _act_case(M, K, xdt, seed=M + K)
+    w = _weight_case(N, K, wdt, seed=N + K)
+    q, s, wp, g = bt.bitnet_quant_operands(to_dev(x), to_dev(w))
+    q2, s2 = bt.bitnet_act_quant(to_dev(x))
+    wp2, g2 = bt.bitnet_weight_quant(to_dev(w))
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(wp, wp2)
+    assert f32_bits_equal(s.cpu().numpy(), s2.cpu().numpy())
+    assert f32_bits_equal(g.cpu().numpy(), g2.cpu().numpy())
+    q_ref, s_ref = oracle.act_quant(host(x))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert f32_bits_equal(s.cpu().numpy(), s_ref)
+    codes_ref, g_ref = oracle.weight_quant(host(w))
+    assert np.array_equal(wp.cpu().numpy(), oracle.pack(codes_ref))
+    assert f32_bits_equal(g.cpu().numpy(), np.array([g_ref], np.float32))
