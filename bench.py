@@ -402,7 +402,7 @@ def bench_layer(args, name):
     # they run on.  A bounded spin first lets the host enqueue the whole loop,
     # so no host gap sits between two events.
     if args.step_only:
-        parts = {n: f for n, f in parts.items() if n in ("bwd_grad_x", "bwd_grad_W")}
+        parts = {n: f for n, f in parts.items() if n in ("bwd_grad_x", "bwd_grad_W", "quant_operands")}
     allc = dict(calls, **parts)
     timed = list(allc)
     g_rep = {n: capture(lambda n=n: [allc[n]() for _ in range(REPS)]) for n in timed}
