@@ -484,8 +484,8 @@ def bench_decode(args):
     x = d["x"].to(dev)
     q2, s2 = torch.empty_like(q), torch.empty_like(s)
 
-    def per_launch_ms(fn):
-        gr = capture(lambda: [fn(wp) for wp in wps])
+    def per_launch_ms(fn, weights=wps):
+        gr = capture(lambda: [fn(wp) for wp in weights])
         for _ in range(max(1, args.warmup // copies)):
             gr.replay()
         torch.cuda.synchronize()
@@ -511,6 +511,10 @@ def bench_decode(args):
         bt.bitnet_act_quant(x, 1e-5, Xq=q2, scale_x=s2), bt.bitnet_linear_fwd(q2, s2, wp, gm, Y=Y))), step_bytes)
     kernels["linear_fwd_decode"] = entry(
         per_launch_ms(lambda wp: bt.bitnet_linear_fwd_decode(x, wp, gm, 1e-5, Y=Y)), step_bytes)
+    if K == 4096:  # the same call on the weights in the decode layout (repacked once, untimed)
+        wds = [bt.bitnet_pack_decode(wp) for wp in wps]
+        kernels["linear_fwd_decode@decode_layout"] = entry(
+            per_launch_ms(lambda wd: bt.bitnet_linear_fwd_decode(x, wd, gm, 1e-5, Y=Y, N=N), wds), step_bytes)
     out = {
         "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,

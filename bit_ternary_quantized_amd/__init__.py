@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libbitnet_amd.so")
 
 BITNET_OK = 0
 BITNET_F32, BITNET_BF16 = 0, 1
+BITNET_LAYOUT_ROWS, BITNET_LAYOUT_DECODE = 0, 1
 (BITNET_OP_WEIGHT_QUANT, BITNET_OP_LINEAR_BWD_STE, BITNET_OP_LINEAR_FWD, BITNET_OP_CODE_COUNTS,
  BITNET_OP_WEIGHT_QUANT_ROWS) = 0, 1, 2, 3, 4
 GEMV_MAX_M = 16  # linear_fwd runs the packed GEMV up to this many tokens
@@ -27,6 +28,7 @@ EXPORTS = (
     "bitnet_pack_ternary", "bitnet_rmsnorm_bwd", "bitnet_linear_bwd_ste_gated", "bitnet_weight_clamp",
     "bitnet_code_counts", "bitnet_weight_quant_rows", "bitnet_linear_fwd_channel",
     "bitnet_linear_bwd_ste_channel", "bitnet_linear_fwd_decode", "bitnet_quant_operands",
+    "bitnet_decode_layout_bytes", "bitnet_pack_decode",
     "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
 )
 
@@ -64,7 +66,9 @@ def load_library(path: str = LIB_PATH):
         "bitnet_weight_quant_rows": (c_int, [p, c_int, i64, i64, p, p, p, sz, p]),
         "bitnet_linear_fwd_channel": (c_int, [p, p, p, p, i64, i64, i64, p, p, p]),
         "bitnet_linear_bwd_ste_channel": (c_int, [p, c_int, p, p, p, p, i64, i64, i64, p, c_int, p, p, sz, p]),
-        "bitnet_linear_fwd_decode": (c_int, [p, c_int, p, p, i64, i64, i64, ctypes.c_float, p, p, p, p]),
+        "bitnet_linear_fwd_decode": (c_int, [p, c_int, p, c_int, p, i64, i64, i64, ctypes.c_float, p, p, p, p]),
+        "bitnet_decode_layout_bytes": (i64, [i64, i64]),
+        "bitnet_pack_decode": (c_int, [p, i64, i64, p, p]),
         "bitnet_quant_operands": (c_int, [p, c_int, i64, i64, ctypes.c_float, p, p, p, c_int, i64, p, p, p, sz, p]),
         "bitnet_workspace_bytes": (sz, [c_int, i64, i64, i64]),
         "bitnet_status_str": (ctypes.c_char_p, [c_int]),
@@ -320,16 +324,26 @@ def bitnet_linear_fwd_channel(Xq, scale_x, W_packed, s, Y=None, acc=None, want_a
 
 
 def bitnet_linear_fwd_decode(X, W_packed, gamma, eps: float = 1e-5, Y=None, Xq=None, scale_x=None,
-                             want_q=False, stream=None):
+                             want_q=False, stream=None, N=None):
     """Decode forward in one launch: act_quant(X) then the packed GEMV, M <= 16,
-    K <= 4096 -> (Y f32 [M,N], Xq int8 or None, scale_x f32 or None)."""
+    K <= 4096 -> (Y f32 [M,N], Xq int8 or None, scale_x f32 or None).
+
+    W_packed is [N, K/4] packed rows, or (with N given) the 1-D output of
+    bitnet_pack_decode for those rows."""
     lib = load_library()
     for t, n in ((X, "X"), (W_packed, "W_packed"), (gamma, "gamma")):
         _need(t, n)
     M, K = X.shape
-    N = W_packed.shape[0]
-    if W_packed.shape[1] * 4 != K:
-        raise ValueError("W_packed must be [N, K/4]")
+    if N is None:
+        layout = BITNET_LAYOUT_ROWS
+        N = W_packed.shape[0]
+        if W_packed.dim() != 2 or W_packed.shape[1] * 4 != K:
+            raise ValueError("W_packed must be [N, K/4]")
+    else:
+        layout = BITNET_LAYOUT_DECODE
+        need = bitnet_decode_layout_bytes(N, K)
+        if W_packed.dim() != 1 or W_packed.dtype != torch.uint8 or W_packed.numel() != need:
+            raise ValueError(f"a decode-layout W_packed is 1-D uint8 of {need} bytes")
     if Y is None:
         Y = torch.empty(M, N, dtype=torch.float32, device=X.device)
     if want_q and Xq is None:
@@ -337,9 +351,32 @@ def bitnet_linear_fwd_decode(X, W_packed, gamma, eps: float = 1e-5, Y=None, Xq=N
     if want_q and scale_x is None:
         scale_x = torch.empty(M, dtype=torch.float32, device=X.device)
     _check("bitnet_linear_fwd_decode", lib.bitnet_linear_fwd_decode(
-        _ptr(X), _dtype_code(X), _ptr(W_packed), _ptr(gamma), M, N, K, ctypes.c_float(eps), _ptr(Y),
-        _ptr(Xq), _ptr(scale_x), _stream(stream)))
+        _ptr(X), _dtype_code(X), _ptr(W_packed), layout, _ptr(gamma), M, N, K, ctypes.c_float(eps),
+        _ptr(Y), _ptr(Xq), _ptr(scale_x), _stream(stream)))
     return Y, Xq, scale_x
+
+
+def bitnet_decode_layout_bytes(N: int, K: int) -> int:
+    """Bytes of the decode layout of [N, K/4] packed rows (ValueError if unsupported)."""
+    n = load_library().bitnet_decode_layout_bytes(N, K)
+    if n < 0:
+        raise ValueError(f"no decode layout for N={N}, K={K} (K must be 4096)")
+    return n
+
+
+def bitnet_pack_decode(W_packed, W_decode=None, stream=None):
+    """Packed rows [N, K/4] -> the same bytes in the decode layout (1-D uint8)."""
+    lib = load_library()
+    _need(W_packed, "W_packed")
+    N, KB = W_packed.shape
+    K = 4 * KB
+    need = bitnet_decode_layout_bytes(N, K)
+    if W_decode is None:
+        W_decode = torch.empty(need, dtype=torch.uint8, device=W_packed.device)
+    elif W_decode.numel() != need:
+        raise ValueError(f"W_decode must hold {need} bytes")
+    _check("bitnet_pack_decode", lib.bitnet_pack_decode(_ptr(W_packed), N, K, _ptr(W_decode), _stream(stream)))
+    return W_decode
 
 
 def bitnet_linear_bwd_ste_channel(grad_y, Xq, scale_x, W_packed, s, want_grad_x=True, want_grad_W=True,

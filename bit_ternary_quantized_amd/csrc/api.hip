@@ -125,20 +125,35 @@ int bitnet_linear_fwd_channel(const int8_t* Xq, const float* scale_x, const uint
     return linear_fwd(Xq, scale_x, W_packed, s, M, N, K, Y, acc, stream, true);
 }
 
-int bitnet_linear_fwd_decode(const void* X, int x_dtype, const uint8_t* W_packed, const float* gamma,
-                             int64_t M, int64_t N, int64_t K, float eps, float* Y, int8_t* Xq,
-                             float* scale_x, void* stream) {
+int bitnet_linear_fwd_decode(const void* X, int x_dtype, const uint8_t* W_packed, int w_layout,
+                             const float* gamma, int64_t M, int64_t N, int64_t K, float eps, float* Y,
+                             int8_t* Xq, float* scale_x, void* stream) {
     if (!X || !W_packed || !gamma || !Y) return BITNET_E_ARG;
     if (!float_dtype(x_dtype)) return BITNET_E_DTYPE;
-    if (!(eps >= 0.0f)) return BITNET_E_ARG;
+    if (!(eps >= 0.0f) || (w_layout != BITNET_LAYOUT_ROWS && w_layout != BITNET_LAYOUT_DECODE))
+        return BITNET_E_ARG;
     if (M < 1 || N < 1 || K < 1 || K % 16 != 0 || N >= kMaxFwdN ||
-        !bitnet::gemv_decode_fits(x_dtype == BITNET_BF16, M, K))
+        !bitnet::gemv_decode_fits(x_dtype == BITNET_BF16, M, K) ||
+        (w_layout == BITNET_LAYOUT_DECODE && !bitnet::decode_layout_supported(K)))
         return BITNET_E_SHAPE;
     if (!aligned16(X) || !aligned16(W_packed) || !aligned16(Y) || !aligned4(gamma) ||
         (Xq && !aligned16(Xq)) || (scale_x && !aligned4(scale_x)))
         return BITNET_E_ALIGN;
     return hip_status(bitnet::launch_gemv_decode(X, x_dtype == BITNET_BF16, W_packed, gamma, M, N, K, eps,
-                                                 Y, Xq, scale_x, as_stream(stream)));
+                                                 Y, Xq, scale_x, as_stream(stream),
+                                                 w_layout == BITNET_LAYOUT_DECODE));
+}
+
+int64_t bitnet_decode_layout_bytes(int64_t N, int64_t K) {
+    if (N < 1 || N >= kMaxFwdN || !bitnet::decode_layout_supported(K)) return -1;
+    return bitnet::decode_layout_bytes(N, K);
+}
+
+int bitnet_pack_decode(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W_decode, void* stream) {
+    if (!W_packed || !W_decode) return BITNET_E_ARG;
+    if (N < 1 || N >= kMaxFwdN || !bitnet::decode_layout_supported(K)) return BITNET_E_SHAPE;
+    if (!aligned16(W_packed) || !aligned16(W_decode)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_pack_decode(W_packed, N, K, W_decode, as_stream(stream)));
 }
 
 int bitnet_weight_quant_rows(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* W_packed,

@@ -247,7 +247,11 @@ bool gemv_supported(int64_t M, int64_t K);  // M <= 16 and the activations fit L
 // launch; xq_out / sx_out (optional) receive q and scale_x.
 hipError_t launch_gemv_decode(const void* X, bool x_bf16, const uint8_t* Wp, const float* gamma,
                               int64_t M, int64_t N, int64_t K, float eps, float* Y, int8_t* xq_out,
-                              float* sx_out, hipStream_t s);
+                              float* sx_out, hipStream_t s, bool decode_layout);
+// the decode layout of a packed W (gemv.hip): supported K, bytes, the repack
+bool decode_layout_supported(int64_t K);
+int64_t decode_layout_bytes(int64_t N, int64_t K);
+hipError_t launch_pack_decode(const uint8_t* Wp, int64_t N, int64_t K, uint8_t* Wd, hipStream_t s);
 // M <= 16, K <= 4096 and M * ceil(K / (64 * elements per 16 bytes)) <= 128
 // (every bf16 shape; fp32: M * ceil(K / 256) <= 128, e.g. 8 rows of 4096)
 bool gemv_decode_fits(bool x_bf16, int64_t M, int64_t K);

@@ -64,10 +64,11 @@ constexpr int kStageMaxK = 4096;  // LDS activation tile bound
 constexpr int kStageStride = kStageMaxK + 16;
 
 // CH: gamma_p holds one scale per output channel (see the GEMM).
+// DL: Wp is in the decode layout (pack_decode_kernel below), else row-major.
 // TX: int8_t, Xin = Xq and scale_x given; uint16_t (bf16) or float, Xin = X
 // unquantized, quantized here with eps (K <= kStageMaxK), scale_x unused,
 // and workgroup 0 writes q and the scales to xq_out / sx_out when non-null.
-template <int S, bool FULL, bool STAGE, bool CH, typename TX = int8_t, int IT = 1>
+template <int S, bool FULL, bool STAGE, bool CH, typename TX = int8_t, int IT = 1, bool DL = false>
 __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
     const void* __restrict__ Xin, const float* __restrict__ scale_x,
     const uint8_t* __restrict__ Wp, const float* __restrict__ gamma_p, int M, int N, int K,
@@ -146,7 +147,21 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
             const bool nv = grp < ngroups && n < N;
             const int nc = nv ? n : 0;  // clamped address, value dropped below
             const uint8_t* src = Wp + (int64_t)nc * KB + kb / 4;
-            if constexpr (FULL && S % 4 == 0) {
+            if constexpr (DL) {
+                // decode layout: this wave's pieces of the row group are S/4
+                // contiguous kilobytes, one per load instruction, in lane order
+                static_assert(FULL && S % 4 == 0, "the decode layout holds whole 16-byte pieces");
+                const int gc = grp < ngroups ? grp : 0;
+                const uint8_t* blk = Wp + ((int64_t)gc * kWaves + wave) * (S / 4) * 1024 + lane * 16;
+#pragma unroll
+                for (int s = 0; s < S; s += 4) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(blk + (s / 4) * 1024);
+                    wq[r][s] = nv ? v.x : 0u;
+                    wq[r][s + 1] = nv ? v.y : 0u;
+                    wq[r][s + 2] = nv ? v.z : 0u;
+                    wq[r][s + 3] = nv ? v.w : 0u;
+                }
+            } else if constexpr (FULL && S % 4 == 0) {
 #pragma unroll
                 for (int s = 0; s < S; s += 4) {
                     const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * s);
@@ -411,11 +426,18 @@ namespace {
 
 template <typename TX, int IT>
 hipError_t decode_launch(const TX* X, const uint8_t* Wp, const float* gamma, int64_t M, int64_t N,
-                         int64_t K, float eps, float* Y, int8_t* xq_out, float* sx_out, hipStream_t s) {
+                         int64_t K, float eps, float* Y, int8_t* xq_out, float* sx_out, hipStream_t s,
+                         bool decode_layout) {
     const int64_t ngroups = (N + 15) / 16;
     const unsigned grid = (unsigned)std::min<int64_t>(ngroups, 256);
     const int64_t steps = (K + 16 * 64 - 1) / (16 * 64);
     const bool full = K % (16 * 64) == 0;
+    if (decode_layout) {
+        if (!decode_layout_supported(K)) return hipErrorInvalidValue;
+        gemv_t2_kernel<4, true, false, false, TX, IT, true><<<grid, kThreads, 0, s>>>(
+            X, nullptr, Wp, gamma, (int)M, (int)N, (int)K, Y, nullptr, eps, xq_out, sx_out);
+        return hipGetLastError();
+    }
 #define BITNET_DECODE_CASE(S_)                                                                  \
     if (steps <= S_) {                                                                          \
         if (full && steps == S_)                                                                \
@@ -435,14 +457,15 @@ hipError_t decode_launch(const TX* X, const uint8_t* Wp, const float* gamma, int
 
 template <typename TX>
 hipError_t decode_dispatch(const TX* X, const uint8_t* Wp, const float* gamma, int64_t M, int64_t N,
-                           int64_t K, float eps, float* Y, int8_t* xq_out, float* sx_out, hipStream_t s) {
+                           int64_t K, float eps, float* Y, int8_t* xq_out, float* sx_out, hipStream_t s,
+                           bool dl) {
     // work items (token row, block) per wave
     constexpr int64_t blk = kWave * Vec16<TX>::E;
     const int64_t per_wave = (M * ((K + blk - 1) / blk) + kWaves - 1) / kWaves;
-    if (per_wave <= 1) return decode_launch<TX, 1>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
-    if (per_wave <= 2) return decode_launch<TX, 2>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
-    if (per_wave <= 4) return decode_launch<TX, 4>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
-    if (per_wave <= 8) return decode_launch<TX, 8>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
+    if (per_wave <= 1) return decode_launch<TX, 1>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s, dl);
+    if (per_wave <= 2) return decode_launch<TX, 2>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s, dl);
+    if (per_wave <= 4) return decode_launch<TX, 4>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s, dl);
+    if (per_wave <= 8) return decode_launch<TX, 8>(X, Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s, dl);
     return hipErrorInvalidValue;
 }
 
@@ -456,11 +479,50 @@ bool gemv_decode_fits(bool x_bf16, int64_t M, int64_t K) {
 
 hipError_t launch_gemv_decode(const void* X, bool x_bf16, const uint8_t* Wp, const float* gamma,
                               int64_t M, int64_t N, int64_t K, float eps, float* Y, int8_t* xq_out,
-                              float* sx_out, hipStream_t s) {
+                              float* sx_out, hipStream_t s, bool decode_layout) {
     if (!gemv_decode_fits(x_bf16, M, K) || K % 16 != 0) return hipErrorInvalidValue;
     if (x_bf16)
-        return decode_dispatch(static_cast<const uint16_t*>(X), Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
-    return decode_dispatch(static_cast<const float*>(X), Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s);
+        return decode_dispatch(static_cast<const uint16_t*>(X), Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s,
+                               decode_layout);
+    return decode_dispatch(static_cast<const float*>(X), Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s,
+                           decode_layout);
+}
+
+// ------------------------------------------------------- the decode layout
+// K = 1024 S: wave v of the GEMV loads row group grp (rows 16 grp .. +15) with
+// S/4 instructions of 16 bytes per lane; lane l = 16 g + c takes row
+// 16 grp + c, packed bytes 16 S v + 4 S g + 16 i in instruction i.  The
+// decode layout stores exactly those pieces in that order: the 1 KB block of
+// (grp, v, i) at ((grp * 16 + v) * S/4 + i) * 1024, lane l's piece at + 16 l,
+// the rows past N as zeros.  A row-major W gives every instruction sixteen
+// 64-byte pieces of sixteen rows; here it reads one contiguous kilobyte.
+// Defined for the shape the fused decode call takes: K = 4096 (S = 4).
+bool decode_layout_supported(int64_t K) { return K == 4096; }
+int64_t decode_layout_bytes(int64_t N, int64_t K) { return (N + 15) / 16 * 16 * (K / 4); }
+
+__global__ __launch_bounds__(256) void pack_decode_kernel(const uint8_t* __restrict__ Wp, int64_t N, int64_t K,
+                                                          uint8_t* __restrict__ Wd) {
+    const int64_t S = K / 1024, S4 = S / 4, KB = K / 4;
+    const int64_t pieces = (N + 15) / 16 * 16 * KB / 16;  // 16-byte pieces of Wd
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < pieces;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const int l = (int)(c & 63);
+        const int64_t rest = c >> 6;  // (grp * 16 + v) * S4 + i
+        const int64_t i = rest % S4, v = (rest / S4) % kWaves, grp = rest / S4 / kWaves;
+        const int64_t row = grp * 16 + (l & 15);
+        const int64_t byte = 16 * S * v + 4 * S * (l >> 4) + 16 * i;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (row < N) val = *reinterpret_cast<const uint4*>(Wp + row * KB + byte);
+        reinterpret_cast<uint4*>(Wd)[c] = val;
+    }
+}
+
+hipError_t launch_pack_decode(const uint8_t* Wp, int64_t N, int64_t K, uint8_t* Wd, hipStream_t s) {
+    if (!decode_layout_supported(K) || N < 1) return hipErrorInvalidValue;
+    const int64_t pieces = decode_layout_bytes(N, K) / 16;
+    const unsigned grid = (unsigned)std::min<int64_t>((pieces + 255) / 256, 8192);
+    pack_decode_kernel<<<grid, 256, 0, s>>>(Wp, N, K, Wd);
+    return hipGetLastError();
 }
 
 }  // namespace bitnet

@@ -66,6 +66,9 @@ typedef enum {
 
 typedef enum { BITNET_F32 = 0, BITNET_BF16 = 1 } bitnet_dtype;
 
+/* layout of packed weights handed to bitnet_linear_fwd_decode */
+typedef enum { BITNET_LAYOUT_ROWS = 0, BITNET_LAYOUT_DECODE = 1 } bitnet_layout;
+
 typedef enum {
     BITNET_OP_WEIGHT_QUANT = 0,
     BITNET_OP_LINEAR_BWD_STE = 1,
@@ -251,7 +254,11 @@ int bitnet_linear_fwd_channel(const int8_t *Xq, const float *scale_x, const uint
  * with bitnet_act_quant's arithmetic, operation for operation, so
  *   Y (and Xq, scale_x when requested) are bit-identical to
  *   bitnet_act_quant(X, ..., eps) followed by bitnet_linear_fwd.
- *   X        [M][K] fp32 or bf16 (x_dtype);  W_packed [N][K/4];  gamma 1 fp32
+ *   X        [M][K] fp32 or bf16 (x_dtype);  gamma 1 fp32
+ *   W_packed [N][K/4] packed rows (w_layout BITNET_LAYOUT_ROWS), or the
+ *            same weights in the decode layout of bitnet_pack_decode
+ *            (BITNET_LAYOUT_DECODE: K == 4096 only; the results are the same
+ *            bits, the weight stream reads whole kilobytes)
  *   Y        [M][N] fp32, written
  *   Xq       [M][K] int8, written when non-NULL (16-byte aligned)
  *   scale_x  [M] fp32, written when non-NULL
@@ -262,12 +269,36 @@ int bitnet_linear_fwd_channel(const int8_t *Xq, const float *scale_x, const uint
  * fp32 X also M * ceil(K / 256) <= 128 (the raw rows stay in registers: up
  * to 8 rows of 4096); N < 2^23; eps >= 0.  Other shapes: bitnet_act_quant
  * followed by bitnet_linear_fwd.
- * Errors: BITNET_E_ARG, BITNET_E_SHAPE, BITNET_E_DTYPE, BITNET_E_ALIGN,
- * BITNET_E_HIP.
+ * Errors: BITNET_E_ARG (also an unknown w_layout), BITNET_E_SHAPE,
+ * BITNET_E_DTYPE, BITNET_E_ALIGN, BITNET_E_HIP.
  */
-int bitnet_linear_fwd_decode(const void *X, int x_dtype, const uint8_t *W_packed,
+int bitnet_linear_fwd_decode(const void *X, int x_dtype, const uint8_t *W_packed, int w_layout,
                              const float *gamma, int64_t M, int64_t N, int64_t K, float eps,
                              float *Y, int8_t *Xq, float *scale_x, void *stream);
+
+/*
+ * The decode layout: the packed weights of [WALL 4.1] rearranged, once per
+ * weight update, into the order in which the decode GEMV's wavefronts load
+ * them.  A decode step reads all of W for a few tokens, so it is bound by
+ * memory bandwidth ([WALL 1], the memory wall), and [WALL 4.1] and 5.1
+ * (item 2) lay the packed weights out for the loads that read them.
+ * The GEMV works on row groups of 16 rows, split over 16 waves of 64 lanes;
+ * for K = 4096 wave v reads, for row 16 grp + c, packed bytes
+ * 64 v + 16 g .. + 15 in lane 16 g + c.  Those 16-byte pieces are stored as
+ *   W_decode[((grp * 16 + v) * 64 + 16 g + c) * 16 + b]
+ *       = W_packed[16 grp + c][64 v + 16 g + b]    (b = 0..15)
+ * with zeros for rows 16 grp + c >= N, so that every load instruction of the
+ * GEMV reads one contiguous kilobyte.  Byte values are copied, nothing else.
+ *   W_packed [N][K/4] bytes, device, 16-byte aligned, read
+ *   W_decode bitnet_decode_layout_bytes(N, K) = ceil(N/16) * 16 * K/4 bytes,
+ *            device, 16-byte aligned, written; must not overlap W_packed
+ * K == 4096 (the shape bitnet_linear_fwd_decode takes in this layout),
+ * 1 <= N < 2^23.  bitnet_decode_layout_bytes returns -1 for other shapes.
+ * Errors: BITNET_E_ARG, BITNET_E_SHAPE, BITNET_E_ALIGN, BITNET_E_HIP.
+ */
+int64_t bitnet_decode_layout_bytes(int64_t N, int64_t K);
+int bitnet_pack_decode(const uint8_t *W_packed, int64_t N, int64_t K, uint8_t *W_decode,
+                       void *stream);
 int bitnet_linear_bwd_ste_channel(const void *grad_y, int gy_dtype, const int8_t *Xq,
                                   const float *scale_x, const uint8_t *W_packed, const float *s,
                                   int64_t M, int64_t N, int64_t K, void *grad_x, int gx_dtype,

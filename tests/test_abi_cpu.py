@@ -175,8 +175,12 @@ def test_channel_calls_reject_bad_arguments():
 
 def test_decode_call_rejects_bad_arguments():
     lib = bt.load_library()
-    f = lib.bitnet_linear_fwd_decode
     eps = ctypes.c_float(1e-5)
+    R, D = bt.BITNET_LAYOUT_ROWS, bt.BITNET_LAYOUT_DECODE
+
+    def f(X, dt, W, gamma, M, N, K, e, Y, Xq, sx, stream, layout=R):
+        return lib.bitnet_linear_fwd_decode(X, dt, W, layout, gamma, M, N, K, e, Y, Xq, sx, stream)
+
     # (X, dtype, W_packed, gamma, M, N, K, eps, Y, Xq, scale_x, stream)
     assert f(NULL, 1, P, P, 1, 16, 64, eps, P, NULL, NULL, NULL) == -1
     assert f(P, 1, P, NULL, 1, 16, 64, eps, P, NULL, NULL, NULL) == -1
@@ -193,6 +197,28 @@ def test_decode_call_rejects_bad_arguments():
     assert f(odd, 1, P, P, 1, 16, 64, eps, P, NULL, NULL, NULL) == -4
     assert f(P, 1, P, P, 1, 16, 64, eps, P, odd, NULL, NULL) == -4
     assert f(P, 1, P, P, 1, 16, 64, eps, P, NULL, ctypes.c_void_p((1 << 20) + 2), NULL) == -4
+    # the decode layout: an unknown layout code, a K it is not defined for
+    assert f(P, 1, P, P, 1, 16, 4096, eps, P, NULL, NULL, NULL, layout=2) == -1
+    assert f(P, 1, P, P, 1, 16, 2048, eps, P, NULL, NULL, NULL, layout=D) == -2
+
+
+def test_decode_layout_size_and_pack_argument_checks():
+    lib = bt.load_library()
+    # ceil(N / 16) row groups of 16 rows, K / 4 bytes a row
+    assert lib.bitnet_decode_layout_bytes(16, 4096) == 16 * 1024
+    assert lib.bitnet_decode_layout_bytes(17, 4096) == 32 * 1024
+    assert lib.bitnet_decode_layout_bytes(11008, 4096) == 11008 * 1024
+    assert lib.bitnet_decode_layout_bytes(1, 4096) == 16 * 1024
+    assert lib.bitnet_decode_layout_bytes(16, 2048) == -1
+    assert lib.bitnet_decode_layout_bytes(0, 4096) == -1
+    assert lib.bitnet_decode_layout_bytes(1 << 23, 4096) == -1
+    with pytest.raises(ValueError):
+        bt.bitnet_decode_layout_bytes(16, 8192)
+    assert lib.bitnet_pack_decode(NULL, 16, 4096, P, NULL) == -1
+    assert lib.bitnet_pack_decode(P, 16, 4096, NULL, NULL) == -1
+    assert lib.bitnet_pack_decode(P, 16, 1024, P, NULL) == -2
+    assert lib.bitnet_pack_decode(P, 0, 4096, P, NULL) == -2
+    assert lib.bitnet_pack_decode(ctypes.c_void_p((1 << 20) + 8), 16, 4096, P, NULL) == -4
 
 
 def test_quant_operands_rejects_bad_arguments():

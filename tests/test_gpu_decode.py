@@ -108,3 +108,48 @@ def test_decode_without_q_outputs_and_repeat():
     torch.cuda.synchronize()
     assert q1 is None and s1 is None
     assert torch.equal(y1, y2)
+
+
+def _decode_layout_host(wp: np.ndarray) -> np.ndarray:
+    """The decode layout written out with numpy from its definition: the
+    16-byte piece of (row group, wave v, lane 16 g + c) is packed bytes
+    64 v + 16 g .. + 15 of row 16 * group + c (K = 4096), rows past N zero."""
+    N, KB = wp.shape
+    G = -(-N // 16)
+    pad = np.zeros((G * 16, KB), dtype=np.uint8)
+    pad[:N] = wp
+    # [group][c][v][g][b] -> [group][v][g][c][b]
+    return pad.reshape(G, 16, 16, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
+@pytest.mark.parametrize("N", [1, 16, 33, 4200, 11008])
+def test_pack_decode_matches_the_layout_definition(N):
+    print(f"pack_decode N={N}", flush=True)
+    codes = workloads.ternary_codes(N, 4096, 0.35, seed=N)
+    wp = oracle.pack(codes.numpy())
+    wd = bt.bitnet_pack_decode(to_dev(torch.from_numpy(wp)))
+    torch.cuda.synchronize()
+    assert np.array_equal(wd.cpu().numpy(), _decode_layout_host(wp))
+
+
+@pytest.mark.parametrize("M,N", [(1, 16), (1, 11008), (3, 33), (8, 4200), (16, 257), (16, 11008)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_layout_gives_the_same_bits(M, N, dtype):
+    # the decode layout changes where the weights are read from, nothing else
+    print(f"linear_fwd_decode decode layout M={M} N={N} {dtype}", flush=True)
+    if dtype == torch.float32 and M > 8:
+        pytest.skip("fp32 X: at most 8 rows of 4096 (the call's register budget)")
+    x, codes, gamma = _case(M, N, 4096, dtype, seed=M * 7 + N)
+    wp = to_dev(torch.from_numpy(oracle.pack(codes.numpy())))
+    wd = bt.bitnet_pack_decode(wp)
+    xd, gd = to_dev(x), to_dev(gamma)
+    y, q, s = bt.bitnet_linear_fwd_decode(xd, wp, gd, want_q=True)
+    y2, q2, s2 = bt.bitnet_linear_fwd_decode(xd, wd, gd, want_q=True, N=N)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2)
+    assert f32_bits_equal(s.cpu().numpy(), s2.cpu().numpy())
+    assert f32_bits_equal(y.cpu().numpy(), y2.cpu().numpy())
+    if M == 1 and N == 11008:
+        q_ref, s_ref = oracle.act_quant(host(x))
+        _, y_ref = oracle.linear_fwd(q_ref, s_ref, codes.numpy(), float(gamma[0]))
+        assert_y_close(y2.cpu().numpy(), y_ref)
