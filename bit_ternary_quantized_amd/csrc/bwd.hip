@@ -595,10 +595,36 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
         return (gate.lo <= w && w <= gate.hi) ? v : 0.0f;
     };
     if (i4 + 4 <= count && (count % 4) == 0) {
-        float4 s = reinterpret_cast<const float4*>(part + i4)[0];
-        for (int p = 1; p < splits; ++p) {
-            const float4 v = reinterpret_cast<const float4*>(part + (int64_t)p * count + i4)[0];
-            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        // the partials of up to kReduceBatch splits are requested together,
+        // then added in split order (a load per split, each waited for before
+        // the next is issued, costs a memory round trip per split); past the
+        // last split the index is clamped, the load repeated and its value
+        // not added (a select, not a branch, so the waits stay graded)
+        constexpr int kReduceBatch = 8;
+        auto load_batch = [&](int p0, float4 (&v)[kReduceBatch]) {
+#pragma unroll
+            for (int j = 0; j < kReduceBatch; ++j) {
+                const int p = min(p0 + j, splits - 1);
+                v[j] = reinterpret_cast<const float4*>(part + (int64_t)p * count + i4)[0];
+            }
+        };
+        auto add_batch = [&](int p0, int j0, const float4 (&v)[kReduceBatch], float4& s) {
+#pragma unroll
+            for (int j = j0; j < kReduceBatch; ++j) {
+                const bool use = p0 + j < splits;
+                s.x = use ? s.x + v[j].x : s.x;
+                s.y = use ? s.y + v[j].y : s.y;
+                s.z = use ? s.z + v[j].z : s.z;
+                s.w = use ? s.w + v[j].w : s.w;
+            }
+        };
+        float4 v[kReduceBatch];
+        load_batch(0, v);
+        float4 s = v[0];
+        add_batch(0, 1, v, s);
+        for (int p0 = kReduceBatch; p0 < splits; p0 += kReduceBatch) {
+            load_batch(p0, v);
+            add_batch(p0, 0, v, s);
         }
         s.x = gated(i4, s.x);
         s.y = gated(i4 + 1, s.y);
