@@ -11,8 +11,8 @@ exactly).  Outputs that decide integers are int8 / float32; references that
 decide nothing are float64.
 
 Pinned against the pages and mathematics in tests/test_oracle_pins.py; the
-reduction order (tree_sum) and the RMSNorm / divide-by-gamma readings are set
-by this build, not printed by any page (see the design notes).
+reduction order (tree_sum) and the RMSNorm / divide-by-gamma readings are
+readings of this library's contract; no page prints them.
 """
 import ctypes
 import os

@@ -26,8 +26,7 @@
  * dequantized output and the STE gradients, which decide nothing, are
  * computed in float64 as references for the tolerance checks.
  *
- * Readings where the pages are silent (each is listed with its reason in the
- * design notes):
+ * Readings where the pages are silent:
  *   - summation order: the canonical pairwise tree tree_sum() below;
  *   - RMSNorm: mean of squares over the row, eps inside the square root,
  *     multiply by the correctly rounded reciprocal of the root, unit gain;
@@ -190,7 +189,7 @@ int oracle_weight_quant(const void *w, int w_dtype, int64_t N, int64_t K,
 
 /* ------------------------------------------------ D1: 2-bit packing
  * [WALL 4.1]: 00 -> 0, 01 -> +1, 10 -> -1, 11 reserved.  Bit order in the
- * byte and row layout are this build's reading (see file header). */
+ * byte and row layout are the library's reading (see file header). */
 int oracle_pack(const int8_t *codes, int64_t N, int64_t K, uint8_t *packed) {
     if (!codes || !packed || N <= 0 || K <= 0 || K % 4 != 0) return -1;
     int64_t KB = K / 4;

@@ -24,7 +24,7 @@ F32_EPS = 2.0 ** -24  # unit roundoff of binary32
 
 
 # ------------------------------------------------------------------ tree sum
-# The summation order is this build's contract (the pages only say "mean");
+# The summation order is the library's contract (the pages only say "mean");
 # the pins below check the tree against exact arithmetic and hand-worked
 # order-sensitive cases.
 
