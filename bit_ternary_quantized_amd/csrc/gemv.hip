@@ -381,12 +381,130 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
     }
 }
 
+// ------------------------------------------------ one token: the row GEMV
+// For a single token the matrix cores would multiply fifteen zero rows, and
+// K4's split of K over sixteen waves needs a reduction through LDS.  Here one
+// wave takes kRowRows weight rows with its lanes across K: lane l holds the
+// 64-column chunks l, l + 64, ... of each row (16 packed bytes per load, so
+// every load instruction reads 1 KB of one row), unpacks them with unpack16,
+// multiplies on the VALU with v_dot4 against the token's matching byte-
+// transposed activation chunks, and the 64 lane sums are added with DPP (the
+// integer sum is exact in any order).  The epilogue is K4's, operation for
+// operation, so Y and acc are the same bits.
+constexpr int kRowRows = 4;   // weight rows per wave
+constexpr int kRowWaves = 4;  // waves per workgroup
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_read_i32(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+// sum over the 64 lanes (every lane active), returned to every lane
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    v += dpp_read_i32<kDppXor1>(v);
+    v += dpp_read_i32<kDppXor2>(v);
+    v += dpp_read_i32<kDppHalfMirror>(v);
+    v += dpp_read_i32<kDppMirror>(v);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+// CHK: 64-column chunks per lane (K <= 4096 CHK); K % 64 == 0.
+template <int CHK, bool CH>
+__global__ __launch_bounds__(kRowWaves * kWave) void gemv_row_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ scale_x, const uint8_t* __restrict__ Wp,
+    const float* __restrict__ gamma_p, int N, int K, float* __restrict__ Y, int32_t* __restrict__ acc_out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row0 = (blockIdx.x * kRowWaves + wave) * kRowRows;
+    if (row0 >= N) return;  // uniform in the wave
+    const int KB = K / 4, nch = K / 64;
+    // the activation chunks first: the weight loads after them are then the
+    // only ones outstanding when the products wait for each row
+    const __amdgpu_buffer_rsrc_t rx = make_buf(Xq);
+    uint4 xr[CHK][4];
+#pragma unroll
+    for (int c = 0; c < CHK; ++c) {
+        const int ch = lane + kWave * c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            xr[c][q] = buf_load16(rx, ch < nch ? (uint32_t)(64 * ch + 16 * q) : kBufOOB);
+    }
+    const __amdgpu_buffer_rsrc_t rw = make_buf(Wp + (int64_t)row0 * KB);
+    uint4 w[kRowRows][CHK];
+#pragma unroll
+    for (int r = 0; r < kRowRows; ++r)
+#pragma unroll
+        for (int c = 0; c < CHK; ++c) {
+            const int ch = lane + kWave * c;
+            w[r][c] = buf_load16(rw, row0 + r < N && ch < nch ? (uint32_t)(r * KB + 16 * ch) : kBufOOB);
+        }
+    uint32_t xa[CHK][16];
+#pragma unroll
+    for (int c = 0; c < CHK; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t a[4] = {xr[c][q].x, xr[c][q].y, xr[c][q].z, xr[c][q].w};
+            uint32_t o[4];
+            transpose4x4_bytes(a, o);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xa[c][4 * q + i] = o[i];
+        }
+    int acc[kRowRows];
+#pragma unroll
+    for (int r = 0; r < kRowRows; ++r) {
+        acc[r] = 0;
+#pragma unroll
+        for (int c = 0; c < CHK; ++c) {
+            const uint32_t wd[4] = {w[r][c].x, w[r][c].y, w[r][c].z, w[r][c].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t b[4];
+                unpack16(wd[q], b);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[r] = __builtin_amdgcn_sdot4((int)xa[c][4 * q + i], (int)b[i], acc[r], false);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kRowRows; ++r) acc[r] = wave_sum_i32(acc[r]);
+    if (lane < kRowRows) {
+        int sum = acc[0];
+#pragma unroll
+        for (int r = 1; r < kRowRows; ++r) sum = lane == r ? acc[r] : sum;
+        const int n = row0 + lane;
+        if (n < N) {
+            const float sx = scale_x[0];
+            if constexpr (CH) {
+                const float rs = 1.0f / sx;
+                Y[n] = ((float)sum * rs) * gamma_p[n];
+            } else {
+                const float rs = *gamma_p / sx;
+                Y[n] = (float)sum * rs;
+            }
+            if (acc_out) acc_out[n] = sum;
+        }
+    }
+}
+
 bool gemv_supported(int64_t M, int64_t K) { return M <= kGemvMaxM && K <= 16 * 64 * 16; }
 
 hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t* Wp,
                           const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
                           int32_t* acc, hipStream_t s, bool channel) {
     if (!gemv_supported(M, K)) return hipErrorInvalidValue;
+    if (M == 1 && K % 64 == 0 && K <= 2 * 64 * 64) {  // one token: the row GEMV
+        const unsigned rgrid = (unsigned)((N + kRowRows * kRowWaves - 1) / (kRowRows * kRowWaves));
+        constexpr unsigned kRowThreads = kRowWaves * kWave;
+        if (K <= 64 * 64) {
+            if (channel) gemv_row_kernel<1, true><<<rgrid, kRowThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)N, (int)K, Y, acc);
+            else gemv_row_kernel<1, false><<<rgrid, kRowThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)N, (int)K, Y, acc);
+        } else {
+            if (channel) gemv_row_kernel<2, true><<<rgrid, kRowThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)N, (int)K, Y, acc);
+            else gemv_row_kernel<2, false><<<rgrid, kRowThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)N, (int)K, Y, acc);
+        }
+        return hipGetLastError();
+    }
     const int64_t ngroups = (N + 15) / 16;
     const unsigned grid = (unsigned)std::min<int64_t>(ngroups, 256);
     const int64_t steps = (K + 16 * 64 - 1) / (16 * 64);  // MFMA steps per wave

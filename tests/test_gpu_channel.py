@@ -39,7 +39,7 @@ def _operands(M, N, K, seed):
 
 
 # GEMV (M <= 16), GEMM with ragged edges, many tiles per workgroup
-FWD_SHAPES = [(1, 300, 256), (16, 1000, 512), (300, 513, 1040), (4200, 4100, 64)]
+FWD_SHAPES = [(1, 300, 256), (1, 70, 8192), (16, 1000, 512), (300, 513, 1040), (4200, 4100, 64)]
 
 
 @pytest.mark.parametrize("M,N,K", FWD_SHAPES)

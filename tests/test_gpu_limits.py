@@ -60,7 +60,7 @@ def test_fwd_longest_contraction():
     assert_y_close(Y.cpu().numpy(), y_ref)
 
 
-@pytest.mark.parametrize("M", [16, 40])  # GEMV, GEMM
+@pytest.mark.parametrize("M", [1, 16, 40])  # one-token row GEMV, GEMV, GEMM
 def test_fwd_widest_output(M):
     N, K = (1 << 23) - 1, 16
     print(f"linear_fwd widest N={N} M={M} K={K}", flush=True)

@@ -30,6 +30,9 @@ FWD_SHAPES = [
     # GEMV path (M <= 16)
     (1, 16, 16), (1, 300, 256), (2, 33, 1040), (5, 257, 4096), (16, 1000, 512),
     (16, 64, 16384), (3, 17, 48),
+    # one token with K % 64 == 0 (the row GEMV): one chunk per lane, two, a
+    # ragged second chunk, a single chunk for the whole row
+    (1, 4099, 64), (1, 33, 8192), (1, 17, 4160), (1, 1000, 4096),
     # GEMM path: several tiles plus ragged edges in M, N and K
     (17, 16, 16), (100, 300, 256), (256, 256, 64), (300, 513, 1040),
     (513, 257, 4096), (1000, 40, 48),
@@ -62,7 +65,7 @@ def test_linear_fwd_extreme_values():
     scale_x = torch.full((M,), 3.0)
     gamma = torch.tensor([0.5])
     wp = oracle.pack(codes.numpy())
-    for m in (M, 4):  # GEMM and GEMV paths
+    for m in (M, 4, 1):  # GEMM, GEMV and one-token row GEMV paths
         Y, acc = bt.bitnet_linear_fwd(to_dev(q[:m]), to_dev(scale_x[:m]), to_dev(torch.from_numpy(wp)),
                                       to_dev(gamma), want_acc=True)
         acc_ref, y_ref = oracle.linear_fwd(q[:m].numpy(), scale_x[:m].numpy(), codes.numpy(), 0.5)
