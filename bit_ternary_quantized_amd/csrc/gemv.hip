@@ -487,6 +487,156 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_row_kernel(
     }
 }
 
+// One token from the unquantized activations (the fused decode forward at
+// M = 1): act_quant's arithmetic on the row, then K4r's products.  The
+// kRowDecWaves waves of a workgroup share the row: wave w reduces act_quant
+// blocks w, w + kRowDecWaves, ... (one 16-byte chunk per lane each), the
+// block partials meet in LDS, every wave forms the same 1/RMS and scale from
+// them in block order, quantizes its blocks into an LDS copy of q, and after
+// a barrier each lane reads its 64-column chunk.  The row is requested first
+// and waited for alone; the weight loads follow and stream in while the row
+// is quantized.
+constexpr int kRowDecWaves = 8;
+constexpr int kRowDecMaxK = 64 * 64;  // one chunk per lane
+
+template <typename TX>
+__global__ __launch_bounds__(kRowDecWaves * kWave) void gemv_row_decode_kernel(
+    const TX* __restrict__ X, const uint8_t* __restrict__ Wp, const float* __restrict__ gamma_p, int N, int K,
+    float eps, float* __restrict__ Y, int8_t* __restrict__ xq_out, float* __restrict__ sx_out) {
+    constexpr int E = Vec16<TX>::E;         // elements per 16-byte chunk
+    constexpr int BLK = kWave * E;          // an act_quant block
+    constexpr int NBX = kRowDecMaxK / BLK;  // blocks of the longest row (power of two)
+    constexpr int IT = (NBX + kRowDecWaves - 1) / kRowDecWaves;  // blocks per wave
+    __shared__ float blk_sq[NBX], blk_max[NBX];
+    __shared__ __align__(16) uint8_t qrow[kRowDecMaxK];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row0 = (blockIdx.x * kRowDecWaves + wave) * kRowRows;  // may pass N: such waves still quantize
+    const int KB = K / 4, nch = K / 64;
+    const int nblk = (K + BLK - 1) / BLK;
+    // 1) the row: block b = wave + kRowDecWaves j, this lane's E elements
+    //    (K % 64 == 0: all of them inside the row or all past it)
+    const __amdgpu_buffer_rsrc_t rx = make_buf(X);
+    uint4 xc[IT];
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+        const int b = wave + kRowDecWaves * j;
+        const int k0 = b * BLK + lane * E;
+        xc[j] = buf_load16(rx, b < nblk && k0 < K ? (uint32_t)(k0 * (int)sizeof(TX)) : kBufOOB);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_sched_barrier(0);
+    // 2) this wave's weight rows, all in flight
+    const __amdgpu_buffer_rsrc_t rw = make_buf(Wp + (int64_t)(row0 < N ? row0 : 0) * KB);
+    uint4 w[kRowRows];
+#pragma unroll
+    for (int r = 0; r < kRowRows; ++r)
+        w[r] = buf_load16(rw, row0 + r < N && lane < nch ? (uint32_t)(r * KB + 16 * lane) : kBufOOB);
+    // 3) block partials: in-lane tree and lane tree of the squares, max |x|
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+        const int b = wave + kRowDecWaves * j;
+        if (b < nblk) {
+            float v[E], sq[E], amax = 0.0f;
+            widen16<TX>(xc[j], v);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                sq[e] = v[e] * v[e];
+                amax = fmaxf(amax, fabsf(v[e]));
+            }
+            const float bsum = wave_tree_sum(lane_tree<E>(sq));
+            amax = wave_max(amax);
+            if (lane == 0) {
+                blk_sq[b] = bsum;
+                blk_max[b] = amax;
+            }
+        }
+    }
+    __syncthreads();
+    // 4) 1/RMS and the scale from the partials in block order (missing
+    //    blocks add +0, which leaves the tree's value unchanged)
+    float bs[NBX], amax = 0.0f;
+#pragma unroll
+    for (int b = 0; b < NBX; ++b) {
+        bs[b] = b < nblk ? blk_sq[b] : 0.0f;
+        amax = fmaxf(amax, b < nblk ? blk_max[b] : 0.0f);
+    }
+    const float ss = lane_tree<NBX>(bs);
+    const float ms = ss / (float)K;
+    const float d = sqrtf(ms + eps);
+    const float inv = 1.0f / d;
+    const float a = amax * inv;  // max|x * inv| == max|x| * inv
+    const float scale = 127.0f / fmaxf(a, 1e-5f);
+    if (sx_out && blockIdx.x == 0 && threadIdx.x == 0) sx_out[0] = scale;
+    // 5) this wave's blocks of q into the row copy
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+        const int b = wave + kRowDecWaves * j;
+        if (b < nblk) {
+            float v[E];
+            widen16<TX>(xc[j], v);
+            uint32_t pk[E / 4];
+#pragma unroll
+            for (int i = 0; i < E / 4; ++i) {
+                uint32_t u = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float r = rintf((v[4 * i + e] * inv) * scale);
+                    r = fminf(fmaxf(r, -128.0f), 127.0f);
+                    u |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * e);
+                }
+                pk[i] = u;
+            }
+            const int k0 = b * BLK + lane * E;
+            if constexpr (E == 8) *reinterpret_cast<uint2*>(qrow + k0) = make_uint2(pk[0], pk[1]);
+            else *reinterpret_cast<uint32_t*>(qrow + k0) = pk[0];
+            if (xq_out && blockIdx.x == 0 && k0 < K) {
+                if constexpr (E == 8) *reinterpret_cast<uint2*>(xq_out + k0) = make_uint2(pk[0], pk[1]);
+                else *reinterpret_cast<uint32_t*>(xq_out + k0) = pk[0];
+            }
+        }
+    }
+    __syncthreads();
+    // 6) the lane's 64 columns of q, byte-transposed for unpack16's order
+    uint32_t xa[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (lane < nch) v = *reinterpret_cast<const uint4*>(qrow + 64 * lane + 16 * q);
+        const uint32_t a4[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+        transpose4x4_bytes(a4, o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xa[4 * q + i] = o[i];
+    }
+    // 7) K4r's products, lane sums and epilogue
+    int acc[kRowRows];
+#pragma unroll
+    for (int r = 0; r < kRowRows; ++r) {
+        acc[r] = 0;
+        const uint32_t wd[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t b[4];
+            unpack16(wd[q], b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[r] = __builtin_amdgcn_sdot4((int)xa[4 * q + i], (int)b[i], acc[r], false);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kRowRows; ++r) acc[r] = wave_sum_i32(acc[r]);
+    if (lane < kRowRows) {
+        int sum = acc[0];
+#pragma unroll
+        for (int r = 1; r < kRowRows; ++r) sum = lane == r ? acc[r] : sum;
+        const int n = row0 + lane;
+        if (n < N) {
+            const float rs = *gamma_p / scale;
+            Y[n] = (float)sum * rs;
+        }
+    }
+}
+
 bool gemv_supported(int64_t M, int64_t K) { return M <= kGemvMaxM && K <= 16 * 64 * 16; }
 
 hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t* Wp,
@@ -599,6 +749,17 @@ hipError_t launch_gemv_decode(const void* X, bool x_bf16, const uint8_t* Wp, con
                               int64_t M, int64_t N, int64_t K, float eps, float* Y, int8_t* xq_out,
                               float* sx_out, hipStream_t s, bool decode_layout) {
     if (!gemv_decode_fits(x_bf16, M, K) || K % 16 != 0) return hipErrorInvalidValue;
+    if (M == 1 && !decode_layout && K % 64 == 0 && K <= kRowDecMaxK) {  // one token: the row GEMV
+        const unsigned grid = (unsigned)((N + kRowRows * kRowDecWaves - 1) / (kRowRows * kRowDecWaves));
+        constexpr unsigned kThreadsDec = kRowDecWaves * kWave;
+        if (x_bf16)
+            gemv_row_decode_kernel<uint16_t><<<grid, kThreadsDec, 0, s>>>(
+                static_cast<const uint16_t*>(X), Wp, gamma, (int)N, (int)K, eps, Y, xq_out, sx_out);
+        else
+            gemv_row_decode_kernel<float><<<grid, kThreadsDec, 0, s>>>(
+                static_cast<const float*>(X), Wp, gamma, (int)N, (int)K, eps, Y, xq_out, sx_out);
+        return hipGetLastError();
+    }
     if (x_bf16)
         return decode_dispatch(static_cast<const uint16_t*>(X), Wp, gamma, M, N, K, eps, Y, xq_out, sx_out, s,
                                decode_layout);

@@ -60,6 +60,9 @@ def _check(x, codes, gamma):
 DECODE_SHAPES = [
     (1, 16, 16), (1, 300, 256), (3, 33, 1040), (8, 100, 528), (8, 257, 4096), (9, 70, 4096),
     (16, 1000, 512), (16, 64, 4096), (5, 4200, 2048), (2, 17, 48), (4, 40, 4096),
+    # one token with K % 64 == 0 (the row kernel): a partial last block, N
+    # ragged against the 32-row workgroups, the smallest K
+    (1, 100, 1088), (1, 4099, 4096), (1, 33, 64),
 ]
 
 
@@ -78,9 +81,10 @@ def test_decode_matches_two_calls_and_oracle(M, N, K, dtype):
 
 
 @pytest.mark.parametrize("special", ["zero_row", "outliers", "single"])
-def test_decode_special_rows(special):
-    print(f"linear_fwd_decode special {special}", flush=True)
-    x, codes, gamma = _case(4, 96, 1024, torch.bfloat16, seed=7, special=special)
+@pytest.mark.parametrize("M", [1, 4])
+def test_decode_special_rows(special, M):
+    print(f"linear_fwd_decode special {special} M={M}", flush=True)
+    x, codes, gamma = _case(M, 96, 1024, torch.bfloat16, seed=7, special=special)
     _check(x, codes, gamma)
 
 
