@@ -263,8 +263,8 @@ int bitnet_linear_fwd_channel(const int8_t *Xq, const float *scale_x, const uint
  *   Xq       [M][K] int8, written when non-NULL (16-byte aligned)
  *   scale_x  [M] fp32, written when non-NULL
  * Every workgroup quantizes all M rows itself, so this pays off for a few
- * tokens (measured at K = 4096, N = 11008: 20% faster than the two calls at
- * M = 1, even at M = 8, slower at M = 16).
+ * tokens (measured at K = 4096, N = 11008: 15-20% faster than the two calls
+ * at M = 1 and 2, even at M = 8, slower at M = 16).
  * 1 <= M <= 16, K % 16 == 0, K <= 4096 (the quantized rows stay in LDS);
  * fp32 X also M * ceil(K / 256) <= 128 (the raw rows stay in registers: up
  * to 8 rows of 4096); N < 2^23; eps >= 0.  Other shapes: bitnet_act_quant
