@@ -383,14 +383,14 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
 
 // ------------------------------------------------ one token: the row GEMV
 // For a single token the matrix cores would multiply fifteen zero rows, and
-// K4's split of K over sixteen waves needs a reduction through LDS.  Here one
-// wave takes kRowRows weight rows with its lanes across K: lane l holds the
-// 64-column chunks l, l + 64, ... of each row (16 packed bytes per load, so
-// every load instruction reads 1 KB of one row), unpacks them with unpack16,
-// multiplies on the VALU with v_dot4 against the token's matching byte-
-// transposed activation chunks, and the 64 lane sums are added with DPP (the
-// integer sum is exact in any order).  The epilogue is K4's, operation for
-// operation, so Y and acc are the same bits.
+// gemv_t2_kernel's split of K over sixteen waves needs a reduction through
+// LDS.  Here one wave takes kRowRows weight rows with its lanes across K:
+// lane l holds the 64-column chunks l, l + 64, ... of each row (16 packed
+// bytes per load, so every load instruction reads 1 KB of one row), unpacks
+// them with unpack16, multiplies on the VALU with v_dot4 against the token's
+// matching byte-transposed activation chunks, and the 64 lane sums are added
+// with DPP (the integer sum is exact in any order).  The epilogue is
+// gemv_t2_kernel's, operation for operation, so Y and acc are the same bits.
 constexpr int kRowRows = 4;   // weight rows per wave
 constexpr int kRowWaves = 4;  // waves per workgroup
 
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_row_kernel(
 }
 
 // One token from the unquantized activations (the fused decode forward at
-// M = 1): act_quant's arithmetic on the row, then K4r's products.  The
+// M = 1): act_quant's arithmetic on the row, then gemv_row_kernel's products.  The
 // kRowDecWaves waves of a workgroup share the row: wave w reduces act_quant
 // blocks w, w + kRowDecWaves, ... (one 16-byte chunk per lane each), the
 // block partials meet in LDS, every wave forms the same 1/RMS and scale from
@@ -609,7 +609,7 @@ __global__ __launch_bounds__(kRowDecWaves * kWave) void gemv_row_decode_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) xa[4 * q + i] = o[i];
     }
-    // 7) K4r's products, lane sums and epilogue
+    // 7) gemv_row_kernel's products, lane sums and epilogue
     int acc[kRowRows];
 #pragma unroll
     for (int r = 0; r < kRowRows; ++r) {

@@ -16,7 +16,7 @@
 
 namespace bitnet {
 
-// ===================================================================== K2
+// ================================== act_quant: RMSNorm + per-token absmax int8
 // One wave per token row.  Block b of the row is the 64*E elements
 // [b*64E, (b+1)*64E); lane l holds elements b*64E + l*E .. +E-1 (one 16-byte
 // load, so each wave load is a fully coalesced 1 KiB).  The sum of squares is
@@ -339,7 +339,7 @@ hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, fl
     return act_quant_dispatch(static_cast<const float*>(X), M, K, eps, Xq, scale_x, s);
 }
 
-// ===================================================================== K1
+// ============================ weight_quant: absmean ternary codes, 2-bit packed
 // Pass 1: one wave per weight row -> tree sum of |w| over the row.
 // Pass 2: the tree over the row sums, gamma = max(S/(N*K), 1e-5), and the
 //         code threshold (below): one workgroup for large N, else every
