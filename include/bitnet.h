@@ -140,8 +140,9 @@ int bitnet_quant_operands(const void *X, int x_dtype, int64_t M, int64_t K, floa
  * (wide accumulator), [WALL 3.1] (+1 adds, -1 subtracts, 0 skips):
  *   acc[m][n] = sum_k Xq[m][k] * code[n][k]      (exact int32)
  *   Y[m][n]   = acc[m][n] * gamma / scale_x[m]   (fp32)
- * M <= 16 (with K <= 16384) takes the bandwidth-bound packed GEMV, other
- * shapes the int8 MFMA GEMM.
+ * M <= 16 (with K <= 16384) takes the bandwidth-bound packed GEMV (one
+ * token with K % 64 == 0 and K <= 8192: a VALU row GEMV, lanes across K),
+ * other shapes the int8 MFMA GEMM.  Every path gives the same bits.
  *   Xq       [M][K] int8;  scale_x [M] fp32;  W_packed [N][K/4];  gamma 1 fp32
  *   Y        [M][N] fp32, written
  *   acc      [M][N] int32, written when non-NULL (for exact checks)
