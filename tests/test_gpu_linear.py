@@ -163,3 +163,18 @@ def test_end_to_end_small_layer():
     gx, gw = bt.bitnet_linear_bwd_ste(to_dev(d["gy"]), out["Xq"], out["scale_x"], out["W_packed"], out["gamma"])
     assert_grad_close(gx.cpu().numpy(), oracle.ste_grad_x(host(d["gy"]), c_ref, g_ref), "grad_x")
     assert_grad_close(gw.cpu().numpy(), oracle.ste_grad_w(host(d["gy"]), q_ref, s_ref), "grad_W")
+
+
+def test_forward_paths_give_the_same_bits():
+    # the same token rows through the GEMM (M = 40), the GEMV (M = 9, 4) and
+    # the one-token row GEMV (M = 1): one epilogue formula, so identical bits
+    M, N, K = 40, 300, 1024
+    q, codes, scale_x, gamma = _quantized_operands(M, N, K, seed=77)
+    wp = to_dev(torch.from_numpy(oracle.pack(codes.numpy())))
+    qd, sd, gd = to_dev(q), to_dev(scale_x), to_dev(gamma)
+    y_all, a_all = bt.bitnet_linear_fwd(qd, sd, wp, gd, want_acc=True)
+    for m in (9, 4, 1):
+        y, a = bt.bitnet_linear_fwd(qd[:m].contiguous(), sd[:m].contiguous(), wp, gd, want_acc=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a, a_all[:m])
+        assert torch.equal(y.view(torch.int32), y_all[:m].view(torch.int32))
