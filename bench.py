@@ -522,7 +522,8 @@ def bench_decode(args):
         "config": {"workload": "decode_7b", "M": M, "N": N, "K": K, "weight_copies": copies,
                    "launches_timed": reps * copies},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "gemv_t2_kernel"},
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gemv_row_kernel" if M == 1 and K % 64 == 0 and K <= 8192 else "gemv_t2_kernel"},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
