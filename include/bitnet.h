@@ -4,15 +4,17 @@
  * Pages the operations follow (cited by title and section):
  *   [NOTES] "BitNet 1.5技术解析：2比特量化在神经网络中的应用与挑战"
  *           (intelliparadigm.com): 2.1 weight quantization, 2.2 activation
- *           quantization, 3.1 the BitLinear layer, 5.2 hardware needs.
+ *           quantization, 3.1 the BitLinear layer, 5.1 graph optimization
+ *           (fused quantize / dequantize), 5.2 hardware needs.
  *   [ENG]   "BitNet 三元权重量化训练工程：直通估计器与梯度裁剪实践"
  *           (blog.hotdry.top, 2025-10-04): section on the straight-through
  *           estimator for ternary weights (absmean, absmax per token,
  *           eps = 1e-5); section on gradient clipping (bf16 forward, fp32
  *           gradients).
  *   [WALL]  "1.58-bit量化技术突破AI算力与内存墙限制" (intelliparadigm.com):
- *           2.2 ternary quantization, 3.1 add/subtract matmul, 3.2 the STE,
- *           4.1 2-bit memory layout.
+ *           1 the memory wall, 2.2 ternary quantization, 3.1 add/subtract
+ *           matmul, 3.2 the STE, 4.1 2-bit memory layout, 5.1 deployment
+ *           (item 2: packing aligned for the loads).
  *
  * Conventions shared by every call
  *   - Tensors are row-major and contiguous.  Every tensor pointer is a
