@@ -105,11 +105,66 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _need(t: torch.Tensor, name: str):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+F32, BF16, I8, U8, I32, I64 = (torch.float32,), (torch.bfloat16,), (torch.int8,), (torch.uint8,), (torch.int32,), \
+    (torch.int64,)
+FLOAT = (torch.float32, torch.bfloat16)
+
+
+def _req(t, name: str, dtypes, numel: int = 0, dim=None, device=None):
+    """Check a tensor before its pointer reaches the library: present, of one
+    of `dtypes`, contiguous, `dim`-dimensional when given and holding at least
+    `numel` elements.  A tensor the kernels would read or write out of bounds
+    is a ValueError here, never a launch.  Where the tensors live is checked
+    by _on_gpu once every tensor of the call has passed this."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must be {dim}-D, got shape {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {numel}")
+    return t
+
+
+def _on_gpu(**tensors):
+    """Every tensor handed to one call is a device tensor, all on one device
+    (None entries are absent optional outputs)."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the call's other tensors on {dev}")
+
+
+def _opt(t, name: str, dtypes, numel: int, device):
+    """_req for an optional output (None passes)."""
+    return None if t is None else _req(t, name, dtypes, numel, device=device)
+
+
+def _ws(t, name: str, need: int, device):
+    """A workspace: a contiguous device tensor of at least `need` bytes."""
+    if t is None:
+        if need == 0:
+            return None
+        raise ValueError(f"{name}: {need} bytes required")
+    _req(t, name, None, 0, device=device)
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {need}")
+    return t
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def bitnet_status_str(status: int) -> str:
@@ -124,34 +179,43 @@ def bitnet_workspace_bytes(op: int, M: int, N: int, K: int) -> int:
     return int(load_library().bitnet_workspace_bytes(int(op), int(M), int(N), int(K)))
 
 
+def _alloc(t, shape, dtype, device):
+    return torch.empty(*shape, dtype=dtype, device=device) if t is None else t
+
+
+def _mk(t, name, what="[rows, cols]"):
+    """Rows and columns of a 2-D input tensor."""
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor {what}")
+    return int(t.shape[0]), int(t.shape[1])
+
+
 def bitnet_weight_quant(W: torch.Tensor, W_packed=None, gamma=None, workspace=None, stream=None):
     """Absmean ternary codes, 2-bit packed -> (W_packed uint8 [N,K/4], gamma f32 [1])."""
     lib = load_library()
-    _need(W, "W")
-    N, K = W.shape
+    N, K = _mk(W, "W", "[N, K]")
+    _req(W, "W", FLOAT)
     dev = W.device
-    if W_packed is None:
-        W_packed = torch.empty(N, K // 4, dtype=torch.uint8, device=dev)
-    if gamma is None:
-        gamma = torch.empty(1, dtype=torch.float32, device=dev)
     need = bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT, 0, N, K)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    W_packed = _req(_alloc(W_packed, (N, K // 4), torch.uint8, dev), "W_packed", U8, N * (K // 4), device=dev)
+    gamma = _req(_alloc(gamma, (1,), torch.float32, dev), "gamma", F32, 1, device=dev)
+    workspace = _ws(_alloc(workspace, (need,), torch.uint8, dev), "workspace", need, dev)
+    _on_gpu(W=W, W_packed=W_packed, gamma=gamma, workspace=workspace)
     _check("bitnet_weight_quant", lib.bitnet_weight_quant(
-        _ptr(W), _dtype_code(W), N, K, _ptr(W_packed), _ptr(gamma), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(W), _dtype_code(W), N, K, _ptr(W_packed), _ptr(gamma), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))
     return W_packed, gamma
 
 
 def bitnet_act_quant(X: torch.Tensor, eps: float = 1e-5, Xq=None, scale_x=None, stream=None):
     """RMSNorm + per-token absmax int8 -> (Xq int8 [M,K], scale_x f32 [M])."""
     lib = load_library()
-    _need(X, "X")
-    M, K = X.shape
-    if Xq is None:
-        Xq = torch.empty(M, K, dtype=torch.int8, device=X.device)
-    if scale_x is None:
-        scale_x = torch.empty(M, dtype=torch.float32, device=X.device)
+    M, K = _mk(X, "X", "[M, K]")
+    _req(X, "X", FLOAT)
+    dev = X.device
+    Xq = _req(_alloc(Xq, (M, K), torch.int8, dev), "Xq", I8, M * K, device=dev)
+    scale_x = _req(_alloc(scale_x, (M,), torch.float32, dev), "scale_x", F32, M, device=dev)
+    _on_gpu(X=X, Xq=Xq, scale_x=scale_x)
     _check("bitnet_act_quant", lib.bitnet_act_quant(
         _ptr(X), _dtype_code(X), M, K, ctypes.c_float(eps), _ptr(Xq), _ptr(scale_x), _stream(stream)))
     return Xq, scale_x
@@ -161,47 +225,74 @@ def bitnet_quant_operands(X, W, eps: float = 1e-5, Xq=None, scale_x=None, W_pack
                           workspace=None, stream=None):
     """act_quant(X) and weight_quant(W) with one launch fewer -> (Xq, scale_x, W_packed, gamma)."""
     lib = load_library()
-    _need(X, "X")
-    _need(W, "W")
-    M, K = X.shape
-    N = W.shape[0]
-    if W.shape[1] != K:
+    M, K = _mk(X, "X", "[M, K]")
+    N, Kw = _mk(W, "W", "[N, K]")
+    if Kw != K:
         raise ValueError("X and W must share K")
+    _req(X, "X", FLOAT)
     dev = X.device
-    if Xq is None:
-        Xq = torch.empty(M, K, dtype=torch.int8, device=dev)
-    if scale_x is None:
-        scale_x = torch.empty(M, dtype=torch.float32, device=dev)
-    if W_packed is None:
-        W_packed = torch.empty(N, K // 4, dtype=torch.uint8, device=dev)
-    if gamma is None:
-        gamma = torch.empty(1, dtype=torch.float32, device=dev)
-    ws_bytes = lib.bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT, 0, N, K)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    _req(W, "W", FLOAT, device=dev)
+    need = bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT, 0, N, K)
+    Xq = _req(_alloc(Xq, (M, K), torch.int8, dev), "Xq", I8, M * K, device=dev)
+    scale_x = _req(_alloc(scale_x, (M,), torch.float32, dev), "scale_x", F32, M, device=dev)
+    W_packed = _req(_alloc(W_packed, (N, K // 4), torch.uint8, dev), "W_packed", U8, N * (K // 4), device=dev)
+    gamma = _req(_alloc(gamma, (1,), torch.float32, dev), "gamma", F32, 1, device=dev)
+    workspace = _ws(_alloc(workspace, (max(need, 16),), torch.uint8, dev), "workspace", need, dev)
+    _on_gpu(X=X, W=W, Xq=Xq, scale_x=scale_x, W_packed=W_packed, gamma=gamma, workspace=workspace)
     _check("bitnet_quant_operands", lib.bitnet_quant_operands(
         _ptr(X), _dtype_code(X), M, K, ctypes.c_float(eps), _ptr(Xq), _ptr(scale_x), _ptr(W), _dtype_code(W), N,
-        _ptr(W_packed), _ptr(gamma), _ptr(workspace), workspace.numel(), _stream(stream)))
+        _ptr(W_packed), _ptr(gamma), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return Xq, scale_x, W_packed, gamma
+
+
+def _linear_operands(Xq, scale_x, W_packed, scale, scale_name, scale_numel):
+    """Shapes and checks shared by the forward and backward calls:
+    Xq int8 [M,K], scale_x f32 [M], W_packed uint8 [N,K/4], a scale."""
+    M, K = _mk(Xq, "Xq", "[M, K]")
+    N, KB = _mk(W_packed, "W_packed", "[N, K/4]")
+    if KB * 4 != K:
+        raise ValueError(f"W_packed must be [N, K/4] = [{N}, {K // 4}], got [{N}, {KB}]")
+    _req(Xq, "Xq", I8)
+    dev = Xq.device
+    _req(W_packed, "W_packed", U8, device=dev)
+    _req(scale_x, "scale_x", F32, M, device=dev)
+    _req(scale, scale_name, F32, scale_numel(N), device=dev)
+    return M, N, K, dev
 
 
 def bitnet_linear_fwd(Xq, scale_x, W_packed, gamma, Y=None, acc=None, want_acc=False, stream=None):
     """y = (Xq . codes^T) * gamma / scale_x -> (Y f32 [M,N], acc int32 [M,N] or None)."""
     lib = load_library()
-    for t, n in ((Xq, "Xq"), (scale_x, "scale_x"), (W_packed, "W_packed"), (gamma, "gamma")):
-        _need(t, n)
-    M, K = Xq.shape
-    N = W_packed.shape[0]
-    if W_packed.shape[1] * 4 != K:
-        raise ValueError("W_packed must be [N, K/4]")
-    if Y is None:
-        Y = torch.empty(M, N, dtype=torch.float32, device=Xq.device)
+    M, N, K, dev = _linear_operands(Xq, scale_x, W_packed, gamma, "gamma", lambda n: 1)
+    Y = _req(_alloc(Y, (M, N), torch.float32, dev), "Y", F32, M * N, device=dev)
     if acc is None and want_acc:
-        acc = torch.empty(M, N, dtype=torch.int32, device=Xq.device)
+        acc = torch.empty(M, N, dtype=torch.int32, device=dev)
+    acc = _opt(acc, "acc", I32, M * N, dev)
+    _on_gpu(Xq=Xq, scale_x=scale_x, W_packed=W_packed, gamma=gamma, Y=Y, acc=acc)
     _check("bitnet_linear_fwd", lib.bitnet_linear_fwd(
         _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(gamma), M, N, K, _ptr(Y), _ptr(acc),
         _stream(stream)))
     return Y, acc
+
+
+def _bwd_outputs(grad_y, M, N, K, dev, want_grad_x, want_grad_W, gx_dtype, grad_x, grad_W, workspace):
+    gy_rows, gy_cols = _mk(grad_y, "grad_y", "[M, N]")
+    if (gy_rows, gy_cols) != (M, N):
+        raise ValueError(f"grad_y must be [M, N] = [{M}, {N}], got [{gy_rows}, {gy_cols}]")
+    _req(grad_y, "grad_y", BF16, device=dev)
+    if grad_x is None and want_grad_x:
+        grad_x = torch.empty(M, K, dtype=gx_dtype, device=dev)
+    if grad_W is None and want_grad_W:
+        grad_W = torch.empty(N, K, dtype=torch.float32, device=dev)
+    grad_x = _opt(grad_x, "grad_x", FLOAT, M * K, dev)
+    grad_W = _opt(grad_W, "grad_W", F32, N * K, dev)
+    if grad_x is None and grad_W is None:
+        raise ValueError("at least one of grad_x, grad_W must be computed")
+    need = bitnet_workspace_bytes(BITNET_OP_LINEAR_BWD_STE, M, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _ws(workspace, "workspace", need, dev)
+    return grad_x, grad_W, workspace
 
 
 def bitnet_linear_bwd_ste(grad_y, Xq, scale_x, W_packed, gamma, want_grad_x=True, want_grad_W=True,
@@ -209,24 +300,15 @@ def bitnet_linear_bwd_ste(grad_y, Xq, scale_x, W_packed, gamma, want_grad_x=True
                           stream=None):
     """STE backward -> (grad_x [M,K] f32/bf16 or None, grad_W f32 [N,K] or None)."""
     lib = load_library()
-    for t, n in ((grad_y, "grad_y"), (Xq, "Xq"), (scale_x, "scale_x"), (W_packed, "W_packed"),
-                 (gamma, "gamma")):
-        _need(t, n)
-    M, K = Xq.shape
-    N = W_packed.shape[0]
-    dev = Xq.device
-    if grad_x is None and want_grad_x:
-        grad_x = torch.empty(M, K, dtype=gx_dtype, device=dev)
-    if grad_W is None and want_grad_W:
-        grad_W = torch.empty(N, K, dtype=torch.float32, device=dev)
-    need = bitnet_workspace_bytes(BITNET_OP_LINEAR_BWD_STE, M, N, K)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    M, N, K, dev = _linear_operands(Xq, scale_x, W_packed, gamma, "gamma", lambda n: 1)
+    grad_x, grad_W, workspace = _bwd_outputs(grad_y, M, N, K, dev, want_grad_x, want_grad_W, gx_dtype, grad_x,
+                                             grad_W, workspace)
     gx_code = _dtype_code(grad_x) if grad_x is not None else BITNET_F32
+    _on_gpu(grad_y=grad_y, Xq=Xq, scale_x=scale_x, W_packed=W_packed, gamma=gamma, grad_x=grad_x, grad_W=grad_W,
+            workspace=workspace)
     _check("bitnet_linear_bwd_ste", lib.bitnet_linear_bwd_ste(
-        _ptr(grad_y), _dtype_code(grad_y), _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(gamma),
-        M, N, K, _ptr(grad_x), gx_code, _ptr(grad_W), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(grad_y), BITNET_BF16, _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(gamma),
+        M, N, K, _ptr(grad_x), gx_code, _ptr(grad_W), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return grad_x, grad_W
 
 
@@ -234,13 +316,14 @@ def bitnet_rmsnorm_bwd(X, grad_n, eps: float = 1e-5, out_dtype=torch.float32, gr
     """Backward of the unit-gain RMSNorm: grad w.r.t. its input X given grad_n
     (w.r.t. its output) -> grad_X [M,K] f32/bf16."""
     lib = load_library()
-    _need(X, "X")
-    _need(grad_n, "grad_n")
-    M, K = X.shape
-    if tuple(grad_n.shape) != (M, K):
+    M, K = _mk(X, "X", "[M, K]")
+    if _mk(grad_n, "grad_n", "[M, K]") != (M, K):
         raise ValueError("grad_n must have X's shape")
-    if grad_X is None:
-        grad_X = torch.empty(M, K, dtype=out_dtype, device=X.device)
+    _req(X, "X", FLOAT)
+    dev = X.device
+    _req(grad_n, "grad_n", FLOAT, device=dev)
+    grad_X = _req(_alloc(grad_X, (M, K), out_dtype, dev), "grad_X", FLOAT, M * K, device=dev)
+    _on_gpu(X=X, grad_n=grad_n, grad_X=grad_X)
     _check("bitnet_rmsnorm_bwd", lib.bitnet_rmsnorm_bwd(
         _ptr(X), _dtype_code(X), _ptr(grad_n), _dtype_code(grad_n), M, K, ctypes.c_float(eps),
         _ptr(grad_X), _dtype_code(grad_X), _stream(stream)))
@@ -253,34 +336,28 @@ def bitnet_linear_bwd_ste_gated(grad_y, Xq, scale_x, W_packed, gamma, W, w_lo=-1
     """STE backward with grad_W zeroed where the master weight W lies outside
     [w_lo, w_hi] -> (grad_x or None, grad_W or None)."""
     lib = load_library()
-    for t, n in ((grad_y, "grad_y"), (Xq, "Xq"), (scale_x, "scale_x"), (W_packed, "W_packed"),
-                 (gamma, "gamma"), (W, "W")):
-        _need(t, n)
-    M, K = Xq.shape
-    N = W_packed.shape[0]
-    if tuple(W.shape) != (N, K):
+    M, N, K, dev = _linear_operands(Xq, scale_x, W_packed, gamma, "gamma", lambda n: 1)
+    if _mk(W, "W", "[N, K]") != (N, K):
         raise ValueError("W must be [N, K]")
-    dev = Xq.device
-    if grad_x is None and want_grad_x:
-        grad_x = torch.empty(M, K, dtype=gx_dtype, device=dev)
-    if grad_W is None and want_grad_W:
-        grad_W = torch.empty(N, K, dtype=torch.float32, device=dev)
-    need = bitnet_workspace_bytes(BITNET_OP_LINEAR_BWD_STE, M, N, K)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _req(W, "W", FLOAT, device=dev)
+    grad_x, grad_W, workspace = _bwd_outputs(grad_y, M, N, K, dev, want_grad_x, want_grad_W, gx_dtype, grad_x,
+                                             grad_W, workspace)
     gx_code = _dtype_code(grad_x) if grad_x is not None else BITNET_F32
+    _on_gpu(grad_y=grad_y, Xq=Xq, scale_x=scale_x, W_packed=W_packed, gamma=gamma, W=W, grad_x=grad_x, grad_W=grad_W,
+            workspace=workspace)
     _check("bitnet_linear_bwd_ste_gated", lib.bitnet_linear_bwd_ste_gated(
-        _ptr(grad_y), _dtype_code(grad_y), _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(gamma),
+        _ptr(grad_y), BITNET_BF16, _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(gamma),
         _ptr(W), _dtype_code(W), ctypes.c_float(w_lo), ctypes.c_float(w_hi), M, N, K, _ptr(grad_x), gx_code,
-        _ptr(grad_W), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(grad_W), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return grad_x, grad_W
 
 
 def bitnet_weight_clamp(W, lo=-1.0, hi=1.0, stream=None):
     """Clamp the master weights in place to [lo, hi]; returns W."""
     lib = load_library()
-    _need(W, "W")
-    N, K = W.shape
+    N, K = _mk(W, "W", "[N, K]")
+    _req(W, "W", FLOAT)
+    _on_gpu(W=W)
     _check("bitnet_weight_clamp", lib.bitnet_weight_clamp(
         _ptr(W), _dtype_code(W), N, K, ctypes.c_float(lo), ctypes.c_float(hi), _stream(stream)))
     return W
@@ -289,35 +366,29 @@ def bitnet_weight_clamp(W, lo=-1.0, hi=1.0, stream=None):
 def bitnet_weight_quant_rows(W: torch.Tensor, W_packed=None, gamma=None, workspace=None, stream=None):
     """Per-output-channel absmean codes -> (W_packed uint8 [N,K/4], gamma f32 [N])."""
     lib = load_library()
-    _need(W, "W")
-    N, K = W.shape
+    N, K = _mk(W, "W", "[N, K]")
+    _req(W, "W", FLOAT)
     dev = W.device
-    if W_packed is None:
-        W_packed = torch.empty(N, K // 4, dtype=torch.uint8, device=dev)
-    if gamma is None:
-        gamma = torch.empty(N, dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = torch.empty(bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT_ROWS, 0, N, K), dtype=torch.uint8,
-                                device=dev)
+    need = bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT_ROWS, 0, N, K)
+    W_packed = _req(_alloc(W_packed, (N, K // 4), torch.uint8, dev), "W_packed", U8, N * (K // 4), device=dev)
+    gamma = _req(_alloc(gamma, (N,), torch.float32, dev), "gamma", F32, N, device=dev)
+    workspace = _ws(_alloc(workspace, (need,), torch.uint8, dev), "workspace", need, dev)
+    _on_gpu(W=W, W_packed=W_packed, gamma=gamma, workspace=workspace)
     _check("bitnet_weight_quant_rows", lib.bitnet_weight_quant_rows(
-        _ptr(W), _dtype_code(W), N, K, _ptr(W_packed), _ptr(gamma), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(W), _dtype_code(W), N, K, _ptr(W_packed), _ptr(gamma), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))
     return W_packed, gamma
 
 
 def bitnet_linear_fwd_channel(Xq, scale_x, W_packed, s, Y=None, acc=None, want_acc=False, stream=None):
     """y = (Xq . codes^T) * s[n] / scale_x[m] -> (Y f32 [M,N], acc int32 or None)."""
     lib = load_library()
-    for t, n in ((Xq, "Xq"), (scale_x, "scale_x"), (W_packed, "W_packed"), (s, "s")):
-        _need(t, n)
-    M, K = Xq.shape
-    N = W_packed.shape[0]
-    if W_packed.shape[1] * 4 != K or s.numel() != N:
-        raise ValueError("W_packed must be [N, K/4] and s [N]")
-    if Y is None:
-        Y = torch.empty(M, N, dtype=torch.float32, device=Xq.device)
+    M, N, K, dev = _linear_operands(Xq, scale_x, W_packed, s, "s", lambda n: n)
+    Y = _req(_alloc(Y, (M, N), torch.float32, dev), "Y", F32, M * N, device=dev)
     if acc is None and want_acc:
-        acc = torch.empty(M, N, dtype=torch.int32, device=Xq.device)
+        acc = torch.empty(M, N, dtype=torch.int32, device=dev)
+    acc = _opt(acc, "acc", I32, M * N, dev)
+    _on_gpu(Xq=Xq, scale_x=scale_x, W_packed=W_packed, s=s, Y=Y, acc=acc)
     _check("bitnet_linear_fwd_channel", lib.bitnet_linear_fwd_channel(
         _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(s), M, N, K, _ptr(Y), _ptr(acc), _stream(stream)))
     return Y, acc
@@ -331,25 +402,31 @@ def bitnet_linear_fwd_decode(X, W_packed, gamma, eps: float = 1e-5, Y=None, Xq=N
     W_packed is [N, K/4] packed rows, or (with N given) the 1-D output of
     bitnet_pack_decode for those rows."""
     lib = load_library()
-    for t, n in ((X, "X"), (W_packed, "W_packed"), (gamma, "gamma")):
-        _need(t, n)
-    M, K = X.shape
+    M, K = _mk(X, "X", "[M, K]")
+    _req(X, "X", FLOAT)
+    dev = X.device
     if N is None:
         layout = BITNET_LAYOUT_ROWS
-        N = W_packed.shape[0]
-        if W_packed.dim() != 2 or W_packed.shape[1] * 4 != K:
+        if not isinstance(W_packed, torch.Tensor) or W_packed.dim() != 2 or W_packed.shape[1] * 4 != K:
             raise ValueError("W_packed must be [N, K/4]")
+        N = int(W_packed.shape[0])
+        _req(W_packed, "W_packed", U8, device=dev)
     else:
         layout = BITNET_LAYOUT_DECODE
         need = bitnet_decode_layout_bytes(N, K)
-        if W_packed.dim() != 1 or W_packed.dtype != torch.uint8 or W_packed.numel() != need:
+        if not isinstance(W_packed, torch.Tensor) or W_packed.dim() != 1 or W_packed.dtype != torch.uint8 \
+                or W_packed.numel() != need:
             raise ValueError(f"a decode-layout W_packed is 1-D uint8 of {need} bytes")
-    if Y is None:
-        Y = torch.empty(M, N, dtype=torch.float32, device=X.device)
+        _req(W_packed, "W_packed", U8, need, device=dev)
+    _req(gamma, "gamma", F32, 1, device=dev)
+    Y = _req(_alloc(Y, (M, N), torch.float32, dev), "Y", F32, M * N, device=dev)
     if want_q and Xq is None:
-        Xq = torch.empty(M, K, dtype=torch.int8, device=X.device)
+        Xq = torch.empty(M, K, dtype=torch.int8, device=dev)
     if want_q and scale_x is None:
-        scale_x = torch.empty(M, dtype=torch.float32, device=X.device)
+        scale_x = torch.empty(M, dtype=torch.float32, device=dev)
+    Xq = _opt(Xq, "Xq", I8, M * K, dev)
+    scale_x = _opt(scale_x, "scale_x", F32, M, dev)
+    _on_gpu(X=X, W_packed=W_packed, gamma=gamma, Y=Y, Xq=Xq, scale_x=scale_x)
     _check("bitnet_linear_fwd_decode", lib.bitnet_linear_fwd_decode(
         _ptr(X), _dtype_code(X), _ptr(W_packed), layout, _ptr(gamma), M, N, K, ctypes.c_float(eps),
         _ptr(Y), _ptr(Xq), _ptr(scale_x), _stream(stream)))
@@ -367,14 +444,13 @@ def bitnet_decode_layout_bytes(N: int, K: int) -> int:
 def bitnet_pack_decode(W_packed, W_decode=None, stream=None):
     """Packed rows [N, K/4] -> the same bytes in the decode layout (1-D uint8)."""
     lib = load_library()
-    _need(W_packed, "W_packed")
-    N, KB = W_packed.shape
+    N, KB = _mk(W_packed, "W_packed", "[N, K/4]")
+    _req(W_packed, "W_packed", U8)
+    dev = W_packed.device
     K = 4 * KB
     need = bitnet_decode_layout_bytes(N, K)
-    if W_decode is None:
-        W_decode = torch.empty(need, dtype=torch.uint8, device=W_packed.device)
-    elif W_decode.numel() != need:
-        raise ValueError(f"W_decode must hold {need} bytes")
+    W_decode = _req(_alloc(W_decode, (need,), torch.uint8, dev), "W_decode", U8, need, device=dev)
+    _on_gpu(W_packed=W_packed, W_decode=W_decode)
     _check("bitnet_pack_decode", lib.bitnet_pack_decode(_ptr(W_packed), N, K, _ptr(W_decode), _stream(stream)))
     return W_decode
 
@@ -383,53 +459,43 @@ def bitnet_linear_bwd_ste_channel(grad_y, Xq, scale_x, W_packed, s, want_grad_x=
                                   gx_dtype=torch.float32, grad_x=None, grad_W=None, workspace=None, stream=None):
     """STE backward at W_deq = s[n] * code -> (grad_x or None, grad_W or None)."""
     lib = load_library()
-    for t, n in ((grad_y, "grad_y"), (Xq, "Xq"), (scale_x, "scale_x"), (W_packed, "W_packed"), (s, "s")):
-        _need(t, n)
-    M, K = Xq.shape
-    N = W_packed.shape[0]
-    if s.numel() != N:
-        raise ValueError("s must be [N]")
-    dev = Xq.device
-    if grad_x is None and want_grad_x:
-        grad_x = torch.empty(M, K, dtype=gx_dtype, device=dev)
-    if grad_W is None and want_grad_W:
-        grad_W = torch.empty(N, K, dtype=torch.float32, device=dev)
-    need = bitnet_workspace_bytes(BITNET_OP_LINEAR_BWD_STE, M, N, K)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    M, N, K, dev = _linear_operands(Xq, scale_x, W_packed, s, "s", lambda n: n)
+    grad_x, grad_W, workspace = _bwd_outputs(grad_y, M, N, K, dev, want_grad_x, want_grad_W, gx_dtype, grad_x,
+                                             grad_W, workspace)
     gx_code = _dtype_code(grad_x) if grad_x is not None else BITNET_F32
+    _on_gpu(grad_y=grad_y, Xq=Xq, scale_x=scale_x, W_packed=W_packed, s=s, grad_x=grad_x, grad_W=grad_W,
+            workspace=workspace)
     _check("bitnet_linear_bwd_ste_channel", lib.bitnet_linear_bwd_ste_channel(
-        _ptr(grad_y), _dtype_code(grad_y), _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(s), M, N, K,
-        _ptr(grad_x), gx_code, _ptr(grad_W), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+        _ptr(grad_y), BITNET_BF16, _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(s), M, N, K,
+        _ptr(grad_x), gx_code, _ptr(grad_W), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return grad_x, grad_W
 
 
 def bitnet_code_counts(W_packed, K: int, counts=None, workspace=None, stream=None):
     """Counts of the packed codes -> int64 device tensor [zeros, +1, -1, unused 11]."""
     lib = load_library()
-    _need(W_packed, "W_packed")
-    N = W_packed.shape[0]
-    if W_packed.shape[1] * 4 != K:
+    N, KB = _mk(W_packed, "W_packed", "[N, K/4]")
+    if KB * 4 != K:
         raise ValueError("W_packed must be [N, K/4]")
-    if counts is None:
-        counts = torch.empty(4, dtype=torch.int64, device=W_packed.device)
-    if workspace is None:
-        workspace = torch.empty(bitnet_workspace_bytes(BITNET_OP_CODE_COUNTS, 0, N, K), dtype=torch.uint8,
-                                device=W_packed.device)
+    _req(W_packed, "W_packed", U8)
+    dev = W_packed.device
+    need = bitnet_workspace_bytes(BITNET_OP_CODE_COUNTS, 0, N, K)
+    counts = _req(_alloc(counts, (4,), torch.int64, dev), "counts", I64, 4, device=dev)
+    workspace = _ws(_alloc(workspace, (need,), torch.uint8, dev), "workspace", need, dev)
+    _on_gpu(W_packed=W_packed, counts=counts, workspace=workspace)
     _check("bitnet_code_counts", lib.bitnet_code_counts(
-        _ptr(W_packed), N, K, _ptr(counts), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+        _ptr(W_packed), N, K, _ptr(counts), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return counts
 
 
 def bitnet_pack_ternary(codes: torch.Tensor, W_packed=None, stream=None):
     """int8 codes [N,K] -> packed uint8 [N,K/4]."""
     lib = load_library()
-    _need(codes, "codes")
-    N, K = codes.shape
-    if W_packed is None:
-        W_packed = torch.empty(N, K // 4, dtype=torch.uint8, device=codes.device)
+    N, K = _mk(codes, "codes", "[N, K]")
+    _req(codes, "codes", I8)
+    dev = codes.device
+    W_packed = _req(_alloc(W_packed, (N, K // 4), torch.uint8, dev), "W_packed", U8, N * (K // 4), device=dev)
+    _on_gpu(codes=codes, W_packed=W_packed)
     _check("bitnet_pack_ternary", lib.bitnet_pack_ternary(
         _ptr(codes), N, K, _ptr(W_packed), _stream(stream)))
     return W_packed

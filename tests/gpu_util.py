@@ -10,7 +10,8 @@ DEV = "cuda:0"
 
 # Tolerances (stated by the workload spec): fp32 outputs within relative
 # error 1e-3; bf16-operand gradients within 2e-2, read elementwise against
-# |r| + RMS(r) (entries of a sum that cancels to ~0 get the row's scale) and
+# |r| + RMS(r), the RMS taken over all the reference entries compared (an
+# entry of a sum that cancels to ~0 gets the scale of the whole output), and
 # as a relative Frobenius error.
 Y_RTOL = 1e-3
 GRAD_TOL = 2e-2

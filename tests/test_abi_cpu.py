@@ -256,3 +256,76 @@ def test_binding_has_no_silent_fallback(tmp_path):
             bt.load_library(str(tmp_path / "missing.so"))
         finally:
             bt._lib = bt._lib_saved
+
+
+def _raises(fn, *a, match=None, **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(*a, **kw)
+
+
+def test_binding_checks_tensors_before_any_call():
+    # dtype, shape, contiguity and size are checked before the device; on this
+    # host every tensor is a CPU tensor, so a well-formed argument list stops
+    # at "must be a device tensor" and nothing reaches the library
+    import torch
+    M, N, K = 8, 16, 64
+    X = torch.zeros(M, K, dtype=torch.bfloat16)
+    W = torch.zeros(N, K, dtype=torch.float32)
+    Xq = torch.zeros(M, K, dtype=torch.int8)
+    sx = torch.ones(M, dtype=torch.float32)
+    wp = torch.zeros(N, K // 4, dtype=torch.uint8)
+    g = torch.ones(1, dtype=torch.float32)
+    gy = torch.zeros(M, N, dtype=torch.bfloat16)
+    # the quantizers
+    _raises(bt.bitnet_act_quant, X.half(), match="X must be")
+    _raises(bt.bitnet_act_quant, X[:, ::2], match="contiguous")
+    _raises(bt.bitnet_act_quant, X.reshape(-1), match="2-D")
+    _raises(bt.bitnet_act_quant, X, match="device tensor")
+    _raises(bt.bitnet_weight_quant, W.double(), match="W must be")
+    _raises(bt.bitnet_weight_quant, W, match="device tensor")
+    _raises(bt.bitnet_quant_operands, X, W[:, :32], match="share K")
+    # forward: every tensor's dtype and size
+    _raises(bt.bitnet_linear_fwd, Xq.float(), sx, wp, g, match="Xq must be")
+    _raises(bt.bitnet_linear_fwd, Xq, sx[:M - 1], wp, g, match="scale_x holds")
+    _raises(bt.bitnet_linear_fwd, Xq, sx.double(), wp, g, match="scale_x must be")
+    _raises(bt.bitnet_linear_fwd, Xq, sx, wp[:, :8], g, match="W_packed must be")
+    _raises(bt.bitnet_linear_fwd, Xq, sx, wp, g[:0], match="gamma holds")
+    _raises(bt.bitnet_linear_fwd, Xq, sx, wp, g, match="device tensor")
+    # backward: grad_y's shape and dtype, the outputs' sizes
+    _raises(bt.bitnet_linear_bwd_ste, gy.float(), Xq, sx, wp, g, match="grad_y must be torch.bfloat16")
+    _raises(bt.bitnet_linear_bwd_ste, gy, Xq, sx, wp, g, grad_W=torch.zeros(N, K - 1), match="grad_W holds")
+    _raises(bt.bitnet_linear_bwd_ste, gy, Xq, sx, wp, g, grad_x=torch.zeros(M, K, dtype=torch.int32),
+            match="grad_x must be")
+    _raises(bt.bitnet_linear_bwd_ste, gy, Xq, sx, wp, g, want_grad_x=False, want_grad_W=False, match="at least one")
+    _raises(bt.bitnet_linear_bwd_ste, gy, Xq, sx, wp, g, match="device tensor")
+    _raises(bt.bitnet_linear_bwd_ste, gy[:, :N - 1].contiguous(), Xq, sx, wp, g, match="grad_y must be")
+    _raises(bt.bitnet_linear_bwd_ste_channel, gy, Xq, sx, wp, g, match="s holds")
+    _raises(bt.bitnet_linear_bwd_ste_gated, gy, Xq, sx, wp, g, W[:, :32], match="W must be")
+    _raises(bt.bitnet_rmsnorm_bwd, X, X[:4], match="grad_n")
+    _raises(bt.bitnet_code_counts, wp, K + 4, match="W_packed must be")
+    _raises(bt.bitnet_pack_ternary, Xq.float(), match="codes must be")
+    _raises(bt.bitnet_linear_fwd_decode, X, wp.reshape(-1), g, match="W_packed must be")
+    _raises(bt.bitnet_linear_fwd_decode, X, wp, g, N=N, match="decode")
+
+
+def test_binding_rejects_undersized_outputs():
+    # an output too small for the kernels' writes, or of the wrong dtype, is
+    # rejected on the host; the device check comes after every tensor's size
+    # and dtype checks
+    import torch
+    from bit_ternary_quantized_amd import _on_gpu, _req, _ws
+    Y = torch.zeros(3, 4, dtype=torch.float32)
+    with pytest.raises(ValueError, match="holds 12 elements"):
+        _req(Y, "Y", bt.F32, 13)
+    with pytest.raises(ValueError, match="Y must be"):
+        _req(Y.half(), "Y", bt.F32, 12)
+    assert _req(Y, "Y", bt.F32, 12) is Y
+    with pytest.raises(ValueError, match="Y must be a device tensor"):
+        _on_gpu(acc=None, Y=Y)
+    with pytest.raises(ValueError, match="is required"):
+        _req(None, "Y", bt.F32, 12)
+    with pytest.raises(ValueError, match="bytes required"):
+        _ws(None, "workspace", 256, None)
+    assert _ws(None, "workspace", 0, None) is None
+    with pytest.raises(ValueError, match="holds 48 bytes, needs 64"):
+        _ws(Y, "workspace", 64, None)

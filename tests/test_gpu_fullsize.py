@@ -1,13 +1,14 @@
 """Parity at the full workload sizes, through the same calls the benchmark
 times (every output preallocated, the backward with its workspace).
 
-The oracle cannot redo a 70B-shaped layer in seconds, so it computes sampled
-outputs one by one: act quant on sampled rows (rows are independent), the
-weight codes and gamma in full (gamma needs the whole matrix), the int32
-accumulators, Y and both STE gradients at sampled entries.  Integer results
-must match bit for bit; Y within relative 1e-3; gradients within 2e-2 (the
-elementwise form against |r| + RMS of the sampled references).  The decode
-GEMV is checked on every output at each token count.
+The oracle cannot redo a 70B-shaped product in seconds, so it quantizes both
+operands in full (every activation row and its scale, the weight codes and
+gamma) and computes the products at sampled entries one by one: the int32
+accumulators, Y and both STE gradients.  Every reference is built from the
+oracle's own q, scale_x, codes and gamma, never from the GPU's buffers.
+Integer results must match bit for bit; Y within relative 1e-3; gradients
+within 2e-2 (the elementwise form against |r| + RMS of the sampled
+references).  The decode GEMV is checked on every output at each token count.
 """
 import numpy as np
 import pytest
@@ -21,13 +22,7 @@ from gpu_util import assert_grad_close, assert_y_close, f32_bits_equal, host, sa
 pytestmark = pytest.mark.gpu
 
 LAYERS = ["tiny", "small_llama", "prefill_7b", "qat_70b_mlp"]
-N_ROWS = 48       # sampled activation rows
 N_SAMPLES = 1500  # sampled (row, column) pairs per output
-
-
-def _rows(M, seed):
-    r = np.random.default_rng(seed).choice(M, size=min(M, N_ROWS), replace=False)
-    return np.unique(np.concatenate([r, [0, M - 1]]))
 
 
 @pytest.mark.parametrize("name", LAYERS)
@@ -55,21 +50,21 @@ def test_layer_full_size(name):
     assert np.array_equal(W_packed.cpu().numpy(), oracle.pack(c_ref)), "packed codes"
     print(f"  weight quant ok (gamma {g_ref:.6e})", flush=True)
 
-    # act quant: sampled rows, bit-exact
-    rows = _rows(M, seed=1)
-    xh = host(d["x"])
-    q_ref, s_ref = oracle.act_quant(xh[rows])
+    # act quant: every row, bit-exact
+    q_ref, s_ref = oracle.act_quant(host(d["x"]))
     q_gpu = Xq.cpu().numpy()
-    s_gpu = scale_x.cpu().numpy()
-    assert np.array_equal(q_gpu[rows], q_ref), "Xq rows"
-    assert f32_bits_equal(s_gpu[rows], s_ref), "scale_x bits"
-    print(f"  act quant ok on {rows.size} rows", flush=True)
+    bad = np.flatnonzero((q_gpu != q_ref).any(axis=1))
+    assert bad.size == 0, f"Xq differs on {bad.size} of {M} rows (first {bad[:8].tolist()})"
+    assert f32_bits_equal(scale_x.cpu().numpy(), s_ref), "scale_x bits"
+    del q_gpu
+    print(f"  act quant ok on all {M} rows", flush=True)
 
-    # forward: exact int32 at sampled (m, n) from the same int8 operands; Y
-    # from the launch the benchmark times (no accumulator output)
+    # forward: exact int32 at sampled (m, n), the reference from the oracle's
+    # q and codes; Y from the launch the benchmark times (no accumulator
+    # output)
     ms, ns = sample_pairs(M, N, N_SAMPLES, seed=2)
-    acc_ref = oracle.gemm_i32_at(q_gpu, c_ref, ms, ns)
-    y_ref = acc_ref.astype(np.float64) * np.float64(g_ref) / s_gpu[ms].astype(np.float64)
+    acc_ref = oracle.gemm_i32_at(q_ref, c_ref, ms, ns)
+    y_ref = acc_ref.astype(np.float64) * np.float64(g_ref) / s_ref[ms].astype(np.float64)
     assert_y_close(Y.cpu().numpy()[ms, ns], y_ref, "Y (sampled)")
     _, acc = bt.bitnet_linear_fwd(Xq, scale_x, W_packed, gamma, want_acc=True)
     torch.cuda.synchronize()
@@ -91,7 +86,7 @@ def test_layer_full_size(name):
     gx_ref = oracle.ste_grad_x_at(gyh, c_ref, g_ref, mk, kk)
     assert_grad_close(grad_x.cpu().numpy()[mk, kk], gx_ref, "grad_x (sampled)")
     nk_, kw = sample_pairs(N, K, N_SAMPLES, seed=4)
-    gw_ref = oracle.ste_grad_w_at(gyh, q_gpu, s_gpu, nk_, kw)
+    gw_ref = oracle.ste_grad_w_at(gyh, q_ref, s_ref, nk_, kw)
     assert_grad_close(grad_W.cpu().numpy()[nk_, kw], gw_ref, "grad_W (sampled)")
     print(f"  backward ok on {mk.size} + {nk_.size} samples", flush=True)
 
