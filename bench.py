@@ -2,35 +2,42 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one pass of the whole hot path over one batch of synthetic input:
-RMSNorm + per-token int8 activation quantization, absmean ternary weight
-quantization + packing (both quantizers in one bitnet_quant_operands call),
-the ternary x int8 forward with dequantization, and the STE backward
-(grad_x and grad_W).  Inputs are generated once on the
-host (seeded, see workloads.py), copied to HBM before timing, and every
-output buffer is preallocated, so the timed region is device work only.
+Default workload: prefill_7b, the 7B-shaped prefill forward (M = 8192 tokens,
+K = 4096, N = 4096; bf16 X with 0.1% outlier columns, bf16 master weights).
+A step is one forward pass of the layer over that batch: RMSNorm + per-token
+int8 activation quantization and absmean ternary weight quantization with
+2-bit packing (both in one bitnet_quant_operands call), then the ternary x
+int8 product with its dequantization (bitnet_linear_fwd).  Inputs are drawn
+once on the host (seeded, workloads.py), copied to HBM before timing, and
+every output buffer is preallocated, so the timed region is device work
+only; each step is one HIP graph replay.
 
-Default workload: small_llama (M=8192 tokens, K=512, N=1376: the MLP
-up-projection of the ~15M-parameter LLaMA-shaped model), the forward plus
-STE backward configuration.  Other workloads (--workload) are for
-profiling: tiny, prefill_7b (forward only), decode_7b (packed GEMV only,
-pre-quantized operands, weight copies rotated so every launch streams its
-weights from HBM), qat_70b_mlp (full step) and copy (a 1 GiB device copy,
-the calibration kernel for the HBM byte counters).
+The JSON line carries:
+  value       forward int8 TOPS: 2*M*N*K over the step time;
+  roofline    the step's dominant kernel, the int8 GEMM (gemm_i8t2_kernel):
+              2*M*N*K over its mean launch time from HIP events on its
+              stream, against the 5.0 POPS dense int8 peak and against the
+              measured ceiling (back-to-back int8 MFMAs on this device), with
+              the clock the device held; traffic = HBM bytes per launch from
+              rocprofv3 FETCH_SIZE + WRITE_SIZE recorded under profiles/;
+  decode      the packed GEMV at the 7B decode shape (N = 11008, K = 4096) at
+              M = 1 and M = 16, weights rotated over enough copies that every
+              launch streams them from HBM: GB/s against 8 TB/s and against a
+              one-launch streaming read of the same byte count;
+  ceilings    the measured ceilings (streaming reads of 11.3 MB, 12.0 MB and
+              67 MB, int8 and bf16 MFMA loops with their clocks);
+  kernels     every call of the step, and the variants, timed on its own;
+  cpu_baseline  the CPU oracle on this host's cores, on a bounded sample of
+              the same workload (threads and CPU model stated);
+  inputs      sha256 of every input tensor.
 
-Prints ONE JSON line.  `value` is the step's algorithmic operation rate:
-(2MNK int8 forward + 2MNK bf16 grad_x + 2MNK bf16 grad_W) / step time,
-in TOPS (forward-only workloads count 2MNK; decode reports GB/s of the
-bytes the GEMV must move).  `roofline` is the longest single product of
-the step (the backward call counts as its grad_x and grad_W products), its
-algorithmic work per launch over its per-launch time from HIP events on the
-stream it runs on; its `traffic` is the HBM bytes per launch from rocprofv3
-FETCH_SIZE + WRITE_SIZE recorded under profiles/ (null once the kernel
-sources differ from the profiled ones).  `kernels` breaks the step down per
-call; `cpu_baseline` is the CPU oracle timed on this host (a bounded sample
-of the same workload).
+Other workloads (--workload): small_llama and qat_70b_mlp add the STE backward
+(value stays the forward int8 rate; the backward's bf16 rate is reported on
+its own), tiny, decode_7b (the GEMV and the fused decode calls in detail) and
+copy (the 1 GiB device copy that calibrates the HBM byte counters).
 """
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -49,6 +56,7 @@ METRIC = "BitLinear fwd int8 TOPS & packed-GEMV GB/s (fraction of MI355X rooflin
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0    # dense int8 MFMA
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+INFINITY_CACHE = 256 << 20
 
 
 def parse():
@@ -56,17 +64,36 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="small_llama",
-                    choices=["small_llama", "tiny", "prefill_7b", "decode_7b", "qat_70b_mlp", "copy"])
-    ap.add_argument("--decode-m", type=int, default=16)
+    ap.add_argument("--workload", default="prefill_7b",
+                    choices=["prefill_7b", "small_llama", "qat_70b_mlp", "tiny", "decode_7b", "copy"])
+    ap.add_argument("--decode-m", type=int, default=16, help="tokens of --workload decode_7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="leave the decode GEMV out of a layer run")
+    ap.add_argument("--no-ceilings", action="store_true", help="leave the calibration kernels out")
     ap.add_argument("--two-streams", action="store_true",
                     help="run the two quantizers as two calls (act_quant, weight_quant) on two streams "
                          "inside the step graph (default: one bitnet_quant_operands call; every call in "
                          "order on one stream)")
     ap.add_argument("--step-only", action="store_true",
-                    help="time only the step's calls and its two backward products (no variant calls)")
+                    help="time only the step's calls (and the backward's two products), no variant calls")
     return ap.parse_args()
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def sha256(t):
+    h = hashlib.sha256()
+    h.update(t.detach().cpu().contiguous().view(torch.uint8).numpy().tobytes())
+    return h.hexdigest()
 
 
 class Timer:
@@ -87,6 +114,122 @@ class Timer:
         return out
 
 
+def capture(fn):
+    """Capture the kernels one call enqueues into a HIP graph (torch stream
+    capture; the library launches on the current stream and allocates
+    nothing when every buffer is passed in)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # one eager run on the capture stream before capturing
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+SLEEP_CYCLES = 50_000_000  # bounded spin that lets the host enqueue ahead
+REPS = 8                   # launches of one call per timed graph
+
+
+def time_graph(g, reps, warmup, per_replay):
+    """Mean device time of one unit of a graph: `reps` replays bracketed by
+    HIP events on the current stream (the stream the graph runs on), after
+    `warmup` untimed replays; each replay holds `per_replay` units."""
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda._sleep(SLEEP_CYCLES)
+    for i in range(reps):
+        ev[i].record()
+        g.replay()
+    ev[-1].record()
+    torch.cuda.synchronize()
+    return statistics.fmean(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / per_replay
+
+
+def hbm_entry(ms, nbytes, ceiling_gbs=None):
+    a = nbytes / (ms * 1e-3) / 1e9
+    e = {"ms": ms, "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a / HBM_PEAK_GBS,
+         "bytes": nbytes}
+    if ceiling_gbs:
+        e["ceiling"] = ceiling_gbs
+        e["frac_of_ceiling"] = a / ceiling_gbs
+    return e
+
+
+def mfma_entry(ms, ops, peak):
+    a = ops / (ms * 1e-3) / 1e12
+    return {"ms": ms, "bound": "mfma", "achieved": a, "peak": peak, "unit": "TFLOP/s", "frac": a / peak, "ops": ops}
+
+
+# ---------------------------------------------------------------- ceilings
+
+def cold_buffers(nbytes, min_total=2 * INFINITY_CACHE, dev="cuda:0"):
+    """Enough distinct buffers of `nbytes` that reading them in turn streams
+    from HBM, not from the 256 MB Infinity Cache."""
+    copies = max(2, -(-min_total // nbytes))
+    return [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(i & 0xff) for i in range(copies)]
+
+
+def stream_ceiling(nbytes, args, bufs=None):
+    """Best one-launch cold read of `nbytes` over a few launch shapes: ms and
+    GB/s, with the per-shape times."""
+    nbytes -= nbytes % 16
+    if bufs is None:
+        bufs = cold_buffers(nbytes)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    reps = max(8, args.steps // len(bufs))
+    per = {}
+    for wg in (256, 512, 1024, 2048, 4096, 8192):
+        g = capture(lambda wg=wg: [bt.bitnet_calib_stream_read(b, nbytes, wg, sink=sink) for b in bufs])
+        per[wg] = time_graph(g, reps, 1, len(bufs))
+    best = min(per, key=per.get)
+    return {"bytes": nbytes, "ms": per[best], "achieved": nbytes / (per[best] * 1e-3) / 1e9, "unit": "GB/s",
+            "workgroups": best, "ms_by_workgroups": {str(k): v for k, v in per.items()},
+            "copies_rotated": len(bufs), "kernel": "stream_read_kernel (bitnet_calib_stream_read)"}
+
+
+def mfma_ceiling(kind, args):
+    """Back-to-back MFMAs on random operands over the whole device; rate and
+    the clock each workgroup measured (cycles / 100 MHz ticks)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs, iters = 4 * cus, 2048  # four 4-wave workgroups per CU: 4 waves per SIMD
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    clocks = torch.zeros(wgs, 2, dtype=torch.int64, device="cuda:0")
+    ops = [0.0]
+
+    def launch():
+        _, ops[0] = bt.bitnet_calib_mfma(kind, wgs, iters, sink=sink, clocks=clocks)
+    g = capture(launch)
+    ms = time_graph(g, max(3, args.steps // 10), 2, 1)
+    c = clocks.cpu().double()
+    ghz = float((c[:, 0] / c[:, 1]).median()) * 0.1
+    i8 = kind in (bt.BITNET_CALIB_MFMA_I8, bt.BITNET_CALIB_MFMA_I8_TERNARY)
+    peak = INT8_PEAK_TOPS if i8 else BF16_PEAK_TFLOPS
+    a = ops[0] / (ms * 1e-3) / 1e12
+    operands = "random x ternary codes" if kind in (bt.BITNET_CALIB_MFMA_I8_TERNARY,
+                                                   bt.BITNET_CALIB_MFMA_BF16_TERNARY) else "random x random"
+    return {"kind": ("int8 v_mfma_i32_32x32x32_i8" if i8 else "bf16 v_mfma_f32_32x32x16_bf16") + ", " + operands,
+            "ms": ms, "achieved": a, "unit": "TFLOP/s", "peak": peak, "frac": a / peak, "clock_ghz": ghz,
+            "workgroups": wgs, "iters": iters}
+
+
+def ceilings(args, sizes):
+    out = {"stream_read": {}, "clock_note": "shader clock = cycle counter / 100 MHz real-time counter, "
+                                            "median over the workgroups of the MFMA loop"}
+    for label, nbytes in sizes.items():
+        out["stream_read"][label] = stream_ceiling(nbytes, args)
+    out["mfma_int8"] = mfma_ceiling(bt.BITNET_CALIB_MFMA_I8, args)
+    out["mfma_int8_ternary"] = mfma_ceiling(bt.BITNET_CALIB_MFMA_I8_TERNARY, args)
+    out["mfma_bf16"] = mfma_ceiling(bt.BITNET_CALIB_MFMA_BF16, args)
+    out["mfma_bf16_ternary"] = mfma_ceiling(bt.BITNET_CALIB_MFMA_BF16_TERNARY, args)
+    return out
+
+
 # --------------------------------------------------------------- workloads
 
 def setup_layer(name):
@@ -100,7 +243,7 @@ def setup_layer(name):
         "scale_x": torch.empty(M, dtype=torch.float32, device=dev),
         "W_packed": torch.empty(N, K // 4, dtype=torch.uint8, device=dev),
         "gamma": torch.empty(1, dtype=torch.float32, device=dev),
-        "ws_wq": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, M, N, K),
+        "ws_wq": torch.empty(max(16, bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, M, N, K)),
                              dtype=torch.uint8, device=dev),
         "Y": torch.empty(M, N, dtype=torch.float32, device=dev),
         "counts": torch.empty(4, dtype=torch.int64, device=dev),
@@ -114,7 +257,7 @@ def setup_layer(name):
     if gy is not None:
         buf["grad_x"] = torch.empty(M, K, dtype=torch.float32, device=dev)
         buf["grad_W"] = torch.empty(N, K, dtype=torch.float32, device=dev)
-        buf["ws_bwd"] = torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, M, N, K),
+        buf["ws_bwd"] = torch.empty(max(16, bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, M, N, K)),
                                     dtype=torch.uint8, device=dev)
         buf["grad_X"] = torch.empty(M, K, dtype=torch.float32, device=dev)
         buf["w_clamp"] = w.clone()  # the clamp runs in place on a copy
@@ -196,12 +339,12 @@ SOURCES_OF = {
     "weight_quant_rows": ["bit_ternary_quantized_amd/csrc/quant.hip"],
     "linear_fwd_channel": ["bit_ternary_quantized_amd/csrc/gemm_i8.hip", "bit_ternary_quantized_amd/csrc/gemv.hip"],
     "bwd_grad_x_channel": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
+    "decode_gemv": ["bit_ternary_quantized_amd/csrc/gemv.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def source_digest(call):
-    import hashlib
     h = hashlib.sha256()
     for rel in SOURCES_OF.get(call, []) + ["bit_ternary_quantized_amd/csrc/common.h"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
@@ -224,23 +367,19 @@ def measured_traffic(call, workload):
 
 
 def rate(entry, ms):
-    s = ms * 1e-3
     if entry["bound"] == "hbm":
-        a = entry["bytes"] / s / 1e9
-        return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a / HBM_PEAK_GBS}
-    a = entry["ops"] / s / 1e12
-    return {"bound": "mfma", "achieved": a, "peak": entry["peak_ops"], "unit": "TFLOP/s",
-            "frac": a / entry["peak_ops"]}
+        return hbm_entry(ms, entry["bytes"])
+    return mfma_entry(ms, entry["ops"], entry["peak_ops"])
 
 
 def cpu_baseline_layer(d, gy_present, budget_s=12.0):
     """The oracle on this host, on the first S tokens of the same layer: act
     quant of those S rows, weight quant of the whole W (a step needs it
-    whatever the token count), forward and STE backward over the S tokens.
-    S is sized from a short calibration run so that one sample takes about
-    half the budget; the sample repeats until the budget is spent (at most
-    three times) and the median counts.  Rate = the GPU's algorithmic ops
-    for S tokens / seconds."""
+    whatever the token count), the forward (and, for a training workload,
+    the STE backward) over the S tokens.  S is sized from a short calibration
+    run so that one sample takes about half the budget; the sample repeats
+    until the budget is spent (at most three times) and the median counts.
+    Rate = the GPU's algorithmic ops for S tokens / seconds."""
     import oracle
     M, N, K = d["M"], d["N"], d["K"]
     xh = workloads.host_array(d["x"])
@@ -257,7 +396,7 @@ def cpu_baseline_layer(d, gy_present, budget_s=12.0):
             oracle.ste_grad_w(gyh[:S], q, s)
         return time.perf_counter() - t0
 
-    S = min(M, 64)
+    S = min(M, 16)
     t = run(S)
     S = int(max(1, min(M, S * (budget_s / 2) / max(t, 1e-9))))
     times = []
@@ -266,56 +405,44 @@ def cpu_baseline_layer(d, gy_present, budget_s=12.0):
         times.append(run(S))
     ops = (2 + (4 if gy_present else 0)) * S * N * K
     sec = statistics.median(times)
-    return {"value": ops / sec / 1e12, "unit": "TOPS", "cores": oracle.get_threads(), "kind": "oracle",
+    return {"value": ops / sec / 1e12, "unit": "TOPS", "cores": oracle.get_threads(), "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"first {S} of {M} tokens: act quant of those rows, weight quant of all of W, "
                       f"forward{' and STE backward' if gy_present else ''}; median of {len(times)} run(s) "
-                      f"of {sec:.2f} s",
+                      f"of {sec:.2f} s; ops counted as the GPU's ({'6' if gy_present else '2'}*S*N*K)",
             "seconds": sec}
-
-
-def capture(fn):
-    """Capture the kernels one call enqueues into a HIP graph (torch stream
-    capture; the library launches on the current stream and allocates
-    nothing when every buffer is passed in)."""
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        fn()  # one eager run on the capture stream before capturing
-    torch.cuda.current_stream().wait_stream(s)
-    with torch.cuda.graph(g):
-        fn()
-    torch.cuda.synchronize()
-    return g
-
-
-SLEEP_CYCLES = 50_000_000  # bounded spin that lets the host enqueue ahead
-REPS = 8                   # launches of one call per timed graph
 
 
 def bench_layer(args, name):
     d, x, w, gy, b = setup_layer(name)
     M, N, K = d["M"], d["N"], d["K"]
+    inputs = {"x": sha256(d["x"]), "w": sha256(d["w"])}
+    if gy is not None:
+        inputs["grad_y"] = sha256(d["gy"])
     calls = {
         "act_quant": lambda: bt.bitnet_act_quant(x, 1e-5, Xq=b["Xq"], scale_x=b["scale_x"]),
         "weight_quant": lambda: bt.bitnet_weight_quant(w, W_packed=b["W_packed"], gamma=b["gamma"],
                                                        workspace=b["ws_wq"]),
+        # both quantizers in one call (one launch fewer; same outputs)
+        "quant_operands": lambda: bt.bitnet_quant_operands(x, w, 1e-5, Xq=b["Xq"], scale_x=b["scale_x"],
+                                                           W_packed=b["W_packed"], gamma=b["gamma"],
+                                                           workspace=b["ws_wq"]),
         "linear_fwd": lambda: bt.bitnet_linear_fwd(b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], Y=b["Y"]),
     }
     if gy is not None:
         calls["linear_bwd_ste"] = lambda: bt.bitnet_linear_bwd_ste(
             gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], grad_x=b["grad_x"], grad_W=b["grad_W"],
             workspace=b["ws_bwd"])
-    names = list(calls)
-    # the backward call's two products, each timed on its own (not part of
-    # the step): grad_x is one kernel, grad_W one kernel plus the ordered
-    # split reduction when its token range is split
-    parts = {
+        # the backward call's two products, each timed on its own: grad_x is
+        # one kernel, grad_W one kernel plus the ordered split reduction when
+        # its token range is split
+        calls["bwd_grad_x"] = lambda: bt.bitnet_linear_bwd_ste(
+            gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], want_grad_W=False, grad_x=b["grad_x"])
+        calls["bwd_grad_W"] = lambda: bt.bitnet_linear_bwd_ste(
+            gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], want_grad_x=False, grad_W=b["grad_W"],
+            workspace=b["ws_bwd"])
+    variants = {
         "code_counts": lambda: bt.bitnet_code_counts(b["W_packed"], K, counts=b["counts"], workspace=b["ws_cc"]),
-        # both quantizers in one call (one launch fewer; same outputs)
-        "quant_operands": lambda: bt.bitnet_quant_operands(x, w, 1e-5, Xq=b["Xq"], scale_x=b["scale_x"],
-                                                           W_packed=b["W_packed"], gamma=b["gamma"],
-                                                           workspace=b["ws_wq"]),
         # per-output-channel variants (own buffers; not part of the step)
         "weight_quant_rows": lambda: bt.bitnet_weight_quant_rows(w, W_packed=b["W_packed_rows"], gamma=b["gamma_rows"],
                                                                  workspace=b["ws_wqr"]),
@@ -323,31 +450,23 @@ def bench_layer(args, name):
                                                                    b["gamma_rows"], Y=b["Y"]),
     }
     if gy is not None:
-        parts["bwd_grad_x"] = lambda: bt.bitnet_linear_bwd_ste(
-            gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], want_grad_W=False, grad_x=b["grad_x"])
-        parts["bwd_grad_x_channel"] = lambda: bt.bitnet_linear_bwd_ste_channel(
+        variants["bwd_grad_x_channel"] = lambda: bt.bitnet_linear_bwd_ste_channel(
             gy, b["Xq"], b["scale_x"], b["W_packed_rows"], b["gamma_rows"], want_grad_W=False, grad_x=b["grad_x"])
-        parts["bwd_grad_W"] = lambda: bt.bitnet_linear_bwd_ste(
-            gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], want_grad_x=False, grad_W=b["grad_W"],
-            workspace=b["ws_bwd"])
         # the gradient through the RMSNorm in front of the quantizer, from the
         # step's grad_x (timed on its own; not part of the step)
-        parts["rmsnorm_bwd"] = lambda: bt.bitnet_rmsnorm_bwd(x, b["grad_x"], 1e-5, grad_X=b["grad_X"])
+        variants["rmsnorm_bwd"] = lambda: bt.bitnet_rmsnorm_bwd(x, b["grad_x"], 1e-5, grad_X=b["grad_X"])
         # the STE variants: grad_W gated by the master weights in [-1, 1], and
         # the clamp of the master weights after an update
-        parts["bwd_grad_W_gated"] = lambda: bt.bitnet_linear_bwd_ste_gated(
+        variants["bwd_grad_W_gated"] = lambda: bt.bitnet_linear_bwd_ste_gated(
             gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], w, -1.0, 1.0, want_grad_x=False,
             grad_W=b["grad_W"], workspace=b["ws_bwd"])
-        parts["weight_clamp"] = lambda: bt.bitnet_weight_clamp(b["w_clamp"], -1.0, 1.0)
+        variants["weight_clamp"] = lambda: bt.bitnet_weight_clamp(b["w_clamp"], -1.0, 1.0)
 
     # --two-streams: the two quantizers (X and W), which are independent, run
     # on two streams (default priority) forked and joined with events, so the
-    # graph holds parallel branches; then the forward GEMM and the backward
-    # call.  Measured: 1-2.5% faster at the 7B and 70B shapes, 7% slower at
-    # small_llama (the join between the branches costs more than the overlap
-    # of two short kernels saves), so the default runs every call in order on
-    # one stream.  The backward's two products on two streams measured slower
-    # still: their workgroups, one per CU each, then compete for the CUs.
+    # graph holds parallel branches.  Measured faster at the 7B and 70B shapes
+    # by 1-2.5% against the two calls in order, but not against the one
+    # bitnet_quant_operands call the default step makes.
     side = torch.cuda.Stream()
 
     def fork_join(main_fn, side_fn):
@@ -362,48 +481,41 @@ def bench_layer(args, name):
         main_fn()
         main.wait_event(e1)
 
-    # The step: both quantizers in one call (bitnet_quant_operands: the same
-    # outputs as act_quant + weight_quant with one launch fewer), the forward,
-    # the backward.
-    step_calls = dict(calls)
-    step_calls["quant_operands"] = parts["quant_operands"]
-    step_names = ["quant_operands", "linear_fwd"] + (["linear_bwd_ste"] if gy is not None else [])
-
-    def step():
-        if not args.two_streams:
-            for n in step_names:
-                step_calls[n]()
-            return
-        fork_join(calls["act_quant"], calls["weight_quant"])
+    def forward():
+        if args.two_streams:
+            fork_join(calls["act_quant"], calls["weight_quant"])
+        else:
+            calls["quant_operands"]()
         calls["linear_fwd"]()
-        if gy is not None:
-            calls["linear_bwd_ste"]()
 
-    g_step = capture(step)
+    # the step: the forward (both quantizers in one call, then the product);
+    # a training workload adds the backward call, timed as its own graph so
+    # the forward's rate stays the forward's
+    g_fwd = capture(forward)
     for _ in range(args.warmup):
-        g_step.replay()
+        g_fwd.replay()
     torch.cuda.synchronize()
-
-    # timed region: K whole steps, one graph launch each
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for _ in range(args.steps):
-        g_step.replay()
+        g_fwd.replay()
     end.record()
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    dev_ms = start.elapsed_time(end) / args.steps
+    fwd_wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    fwd_ms = start.elapsed_time(end) / args.steps
+    bwd_ms = None
+    if gy is not None:
+        g_bwd = capture(calls["linear_bwd_ste"])
+        bwd_ms = time_graph(g_bwd, args.steps, args.warmup, 1)
 
     # per-call device time: each call captured REPS times back to back in
     # one graph; K replays of each, bracketed by HIP events on the stream
     # they run on.  A bounded spin first lets the host enqueue the whole loop,
     # so no host gap sits between two events.
-    if args.step_only:
-        parts = {n: f for n, f in parts.items() if n in ("bwd_grad_x", "bwd_grad_W", "quant_operands")}
-    allc = dict(calls, **parts)
+    allc = dict(calls) if args.step_only else dict(calls, **variants)
     timed = list(allc)
     g_rep = {n: capture(lambda n=n: [allc[n]() for _ in range(REPS)]) for n in timed}
     timer = Timer(timed, args.steps)
@@ -416,124 +528,159 @@ def bench_layer(args, name):
         timer.mark(i, len(timed))
     torch.cuda.synchronize()
     per = {n: v / REPS for n, v in timer.mean_ms().items()}
+    del g_rep
 
     counts = layer_counts(M, N, K, d["x"].element_size(), d["w"].element_size(), gy is not None)
-    kernels = {n: {"ms": per[n], **rate(counts[n], per[n])} for n in timed}
-    fwd_bwd = 2 + (4 if gy is not None else 0)
-    value = fwd_bwd * M * N * K / (ms * 1e-3) / 1e12
-    # roofline: the longest single product of the step (the backward call
-    # counts as its two products)
-    # the step's own products only (the other timed calls are variants)
-    cands = [n for n in timed if n in ("act_quant", "weight_quant", "linear_fwd", "bwd_grad_x", "bwd_grad_W")]
-    dom = max(cands, key=lambda n: per[n])
-    roof = dict(rate(counts[dom], per[dom]))
-    roof["kernel"] = KERNEL_OF[dom] + f" ({dom})"
-    roof["traffic"] = measured_traffic(dom, name)
+    kernels = {n: rate(counts[n], per[n]) for n in timed}
+    for n in kernels:
+        kernels[n]["kernel"] = KERNEL_OF.get(n, n)
+
+    ceil = None
+    if not args.no_ceilings:
+        sizes = {"act_quant_x": M * K * d["x"].element_size()}
+        ceil = ceilings(args, sizes)
+        # the activation quantizer against a one-launch read of its input
+        kernels["act_quant"]["ceiling_read_gbs"] = ceil["stream_read"]["act_quant_x"]["achieved"]
+        # the products against back-to-back MFMAs on operands of their kind:
+        # the forward and grad_x multiply by ternary codes, grad_W by
+        # dequantized activations
+        for n, c in (("linear_fwd", "mfma_int8_ternary"), ("bwd_grad_x", "mfma_bf16_ternary"),
+                     ("bwd_grad_W", "mfma_bf16")):
+            if n in kernels and kernels[n]["bound"] == "mfma":
+                kernels[n]["ceiling"] = ceil[c]["achieved"]
+                kernels[n]["frac_of_ceiling"] = kernels[n]["achieved"] / ceil[c]["achieved"]
+
+    value = 2 * M * N * K / (fwd_ms * 1e-3) / 1e12
+    # roofline: the forward's dominant kernel (the int8 GEMM at the
+    # prefill and training shapes)
+    roof = dict(kernels["linear_fwd"])
+    roof["kernel"] = KERNEL_OF["linear_fwd"] + " (bitnet_linear_fwd)"
+    roof["traffic"] = measured_traffic("linear_fwd", name)
+    roof["per_launch"] = f"{M}x{N}x{K} int8 product, 2*M*N*K = {2 * M * N * K} ops per launch"
+    if ceil is not None and roof["bound"] == "mfma":
+        # the forward's operands are int8 activations and ternary codes
+        c = ceil["mfma_int8_ternary"]
+        roof["ceiling"] = c["achieved"]
+        roof["frac_of_ceiling"] = roof["achieved"] / c["achieved"]
+        roof["ceiling_clock_ghz"] = c["clock_ghz"]
     out = {
         "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "device_ms_per_step": dev_ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "i8+bf16" if gy is not None else "i8",
-        "data": "synthetic",
+        "warmup": args.warmup, "ms_per_step": fwd_ms, "host_ms_per_step": fwd_wall_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": name, "M": M, "N": N, "K": K, "x_dtype": str(d["x"].dtype).split(".")[-1],
                    "w_dtype": str(d["w"].dtype).split(".")[-1],
-                   "step": "act_quant+weight_quant (two streams)+" + "+".join(step_names[1:]) if args.two_streams
-                   else "+".join(step_names), "launch": "one HIP graph per step",
-                   "schedule": "two streams: act_quant || weight_quant, then linear_fwd, then linear_bwd_ste"
-                   if args.two_streams else "every call in order on one stream"},
+                   "step": ("act_quant || weight_quant (two streams)" if args.two_streams else "quant_operands")
+                   + " + linear_fwd (the forward)",
+                   "value": "2*M*N*K int8 ops per forward step / step time",
+                   "launch": "one HIP graph per step"},
         "roofline": roof,
-        "kernels": kernels,
     }
+    if bwd_ms is not None:
+        out["backward"] = {"ms": bwd_ms, "call": "linear_bwd_ste (grad_x and grad_W)",
+                           **{k: v for k, v in mfma_entry(bwd_ms, 4 * M * N * K, BF16_PEAK_TFLOPS).items()
+                              if k != "ms"}}
+        out["config"]["backward"] = "linear_bwd_ste timed as its own graph; not in value"
+        dom = max(("bwd_grad_x", "bwd_grad_W"), key=lambda n: per[n])
+        out["backward"]["dominant"] = dom
+        out["backward"]["dominant_traffic"] = measured_traffic(dom, name)
+    if not args.no_decode and name == "prefill_7b":
+        out["decode"] = {}
+        for m in (1, 16):
+            e = decode_gemv(args, m)[0]
+            e.pop("inputs_sha256")
+            out["decode"][f"M={m}"] = e
+    out["kernels"] = kernels
+    if ceil is not None:
+        out["ceilings"] = ceil
+    out["inputs"] = {"generator": "workloads.py (torch CPU generators; X seed 0, W 1, grad_y 2)", "sha256": inputs}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_layer(d, gy is not None)
     return out
 
 
-def bench_decode(args):
-    """Packed GEMV at decode shape; weights rotated over enough copies that
-    every launch reads its 2-bit weights from HBM, not the 256 MB cache."""
-    M = args.decode_m
+# ------------------------------------------------------------------ decode
+
+def decode_gemv(args, M):
+    """The packed GEMV (bitnet_linear_fwd from q) at the 7B decode shape, with
+    the weights rotated over enough copies that every launch reads them from
+    HBM; and a one-launch cold streaming read of the same byte count."""
     d = workloads.workload("decode_7b", M=M)
     N, K = d["N"], d["K"]
     dev = "cuda:0"
     q, s, gm = d["q"].to(dev), d["scale_x"].to(dev), d["gamma"].to(dev)
     wp0 = bt.bitnet_pack_ternary(d["codes"].to(dev))
-    copies = max(2, (512 << 20) // wp0.numel() + 1)  # > 2x the Infinity Cache
+    copies = max(2, (2 * INFINITY_CACHE) // wp0.numel() + 1)
     wps = [wp0] + [wp0.clone() for _ in range(copies - 1)]
     Y = torch.empty(M, N, dtype=torch.float32, device=dev)
-    # one graph = one launch per weight copy, back to back; each replay
-    # streams every copy once
     g = capture(lambda: [bt.bitnet_linear_fwd(q, s, wp, gm, Y=Y) for wp in wps])
-    for _ in range(max(1, args.warmup // copies)):
-        g.replay()
-    torch.cuda.synchronize()
-    reps = max(1, args.steps // copies)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    torch.cuda._sleep(SLEEP_CYCLES)
-    t0 = time.perf_counter()
-    for i in range(reps):
-        ev[i].record()
-        g.replay()
-    ev[-1].record()
-    torch.cuda.synchronize()
-    ms = statistics.fmean(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / copies
+    reps = max(8, args.steps // copies * 4)
+    ms = time_graph(g, reps, max(1, args.warmup // copies), copies)
+    del g
     nbytes = N * K // 4 + M * K + 4 * M + 4 + 4 * M * N
-    gbs = nbytes / (ms * 1e-3) / 1e9
+    ceiling = None
+    if not args.no_ceilings:
+        ceiling = stream_ceiling(nbytes, args)
+    e = hbm_entry(ms, nbytes, ceiling["achieved"] if ceiling else None)
+    e["kernel"] = "gemv_row_kernel" if M == 1 and K % 64 == 0 and K <= 8192 else "gemv_t2_kernel"
+    e["traffic"] = measured_traffic("decode_gemv", f"decode_7b_m{M}")
+    e["config"] = {"M": M, "N": N, "K": K, "weight_copies": copies, "launches_timed": reps * copies,
+                   "bytes": "N*K/4 packed weights + M*K q + 4*M scale_x + 4 gamma + 4*M*N Y"}
+    if ceiling:
+        e["ceiling_read"] = ceiling
+    e["inputs_sha256"] = {"q": sha256(d["q"]), "codes": sha256(d["codes"]), "scale_x": sha256(d["scale_x"])}
+    return e, (q, s, gm, wps, Y, d)
 
-    # a whole decode step from the unquantized activations, per weight copy:
-    # act_quant then the GEMV (two launches), and the fused call (one launch)
+
+def bench_decode(args):
+    """Packed GEMV at decode shape and the whole decode step from bf16 X (two
+    calls, the fused call, the fused call on the decode layout)."""
+    M = args.decode_m
+    e, (q, s, gm, wps, Y, d) = decode_gemv(args, M)
+    N, K = d["N"], d["K"]
+    dev = "cuda:0"
+    copies = len(wps)
+    reps = max(8, args.steps // copies * 4)
     x = d["x"].to(dev)
     q2, s2 = torch.empty_like(q), torch.empty_like(s)
 
     def per_launch_ms(fn, weights=wps):
         gr = capture(lambda: [fn(wp) for wp in weights])
-        for _ in range(max(1, args.warmup // copies)):
-            gr.replay()
-        torch.cuda.synchronize()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        torch.cuda._sleep(SLEEP_CYCLES)
-        for i in range(reps):
-            e[i].record()
-            gr.replay()
-        e[-1].record()
-        torch.cuda.synchronize()
-        return statistics.fmean(e[i].elapsed_time(e[i + 1]) for i in range(reps)) / copies
+        return time_graph(gr, reps, max(1, args.warmup // copies), copies)
 
     # algorithmic bytes of a decode step: x (bf16) and the packed weights in, Y out
     step_bytes = N * K // 4 + 2 * M * K + 4 + 4 * M * N
-
-    def entry(t_ms, nb):
-        a = nb / (t_ms * 1e-3) / 1e9
-        return {"ms": t_ms, "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": a / HBM_PEAK_GBS}
-
-    kernels = {"linear_fwd": entry(ms, nbytes)}
-    kernels["act_quant+linear_fwd"] = entry(per_launch_ms(lambda wp: (
+    kernels = {"linear_fwd": {k: v for k, v in e.items() if k not in ("ceiling_read", "inputs_sha256")}}
+    kernels["act_quant+linear_fwd"] = hbm_entry(per_launch_ms(lambda wp: (
         bt.bitnet_act_quant(x, 1e-5, Xq=q2, scale_x=s2), bt.bitnet_linear_fwd(q2, s2, wp, gm, Y=Y))), step_bytes)
-    kernels["linear_fwd_decode"] = entry(
+    kernels["linear_fwd_decode"] = hbm_entry(
         per_launch_ms(lambda wp: bt.bitnet_linear_fwd_decode(x, wp, gm, 1e-5, Y=Y)), step_bytes)
     if K == 4096:  # the same call on the weights in the decode layout (repacked once, untimed)
         wds = [bt.bitnet_pack_decode(wp) for wp in wps]
-        kernels["linear_fwd_decode@decode_layout"] = entry(
+        kernels["linear_fwd_decode@decode_layout"] = hbm_entry(
             per_launch_ms(lambda wd: bt.bitnet_linear_fwd_decode(x, wd, gm, 1e-5, Y=Y, N=N), wds), step_bytes)
     out = {
-        "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "metric": METRIC, "value": e["achieved"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": e["ms"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
-        "config": {"workload": "decode_7b", "M": M, "N": N, "K": K, "weight_copies": copies,
-                   "launches_timed": reps * copies},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gemv_row_kernel" if M == 1 and K % 64 == 0 and K <= 8192 else "gemv_t2_kernel"},
+        "config": {"workload": "decode_7b", **e["config"]},
+        "roofline": {k: e[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel")},
         "kernels": kernels,
+        "inputs": {"sha256": e["inputs_sha256"]},
     }
+    if "ceiling_read" in e:
+        out["roofline"]["ceiling"] = e["ceiling"]
+        out["roofline"]["frac_of_ceiling"] = e["frac_of_ceiling"]
+        out["ceilings"] = {"stream_read": {"decode_bytes": e["ceiling_read"]}}
     if not args.no_cpu_baseline:
         import oracle
         qh, ch = d["q"].numpy(), d["codes"].numpy()
         t = time.perf_counter()
         oracle.gemm_i32(qh, ch)
         sec = time.perf_counter() - t
+        nbytes = e["bytes"]
         out["cpu_baseline"] = {"value": nbytes / sec / 1e9, "unit": "GB/s", "cores": oracle.get_threads(),
-                               "kind": "oracle", "sample": f"whole GEMV (M={M}) once, {sec:.2f} s"}
+                               "cpu": cpu_model(), "kind": "oracle",
+                               "sample": f"whole GEMV (M={M}) once, {sec:.2f} s"}
     return out
 
 

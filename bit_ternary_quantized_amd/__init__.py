@@ -30,7 +30,10 @@ EXPORTS = (
     "bitnet_linear_bwd_ste_channel", "bitnet_linear_fwd_decode", "bitnet_quant_operands",
     "bitnet_decode_layout_bytes", "bitnet_pack_decode",
     "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
+    # calibration kernels (include/bitnet_calib.h): measured ceilings
+    "bitnet_calib_stream_read", "bitnet_calib_mfma", "bitnet_calib_mfma_ops",
 )
+BITNET_CALIB_MFMA_I8, BITNET_CALIB_MFMA_BF16, BITNET_CALIB_MFMA_I8_TERNARY, BITNET_CALIB_MFMA_BF16_TERNARY = 0, 1, 2, 3
 
 
 class BitnetError(RuntimeError):
@@ -73,6 +76,9 @@ def load_library(path: str = LIB_PATH):
         "bitnet_workspace_bytes": (sz, [c_int, i64, i64, i64]),
         "bitnet_status_str": (ctypes.c_char_p, [c_int]),
         "bitnet_version": (c_int, []),
+        "bitnet_calib_stream_read": (c_int, [p, i64, c_int, p, p]),
+        "bitnet_calib_mfma": (c_int, [c_int, c_int, c_int, p, p, p]),
+        "bitnet_calib_mfma_ops": (ctypes.c_double, [c_int, c_int, c_int]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -499,6 +505,34 @@ def bitnet_pack_ternary(codes: torch.Tensor, W_packed=None, stream=None):
     _check("bitnet_pack_ternary", lib.bitnet_pack_ternary(
         _ptr(codes), N, K, _ptr(W_packed), _stream(stream)))
     return W_packed
+
+
+def bitnet_calib_stream_read(src, nbytes: int = None, workgroups: int = 1024, sink=None, stream=None):
+    """One-launch read of the first `nbytes` bytes of `src` (the measured
+    streaming ceiling of a bandwidth-bound call of that byte count)."""
+    lib = load_library()
+    _req(src, "src", None)
+    nbytes = _nbytes(src) if nbytes is None else int(nbytes)
+    if nbytes > _nbytes(src):
+        raise ValueError(f"src holds {_nbytes(src)} bytes, fewer than {nbytes}")
+    sink = _req(_alloc(sink, (1,), torch.int32, src.device), "sink", I32, 1)
+    _on_gpu(src=src, sink=sink)
+    _check("bitnet_calib_stream_read", lib.bitnet_calib_stream_read(
+        _ptr(src), nbytes, int(workgroups), _ptr(sink), _stream(stream)))
+    return sink
+
+
+def bitnet_calib_mfma(kind: int, workgroups: int, iters: int, sink=None, clocks=None, device="cuda",
+                      stream=None):
+    """Back-to-back MFMAs (int8 or bf16) -> (clocks int64 [workgroups, 2]: shader
+    cycles and 100 MHz ticks of each workgroup's loop, operation count)."""
+    lib = load_library()
+    sink = _req(_alloc(sink, (1,), torch.int32, device), "sink", I32, 1)
+    clocks = _req(_alloc(clocks, (workgroups, 2), torch.int64, device), "clocks", I64, 2 * workgroups)
+    _on_gpu(sink=sink, clocks=clocks)
+    _check("bitnet_calib_mfma", lib.bitnet_calib_mfma(int(kind), int(workgroups), int(iters), _ptr(sink),
+                                                      _ptr(clocks), _stream(stream)))
+    return clocks, float(lib.bitnet_calib_mfma_ops(int(kind), int(workgroups), int(iters)))
 
 
 def bitlinear_forward(X, W, eps: float = 1e-5, want_acc=False, stream=None):

@@ -10,6 +10,8 @@ import bit_ternary_quantized_amd as bt
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitnet.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 # Fake, 16-byte-aligned device addresses: every call below fails its host
 # checks first, so nothing is ever dereferenced or launched.
@@ -17,13 +19,17 @@ P = ctypes.c_void_p(1 << 20)
 NULL = None
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bitnet_\w+)\s*\(", text)))
+def declared_functions(paths=None):
+    names = set()
+    for path in paths or HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(bitnet_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_four_calls_and_helpers():
+    for n in ("bitnet_weight_quant", "bitnet_act_quant", "bitnet_linear_fwd", "bitnet_linear_bwd_ste"):
+        assert n in declared_functions([HEADER])
     names = declared_functions()
     for n in ("bitnet_weight_quant", "bitnet_act_quant", "bitnet_linear_fwd", "bitnet_linear_bwd_ste"):
         assert n in names
@@ -329,3 +335,27 @@ def test_binding_rejects_undersized_outputs():
     assert _ws(None, "workspace", 0, None) is None
     with pytest.raises(ValueError, match="holds 48 bytes, needs 64"):
         _ws(Y, "workspace", 64, None)
+
+
+def test_calibration_calls_reject_bad_arguments():
+    lib = bt.load_library()
+    f = lib.bitnet_calib_stream_read
+    assert f(NULL, 1024, 64, P, NULL) == -1
+    assert f(P, 1024, 64, NULL, NULL) == -1
+    assert f(P, 1000, 64, P, NULL) == -2   # not whole 16-byte loads
+    assert f(P, 0, 64, P, NULL) == -2
+    assert f(P, 1024, 0, P, NULL) == -2
+    assert f(ctypes.c_void_p((1 << 20) + 4), 1024, 64, P, NULL) == -4
+    g = lib.bitnet_calib_mfma
+    assert g(0, 4, 1, NULL, P, NULL) == -1
+    assert g(4, 4, 1, P, P, NULL) == -1    # unknown kind
+    assert g(-1, 4, 1, P, P, NULL) == -1
+    assert g(0, 0, 1, P, P, NULL) == -2
+    assert g(1, 4, 0, P, P, NULL) == -2
+    assert g(0, 4, 1, P, ctypes.c_void_p((1 << 20) + 4), NULL) == -4
+    # 4 waves x 8 MFMAs per iteration; 2*32*32*32 int8 ops, 2*32*32*16 bf16 flops
+    assert lib.bitnet_calib_mfma_ops(0, 3, 5) == 3 * 4 * 8 * 5 * 65536
+    assert lib.bitnet_calib_mfma_ops(1, 3, 5) == 3 * 4 * 8 * 5 * 32768
+    assert lib.bitnet_calib_mfma_ops(2, 3, 5) == 3 * 4 * 8 * 5 * 65536
+    assert lib.bitnet_calib_mfma_ops(3, 3, 5) == 3 * 4 * 8 * 5 * 32768
+    assert lib.bitnet_calib_mfma_ops(4, 3, 5) == 0.0
