@@ -22,6 +22,8 @@ BITNET_LAYOUT_ROWS, BITNET_LAYOUT_DECODE = 0, 1
 (BITNET_OP_WEIGHT_QUANT, BITNET_OP_LINEAR_BWD_STE, BITNET_OP_LINEAR_FWD, BITNET_OP_CODE_COUNTS,
  BITNET_OP_WEIGHT_QUANT_ROWS) = 0, 1, 2, 3, 4
 GEMV_MAX_M = 16  # linear_fwd runs the packed GEMV up to this many tokens
+BITNET_E_SCRATCH = -7
+NOALLOC_MAX_N = 1 << 18  # rows bitnet_weight_quant_noalloc's fixed scratch holds
 
 EXPORTS = (
     "bitnet_weight_quant", "bitnet_act_quant", "bitnet_linear_fwd", "bitnet_linear_bwd_ste",
@@ -30,6 +32,7 @@ EXPORTS = (
     "bitnet_linear_bwd_ste_channel", "bitnet_linear_fwd_decode", "bitnet_quant_operands",
     "bitnet_decode_layout_bytes", "bitnet_pack_decode",
     "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
+    "bitnet_weight_quant_noalloc",
     # calibration kernels (include/bitnet_calib.h): measured ceilings
     "bitnet_calib_stream_read", "bitnet_calib_mfma", "bitnet_calib_mfma_ops",
 )
@@ -76,6 +79,7 @@ def load_library(path: str = LIB_PATH):
         "bitnet_workspace_bytes": (sz, [c_int, i64, i64, i64]),
         "bitnet_status_str": (ctypes.c_char_p, [c_int]),
         "bitnet_version": (c_int, []),
+        "bitnet_weight_quant_noalloc": (c_int, [p, c_int, i64, i64, p, p, p]),
         "bitnet_calib_stream_read": (c_int, [p, i64, c_int, p, p]),
         "bitnet_calib_mfma": (c_int, [c_int, c_int, c_int, p, p, p]),
         "bitnet_calib_mfma_ops": (ctypes.c_double, [c_int, c_int, c_int]),
@@ -210,6 +214,20 @@ def bitnet_weight_quant(W: torch.Tensor, W_packed=None, gamma=None, workspace=No
     _check("bitnet_weight_quant", lib.bitnet_weight_quant(
         _ptr(W), _dtype_code(W), N, K, _ptr(W_packed), _ptr(gamma), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
+    return W_packed, gamma
+
+
+def bitnet_weight_quant_noalloc(W: torch.Tensor, W_packed, gamma, stream=None):
+    """bitnet_weight_quant without a workspace (the library's fixed device
+    scratch; N <= NOALLOC_MAX_N) into caller-provided W_packed and gamma."""
+    lib = load_library()
+    N, K = _mk(W, "W", "[N, K]")
+    _req(W, "W", FLOAT)
+    _req(W_packed, "W_packed", U8, N * (K // 4))
+    _req(gamma, "gamma", F32, 1)
+    _on_gpu(W=W, W_packed=W_packed, gamma=gamma)
+    _check("bitnet_weight_quant_noalloc", lib.bitnet_weight_quant_noalloc(
+        _ptr(W), _dtype_code(W), N, K, _ptr(W_packed), _ptr(gamma), _stream(stream)))
     return W_packed, gamma
 
 

@@ -4,6 +4,8 @@
 #include "../../include/bitnet.h"
 #include "common.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
@@ -34,6 +36,7 @@ const char* bitnet_status_str(int status) {
         case BITNET_E_ALIGN: return "pointer not 16-byte aligned";
         case BITNET_E_WORKSPACE: return "workspace missing or too small";
         case BITNET_E_HIP: return "HIP launch or runtime error";
+        case BITNET_E_SCRATCH: return "size beyond the fixed scratch of a no-allocation call";
         default: return "unknown status";
     }
 }
@@ -283,3 +286,55 @@ int bitnet_pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* W_pa
 }
 
 }  // extern "C"
+
+// ------------------------------------------------ no-allocation weight quant
+// bitnet_weight_quant_noalloc keeps the weight quantizer's scratch (the N row
+// sums and the code threshold) in this file-scope device array instead of a
+// caller workspace.  Each device the library runs on holds its own copy until
+// the process ends.  In host code `scratch` names a host-side stand-in, so
+// its device address is looked up once per device (hipGetSymbolAddress with
+// that device current) and only that address reaches the kernels.
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)(((BITNET_NOALLOC_MAX_N * 4 + 255) / 256) * 256 + 256);
+static_assert(kNoAllocScratchBytes >= 0, "scratch size");
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device); BITNET_E_HIP when the lookup fails.
+int scratch_ptr(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BITNET_E_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BITNET_E_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return BITNET_OK;
+}
+
+}  // namespace
+
+extern "C" int bitnet_weight_quant_noalloc(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* W_packed,
+                                           float* gamma, void* stream) {
+    if (!W || !W_packed || !gamma) return BITNET_E_ARG;
+    if (!float_dtype(w_dtype)) return BITNET_E_DTYPE;
+    if (N < 1 || K < 1 || K % 4 != 0 || N > kMaxDim || K > kMaxDim) return BITNET_E_SHAPE;
+    if (N > BITNET_NOALLOC_MAX_N) return BITNET_E_SCRATCH;
+    if (!aligned16(W) || !aligned16(W_packed) || !aligned4(gamma)) return BITNET_E_ALIGN;
+    if (bitnet::weight_quant_ws_bytes(N) > kNoAllocScratchBytes) return BITNET_E_SCRATCH;
+    void* ws = nullptr;
+    const int st = scratch_ptr(&ws);
+    if (st != BITNET_OK) return st;
+    // the kernels overwrite every scratch word they read (row sums, then the
+    // threshold): nothing needs clearing
+    return hip_status(bitnet::launch_weight_quant(W, w_dtype == BITNET_BF16, N, K, W_packed, gamma, ws,
+                                                  as_stream(stream)));
+}

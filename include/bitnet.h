@@ -23,7 +23,9 @@
  *     the host).  Pointers must be 16-byte aligned.
  *   - Ownership: the caller allocates and frees every buffer.  The library
  *     never allocates device memory, keeps no pointer after returning and
- *     has no mutable global state.
+ *     has no mutable global state, except the fixed device scratch of
+ *     bitnet_weight_quant_noalloc (one static array per device, described
+ *     there).
  *   - Asynchrony: a call validates its arguments on the host, enqueues its
  *     kernels on `stream` (a hipStream_t passed as void*; NULL = the null
  *     stream) and returns.  Outputs are valid once the stream reaches that
@@ -63,7 +65,8 @@ typedef enum {
     BITNET_E_DTYPE = -3,     /* unknown or unsupported dtype code           */
     BITNET_E_ALIGN = -4,     /* a pointer is not 16-byte aligned            */
     BITNET_E_WORKSPACE = -5, /* workspace missing or smaller than required  */
-    BITNET_E_HIP = -6        /* a HIP launch or runtime call failed         */
+    BITNET_E_HIP = -6,       /* a HIP launch or runtime call failed         */
+    BITNET_E_SCRATCH = -7    /* size beyond a no-allocation call's scratch  */
 } bitnet_status;
 
 typedef enum { BITNET_F32 = 0, BITNET_BF16 = 1 } bitnet_dtype;
@@ -99,6 +102,28 @@ typedef enum {
 int bitnet_weight_quant(const void *W, int w_dtype, int64_t N, int64_t K,
                         uint8_t *W_packed, float *gamma,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * bitnet_weight_quant without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same operation, same kernels and the same output
+ * bits as bitnet_weight_quant; the row sums and the code threshold live in a
+ * fixed device array inside the library instead of the caller's workspace.
+ *   W, w_dtype, N, K, W_packed, gamma as bitnet_weight_quant
+ *   N <= BITNET_NOALLOC_MAX_N (the scratch holds that many row sums,
+ *   1 MiB + 256 bytes per device); larger N returns BITNET_E_SCRATCH.
+ * The call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  Each GPU holds one copy of the scratch from the first call on it
+ * until the process ends, and every call on that GPU shares it: calls that
+ * overlap on one GPU (on different streams, or from several threads without
+ * ordering) race on it and give undefined results.  Calls ordered on one
+ * stream are safe; nothing in the scratch needs clearing between calls.
+ * Errors: BITNET_E_ARG, BITNET_E_SHAPE (K % 4), BITNET_E_DTYPE,
+ * BITNET_E_SCRATCH, BITNET_E_ALIGN, BITNET_E_HIP.
+ */
+#define BITNET_NOALLOC_MAX_N ((int64_t)1 << 18)
+int bitnet_weight_quant_noalloc(const void *W, int w_dtype, int64_t N, int64_t K,
+                                uint8_t *W_packed, float *gamma, void *stream);
 
 /*
  * RMSNorm (unit gain) followed by per-token absmax int8 quantization.

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     assert bt.bitnet_status_str(0) == "ok"
-    for s in range(-6, 0):
+    for s in range(-7, 0):
         assert bt.bitnet_status_str(s) not in ("ok", "unknown status")
     assert bt.bitnet_status_str(-99) == "unknown status"
     assert bt.bitnet_version() >= 10000
@@ -359,3 +359,17 @@ def test_calibration_calls_reject_bad_arguments():
     assert lib.bitnet_calib_mfma_ops(2, 3, 5) == 3 * 4 * 8 * 5 * 65536
     assert lib.bitnet_calib_mfma_ops(3, 3, 5) == 3 * 4 * 8 * 5 * 32768
     assert lib.bitnet_calib_mfma_ops(4, 3, 5) == 0.0
+
+
+def test_noalloc_weight_quant_rejects_bad_arguments():
+    lib = bt.load_library()
+    f = lib.bitnet_weight_quant_noalloc
+    assert f(NULL, 0, 4, 4, P, P, NULL) == -1
+    assert f(P, 0, 4, 4, NULL, P, NULL) == -1
+    assert f(P, 7, 4, 4, P, P, NULL) == -3
+    assert f(P, 0, 4, 6, P, P, NULL) == -2
+    assert f(P, 0, 0, 4, P, P, NULL) == -2
+    # more rows than the fixed scratch holds: its own status, nothing launched
+    assert f(P, 0, (1 << 18) + 1, 4, P, P, NULL) == -7
+    assert bt.bitnet_status_str(-7) != "unknown status"
+    assert f(ctypes.c_void_p((1 << 20) + 8), 0, 4, 4, P, P, NULL) == -4
