@@ -61,6 +61,10 @@ def _load():
         "oracle_weight_quant_rows": (ctypes.c_int, [_p, ctypes.c_int, _i64, _i64, _p, _p]),
         "oracle_dequant_channel": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _p]),
         "oracle_ste_grad_x_channel": (ctypes.c_int, [_p, ctypes.c_int, _p, _p, _i64, _i64, _i64, _p]),
+        "oracle_channel_scale_grad": (ctypes.c_int, [_p, ctypes.c_int, _p, _p, _p, _i64, _i64, _i64, _p]),
+        "oracle_channel_scale_grad_at": (ctypes.c_int, [_p, ctypes.c_int, _p, _p, _p, _i64, _i64, _i64, _p, _i64,
+                                                        _p]),
+        "oracle_codes_row_dot": (ctypes.c_int, [_p, _p, _i64, _i64, _p]),
         "oracle_mul_add_probe": (ctypes.c_float, [ctypes.c_float, ctypes.c_float, ctypes.c_float]),
     }
     for name, (res, args) in sig.items():
@@ -316,6 +320,40 @@ def ste_grad_x_channel(gy, codes, s):
     out = np.empty((M, K), np.float64)
     _check(_load().oracle_ste_grad_x_channel(_ptr(gy), dt, _ptr(codes), _ptr(s), M, N, K, _ptr(out)),
            "ste_grad_x_channel")
+    return out
+
+
+def channel_scale_grad(gy, q, scale_x, codes, ns=None):
+    """Gradient of a learned per-output-channel scale s (float64 [N], or at
+    the sampled channels ns): sum_m gy[m,n] * acc[m,n] / scale_x[m]."""
+    gy, dt = _float_input(gy)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scale_x = np.ascontiguousarray(scale_x, dtype=np.float32)
+    M, N = gy.shape
+    K = q.shape[1]
+    assert q.shape == (M, K) and codes.shape == (N, K) and scale_x.shape == (M,)
+    if ns is None:
+        out = np.empty(N, np.float64)
+        _check(_load().oracle_channel_scale_grad(_ptr(gy), dt, _ptr(q), _ptr(scale_x), _ptr(codes), M, N, K,
+                                                 _ptr(out)), "channel_scale_grad")
+        return out
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    out = np.empty(ns.size, np.float64)
+    _check(_load().oracle_channel_scale_grad_at(_ptr(gy), dt, _ptr(q), _ptr(scale_x), _ptr(codes), M, N, K,
+                                                _ptr(ns), ns.size, _ptr(out)), "channel_scale_grad_at")
+    return out
+
+
+def codes_row_dot(G, codes):
+    """sum_k codes[n,k] * G[n,k] per row in binary32 (canonical tree; a zero
+    total as +0) -> float32 [N]."""
+    G = np.ascontiguousarray(G, dtype=np.float32)
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    N, K = G.shape
+    assert codes.shape == (N, K)
+    out = np.empty(N, np.float32)
+    _check(_load().oracle_codes_row_dot(_ptr(G), _ptr(codes), N, K, _ptr(out)), "codes_row_dot")
     return out
 
 

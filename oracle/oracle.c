@@ -511,6 +511,66 @@ int oracle_ste_grad_x_channel(const void *gy, int gy_dtype, const int8_t *codes,
     return 0;
 }
 
+/* -------------------------- N4c: gradient of a learned per-channel scale
+ * "BitNet量化感知训练中的梯度传播优化" (blog.hotdry.top), section on the
+ * BitLinear implementation, 1 (weight scaling): output = (sign(W) . s) x with
+ * s in R^{d_out x 1} one scale per output row, LEARNED by gradient descent.
+ * With the per-channel forward above, y[m,n] = s_n * sum_k X_deq[m,k] *
+ * c[n,k] (X_deq = q / scale_x), so the chain rule gives
+ *   grad_s[n] = sum_m gy[m,n] * sum_k X_deq[m,k] * c[n,k]
+ *             = sum_m gy[m,n] * acc[m,n] / scale_x[m]
+ * with acc the exact integer product.  Float64 (a reference: it decides no
+ * integer); gy fp32 or bf16 (dtype flag as above). */
+static double scale_grad_row(const void *gy, int gy_dtype, const int8_t *q, const float *scale_x,
+                             const int8_t *codes, int64_t M, int64_t N, int64_t K, int64_t n) {
+    double s = 0.0;
+    for (int64_t m = 0; m < M; m++) {
+        int64_t acc = 0;
+        for (int64_t k = 0; k < K; k++) acc += (int64_t)q[m * K + k] * (int64_t)codes[n * K + k];
+        s += (double)load_elem(gy, gy_dtype, m * N + n) * (double)acc / (double)scale_x[m];
+    }
+    return s;
+}
+
+int oracle_channel_scale_grad(const void *gy, int gy_dtype, const int8_t *q, const float *scale_x,
+                              const int8_t *codes, int64_t M, int64_t N, int64_t K, double *gs) {
+    if (!gy || !q || !scale_x || !codes || !gs || M <= 0 || N <= 0 || K <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) gs[n] = scale_grad_row(gy, gy_dtype, q, scale_x, codes, M, N, K, n);
+    return 0;
+}
+
+/* The same at sampled output channels ns[0..count). */
+int oracle_channel_scale_grad_at(const void *gy, int gy_dtype, const int8_t *q, const float *scale_x,
+                                 const int8_t *codes, int64_t M, int64_t N, int64_t K, const int64_t *ns,
+                                 int64_t count, double *out) {
+    if (!gy || !q || !scale_x || !codes || !ns || !out || M <= 0 || N <= 0 || K <= 0) return -1;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t i = 0; i < count; i++) out[i] = scale_grad_row(gy, gy_dtype, q, scale_x, codes, M, N, K, ns[i]);
+    return 0;
+}
+
+/* Exchanging the two sums of grad_s: sum_m gy[m,n] * X_deq[m,k] is the STE
+ * gradient G = grad_W[n,k] of the dequantized weights (above), so
+ *   grad_s[n] = sum_k c[n,k] * G[n,k],
+ * the form that reuses the backward's grad_W.  Given a binary32 G this is
+ * evaluated in binary32: each product c*G (exact: c in {-1, 0, 1}) then the
+ * canonical tree over the row; a zero total is returned as +0 (the tree plus
+ * +0.0f).  out [N] fp32. */
+int oracle_codes_row_dot(const float *G, const int8_t *codes, int64_t N, int64_t K, float *out) {
+    if (!G || !codes || !out || N <= 0 || K <= 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++) {
+        float *p = (float *)malloc((size_t)K * sizeof(float));
+        if (!p) { bad |= 1; continue; }
+        for (int64_t k = 0; k < K; k++) p[k] = (float)codes[n * K + k] * G[n * K + k];
+        out[n] = oracle_tree_sum_f32(p, K) + 0.0f;
+        free(p);
+    }
+    return bad ? -2 : 0;
+}
+
 /* ------------------------------------------------- build-flag probe
  * Returns a*b + c as this file's build evaluates it.  With contraction off
  * it is fl(fl(a*b) + c), never fma(a, b, c); a test pins that. */

@@ -656,6 +656,87 @@ def test_channel_forward_and_grad_x():
     np.testing.assert_allclose(y, (xt.detach().numpy() @ wdeq.numpy().T), rtol=1e-12)
 
 
+# ------------------------------- gradient of a learned per-channel scale
+# "BitNet量化感知训练中的梯度传播优化", section on the BitLinear
+# implementation, 1: output = (sign(W) . s) x with s in R^{d_out x 1}
+# learned by gradient descent.
+
+def test_channel_scale_grad_equals_autograd_of_the_scaled_linear():
+    # float64 autograd of y = X_deq . (c * s)^T with s a parameter
+    rng = np.random.default_rng(90)
+    M, N, K = 7, 9, 24
+    q = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    codes = rng.integers(-1, 2, (N, K), dtype=np.int8)
+    sx = rng.uniform(20, 40, M).astype(np.float32)
+    gy = rng.standard_normal((M, N)).astype(np.float32)
+    s = torch.tensor(rng.uniform(0.01, 0.05, N), dtype=torch.float64, requires_grad=True)
+    xd = torch.tensor(q.astype(np.float64) / sx.astype(np.float64)[:, None])
+    c = torch.tensor(codes.astype(np.float64))
+    torch.nn.functional.linear(xd, c * s[:, None]).backward(torch.tensor(gy, dtype=torch.float64))
+    gs = oracle.channel_scale_grad(gy, q, sx, codes)
+    np.testing.assert_allclose(gs, s.grad.numpy(), rtol=1e-12, atol=1e-13)
+    # sampled form, and the bf16-bits input path
+    ns = np.array([0, 8, 3, 3], np.int64)
+    np.testing.assert_array_equal(oracle.channel_scale_grad(gy, q, sx, codes, ns=ns), gs[ns])
+    gyb = workloads.bf16_bits(torch.from_numpy(gy).to(torch.bfloat16))
+    gyw = torch.from_numpy(gy).to(torch.bfloat16).double().numpy()
+    ref = ((q.astype(np.float64) @ codes.astype(np.float64).T) / sx.astype(np.float64)[:, None] * gyw).sum(0)
+    np.testing.assert_allclose(oracle.channel_scale_grad(gyb, q, sx, codes), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_channel_scale_grad_worked_case():
+    # q = [[1, 2], [3, -4]], codes = [[1, -1], [0, 1]], scale_x = [2, 4]:
+    # acc = q c^T = [[-1, 2], [7, -4]]; acc / scale_x = [[-0.5, 1], [1.75, -1]]
+    # gy = [[1, 0.5], [2, -1]]: grad_s = [1*-0.5 + 2*1.75, 0.5*1 + -1*-1] = [3, 1.5]
+    q = np.array([[1, 2], [3, -4]], np.int8)
+    codes = np.array([[1, -1], [0, 1]], np.int8)
+    sx = np.array([2, 4], np.float32)
+    gy = np.array([[1, 0.5], [2, -1]], np.float32)
+    assert oracle.channel_scale_grad(gy, q, sx, codes).tolist() == [3.0, 1.5]
+    # a unit upstream gradient at (m, n) picks acc[m, n] / scale_x[m]
+    e = np.zeros((2, 2), np.float32)
+    e[1, 0] = 1.0
+    assert oracle.channel_scale_grad(e, q, sx, codes).tolist() == [1.75, 0.0]
+
+
+def test_channel_scale_grad_is_the_code_dot_of_grad_w():
+    # exchanging the sums: grad_s[n] = sum_k c[n,k] * grad_W[n,k]
+    rng = np.random.default_rng(91)
+    M, N, K = 11, 6, 40
+    q = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    codes = rng.integers(-1, 2, (N, K), dtype=np.int8)
+    sx = rng.uniform(20, 40, M).astype(np.float32)
+    gy = rng.standard_normal((M, N)).astype(np.float32)
+    gw = oracle.ste_grad_w(gy, q, sx)
+    np.testing.assert_allclose((codes.astype(np.float64) * gw).sum(1), oracle.channel_scale_grad(gy, q, sx, codes),
+                               rtol=1e-11, atol=1e-12)
+
+
+def test_codes_row_dot_order_and_signs():
+    # the canonical tree: (1e8 + 1) + (-1e8 + 1) = 1e8 + -1e8 = 0 in binary32,
+    # where a left-to-right sum would give 1
+    G = np.array([[1e8, 1.0, -1e8, 1.0]], np.float32)
+    one = np.ones((1, 4), np.int8)
+    assert oracle.codes_row_dot(G, one)[0] == np.float32(0.0)
+    # codes flip signs exactly; zero codes give +0 whatever the signs of G
+    c = np.array([[1, -1, -1, 0]], np.int8)
+    assert oracle.codes_row_dot(np.array([[2.0, 3.0, -5.0, 7.0]], np.float32), c)[0] == np.float32(4.0)
+    z = oracle.codes_row_dot(np.array([[-1.0, -2.0, -3.0, -4.0]], np.float32), np.zeros((1, 4), np.int8))[0]
+    assert z == 0.0 and not np.signbit(z)
+    # all codes +1: the tree sum of the row; negated codes: the exact negation
+    rng = np.random.default_rng(92)
+    G = rng.standard_normal((5, 300)).astype(np.float32)
+    ones = np.ones((5, 300), np.int8)
+    for n in range(5):
+        assert oracle.codes_row_dot(G, ones)[n] == oracle.tree_sum(G[n]) + np.float32(0.0)
+    cr = rng.integers(-1, 2, (5, 300), dtype=np.int8)
+    np.testing.assert_array_equal(oracle.codes_row_dot(G, -cr), -oracle.codes_row_dot(G, cr) + np.float32(0.0))
+    # close to the float64 dot product (within the tree's error bound)
+    ref = (cr.astype(np.float64) * G.astype(np.float64)).sum(1)
+    bound = 300 * 2.0 ** -24 * np.abs(G.astype(np.float64)).sum(1)
+    assert (np.abs(oracle.codes_row_dot(G, cr) - ref) <= bound).all()
+
+
 def test_oracle_does_not_contract_multiply_add():
     # a*b = 1 + 2^-11 + 2^-24 rounds to 1 + 2^-11 (tie to even), so the
     # unfused result is 0 while fma(a, b, c) would be 2^-24.
