@@ -29,7 +29,12 @@ The JSON line carries:
   kernels     every call of the step, and the variants, timed on its own;
   cpu_baseline  the CPU oracle on this host's cores, on a bounded sample of
               the same workload (threads and CPU model stated);
-  inputs      sha256 of every input tensor.
+  inputs      sha256 of every input tensor;
+  configs     the other layer configurations of the job, compactly: tiny
+              (32x256->256 fp32), small_llama (8192x512->1376, forward and
+              STE backward) and qat_70b_mlp (4096x8192->28672, forward and
+              STE backward): forward and backward times and rates, and each
+              call of their steps.
 
 Other workloads (--workload): small_llama and qat_70b_mlp add the STE backward
 (value stays the forward int8 rate; the backward's bf16 rate is reported on
@@ -70,6 +75,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="leave the decode GEMV out of a layer run")
     ap.add_argument("--no-ceilings", action="store_true", help="leave the calibration kernels out")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="prefill_7b: leave out the compact timings of tiny, small_llama and qat_70b_mlp")
     ap.add_argument("--two-streams", action="store_true",
                     help="run the two quantizers as two calls (act_quant, weight_quant) on two streams "
                          "inside the step graph (default: one bitnet_quant_operands call; every call in "
@@ -709,6 +716,30 @@ def bench_copy(args):
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "device copy"}}
 
 
+def config_summary(args, name):
+    """The step of another configuration, compactly: the forward (both
+    quantizers in one call, then the product) and, for a training
+    configuration, the STE backward, each as its own graph, and the step's
+    calls one by one."""
+    sub = argparse.Namespace(**vars(args))
+    sub.step_only, sub.no_ceilings, sub.no_cpu_baseline, sub.no_decode, sub.two_streams = True, True, True, True, False
+    sub.steps, sub.warmup = max(5, args.steps // 5), max(2, args.warmup // 5)
+    r = bench_layer(sub, name)
+    c = r["config"]
+    out = {"M": c["M"], "N": c["N"], "K": c["K"], "x_dtype": c["x_dtype"], "w_dtype": c["w_dtype"],
+           "forward_us": r["ms_per_step"] * 1e3, "forward_int8_tops": r["value"],
+           "gemm": {k: r["roofline"][k] for k in ("ms", "bound", "achieved", "unit", "frac")}}
+    if "backward" in r:
+        b = r["backward"]
+        out["backward_us"] = b["ms"] * 1e3
+        out["backward_bf16_tflops"] = b["achieved"]
+        out["backward_frac"] = b["frac"]
+        out["step_us"] = (r["ms_per_step"] + b["ms"]) * 1e3
+    out["calls_us"] = {n: e["ms"] * 1e3 for n, e in r["kernels"].items()}
+    out["inputs_sha256"] = r["inputs"]["sha256"]
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -722,6 +753,13 @@ def main():
         out = bench_copy(args)
     else:
         out = bench_layer(args, args.workload)
+        if args.workload == "prefill_7b" and not args.no_configs:
+            # the other layer configurations of the same job, compactly (their
+            # parity is in the tests; these are their timings on this device)
+            out["configs"] = {}
+            for name in ("tiny", "small_llama", "qat_70b_mlp"):
+                out["configs"][name] = config_summary(args, name)
+                torch.cuda.empty_cache()
     print(json.dumps(out))
 
 

@@ -32,7 +32,7 @@ EXPORTS = (
     "bitnet_linear_bwd_ste_channel", "bitnet_linear_fwd_decode", "bitnet_quant_operands",
     "bitnet_decode_layout_bytes", "bitnet_pack_decode",
     "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
-    "bitnet_weight_quant_noalloc",
+    "bitnet_weight_quant_noalloc", "bitnet_channel_scale_grad",
     # calibration kernels (include/bitnet_calib.h): measured ceilings
     "bitnet_calib_stream_read", "bitnet_calib_mfma", "bitnet_calib_mfma_ops",
 )
@@ -80,6 +80,7 @@ def load_library(path: str = LIB_PATH):
         "bitnet_status_str": (ctypes.c_char_p, [c_int]),
         "bitnet_version": (c_int, []),
         "bitnet_weight_quant_noalloc": (c_int, [p, c_int, i64, i64, p, p, p]),
+        "bitnet_channel_scale_grad": (c_int, [p, p, i64, i64, p, p]),
         "bitnet_calib_stream_read": (c_int, [p, i64, c_int, p, p]),
         "bitnet_calib_mfma": (c_int, [c_int, c_int, c_int, p, p, p]),
         "bitnet_calib_mfma_ops": (ctypes.c_double, [c_int, c_int, c_int]),
@@ -493,6 +494,23 @@ def bitnet_linear_bwd_ste_channel(grad_y, Xq, scale_x, W_packed, s, want_grad_x=
         _ptr(grad_y), BITNET_BF16, _ptr(Xq), _ptr(scale_x), _ptr(W_packed), _ptr(s), M, N, K,
         _ptr(grad_x), gx_code, _ptr(grad_W), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return grad_x, grad_W
+
+
+def bitnet_channel_scale_grad(grad_W, W_packed, grad_s=None, stream=None):
+    """Gradient of a learned per-output-channel scale from the STE backward's
+    grad_W [N,K] and the packed codes -> grad_s f32 [N]."""
+    lib = load_library()
+    N, K = _mk(grad_W, "grad_W", "[N, K]")
+    if _mk(W_packed, "W_packed", "[N, K/4]") != (N, K // 4) or K % 4:
+        raise ValueError(f"W_packed must be [N, K/4] = [{N}, {K // 4}]")
+    _req(grad_W, "grad_W", F32)
+    dev = grad_W.device
+    _req(W_packed, "W_packed", U8)
+    grad_s = _req(_alloc(grad_s, (N,), torch.float32, dev), "grad_s", F32, N)
+    _on_gpu(grad_W=grad_W, W_packed=W_packed, grad_s=grad_s)
+    _check("bitnet_channel_scale_grad", lib.bitnet_channel_scale_grad(
+        _ptr(grad_W), _ptr(W_packed), N, K, _ptr(grad_s), _stream(stream)))
+    return grad_s
 
 
 def bitnet_code_counts(W_packed, K: int, counts=None, workspace=None, stream=None):

@@ -277,6 +277,14 @@ int bitnet_rmsnorm_bwd(const void* X, int x_dtype, const void* grad_n, int g_dty
                                                  as_stream(stream)));
 }
 
+int bitnet_channel_scale_grad(const float* grad_W, const uint8_t* W_packed, int64_t N, int64_t K, float* grad_s,
+                              void* stream) {
+    if (!grad_W || !W_packed || !grad_s) return BITNET_E_ARG;
+    if (N < 1 || K < 1 || K % 16 != 0 || K >= kMaxK || N > kMaxDim) return BITNET_E_SHAPE;
+    if (!aligned16(grad_W) || !aligned16(W_packed) || !aligned4(grad_s)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_channel_scale_grad(grad_W, W_packed, N, K, grad_s, as_stream(stream)));
+}
+
 int bitnet_pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* W_packed,
                         void* stream) {
     if (!codes || !W_packed) return BITNET_E_ARG;

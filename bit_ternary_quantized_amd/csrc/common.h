@@ -272,6 +272,9 @@ hipError_t launch_code_counts(const uint8_t* W_packed, int64_t nbytes, uint64_t*
                               hipStream_t s);
 size_t code_counts_ws_bytes();
 size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K);
+// grad_s[n] = sum_k code[n][k] * G[n][k] (canonical tree; K % 16 == 0)
+hipError_t launch_channel_scale_grad(const float* G, const uint8_t* Wp, int64_t N, int64_t K, float* gs,
+                                     hipStream_t s);
 hipError_t launch_rmsnorm_bwd(const void* X, bool x_bf16, const void* G, bool g_bf16, int64_t M,
                               int64_t K, float eps, void* Out, bool out_bf16, hipStream_t s);
 

@@ -275,6 +275,31 @@ int bitnet_linear_fwd_channel(const int8_t *Xq, const float *scale_x, const uint
                               int32_t *acc, void *stream);
 
 /*
+ * Gradient of a LEARNED per-output-channel scale s ("BitNet量化感知训练中的
+ * 梯度传播优化" (blog.hotdry.top), section on the BitLinear implementation,
+ * 1: output = (sign(W) . s) x, s in R^{d_out x 1} learned by gradient
+ * descent).  With the forward of bitnet_linear_fwd_channel,
+ *   y[m][n] = s[n] * sum_k X_deq[m][k] * code[n][k],  X_deq = Xq / scale_x,
+ * the chain rule gives grad_s[n] = sum_m grad_y[m][n] * sum_k X_deq[m][k] *
+ * code[n][k]; exchanging the sums,
+ *   grad_s[n] = sum_k code[n][k] * grad_W[n][k]
+ * where grad_W = grad_y^T X_deq is the (ungated) grad_W output of
+ * bitnet_linear_bwd_ste_channel / bitnet_linear_bwd_ste on the same
+ * operands.  Each product is one binary32 multiplication (exact for codes in
+ * {-1, 0, +1}); each row is summed in binary32 as a pairwise tree over the
+ * row zero-padded to a power of two (the order of bitnet_weight_quant's
+ * sums); a zero total is written as +0.  The result follows from grad_W
+ * bit for bit.
+ *   grad_W   [N][K] fp32, read
+ *   W_packed [N][K/4] packed codes ([WALL 4.1] layout)
+ *   grad_s   [N] fp32, written
+ * K % 16 == 0, K < 2^24.
+ * Errors: BITNET_E_ARG, BITNET_E_SHAPE, BITNET_E_ALIGN, BITNET_E_HIP.
+ */
+int bitnet_channel_scale_grad(const float *grad_W, const uint8_t *W_packed, int64_t N, int64_t K,
+                              float *grad_s, void *stream);
+
+/*
  * Decode forward from the unquantized activations in one launch: the
  * activation quantizer of bitnet_act_quant fused into the packed GEMV of
  * bitnet_linear_fwd ([NOTES 5.1]: fuse the quantize and dequantize steps with

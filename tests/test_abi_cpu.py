@@ -373,3 +373,16 @@ def test_noalloc_weight_quant_rejects_bad_arguments():
     assert f(P, 0, (1 << 18) + 1, 4, P, P, NULL) == -7
     assert bt.bitnet_status_str(-7) != "unknown status"
     assert f(ctypes.c_void_p((1 << 20) + 8), 0, 4, 4, P, P, NULL) == -4
+
+
+def test_channel_scale_grad_rejects_bad_arguments():
+    lib = bt.load_library()
+    f = lib.bitnet_channel_scale_grad
+    assert f(NULL, P, 4, 16, P, NULL) == -1
+    assert f(P, NULL, 4, 16, P, NULL) == -1
+    assert f(P, P, 4, 16, NULL, NULL) == -1
+    assert f(P, P, 4, 8, P, NULL) == -2     # K % 16
+    assert f(P, P, 0, 16, P, NULL) == -2
+    assert f(P, P, 4, 1 << 24, P, NULL) == -2
+    assert f(ctypes.c_void_p((1 << 20) + 4), P, 4, 16, P, NULL) == -4
+    assert f(P, P, 4, 16, ctypes.c_void_p((1 << 20) + 2), NULL) == -4

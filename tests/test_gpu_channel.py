@@ -80,8 +80,11 @@ def test_channel_end_to_end_with_row_gammas():
     Y, acc = bt.bitnet_linear_fwd_channel(Xq, sx, wp, g, want_acc=True)
     gx, _ = bt.bitnet_linear_bwd_ste_channel(to_dev(d["gy"]), Xq, sx, wp, g, want_grad_W=False)
     torch.cuda.synchronize()
+    q_ref, s_ref = oracle.act_quant(host(d["x"]))
+    assert np.array_equal(Xq.cpu().numpy(), q_ref) and f32_bits_equal(sx.cpu().numpy(), s_ref)
     c_ref, g_ref = oracle.weight_quant_rows(host(d["w"]))
-    acc_ref, y_ref = oracle.linear_fwd_channel(Xq.cpu().numpy(), sx.cpu().numpy(), c_ref, g_ref)
+    assert np.array_equal(wp.cpu().numpy(), oracle.pack(c_ref)) and f32_bits_equal(g.cpu().numpy(), g_ref)
+    acc_ref, y_ref = oracle.linear_fwd_channel(q_ref, s_ref, c_ref, g_ref)
     assert np.array_equal(acc.cpu().numpy(), acc_ref)
     assert_y_close(Y.cpu().numpy(), y_ref)
     assert_grad_close(gx.cpu().numpy(), oracle.ste_grad_x_channel(host(d["gy"]), c_ref, g_ref), "grad_x")

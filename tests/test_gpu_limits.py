@@ -122,7 +122,10 @@ def test_linear_past_2_31_elements(big):
     codes = workloads.ternary_codes(N, BIG_K, 0.35, seed=5)
     wp = torch.from_numpy(oracle.pack(codes.numpy())).to(DEV)
     gamma = torch.tensor([0.0123], dtype=torch.float32, device=DEV)
-    Xq, scale_x = big["Xq"], big["scale_x"]
+    # seeded int8 operands and scales of this size (inputs, not act_quant's
+    # outputs: every reference below is computed from them)
+    Xq = torch.randint(-127, 128, (BIG_M, BIG_K), generator=_gen(9), device=DEV, dtype=torch.int32).to(torch.int8)
+    scale_x = torch.linspace(20.0, 40.0, BIG_M, dtype=torch.float32, device=DEV)
     gy = (torch.randn(BIG_M, N, generator=_gen(6), device=DEV, dtype=torch.float32) * 1e-3).to(torch.bfloat16)
     Y, acc = bt.bitnet_linear_fwd(Xq, scale_x, wp, gamma, want_acc=True)
     gx, gw = bt.bitnet_linear_bwd_ste(gy, Xq, scale_x, wp, gamma)

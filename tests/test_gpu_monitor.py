@@ -19,7 +19,9 @@ def test_code_counts_of_quantized_weights(N, K):
     c = bt.bitnet_code_counts(wp, K)
     c2 = bt.bitnet_code_counts(wp, K)  # counters cleared on every call
     torch.cuda.synchronize()
-    want = oracle.code_counts(wp.cpu().numpy(), K).astype(np.int64)
+    packed_ref = oracle.pack(oracle.weight_quant(host(w))[0])
+    assert np.array_equal(wp.cpu().numpy(), packed_ref)
+    want = oracle.code_counts(packed_ref, K).astype(np.int64)
     assert np.array_equal(c.cpu().numpy(), want)
     assert np.array_equal(c2.cpu().numpy(), want)
     assert int(want.sum()) == N * K and want[3] == 0

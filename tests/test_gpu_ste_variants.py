@@ -13,7 +13,7 @@ import torch
 import bit_ternary_quantized_amd as bt
 import oracle
 import workloads
-from gpu_util import host, to_dev
+from gpu_util import f32_bits_equal, host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +28,14 @@ def _operands(M, N, K, w_dtype, seed):
     return d, wd, gy, Xq, sx, Wp, gamma
 
 
+def _oracle_q(d, Xq, sx):
+    """The oracle's q and scale_x of the layer's X, checked equal to the
+    library's (the references below are built from the oracle's)."""
+    q_ref, s_ref = oracle.act_quant(host(d["x"]))
+    assert np.array_equal(Xq.cpu().numpy(), q_ref) and f32_bits_equal(sx.cpu().numpy(), s_ref)
+    return q_ref, s_ref
+
+
 # plain 128x128 tiles, a token split (2048 tokens over 100x48), 256x256 tiles
 GATE_SHAPES = [(300, 257, 272), (2048, 100, 48), (64, 1024, 16384)]
 
@@ -39,7 +47,8 @@ def test_gated_ste_grad_w(M, N, K, w_dtype):
     d, wd, gy, Xq, sx, Wp, gamma = _operands(M, N, K, w_dtype, seed=M + N + K)
     gx0, _ = bt.bitnet_linear_bwd_ste(gy, Xq, sx, Wp, gamma, want_grad_W=False)
     torch.cuda.synchronize()
-    ref = oracle.ste_grad_w(host(gy), Xq.cpu().numpy(), sx.cpu().numpy())
+    q_ref, s_ref = _oracle_q(d, Xq, sx)
+    ref = oracle.ste_grad_w(host(gy), q_ref, s_ref)
     rms = float(np.sqrt(np.mean(ref * ref)))
     for lo, hi in ((-1.0, 1.0), (-0.5, 0.25)):
         gx, gw = bt.bitnet_linear_bwd_ste_gated(gy, Xq, sx, Wp, gamma, wd, lo, hi)
