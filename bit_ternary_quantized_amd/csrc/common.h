@@ -194,13 +194,22 @@ struct PairwiseStack {
 // c0+12+j in bytes 0..3 (a 4x4 byte transpose of the natural order); the
 // other matrix-core operand is brought into the same order with
 // transpose4x4_bytes() so that every dot product pairs equal columns.
+//
+// Nine VALU operations per 16 codes.  v_perm_b32 picks byte sel (0..7) of
+// {S0, S1} (S1 = bytes 0..3), and for sel 8 the sign of byte 1 replicated,
+// for sel 12 the byte 0x00.  Codes 0 and 2 of each byte are masked in place
+// (sel 0..3) and looked up in kLut; codes 1 and 3 are masked without a shift
+// (sel 0, 4, 8, 12 for the codes 00, 01, 10, 11) and looked up in the pair
+// {S0 = 0x01, S1 = 0x8000}: sel 0 -> 0x00, 4 -> 0x01, 8 -> 0xff (sign of
+// 0x80), 12 -> 0x00.  The unused code 11 unpacks to 0 in every position.
 __device__ __forceinline__ void unpack16(uint32_t w, uint32_t (&out)[4]) {
     // byte LUT indexed by the 2-bit code: 0 -> 0x00, 1 -> 0x01, 2 -> 0xff
     constexpr uint32_t kLut = 0x00ff0100u;
     out[0] = __builtin_amdgcn_perm(0u, kLut, w & 0x03030303u);
-    out[1] = __builtin_amdgcn_perm(0u, kLut, (w >> 2) & 0x03030303u);
-    out[2] = __builtin_amdgcn_perm(0u, kLut, (w >> 4) & 0x03030303u);
-    out[3] = __builtin_amdgcn_perm(0u, kLut, (w >> 6) & 0x03030303u);
+    out[1] = __builtin_amdgcn_perm(0x00000001u, 0x00008000u, w & 0x0C0C0C0Cu);
+    const uint32_t w4 = w >> 4;
+    out[2] = __builtin_amdgcn_perm(0u, kLut, w4 & 0x03030303u);
+    out[3] = __builtin_amdgcn_perm(0x00000001u, 0x00008000u, w4 & 0x0C0C0C0Cu);
 }
 
 // a[j] byte b -> out[b] byte j.

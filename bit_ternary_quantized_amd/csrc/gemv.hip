@@ -17,9 +17,12 @@
 // step s the s-th 16-column chunk of every quarter (the sum over k is exact
 // and order-free).  A lane's activation operand is then the same columns for
 // every row group, held in registers (byte-transposed 4 x 4 to match the
-// column order unpack16 produces; tokens >= M are zero).  Its loads are
-// issued first, so the later wait for them does not wait for the weight
-// stream (loads retire in issue order).  Then every packed
+// column order unpack16 produces; tokens >= M are zero).  With K <= 4096 the
+// token rows come in as coalesced 16-byte loads, are byte-transposed and
+// written to an LDS tile, all before the first weight load is issued (with
+// the weight stream already in flight the activation lines return behind
+// it), and every lane then reads its operand from the tile.  The row factors
+// gamma / scale_x are requested at the start as well.  Then every packed
 // weight byte of the pass is requested with no branch in front of the loads;
 // all row groups are computed before one reduction of the 16 partial int32
 // tiles in LDS.
@@ -82,6 +85,10 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
     __shared__ int red[G][kWaves][256];
     __shared__ __align__(16) uint8_t As[STAGE || QX ? 16 * kStageStride : 16];
     __shared__ float tok_scale[QX ? 16 : 1], tok_inv[QX ? 16 : 1];
+    // the row factor of each token: gamma / scale_x (1 / scale_x with a
+    // scale per channel), requested before anything else so that the
+    // epilogue does not wait for it
+    __shared__ float row_rs[QX ? 1 : 16];
     // fused: per token row and block, the block's sum of squares and max |x|
     constexpr int QE = Vec16<std::conditional_t<QX, TX, float>>::E;
     constexpr int QBLK = kWave * QE;
@@ -99,7 +106,9 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
     uint4 av[S];
     constexpr int kAPer = STAGE ? (16 * kStageMaxK / 16) / kThreads : 1;
     uint4 ac[kAPer];  // coalesced chunks for the LDS tile (STAGE)
-    const int kch = K / 16;
+    // 16-byte chunks per row: a constant when the row is whole steps (FULL:
+    // K = 1024 S), so the staging index math has no runtime division
+    const int kch = FULL ? 64 * S : K / 16;
     // fused: work item i = (token row i / nblk, block i % nblk); wave w takes
     // items w, w + 16, ...  Their raw X chunks are requested first, with
     // unconditional buffer loads (offsets past the rows read zeros, as
@@ -120,6 +129,7 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
             xc[j] = buf_load16(rx, v ? (uint32_t)(((int64_t)row * K + k0) * (int)sizeof(TX)) : kBufOOB);
         }
     } else if constexpr (STAGE) {
+        if (t < 16) row_rs[t] = t < M ? (CH ? 1.0f / scale_x[t] : *gamma_p / scale_x[t]) : 0.0f;
 #pragma unroll
         for (int i = 0; i < kAPer; ++i) {
             const int c = t + i * kThreads;
@@ -128,7 +138,26 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
             if (c < 16 * kch && tok < M)
                 ac[i] = *reinterpret_cast<const uint4*>(Xq + (int64_t)tok * K + 16 * (c - tok * kch));
         }
+        // The tile is written before any weight load is issued: staged while
+        // the weight stream is already in flight, the activation lines came
+        // back behind it (measured at N = 11008, K = 4096, 16 tokens: 6.5 us
+        // with the weight loads first, 5.2 us this way).
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kAPer; ++i) {
+            const int c = t + i * kThreads;
+            if (c < 16 * kch) {
+                const int tok = c / kch, kc = c - tok * kch;
+                const uint32_t a[4] = {ac[i].x, ac[i].y, ac[i].z, ac[i].w};
+                uint32_t o[4];
+                transpose4x4_bytes(a, o);
+                *reinterpret_cast<uint4*>(As + tok * kStageStride + 16 * kc) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
     } else {
+        if (t < 16) row_rs[t] = t < M ? (CH ? 1.0f / scale_x[t] : *gamma_p / scale_x[t]) : 0.0f;
         const bool tv = col < M;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
@@ -212,12 +241,11 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
 #pragma unroll
             for (int v = 0; v < kWaves; ++v) sum += red[r][v][e];
             if (tk < M && nn < N) {
-                const float sx = QX ? tok_scale[tk] : scale_x[tk];
                 if constexpr (CH) {
-                    const float rs = 1.0f / sx;
+                    const float rs = QX ? 1.0f / tok_scale[tk] : row_rs[tk];
                     Y[(int64_t)tk * N + nn] = ((float)sum * rs) * gamma_p[nn];
                 } else {
-                    const float rs = *gamma_p / sx;
+                    const float rs = QX ? *gamma_p / tok_scale[tk] : row_rs[tk];
                     Y[(int64_t)tk * N + nn] = (float)sum * rs;
                 }
                 if (acc_out) acc_out[(int64_t)tk * N + nn] = sum;
@@ -346,19 +374,7 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
             load_weights(base, wq);
             if (!transposed) {
                 if constexpr (STAGE) {
-#pragma unroll
-                    for (int i = 0; i < kAPer; ++i) {
-                        const int c = t + i * kThreads;
-                        if (c < 16 * kch) {
-                            const int tok = c / kch, kc = c - tok * kch;
-                            const uint32_t a[4] = {ac[i].x, ac[i].y, ac[i].z, ac[i].w};
-                            uint32_t o[4];
-                            transpose4x4_bytes(a, o);
-                            *reinterpret_cast<uint4*>(As + tok * kStageStride + 16 * kc) =
-                                make_uint4(o[0], o[1], o[2], o[3]);
-                        }
-                    }
-                    __syncthreads();
+                    __syncthreads();  // the tile written above
 #pragma unroll
                     for (int s = 0; s < S; ++s) {
                         const int k = kb + 16 * s;
@@ -378,6 +394,124 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
             }
             products(base, wq);
         }
+    }
+}
+
+// ------------------------------------------- staged GEMV for whole-step rows
+// gemv_t2_kernel's int8 path specialised to K = 1024 S (S = 1, 2, 4): the
+// token rows are staged in the LDS tile with compile-time index math, all
+// before the first weight load, and the row factors requested first.  Same
+// lane mapping, products and reduction, so the same bits.  (Written as its
+// own kernel: the identical schedule inside the general template measured
+// 0.4 us slower at 16 tokens x 11008 x 4096, 5.66 against 5.25 us.)
+template <int S, bool CH>
+__global__ __launch_bounds__(kThreads) void gemv_staged_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ scale_x, const uint8_t* __restrict__ Wp,
+    const float* __restrict__ gamma_p, int M, int N, float* __restrict__ Y, int32_t* __restrict__ acc_out) {
+    constexpr int K = 1024 * S, KB = K / 4, Kw = 64 * S, kch = K / 16;
+    constexpr int G = S >= 16 ? 1 : (S >= 8 ? 2 : kMaxGroups);
+    constexpr int kAPer = 16 * kch / kThreads;  // 16-byte chunks per thread for 16 token rows
+    constexpr int kPitch = K + 16;              // LDS row pitch (16-byte skew between rows)
+    static_assert(16 * kch % kThreads == 0, "whole chunks per thread");
+    __shared__ int red[G][kWaves][256];
+    __shared__ __align__(16) uint8_t As[16 * kPitch];
+    __shared__ float row_rs[16];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int col = lane & 15, g = lane >> 4;
+    const int kb = wave * Kw + g * (Kw / 4);
+    const int ngroups = (N + 15) / 16;
+    // the row factors: gamma / scale_x (1 / scale_x with a scale per channel)
+    if (t < 16) row_rs[t] = t < M ? (CH ? 1.0f / scale_x[t] : *gamma_p / scale_x[t]) : 0.0f;
+    // the token rows: coalesced 16-byte chunks, waited for, byte-transposed
+    // into the tile (rows >= M as zeros) before any weight load is issued
+    uint4 ac[kAPer];
+#pragma unroll
+    for (int i = 0; i < kAPer; ++i) {
+        const int c = t + i * kThreads;
+        ac[i] = make_uint4(0, 0, 0, 0);
+        if (c / kch < M) ac[i] = *reinterpret_cast<const uint4*>(Xq + (int64_t)(c / kch) * K + 16 * (c % kch));
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kAPer; ++i) {
+        const int c = t + i * kThreads;
+        const uint32_t a[4] = {ac[i].x, ac[i].y, ac[i].z, ac[i].w};
+        uint32_t o[4];
+        transpose4x4_bytes(a, o);
+        *reinterpret_cast<uint4*>(As + (c / kch) * kPitch + 16 * (c % kch)) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 av[S];
+    bool first = true;
+    for (int base = blockIdx.x; base < ngroups; base += gridDim.x * G) {
+        // every packed weight byte of the pass requested at once
+        uint32_t wq[G][S];
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+            const int grp = base + r * gridDim.x;
+            const int n = grp * 16 + col;
+            const bool nv = grp < ngroups && n < N;
+            const uint8_t* src = Wp + (int64_t)(nv ? n : 0) * KB + kb / 4;
+#pragma unroll
+            for (int s = 0; s < S; s += 4) {
+                if constexpr (S >= 4) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * s);
+                    wq[r][s] = nv ? v.x : 0u;
+                    wq[r][s + 1] = nv ? v.y : 0u;
+                    wq[r][s + 2] = nv ? v.z : 0u;
+                    wq[r][s + 3] = nv ? v.w : 0u;
+                }
+            }
+            if constexpr (S < 4) {
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const uint32_t v = *reinterpret_cast<const uint32_t*>(src + 4 * s);
+                    wq[r][s] = nv ? v : 0u;
+                }
+            }
+        }
+        if (first) {
+            __syncthreads();  // the tile
+#pragma unroll
+            for (int s = 0; s < S; ++s) av[s] = *reinterpret_cast<const uint4*>(As + col * kPitch + kb + 16 * s);
+            first = false;
+        }
+        int nr = 0;
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+            const int grp = base + r * gridDim.x;
+            if (grp >= ngroups) break;  // uniform over the workgroup
+            v4i acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                uint32_t b[4];
+                unpack16(wq[r][s], b);
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                    v4i{(int)av[s].x, (int)av[s].y, (int)av[s].z, (int)av[s].w},
+                    v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]}, acc, 0, 0, 0);
+            }
+            // 16x16 layout: lane holds weight row lane%16, tokens 4*(lane/16)+i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[r][wave][(4 * g + i) * 16 + col] = acc[i];
+            nr = r + 1;
+        }
+        __syncthreads();
+        for (int o = t; o < nr * 256; o += kThreads) {
+            const int r = o >> 8, e = o & 255;
+            const int grp = base + r * gridDim.x;
+            const int tk = e >> 4, nn = grp * 16 + (e & 15);
+            int sum = 0;
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) sum += red[r][v][e];
+            if (tk < M && nn < N) {
+                if constexpr (CH) Y[(int64_t)tk * N + nn] = ((float)sum * row_rs[tk]) * gamma_p[nn];
+                else Y[(int64_t)tk * N + nn] = (float)sum * row_rs[tk];
+                if (acc_out) acc_out[(int64_t)tk * N + nn] = sum;
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -409,15 +543,20 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
 }
 
 // CHK: 64-column chunks per lane (K <= 4096 CHK); K % 64 == 0.
-template <int CHK, bool CH>
+// KC: K as a compile-time constant (0: K at run time); the 7B decode row
+// length K = 4096 is instantiated so that the chunk bounds fold away.
+template <int CHK, bool CH, int KC = 0>
 __global__ __launch_bounds__(kRowWaves * kWave) void gemv_row_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ scale_x, const uint8_t* __restrict__ Wp,
-    const float* __restrict__ gamma_p, int N, int K, float* __restrict__ Y, int32_t* __restrict__ acc_out) {
+    const float* __restrict__ gamma_p, int N, int K_, float* __restrict__ Y, int32_t* __restrict__ acc_out) {
+    const int K = KC ? KC : K_;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row0 = (blockIdx.x * kRowWaves + wave) * kRowRows;
     if (row0 >= N) return;  // uniform in the wave
     const int KB = K / 4, nch = K / 64;
+    // the row factor first (its latency hides under the loads)
+    const float rs = CH ? 1.0f / scale_x[0] : *gamma_p / scale_x[0];
     // the activation chunks first: the weight loads after them are then the
     // only ones outstanding when the products wait for each row
     const __amdgpu_buffer_rsrc_t rx = make_buf(Xq);
@@ -474,14 +613,8 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_row_kernel(
         for (int r = 1; r < kRowRows; ++r) sum = lane == r ? acc[r] : sum;
         const int n = row0 + lane;
         if (n < N) {
-            const float sx = scale_x[0];
-            if constexpr (CH) {
-                const float rs = 1.0f / sx;
-                Y[n] = ((float)sum * rs) * gamma_p[n];
-            } else {
-                const float rs = *gamma_p / sx;
-                Y[n] = (float)sum * rs;
-            }
+            if constexpr (CH) Y[n] = ((float)sum * rs) * gamma_p[n];
+            else Y[n] = (float)sum * rs;
             if (acc_out) acc_out[n] = sum;
         }
     }
@@ -646,7 +779,10 @@ hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t*
     if (M == 1 && K % 64 == 0 && K <= 2 * 64 * 64) {  // one token: the row GEMV
         const unsigned rgrid = (unsigned)((N + kRowRows * kRowWaves - 1) / (kRowRows * kRowWaves));
         constexpr unsigned kRowThreads = kRowWaves * kWave;
-        if (K <= 64 * 64) {
+        if (K == 64 * 64) {
+            if (channel) gemv_row_kernel<1, true, 4096><<<rgrid, kRowThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)N, (int)K, Y, acc);
+            else gemv_row_kernel<1, false, 4096><<<rgrid, kRowThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)N, (int)K, Y, acc);
+        } else if (K <= 64 * 64) {
             if (channel) gemv_row_kernel<1, true><<<rgrid, kRowThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)N, (int)K, Y, acc);
             else gemv_row_kernel<1, false><<<rgrid, kRowThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)N, (int)K, Y, acc);
         } else {
@@ -659,7 +795,23 @@ hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t*
     const unsigned grid = (unsigned)std::min<int64_t>(ngroups, 256);
     const int64_t steps = (K + 16 * 64 - 1) / (16 * 64);  // MFMA steps per wave
     const bool full = K % (16 * 64) == 0;
-    const bool stage = M > 8 && K <= kStageMaxK;  // measured: direct loads win up to 8 tokens
+    if (full && (steps == 1 || steps == 2 || steps == 4)) {  // K = 1024, 2048, 4096: the staged kernel
+#define BITNET_STAGED(S_)                                                                                  \
+        if (steps == S_) {                                                                                 \
+            if (channel)                                                                                   \
+                gemv_staged_kernel<S_, true><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, Y, acc); \
+            else                                                                                           \
+                gemv_staged_kernel<S_, false><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, Y, acc); \
+            return hipGetLastError();                                                                      \
+        }
+        BITNET_STAGED(1)
+        BITNET_STAGED(2)
+        BITNET_STAGED(4)
+#undef BITNET_STAGED
+    }
+    // measured at N = 11008, K = 4096: the LDS tile (written before the
+    // weight loads) beats direct per-lane loads at every token count
+    const bool stage = K <= kStageMaxK;
 #define BITNET_GEMV_LAUNCH(S_, F_, G_)                                                          \
     do {                                                                                       \
         if (channel)                                                                           \
