@@ -304,8 +304,7 @@ int bitnet_pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* W_pa
 // that device current) and only that address reaches the kernels.
 namespace {
 
-constexpr size_t kNoAllocScratchBytes = (size_t)(((BITNET_NOALLOC_MAX_N * 4 + 255) / 256) * 256 + 256);
-static_assert(kNoAllocScratchBytes >= 0, "scratch size");
+constexpr size_t kNoAllocScratchBytes = bitnet::weight_quant_ws_size(BITNET_NOALLOC_MAX_N);
 
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 

@@ -232,6 +232,11 @@ hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, fl
                             int8_t* Xq, float* scale_x, hipStream_t s);
 hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
                                uint8_t* W_packed, float* gamma, void* ws, hipStream_t s);
+// weight_quant's workspace: the N row sums, the code threshold and the
+// ceil(N/4) four-row tree nodes, each 256-byte aligned
+constexpr size_t weight_quant_ws_size(int64_t N) {
+    return (size_t)(((N * 4 + 255) / 256) * 256 + 256 + (((N + 3) / 4 * 4 + 255) / 256) * 256);
+}
 size_t weight_quant_ws_bytes(int64_t N);
 // act_quant of X and weight_quant of W (same K) with one launch fewer;
 // outputs bit-identical to the two; ws as weight_quant's

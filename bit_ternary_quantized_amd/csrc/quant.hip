@@ -340,10 +340,12 @@ hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, fl
 }
 
 // ============================ weight_quant: absmean ternary codes, 2-bit packed
-// Pass 1: one wave per weight row -> tree sum of |w| over the row.
-// Pass 2: the tree over the row sums, gamma = max(S/(N*K), 1e-5), and the
-//         code threshold (below): one workgroup for large N, else every
-//         workgroup of pass 3 redundantly (one launch fewer).
+// Pass 1: one wave per weight row -> tree sum of |w| over the row; each
+//         workgroup (4 rows) also writes the tree node over its rows.
+// Pass 2: the tree over those nodes (the tree over the row sums), gamma =
+//         max(S/(N*K), 1e-5), and the code threshold (below): one workgroup
+//         for large matrices, else every workgroup of pass 3 redundantly
+//         (one launch fewer).
 // Pass 3: each thread turns kPackU groups of 4 weights into packed bytes.
 //
 // Code decision without a per-element division.  code != 0 exactly when
@@ -356,17 +358,24 @@ hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, fl
 
 constexpr int kWqWaves = 4;
 
+// quad_sums (when non-null): the workgroup also writes the tree node over
+// its kWqWaves = 4 rows, (r0 + r1) + (r2 + r3) with rows past N as +0: the
+// canonical tree over the row sums is the tree over these aligned 4-row
+// nodes (the row sums are >= +0, so the zero padding changes no bit), and
+// gamma is evaluated from N/4 values instead of N.
 template <typename T>
 __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int64_t N, int64_t K,
-                                                    float* __restrict__ row_sums, int bid) {
+                                                    float* __restrict__ row_sums, int bid,
+                                                    float* __restrict__ quad_sums) {
     constexpr int E = Vec16<T>::E;
     constexpr int BLK = kWave * E;
     constexpr int G = 8;  // loads in flight per lane
+    __shared__ float quad[kWqWaves];
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t row = (int64_t)bid * kWqWaves + (threadIdx.x >> 6);
-    if (row >= N) return;
-    const T* w = W + row * K;
-    const int64_t nblk = (K + BLK - 1) / BLK;
+    const int wv = threadIdx.x >> 6;
+    const int64_t row = (int64_t)bid * kWqWaves + wv;
+    const T* w = W + (row < N ? row : 0) * K;
+    const int64_t nblk = row < N ? (K + BLK - 1) / BLK : 0;  // uniform in the wave
     const bool vec_ok = (K % E) == 0;
     PairwiseStack st;
     for (int64_t b0 = 0; b0 < nblk; b0 += G) {
@@ -392,30 +401,37 @@ __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int
             }
         }
     }
-    if (lane == 0) row_sums[row] = st.total();
+    const float total = row < N ? st.total() : 0.0f;
+    if (lane == 0 && row < N) row_sums[row] = total;
+    if (quad_sums) {  // uniform: a kernel argument
+        if (lane == 0) quad[wv] = total;
+        __syncthreads();
+        if (threadIdx.x == 0) quad_sums[bid] = (quad[0] + quad[1]) + (quad[2] + quad[3]);
+    }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kWqWaves * kWave) void wq_row_abs_sum_kernel(
-    const T* __restrict__ W, int64_t N, int64_t K, float* __restrict__ row_sums) {
-    wq_row_abs_sum_body<T>(W, N, K, row_sums, blockIdx.x);
+    const T* __restrict__ W, int64_t N, int64_t K, float* __restrict__ row_sums, float* __restrict__ quad_sums) {
+    wq_row_abs_sum_body<T>(W, N, K, row_sums, blockIdx.x, quad_sums);
 }
 
-// Pass 2: the tree over the N row sums.  With P = N rounded up to a power of
-// two and L = max(256, P/W), wave w of W sums the aligned range [w*L,
-// (w+1)*L) as a tree and the W partial sums are combined as a tree (ranges
-// beyond N are +0).  Every W gives the same bits: it is the canonical tree
-// over the row sums padded with zeros, and extra zero padding adds exact
-// zeros.
+// Pass 2: the tree over the n = ceil(N/4) four-row nodes of pass 1 (the
+// tree over the N row sums).  With P = n rounded up to a power of two and L
+// = max(256, P/W), wave w of W sums the aligned range [w*L, (w+1)*L) as a
+// tree and the W partial sums are combined as a tree (ranges beyond n are
+// +0).  Every W gives the same bits: it is the canonical tree over the nodes
+// padded with zeros, and extra zero padding adds exact zeros.
 template <int W>
-__device__ __forceinline__ void gamma_and_thr(const float* __restrict__ row_sums, int64_t N,
+__device__ __forceinline__ void gamma_and_thr(const float* __restrict__ nodes, int64_t n, int64_t N,
                                               int64_t K, float* part, float& g, float& thr) {
+    const float* __restrict__ row_sums = nodes;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x >> 6;
     constexpr int E = 4;
     constexpr int BLK = kWave * E;
     int64_t P = 1;
-    while (P < N) P *= 2;
+    while (P < n) P *= 2;
     const int64_t L = P / W > BLK ? P / W : BLK;
     const int64_t lo = (int64_t)wv * L;
     const int64_t nblk = L / BLK;
@@ -427,7 +443,7 @@ __device__ __forceinline__ void gamma_and_thr(const float* __restrict__ row_sums
             const int64_t k0 = lo + (b0 + gi) * BLK + (int64_t)lane * E;
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                v[gi][e] = (b0 + gi < nblk && k0 + e < N) ? row_sums[k0 + e] : 0.0f;
+                v[gi][e] = (b0 + gi < nblk && k0 + e < n) ? row_sums[k0 + e] : 0.0f;
         }
 #pragma unroll
         for (int gi = 0; gi < 8; ++gi)
@@ -449,11 +465,11 @@ __device__ __forceinline__ void gamma_and_thr(const float* __restrict__ row_sums
 constexpr int kGammaWaves = 16;
 
 __global__ __launch_bounds__(kGammaWaves * kWave) void wq_gamma_kernel(
-    const float* __restrict__ row_sums, int64_t N, int64_t K, float* __restrict__ gamma,
+    const float* __restrict__ nodes, int64_t N, int64_t K, float* __restrict__ gamma,
     float* __restrict__ thr_out) {
     __shared__ float part[kGammaWaves];
     float g, thr;
-    gamma_and_thr<kGammaWaves>(row_sums, N, K, part, g, thr);
+    gamma_and_thr<kGammaWaves>(nodes, (N + 3) / 4, N, K, part, g, thr);
     if (threadIdx.x == 0) {
         gamma[0] = g;
         thr_out[0] = thr;
@@ -467,17 +483,20 @@ __device__ __forceinline__ uint32_t code_bits(float w, float thr) {
 
 constexpr int kPackU = 4;  // groups of 4 weights per thread (loads in flight)
 // When (rows x pack workgroups) is at most this, every pack workgroup
-// evaluates gamma and the threshold itself from the row sums (one launch
-// fewer, for small matrices); otherwise a single workgroup does and the pack
-// kernel reads the threshold.
+// evaluates gamma and the threshold itself from the four-row nodes (one
+// launch fewer, for small matrices; the weight loads are issued first, so
+// the evaluation hides under them); otherwise a single workgroup does and
+// the pack kernel reads the threshold.  Measured at 4096 x 4096 bf16: every
+// workgroup evaluating gamma from the 1024 nodes, 27.0 us for the call,
+// against 21.7 us with the single gamma workgroup.
 constexpr int64_t kFusedGammaMaxWork = (int64_t)1 << 22;
 
-// FUSED: the threshold is computed here from the row sums (block 0 also
-// writes gamma); otherwise it is read from thr_p.
+// FUSED: the threshold is computed here from the four-row nodes (block 0
+// also writes gamma); otherwise it is read from thr_p.
 template <typename T, bool FUSED>
 __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, int64_t total4,
                                                       const float* __restrict__ thr_p,
-                                                      const float* __restrict__ row_sums,
+                                                      const float* __restrict__ nodes,
                                                       int64_t N, int64_t K, float* __restrict__ gamma,
                                                       uint8_t* __restrict__ out) {
     const int64_t base = (int64_t)blockIdx.x * (256 * kPackU) + threadIdx.x;
@@ -502,7 +521,7 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, i
     if constexpr (FUSED) {
         __shared__ float part[4];
         float g;
-        gamma_and_thr<4>(row_sums, N, K, part, g, thr);
+        gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
         if (blockIdx.x == 0 && threadIdx.x == 0) gamma[0] = g;
     } else {
         thr = *thr_p;
@@ -584,9 +603,10 @@ hipError_t launch_weight_quant_rows(const void* W, bool w_bf16, int64_t N, int64
     float* thr = reinterpret_cast<float*>(static_cast<char*>(ws) + ((N * 4 + 255) / 256) * 256);
     const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
     if (w_bf16)
-        wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K, row_sums);
+        wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K, row_sums,
+                                                           nullptr);
     else
-        wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K, row_sums);
+        wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K, row_sums, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     wq_rows_gamma_kernel<<<(unsigned)((N + 255) / 256), 256, 0, s>>>(row_sums, N, K, gamma, thr);
@@ -602,10 +622,7 @@ hipError_t launch_weight_quant_rows(const void* W, bool w_bf16, int64_t N, int64
     return hipGetLastError();
 }
 
-size_t weight_quant_ws_bytes(int64_t N) {
-    // row sums, then the threshold float, 256-byte aligned
-    return (size_t)(((N * 4 + 255) / 256) * 256 + 256);
-}
+size_t weight_quant_ws_bytes(int64_t N) { return weight_quant_ws_size(N); }
 
 static unsigned stream_grid(int64_t work_items, int per_block) {
     int64_t g = (work_items + per_block - 1) / per_block;
@@ -759,11 +776,20 @@ hipError_t launch_weight_clamp(void* W, bool w_bf16, int64_t count, float lo, fl
 }
 
 
-// Passes 2 and 3 (gamma, threshold, packing) from the row sums in ws.
+// Workspace of weight_quant: row sums | threshold | four-row nodes
+// (weight_quant_ws_size in common.h).
+static float* ws_thr(void* ws, int64_t N) {
+    return reinterpret_cast<float*>(static_cast<char*>(ws) + ((N * 4 + 255) / 256) * 256);
+}
+static float* ws_nodes(void* ws, int64_t N) {
+    return reinterpret_cast<float*>(static_cast<char*>(ws) + ((N * 4 + 255) / 256) * 256 + 256);
+}
+
+// Passes 2 and 3 (gamma, threshold, packing) from the four-row nodes in ws.
 static hipError_t weight_quant_pack(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* W_packed,
                                     float* gamma, void* ws, hipStream_t s) {
-    float* row_sums = static_cast<float*>(ws);
-    float* thr = reinterpret_cast<float*>(static_cast<char*>(ws) + ((N * 4 + 255) / 256) * 256);
+    float* thr = ws_thr(ws, N);
+    const float* nodes = ws_nodes(ws, N);
     hipError_t e;
     const int64_t total4 = N * K / 4;
     const unsigned g3 = (unsigned)((total4 + 256 * kPackU - 1) / (256 * kPackU));
@@ -771,31 +797,32 @@ static hipError_t weight_quant_pack(const void* W, bool w_bf16, int64_t N, int64
     const float* Wf = static_cast<const float*>(W);
     if (N * (int64_t)g3 <= kFusedGammaMaxWork) {
         if (w_bf16)
-            wq_pack_kernel<uint16_t, true><<<g3, 256, 0, s>>>(Wb, total4, thr, row_sums, N, K, gamma, W_packed);
+            wq_pack_kernel<uint16_t, true><<<g3, 256, 0, s>>>(Wb, total4, thr, nodes, N, K, gamma, W_packed);
         else
-            wq_pack_kernel<float, true><<<g3, 256, 0, s>>>(Wf, total4, thr, row_sums, N, K, gamma, W_packed);
+            wq_pack_kernel<float, true><<<g3, 256, 0, s>>>(Wf, total4, thr, nodes, N, K, gamma, W_packed);
         return hipGetLastError();
     }
-    wq_gamma_kernel<<<1, kGammaWaves * kWave, 0, s>>>(row_sums, N, K, gamma, thr);
+    wq_gamma_kernel<<<1, kGammaWaves * kWave, 0, s>>>(nodes, N, K, gamma, thr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (w_bf16)
-        wq_pack_kernel<uint16_t, false><<<g3, 256, 0, s>>>(Wb, total4, thr, row_sums, N, K, gamma, W_packed);
+        wq_pack_kernel<uint16_t, false><<<g3, 256, 0, s>>>(Wb, total4, thr, nodes, N, K, gamma, W_packed);
     else
-        wq_pack_kernel<float, false><<<g3, 256, 0, s>>>(Wf, total4, thr, row_sums, N, K, gamma, W_packed);
+        wq_pack_kernel<float, false><<<g3, 256, 0, s>>>(Wf, total4, thr, nodes, N, K, gamma, W_packed);
     return hipGetLastError();
 }
 
 hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
                                uint8_t* W_packed, float* gamma, void* ws, hipStream_t s) {
     float* row_sums = static_cast<float*>(ws);
+    float* nodes = ws_nodes(ws, N);
     const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
     if (w_bf16)
         wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K,
-                                                           row_sums);
+                                                           row_sums, nodes);
     else
         wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K,
-                                                        row_sums);
+                                                        row_sums, nodes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s);
@@ -810,36 +837,38 @@ hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
 template <typename TX, int NB, typename TW>
 __global__ __launch_bounds__(kAqWaves * kWave) void quant_operands_kernel(
     const TX* __restrict__ X, int64_t M, int64_t K, float eps, int8_t* __restrict__ Q, float* __restrict__ S,
-    int act_blocks, const TW* __restrict__ W, int64_t N, float* __restrict__ row_sums) {
+    int act_blocks, const TW* __restrict__ W, int64_t N, float* __restrict__ row_sums,
+    float* __restrict__ nodes) {
     static_assert(kAqWaves == kWqWaves, "one workgroup shape for both bodies");
     const int b = blockIdx.x;  // uniform
     if (b < act_blocks) act_quant_rows_body<TX, NB>(X, M, K, eps, Q, S, b, act_blocks);
-    else wq_row_abs_sum_body<TW>(W, N, K, row_sums, b - act_blocks);
+    else wq_row_abs_sum_body<TW>(W, N, K, row_sums, b - act_blocks, nodes);
 }
 
 namespace {
 template <typename TX, typename TW>
 hipError_t quant_operands_pass1(const TX* X, int64_t M, int64_t K, float eps, int8_t* Q, float* S, const TW* W,
-                                int64_t N, float* row_sums, int nblk, hipStream_t s) {
+                                int64_t N, float* row_sums, float* nodes, int nblk, hipStream_t s) {
     const int64_t groups = (M + kAqWaves - 1) / kAqWaves;
     const int act_blocks = (int)std::min<int64_t>(groups, kAqMaxGroups);
     const int64_t wq_blocks = (N + kWqWaves - 1) / kWqWaves;
     const dim3 grid((unsigned)(act_blocks + wq_blocks)), block(kAqWaves * kWave);
     switch (nblk) {
-        case 1: quant_operands_kernel<TX, 1, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums); break;
-        case 2: quant_operands_kernel<TX, 2, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums); break;
-        case 4: quant_operands_kernel<TX, 4, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums); break;
-        case 8: quant_operands_kernel<TX, 8, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums); break;
-        case 16: quant_operands_kernel<TX, 16, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums); break;
+        case 1: quant_operands_kernel<TX, 1, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes); break;
+        case 2: quant_operands_kernel<TX, 2, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes); break;
+        case 4: quant_operands_kernel<TX, 4, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes); break;
+        case 8: quant_operands_kernel<TX, 8, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes); break;
+        case 16: quant_operands_kernel<TX, 16, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 template <typename TX>
 hipError_t quant_operands_w(const TX* X, int64_t M, int64_t K, float eps, int8_t* Q, float* S, const void* W,
-                            bool w_bf16, int64_t N, float* row_sums, int nblk, hipStream_t s) {
-    if (w_bf16) return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const uint16_t*>(W), N, row_sums, nblk, s);
-    return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const float*>(W), N, row_sums, nblk, s);
+                            bool w_bf16, int64_t N, float* row_sums, float* nodes, int nblk, hipStream_t s) {
+    if (w_bf16)
+        return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const uint16_t*>(W), N, row_sums, nodes, nblk, s);
+    return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const float*>(W), N, row_sums, nodes, nblk, s);
 }
 }  // namespace
 
@@ -856,10 +885,11 @@ hipError_t launch_quant_operands(const void* X, bool x_bf16, int64_t M, int64_t 
         return launch_weight_quant(W, w_bf16, N, K, W_packed, gamma, ws, s);
     }
     float* row_sums = static_cast<float*>(ws);
+    float* nodes = ws_nodes(ws, N);
     e = x_bf16 ? quant_operands_w(static_cast<const uint16_t*>(X), M, K, eps, Xq, scale_x, W, w_bf16, N, row_sums,
-                                  (int)nblk, s)
+                                  nodes, (int)nblk, s)
                : quant_operands_w(static_cast<const float*>(X), M, K, eps, Xq, scale_x, W, w_bf16, N, row_sums,
-                                  (int)nblk, s);
+                                  nodes, (int)nblk, s);
     if (e != hipSuccess) return e;
     return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s);
 }

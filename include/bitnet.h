@@ -107,11 +107,11 @@ int bitnet_weight_quant(const void *W, int w_dtype, int64_t N, int64_t K,
  * bitnet_weight_quant without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Same operation, same kernels and the same output
- * bits as bitnet_weight_quant; the row sums and the code threshold live in a
+ * bits as bitnet_weight_quant; its row sums, tree nodes and code threshold live in a
  * fixed device array inside the library instead of the caller's workspace.
  *   W, w_dtype, N, K, W_packed, gamma as bitnet_weight_quant
  *   N <= BITNET_NOALLOC_MAX_N (the scratch holds that many row sums,
- *   1 MiB + 256 bytes per device); larger N returns BITNET_E_SCRATCH.
+ *   1.25 MiB + 256 bytes per device); larger N returns BITNET_E_SCRATCH.
  * The call allocates nothing: no hipMalloc, hipFree or allocating library
  * routine.  Each GPU holds one copy of the scratch from the first call on it
  * until the process ends, and every call on that GPU shares it: calls that
