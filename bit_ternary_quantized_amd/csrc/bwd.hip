@@ -464,14 +464,16 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     // step i + 1 (loaded two steps ago, converted since) into LDS, loads of
     // step i + 3 into the freed staging set; compute phase = the MFMAs, with
     // the conversion of the other staging set (stored next step) between
-    // them.  Past the group's last step the loads read zeros, which add
-    // nothing.
+    // them.  The memory phase runs at raised wave priority: it sets the step
+    // time while the other group's MFMAs run.  Past the group's last step the
+    // loads read zeros, which add nothing.
     auto step = [&](int i, StageT& cur, StageT& nx) {
+        __builtin_amdgcn_s_setprio(1);
         read_operands(i);
         store_lds(i + 1, cur);
         load_global(i + 3, cur);
+        __builtin_amdgcn_s_setprio(0);
         phase_barrier(false);
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq)
 #pragma unroll
@@ -480,7 +482,6 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
                 for (int j = 0; j < JN; ++j)
                     acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kq][ii], b[kq][j], acc[ii][j], 0, 0, 0);
         convert(nx);
-        __builtin_amdgcn_s_setprio(0);
         phase_barrier(true);
     };
 
