@@ -258,6 +258,7 @@ def setup_layer(name):
                              device=dev),
         "W_packed_rows": torch.empty(N, K // 4, dtype=torch.uint8, device=dev),
         "gamma_rows": torch.empty(N, dtype=torch.float32, device=dev),
+        "grad_s": torch.empty(N, dtype=torch.float32, device=dev),
         "ws_wqr": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT_ROWS, 0, N, K), dtype=torch.uint8,
                               device=dev),
     }
@@ -308,6 +309,8 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
                                  "peak_ops": BF16_PEAK_TFLOPS}
         # the master-weight clamp: read and written in place
         c["weight_clamp"] = {"bytes": 2 * N * K * w_bytes, "bound": "hbm"}
+        # gradient of a learned per-channel scale: grad_W and the codes read once
+        c["channel_scale_grad"] = {"bytes": 4 * N * K + N * K // 4 + 4 * N, "bound": "hbm"}
     for v in c.values():
         if "ops" in v:
             ridge = v["peak_ops"] * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -329,6 +332,7 @@ KERNEL_OF = {
     "weight_quant_rows": "wq_row_abs_sum_kernel + wq_rows_gamma_kernel + wq_pack_rows_kernel",
     "linear_fwd_channel": "gemm_i8t2_kernel (per-channel epilogue) or gemv_t2_kernel",
     "bwd_grad_x_channel": "bwd_kernel<grad_x> (per-channel code scales)",
+    "channel_scale_grad": "channel_scale_grad_kernel",
 }
 # sources each call's kernels are built from: the HBM traffic recorded under
 # profiles/ is used only while these files are unchanged
@@ -347,6 +351,7 @@ SOURCES_OF = {
     "linear_fwd_channel": ["bit_ternary_quantized_amd/csrc/gemm_i8.hip", "bit_ternary_quantized_amd/csrc/gemv.hip"],
     "bwd_grad_x_channel": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
     "decode_gemv": ["bit_ternary_quantized_amd/csrc/gemv.hip"],
+    "channel_scale_grad": ["bit_ternary_quantized_amd/csrc/scale_grad.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -468,6 +473,9 @@ def bench_layer(args, name):
             gy, b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], w, -1.0, 1.0, want_grad_x=False,
             grad_W=b["grad_W"], workspace=b["ws_bwd"])
         variants["weight_clamp"] = lambda: bt.bitnet_weight_clamp(b["w_clamp"], -1.0, 1.0)
+        # the gradient of a learned per-channel scale from the step's grad_W
+        variants["channel_scale_grad"] = lambda: bt.bitnet_channel_scale_grad(b["grad_W"], b["W_packed_rows"],
+                                                                               grad_s=b["grad_s"])
 
     # --two-streams: the two quantizers (X and W), which are independent, run
     # on two streams (default priority) forked and joined with events, so the
