@@ -140,6 +140,24 @@ __device__ __forceinline__ float wave_tree_sum(float v) {
     return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
 }
 
+// The int8 codes of four quantizer products y = fl(fl(x * inv) * scale),
+// packed into one dword (element 0 in the low byte): clamp to [-128, 127],
+// then round half to even by adding 1.5 * 2^23 (in [2^23, 2^24) the unit in
+// the last place is 1, so the addition itself rounds to the nearest integer,
+// ties to even, and leaves that integer in the low mantissa bits as two's
+// complement); two byte permutes and an or gather the four low bytes.  For
+// every non-NaN y this equals clamp(rint(y), -128, 127): clamping to integer
+// bounds commutes with rounding to an integer.
+__device__ __forceinline__ uint32_t q8x4(float y0, float y1, float y2, float y3) {
+    constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+    const uint32_t a = __float_as_uint(fminf(fmaxf(y0, -128.0f), 127.0f) + kRound);
+    const uint32_t b = __float_as_uint(fminf(fmaxf(y1, -128.0f), 127.0f) + kRound);
+    const uint32_t c = __float_as_uint(fminf(fmaxf(y2, -128.0f), 127.0f) + kRound);
+    const uint32_t d = __float_as_uint(fminf(fmaxf(y3, -128.0f), 127.0f) + kRound);
+    // v_perm_b32(S0, S1, sel): selector byte 0-3 picks a byte of S1, 4-7 of S0, 0x0c gives 0
+    return __builtin_amdgcn_perm(b, a, 0x0c0c0400u) | __builtin_amdgcn_perm(d, c, 0x04000c0cu);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp_read<kDppXor1>(v));
     v = fmaxf(v, dpp_read<kDppXor2>(v));

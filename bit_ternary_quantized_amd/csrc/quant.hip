@@ -262,16 +262,9 @@ __device__ __forceinline__ void act_quant_rows_body(const T* __restrict__ X, int
             widen(c[b], v);
             uint32_t pk[E / 4];
 #pragma unroll
-            for (int i = 0; i < E / 4; ++i) {
-                uint32_t w = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float r = rintf((v[4 * i + e] * inv) * scale);
-                    r = fminf(fmaxf(r, -128.0f), 127.0f);
-                    w |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * e);
-                }
-                pk[i] = w;
-            }
+            for (int i = 0; i < E / 4; ++i)
+                pk[i] = q8x4((v[4 * i] * inv) * scale, (v[4 * i + 1] * inv) * scale, (v[4 * i + 2] * inv) * scale,
+                             (v[4 * i + 3] * inv) * scale);
             const int64_t k0 = b * BLK + lane * E;
             if constexpr (E == 8) *reinterpret_cast<uint2*>(q + k0) = make_uint2(pk[0], pk[1]);
             else *reinterpret_cast<uint32_t*>(q + k0) = pk[0];
