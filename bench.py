@@ -320,7 +320,7 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
 
 KERNEL_OF = {
     "act_quant": "act_quant_rows_kernel (rows of whole 16-byte blocks), else act_quant_kernel",
-    "weight_quant": "wq_row_abs_sum_kernel + wq_gamma_kernel + wq_pack_kernel",
+    "weight_quant": "wq_row_abs_sum_kernel + wq_pack_kernel (gamma in the pack launch)",
     "linear_fwd": "gemm_i8t2_kernel",
     "bwd_grad_x": "bwd_kernel<grad_x>",
     "bwd_grad_W": "bwd_kernel<grad_W> (+ split_reduce_kernel when split)",
@@ -328,7 +328,7 @@ KERNEL_OF = {
     "bwd_grad_W_gated": "bwd_kernel<grad_W> with the range gate (+ split_reduce_kernel when split)",
     "weight_clamp": "weight_clamp_kernel",
     "code_counts": "code_counts_kernel + code_counts_final_kernel",
-    "quant_operands": "quant_operands_kernel + wq_pack_kernel (+ wq_gamma_kernel)",
+    "quant_operands": "quant_operands_kernel + wq_pack_kernel",
     "weight_quant_rows": "wq_row_abs_sum_kernel + wq_rows_gamma_kernel + wq_pack_rows_kernel",
     "linear_fwd_channel": "gemm_i8t2_kernel (per-channel epilogue) or gemv_t2_kernel",
     "bwd_grad_x_channel": "bwd_kernel<grad_x> (per-channel code scales)",

@@ -336,9 +336,10 @@ hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, fl
 // Pass 1: one wave per weight row -> tree sum of |w| over the row; each
 //         workgroup (4 rows) also writes the tree node over its rows.
 // Pass 2: the tree over those nodes (the tree over the row sums), gamma =
-//         max(S/(N*K), 1e-5), and the code threshold (below): one workgroup
-//         for large matrices, else every workgroup of pass 3 redundantly
-//         (one launch fewer).
+//         max(S/(N*K), 1e-5), and the code threshold (below), evaluated in
+//         the pack launch: by its workgroup 0, which publishes the threshold
+//         to the others, for large matrices; by every workgroup for small
+//         ones.
 // Pass 3: each thread turns kPackU groups of 4 weights into packed bytes.
 //
 // Code decision without a per-element division.  code != 0 exactly when
@@ -356,10 +357,15 @@ constexpr int kWqWaves = 4;
 // canonical tree over the row sums is the tree over these aligned 4-row
 // nodes (the row sums are >= +0, so the zero padding changes no bit), and
 // gamma is evaluated from N/4 values instead of N.
+// gate (when non-null): the pack launch's threshold word, cleared here by
+// workgroup 0 (this pass always runs first in the call, so the pack launch
+// never sees a ready mark left by an earlier call).
 template <typename T>
 __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int64_t N, int64_t K,
                                                     float* __restrict__ row_sums, int bid,
-                                                    float* __restrict__ quad_sums) {
+                                                    float* __restrict__ quad_sums,
+                                                    uint64_t* __restrict__ gate) {
+    if (gate && bid == 0 && threadIdx.x == 0) *gate = 0;
     constexpr int E = Vec16<T>::E;
     constexpr int BLK = kWave * E;
     constexpr int G = 8;  // loads in flight per lane
@@ -405,8 +411,9 @@ __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int
 
 template <typename T>
 __global__ __launch_bounds__(kWqWaves * kWave) void wq_row_abs_sum_kernel(
-    const T* __restrict__ W, int64_t N, int64_t K, float* __restrict__ row_sums, float* __restrict__ quad_sums) {
-    wq_row_abs_sum_body<T>(W, N, K, row_sums, blockIdx.x, quad_sums);
+    const T* __restrict__ W, int64_t N, int64_t K, float* __restrict__ row_sums, float* __restrict__ quad_sums,
+    uint64_t* __restrict__ gate) {
+    wq_row_abs_sum_body<T>(W, N, K, row_sums, blockIdx.x, quad_sums, gate);
 }
 
 // Pass 2: the tree over the n = ceil(N/4) four-row nodes of pass 1 (the
@@ -455,19 +462,6 @@ __device__ __forceinline__ void gamma_and_thr(const float* __restrict__ nodes, i
     if ((double)thr <= t) thr = __uint_as_float(__float_as_uint(thr) + 1u);
 }
 
-constexpr int kGammaWaves = 16;
-
-__global__ __launch_bounds__(kGammaWaves * kWave) void wq_gamma_kernel(
-    const float* __restrict__ nodes, int64_t N, int64_t K, float* __restrict__ gamma,
-    float* __restrict__ thr_out) {
-    __shared__ float part[kGammaWaves];
-    float g, thr;
-    gamma_and_thr<kGammaWaves>(nodes, (N + 3) / 4, N, K, part, g, thr);
-    if (threadIdx.x == 0) {
-        gamma[0] = g;
-        thr_out[0] = thr;
-    }
-}
 
 __device__ __forceinline__ uint32_t code_bits(float w, float thr) {
     // 01 = +1, 10 = -1, 00 = 0
@@ -475,57 +469,114 @@ __device__ __forceinline__ uint32_t code_bits(float w, float thr) {
 }
 
 constexpr int kPackU = 4;  // groups of 4 weights per thread (loads in flight)
+// with the published threshold: twice as many per thread, so that at 4096 x
+// 4096 bf16 the whole matrix is requested by workgroups resident at once and
+// its loads stream while workgroup 0 evaluates gamma
+constexpr int kPackUPub = 8;
 // When (rows x pack workgroups) is at most this, every pack workgroup
-// evaluates gamma and the threshold itself from the four-row nodes (one
-// launch fewer, for small matrices; the weight loads are issued first, so
-// the evaluation hides under them); otherwise a single workgroup does and
-// the pack kernel reads the threshold.  Measured at 4096 x 4096 bf16: every
-// workgroup evaluating gamma from the 1024 nodes, 27.0 us for the call,
-// against 21.7 us with the single gamma workgroup.
+// evaluates gamma and the threshold itself from the four-row nodes (for
+// small matrices; the weight loads are issued first, so the evaluation hides
+// under them).  Above it workgroup 0 evaluates them once and publishes the
+// threshold to the others (below).  Measured at 4096 x 4096 bf16, the call:
+// gamma in a launch of its own 21.8 us; published 20.0 us; every workgroup
+// evaluating it 23.0 us.
 constexpr int64_t kFusedGammaMaxWork = (int64_t)1 << 22;
+// reads of the published threshold before a workgroup evaluates it itself
+constexpr int kGatePolls = 32;
 
-// FUSED: the threshold is computed here from the four-row nodes (block 0
-// also writes gamma); otherwise it is read from thr_p.
-template <typename T, bool FUSED>
+// FUSED: every workgroup computes the threshold from the four-row nodes
+// (block 0 also writes gamma).  Otherwise workgroup 0 computes gamma and the
+// threshold and publishes the threshold in `gate`, one 64-bit word holding
+// the threshold bits and a ready mark, written with a single store (cleared
+// by pass 1 of the same call); every other workgroup reads that word after
+// issuing its weight loads, and one that still finds no ready mark after
+// kGatePolls reads (a short sleep apart) computes the threshold itself from
+// the nodes, which gives the same bits.  No workgroup waits on another's
+// progress beyond that bounded number of reads.
+template <typename T, bool FUSED, int U>
 __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, int64_t total4,
-                                                      const float* __restrict__ thr_p,
+                                                      uint64_t* __restrict__ gate,
                                                       const float* __restrict__ nodes,
                                                       int64_t N, int64_t K, float* __restrict__ gamma,
                                                       uint8_t* __restrict__ out) {
-    const int64_t base = (int64_t)blockIdx.x * (256 * kPackU) + threadIdx.x;
-    float v[kPackU][4];
+    // the workgroup's groups of 4 weights through one buffer descriptor: every
+    // load is unconditional (past total4 an out-of-range offset reads zeros),
+    // so all U loads are in flight together and nothing waits for them before
+    // the threshold is known
+    const int64_t g0 = (int64_t)blockIdx.x * (256 * U);
+    const int64_t base = g0 + threadIdx.x;
+    const __amdgpu_buffer_rsrc_t rw = make_buf(W + g0 * 4);
+    constexpr uint32_t kGroupBytes = 4 * sizeof(T);
+    uint4 raw[U];
 #pragma unroll
-    for (int u = 0; u < kPackU; ++u) {
-        const int64_t i = base + u * 256;
-        if (i < total4) {
-            if constexpr (sizeof(T) == 4) {
-                const float4 q = reinterpret_cast<const float4*>(W)[i];
-                v[u][0] = q.x; v[u][1] = q.y; v[u][2] = q.z; v[u][3] = q.w;
-            } else {
-                const uint2 q = reinterpret_cast<const uint2*>(W)[i];
-                v[u][0] = __uint_as_float(q.x << 16);
-                v[u][1] = __uint_as_float(q.x & 0xffff0000u);
-                v[u][2] = __uint_as_float(q.y << 16);
-                v[u][3] = __uint_as_float(q.y & 0xffff0000u);
-            }
+    for (int u = 0; u < U; ++u) {
+        const uint32_t off = base + u * 256 < total4 ? (threadIdx.x + u * 256) * kGroupBytes : kBufOOB;
+        if constexpr (sizeof(T) == 4) {
+            raw[u] = buf_load16(rw, off);
+        } else {
+            const uint2 q = buf_load8(rw, off);
+            raw[u] = make_uint4(q.x, q.y, 0u, 0u);
         }
     }
     float thr;
+    __shared__ float part[4];
     if constexpr (FUSED) {
-        __shared__ float part[4];
         float g;
         gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
         if (blockIdx.x == 0 && threadIdx.x == 0) gamma[0] = g;
+    } else if (blockIdx.x == 0) {  // uniform
+        float g;
+        gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
+        if (threadIdx.x == 0) {
+            gamma[0] = g;
+            __hip_atomic_store(gate, ((uint64_t)1 << 32) | __float_as_uint(thr), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     } else {
-        thr = *thr_p;
+        __shared__ float pub_thr;
+        __shared__ int pub_ok;
+        if (threadIdx.x == 0) {
+            int ok = 0;
+            float t = 0.0f;
+            for (int i = 0; i < kGatePolls; ++i) {
+                const uint64_t word = __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((uint32_t)(word >> 32) == 1u) {
+                    ok = 1;
+                    t = __uint_as_float((uint32_t)word);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            pub_ok = ok;
+            pub_thr = t;
+        }
+        __syncthreads();
+        if (pub_ok) {  // uniform: one LDS value for the workgroup
+            thr = pub_thr;
+        } else {
+            float g;
+            gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
+        }
     }
 #pragma unroll
-    for (int u = 0; u < kPackU; ++u) {
+    for (int u = 0; u < U; ++u) {
         const int64_t i = base + u * 256;
+        float v[4];
+        if constexpr (sizeof(T) == 4) {
+            v[0] = __uint_as_float(raw[u].x);
+            v[1] = __uint_as_float(raw[u].y);
+            v[2] = __uint_as_float(raw[u].z);
+            v[3] = __uint_as_float(raw[u].w);
+        } else {
+            v[0] = __uint_as_float(raw[u].x << 16);
+            v[1] = __uint_as_float(raw[u].x & 0xffff0000u);
+            v[2] = __uint_as_float(raw[u].y << 16);
+            v[3] = __uint_as_float(raw[u].y & 0xffff0000u);
+        }
         if (i < total4) {
             uint32_t byte = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) byte |= code_bits(v[u][j], thr) << (2 * j);
+            for (int j = 0; j < 4; ++j) byte |= code_bits(v[j], thr) << (2 * j);
             out[i] = (uint8_t)byte;
         }
     }
@@ -597,9 +648,10 @@ hipError_t launch_weight_quant_rows(const void* W, bool w_bf16, int64_t N, int64
     const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
     if (w_bf16)
         wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K, row_sums,
-                                                           nullptr);
+                                                           nullptr, nullptr);
     else
-        wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K, row_sums, nullptr);
+        wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K, row_sums, nullptr,
+                                                        nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     wq_rows_gamma_kernel<<<(unsigned)((N + 255) / 256), 256, 0, s>>>(row_sums, N, K, gamma, thr);
@@ -771,37 +823,37 @@ hipError_t launch_weight_clamp(void* W, bool w_bf16, int64_t count, float lo, fl
 
 // Workspace of weight_quant: row sums | threshold | four-row nodes
 // (weight_quant_ws_size in common.h).
-static float* ws_thr(void* ws, int64_t N) {
-    return reinterpret_cast<float*>(static_cast<char*>(ws) + ((N * 4 + 255) / 256) * 256);
+// the 64-bit threshold word of the pack launch, in the 256-byte slot after the row sums
+static uint64_t* ws_gate(void* ws, int64_t N) {
+    return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + ((N * 4 + 255) / 256) * 256);
 }
 static float* ws_nodes(void* ws, int64_t N) {
     return reinterpret_cast<float*>(static_cast<char*>(ws) + ((N * 4 + 255) / 256) * 256 + 256);
 }
 
-// Passes 2 and 3 (gamma, threshold, packing) from the four-row nodes in ws.
+// Passes 2 and 3 (gamma, threshold, packing) from the four-row nodes in ws,
+// in one launch.
 static hipError_t weight_quant_pack(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* W_packed,
                                     float* gamma, void* ws, hipStream_t s) {
-    float* thr = ws_thr(ws, N);
+    uint64_t* gate = ws_gate(ws, N);
     const float* nodes = ws_nodes(ws, N);
-    hipError_t e;
     const int64_t total4 = N * K / 4;
     const unsigned g3 = (unsigned)((total4 + 256 * kPackU - 1) / (256 * kPackU));
+    const unsigned g3p = (unsigned)((total4 + 256 * kPackUPub - 1) / (256 * kPackUPub));
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
     const float* Wf = static_cast<const float*>(W);
-    if (N * (int64_t)g3 <= kFusedGammaMaxWork) {
-        if (w_bf16)
-            wq_pack_kernel<uint16_t, true><<<g3, 256, 0, s>>>(Wb, total4, thr, nodes, N, K, gamma, W_packed);
-        else
-            wq_pack_kernel<float, true><<<g3, 256, 0, s>>>(Wf, total4, thr, nodes, N, K, gamma, W_packed);
-        return hipGetLastError();
-    }
-    wq_gamma_kernel<<<1, kGammaWaves * kWave, 0, s>>>(nodes, N, K, gamma, thr);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (w_bf16)
-        wq_pack_kernel<uint16_t, false><<<g3, 256, 0, s>>>(Wb, total4, thr, nodes, N, K, gamma, W_packed);
-    else
-        wq_pack_kernel<float, false><<<g3, 256, 0, s>>>(Wf, total4, thr, nodes, N, K, gamma, W_packed);
+    const bool fused = N * (int64_t)g3 <= kFusedGammaMaxWork;
+#define BITNET_PACK(T_, W_)                                                                                  \
+    do {                                                                                                     \
+        if (fused)                                                                                           \
+            wq_pack_kernel<T_, true, kPackU><<<g3, 256, 0, s>>>(W_, total4, gate, nodes, N, K, gamma, W_packed); \
+        else                                                                                                 \
+            wq_pack_kernel<T_, false, kPackUPub><<<g3p, 256, 0, s>>>(W_, total4, gate, nodes, N, K, gamma,  \
+                                                                       W_packed);                            \
+    } while (0)
+    if (w_bf16) BITNET_PACK(uint16_t, Wb);
+    else BITNET_PACK(float, Wf);
+#undef BITNET_PACK
     return hipGetLastError();
 }
 
@@ -809,13 +861,14 @@ hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
                                uint8_t* W_packed, float* gamma, void* ws, hipStream_t s) {
     float* row_sums = static_cast<float*>(ws);
     float* nodes = ws_nodes(ws, N);
+    uint64_t* gate = ws_gate(ws, N);
     const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
     if (w_bf16)
         wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K,
-                                                           row_sums, nodes);
+                                                           row_sums, nodes, gate);
     else
         wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K,
-                                                        row_sums, nodes);
+                                                        row_sums, nodes, gate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s);
@@ -824,44 +877,48 @@ hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
 // ============================================= both quantizers, one launch fewer
 // Launch 1 runs act_quant's row-walking kernel on workgroups [0, A) and the
 // weight row sums on [A, A + ceil(N/4)): two independent streams of HBM
-// reads in one grid, with no launch boundary between them.  Launch 2 (and
-// the gamma kernel for large N) is weight_quant's.  Same bodies, same
+// reads in one grid, with no launch boundary between them.  Launch 2 is
+// weight_quant's pack (with gamma).  Same bodies, same
 // arithmetic: the outputs are bit-identical to the two separate calls.
 template <typename TX, int NB, typename TW>
 __global__ __launch_bounds__(kAqWaves * kWave) void quant_operands_kernel(
     const TX* __restrict__ X, int64_t M, int64_t K, float eps, int8_t* __restrict__ Q, float* __restrict__ S,
     int act_blocks, const TW* __restrict__ W, int64_t N, float* __restrict__ row_sums,
-    float* __restrict__ nodes) {
+    float* __restrict__ nodes, uint64_t* __restrict__ gate) {
     static_assert(kAqWaves == kWqWaves, "one workgroup shape for both bodies");
     const int b = blockIdx.x;  // uniform
     if (b < act_blocks) act_quant_rows_body<TX, NB>(X, M, K, eps, Q, S, b, act_blocks);
-    else wq_row_abs_sum_body<TW>(W, N, K, row_sums, b - act_blocks, nodes);
+    else wq_row_abs_sum_body<TW>(W, N, K, row_sums, b - act_blocks, nodes, gate);
 }
 
 namespace {
 template <typename TX, typename TW>
 hipError_t quant_operands_pass1(const TX* X, int64_t M, int64_t K, float eps, int8_t* Q, float* S, const TW* W,
-                                int64_t N, float* row_sums, float* nodes, int nblk, hipStream_t s) {
+                                int64_t N, float* row_sums, float* nodes, uint64_t* gate, int nblk,
+                                hipStream_t s) {
     const int64_t groups = (M + kAqWaves - 1) / kAqWaves;
     const int act_blocks = (int)std::min<int64_t>(groups, kAqMaxGroups);
     const int64_t wq_blocks = (N + kWqWaves - 1) / kWqWaves;
     const dim3 grid((unsigned)(act_blocks + wq_blocks)), block(kAqWaves * kWave);
     switch (nblk) {
-        case 1: quant_operands_kernel<TX, 1, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes); break;
-        case 2: quant_operands_kernel<TX, 2, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes); break;
-        case 4: quant_operands_kernel<TX, 4, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes); break;
-        case 8: quant_operands_kernel<TX, 8, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes); break;
-        case 16: quant_operands_kernel<TX, 16, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes); break;
+        case 1: quant_operands_kernel<TX, 1, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes, gate); break;
+        case 2: quant_operands_kernel<TX, 2, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes, gate); break;
+        case 4: quant_operands_kernel<TX, 4, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes, gate); break;
+        case 8: quant_operands_kernel<TX, 8, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes, gate); break;
+        case 16: quant_operands_kernel<TX, 16, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes, gate); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 template <typename TX>
 hipError_t quant_operands_w(const TX* X, int64_t M, int64_t K, float eps, int8_t* Q, float* S, const void* W,
-                            bool w_bf16, int64_t N, float* row_sums, float* nodes, int nblk, hipStream_t s) {
+                            bool w_bf16, int64_t N, float* row_sums, float* nodes, uint64_t* gate, int nblk,
+                            hipStream_t s) {
     if (w_bf16)
-        return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const uint16_t*>(W), N, row_sums, nodes, nblk, s);
-    return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const float*>(W), N, row_sums, nodes, nblk, s);
+        return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const uint16_t*>(W), N, row_sums, nodes, gate,
+                                    nblk, s);
+    return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const float*>(W), N, row_sums, nodes, gate, nblk,
+                                s);
 }
 }  // namespace
 
@@ -879,10 +936,11 @@ hipError_t launch_quant_operands(const void* X, bool x_bf16, int64_t M, int64_t 
     }
     float* row_sums = static_cast<float*>(ws);
     float* nodes = ws_nodes(ws, N);
+    uint64_t* gate = ws_gate(ws, N);
     e = x_bf16 ? quant_operands_w(static_cast<const uint16_t*>(X), M, K, eps, Xq, scale_x, W, w_bf16, N, row_sums,
-                                  nodes, (int)nblk, s)
+                                  nodes, gate, (int)nblk, s)
                : quant_operands_w(static_cast<const float*>(X), M, K, eps, Xq, scale_x, W, w_bf16, N, row_sums,
-                                  nodes, (int)nblk, s);
+                                  nodes, gate, (int)nblk, s);
     if (e != hipSuccess) return e;
     return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s);
 }
