@@ -329,7 +329,7 @@ KERNEL_OF = {
     "weight_clamp": "weight_clamp_kernel",
     "code_counts": "code_counts_kernel + code_counts_final_kernel",
     "quant_operands": "quant_operands_kernel + wq_pack_kernel",
-    "weight_quant_rows": "wq_row_abs_sum_kernel + wq_rows_gamma_kernel + wq_pack_rows_kernel",
+    "weight_quant_rows": "wq_row_abs_sum_kernel (with the row gammas) + wq_pack_rows_kernel",
     "linear_fwd_channel": "gemm_i8t2_kernel (per-channel epilogue) or gemv_t2_kernel",
     "bwd_grad_x_channel": "bwd_kernel<grad_x> (per-channel code scales)",
     "channel_scale_grad": "channel_scale_grad_kernel",

@@ -360,11 +360,17 @@ constexpr int kWqWaves = 4;
 // gate (when non-null): the pack launch's threshold word, cleared here by
 // workgroup 0 (this pass always runs first in the call, so the pack launch
 // never sees a ready mark left by an earlier call).
+__device__ __forceinline__ float code_threshold(float g);
+
+// row_gamma / row_thr (when non-null): the per-output-channel variant's
+// gamma_n = max(S_n / K, 1e-5) and its code threshold, written with the row sum.
 template <typename T>
 __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int64_t N, int64_t K,
                                                     float* __restrict__ row_sums, int bid,
                                                     float* __restrict__ quad_sums,
-                                                    uint64_t* __restrict__ gate) {
+                                                    uint64_t* __restrict__ gate,
+                                                    float* __restrict__ row_gamma = nullptr,
+                                                    float* __restrict__ row_thr = nullptr) {
     if (gate && bid == 0 && threadIdx.x == 0) *gate = 0;
     constexpr int E = Vec16<T>::E;
     constexpr int BLK = kWave * E;
@@ -401,7 +407,14 @@ __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int
         }
     }
     const float total = row < N ? st.total() : 0.0f;
-    if (lane == 0 && row < N) row_sums[row] = total;
+    if (lane == 0 && row < N) {
+        row_sums[row] = total;
+        if (row_gamma) {  // uniform: a kernel argument
+            const float g = fmaxf(total / (float)K, 1e-5f);
+            row_gamma[row] = g;
+            row_thr[row] = code_threshold(g);
+        }
+    }
     if (quad_sums) {  // uniform: a kernel argument
         if (lane == 0) quad[wv] = total;
         __syncthreads();
@@ -412,8 +425,8 @@ __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int
 template <typename T>
 __global__ __launch_bounds__(kWqWaves * kWave) void wq_row_abs_sum_kernel(
     const T* __restrict__ W, int64_t N, int64_t K, float* __restrict__ row_sums, float* __restrict__ quad_sums,
-    uint64_t* __restrict__ gate) {
-    wq_row_abs_sum_body<T>(W, N, K, row_sums, blockIdx.x, quad_sums, gate);
+    uint64_t* __restrict__ gate, float* __restrict__ row_gamma, float* __restrict__ row_thr) {
+    wq_row_abs_sum_body<T>(W, N, K, row_sums, blockIdx.x, quad_sums, gate, row_gamma, row_thr);
 }
 
 // Pass 2: the tree over the n = ceil(N/4) four-row nodes of pass 1 (the
@@ -596,36 +609,43 @@ __device__ __forceinline__ float code_threshold(float g) {
     return thr;
 }
 
-__global__ __launch_bounds__(256) void wq_rows_gamma_kernel(const float* __restrict__ row_sums, int64_t N,
-                                                            int64_t K, float* __restrict__ gamma,
-                                                            float* __restrict__ thr) {
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (n >= N) return;
-    const float mean = row_sums[n] / (float)K;
-    const float g = fmaxf(mean, 1e-5f);
-    gamma[n] = g;
-    thr[n] = code_threshold(g);
-}
-
+// The weights of each thread come in with unconditional buffer loads (past
+// the end an out-of-range offset reads zeros), all in flight together, then
+// the thresholds of their rows (L2-resident after the first reads).
 template <typename T>
 __global__ __launch_bounds__(256) void wq_pack_rows_kernel(const T* __restrict__ W, int64_t total4, int64_t KB,
                                                            const float* __restrict__ thr,
                                                            uint8_t* __restrict__ out) {
-    const int64_t base = (int64_t)blockIdx.x * (256 * kPackU) + threadIdx.x;
+    const int64_t g0 = (int64_t)blockIdx.x * (256 * kPackU);
+    const int64_t base = g0 + threadIdx.x;
+    const __amdgpu_buffer_rsrc_t rw = make_buf(W + g0 * 4);
+    constexpr uint32_t kGroupBytes = 4 * sizeof(T);
+    uint4 raw[kPackU];
+#pragma unroll
+    for (int u = 0; u < kPackU; ++u) {
+        const uint32_t off = base + u * 256 < total4 ? (threadIdx.x + u * 256) * kGroupBytes : kBufOOB;
+        if constexpr (sizeof(T) == 4) {
+            raw[u] = buf_load16(rw, off);
+        } else {
+            const uint2 q = buf_load8(rw, off);
+            raw[u] = make_uint4(q.x, q.y, 0u, 0u);
+        }
+    }
 #pragma unroll
     for (int u = 0; u < kPackU; ++u) {
         const int64_t i = base + u * 256;  // packed byte: 4 weights of row i / KB
         if (i < total4) {
             float v[4];
             if constexpr (sizeof(T) == 4) {
-                const float4 q = reinterpret_cast<const float4*>(W)[i];
-                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+                v[0] = __uint_as_float(raw[u].x);
+                v[1] = __uint_as_float(raw[u].y);
+                v[2] = __uint_as_float(raw[u].z);
+                v[3] = __uint_as_float(raw[u].w);
             } else {
-                const uint2 q = reinterpret_cast<const uint2*>(W)[i];
-                v[0] = __uint_as_float(q.x << 16);
-                v[1] = __uint_as_float(q.x & 0xffff0000u);
-                v[2] = __uint_as_float(q.y << 16);
-                v[3] = __uint_as_float(q.y & 0xffff0000u);
+                v[0] = __uint_as_float(raw[u].x << 16);
+                v[1] = __uint_as_float(raw[u].x & 0xffff0000u);
+                v[2] = __uint_as_float(raw[u].y << 16);
+                v[3] = __uint_as_float(raw[u].y & 0xffff0000u);
             }
             const float t = thr[i / KB];
             uint32_t byte = 0;
@@ -648,14 +668,11 @@ hipError_t launch_weight_quant_rows(const void* W, bool w_bf16, int64_t N, int64
     const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
     if (w_bf16)
         wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K, row_sums,
-                                                           nullptr, nullptr);
+                                                           nullptr, nullptr, gamma, thr);
     else
         wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K, row_sums, nullptr,
-                                                        nullptr);
+                                                        nullptr, gamma, thr);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    wq_rows_gamma_kernel<<<(unsigned)((N + 255) / 256), 256, 0, s>>>(row_sums, N, K, gamma, thr);
-    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total4 = N * K / 4;
     const unsigned g3 = (unsigned)((total4 + 256 * kPackU - 1) / (256 * kPackU));
@@ -865,10 +882,10 @@ hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
     const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
     if (w_bf16)
         wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K,
-                                                           row_sums, nodes, gate);
+                                                           row_sums, nodes, gate, nullptr, nullptr);
     else
         wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K,
-                                                        row_sums, nodes, gate);
+                                                        row_sums, nodes, gate, nullptr, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s);
