@@ -71,6 +71,10 @@ def _weight_case(N, K, dtype, seed, special=None):
     (64, 8192, torch.float32, None),
     (7, 64, torch.float32, "zero"),
     (4099, 64, torch.bfloat16, None),        # many rows: second-level tree over > 4096 sums
+    # large matrices: gamma evaluated by the pack launch's workgroup 0 and
+    # published to the other workgroups (ragged last workgroup)
+    (2111, 4096, torch.bfloat16, "heavy"),
+    (4099, 1024, torch.float32, None),
 ])
 def test_weight_quant_bit_exact(N, K, dtype, special):
     print(f"weight_quant N={N} K={K} {dtype} {special}", flush=True)
@@ -80,6 +84,23 @@ def test_weight_quant_bit_exact(N, K, dtype, special):
     c_ref, g_ref = oracle.weight_quant(host(w))
     assert f32_bits_equal(gamma.cpu().numpy(), np.array([g_ref], np.float32))
     assert np.array_equal(wp.cpu().numpy(), oracle.pack(c_ref))
+
+
+def test_weight_quant_published_threshold_is_per_call():
+    # one workspace for consecutive calls on matrices with different gammas:
+    # every call must use its own threshold, never the word a previous call
+    # published (the row-sum pass clears it)
+    N, K = 2111, 4096
+    ws = torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, 0, N, K), dtype=torch.uint8,
+                     device="cuda")
+    base = _weight_case(N, K, torch.float32, seed=91)
+    for scale in (1.0, 3.0, 0.25):
+        w = base * scale
+        wp, gamma = bt.bitnet_weight_quant(to_dev(w), workspace=ws)
+        torch.cuda.synchronize()
+        c_ref, g_ref = oracle.weight_quant(host(w))
+        assert f32_bits_equal(gamma.cpu().numpy(), np.array([g_ref], np.float32))
+        assert np.array_equal(wp.cpu().numpy(), oracle.pack(c_ref))
 
 
 @pytest.mark.parametrize("j", [25, 31, 41, 47, 97, 127])
@@ -138,6 +159,10 @@ def test_quantizers_are_deterministic():
     (9, 1376, 8192, torch.bfloat16, torch.float32),    # 16 blocks
     (17, 33, 100, torch.bfloat16, torch.float32),      # ragged K: the general activation kernel
     (5000, 8, 1024, torch.float32, torch.float32),     # more rows than the row-walking grid
+    # large N: gamma evaluated by the pack launch's workgroup 0 and published
+    # to the other workgroups (ragged last workgroup)
+    (300, 2111, 4096, torch.bfloat16, torch.bfloat16),
+    (64, 2111, 4096, torch.float32, torch.float32),
 ])
 def test_quant_operands_matches_the_two_calls(M, N, K, xdt, wdt):
     print(f"quant_operands M={M} N={N} K={K} {xdt} {wdt}", flush=True)
