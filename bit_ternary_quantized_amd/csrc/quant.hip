@@ -377,33 +377,50 @@ __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int
     constexpr int G = 8;  // loads in flight per lane
     __shared__ float quad[kWqWaves];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the row base stays scalar
     const int64_t row = (int64_t)bid * kWqWaves + wv;
     const T* w = W + (row < N ? row : 0) * K;
     const int64_t nblk = row < N ? (K + BLK - 1) / BLK : 0;  // uniform in the wave
-    const bool vec_ok = (K % E) == 0;
     PairwiseStack st;
-    for (int64_t b0 = 0; b0 < nblk; b0 += G) {
-        float v[G][E];
+    auto push_block = [&](const float (&v)[E]) {
+        float a[E];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int64_t k0 = (b0 + g) * BLK + (int64_t)lane * E;
-            if (b0 + g < nblk && vec_ok && k0 + E <= K) {
-                Vec16<T>::load(w + k0, v[g]);
-            } else {
+        for (int e = 0; e < E; ++e) a[e] = fabsf(v[e]);
+        st.push(wave_tree_sum(lane_tree<E>(a)));
+    };
+    if ((K % E) == 0) {  // uniform: rows of whole 16-byte vectors (the usual case)
+        // unconditional buffer loads (a vector past the row reads zeros), so
+        // the G loads of a round are in flight together
+        const __amdgpu_buffer_rsrc_t rw = make_buf(w);
+        for (int64_t b0 = 0; b0 < nblk; b0 += G) {
+            uint4 raw[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int64_t k0 = (b0 + g) * BLK + (int64_t)lane * E;
+                raw[g] = buf_load16(rw, b0 + g < nblk && k0 < K ? (uint32_t)(k0 * (int64_t)sizeof(T)) : kBufOOB);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (b0 + g < nblk) {
+                    float v[E];
+                    widen16<T>(raw[g], v);
+                    push_block(v);
+                }
+            }
+        }
+    } else {
+        for (int64_t b0 = 0; b0 < nblk; b0 += G) {
+            float v[G][E];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int64_t k0 = (b0 + g) * BLK + (int64_t)lane * E;
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     v[g][e] = (b0 + g < nblk && k0 + e < K) ? load_elem(w, k0 + e) : 0.0f;
             }
-        }
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (b0 + g < nblk) {
-                float a[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e) a[e] = fabsf(v[g][e]);
-                st.push(wave_tree_sum(lane_tree<E>(a)));
-            }
+            for (int g = 0; g < G; ++g)
+                if (b0 + g < nblk) push_block(v[g]);
         }
     }
     const float total = row < N ? st.total() : 0.0f;
