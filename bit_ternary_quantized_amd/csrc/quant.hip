@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kAqWaves * kWave) void act_quant_kernel(
     constexpr int E = Vec16<T>::E;
     constexpr int BLK = kWave * E;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t row = (int64_t)blockIdx.x * kAqWaves + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * kAqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= M) return;  // uniform per wave
     const T* x = X + row * K;
     int8_t* q = Q + row * K;
@@ -60,9 +60,12 @@ __global__ __launch_bounds__(kAqWaves * kWave) void act_quant_kernel(
     // The row cache holds the 16 loaded bytes per block as they are (8 bf16
     // in 4 registers rather than 8 floats), widened to float where used, so
     // twice as many waves fit when the input is bf16.
+    const __amdgpu_buffer_rsrc_t rx = make_buf(x);
     auto load_raw = [&](int64_t b) -> uint4 {
         const int64_t k0 = b * BLK + (int64_t)lane * E;
-        if (vec_ok && k0 + E <= K) return *reinterpret_cast<const uint4*>(x + k0);
+        // rows of whole vectors: an unconditional buffer load (past the row it
+        // reads zeros), so the loads of a row are in flight together
+        if (vec_ok) return buf_load16(rx, k0 < K ? (uint32_t)(k0 * (int64_t)sizeof(T)) : kBufOOB);
         uint32_t w[4] = {0u, 0u, 0u, 0u};
         if constexpr (sizeof(T) == 4) {
 #pragma unroll
