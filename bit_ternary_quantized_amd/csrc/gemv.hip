@@ -404,7 +404,13 @@ __global__ __launch_bounds__(kThreads) void gemv_t2_kernel(
 // lane mapping, products and reduction, so the same bits.  (Written as its
 // own kernel: the identical schedule inside the general template measured
 // 0.4 us slower at 16 tokens x 11008 x 4096, 5.66 against 5.25 us.)
-template <int S, bool CH>
+// DENSE (more than 4 tokens): every token-row load is an unconditional
+// buffer load (rows >= M read zeros), so all of them are in flight together;
+// a load under a per-thread condition made the compiler wait after every
+// second one (16 tokens: 5.41 -> 5.21 us).  With at most 4 tokens most of
+// those loads would read nothing, and the conditional form measured faster
+// (2 tokens: 4.99 against 5.07 us).
+template <int S, bool CH, bool DENSE>
 __global__ __launch_bounds__(kThreads) void gemv_staged_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ scale_x, const uint8_t* __restrict__ Wp,
     const float* __restrict__ gamma_p, int M, int N, float* __restrict__ Y, int32_t* __restrict__ acc_out) {
@@ -421,16 +427,28 @@ __global__ __launch_bounds__(kThreads) void gemv_staged_kernel(
     const int col = lane & 15, g = lane >> 4;
     const int kb = wave * Kw + g * (Kw / 4);
     const int ngroups = (N + 15) / 16;
-    // the row factors: gamma / scale_x (1 / scale_x with a scale per channel)
-    if (t < 16) row_rs[t] = t < M ? (CH ? 1.0f / scale_x[t] : *gamma_p / scale_x[t]) : 0.0f;
     // the token rows: coalesced 16-byte chunks, waited for, byte-transposed
-    // into the tile (rows >= M as zeros) before any weight load is issued
+    // into the tile (rows >= M as zeros) before any weight load is issued;
+    // the row factors: gamma / scale_x (1 / scale_x with a scale per channel)
     uint4 ac[kAPer];
+    if constexpr (DENSE) {
+        const float sxv = __uint_as_float(buf_load4(make_buf(scale_x), t < M ? 4u * t : kBufOOB));
+        const __amdgpu_buffer_rsrc_t rx = make_buf(Xq);
 #pragma unroll
-    for (int i = 0; i < kAPer; ++i) {
-        const int c = t + i * kThreads;
-        ac[i] = make_uint4(0, 0, 0, 0);
-        if (c / kch < M) ac[i] = *reinterpret_cast<const uint4*>(Xq + (int64_t)(c / kch) * K + 16 * (c % kch));
+        for (int i = 0; i < kAPer; ++i) {
+            const int c = t + i * kThreads;
+            ac[i] = buf_load16(rx, c / kch < M ? (uint32_t)((c / kch) * K + 16 * (c % kch)) : kBufOOB);
+        }
+        const float rs = t < M ? (CH ? 1.0f / sxv : *gamma_p / sxv) : 0.0f;  // every thread: no sunk load
+        if (t < 16) row_rs[t] = rs;
+    } else {
+        if (t < 16) row_rs[t] = t < M ? (CH ? 1.0f / scale_x[t] : *gamma_p / scale_x[t]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kAPer; ++i) {
+            const int c = t + i * kThreads;
+            ac[i] = make_uint4(0, 0, 0, 0);
+            if (c / kch < M) ac[i] = *reinterpret_cast<const uint4*>(Xq + (int64_t)(c / kch) * K + 16 * (c % kch));
+        }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __builtin_amdgcn_sched_barrier(0);
@@ -798,10 +816,14 @@ hipError_t launch_gemv_t2(const int8_t* Xq, const float* scale_x, const uint8_t*
     if (full && (steps == 1 || steps == 2 || steps == 4)) {  // K = 1024, 2048, 4096: the staged kernel
 #define BITNET_STAGED(S_)                                                                                  \
         if (steps == S_) {                                                                                 \
-            if (channel)                                                                                   \
-                gemv_staged_kernel<S_, true><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, Y, acc); \
+            if (channel && M > 4)                                                                          \
+                gemv_staged_kernel<S_, true, true><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, Y, acc); \
+            else if (channel)                                                                              \
+                gemv_staged_kernel<S_, true, false><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, Y, acc); \
+            else if (M > 4)                                                                                \
+                gemv_staged_kernel<S_, false, true><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, Y, acc); \
             else                                                                                           \
-                gemv_staged_kernel<S_, false><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, Y, acc); \
+                gemv_staged_kernel<S_, false, false><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, Y, acc); \
             return hipGetLastError();                                                                      \
         }
         BITNET_STAGED(1)
