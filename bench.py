@@ -285,6 +285,8 @@ def setup_layer(name):
         "W_packed_rows": torch.empty(N, K // 4, dtype=torch.uint8, device=dev),
         "gamma_rows": torch.empty(N, dtype=torch.float32, device=dev),
         "grad_s": torch.empty(N, dtype=torch.float32, device=dev),
+        "ws_wqc": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT_COUNTED, 0, N, K),
+                              dtype=torch.uint8, device=dev),
         "ws_wqr": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT_ROWS, 0, N, K), dtype=torch.uint8,
                               device=dev),
     }
@@ -311,6 +313,8 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
                            "bound": "hbm"},
         # zero / +1 / -1 counts of the packed codes (monitoring): the codes read once
         "code_counts": {"bytes": N * K // 4 + 32, "bound": "hbm"},
+        # weight quant counting its codes as it writes them: weight_quant's bytes plus the counts
+        "weight_quant_counted": {"bytes": 2 * N * K * w_bytes + N * K // 4 + 4 + 32, "bound": "hbm"},
         # per-output-channel variants: per-row weight quant (two reads of W),
         # the forward with a scale per output channel
         "weight_quant_rows": {"bytes": 2 * N * K * w_bytes + N * K // 4 + 4 * N, "bound": "hbm"},
@@ -354,6 +358,7 @@ KERNEL_OF = {
     "bwd_grad_W_gated": "bwd_kernel<grad_W> with the range gate (+ split_reduce_kernel when split)",
     "weight_clamp": "weight_clamp_kernel",
     "code_counts": "code_counts_kernel + code_counts_final_kernel",
+    "weight_quant_counted": "wq_row_abs_sum_kernel + wq_pack_kernel (counting) + code_counts_final_kernel",
     "quant_operands": "quant_operands_kernel + wq_pack_kernel",
     "weight_quant_rows": "wq_row_abs_sum_kernel (with the row gammas) + wq_pack_rows_kernel",
     "linear_fwd_channel": "gemm_i8t2_kernel (per-channel epilogue) or gemv_t2_kernel",
@@ -372,6 +377,7 @@ SOURCES_OF = {
     "bwd_grad_W_gated": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
     "weight_clamp": ["bit_ternary_quantized_amd/csrc/quant.hip"],
     "code_counts": ["bit_ternary_quantized_amd/csrc/quant.hip"],
+    "weight_quant_counted": ["bit_ternary_quantized_amd/csrc/quant.hip"],
     "quant_operands": ["bit_ternary_quantized_amd/csrc/quant.hip"],
     "weight_quant_rows": ["bit_ternary_quantized_amd/csrc/quant.hip"],
     "linear_fwd_channel": ["bit_ternary_quantized_amd/csrc/gemm_i8.hip", "bit_ternary_quantized_amd/csrc/gemv.hip"],
@@ -481,6 +487,9 @@ def bench_layer(args, name):
             workspace=b["ws_bwd"])
     variants = {
         "code_counts": lambda: bt.bitnet_code_counts(b["W_packed"], K, counts=b["counts"], workspace=b["ws_cc"]),
+        # the weight quantizer with the counts made on the way (one pass fewer over the codes)
+        "weight_quant_counted": lambda: bt.bitnet_weight_quant_counted(w, W_packed=b["W_packed"], gamma=b["gamma"],
+                                                                       counts=b["counts"], workspace=b["ws_wqc"]),
         # per-output-channel variants (own buffers; not part of the step)
         "weight_quant_rows": lambda: bt.bitnet_weight_quant_rows(w, W_packed=b["W_packed_rows"], gamma=b["gamma_rows"],
                                                                  workspace=b["ws_wqr"]),

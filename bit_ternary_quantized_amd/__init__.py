@@ -20,7 +20,7 @@ BITNET_OK = 0
 BITNET_F32, BITNET_BF16 = 0, 1
 BITNET_LAYOUT_ROWS, BITNET_LAYOUT_DECODE = 0, 1
 (BITNET_OP_WEIGHT_QUANT, BITNET_OP_LINEAR_BWD_STE, BITNET_OP_LINEAR_FWD, BITNET_OP_CODE_COUNTS,
- BITNET_OP_WEIGHT_QUANT_ROWS) = 0, 1, 2, 3, 4
+ BITNET_OP_WEIGHT_QUANT_ROWS, BITNET_OP_WEIGHT_QUANT_COUNTED) = 0, 1, 2, 3, 4, 5
 GEMV_MAX_M = 16  # linear_fwd runs the packed GEMV up to this many tokens
 BITNET_E_SCRATCH = -7
 NOALLOC_MAX_N = 1 << 18  # rows bitnet_weight_quant_noalloc's fixed scratch holds
@@ -32,7 +32,7 @@ EXPORTS = (
     "bitnet_linear_bwd_ste_channel", "bitnet_linear_fwd_decode", "bitnet_quant_operands",
     "bitnet_decode_layout_bytes", "bitnet_pack_decode",
     "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
-    "bitnet_weight_quant_noalloc", "bitnet_channel_scale_grad",
+    "bitnet_weight_quant_noalloc", "bitnet_channel_scale_grad", "bitnet_weight_quant_counted",
     # calibration kernels (include/bitnet_calib.h): measured ceilings
     "bitnet_calib_stream_read", "bitnet_calib_mfma", "bitnet_calib_mfma_ops",
 )
@@ -81,6 +81,7 @@ def load_library(path: str = LIB_PATH):
         "bitnet_version": (c_int, []),
         "bitnet_weight_quant_noalloc": (c_int, [p, c_int, i64, i64, p, p, p]),
         "bitnet_channel_scale_grad": (c_int, [p, p, i64, i64, p, p]),
+        "bitnet_weight_quant_counted": (c_int, [p, c_int, i64, i64, p, p, p, p, sz, p]),
         "bitnet_calib_stream_read": (c_int, [p, i64, c_int, p, p]),
         "bitnet_calib_mfma": (c_int, [c_int, c_int, c_int, p, p, p]),
         "bitnet_calib_mfma_ops": (ctypes.c_double, [c_int, c_int, c_int]),
@@ -216,6 +217,26 @@ def bitnet_weight_quant(W: torch.Tensor, W_packed=None, gamma=None, workspace=No
         _ptr(W), _dtype_code(W), N, K, _ptr(W_packed), _ptr(gamma), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
     return W_packed, gamma
+
+
+def bitnet_weight_quant_counted(W: torch.Tensor, W_packed=None, gamma=None, counts=None, workspace=None,
+                                stream=None):
+    """bitnet_weight_quant plus the code counts of its result, counted as the
+    codes are written -> (W_packed, gamma, counts int64 [zeros, +1, -1, unused 11])."""
+    lib = load_library()
+    N, K = _mk(W, "W", "[N, K]")
+    _req(W, "W", FLOAT)
+    dev = W.device
+    need = bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT_COUNTED, 0, N, K)
+    W_packed = _req(_alloc(W_packed, (N, K // 4), torch.uint8, dev), "W_packed", U8, N * (K // 4), device=dev)
+    gamma = _req(_alloc(gamma, (1,), torch.float32, dev), "gamma", F32, 1, device=dev)
+    counts = _req(_alloc(counts, (4,), torch.int64, dev), "counts", I64, 4, device=dev)
+    workspace = _ws(_alloc(workspace, (need,), torch.uint8, dev), "workspace", need, dev)
+    _on_gpu(W=W, W_packed=W_packed, gamma=gamma, counts=counts, workspace=workspace)
+    _check("bitnet_weight_quant_counted", lib.bitnet_weight_quant_counted(
+        _ptr(W), _dtype_code(W), N, K, _ptr(W_packed), _ptr(gamma), _ptr(counts), _ptr(workspace),
+        _nbytes(workspace), _stream(stream)))
+    return W_packed, gamma, counts
 
 
 def bitnet_weight_quant_noalloc(W: torch.Tensor, W_packed, gamma, stream=None):

@@ -48,6 +48,7 @@ size_t bitnet_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
         case BITNET_OP_LINEAR_BWD_STE: return bitnet::bwd_ws_bytes(M, N, K);
         case BITNET_OP_CODE_COUNTS: return bitnet::code_counts_ws_bytes();
         case BITNET_OP_WEIGHT_QUANT_ROWS: return bitnet::weight_quant_rows_ws_bytes(N);
+        case BITNET_OP_WEIGHT_QUANT_COUNTED: return bitnet::weight_quant_counted_ws_bytes(N, K);
         default: return 0;
     }
 }
@@ -62,6 +63,20 @@ int bitnet_weight_quant(const void* W, int w_dtype, int64_t N, int64_t K, uint8_
     if (!aligned16(workspace)) return BITNET_E_ALIGN;
     return hip_status(bitnet::launch_weight_quant(W, w_dtype == BITNET_BF16, N, K, W_packed, gamma,
                                                   workspace, as_stream(stream)));
+}
+
+int bitnet_weight_quant_counted(const void* W, int w_dtype, int64_t N, int64_t K, uint8_t* W_packed,
+                                float* gamma, uint64_t* counts, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    if (!W || !W_packed || !gamma || !counts) return BITNET_E_ARG;
+    if (!float_dtype(w_dtype)) return BITNET_E_DTYPE;
+    if (N < 1 || K < 1 || K % 4 != 0 || N > kMaxDim || K > kMaxDim) return BITNET_E_SHAPE;
+    if (!aligned16(W) || !aligned16(W_packed) || !aligned4(gamma)) return BITNET_E_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(counts) & 7u) != 0) return BITNET_E_ALIGN;
+    if (!workspace || workspace_bytes < bitnet::weight_quant_counted_ws_bytes(N, K)) return BITNET_E_WORKSPACE;
+    if (!aligned16(workspace)) return BITNET_E_ALIGN;
+    return hip_status(bitnet::launch_weight_quant_counted(W, w_dtype == BITNET_BF16, N, K, W_packed, gamma, counts,
+                                                          workspace, as_stream(stream)));
 }
 
 int bitnet_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, float eps, int8_t* Xq,

@@ -256,6 +256,10 @@ constexpr size_t weight_quant_ws_size(int64_t N) {
     return (size_t)(((N * 4 + 255) / 256) * 256 + 256 + (((N + 3) / 4 * 4 + 255) / 256) * 256);
 }
 size_t weight_quant_ws_bytes(int64_t N);
+// weight_quant and the code counts (zeros, +1, -1, 11) of the codes it packs
+hipError_t launch_weight_quant_counted(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* W_packed,
+                                       float* gamma, uint64_t* counts, void* ws, hipStream_t s);
+size_t weight_quant_counted_ws_bytes(int64_t N, int64_t K);
 // act_quant of X and weight_quant of W (same K) with one launch fewer;
 // outputs bit-identical to the two; ws as weight_quant's
 hipError_t launch_quant_operands(const void* X, bool x_bf16, int64_t M, int64_t K, float eps, int8_t* Xq,

@@ -354,6 +354,7 @@ hipError_t launch_act_quant(const void* X, bool x_bf16, int64_t M, int64_t K, fl
 // |w| the test |w| > t equals |w| >= thr, thr = the least float above t.
 
 constexpr int kWqWaves = 4;
+constexpr int kCountSlots = 1024;  // count slots of the counted weight quant
 
 // quad_sums (when non-null): the workgroup also writes the tree node over
 // its kWqWaves = 4 rows, (r0 + r1) + (r2 + r3) with rows past N as +0: the
@@ -373,8 +374,12 @@ __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int
                                                     float* __restrict__ quad_sums,
                                                     uint64_t* __restrict__ gate,
                                                     float* __restrict__ row_gamma = nullptr,
-                                                    float* __restrict__ row_thr = nullptr) {
+                                                    float* __restrict__ row_thr = nullptr,
+                                                    uint32_t* __restrict__ count_slots = nullptr) {
     if (gate && bid == 0 && threadIdx.x == 0) *gate = 0;
+    // the counted call's count slots, cleared before its pack launch adds into them
+    if (count_slots && bid == 0)
+        for (int i = threadIdx.x; i < 4 * kCountSlots; i += kWqWaves * kWave) count_slots[i] = 0u;
     constexpr int E = Vec16<T>::E;
     constexpr int BLK = kWave * E;
     constexpr int G = 8;  // loads in flight per lane
@@ -445,8 +450,9 @@ __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int
 template <typename T>
 __global__ __launch_bounds__(kWqWaves * kWave) void wq_row_abs_sum_kernel(
     const T* __restrict__ W, int64_t N, int64_t K, float* __restrict__ row_sums, float* __restrict__ quad_sums,
-    uint64_t* __restrict__ gate, float* __restrict__ row_gamma, float* __restrict__ row_thr) {
-    wq_row_abs_sum_body<T>(W, N, K, row_sums, blockIdx.x, quad_sums, gate, row_gamma, row_thr);
+    uint64_t* __restrict__ gate, float* __restrict__ row_gamma, float* __restrict__ row_thr,
+    uint32_t* __restrict__ count_slots = nullptr) {
+    wq_row_abs_sum_body<T>(W, N, K, row_sums, blockIdx.x, quad_sums, gate, row_gamma, row_thr, count_slots);
 }
 
 // Pass 2: the tree over the n = ceil(N/4) four-row nodes of pass 1 (the
@@ -501,6 +507,26 @@ __device__ __forceinline__ uint32_t code_bits(float w, float thr) {
     return fabsf(w) >= thr ? (w > 0.0f ? 1u : 2u) : 0u;
 }
 
+// Adds the 2-bit fields of w (one bit per field in field_mask) to the counts
+// of zeros, +1 (01), -1 (10) and the unused pattern 11.
+__device__ __forceinline__ void count_code_fields(uint32_t w, uint32_t field_mask, uint32_t (&c)[4]) {
+    const uint32_t lo = w & field_mask, hi = (w >> 1) & field_mask;
+    c[0] += __builtin_popcount(~(lo | hi) & field_mask);
+    c[1] += __builtin_popcount(lo & ~hi);
+    c[2] += __builtin_popcount(hi & ~lo);
+    c[3] += __builtin_popcount(lo & hi);
+}
+
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* red) {  // 256 threads
+#pragma unroll
+    for (int m = 1; m < kWave; m *= 2) v += __shfl_xor(v, m, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const uint32_t t = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    return t;
+}
+
 constexpr int kPackU = 4;  // groups of 4 weights per thread (loads in flight)
 // with the published threshold: twice as many per thread, so that at 4096 x
 // 4096 bf16 the whole matrix is requested by workgroups resident at once and
@@ -526,12 +552,19 @@ constexpr int kGatePolls = 32;
 // kGatePolls reads (a short sleep apart) computes the threshold itself from
 // the nodes, which gives the same bits.  No workgroup waits on another's
 // progress beyond that bounded number of reads.
-template <typename T, bool FUSED, int U>
+// COUNT: the workgroup also counts the codes it writes (zeros, +1, -1, and
+// the unused pattern 11, always 0 here) and adds its four sums into slot
+// blockIdx.x % kCountSlots of count_partial (integer atomics: exact in any
+// order; the slots were cleared by pass 1 of the same call), which
+// code_counts_final_kernel then adds up: the monitoring counts without a
+// second read of the packed weights.
+template <typename T, bool FUSED, int U, bool COUNT = false>
 __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, int64_t total4,
                                                       uint64_t* __restrict__ gate,
                                                       const float* __restrict__ nodes,
                                                       int64_t N, int64_t K, float* __restrict__ gamma,
-                                                      uint8_t* __restrict__ out) {
+                                                      uint8_t* __restrict__ out,
+                                                      uint32_t* __restrict__ count_partial = nullptr) {
     // the workgroup's groups of 4 weights through one buffer descriptor: every
     // load is unconditional (past total4 an out-of-range offset reads zeros),
     // so all U loads are in flight together and nothing waits for them before
@@ -540,6 +573,7 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, i
     const int64_t base = g0 + threadIdx.x;
     const __amdgpu_buffer_rsrc_t rw = make_buf(W + g0 * 4);
     constexpr uint32_t kGroupBytes = 4 * sizeof(T);
+    uint32_t cnt[4] = {0u, 0u, 0u, 0u};  // COUNT: zeros, +1, -1, 11
     uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -611,6 +645,15 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, i
 #pragma unroll
             for (int j = 0; j < 4; ++j) byte |= code_bits(v[j], thr) << (2 * j);
             out[i] = (uint8_t)byte;
+            if constexpr (COUNT) count_code_fields(byte, 0x55u, cnt);
+        }
+    }
+    if constexpr (COUNT) {
+        __shared__ uint32_t red[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t t = block_sum_u32(cnt[j], red);
+            if (threadIdx.x == 0) atomicAdd(&count_partial[4 * (blockIdx.x % kCountSlots) + j], t);
         }
     }
 }
@@ -725,27 +768,11 @@ static unsigned stream_grid(int64_t work_items, int per_block) {
 // order.  Integers throughout, no atomics: exact and deterministic.
 constexpr int kCountGroups = 1024;  // pass-1 workgroups at most
 
-__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* red) {  // 256 threads
-#pragma unroll
-    for (int m = 1; m < kWave; m *= 2) v += __shfl_xor(v, m, kWave);
-    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    const uint32_t t = red[0] + red[1] + red[2] + red[3];
-    __syncthreads();
-    return t;
-}
-
 __global__ __launch_bounds__(256) void code_counts_kernel(const uint8_t* __restrict__ P, int64_t nbytes,
                                                           uint32_t* __restrict__ partial) {
     __shared__ uint32_t red[4];
     uint32_t c[4] = {0u, 0u, 0u, 0u};  // zeros, +1, -1, 11
-    auto count_fields = [&](uint32_t w, uint32_t field_mask) {  // one bit per 2-bit field
-        const uint32_t lo = w & field_mask, hi = (w >> 1) & field_mask;
-        c[0] += __builtin_popcount(~(lo | hi) & field_mask);
-        c[1] += __builtin_popcount(lo & ~hi);
-        c[2] += __builtin_popcount(hi & ~lo);
-        c[3] += __builtin_popcount(lo & hi);
-    };
+    auto count_fields = [&](uint32_t w, uint32_t field_mask) { count_code_fields(w, field_mask, c); };
     const int64_t nvec = nbytes / 16;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * 256) {
         const uint4 v = reinterpret_cast<const uint4*>(P)[i];
@@ -870,8 +897,11 @@ static float* ws_nodes(void* ws, int64_t N) {
 
 // Passes 2 and 3 (gamma, threshold, packing) from the four-row nodes in ws,
 // in one launch.
+// counts (when non-null): the pack launch also writes per-workgroup code
+// counts to `count_partial` and one workgroup adds them into counts[4].
 static hipError_t weight_quant_pack(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* W_packed,
-                                    float* gamma, void* ws, hipStream_t s) {
+                                    float* gamma, void* ws, hipStream_t s, uint64_t* counts = nullptr,
+                                    uint32_t* count_partial = nullptr) {
     uint64_t* gate = ws_gate(ws, N);
     const float* nodes = ws_nodes(ws, N);
     const int64_t total4 = N * K / 4;
@@ -880,18 +910,34 @@ static hipError_t weight_quant_pack(const void* W, bool w_bf16, int64_t N, int64
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
     const float* Wf = static_cast<const float*>(W);
     const bool fused = N * (int64_t)g3 <= kFusedGammaMaxWork;
-#define BITNET_PACK(T_, W_)                                                                                  \
+#define BITNET_PACK(T_, W_, C_)                                                                              \
     do {                                                                                                     \
         if (fused)                                                                                           \
-            wq_pack_kernel<T_, true, kPackU><<<g3, 256, 0, s>>>(W_, total4, gate, nodes, N, K, gamma, W_packed); \
+            wq_pack_kernel<T_, true, kPackU, C_><<<g3, 256, 0, s>>>(W_, total4, gate, nodes, N, K, gamma,     \
+                                                                     W_packed, count_partial);               \
         else                                                                                                 \
-            wq_pack_kernel<T_, false, kPackUPub><<<g3p, 256, 0, s>>>(W_, total4, gate, nodes, N, K, gamma,  \
-                                                                       W_packed);                            \
+            wq_pack_kernel<T_, false, kPackUPub, C_><<<g3p, 256, 0, s>>>(W_, total4, gate, nodes, N, K, gamma, \
+                                                                           W_packed, count_partial);         \
     } while (0)
-    if (w_bf16) BITNET_PACK(uint16_t, Wb);
-    else BITNET_PACK(float, Wf);
+    if (counts) {
+        if (w_bf16) BITNET_PACK(uint16_t, Wb, true);
+        else BITNET_PACK(float, Wf, true);
+    } else {
+        if (w_bf16) BITNET_PACK(uint16_t, Wb, false);
+        else BITNET_PACK(float, Wf, false);
+    }
 #undef BITNET_PACK
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !counts) return e;
+    code_counts_final_kernel<<<1, 256, 0, s>>>(count_partial, kCountSlots,
+                                               reinterpret_cast<unsigned long long*>(counts));
     return hipGetLastError();
+}
+
+// the count slots of the counted call, after weight_quant's workspace
+static size_t weight_quant_counted_slots_offset(int64_t N) { return weight_quant_ws_size(N); }
+size_t weight_quant_counted_ws_bytes(int64_t N, int64_t) {
+    return weight_quant_ws_size(N) + (size_t)kCountSlots * 4 * sizeof(uint32_t);
 }
 
 hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
@@ -909,6 +955,27 @@ hipError_t launch_weight_quant(const void* W, bool w_bf16, int64_t N, int64_t K,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s);
+}
+
+// weight_quant plus the code counts, written by the pack launch's workgroups
+// as they pack (no second read of the packed weights)
+hipError_t launch_weight_quant_counted(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* W_packed,
+                                       float* gamma, uint64_t* counts, void* ws, hipStream_t s) {
+    float* row_sums = static_cast<float*>(ws);
+    float* nodes = ws_nodes(ws, N);
+    uint64_t* gate = ws_gate(ws, N);
+    uint32_t* slots =
+        reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + weight_quant_counted_slots_offset(N));
+    const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
+    if (w_bf16)
+        wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K,
+                                                           row_sums, nodes, gate, nullptr, nullptr, slots);
+    else
+        wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K,
+                                                        row_sums, nodes, gate, nullptr, nullptr, slots);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s, counts, slots);
 }
 
 // ============================================= both quantizers, one launch fewer

@@ -79,7 +79,8 @@ typedef enum {
     BITNET_OP_LINEAR_BWD_STE = 1,
     BITNET_OP_LINEAR_FWD = 2,
     BITNET_OP_CODE_COUNTS = 3,
-    BITNET_OP_WEIGHT_QUANT_ROWS = 4
+    BITNET_OP_WEIGHT_QUANT_ROWS = 4,
+    BITNET_OP_WEIGHT_QUANT_COUNTED = 5
 } bitnet_op;
 
 /*
@@ -376,6 +377,27 @@ int bitnet_linear_bwd_ste_channel(const void *grad_y, int gy_dtype, const int8_t
  */
 int bitnet_code_counts(const uint8_t *W_packed, int64_t N, int64_t K, uint64_t *counts,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * bitnet_weight_quant and bitnet_code_counts of its result in one call: the
+ * workgroups that write the packed codes also count them, so the counts
+ * need no second read of W_packed ([NOTES 6], practice notes, item 3: the
+ * zero share; "BitNet量化感知训练中的梯度传播优化", convergence monitoring:
+ * polarity balance).  W_packed and gamma are the same bits as
+ * bitnet_weight_quant's; counts as bitnet_code_counts's (counts[3], the
+ * unused pattern 11, is 0).
+ *   W, W_packed, gamma: as bitnet_weight_quant
+ *   counts    4 uint64, DEVICE memory, 8-byte aligned, written
+ *   workspace >= bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT_COUNTED, 0, N, K)
+ *            device scratch: weight_quant's, then 1024 x 4 count slots the
+ *            call clears before adding into them (integer atomics, exact in
+ *            any order); contents on entry ignored.
+ * Errors: BITNET_E_ARG, BITNET_E_DTYPE, BITNET_E_SHAPE, BITNET_E_ALIGN,
+ * BITNET_E_WORKSPACE, BITNET_E_HIP.
+ */
+int bitnet_weight_quant_counted(const void *W, int w_dtype, int64_t N, int64_t K,
+                                uint8_t *W_packed, float *gamma, uint64_t *counts,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Backward of the unit-gain RMSNorm in front of the activation quantizer

@@ -375,6 +375,22 @@ def test_noalloc_weight_quant_rejects_bad_arguments():
     assert f(ctypes.c_void_p((1 << 20) + 8), 0, 4, 4, P, P, NULL) == -4
 
 
+def test_weight_quant_counted_rejects_bad_arguments():
+    lib = bt.load_library()
+    f = lib.bitnet_weight_quant_counted
+    ws = bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT_COUNTED, 0, 8, 16)
+    assert ws >= bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, 0, 8, 16) + 1024 * 16
+    # (W, dtype, N, K, W_packed, gamma, counts, ws, ws_bytes, stream)
+    assert f(NULL, 0, 8, 16, P, P, P, P, ws, NULL) == -1
+    assert f(P, 0, 8, 16, P, P, NULL, P, ws, NULL) == -1
+    assert f(P, 5, 8, 16, P, P, P, P, ws, NULL) == -3
+    assert f(P, 0, 8, 18, P, P, P, P, ws, NULL) == -2
+    assert f(P, 0, 0, 16, P, P, P, P, ws, NULL) == -2
+    assert f(P, 0, 8, 16, P, P, ctypes.c_void_p((1 << 20) + 4), P, ws, NULL) == -4
+    assert f(P, 0, 8, 16, P, P, P, P, ws - 16, NULL) == -5
+    assert f(P, 0, 8, 16, P, P, P, NULL, ws, NULL) == -5
+
+
 def test_channel_scale_grad_rejects_bad_arguments():
     lib = bt.load_library()
     f = lib.bitnet_channel_scale_grad
