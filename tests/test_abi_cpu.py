@@ -379,7 +379,10 @@ def test_weight_quant_counted_rejects_bad_arguments():
     lib = bt.load_library()
     f = lib.bitnet_weight_quant_counted
     ws = bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT_COUNTED, 0, 8, 16)
-    assert ws >= bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, 0, 8, 16) + 1024 * 16
+    assert ws >= bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, 0, 8, 16) + 8
+    # one 8-byte pair per 4096 weights
+    big = bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT_COUNTED, 0, 4096, 4096)
+    assert big >= bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, 0, 4096, 4096) + 8 * 4096
     # (W, dtype, N, K, W_packed, gamma, counts, ws, ws_bytes, stream)
     assert f(NULL, 0, 8, 16, P, P, P, P, ws, NULL) == -1
     assert f(P, 0, 8, 16, P, P, NULL, P, ws, NULL) == -1

@@ -51,8 +51,10 @@ def test_code_counts_decode_layer():
 # codes and gamma as the oracle, the counts of those codes; small matrices
 # (gamma in every pack workgroup) and large ones (gamma published by one)
 @pytest.mark.parametrize("N,K,dt", [(1, 4, "f32"), (37, 100, "bf16"), (1376, 512, "f32"), (2111, 4096, "bf16"),
-                                    (4099, 1024, "f32")])
+                                    (4099, 1024, "f32"), (8209, 8192, "bf16")])
 def test_weight_quant_counted(N, K, dt):
+    # the last case has more pack workgroups (8209) than the final sum takes
+    # in one pass (4096): three passes
     print(f"weight_quant_counted N={N} K={K} {dt}", flush=True)
     w = workloads.normal((N, K), 0.02, seed=3 * N + K, dtype=dt)
     wp, g, c = bt.bitnet_weight_quant_counted(to_dev(w))
