@@ -460,7 +460,7 @@ __device__ __forceinline__ void gamma_and_thr(const float* __restrict__ nodes, i
                                               int64_t K, float* part, float& g, float& thr) {
     const float* __restrict__ row_sums = nodes;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x >> 6;
+    const int wv = W == 1 ? 0 : threadIdx.x >> 6;
     constexpr int E = 4;
     constexpr int BLK = kWave * E;
     int64_t P = 1;
@@ -482,12 +482,17 @@ __device__ __forceinline__ void gamma_and_thr(const float* __restrict__ nodes, i
         for (int gi = 0; gi < 8; ++gi)
             if (b0 + gi < nblk) st.push(wave_tree_sum(lane_tree<E>(v[gi])));
     }
-    if (lane == 0) part[wv] = st.total();
-    __syncthreads();
-    float pw[W];
+    float total;
+    if constexpr (W == 1) {  // one wave (any wave of the workgroup), no barrier; part unused
+        total = st.total();
+    } else {
+        if (lane == 0) part[wv] = st.total();
+        __syncthreads();
+        float pw[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) pw[i] = part[i];
-    const float total = lane_tree<W>(pw);
+        for (int i = 0; i < W; ++i) pw[i] = part[i];
+        total = lane_tree<W>(pw);
+    }
     const float mean = total / (float)(N * K);
     g = fmaxf(mean, 1e-5f);
     const double t = (double)g * (0.5 + 0x1p-25);
@@ -512,10 +517,15 @@ __device__ __forceinline__ void count_code_fields(uint32_t w, uint32_t field_mas
 }
 
 constexpr int kPackU = 4;  // groups of 4 weights per thread (loads in flight)
-// with the published threshold: twice as many per thread, so that at 4096 x
-// 4096 bf16 the whole matrix is requested by workgroups resident at once and
-// its loads stream while workgroup 0 evaluates gamma
-constexpr int kPackUPub = 8;
+// with the published threshold, groups per thread: with the fifth wave, 128
+// bytes of weights per thread (16 groups of bf16, 8 of fp32), so that at
+// 4096 x 4096 bf16 the whole matrix is requested by one round of resident
+// workgroups (1024 of five waves; a CU holds six) and its loads stream while
+// workgroup 0 evaluates gamma; else 8 groups (16 fp32 groups per thread
+// measured slower at 28672 x 8192: 362 against 335 us)
+template <typename T, bool POLLER>
+constexpr int pack_u_pub() { return POLLER ? 128 / (4 * (int)sizeof(T)) : 8; }
+constexpr int kPollerGroupsPerCu = 6;  // five-wave workgroups a CU holds (32 wave slots)
 // When (rows x pack workgroups) is at most this, every pack workgroup
 // evaluates gamma and the threshold itself from the four-row nodes (for
 // small matrices; the weight loads are issued first, so the evaluation hides
@@ -527,46 +537,47 @@ constexpr int64_t kFusedGammaMaxWork = (int64_t)1 << 22;
 // reads of the published threshold before a workgroup evaluates it itself
 constexpr int kGatePolls = 32;
 
-// FUSED: every workgroup computes the threshold from the four-row nodes
-// (block 0 also writes gamma).  Otherwise workgroup 0 computes gamma and the
-// threshold and publishes the threshold in `gate`, one 64-bit word holding
-// the threshold bits and a ready mark, written with a single store (cleared
-// by pass 1 of the same call); every other workgroup reads that word after
-// issuing its weight loads, and one that still finds no ready mark after
-// kGatePolls reads (a short sleep apart) computes the threshold itself from
-// the nodes, which gives the same bits.  No workgroup waits on another's
-// progress beyond that bounded number of reads.
-// COUNT: the workgroup also counts the codes it writes.  Each thread keeps
-// its +1 and -1 counts in the two halves of one word (at most 4U codes a
-// thread, 256 * 4U = 8192 a workgroup: well inside 16 bits), each wave adds
-// its 64 words with lane exchanges, and after one barrier thread 0 stores the
-// workgroup's pair (+1, -1) in slot blockIdx.x of count_partial: a plain
-// store, every slot written once per call, nothing to clear.  (Device-scope
-// atomics into shared slots instead were measured slower: at 4096 x 4096
-// bf16 the counting pack took 12.2 us with one set of atomics per
-// workgroup, 13.8 us with one per wave, against 11.6 us with stores.)
-// counted_final_kernel then adds the pairs: the monitoring counts without a
-// second read of the packed weights.
-template <typename T, bool FUSED, int U, bool COUNT = false>
-__global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, int64_t total4,
-                                                      uint64_t* __restrict__ gate,
-                                                      const float* __restrict__ nodes,
-                                                      int64_t N, int64_t K, float* __restrict__ gamma,
-                                                      uint8_t* __restrict__ out,
-                                                      uint32_t* __restrict__ count_partial = nullptr) {
-    // the workgroup's groups of 4 weights through one buffer descriptor: every
-    // load is unconditional (past total4 an out-of-range offset reads zeros),
-    // so all U loads are in flight together and nothing waits for them before
-    // the threshold is known
-    const int64_t g0 = (int64_t)blockIdx.x * (256 * U);
-    const int64_t base = g0 + threadIdx.x;
+// The pack of a group of 4 weights into one byte of codes, and the counts of
+// the codes written (COUNT: +1 codes in the low half of cnt, -1 codes in the
+// high half).
+template <typename T, bool COUNT>
+__device__ __forceinline__ void pack_group(const uint4& raw, float thr, int64_t i, uint8_t* __restrict__ out,
+                                           uint32_t& cnt) {
+    float v[4];
+    if constexpr (sizeof(T) == 4) {
+        v[0] = __uint_as_float(raw.x);
+        v[1] = __uint_as_float(raw.y);
+        v[2] = __uint_as_float(raw.z);
+        v[3] = __uint_as_float(raw.w);
+    } else {
+        v[0] = __uint_as_float(raw.x << 16);
+        v[1] = __uint_as_float(raw.x & 0xffff0000u);
+        v[2] = __uint_as_float(raw.y << 16);
+        v[3] = __uint_as_float(raw.y & 0xffff0000u);
+    }
+    uint32_t byte = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) byte |= code_bits(v[j], thr) << (2 * j);
+    out[i] = (uint8_t)byte;
+    if constexpr (COUNT) {
+        const uint32_t lo = byte & 0x55u, hi = (byte >> 1) & 0x55u;
+        cnt += __builtin_popcount(lo & ~hi) + (__builtin_popcount(hi & ~lo) << 16);
+    }
+}
+
+// The weights of a workgroup's NT U groups of 4 (NT threads), thread t taking
+// groups t, t + NT, ...: one buffer descriptor at the workgroup's first
+// group, every load unconditional (past total4 an out-of-range offset reads
+// zeros), so all U loads are in flight together and nothing waits for them
+// before the threshold is known.
+template <typename T, int U, int NT>
+__device__ __forceinline__ void load_groups(const T* __restrict__ W, int64_t g0, int64_t total4, int t,
+                                            uint4 (&raw)[U]) {
     const __amdgpu_buffer_rsrc_t rw = make_buf(W + g0 * 4);
     constexpr uint32_t kGroupBytes = 4 * sizeof(T);
-    uint32_t cnt = 0u;  // COUNT: +1 codes in the low half, -1 codes in the high half
-    uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint32_t off = base + u * 256 < total4 ? (threadIdx.x + u * 256) * kGroupBytes : kBufOOB;
+        const uint32_t off = g0 + t + u * NT < total4 ? (t + u * NT) * kGroupBytes : kBufOOB;
         if constexpr (sizeof(T) == 4) {
             raw[u] = buf_load16(rw, off);
         } else {
@@ -574,83 +585,172 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, i
             raw[u] = make_uint4(q.x, q.y, 0u, 0u);
         }
     }
-    float thr;
-    __shared__ float part[4];
-    if constexpr (FUSED) {
-        float g;
-        gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
-        if (blockIdx.x == 0 && threadIdx.x == 0) gamma[0] = g;
-    } else if (blockIdx.x == 0) {  // uniform
-        float g;
-        gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
-        if (threadIdx.x == 0) {
-            gamma[0] = g;
-            __hip_atomic_store(gate, ((uint64_t)1 << 32) | __float_as_uint(thr), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    } else {
-        __shared__ float pub_thr;
-        __shared__ int pub_ok;
-        if (threadIdx.x == 0) {
-            int ok = 0;
-            float t = 0.0f;
-            for (int i = 0; i < kGatePolls; ++i) {
-                const uint64_t word = __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if ((uint32_t)(word >> 32) == 1u) {
-                    ok = 1;
-                    t = __uint_as_float((uint32_t)word);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
-            pub_ok = ok;
-            pub_thr = t;
-        }
-        __syncthreads();
-        if (pub_ok) {  // uniform: one LDS value for the workgroup
-            thr = pub_thr;
-        } else {
-            float g;
-            gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t i = base + u * 256;
-        float v[4];
-        if constexpr (sizeof(T) == 4) {
-            v[0] = __uint_as_float(raw[u].x);
-            v[1] = __uint_as_float(raw[u].y);
-            v[2] = __uint_as_float(raw[u].z);
-            v[3] = __uint_as_float(raw[u].w);
-        } else {
-            v[0] = __uint_as_float(raw[u].x << 16);
-            v[1] = __uint_as_float(raw[u].x & 0xffff0000u);
-            v[2] = __uint_as_float(raw[u].y << 16);
-            v[3] = __uint_as_float(raw[u].y & 0xffff0000u);
-        }
-        if (i < total4) {
-            uint32_t byte = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) byte |= code_bits(v[j], thr) << (2 * j);
-            out[i] = (uint8_t)byte;
-            if constexpr (COUNT) {
-                const uint32_t lo = byte & 0x55u, hi = (byte >> 1) & 0x55u;
-                cnt += __builtin_popcount(lo & ~hi) + (__builtin_popcount(hi & ~lo) << 16);
-            }
-        }
-    }
+}
+
+// COUNT (both pack kernels): the workgroup also counts the codes it writes.
+// Each thread keeps its +1 and -1 counts in the two halves of one word (at
+// most 4U codes a thread, at most 256 * 64 = 16384 a workgroup: inside 16
+// bits), each wave adds its 64 words with lane exchanges, and after one
+// barrier thread 0
+// stores the workgroup's pair (+1, -1) in slot blockIdx.x of count_partial: a
+// plain store, every slot written once per call, nothing to clear.
+// (Device-scope atomics into shared slots instead were measured slower: at
+// 4096 x 4096 bf16 the counting pack took 12.2 us with one set of atomics per
+// workgroup, 13.8 us with one per wave, against 11.6 us with stores.)
+// counted_final_kernel then adds the pairs: the monitoring counts without a
+// second read of the packed weights.
+static_assert(256 * 4 * 16 < 65536, "per-workgroup code counts fit 16 bits");
+template <bool COUNT, int NW>
+__device__ __forceinline__ void store_group_counts(uint32_t cnt, uint32_t* __restrict__ count_partial) {
     if constexpr (COUNT) {
-        __shared__ uint32_t red[4];
+        __shared__ uint32_t red[NW];
 #pragma unroll
         for (int m = 1; m < kWave; m *= 2) cnt += __shfl_xor(cnt, m, kWave);
-        if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x >> 6] = cnt;
+        if ((threadIdx.x & (kWave - 1)) == 0 && (threadIdx.x >> 6) < NW) red[threadIdx.x >> 6] = cnt;
         __syncthreads();
         if (threadIdx.x == 0) {
-            const uint32_t t = red[0] + red[1] + red[2] + red[3];
+            uint32_t t = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) t += red[w];
             reinterpret_cast<uint2*>(count_partial)[blockIdx.x] = make_uint2(t & 0xffffu, t >> 16);
         }
     }
+}
+
+// Small matrices: every workgroup computes gamma and the threshold from the
+// four-row nodes (its weight loads issued first, so the evaluation hides
+// under them); block 0 also writes gamma.
+template <typename T, int U, bool COUNT = false>
+__global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, int64_t total4,
+                                                      const float* __restrict__ nodes,
+                                                      int64_t N, int64_t K, float* __restrict__ gamma,
+                                                      uint8_t* __restrict__ out,
+                                                      uint32_t* __restrict__ count_partial = nullptr) {
+    const int64_t g0 = (int64_t)blockIdx.x * (256 * U);
+    uint4 raw[U];
+    load_groups<T, U, 256>(W, g0, total4, threadIdx.x, raw);
+    float thr, g;
+    __shared__ float part[4];
+    gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
+    if (blockIdx.x == 0 && threadIdx.x == 0) gamma[0] = g;
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = g0 + threadIdx.x + u * 256;
+        if (i < total4) pack_group<T, COUNT>(raw[u], thr, i, out, cnt);
+    }
+    store_group_counts<COUNT, 4>(cnt, count_partial);
+}
+
+// Large matrices: the threshold is evaluated once, by workgroup 0, and
+// published in `gate`, one 64-bit word holding the threshold bits and a
+// ready mark, written with a single store (cleared by pass 1 of the same
+// call).  Every other workgroup reads that word until the mark is there, at
+// most kGatePolls times a short sleep apart, and then evaluates the threshold
+// itself from the four-row nodes (the same bits).  No workgroup waits on
+// another's progress beyond that bounded number of reads.  Waves 0-3 load and
+// pack the weights (256 U groups of 4 a workgroup).
+// POLLER: a fifth wave, with no weight loads, does the reading (or, in
+// workgroup 0, evaluates gamma and the threshold: one wave, the same tree,
+// so the same bits) and hands the threshold to waves 0-3 through LDS and one
+// barrier.  A wave's reads wait for all of its earlier loads, so reads
+// issued by a loading wave return only after its weights: when the whole
+// matrix is requested in one round of resident workgroups, the threshold is
+// on the critical path (4096 x 4096 bf16: 17.2 us for the call with thread 0
+// reading, 14.6 us with the fifth wave, 15.6 us with the wait taken out
+// altogether).  Over many rounds of workgroups the mark is there at the
+// first read, and the fifth wave only leaves a CU fewer loading waves
+// (28672 x 8192 fp32: 349 against 335 us), so there thread 0 reads the word
+// after issuing its weight loads (workgroup 0: all four waves evaluate).
+template <bool POLLER>
+constexpr int pub_threads() { return POLLER ? 5 * kWave : 4 * kWave; }
+template <typename T, int U, bool POLLER, bool COUNT = false>
+__global__ __launch_bounds__(pub_threads<POLLER>()) void wq_pack_pub_kernel(
+    const T* __restrict__ W, int64_t total4, uint64_t* __restrict__ gate, const float* __restrict__ nodes,
+    int64_t N, int64_t K, float* __restrict__ gamma, uint8_t* __restrict__ out,
+    uint32_t* __restrict__ count_partial = nullptr) {
+    const int64_t g0 = (int64_t)blockIdx.x * (256 * U);
+    __shared__ float pub_thr;
+    __shared__ int pub_ok;
+    uint4 raw[U];
+    float thr = 0.0f;
+    if constexpr (POLLER) {
+        const bool loader = threadIdx.x < 256;  // uniform in each wave
+        if (loader) {
+            load_groups<T, U, 256>(W, g0, total4, threadIdx.x, raw);
+        } else {
+            float g;
+            bool ok = false;
+            if (blockIdx.x == 0) {
+                gamma_and_thr<1>(nodes, (N + 3) / 4, N, K, nullptr, g, thr);
+                if (threadIdx.x == 256) {
+                    gamma[0] = g;
+                    __hip_atomic_store(gate, ((uint64_t)1 << 32) | __float_as_uint(thr), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+                ok = true;
+            } else {
+                for (int i = 0; i < kGatePolls; ++i) {
+                    // every lane reads the same word: the wave's decision is uniform
+                    const uint64_t word = __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if ((uint32_t)(word >> 32) == 1u) {
+                        ok = true;
+                        thr = __uint_as_float((uint32_t)word);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            if (!ok) gamma_and_thr<1>(nodes, (N + 3) / 4, N, K, nullptr, g, thr);
+            if (threadIdx.x == 256) pub_thr = thr;
+        }
+        __syncthreads();
+        thr = pub_thr;
+    } else {
+        __shared__ float part[4];
+        load_groups<T, U, 256>(W, g0, total4, threadIdx.x, raw);
+        if (blockIdx.x == 0) {  // uniform
+            float g;
+            gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
+            if (threadIdx.x == 0) {
+                gamma[0] = g;
+                __hip_atomic_store(gate, ((uint64_t)1 << 32) | __float_as_uint(thr), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            if (threadIdx.x == 0) {
+                int ok = 0;
+                float t = 0.0f;
+                for (int i = 0; i < kGatePolls; ++i) {
+                    const uint64_t word = __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if ((uint32_t)(word >> 32) == 1u) {
+                        ok = 1;
+                        t = __uint_as_float((uint32_t)word);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                pub_ok = ok;
+                pub_thr = t;
+            }
+            __syncthreads();
+            if (pub_ok) {  // uniform: one LDS value for the workgroup
+                thr = pub_thr;
+            } else {
+                float g;
+                gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
+            }
+        }
+    }
+    uint32_t cnt = 0u;
+    if (threadIdx.x < 256) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = g0 + threadIdx.x + u * 256;
+            if (i < total4) pack_group<T, COUNT>(raw[u], thr, i, out, cnt);
+        }
+    }
+    store_group_counts<COUNT, 4>(cnt, count_partial);
 }
 
 // ===================================================== per-row weight quant
@@ -984,18 +1084,33 @@ static hipError_t weight_quant_pack(const void* W, bool w_bf16, int64_t N, int64
     const float* nodes = ws_nodes(ws, N);
     const int64_t total4 = N * K / 4;
     const unsigned g3 = (unsigned)((total4 + 256 * kPackU - 1) / (256 * kPackU));
-    const unsigned g3p = (unsigned)((total4 + 256 * kPackUPub - 1) / (256 * kPackUPub));
+    const bool fused = N * (int64_t)g3 <= kFusedGammaMaxWork;
+    // the fifth-wave reader when one round of resident workgroups covers the matrix
+    const int up5 = w_bf16 ? pack_u_pub<uint16_t, true>() : pack_u_pub<float, true>();
+    const int64_t g5 = (total4 + 256 * up5 - 1) / (256 * up5);
+    int dev = 0, cus = 0;
+    hipError_t e = hipSuccess;
+    if (!fused) {
+        e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
+    const bool poller = g5 <= (int64_t)kPollerGroupsPerCu * cus;
+    const int up = poller ? up5 : pack_u_pub<float, false>();
+    const unsigned g3p = (unsigned)((total4 + 256 * up - 1) / (256 * up));
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
     const float* Wf = static_cast<const float*>(W);
-    const bool fused = N * (int64_t)g3 <= kFusedGammaMaxWork;
 #define BITNET_PACK(T_, W_, C_)                                                                              \
     do {                                                                                                     \
         if (fused)                                                                                           \
-            wq_pack_kernel<T_, true, kPackU, C_><<<g3, 256, 0, s>>>(W_, total4, gate, nodes, N, K, gamma,     \
-                                                                     W_packed, count_partial);               \
+            wq_pack_kernel<T_, kPackU, C_><<<g3, 256, 0, s>>>(W_, total4, nodes, N, K, gamma, W_packed,        \
+                                                               count_partial);                               \
+        else if (poller)                                                                                     \
+            wq_pack_pub_kernel<T_, pack_u_pub<T_, true>(), true, C_><<<g3p, pub_threads<true>(), 0, s>>>(     \
+                W_, total4, gate, nodes, N, K, gamma, W_packed, count_partial);                              \
         else                                                                                                 \
-            wq_pack_kernel<T_, false, kPackUPub, C_><<<g3p, 256, 0, s>>>(W_, total4, gate, nodes, N, K, gamma, \
-                                                                           W_packed, count_partial);         \
+            wq_pack_pub_kernel<T_, pack_u_pub<T_, false>(), false, C_><<<g3p, pub_threads<false>(), 0, s>>>(  \
+                W_, total4, gate, nodes, N, K, gamma, W_packed, count_partial);                              \
     } while (0)
     if (counts) {
         if (w_bf16) BITNET_PACK(uint16_t, Wb, true);
@@ -1005,7 +1120,7 @@ static hipError_t weight_quant_pack(const void* W, bool w_bf16, int64_t N, int64
         else BITNET_PACK(float, Wf, false);
     }
 #undef BITNET_PACK
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess || !counts) return e;
     counted_final_kernel<<<1, kCountedFinalThreads, 0, s>>>(reinterpret_cast<const uint2*>(count_partial),
                                                             fused ? g3 : g3p, N * K,
