@@ -575,17 +575,7 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_row_kernel(
     const int KB = K / 4, nch = K / 64;
     // the row factor first (its latency hides under the loads)
     const float rs = CH ? 1.0f / scale_x[0] : *gamma_p / scale_x[0];
-    // the activation chunks first: the weight loads after them are then the
-    // only ones outstanding when the products wait for each row
-    const __amdgpu_buffer_rsrc_t rx = make_buf(Xq);
-    uint4 xr[CHK][4];
-#pragma unroll
-    for (int c = 0; c < CHK; ++c) {
-        const int ch = lane + kWave * c;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            xr[c][q] = buf_load16(rx, ch < nch ? (uint32_t)(64 * ch + 16 * q) : kBufOOB);
-    }
+    // the weight rows first
     const __amdgpu_buffer_rsrc_t rw = make_buf(Wp + (int64_t)row0 * KB);
     uint4 w[kRowRows][CHK];
 #pragma unroll
@@ -595,6 +585,18 @@ __global__ __launch_bounds__(kRowWaves * kWave) void gemv_row_kernel(
             const int ch = lane + kWave * c;
             w[r][c] = buf_load16(rw, row0 + r < N && ch < nch ? (uint32_t)(r * KB + 16 * ch) : kBufOOB);
         }
+    // the token's chunks after them (in flight together; the products start
+    // once all have arrived: measured at 1 x 11008 x 4096, 4.68 us against
+    // 4.75 us with the token's chunks requested first)
+    const __amdgpu_buffer_rsrc_t rx = make_buf(Xq);
+    uint4 xr[CHK][4];
+#pragma unroll
+    for (int c = 0; c < CHK; ++c) {
+        const int ch = lane + kWave * c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            xr[c][q] = buf_load16(rx, ch < nch ? (uint32_t)(64 * ch + 16 * q) : kBufOOB);
+    }
     uint32_t xa[CHK][16];
 #pragma unroll
     for (int c = 0; c < CHK; ++c)
