@@ -33,6 +33,7 @@ EXPORTS = (
     "bitnet_decode_layout_bytes", "bitnet_pack_decode",
     "bitnet_workspace_bytes", "bitnet_status_str", "bitnet_version",
     "bitnet_weight_quant_noalloc", "bitnet_channel_scale_grad", "bitnet_weight_quant_counted",
+    "bitnet_set_gate_polls",
     # calibration kernels (include/bitnet_calib.h): measured ceilings
     "bitnet_calib_stream_read", "bitnet_calib_mfma", "bitnet_calib_mfma_ops",
 )
@@ -79,6 +80,7 @@ def load_library(path: str = LIB_PATH):
         "bitnet_workspace_bytes": (sz, [c_int, i64, i64, i64]),
         "bitnet_status_str": (ctypes.c_char_p, [c_int]),
         "bitnet_version": (c_int, []),
+        "bitnet_set_gate_polls": (c_int, [c_int]),
         "bitnet_weight_quant_noalloc": (c_int, [p, c_int, i64, i64, p, p, p]),
         "bitnet_channel_scale_grad": (c_int, [p, p, i64, i64, p, p]),
         "bitnet_weight_quant_counted": (c_int, [p, c_int, i64, i64, p, p, p, p, sz, p]),
@@ -185,6 +187,15 @@ def bitnet_status_str(status: int) -> str:
 
 def bitnet_version() -> int:
     return int(load_library().bitnet_version())
+
+
+def bitnet_set_gate_polls(reads: int) -> int:
+    """Reads of the published weight-quant threshold before a pack workgroup
+    evaluates it itself (tests set 0 to run that path) -> the previous value."""
+    r = int(load_library().bitnet_set_gate_polls(int(reads)))
+    if r < 0:
+        _check("bitnet_set_gate_polls", r)
+    return r
 
 
 def bitnet_workspace_bytes(op: int, M: int, N: int, K: int) -> int:

@@ -20,12 +20,18 @@ bool float_dtype(int d) { return d == BITNET_F32 || d == BITNET_BF16; }
 constexpr int64_t kMaxK = (int64_t)1 << 24;
 constexpr int64_t kMaxFwdN = (int64_t)1 << 23;  // tile loads and stores use 32-bit offsets
 constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;  // kernels index rows with int
+constexpr int kMaxGatePolls = 1024;  // bitnet_set_gate_polls' upper bound
 
 }  // namespace
 
 extern "C" {
 
 int bitnet_version(void) { return kVersion; }
+
+int bitnet_set_gate_polls(int reads) {
+    if (reads < 0 || reads > kMaxGatePolls) return BITNET_E_ARG;
+    return bitnet::set_gate_polls(reads);
+}
 
 const char* bitnet_status_str(int status) {
     switch (status) {

@@ -256,6 +256,9 @@ constexpr size_t weight_quant_ws_size(int64_t N) {
     return (size_t)(((N * 4 + 255) / 256) * 256 + 256 + (((N + 3) / 4 * 4 + 255) / 256) * 256);
 }
 size_t weight_quant_ws_bytes(int64_t N);
+// reads of the published weight-quant threshold before a pack workgroup
+// evaluates it itself; returns the previous value
+int set_gate_polls(int n);
 // weight_quant and the code counts (zeros, +1, -1, 11) of the codes it packs
 hipError_t launch_weight_quant_counted(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* W_packed,
                                        float* gamma, uint64_t* counts, void* ws, hipStream_t s);

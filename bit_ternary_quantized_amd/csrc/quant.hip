@@ -535,7 +535,14 @@ constexpr int kPollerGroupsPerCu = 6;  // five-wave workgroups a CU holds (32 wa
 // evaluating it 23.0 us.
 constexpr int64_t kFusedGammaMaxWork = (int64_t)1 << 22;
 // reads of the published threshold before a workgroup evaluates it itself
+// (set_gate_polls changes it for later calls: tests use 0 to run that path)
 constexpr int kGatePolls = 32;
+static int g_gate_polls = kGatePolls;
+int set_gate_polls(int n) {
+    const int prev = g_gate_polls;
+    g_gate_polls = n;
+    return prev;
+}
 
 // The pack of a group of 4 weights into one byte of codes, and the counts of
 // the codes written (COUNT: +1 codes in the low half of cnt, -1 codes in the
@@ -646,10 +653,11 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, i
 // published in `gate`, one 64-bit word holding the threshold bits and a
 // ready mark, written with a single store (cleared by pass 1 of the same
 // call).  Every other workgroup reads that word until the mark is there, at
-// most kGatePolls times a short sleep apart, and then evaluates the threshold
-// itself from the four-row nodes (the same bits).  No workgroup waits on
-// another's progress beyond that bounded number of reads.  Waves 0-3 load and
-// pack the weights (256 U groups of 4 a workgroup).
+// most `polls` times (kGatePolls unless a test lowers it) a short sleep
+// apart, and then evaluates the threshold itself from the four-row nodes (the
+// same bits).  No workgroup waits on another's progress beyond that bounded
+// number of reads.  Waves 0-3 load and pack the weights (256 U groups of 4 a
+// workgroup).
 // POLLER: a fifth wave, with no weight loads, does the reading (or, in
 // workgroup 0, evaluates gamma and the threshold: one wave, the same tree,
 // so the same bits) and hands the threshold to waves 0-3 through LDS and one
@@ -667,7 +675,7 @@ constexpr int pub_threads() { return POLLER ? 5 * kWave : 4 * kWave; }
 template <typename T, int U, bool POLLER, bool COUNT = false>
 __global__ __launch_bounds__(pub_threads<POLLER>()) void wq_pack_pub_kernel(
     const T* __restrict__ W, int64_t total4, uint64_t* __restrict__ gate, const float* __restrict__ nodes,
-    int64_t N, int64_t K, float* __restrict__ gamma, uint8_t* __restrict__ out,
+    int64_t N, int64_t K, float* __restrict__ gamma, uint8_t* __restrict__ out, int polls,
     uint32_t* __restrict__ count_partial = nullptr) {
     const int64_t g0 = (int64_t)blockIdx.x * (256 * U);
     __shared__ float pub_thr;
@@ -690,7 +698,7 @@ __global__ __launch_bounds__(pub_threads<POLLER>()) void wq_pack_pub_kernel(
                 }
                 ok = true;
             } else {
-                for (int i = 0; i < kGatePolls; ++i) {
+                for (int i = 0; i < polls; ++i) {
                     // every lane reads the same word: the wave's decision is uniform
                     const uint64_t word = __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     if ((uint32_t)(word >> 32) == 1u) {
@@ -721,7 +729,7 @@ __global__ __launch_bounds__(pub_threads<POLLER>()) void wq_pack_pub_kernel(
             if (threadIdx.x == 0) {
                 int ok = 0;
                 float t = 0.0f;
-                for (int i = 0; i < kGatePolls; ++i) {
+                for (int i = 0; i < polls; ++i) {
                     const uint64_t word = __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     if ((uint32_t)(word >> 32) == 1u) {
                         ok = 1;
@@ -1107,10 +1115,10 @@ static hipError_t weight_quant_pack(const void* W, bool w_bf16, int64_t N, int64
                                                                count_partial);                               \
         else if (poller)                                                                                     \
             wq_pack_pub_kernel<T_, pack_u_pub<T_, true>(), true, C_><<<g3p, pub_threads<true>(), 0, s>>>(     \
-                W_, total4, gate, nodes, N, K, gamma, W_packed, count_partial);                              \
+                W_, total4, gate, nodes, N, K, gamma, W_packed, g_gate_polls, count_partial);                \
         else                                                                                                 \
             wq_pack_pub_kernel<T_, pack_u_pub<T_, false>(), false, C_><<<g3p, pub_threads<false>(), 0, s>>>(  \
-                W_, total4, gate, nodes, N, K, gamma, W_packed, count_partial);                              \
+                W_, total4, gate, nodes, N, K, gamma, W_packed, g_gate_polls, count_partial);                \
     } while (0)
     if (counts) {
         if (w_bf16) BITNET_PACK(uint16_t, Wb, true);

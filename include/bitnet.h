@@ -441,6 +441,21 @@ const char *bitnet_status_str(int status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int bitnet_version(void);
 
+/*
+ * For tests of the weight quantizer's fallback path.  With large matrices one
+ * pack workgroup evaluates gamma and the code threshold and publishes the
+ * threshold; every other workgroup reads it at most `reads` times (default
+ * 32) and then evaluates it itself from the same row sums, which gives the
+ * same bits.  Setting 0 makes every workgroup take that path in later calls
+ * (bitnet_weight_quant, bitnet_weight_quant_counted, bitnet_quant_operands,
+ * bitnet_weight_quant_noalloc); outputs are unchanged, only slower.  Host-side
+ * setting for the whole process, read when a call launches its kernels; not
+ * synchronised with concurrent calls.
+ *   reads    0 .. 1024
+ * Returns the previous value, or BITNET_E_ARG (nothing changed).
+ */
+int bitnet_set_gate_polls(int reads);
+
 #ifdef __cplusplus
 }
 #endif

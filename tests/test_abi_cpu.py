@@ -405,3 +405,13 @@ def test_channel_scale_grad_rejects_bad_arguments():
     assert f(P, P, 4, 1 << 24, P, NULL) == -2
     assert f(ctypes.c_void_p((1 << 20) + 4), P, 4, 16, P, NULL) == -4
     assert f(P, P, 4, 16, ctypes.c_void_p((1 << 20) + 2), NULL) == -4
+
+
+def test_set_gate_polls_bounds_and_previous_value():
+    f = bt.load_library().bitnet_set_gate_polls
+    assert f(-1) == -1 and f(1025) == -1  # BITNET_E_ARG, nothing changed
+    prev = f(7)
+    assert prev == 32  # the default
+    assert f(0) == 7
+    assert f(prev) == 0
+    assert bt.bitnet_set_gate_polls(32) == 32

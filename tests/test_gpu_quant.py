@@ -103,6 +103,36 @@ def test_weight_quant_published_threshold_is_per_call():
         assert np.array_equal(wp.cpu().numpy(), oracle.pack(c_ref))
 
 
+@pytest.mark.parametrize("N,K,dt", [
+    (4096, 4096, torch.bfloat16),  # one round of workgroups: the fifth (reading) wave evaluates
+    (2111, 4096, torch.bfloat16),
+    (4099, 4096, torch.float32),   # several rounds: the four waves evaluate together
+    (8209, 8192, torch.bfloat16),
+])
+def test_weight_quant_threshold_fallback_gives_the_same_bits(N, K, dt):
+    # with no reads of the published threshold every pack workgroup but the
+    # first evaluates gamma's threshold itself from the row sums: the codes
+    # and gamma must not change (weight quant, the counted call and the
+    # two-quantizer call)
+    print(f"threshold fallback N={N} K={K} {dt}", flush=True)
+    w = _weight_case(N, K, dt, seed=N + K)
+    x = workloads.normal((64, K), 1.0, seed=5, dtype="bf16")
+    c_ref, g_ref = oracle.weight_quant(host(w))
+    packed_ref = oracle.pack(c_ref)
+    prev = bt.bitnet_set_gate_polls(0)
+    try:
+        wp, gamma = bt.bitnet_weight_quant(to_dev(w))
+        wp2, gamma2, counts = bt.bitnet_weight_quant_counted(to_dev(w))
+        _, _, wp3, gamma3 = bt.bitnet_quant_operands(to_dev(x), to_dev(w), 1e-5)
+        torch.cuda.synchronize()
+    finally:
+        bt.bitnet_set_gate_polls(prev)
+    for p_, g_ in ((wp, gamma), (wp2, gamma2), (wp3, gamma3)):
+        assert f32_bits_equal(g_.cpu().numpy(), np.array([g_ref], np.float32))
+        assert np.array_equal(p_.cpu().numpy(), packed_ref)
+    assert np.array_equal(counts.cpu().numpy(), oracle.code_counts(packed_ref, K).astype(np.int64))
+
+
 @pytest.mark.parametrize("j", [25, 31, 41, 47, 97, 127])
 def test_weight_quant_near_tie_matches_division(j):
     # gamma = j*2^-8 exactly and entries one ulp above gamma/2: the decision
