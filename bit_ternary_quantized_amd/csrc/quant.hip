@@ -373,8 +373,11 @@ __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int
                                                     float* __restrict__ quad_sums,
                                                     uint64_t* __restrict__ gate,
                                                     float* __restrict__ row_gamma = nullptr,
-                                                    float* __restrict__ row_thr = nullptr) {
+                                                    float* __restrict__ row_thr = nullptr,
+                                                    uint64_t* __restrict__ counts_clear = nullptr) {
     if (gate && bid == 0 && threadIdx.x == 0) *gate = 0;
+    // the counted call's four counts, added into by its last launch
+    if (counts_clear && bid == 0 && threadIdx.x < 4) counts_clear[threadIdx.x] = 0;
     constexpr int E = Vec16<T>::E;
     constexpr int BLK = kWave * E;
     constexpr int G = 8;  // loads in flight per lane
@@ -445,8 +448,9 @@ __device__ __forceinline__ void wq_row_abs_sum_body(const T* __restrict__ W, int
 template <typename T>
 __global__ __launch_bounds__(kWqWaves * kWave) void wq_row_abs_sum_kernel(
     const T* __restrict__ W, int64_t N, int64_t K, float* __restrict__ row_sums, float* __restrict__ quad_sums,
-    uint64_t* __restrict__ gate, float* __restrict__ row_gamma, float* __restrict__ row_thr) {
-    wq_row_abs_sum_body<T>(W, N, K, row_sums, blockIdx.x, quad_sums, gate, row_gamma, row_thr);
+    uint64_t* __restrict__ gate, float* __restrict__ row_gamma, float* __restrict__ row_thr,
+    uint64_t* __restrict__ counts_clear = nullptr) {
+    wq_row_abs_sum_body<T>(W, N, K, row_sums, blockIdx.x, quad_sums, gate, row_gamma, row_thr, counts_clear);
 }
 
 // Pass 2: the tree over the n = ceil(N/4) four-row nodes of pass 1 (the
@@ -604,15 +608,30 @@ __device__ __forceinline__ void load_groups(const T* __restrict__ W, int64_t g0,
 // (Device-scope atomics into shared slots instead were measured slower: at
 // 4096 x 4096 bf16 the counting pack took 12.2 us with one set of atomics per
 // workgroup, 13.8 us with one per wave, against 11.6 us with stores.)
-// counted_final_kernel then adds the pairs: the monitoring counts without a
+// counted_sum_kernel then adds the pairs: the monitoring counts without a
 // second read of the packed weights.
 static_assert(256 * 4 * 16 < 65536, "per-workgroup code counts fit 16 bits");
+// sum over the 64 lanes (every lane active) with row moves, returned to
+// every lane (integers: exact in any order).  (Lane exchanges through
+// ds_bpermute instead: the counting pack at 28672 x 8192 fp32 took 184 us,
+// the plain one 173.5 us.)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+    v += dpp_u32<kDppXor1>(v);
+    v += dpp_u32<kDppXor2>(v);
+    v += dpp_u32<kDppHalfMirror>(v);
+    v += dpp_u32<kDppMirror>(v);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
 template <bool COUNT, int NW>
 __device__ __forceinline__ void store_group_counts(uint32_t cnt, uint32_t* __restrict__ count_partial) {
     if constexpr (COUNT) {
         __shared__ uint32_t red[NW];
-#pragma unroll
-        for (int m = 1; m < kWave; m *= 2) cnt += __shfl_xor(cnt, m, kWave);
+        cnt = wave_sum_u32(cnt);
         if ((threadIdx.x & (kWave - 1)) == 0 && (threadIdx.x >> 6) < NW) red[threadIdx.x >> 6] = cnt;
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -958,56 +977,55 @@ hipError_t launch_code_counts(const uint8_t* W_packed, int64_t nbytes, uint64_t*
 }
 
 // The counted weight quant's last step: adds the (+1, -1) pairs of the pack
-// workgroups (`groups` pairs of uint32) and writes the four counts.  Every
-// code that pack writes is 00, 01 or 10, so the zeros are the matrix's
-// `codes` minus the nonzero ones and the pattern 11 count is 0.  256
-// threads; each pass requests 16 pairs per thread at once through a buffer
-// descriptor at the pass's first pair (past `groups` an out-of-range offset
-// reads zeros): one pass up to 4096 x 4096 weights.  (1024 threads x 8 pairs
-// measured 3.8 us at 2048 pairs, against 2.4 us for the 256-thread sum of
-// code_counts.)
-constexpr int kCountedFinalThreads = 256;
-constexpr int kCountedFinalPairs = 16;  // pairs per thread and pass
+// workgroups (`pairs` pairs of uint32, pair p from the pack workgroup that
+// wrote groups of 4 weights [p * gpw, (p + 1) * gpw) of `total4`) into the
+// four counts, which pass 1 of the same call zeroed.  One pass: workgroup b
+// adds pairs [4096 b, 4096 b + 4096), each thread 16 of them requested at
+// once through a buffer descriptor (past `pairs` an out-of-range offset
+// reads zeros), and thread 0 adds the workgroup's +1, -1 and zero counts
+// into counts[1], [2], [0] with 64-bit integer atomics (exact in any order).
+// Every code that pack writes is 00, 01 or 10, so a workgroup's zeros are the
+// codes its pairs cover minus their nonzero ones, and counts[3] (pattern 11)
+// stays 0.  (One workgroup in dependent passes instead: 7.5 us for the 57344
+// pairs of 28672 x 8192 fp32.)
+constexpr int kCountedPairsPerThread = 16;
+constexpr int kCountedPairsPerGroup = 256 * kCountedPairsPerThread;
 
-__global__ __launch_bounds__(kCountedFinalThreads) void counted_final_kernel(
-    const uint2* __restrict__ partial, int64_t groups, int64_t codes, unsigned long long* __restrict__ counts) {
-    constexpr int kPass = kCountedFinalThreads * kCountedFinalPairs;
-    unsigned long long plus = 0ull, minus = 0ull;
-    for (int64_t p0 = 0; p0 < groups; p0 += kPass) {
-        const __amdgpu_buffer_rsrc_t rp = make_buf(partial + p0);
-        uint2 v[kCountedFinalPairs];
+__global__ __launch_bounds__(256) void counted_sum_kernel(const uint2* __restrict__ partial, int64_t pairs,
+                                                          int64_t gpw, int64_t total4,
+                                                          unsigned long long* __restrict__ counts) {
+    const int64_t p0 = (int64_t)blockIdx.x * kCountedPairsPerGroup;
+    const __amdgpu_buffer_rsrc_t rp = make_buf(partial + p0);
+    uint2 v[kCountedPairsPerThread];
 #pragma unroll
-        for (int r = 0; r < kCountedFinalPairs; ++r) {
-            const int b = threadIdx.x + kCountedFinalThreads * r;
-            v[r] = buf_load8(rp, p0 + b < groups ? (uint32_t)b * 8u : kBufOOB);
-        }
-#pragma unroll
-        for (int r = 0; r < kCountedFinalPairs; ++r) {
-            plus += v[r].x;
-            minus += v[r].y;
-        }
+    for (int r = 0; r < kCountedPairsPerThread; ++r) {
+        const int b = threadIdx.x + 256 * r;
+        v[r] = buf_load8(rp, p0 + b < pairs ? (uint32_t)b * 8u : kBufOOB);
     }
+    // at most 4096 pairs of at most 16384 codes: 2^26, inside 32 bits
+    uint32_t plus = 0u, minus = 0u;
 #pragma unroll
-    for (int m = 1; m < kWave; m *= 2) {
-        plus += __shfl_xor(plus, m, kWave);
-        minus += __shfl_xor(minus, m, kWave);
+    for (int r = 0; r < kCountedPairsPerThread; ++r) {
+        plus += v[r].x;
+        minus += v[r].y;
     }
-    __shared__ unsigned long long red[kCountedFinalThreads / kWave][2];
+    plus = wave_sum_u32(plus);
+    minus = wave_sum_u32(minus);
+    __shared__ uint32_t red[4][2];
     if ((threadIdx.x & (kWave - 1)) == 0) {
-        red[threadIdx.x / kWave][0] = plus;
-        red[threadIdx.x / kWave][1] = minus;
+        red[threadIdx.x >> 6][0] = plus;
+        red[threadIdx.x >> 6][1] = minus;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        unsigned long long p = 0ull, m = 0ull;
-        for (int w = 0; w < kCountedFinalThreads / kWave; ++w) {
-            p += red[w][0];
-            m += red[w][1];
-        }
-        counts[0] = (unsigned long long)codes - p - m;
-        counts[1] = p;
-        counts[2] = m;
-        counts[3] = 0ull;
+        const unsigned long long p = (unsigned long long)red[0][0] + red[1][0] + red[2][0] + red[3][0];
+        const unsigned long long m = (unsigned long long)red[0][1] + red[1][1] + red[2][1] + red[3][1];
+        const int64_t p1 = p0 + kCountedPairsPerGroup < pairs ? p0 + kCountedPairsPerGroup : pairs;
+        const int64_t g_end = p1 * gpw < total4 ? p1 * gpw : total4;
+        const unsigned long long codes = 4ull * (unsigned long long)(g_end - p0 * gpw);
+        atomicAdd(&counts[0], codes - p - m);
+        atomicAdd(&counts[1], p);
+        atomicAdd(&counts[2], m);
     }
 }
 
@@ -1130,9 +1148,11 @@ static hipError_t weight_quant_pack(const void* W, bool w_bf16, int64_t N, int64
 #undef BITNET_PACK
     e = hipGetLastError();
     if (e != hipSuccess || !counts) return e;
-    counted_final_kernel<<<1, kCountedFinalThreads, 0, s>>>(reinterpret_cast<const uint2*>(count_partial),
-                                                            fused ? g3 : g3p, N * K,
-                                                            reinterpret_cast<unsigned long long*>(counts));
+    const int64_t pairs = fused ? g3 : g3p;
+    const int64_t gpw = 256 * (int64_t)(fused ? kPackU : up);  // groups of 4 weights a pack workgroup
+    counted_sum_kernel<<<(unsigned)((pairs + kCountedPairsPerGroup - 1) / kCountedPairsPerGroup), 256, 0, s>>>(
+        reinterpret_cast<const uint2*>(count_partial), pairs, gpw, total4,
+        reinterpret_cast<unsigned long long*>(counts));
     return hipGetLastError();
 }
 
@@ -1173,10 +1193,10 @@ hipError_t launch_weight_quant_counted(const void* W, bool w_bf16, int64_t N, in
     const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
     if (w_bf16)
         wq_row_abs_sum_kernel<uint16_t><<<g1, b1, 0, s>>>(static_cast<const uint16_t*>(W), N, K,
-                                                           row_sums, nodes, gate, nullptr, nullptr);
+                                                           row_sums, nodes, gate, nullptr, nullptr, counts);
     else
         wq_row_abs_sum_kernel<float><<<g1, b1, 0, s>>>(static_cast<const float*>(W), N, K,
-                                                        row_sums, nodes, gate, nullptr, nullptr);
+                                                        row_sums, nodes, gate, nullptr, nullptr, counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s, counts, slots);

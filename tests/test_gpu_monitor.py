@@ -51,10 +51,11 @@ def test_code_counts_decode_layer():
 # codes and gamma as the oracle, the counts of those codes; small matrices
 # (gamma in every pack workgroup) and large ones (gamma published by one)
 @pytest.mark.parametrize("N,K,dt", [(1, 4, "f32"), (37, 100, "bf16"), (1376, 512, "f32"), (2111, 4096, "bf16"),
-                                    (4099, 1024, "f32"), (8209, 8192, "bf16")])
+                                    (4099, 1024, "f32"), (8209, 8192, "bf16"), (16411, 8192, "bf16")])
 def test_weight_quant_counted(N, K, dt):
-    # the last case has more pack workgroups (8209) than the final sum takes
-    # in one pass (4096): three passes
+    # the last two cases have more pack workgroups (8209, 16411) than the
+    # 256-thread final sum takes in one pass (4096): the 1024-thread sum, in
+    # one pass and in two (16384 a pass)
     print(f"weight_quant_counted N={N} K={K} {dt}", flush=True)
     w = workloads.normal((N, K), 0.02, seed=3 * N + K, dtype=dt)
     wp, g, c = bt.bitnet_weight_quant_counted(to_dev(w))
