@@ -907,10 +907,7 @@ __global__ __launch_bounds__(256) void code_counts_kernel(const uint8_t* __restr
     // the four sums: each wave adds its lanes, one barrier, four threads add
     // the four waves
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int m = 1; m < kWave; m *= 2) c[j] += __shfl_xor(c[j], m, kWave);
-    }
+    for (int j = 0; j < 4; ++j) c[j] = wave_sum_u32(c[j]);
     if ((threadIdx.x & (kWave - 1)) == 0)
 #pragma unroll
         for (int j = 0; j < 4; ++j) red[j][threadIdx.x >> 6] = c[j];
