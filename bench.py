@@ -350,7 +350,7 @@ def layer_counts(M, N, K, x_bytes, w_bytes, gy):
 
 KERNEL_OF = {
     "act_quant": "act_quant_rows_kernel (rows of whole 16-byte blocks), else act_quant_kernel",
-    "weight_quant": "wq_row_abs_sum_kernel + wq_pack_kernel (gamma in the pack launch)",
+    "weight_quant": "wq_row_abs_sum_kernel + wq_pack_kernel / wq_pack_pub_kernel (gamma in the pack launch)",
     "linear_fwd": "gemm_i8t2_kernel",
     "bwd_grad_x": "bwd_kernel<grad_x>",
     "bwd_grad_W": "bwd_kernel<grad_W> (+ split_reduce_kernel when split)",
@@ -358,8 +358,8 @@ KERNEL_OF = {
     "bwd_grad_W_gated": "bwd_kernel<grad_W> with the range gate (+ split_reduce_kernel when split)",
     "weight_clamp": "weight_clamp_kernel",
     "code_counts": "code_counts_kernel + code_counts_final_kernel",
-    "weight_quant_counted": "wq_row_abs_sum_kernel + wq_pack_kernel (counting) + code_counts_final_kernel",
-    "quant_operands": "quant_operands_kernel + wq_pack_kernel",
+    "weight_quant_counted": "wq_row_abs_sum_kernel + the counting pack + counted_sum_kernel",
+    "quant_operands": "quant_operands_kernel + wq_pack_kernel / wq_pack_pub_kernel",
     "weight_quant_rows": "wq_row_abs_sum_kernel (with the row gammas) + wq_pack_rows_kernel",
     "linear_fwd_channel": "gemm_i8t2_kernel (per-channel epilogue) or gemv_t2_kernel",
     "bwd_grad_x_channel": "bwd_kernel<grad_x> (per-channel code scales)",
