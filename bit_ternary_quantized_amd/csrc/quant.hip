@@ -628,7 +628,8 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
            (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 template <bool COUNT, int NW>
-__device__ __forceinline__ void store_group_counts(uint32_t cnt, uint32_t* __restrict__ count_partial) {
+__device__ __forceinline__ void store_group_counts(uint32_t cnt, uint32_t* __restrict__ count_partial,
+                                                   int slot) {
     if constexpr (COUNT) {
         __shared__ uint32_t red[NW];
         cnt = wave_sum_u32(cnt);
@@ -638,7 +639,7 @@ __device__ __forceinline__ void store_group_counts(uint32_t cnt, uint32_t* __res
             uint32_t t = 0;
 #pragma unroll
             for (int w = 0; w < NW; ++w) t += red[w];
-            reinterpret_cast<uint2*>(count_partial)[blockIdx.x] = make_uint2(t & 0xffffu, t >> 16);
+            reinterpret_cast<uint2*>(count_partial)[slot] = make_uint2(t & 0xffffu, t >> 16);
         }
     }
 }
@@ -646,26 +647,35 @@ __device__ __forceinline__ void store_group_counts(uint32_t cnt, uint32_t* __res
 // Small matrices: every workgroup computes gamma and the threshold from the
 // four-row nodes (its weight loads issued first, so the evaluation hides
 // under them); block 0 also writes gamma.
-template <typename T, int U, bool COUNT = false>
-__global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, int64_t total4,
-                                                      const float* __restrict__ nodes,
-                                                      int64_t N, int64_t K, float* __restrict__ gamma,
-                                                      uint8_t* __restrict__ out,
-                                                      uint32_t* __restrict__ count_partial = nullptr) {
-    const int64_t g0 = (int64_t)blockIdx.x * (256 * U);
+// (The pack bodies take their workgroup index `bid`, so that a launch can
+// also run other work on other workgroups.)
+template <typename T, int U, bool COUNT>
+__device__ __forceinline__ void wq_pack_body(const T* __restrict__ W, int64_t total4,
+                                             const float* __restrict__ nodes, int64_t N, int64_t K,
+                                             float* __restrict__ gamma, uint8_t* __restrict__ out,
+                                             uint32_t* __restrict__ count_partial, int bid) {
+    const int64_t g0 = (int64_t)bid * (256 * U);
     uint4 raw[U];
     load_groups<T, U, 256>(W, g0, total4, threadIdx.x, raw);
     float thr, g;
     __shared__ float part[4];
     gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
-    if (blockIdx.x == 0 && threadIdx.x == 0) gamma[0] = g;
+    if (bid == 0 && threadIdx.x == 0) gamma[0] = g;
     uint32_t cnt = 0u;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t i = g0 + threadIdx.x + u * 256;
         if (i < total4) pack_group<T, COUNT>(raw[u], thr, i, out, cnt);
     }
-    store_group_counts<COUNT, 4>(cnt, count_partial);
+    store_group_counts<COUNT, 4>(cnt, count_partial, bid);
+}
+template <typename T, int U, bool COUNT = false>
+__global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, int64_t total4,
+                                                      const float* __restrict__ nodes,
+                                                      int64_t N, int64_t K, float* __restrict__ gamma,
+                                                      uint8_t* __restrict__ out,
+                                                      uint32_t* __restrict__ count_partial = nullptr) {
+    wq_pack_body<T, U, COUNT>(W, total4, nodes, N, K, gamma, out, count_partial, blockIdx.x);
 }
 
 // Large matrices: the threshold is evaluated once, by workgroup 0, and
@@ -691,17 +701,73 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, i
 // after issuing its weight loads (workgroup 0: all four waves evaluate).
 template <bool POLLER>
 constexpr int pub_threads() { return POLLER ? 5 * kWave : 4 * kWave; }
+// The four-wave form, as a body of the workgroup index.
+template <typename T, int U, bool COUNT>
+__device__ __forceinline__ void wq_pack_pub4_body(const T* __restrict__ W, int64_t total4,
+                                                  uint64_t* __restrict__ gate, const float* __restrict__ nodes,
+                                                  int64_t N, int64_t K, float* __restrict__ gamma,
+                                                  uint8_t* __restrict__ out, int polls,
+                                                  uint32_t* __restrict__ count_partial, int bid) {
+    const int64_t g0 = (int64_t)bid * (256 * U);
+    __shared__ float pub_thr;
+    __shared__ int pub_ok;
+    __shared__ float part[4];
+    uint4 raw[U];
+    float thr = 0.0f;
+    load_groups<T, U, 256>(W, g0, total4, threadIdx.x, raw);
+    if (bid == 0) {  // uniform
+        float g;
+        gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
+        if (threadIdx.x == 0) {
+            gamma[0] = g;
+            __hip_atomic_store(gate, ((uint64_t)1 << 32) | __float_as_uint(thr), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        if (threadIdx.x == 0) {
+            int ok = 0;
+            float t = 0.0f;
+            for (int i = 0; i < polls; ++i) {
+                const uint64_t word = __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((uint32_t)(word >> 32) == 1u) {
+                    ok = 1;
+                    t = __uint_as_float((uint32_t)word);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            pub_ok = ok;
+            pub_thr = t;
+        }
+        __syncthreads();
+        if (pub_ok) {  // uniform: one LDS value for the workgroup
+            thr = pub_thr;
+        } else {
+            float g;
+            gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
+        }
+    }
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = g0 + threadIdx.x + u * 256;
+        if (i < total4) pack_group<T, COUNT>(raw[u], thr, i, out, cnt);
+    }
+    store_group_counts<COUNT, 4>(cnt, count_partial, bid);
+}
+
 template <typename T, int U, bool POLLER, bool COUNT = false>
 __global__ __launch_bounds__(pub_threads<POLLER>()) void wq_pack_pub_kernel(
     const T* __restrict__ W, int64_t total4, uint64_t* __restrict__ gate, const float* __restrict__ nodes,
     int64_t N, int64_t K, float* __restrict__ gamma, uint8_t* __restrict__ out, int polls,
     uint32_t* __restrict__ count_partial = nullptr) {
-    const int64_t g0 = (int64_t)blockIdx.x * (256 * U);
-    __shared__ float pub_thr;
-    __shared__ int pub_ok;
-    uint4 raw[U];
-    float thr = 0.0f;
-    if constexpr (POLLER) {
+    if constexpr (!POLLER) {
+        wq_pack_pub4_body<T, U, COUNT>(W, total4, gate, nodes, N, K, gamma, out, polls, count_partial, blockIdx.x);
+    } else {
+        const int64_t g0 = (int64_t)blockIdx.x * (256 * U);
+        __shared__ float pub_thr;
+        uint4 raw[U];
+        float thr = 0.0f;
         const bool loader = threadIdx.x < 256;  // uniform in each wave
         if (loader) {
             load_groups<T, U, 256>(W, g0, total4, threadIdx.x, raw);
@@ -733,51 +799,16 @@ __global__ __launch_bounds__(pub_threads<POLLER>()) void wq_pack_pub_kernel(
         }
         __syncthreads();
         thr = pub_thr;
-    } else {
-        __shared__ float part[4];
-        load_groups<T, U, 256>(W, g0, total4, threadIdx.x, raw);
-        if (blockIdx.x == 0) {  // uniform
-            float g;
-            gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
-            if (threadIdx.x == 0) {
-                gamma[0] = g;
-                __hip_atomic_store(gate, ((uint64_t)1 << 32) | __float_as_uint(thr), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-        } else {
-            if (threadIdx.x == 0) {
-                int ok = 0;
-                float t = 0.0f;
-                for (int i = 0; i < polls; ++i) {
-                    const uint64_t word = __hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if ((uint32_t)(word >> 32) == 1u) {
-                        ok = 1;
-                        t = __uint_as_float((uint32_t)word);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-                }
-                pub_ok = ok;
-                pub_thr = t;
-            }
-            __syncthreads();
-            if (pub_ok) {  // uniform: one LDS value for the workgroup
-                thr = pub_thr;
-            } else {
-                float g;
-                gamma_and_thr<4>(nodes, (N + 3) / 4, N, K, part, g, thr);
-            }
-        }
-    }
-    uint32_t cnt = 0u;
-    if (threadIdx.x < 256) {
+        uint32_t cnt = 0u;
+        if (threadIdx.x < 256) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = g0 + threadIdx.x + u * 256;
-            if (i < total4) pack_group<T, COUNT>(raw[u], thr, i, out, cnt);
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = g0 + threadIdx.x + u * 256;
+                if (i < total4) pack_group<T, COUNT>(raw[u], thr, i, out, cnt);
+            }
         }
+        store_group_counts<COUNT, 4>(cnt, count_partial, blockIdx.x);
     }
-    store_group_counts<COUNT, 4>(cnt, count_partial);
 }
 
 // ===================================================== per-row weight quant
@@ -1199,12 +1230,22 @@ hipError_t launch_weight_quant_counted(const void* W, bool w_bf16, int64_t N, in
     return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s, counts, slots);
 }
 
-// ============================================= both quantizers, one launch fewer
-// Launch 1 runs act_quant's row-walking kernel on workgroups [0, A) and the
-// weight row sums on [A, A + ceil(N/4)): two independent streams of HBM
-// reads in one grid, with no launch boundary between them.  Launch 2 is
-// weight_quant's pack (with gamma).  Same bodies, same
-// arithmetic: the outputs are bit-identical to the two separate calls.
+// ============================================ both quantizers, one launch fewer
+// Two launches either way, the activation stream beside one of the two
+// weight passes; same bodies, same arithmetic, so the outputs are
+// bit-identical to the two separate calls.
+//  - activation bytes >= weight bytes (prefill, small layers): launch 1 is
+//    weight_quant's pass 1 (row sums and nodes); launch 2 runs act_quant's
+//    row-walking body on workgroups [0, A) and the weight pack on [A, A + P),
+//    so the pack's second read of W streams beside the activations instead
+//    of alone, and gamma's nodes are complete before launch 2 starts.
+//    8192 x 4096 x 4096 bf16: 30.0 us against 32.3 us the other way; with
+//    the pack's workgroups first in the grid 34.1 us (they take every slot
+//    and the activation workgroups queue behind them).
+//  - otherwise (a weight matrix far larger than the activations): launch 1
+//    runs act_quant on [0, A) and the row sums on [A, A + ceil(N/4)); launch 2
+//    is weight_quant's pack.  4096 x 28672 x 8192 (fp32 W): 362 us against
+//    366 us the other way.
 template <typename TX, int NB, typename TW>
 __global__ __launch_bounds__(kAqWaves * kWave) void quant_operands_kernel(
     const TX* __restrict__ X, int64_t M, int64_t K, float eps, int8_t* __restrict__ Q, float* __restrict__ S,
@@ -1216,34 +1257,79 @@ __global__ __launch_bounds__(kAqWaves * kWave) void quant_operands_kernel(
     else wq_row_abs_sum_body<TW>(W, N, K, row_sums, b - act_blocks, nodes, gate);
 }
 
-namespace {
-template <typename TX, typename TW>
-hipError_t quant_operands_pass1(const TX* X, int64_t M, int64_t K, float eps, int8_t* Q, float* S, const TW* W,
-                                int64_t N, float* row_sums, float* nodes, uint64_t* gate, int nblk,
-                                hipStream_t s) {
-    const int64_t groups = (M + kAqWaves - 1) / kAqWaves;
-    const int act_blocks = (int)std::min<int64_t>(groups, kAqMaxGroups);
-    const int64_t wq_blocks = (N + kWqWaves - 1) / kWqWaves;
-    const dim3 grid((unsigned)(act_blocks + wq_blocks)), block(kAqWaves * kWave);
-    switch (nblk) {
-        case 1: quant_operands_kernel<TX, 1, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes, gate); break;
-        case 2: quant_operands_kernel<TX, 2, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes, gate); break;
-        case 4: quant_operands_kernel<TX, 4, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes, gate); break;
-        case 8: quant_operands_kernel<TX, 8, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes, gate); break;
-        case 16: quant_operands_kernel<TX, 16, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums, nodes, gate); break;
-        default: return hipErrorInvalidValue;
+template <typename TX, int NB, typename TW, bool FUSED>
+__global__ __launch_bounds__(kAqWaves * kWave) void act_pack_kernel(
+    const TX* __restrict__ X, int64_t M, int64_t K, float eps, int8_t* __restrict__ Q, float* __restrict__ S,
+    int act_blocks, const TW* __restrict__ W, int64_t total4, uint64_t* __restrict__ gate,
+    const float* __restrict__ nodes, int64_t N, float* __restrict__ gamma, uint8_t* __restrict__ out,
+    int pack_blocks, int polls) {
+    static_assert(kAqWaves == 4, "one workgroup shape for both bodies");
+    const int b = blockIdx.x;  // uniform
+    if (b < act_blocks) {
+        act_quant_rows_body<TX, NB>(X, M, K, eps, Q, S, b, act_blocks);
+    } else {
+        const int pb = b - act_blocks;
+        if constexpr (FUSED) wq_pack_body<TW, kPackU, false>(W, total4, nodes, N, K, gamma, out, nullptr, pb);
+        else wq_pack_pub4_body<TW, pack_u_pub<TW, false>(), false>(W, total4, gate, nodes, N, K, gamma, out,
+                                                                   polls, nullptr, pb);
     }
+}
+
+namespace {
+template <typename TX, typename TW, int NB>
+hipError_t act_pack_launch(const TX* X, int64_t M, int64_t K, float eps, int8_t* Q, float* S, const TW* W,
+                           int64_t N, uint8_t* W_packed, float* gamma, void* ws, hipStream_t s) {
+    float* row_sums = static_cast<float*>(ws);
+    float* nodes = ws_nodes(ws, N);
+    uint64_t* gate = ws_gate(ws, N);
+    const int act_blocks = (int)std::min<int64_t>((M + kAqWaves - 1) / kAqWaves, kAqMaxGroups);
+    if (M * K * (int64_t)sizeof(TX) < N * K * (int64_t)sizeof(TW)) {  // act_quant beside the row sums
+        const int64_t wq_blocks = (N + kWqWaves - 1) / kWqWaves;
+        const dim3 grid((unsigned)(act_blocks + wq_blocks)), block(kAqWaves * kWave);
+        quant_operands_kernel<TX, NB, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums,
+                                                                 nodes, gate);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return weight_quant_pack(W, sizeof(TW) == 2, N, K, W_packed, gamma, ws, s);
+    }
+    const dim3 g1((unsigned)((N + kWqWaves - 1) / kWqWaves)), b1(kWqWaves * kWave);
+    wq_row_abs_sum_kernel<TW><<<g1, b1, 0, s>>>(W, N, K, row_sums, nodes, gate, nullptr, nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total4 = N * K / 4;
+    const int64_t g3 = (total4 + 256 * kPackU - 1) / (256 * kPackU);
+    const bool fused = N * g3 <= kFusedGammaMaxWork;
+    constexpr int up = pack_u_pub<TW, false>();
+    const int pack_blocks = (int)(fused ? g3 : (total4 + 256 * up - 1) / (256 * up));
+    const dim3 grid((unsigned)(pack_blocks + act_blocks)), block(kAqWaves * kWave);
+    if (fused)
+        act_pack_kernel<TX, NB, TW, true><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, total4, gate,
+                                                                 nodes, N, gamma, W_packed, pack_blocks,
+                                                                 g_gate_polls);
+    else
+        act_pack_kernel<TX, NB, TW, false><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, total4, gate,
+                                                                  nodes, N, gamma, W_packed, pack_blocks,
+                                                                  g_gate_polls);
     return hipGetLastError();
 }
+template <typename TX, typename TW>
+hipError_t act_pack_nb(const TX* X, int64_t M, int64_t K, float eps, int8_t* Q, float* S, const TW* W, int64_t N,
+                       uint8_t* W_packed, float* gamma, void* ws, int nblk, hipStream_t s) {
+    switch (nblk) {
+        case 1: return act_pack_launch<TX, TW, 1>(X, M, K, eps, Q, S, W, N, W_packed, gamma, ws, s);
+        case 2: return act_pack_launch<TX, TW, 2>(X, M, K, eps, Q, S, W, N, W_packed, gamma, ws, s);
+        case 4: return act_pack_launch<TX, TW, 4>(X, M, K, eps, Q, S, W, N, W_packed, gamma, ws, s);
+        case 8: return act_pack_launch<TX, TW, 8>(X, M, K, eps, Q, S, W, N, W_packed, gamma, ws, s);
+        case 16: return act_pack_launch<TX, TW, 16>(X, M, K, eps, Q, S, W, N, W_packed, gamma, ws, s);
+        default: return hipErrorInvalidValue;
+    }
+}
 template <typename TX>
-hipError_t quant_operands_w(const TX* X, int64_t M, int64_t K, float eps, int8_t* Q, float* S, const void* W,
-                            bool w_bf16, int64_t N, float* row_sums, float* nodes, uint64_t* gate, int nblk,
-                            hipStream_t s) {
+hipError_t act_pack_w(const TX* X, int64_t M, int64_t K, float eps, int8_t* Q, float* S, const void* W,
+                      bool w_bf16, int64_t N, uint8_t* W_packed, float* gamma, void* ws, int nblk, hipStream_t s) {
     if (w_bf16)
-        return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const uint16_t*>(W), N, row_sums, nodes, gate,
-                                    nblk, s);
-    return quant_operands_pass1(X, M, K, eps, Q, S, static_cast<const float*>(W), N, row_sums, nodes, gate, nblk,
-                                s);
+        return act_pack_nb(X, M, K, eps, Q, S, static_cast<const uint16_t*>(W), N, W_packed, gamma, ws, nblk, s);
+    return act_pack_nb(X, M, K, eps, Q, S, static_cast<const float*>(W), N, W_packed, gamma, ws, nblk, s);
 }
 }  // namespace
 
@@ -1253,21 +1339,15 @@ hipError_t launch_quant_operands(const void* X, bool x_bf16, int64_t M, int64_t 
     const int64_t E = x_bf16 ? 8 : 4;
     const int64_t nblk = (K + kWave * E - 1) / (kWave * E);
     const bool rows = K == nblk * kWave * E && (nblk == 1 || nblk == 2 || nblk == 4 || nblk == 8 || nblk == 16);
-    hipError_t e;
     if (!rows) {  // act_quant's general kernel: the two calls' launches in order
-        e = launch_act_quant(X, x_bf16, M, K, eps, Xq, scale_x, s);
+        hipError_t e = launch_act_quant(X, x_bf16, M, K, eps, Xq, scale_x, s);
         if (e != hipSuccess) return e;
         return launch_weight_quant(W, w_bf16, N, K, W_packed, gamma, ws, s);
     }
-    float* row_sums = static_cast<float*>(ws);
-    float* nodes = ws_nodes(ws, N);
-    uint64_t* gate = ws_gate(ws, N);
-    e = x_bf16 ? quant_operands_w(static_cast<const uint16_t*>(X), M, K, eps, Xq, scale_x, W, w_bf16, N, row_sums,
-                                  nodes, gate, (int)nblk, s)
-               : quant_operands_w(static_cast<const float*>(X), M, K, eps, Xq, scale_x, W, w_bf16, N, row_sums,
-                                  nodes, gate, (int)nblk, s);
-    if (e != hipSuccess) return e;
-    return weight_quant_pack(W, w_bf16, N, K, W_packed, gamma, ws, s);
+    return x_bf16 ? act_pack_w(static_cast<const uint16_t*>(X), M, K, eps, Xq, scale_x, W, w_bf16, N, W_packed,
+                               gamma, ws, (int)nblk, s)
+                  : act_pack_w(static_cast<const float*>(X), M, K, eps, Xq, scale_x, W, w_bf16, N, W_packed, gamma,
+                               ws, (int)nblk, s);
 }
 
 // ============================================================ pack helper

@@ -116,7 +116,9 @@ def test_weight_quant_threshold_fallback_gives_the_same_bits(N, K, dt):
     # two-quantizer call)
     print(f"threshold fallback N={N} K={K} {dt}", flush=True)
     w = _weight_case(N, K, dt, seed=N + K)
-    x = workloads.normal((64, K), 1.0, seed=5, dtype="bf16")
+    # twice as many token rows as weight rows: more activation bytes than
+    # weight bytes, so the two-quantizer call packs beside act_quant
+    x = workloads.normal((2 * N, K), 1.0, seed=5, dtype="bf16")
     c_ref, g_ref = oracle.weight_quant(host(w))
     packed_ref = oracle.pack(c_ref)
     prev = bt.bitnet_set_gate_polls(0)
@@ -193,6 +195,11 @@ def test_quantizers_are_deterministic():
     # to the other workgroups (ragged last workgroup)
     (300, 2111, 4096, torch.bfloat16, torch.bfloat16),
     (64, 2111, 4096, torch.float32, torch.float32),
+    # more activation bytes than weight bytes: the pack beside act_quant in
+    # the second launch, with gamma published (the cases above with small W
+    # take this order too, with gamma in every pack workgroup)
+    (8192, 2111, 4096, torch.bfloat16, torch.bfloat16),
+    (8200, 2500, 4096, torch.float32, torch.bfloat16),
 ])
 def test_quant_operands_matches_the_two_calls(M, N, K, xdt, wdt):
     print(f"quant_operands M={M} N={N} K={K} {xdt} {wdt}", flush=True)
