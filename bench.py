@@ -359,7 +359,8 @@ KERNEL_OF = {
     "weight_clamp": "weight_clamp_kernel",
     "code_counts": "code_counts_kernel + code_counts_final_kernel",
     "weight_quant_counted": "wq_row_abs_sum_kernel + the counting pack + counted_sum_kernel",
-    "quant_operands": "quant_operands_kernel + wq_pack_kernel / wq_pack_pub_kernel",
+    "quant_operands": "wq_row_abs_sum_kernel + act_pack_kernel (more activation than weight bytes), "
+                      "else quant_operands_kernel + wq_pack_kernel / wq_pack_pub_kernel",
     "weight_quant_rows": "wq_row_abs_sum_kernel (with the row gammas) + wq_pack_rows_kernel",
     "linear_fwd_channel": "gemm_i8t2_kernel (per-channel epilogue) or gemv_t2_kernel",
     "bwd_grad_x_channel": "bwd_kernel<grad_x> (per-channel code scales)",
