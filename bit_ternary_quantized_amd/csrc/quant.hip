@@ -1234,18 +1234,21 @@ hipError_t launch_weight_quant_counted(const void* W, bool w_bf16, int64_t N, in
 // Two launches either way, the activation stream beside one of the two
 // weight passes; same bodies, same arithmetic, so the outputs are
 // bit-identical to the two separate calls.
-//  - activation bytes >= weight bytes (prefill, small layers): launch 1 is
-//    weight_quant's pass 1 (row sums and nodes); launch 2 runs act_quant's
-//    row-walking body on workgroups [0, A) and the weight pack on [A, A + P),
-//    so the pack's second read of W streams beside the activations instead
-//    of alone, and gamma's nodes are complete before launch 2 starts.
-//    8192 x 4096 x 4096 bf16: 30.0 us against 32.3 us the other way; with
-//    the pack's workgroups first in the grid 34.1 us (they take every slot
-//    and the activation workgroups queue behind them).
-//  - otherwise (a weight matrix far larger than the activations): launch 1
-//    runs act_quant on [0, A) and the row sums on [A, A + ceil(N/4)); launch 2
-//    is weight_quant's pack.  4096 x 28672 x 8192 (fp32 W): 362 us against
-//    366 us the other way.
+//  - activation bytes >= weight bytes and a matrix large enough for the
+//    published threshold (the 7B prefill layer): launch 1 is weight_quant's
+//    pass 1 (row sums and nodes); launch 2 runs act_quant's row-walking body
+//    on workgroups [0, A) and the weight pack on [A, A + P), so the pack's
+//    second read of W streams beside the activations instead of alone, and
+//    gamma's nodes are complete before launch 2 starts.  8192 x 4096 x 4096
+//    bf16: 30.0 us against 32.3 us the other way; with the pack's workgroups
+//    first in the grid 34.1 us (they take every slot and the activation
+//    workgroups queue behind them).
+//  - otherwise: launch 1 runs act_quant on [0, A) and the row sums on
+//    [A, A + ceil(N/4)); launch 2 is weight_quant's pack.  A weight matrix
+//    far larger than the activations (4096 x 28672 x 8192, fp32 W): 362 us
+//    against 366 us the other way; a small layer (8192 x 1376 x 512): the
+//    call alone 9.4 against 9.15 us, but the forward step (the call and the
+//    product) 30.8-31.5 against 31.8-32.0 us.
 template <typename TX, int NB, typename TW>
 __global__ __launch_bounds__(kAqWaves * kWave) void quant_operands_kernel(
     const TX* __restrict__ X, int64_t M, int64_t K, float eps, int8_t* __restrict__ Q, float* __restrict__ S,
@@ -1257,21 +1260,19 @@ __global__ __launch_bounds__(kAqWaves * kWave) void quant_operands_kernel(
     else wq_row_abs_sum_body<TW>(W, N, K, row_sums, b - act_blocks, nodes, gate);
 }
 
-template <typename TX, int NB, typename TW, bool FUSED>
+template <typename TX, int NB, typename TW>
 __global__ __launch_bounds__(kAqWaves * kWave) void act_pack_kernel(
     const TX* __restrict__ X, int64_t M, int64_t K, float eps, int8_t* __restrict__ Q, float* __restrict__ S,
     int act_blocks, const TW* __restrict__ W, int64_t total4, uint64_t* __restrict__ gate,
     const float* __restrict__ nodes, int64_t N, float* __restrict__ gamma, uint8_t* __restrict__ out,
-    int pack_blocks, int polls) {
+    int polls) {
     static_assert(kAqWaves == 4, "one workgroup shape for both bodies");
     const int b = blockIdx.x;  // uniform
     if (b < act_blocks) {
         act_quant_rows_body<TX, NB>(X, M, K, eps, Q, S, b, act_blocks);
     } else {
-        const int pb = b - act_blocks;
-        if constexpr (FUSED) wq_pack_body<TW, kPackU, false>(W, total4, nodes, N, K, gamma, out, nullptr, pb);
-        else wq_pack_pub4_body<TW, pack_u_pub<TW, false>(), false>(W, total4, gate, nodes, N, K, gamma, out,
-                                                                   polls, nullptr, pb);
+        wq_pack_pub4_body<TW, pack_u_pub<TW, false>(), false>(W, total4, gate, nodes, N, K, gamma, out, polls,
+                                                              nullptr, b - act_blocks);
     }
 }
 
@@ -1283,7 +1284,10 @@ hipError_t act_pack_launch(const TX* X, int64_t M, int64_t K, float eps, int8_t*
     float* nodes = ws_nodes(ws, N);
     uint64_t* gate = ws_gate(ws, N);
     const int act_blocks = (int)std::min<int64_t>((M + kAqWaves - 1) / kAqWaves, kAqMaxGroups);
-    if (M * K * (int64_t)sizeof(TX) < N * K * (int64_t)sizeof(TW)) {  // act_quant beside the row sums
+    const int64_t total4 = N * K / 4;
+    const int64_t g3 = (total4 + 256 * kPackU - 1) / (256 * kPackU);
+    const bool fused = N * g3 <= kFusedGammaMaxWork;
+    if (fused || M * K * (int64_t)sizeof(TX) < N * K * (int64_t)sizeof(TW)) {  // act_quant beside the row sums
         const int64_t wq_blocks = (N + kWqWaves - 1) / kWqWaves;
         const dim3 grid((unsigned)(act_blocks + wq_blocks)), block(kAqWaves * kWave);
         quant_operands_kernel<TX, NB, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, N, row_sums,
@@ -1296,20 +1300,11 @@ hipError_t act_pack_launch(const TX* X, int64_t M, int64_t K, float eps, int8_t*
     wq_row_abs_sum_kernel<TW><<<g1, b1, 0, s>>>(W, N, K, row_sums, nodes, gate, nullptr, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t total4 = N * K / 4;
-    const int64_t g3 = (total4 + 256 * kPackU - 1) / (256 * kPackU);
-    const bool fused = N * g3 <= kFusedGammaMaxWork;
     constexpr int up = pack_u_pub<TW, false>();
-    const int pack_blocks = (int)(fused ? g3 : (total4 + 256 * up - 1) / (256 * up));
+    const int pack_blocks = (int)((total4 + 256 * up - 1) / (256 * up));
     const dim3 grid((unsigned)(pack_blocks + act_blocks)), block(kAqWaves * kWave);
-    if (fused)
-        act_pack_kernel<TX, NB, TW, true><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, total4, gate,
-                                                                 nodes, N, gamma, W_packed, pack_blocks,
-                                                                 g_gate_polls);
-    else
-        act_pack_kernel<TX, NB, TW, false><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, total4, gate,
-                                                                  nodes, N, gamma, W_packed, pack_blocks,
-                                                                  g_gate_polls);
+    act_pack_kernel<TX, NB, TW><<<grid, block, 0, s>>>(X, M, K, eps, Q, S, act_blocks, W, total4, gate, nodes, N,
+                                                       gamma, W_packed, g_gate_polls);
     return hipGetLastError();
 }
 template <typename TX, typename TW>

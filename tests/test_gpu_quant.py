@@ -195,9 +195,8 @@ def test_quantizers_are_deterministic():
     # to the other workgroups (ragged last workgroup)
     (300, 2111, 4096, torch.bfloat16, torch.bfloat16),
     (64, 2111, 4096, torch.float32, torch.float32),
-    # more activation bytes than weight bytes: the pack beside act_quant in
-    # the second launch, with gamma published (the cases above with small W
-    # take this order too, with gamma in every pack workgroup)
+    # more activation bytes than weight bytes and gamma published: the pack
+    # beside act_quant in the second launch
     (8192, 2111, 4096, torch.bfloat16, torch.bfloat16),
     (8200, 2500, 4096, torch.float32, torch.bfloat16),
 ])
