@@ -598,13 +598,13 @@ __device__ __forceinline__ void load_groups(const T* __restrict__ W, int64_t g0,
     }
 }
 
-// COUNT (both pack kernels): the workgroup also counts the codes it writes.
+// COUNT (the pack bodies): the workgroup also counts the codes it writes.
 // Each thread keeps its +1 and -1 counts in the two halves of one word (at
 // most 4U codes a thread, at most 256 * 64 = 16384 a workgroup: inside 16
-// bits), each wave adds its 64 words with lane exchanges, and after one
-// barrier thread 0
-// stores the workgroup's pair (+1, -1) in slot blockIdx.x of count_partial: a
-// plain store, every slot written once per call, nothing to clear.
+// bits), each wave adds its 64 words with DPP row moves (wave_sum_u32), and
+// after one barrier thread 0 stores the workgroup's pair (+1, -1) in slot
+// `slot` (the pack workgroup's index) of count_partial: a plain store, every
+// slot written once per call, nothing to clear.
 // (Device-scope atomics into shared slots instead were measured slower: at
 // 4096 x 4096 bf16 the counting pack took 12.2 us with one set of atomics per
 // workgroup, 13.8 us with one per wave, against 11.6 us with stores.)
