@@ -40,6 +40,18 @@ FWD_SHAPES = _product_shapes(14, 700, 700, 4200, 1e8) + [(1, _dim(1, 3000), _dim
 BWD_SHAPES = _product_shapes(10, 4000, 400, 1200, 3e8)
 DEC_SHAPES = [(_dim(1, 16), _dim(1, 3000), _dim(16, 4096, 16)) for _ in range(10)] + \
     [(1, _dim(1, 3000), _dim(64, 4096, 64)) for _ in range(2)]
+# large weight matrices (gamma published by one pack workgroup: the five-wave
+# reader form when one round of workgroups covers the matrix, the four-wave
+# form otherwise), with token counts on both sides of the weight bytes so
+# that the two-quantizer call takes each of its two orders
+# (K mostly a whole number of row blocks, which the two-quantizer call needs
+# for its fused launches; now and then a ragged one)
+def _big_k():
+    return int(_rng.choice([2048, 4096, 8192])) if _rng.random() < 0.75 else _dim(2048, 8192, 4)
+
+
+BIG_WQ_SHAPES = [(_dim(1500, 9000), _big_k(), str(_rng.choice(["f32", "bf16"])), _dim(1, 3) / 2)
+                 for _ in range(8)]
 
 
 def _x(M, K, dt, seed):
@@ -118,3 +130,24 @@ def test_random_decode_and_quant_operands(M, N, K):
     torch.cuda.synchronize()
     assert torch.equal(q3, q2) and f32_bits_equal(s3.cpu().numpy(), s2.cpu().numpy())
     assert torch.equal(wp3, wp4) and f32_bits_equal(g3.cpu().numpy(), g4.cpu().numpy())
+
+
+@pytest.mark.parametrize("N,K,dt,tokens_per_row", BIG_WQ_SHAPES)
+def test_random_large_weight_quant_counted_and_quant_operands(N, K, dt, tokens_per_row):
+    M = max(1, int(N * tokens_per_row))
+    print(f"random large weight quant N={N} K={K} {dt}, quant_operands M={M}", flush=True)
+    w = workloads.normal((N, K), 0.02, seed=N * 3 + K, dtype=dt)
+    x = _x(M, K, "bf16", seed=M + K)
+    c_ref, g_ref = oracle.weight_quant(host(w))
+    packed_ref = oracle.pack(c_ref)
+    wp, g = bt.bitnet_weight_quant(to_dev(w))
+    wp2, g2, counts = bt.bitnet_weight_quant_counted(to_dev(w))
+    q3, s3, wp3, g3 = bt.bitnet_quant_operands(to_dev(x), to_dev(w))
+    torch.cuda.synchronize()
+    for p_, g_ in ((wp, g), (wp2, g2), (wp3, g3)):
+        assert np.array_equal(p_.cpu().numpy(), packed_ref)
+        assert f32_bits_equal(g_.cpu().numpy(), np.array([g_ref], np.float32))
+    assert np.array_equal(counts.cpu().numpy(), oracle.code_counts(packed_ref, K).astype(np.int64))
+    q_ref, s_ref = oracle.act_quant(host(x))
+    assert np.array_equal(q3.cpu().numpy(), q_ref)
+    assert f32_bits_equal(s3.cpu().numpy(), s_ref)
