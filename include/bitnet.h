@@ -387,13 +387,15 @@ int bitnet_code_counts(const uint8_t *W_packed, int64_t N, int64_t K, uint64_t *
  * bitnet_weight_quant's; counts as bitnet_code_counts's (counts[3], the
  * unused pattern 11, is 0).
  *   W, W_packed, gamma: as bitnet_weight_quant
- *   counts    4 uint64, DEVICE memory, 8-byte aligned, written
+ *   counts    4 uint64, DEVICE memory, 8-byte aligned, written: zeroed by
+ *            the call's first launch and summed into by its last with
+ *            64-bit integer atomics (exact in any order)
  *   workspace >= bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT_COUNTED, 0, N, K)
  *            device scratch: weight_quant's, then one (+1, -1) pair of
- *            uint32 per pack workgroup (8 bytes per 4096 weights), each
- *            written once by the call; contents on entry ignored.  The
- *            zeros are N*K minus the nonzero codes: every code the call
- *            writes is 00, 01 or 10.
+ *            uint32 per pack workgroup (8 bytes per 1024 to 4096 weights),
+ *            each written once by the call; contents on entry ignored.
+ *            The zeros are the codes minus the nonzero ones: every code the
+ *            call writes is 00, 01 or 10.
  * Errors: BITNET_E_ARG, BITNET_E_DTYPE, BITNET_E_SHAPE, BITNET_E_ALIGN,
  * BITNET_E_WORKSPACE, BITNET_E_HIP.
  */
