@@ -392,8 +392,9 @@ int bitnet_code_counts(const uint8_t *W_packed, int64_t N, int64_t K, uint64_t *
  *            64-bit integer atomics (exact in any order)
  *   workspace >= bitnet_workspace_bytes(BITNET_OP_WEIGHT_QUANT_COUNTED, 0, N, K)
  *            device scratch: weight_quant's, then one (+1, -1) pair of
- *            uint32 per pack workgroup (8 bytes per 1024 to 4096 weights),
- *            each written once by the call; contents on entry ignored.
+ *            uint32 per pack workgroup (a workgroup packs 4096 to 16384
+ *            weights; sized for one pair per 4096), each written once by the
+ *            call; contents on entry ignored.
  *            The zeros are the codes minus the nonzero ones: every code the
  *            call writes is 00, 01 or 10.
  * Errors: BITNET_E_ARG, BITNET_E_DTYPE, BITNET_E_SHAPE, BITNET_E_ALIGN,
