@@ -98,3 +98,67 @@ def test_two_stream_step_graph_replays_match_eager(M, N, K):
         torch.cuda.synchronize()
         for n in OUTS:
             assert torch.equal(b[n], ref[n]), f"replay {rep}: {n} differs from the eager result"
+
+
+def test_published_threshold_graph_replays_follow_the_weights():
+    # the bench step's calls at a size where one pack workgroup publishes the
+    # weight threshold (the two-quantizer call packing beside act_quant, the
+    # five-wave weight quant, the counted call), captured once; the weights
+    # are rescaled in place between replays, so every replay must publish its
+    # own threshold (the row-sum launch clears the word) and match eager calls
+    M, N, K = 8192, 4096, 2048
+    print(f"published-threshold graph M={M} N={N} K={K}", flush=True)
+    dev = "cuda"
+    x = to_dev(workloads.normal((M, K), 1.0, seed=3, dtype="bf16"))
+    w = to_dev(workloads.normal((N, K), 0.02, seed=4, dtype="bf16"))
+
+    def bufs():
+        return {
+            "Xq": torch.empty(M, K, dtype=torch.int8, device=dev),
+            "scale_x": torch.empty(M, dtype=torch.float32, device=dev),
+            "W_packed": torch.empty(N, K // 4, dtype=torch.uint8, device=dev),
+            "gamma": torch.empty(1, dtype=torch.float32, device=dev),
+            "Y": torch.empty(M, N, dtype=torch.float32, device=dev),
+            "W2": torch.empty(N, K // 4, dtype=torch.uint8, device=dev),
+            "g2": torch.empty(1, dtype=torch.float32, device=dev),
+            "W3": torch.empty(N, K // 4, dtype=torch.uint8, device=dev),
+            "g3": torch.empty(1, dtype=torch.float32, device=dev),
+            "counts": torch.empty(4, dtype=torch.int64, device=dev),
+            "ws": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, 0, N, K), dtype=torch.uint8,
+                              device=dev),
+            "ws2": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, 0, N, K), dtype=torch.uint8,
+                               device=dev),
+            "ws3": torch.empty(bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT_COUNTED, 0, N, K),
+                               dtype=torch.uint8, device=dev),
+        }
+
+    def step(b):
+        bt.bitnet_quant_operands(x, w, 1e-5, Xq=b["Xq"], scale_x=b["scale_x"], W_packed=b["W_packed"],
+                                 gamma=b["gamma"], workspace=b["ws"])
+        bt.bitnet_linear_fwd(b["Xq"], b["scale_x"], b["W_packed"], b["gamma"], Y=b["Y"])
+        bt.bitnet_weight_quant(w, W_packed=b["W2"], gamma=b["g2"], workspace=b["ws2"])
+        bt.bitnet_weight_quant_counted(w, W_packed=b["W3"], gamma=b["g3"], counts=b["counts"], workspace=b["ws3"])
+
+    b, ref = bufs(), bufs()
+    outs = ("Xq", "scale_x", "W_packed", "gamma", "Y", "W2", "g2", "W3", "g3", "counts")
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step(b)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(b)
+    torch.cuda.synchronize()
+    for rep, scale in enumerate((1.0, 3.0, 0.25)):
+        w.mul_(scale)
+        for n in outs:
+            b[n].zero_()
+        step(ref)  # eager, on the same weights
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in outs:
+            assert torch.equal(b[n], ref[n]), f"replay {rep}: {n} differs from the eager result"
+        assert int(b["counts"].sum()) == N * K
