@@ -374,6 +374,7 @@ SOURCES_OF = {
     "linear_fwd": ["bit_ternary_quantized_amd/csrc/gemm_i8.hip", "bit_ternary_quantized_amd/csrc/gemv.hip"],
     "bwd_grad_x": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
     "bwd_grad_W": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
+    "linear_bwd_ste": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
     "rmsnorm_bwd": ["bit_ternary_quantized_amd/csrc/norm_bwd.hip"],
     "bwd_grad_W_gated": ["bit_ternary_quantized_amd/csrc/bwd.hip"],
     "weight_clamp": ["bit_ternary_quantized_amd/csrc/quant.hip"],
