@@ -24,8 +24,10 @@
 // other does its memory phase: write the next tile into LDS, issue the
 // global loads of the tile after it, read and unpack its operands of the
 // current tile into registers.  Each group stages its own activation half
-// and its own copy of the weight tile (double-buffered, 64 KB in all), so
-// the groups share no LDS data and a barrier only orders the phases.  Global
+// and its own copy of the weight tile, both double-buffered (32 KB of
+// activations and 64 KB of weight codes in all, plus the row scales: 97 KB
+// of LDS, one workgroup a CU), so the groups share no LDS data and a
+// barrier only orders the phases.  Global
 // loads are buffer loads whose tails (rows past M or N, columns past K) read
 // zeros, so the loop has no branch.
 #include <type_traits>
