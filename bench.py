@@ -26,7 +26,9 @@ The JSON line carries:
               one-launch streaming read of the same byte count;
   ceilings    the measured ceilings (streaming reads of 11.3 MB, 12.0 MB and
               67 MB, int8 and bf16 MFMA loops with their clocks);
-  kernels     every call of the step, and the variants, timed on its own;
+  kernels     every call of the step, and the variants, timed on its own (8
+              launches back to back; warm_cache marks the calls whose bytes
+              fit in the 256 MB Infinity Cache, which then serves them);
   cpu_baseline  the CPU oracle on this host's cores, on a bounded sample of
               the same workload (threads and CPU model stated);
   inputs      sha256 of every input tensor;
