@@ -25,7 +25,7 @@
  *     never allocates device memory, keeps no pointer after returning and
  *     has no mutable global state, except the fixed device scratch of
  *     bitnet_weight_quant_noalloc (one static array per device, described
- *     there).
+ *     there) and the host-side test setting of bitnet_set_gate_polls.
  *   - Asynchrony: a call validates its arguments on the host, enqueues its
  *     kernels on `stream` (a hipStream_t passed as void*; NULL = the null
  *     stream) and returns.  Outputs are valid once the stream reaches that
