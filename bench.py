@@ -355,9 +355,9 @@ KERNEL_OF = {
     "weight_quant": "wq_row_abs_sum_kernel + wq_pack_kernel / wq_pack_pub_kernel (gamma in the pack launch)",
     "linear_fwd": "gemm_i8t2_kernel",
     "bwd_grad_x": "bwd_kernel<grad_x>",
-    "bwd_grad_W": "bwd_kernel<grad_W> (+ split_reduce_kernel when split)",
+    "bwd_grad_W": "bwd_kernel<grad_W> (+ split_reduce_kernel when split; xdeq_t_kernel first for a tall output)",
     "rmsnorm_bwd": "rmsnorm_bwd_kernel",
-    "bwd_grad_W_gated": "bwd_kernel<grad_W> with the range gate (+ split_reduce_kernel when split)",
+    "bwd_grad_W_gated": "bwd_kernel<grad_W> with the range gate (+ split_reduce_kernel when split; xdeq_t_kernel first for a tall output)",
     "weight_clamp": "weight_clamp_kernel",
     "code_counts": "code_counts_kernel + code_counts_final_kernel",
     "weight_quant_counted": "wq_row_abs_sum_kernel + the counting pack + counted_sum_kernel",

@@ -50,7 +50,8 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-enum { kGradX = 0, kGradW = 1 };
+// kGradWT: grad_W with its B operand read from X_deq^T (see xdeq_t_kernel)
+enum { kGradX = 0, kGradW = 1, kGradWT = 2 };
 constexpr int kThreads = 512;
 constexpr int kGroupThreads = 256;
 
@@ -62,13 +63,13 @@ constexpr int kGroupThreads = 256;
 // the two partial tiles are added once at the end.  The latter gives each
 // wave a square 64 x 64 accumulator block, which needs a quarter fewer LDS
 // bytes per MFMA than a 64 x 32 one.
-template <int BM_, int BN_, int BK_, bool KSPLIT_>
+template <int BM_, int BN_, int BK_, bool KSPLIT_, int WAVES_M_ = (KSPLIT_ ? 2 : 1)>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr bool KSPLIT = KSPLIT_;
     static constexpr int GROWS = KSPLIT ? BM : BM / 2;   // output rows of a group
     static constexpr int GBCOLS = KSPLIT ? BN : BN / 2;  // B columns a group stages
-    static constexpr int WAVES_M = KSPLIT ? 2 : 1, WAVES_N = 4 / WAVES_M;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = 4 / WAVES_M;  // a group's waves
     static constexpr int WTM = GROWS / WAVES_M;          // wave tile rows
     static constexpr int WTN = BN / WAVES_N;             // wave tile columns
     static constexpr int IM = WTM / 32, JN = WTN / 32;
@@ -89,6 +90,10 @@ struct Tile {
 using TileL = Tile<256, 256, 32, false>;
 using TileS = Tile<128, 128, 64, false>;   // small outputs, grad_x
 using TileSK = Tile<128, 128, 64, true>;  // small outputs, grad_W (measured faster)
+// grad_W from X_deq^T: the group's four waves as 2 x 2 (64 x 128 wave tiles),
+// so a wave makes 8 transposing reads of its gy operand and 8 plain 16-byte
+// reads of X_deq^T per step instead of 16 and 4
+using TileLW = Tile<256, 256, 32, false, 2>;
 
 // Chunk c of row r of a "rows" tile: each 256-byte bank window holds 16/CPR
 // rows; XOR-ing the chunk index with the window index gives every 16-lane
@@ -224,6 +229,11 @@ struct Stage<kGradW, NA, NB> {
     float sx[NB];
     uint4 bcv[NB];
 };
+template <int NA, int NB>
+struct Stage<kGradWT, NA, NB> {
+    uint4 a[NA];
+    uint4 b[NB];  // 8 bf16 of X_deq^T, stored as loaded
+};
 
 }  // namespace
 
@@ -232,6 +242,11 @@ struct Stage<kGradW, NA, NB> {
 // MODE kGradW: out [N][K] fp32 = gy^T . X_deq, rows n, columns k, contraction
 //   m over the split's token range; with splits > 1 the tile goes to
 //   out + sp*N*K (partials).  `second` = Xq, `aux` = scale_x.
+// MODE kGradWT: kGradW with `second` = X_deq^T [K][Mp] bf16 (Mp = M rounded
+//   up to 8, zero past M; written by xdeq_t_kernel with the same rounding as
+//   kGradW's conversion, so the two modes give the same bits).  Its B tile is
+//   a "rows" tile read with plain 16-byte reads: no transposing B reads and no
+//   conversion in the loop.  `aux` unused.
 // VEC: N % 8 == 0 (gy rows 16-byte aligned, 8-element chunks all in or out);
 // otherwise gy is read element by element.  GATED (grad_W, one split only):
 // the master-weight range gate `gate` applied as the tile is written.
@@ -244,10 +259,12 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     constexpr int BK = T::BK, GROWS = T::GROWS, IM = T::IM, JN = T::JN, KQ = T::KQ;
     constexpr int NA = T::NA, NB = T::NB;
     constexpr bool KS = T::KSPLIT;
-    constexpr int PB = T::pitch(T::BN);  // B tile
+    constexpr bool GW = MODE != kGradX;   // a grad_W product
+    constexpr bool BT = MODE == kGradWT;  // its B operand from X_deq^T rows
+    constexpr int PB = T::pitch(T::BN);  // B tile ("cols")
     constexpr int PA = T::pitch(GROWS);  // grad_W A tile
     constexpr int A_BYTES = MODE == kGradX ? T::ROWS_BYTES : T::cols_bytes(GROWS);
-    constexpr int B_BYTES = T::cols_bytes(T::BN);
+    constexpr int B_BYTES = BT ? T::BN * 2 * BK : T::cols_bytes(T::BN);
     constexpr int CPA = GROWS / 8;       // grad_W: 8-element gy chunks per A row
     constexpr int NBUF_B = KS ? 2 : 1;   // B tiles per buffer: per group, or one shared
     __shared__ __align__(16) uint8_t smem_a[2][2][A_BYTES];       // [group][buffer]
@@ -268,9 +285,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
             ch = 4 * (q & 1) + (l & 3);
         }
     };
-    const int R = MODE == kGradX ? M : N;  // output rows
-    const int C = K;                        // output columns
-    const int KC = MODE == kGradX ? N : M;  // contraction length
+    const int R = GW ? N : M;  // output rows
+    const int C = K;           // output columns
+    const int KC = GW ? M : N; // contraction length
     int tm, tn, sp;
     tile_of(blockIdx.x, (R + T::BM - 1) / T::BM, (C + T::BN - 1) / T::BN, splits, tm, tn, sp);
     const int r0 = tm * T::BM, c0 = tn * T::BN;
@@ -283,8 +300,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     const int KB = K / 4;
     const int rg = r0 + (KS ? 0 : wm * GROWS);    // first output row of the group
     const int cb = c0 + (KS ? 0 : wm * T::GBCOLS);  // first column the group stages
-    const int wr = KS ? (wn >> 1) * T::WTM : 0;     // wave tile origin in the group
-    const int wc = (KS ? (wn & 1) : wn) * T::WTN;
+    const int wr = (wn / T::WAVES_N) * T::WTM;      // wave tile origin in the group
+    const int wc = (wn % T::WAVES_N) * T::WTN;
     // the group's steps: all of them, or (KSPLIT) every other one
     const int nsteps_g = KS ? (nsteps + 1 - wm) / 2 : nsteps;
     auto kstep = [&](int i) { return KS ? 2 * i + wm : i; };
@@ -330,6 +347,20 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     const bool b_ok = cb + 8 * bj < C;
     const uint32_t boff = MODE == kGradX ? (uint32_t)(bk * KB + 2 * bj) : (uint32_t)(bk * K + 8 * bj);
     const uint32_t bstep = MODE == kGradX ? (uint32_t)(RPP * KB) : (uint32_t)(RPP * K);
+    // BT: B chunks c = tg + 256 h, 8 tokens each: X_deq^T row (output column)
+    // c / CPR of the group's staged columns, token chunk c % CPR (the same for
+    // every h, since 256 is a multiple of CPR); rows past K read zeros.
+    static_assert(!BT || NB * kGroupThreads == T::GBCOLS * T::CPR, "X_deq^T chunks cover the step");
+    const int Mp = (M + 7) & ~7;           // X_deq^T row pitch (elements)
+    const int btc = tg % T::CPR;           // token chunk of this thread
+    const int btrow = tg / T::CPR;         // first staged row, + h * 256 / CPR
+    uint32_t btoff[BT ? NB : 1];
+#pragma unroll
+    for (int h = 0; h < (BT ? NB : 1); ++h) {
+        const int row = btrow + h * (kGroupThreads / T::CPR);
+        btoff[h] = cb + row < C ? (uint32_t)((row * Mp + 8 * btc) * 2) : kBufOOB;
+    }
+    (void)Mp;
 
     auto load_a = [&](int kb, const __amdgpu_buffer_rsrc_t& ra, int u) -> uint4 {
         // kb: contraction base of the step
@@ -378,6 +409,15 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
                     p.sn[h] = __builtin_bit_cast(float, buf_load4(rsn, tv ? (uint32_t)(4 * (bk + h * RPP)) : kBufOOB));
                 }
             }
+        } else if constexpr (BT) {
+            const __amdgpu_buffer_rsrc_t ra = make_buf(gy + (int64_t)kb * N + rg);
+#pragma unroll
+            for (int u = 0; u < NA; ++u) p.a[u] = load_a(kb, ra, u);
+            const __amdgpu_buffer_rsrc_t rb =
+                make_buf(static_cast<const uint16_t*>(second) + (int64_t)cb * Mp + kb);
+            const bool tv = kb + 8 * btc < khi;
+#pragma unroll
+            for (int h = 0; h < NB; ++h) p.b[h] = buf_load16(rb, tv ? btoff[h] : kBufOOB);
         } else {
             const __amdgpu_buffer_rsrc_t ra = make_buf(gy + (int64_t)kb * N + rg);
 #pragma unroll
@@ -395,11 +435,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
         }
     };
     auto convert = [&](StageT& p) {
+        if constexpr (!BT) {  // (BT: stored as loaded)
 #pragma unroll
-        for (int h = 0; h < NB; ++h) {
-            if constexpr (MODE == kGradX && CH) p.bcv[h] = codes8_to_bf16_scaled(p.braw[h], p.sn[h]);
-            else if constexpr (MODE == kGradX) p.bcv[h] = codes8_to_bf16(p.braw[h]);
-            else p.bcv[h] = int8x8_to_bf16(p.braw[h], p.sx[h] > 0.0f ? __builtin_amdgcn_rcpf(p.sx[h]) : 0.0f);
+            for (int h = 0; h < NB; ++h) {
+                if constexpr (MODE == kGradX && CH) p.bcv[h] = codes8_to_bf16_scaled(p.braw[h], p.sn[h]);
+                else if constexpr (MODE == kGradX) p.bcv[h] = codes8_to_bf16(p.braw[h]);
+                else p.bcv[h] = int8x8_to_bf16(p.braw[h], p.sx[h] > 0.0f ? __builtin_amdgcn_rcpf(p.sx[h]) : 0.0f);
+            }
         }
     };
     auto store_lds = [&](int i, const StageT& p) {
@@ -416,9 +458,16 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
                 *reinterpret_cast<uint4*>(As + row * PA + 16 * ch) = p.a[u];
             }
         }
+        if constexpr (BT) {
 #pragma unroll
-        for (int h = 0; h < NB; ++h)
-            *reinterpret_cast<uint4*>(Bs + (bk + h * RPP) * PB + 2 * bcol) = p.bcv[h];
+            for (int h = 0; h < NB; ++h)
+                *reinterpret_cast<uint4*>(Bs + rows_slot<T>((cb - c0) + btrow + h * (kGroupThreads / T::CPR), btc)) =
+                    p.b[h];
+        } else {
+#pragma unroll
+            for (int h = 0; h < NB; ++h)
+                *reinterpret_cast<uint4*>(Bs + (bk + h * RPP) * PB + 2 * bcol) = p.bcv[h];
+        }
     };
 
     v16f acc[IM][JN];
@@ -436,7 +485,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
 #pragma unroll
-            for (int j = 0; j < JN; ++j) b[kq][j] = cols_operand<PB>(Bs, 16 * kq, wc + j * 32, lane);
+            for (int j = 0; j < JN; ++j) {
+                if constexpr (BT) b[kq][j] = rows_operand<T>(Bs, kq, wc + j * 32, lane);
+                else b[kq][j] = cols_operand<PB>(Bs, 16 * kq, wc + j * 32, lane);
+            }
 #pragma unroll
             for (int ii = 0; ii < IM; ++ii) {
                 if constexpr (MODE == kGradX) a[kq][ii] = rows_operand<T>(As, kq, wr + ii * 32, lane);
@@ -548,7 +600,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     // 8*(r/4) + 4*g + r%4
     const float scale = MODE == kGradX && !CH ? *aux : 1.0f;
     float* outf = static_cast<float*>(out);
-    if constexpr (MODE == kGradW) outf += (int64_t)sp * N * K;
+    if constexpr (GW) outf += (int64_t)sp * N * K;
 #pragma unroll
     for (int ii = 0; ii < IM; ++ii) {
         // gated: the master weights of this 32-row block first (clamped
@@ -649,6 +701,54 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
     }
 }
 
+// X_deq^T for the grad_W product: XdT[k][m] = bf16(Xq[m][k] * (1/scale_x[m]))
+// (the reciprocal and the rounding of int8x8_to_bf16, so kGradWT sees the
+// very operand values kGradW converts in its loop), for m < Mp = M rounded up
+// to 8, zero for m >= M.  A 64-token x 64-column tile per 256-thread
+// workgroup, transposed through LDS: each thread loads 16 int8 of a token row
+// (four threads cover 64 contiguous bytes of the row) and writes 16 bf16
+// values down a column of the LDS tile; then each thread stores 16 bf16 of an
+// X_deq^T row (four threads cover 128 contiguous bytes).  The LDS pitch of 66
+// elements (33 dwords) puts the four column groups of a wave's 2-byte writes
+// on different banks.
+constexpr int kXtTile = 64, kXtPitch = kXtTile + 2;
+__global__ __launch_bounds__(256) void xdeq_t_kernel(const int8_t* __restrict__ Xq,
+                                                     const float* __restrict__ scale_x, int M, int K,
+                                                     int Mp, int tiles_m, uint16_t* __restrict__ XdT) {
+    __shared__ uint16_t tile[kXtTile * kXtPitch];
+    const int t = threadIdx.x;
+    const int tm = blockIdx.x % tiles_m, tk = blockIdx.x / tiles_m;
+    const int m0 = tm * kXtTile, k0 = tk * kXtTile;
+    {
+        const int ml = t >> 2, kl = (t & 3) * 16;
+        const int m = m0 + ml, k = k0 + kl;
+        uint4 q = make_uint4(0, 0, 0, 0);
+        float rs = 0.0f;
+        if (m < M && k < K) {  // K % 16 == 0: a 16-column chunk is all in or all out
+            q = *reinterpret_cast<const uint4*>(Xq + (int64_t)m * K + k);
+            const float sx = scale_x[m];
+            rs = sx > 0.0f ? __builtin_amdgcn_rcpf(sx) : 0.0f;
+        }
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float v = (float)(int8_t)(w[i >> 2] >> (8 * (i & 3))) * rs;
+            tile[(kl + i) * kXtPitch + ml] = __builtin_bit_cast(uint16_t, (__bf16)v);
+        }
+    }
+    __syncthreads();
+    const int kl = t >> 2, ml = (t & 3) * 16;
+    const int k = k0 + kl, m = m0 + ml;
+    if (k >= K) return;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tile + kl * kXtPitch + ml);  // dword aligned
+    uint16_t* dst = XdT + (int64_t)k * Mp + m;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)  // two 8-element halves; Mp % 8 == 0
+        if (m + 8 * h < Mp)
+            *reinterpret_cast<uint4*>(dst + 8 * h) =
+                make_uint4(src[4 * h], src[4 * h + 1], src[4 * h + 2], src[4 * h + 3]);
+}
+
 // ------------------------------------------------------------------ plans
 namespace {
 
@@ -682,6 +782,20 @@ Plan plan_for(int64_t rows, int64_t cols, int64_t depth, bool allow_split) {
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
+// grad_W reads X_deq^T (kGradWT) on the large tiles of a tall output
+// (N >= 8192), when its staging offsets fit 32 bits (128 rows of Mp bf16) and
+// the transposed copy stays within 2 GiB.  The pass over X costs the same
+// for any N (3 bytes an element: about 20 us at 4096 x 8192) while the
+// product's saving grows with N (its steps run about 6% faster; measured at
+// 28672 x 8192 from 4096 tokens 1751 -> 1663 us for the call, bit-identical;
+// at N = 4096 (8192 tokens, K = 4096) 248 -> 255 us, so not used there; on
+// the small split tiles the extra pass also costs more than it saves).
+bool use_xdt(const Plan& p, int64_t M, int64_t N, int64_t K) {
+    const int64_t Mp = (M + 7) / 8 * 8;
+    return p.big && N >= 8192 && Mp <= ((int64_t)1 << 22) && K * Mp * 2 <= ((int64_t)1 << 31);
+}
+size_t xdt_bytes(int64_t M, int64_t K) { return align256((size_t)K * (size_t)((M + 7) / 8 * 8) * 2); }
+
 template <int MODE, class T, bool OUT_BF16>
 hipError_t launch_one(const uint16_t* gy, const void* second, const float* aux, int M, int N, int K,
                       const Plan& p, void* out, hipStream_t s, const SteGate& gate = SteGate{},
@@ -689,11 +803,11 @@ hipError_t launch_one(const uint16_t* gy, const void* second, const float* aux, 
     const unsigned grid = (unsigned)(p.tiles * p.splits);
     // the gate rides in the tile epilogue only without a token split (with
     // one, split_reduce_kernel applies it)
-    const bool gated = MODE == kGradW && gate.w != nullptr && p.splits == 1;
+    const bool gated = MODE != kGradX && gate.w != nullptr && p.splits == 1;
 #define BITNET_BWD_LAUNCH(V_, G_)                                                                \
     bwd_kernel<MODE, T, V_, OUT_BF16, G_><<<grid, kThreads, 0, s>>>(gy, second, aux, M, N, K,   \
                                                                    p.splits, p.kper, out, gate)
-    if constexpr (MODE == kGradW) {
+    if constexpr (MODE != kGradX) {
         if (gated) {
             if (N % 8 == 0) BITNET_BWD_LAUNCH(true, true);
             else BITNET_BWD_LAUNCH(false, true);
@@ -718,9 +832,10 @@ hipError_t launch_one(const uint16_t* gy, const void* second, const float* aux, 
 
 }  // namespace
 
+// grad_W's workspace: the split partials (if any), then X_deq^T (if used)
 size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K) {
     const Plan p = plan_for(N, K, M, true);
-    return p.splits > 1 ? align256((size_t)p.splits * N * K * 4) : 0;
+    return (p.splits > 1 ? align256((size_t)p.splits * N * K * 4) : 0) + (use_xdt(p, M, N, K) ? xdt_bytes(M, K) : 0);
 }
 
 hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* scale_x,
@@ -742,8 +857,21 @@ hipError_t launch_bwd_ste(const uint16_t* gy, const int8_t* Xq, const float* sca
     if (grad_W) {
         const Plan p = plan_for(N, K, M, true);
         void* dst = p.splits > 1 ? ws : static_cast<void*>(grad_W);
-        hipError_t e = p.big ? launch_one<kGradW, TileL, false>(gy, Xq, scale_x, m, n, k, p, dst, s, gate)
-                             : launch_one<kGradW, TileSK, false>(gy, Xq, scale_x, m, n, k, p, dst, s, gate);
+        hipError_t e;
+        if (use_xdt(p, M, N, K)) {
+            const size_t part = p.splits > 1 ? align256((size_t)p.splits * N * K * 4) : 0;
+            uint16_t* xdt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + part);
+            const int64_t Mp = (M + 7) / 8 * 8;
+            const int64_t tiles_m = ceil_div(Mp, kXtTile), tiles = tiles_m * ceil_div(K, kXtTile);
+            if (tiles > INT32_MAX) return hipErrorInvalidValue;
+            xdeq_t_kernel<<<(unsigned)tiles, 256, 0, s>>>(Xq, scale_x, m, k, (int)Mp, (int)tiles_m, xdt);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            e = launch_one<kGradWT, TileLW, false>(gy, xdt, nullptr, m, n, k, p, dst, s, gate);
+        } else {
+            e = p.big ? launch_one<kGradW, TileL, false>(gy, Xq, scale_x, m, n, k, p, dst, s, gate)
+                      : launch_one<kGradW, TileSK, false>(gy, Xq, scale_x, m, n, k, p, dst, s, gate);
+        }
         if (e != hipSuccess) return e;
         if (p.splits > 1) {
             const int64_t count = N * K;

@@ -197,9 +197,11 @@ int bitnet_linear_fwd(const int8_t *Xq, const float *scale_x, const uint8_t *W_p
  *   grad_x  [M][K] fp32 or bf16 (gx_dtype), written when non-NULL
  *   grad_W  [N][K] fp32, written when non-NULL
  *   workspace >= bitnet_workspace_bytes(BITNET_OP_LINEAR_BWD_STE, M, N, K)
- *            device scratch for fp32 partial tiles of grad_W when its
- *            output is too small to fill the GPU and the token range is
- *            split (splits*N*K*4 bytes; 0 otherwise, then NULL is allowed);
+ *            device scratch of grad_W: fp32 partial tiles when its output is
+ *            too small to fill the GPU and the token range is split
+ *            (splits*N*K*4 bytes), and X_deq transposed (K rows of M rounded
+ *            up to 8 tokens, bf16) for a tall output (N >= 8192) on the large
+ *            tiles; 0 bytes when neither applies, then NULL is allowed;
  *            contents on entry ignored.
  * K % 16 == 0, K < 2^24, N < 2^23 (tile loads use 32-bit offsets).
  * Errors: BITNET_E_ARG (both outputs NULL), BITNET_E_SHAPE, BITNET_E_DTYPE,

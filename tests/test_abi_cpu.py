@@ -57,8 +57,13 @@ def test_workspace_sizes():
     assert bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_FWD, 8, 8, 16) == 0
     wq = bt.bitnet_workspace_bytes(bt.BITNET_OP_WEIGHT_QUANT, 0, 28672, 8192)
     assert wq >= 28672 * 4 + 4 and wq % 256 == 0
-    # grad_W of a large layer fills the GPU without splitting its tokens
-    assert bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, 4096, 28672, 8192) == 0
+    # grad_W of a large, tall layer fills the GPU without splitting its tokens
+    # and reads X_deq transposed: K x M bf16
+    assert bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, 4096, 28672, 8192) == 8192 * 4096 * 2
+    # the token count rounded up to 8 in that copy
+    assert bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, 4093, 28672, 8192) == 8192 * 4096 * 2
+    # a large, short one (N = 4096) needs no workspace
+    assert bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, 8192, 4096, 4096) == 0
     # a small one (N*K = 1376*512) splits 8192 tokens: fp32 partial tiles
     bw = bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, 8192, 1376, 512)
     assert bw >= 2 * 1376 * 512 * 4 and bw % 256 == 0

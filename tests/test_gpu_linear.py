@@ -133,6 +133,48 @@ def test_linear_bwd_token_split(M, N, K):
     assert np.array_equal(gw3.cpu().numpy(), first)
 
 
+# grad_W of a tall output (N >= 8192) on the 256 x 256 tiles reads X_deq
+# transposed from the workspace (K x M rounded up to 8 tokens, bf16), written
+# by a pass before the product: token counts that are not a multiple of 8 (the
+# copy's zero padding), ragged tile edges in N and K, a workspace that starts
+# as 0xff bytes, repeat calls (identical bits), and the range-gated variant
+# whose gate rides in the product's epilogue.
+XT_SHAPES = [(300, 8200, 2000), (1029, 8192, 2064), (40, 8448, 1936)]
+
+
+@pytest.mark.parametrize("M,N,K", XT_SHAPES)
+def test_linear_bwd_grad_w_from_transposed_x(M, N, K):
+    print(f"linear_bwd grad_W from X_deq^T M={M} N={N} K={K}", flush=True)
+    nws = bt.bitnet_workspace_bytes(bt.BITNET_OP_LINEAR_BWD_STE, M, N, K)
+    assert nws >= K * ((M + 7) // 8 * 8) * 2  # the transposed copy is in use
+    q, codes, scale_x, gamma = _quantized_operands(M, N, K, seed=M + 11 * N + K)
+    gy = workloads.normal((M, N), 1e-3, seed=M + 5 * N, dtype="bf16")
+    wp = to_dev(torch.from_numpy(oracle.pack(codes.numpy())))
+    ws = torch.full((nws,), 255, dtype=torch.uint8, device="cuda")
+    args = (to_dev(gy), to_dev(q), to_dev(scale_x), wp, to_dev(gamma))
+    _, gw = bt.bitnet_linear_bwd_ste(*args, want_grad_x=False, workspace=ws)
+    torch.cuda.synchronize()
+    gw_ref = oracle.ste_grad_w(host(gy), q.numpy(), scale_x.numpy())
+    first = gw.cpu().numpy()
+    assert_grad_close(first, gw_ref, "grad_W")
+    ws.fill_(255)
+    _, gw2 = bt.bitnet_linear_bwd_ste(*args, want_grad_x=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(gw2.cpu().numpy(), first)
+    # the gated variant: master weights around the gate bounds
+    w = workloads.normal((N, K), 0.5, seed=M + N + 1, dtype="f32")
+    _, gwg = bt.bitnet_linear_bwd_ste_gated(*args, to_dev(w), -0.6, 0.6, want_grad_x=False, workspace=ws)
+    torch.cuda.synchronize()
+    gated_ref = oracle.ste_gate(gw_ref, workloads.host_array(w), -0.6, 0.6)
+    got = gwg.cpu().numpy()
+    wn = workloads.host_array(w)
+    outside = (wn < np.float32(-0.6)) | (wn > np.float32(0.6))
+    assert outside.any() and (~outside).any()
+    assert (got[outside] == 0).all()
+    assert np.array_equal(got[~outside], first[~outside])
+    assert_grad_close(got, gated_ref, "gated grad_W")
+
+
 def test_linear_bwd_single_outputs():
     M, N, K = 70, 90, 128
     q, codes, scale_x, gamma = _quantized_operands(M, N, K, seed=9)
