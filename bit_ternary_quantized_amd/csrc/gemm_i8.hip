@@ -105,159 +105,189 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
     // the next tile's loads and MFMAs run instead of ending every round of
     // workgroups with a write burst.  Tile v maps as workgroup v would in a
     // one-tile-per-workgroup launch (same XCD when the grid is a multiple
-    // of 8).
+    // of 8).  The next tile's first loads are issued before this tile's y
+    // stores: a wave's memory operations complete in issue order, so loads
+    // issued after 128 stores would wait for all of them.
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    for (int tile = blockIdx.x; tile < tiles_m * tiles_n; tile += gridDim.x) {
+    const int ntiles = tiles_m * tiles_n;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform in the wave
+    const int wm = wave >> 2, wn = wave & 3;                   // wm: the wave group
+    const int tg = t & (kGroupThreads - 1);                    // thread inside the group
+    const int KB = K / 4;                                      // packed bytes per weight row
+    const int nk = (K + BK - 1) / BK;
+
+    // Activations: thread tg stages chunks tg + 256 u (row c / 4, chunk c % 4)
+    // of the group's 128 rows; offsets relative to the step's base address.
+    int arow[kAPer], acol[kAPer];
+#pragma unroll
+    for (int u = 0; u < kAPer; ++u) {
+        const int c = tg + u * kGroupThreads;
+        arow[u] = c >> 2;
+        acol[u] = (c & 3) * 16;
+    }
+    // Weights: in a quarter, thread tg stages slice bc = tg % 4 of row
+    // bq = tg / 4 (+ 64 per quarter), both 8-byte halves in slot order.
+    const int bq = tg >> 2, bc = tg & 3, bsw = half_swap(bq);
+    const uint32_t boff = (uint32_t)(bq * KB + 16 * bc);
+
+    // where a tile's operands start (uniform) and this thread's activation offsets
+    struct Geo {
+        int m0, n0;
+        const int8_t* Xt;
+        const uint8_t* Wt;
+        uint32_t aoff[kAPer];
+    };
+    // (live = false: a tile that does not exist, every load of it past the
+    // buffer: no memory access, zeros)
+    auto geo_of = [&](int tile, bool live) {
+        Geo g;
         int tm, tn;
         tile_of(tile, tiles_m, tiles_n, tm, tn);
-        const int m0 = tm * BM, n0 = tn * BN;
-        const int t = threadIdx.x;
-        const int lane = t & 63;
-        const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform in the wave
-        const int wm = wave >> 2, wn = wave & 3;                   // wm: the wave group
-        const int tg = t & (kGroupThreads - 1);                    // thread inside the group
-        const int KB = K / 4;                                      // packed bytes per weight row
-        const int nk = (K + BK - 1) / BK;
+        g.m0 = tm * BM;
+        g.n0 = live ? tn * BN : N;
+        const int mh = g.m0 + wm * HM;  // first row of the group's half
+#pragma unroll
+        for (int u = 0; u < kAPer; ++u)
+            g.aoff[u] = live && mh + arow[u] < M ? (uint32_t)(arow[u] * K + acol[u]) : kBufOOB;
+        g.Xt = Xq + (int64_t)mh * K;
+        g.Wt = Wp + (int64_t)g.n0 * KB;
+        return g;
+    };
 
+    auto load_a = [&](const Geo& g, int it, uint4 (&a)[kAPer]) {
+        const int k0 = it * BK;
+        const __amdgpu_buffer_rsrc_t ra = make_buf(g.Xt + k0);
+#pragma unroll
+        for (int u = 0; u < kAPer; ++u) a[u] = buf_load16(ra, k0 + acol[u] < K ? g.aoff[u] : kBufOOB);
+    };
+    auto load_b = [&](const Geo& g, int qi, uint4& b) {  // quarter qi: block qi / 4, rows 64 (qi % 4) + bq
+        const int blk = qi >> 2, part = qi & 3;
+        const int kb0 = blk * kStepsPerBlock * BK;  // first column of the block
+        const __amdgpu_buffer_rsrc_t rb = make_buf(g.Wt + (int64_t)part * kQuarterRows * KB + blk * ROW_BYTES);
+        const bool rv = g.n0 + part * kQuarterRows + bq < N;
+        const int kc = kb0 + bc * BK;  // first column of the slice
+        if constexpr (VECB) {
+            const bool v = rv && kc < K;
+            const uint2 lo = buf_load8(rb, v ? boff + 8 * bsw : kBufOOB);
+            const uint2 hi = buf_load8(rb, v ? boff + 8 * (bsw ^ 1) : kBufOOB);
+            b = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {  // dword d of the slice covers columns kc + 16 d .. + 15
+            const int d0 = 2 * bsw, d1 = 2 * (bsw ^ 1);
+            b.x = buf_load4(rb, rv && kc + 16 * d0 < K ? boff + 4 * d0 : kBufOOB);
+            b.y = buf_load4(rb, rv && kc + 16 * d0 + 16 < K ? boff + 4 * d0 + 4 : kBufOOB);
+            b.z = buf_load4(rb, rv && kc + 16 * d1 < K ? boff + 4 * d1 : kBufOOB);
+            b.w = buf_load4(rb, rv && kc + 16 * d1 + 16 < K ? boff + 4 * d1 + 4 : kBufOOB);
+        }
+    };
+    // staged activation chunks are byte-transposed in registers (in a
+    // compute phase, where the VALU is otherwise idle) and stored as they are
+    auto transpose_a = [&](uint4 (&a)[kAPer]) {
+#pragma unroll
+        for (int u = 0; u < kAPer; ++u) {
+            const uint32_t in[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
+            uint32_t o[4];
+            transpose4x4_bytes(in, o);
+            a[u] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    };
+    auto store_a = [&](int buf, const uint4 (&a)[kAPer]) {
+        uint8_t* As = smem_a[wm][buf];
+#pragma unroll
+        for (int u = 0; u < kAPer; ++u) {
+            const int c = tg + u * kGroupThreads;
+            *reinterpret_cast<uint4*>(As + row_slot(c >> 2, c & 3)) = a[u];
+        }
+    };
+    auto store_b = [&](int qi, const uint4& b) {
+        uint8_t* Bs = smem_b[wm][(qi >> 2) & 1];
+        *reinterpret_cast<uint4*>(Bs + row_slot((qi & 3) * kQuarterRows + bq, bc)) = b;
+    };
+    // tile t of the activations and quarter t + 3 of the weights
+    auto load_global = [&](const Geo& g, int it, Stage& p) {
+        load_a(g, it, p.a);
+        load_b(g, it + 3, p.b);
+    };
+    auto store_lds = [&](int it, const Stage& p) {
+        store_a(it & 1, p.a);
+        store_b(it + 3, p.b);
+    };
+
+    const int g = lane >> 5;    // lane group: k chunks 2g, 2g+1 of the step
+    const int l32 = lane & 31;  // row (A) / column (B) inside a 32-block
+
+    // Operands of one step: MFMA half kh pairs activation chunk 2g+kh with
+    // the same chunk of the codes (one packed dword per half).
+    v4i a[2][4], b[2][JN];
+    uint2 bp[JN];
+    auto read_codes = [&](int it) {
+        const uint8_t* Bs = smem_b[wm][(it >> 2) & 1];
+        const int c = it & 3;
+#pragma unroll
+        for (int j = 0; j < JN; ++j) {
+            const int r = wn * 64 + j * 32 + l32;
+            bp[j] = *reinterpret_cast<const uint2*>(Bs + row_slot(r, c) + 8 * (g ^ half_swap(r)));
+        }
+    };
+    auto read_acts = [&](int buf) {
+        const uint8_t* As = smem_a[wm][buf];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 v = *reinterpret_cast<const uint4*>(As + row_slot(i * 32 + l32, 2 * g + kh));
+                a[kh][i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            }
+    };
+    auto unpack_codes = [&] {
+#pragma unroll
+        for (int j = 0; j < JN; ++j) {
+            uint32_t u[4];
+            unpack16(bp[j].x, u);
+            b[0][j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
+            unpack16(bp[j].y, u);
+            b[1][j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
+        }
+    };
+    auto barrier = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    if ((int)blockIdx.x >= ntiles) return;  // (the grid has at most ntiles workgroups)
+    Geo cur = geo_of(blockIdx.x, true);
+    // the first tile's prologue loads: weight quarters 0-2, activation tile 0 + quarter 3
+    uint4 q0, q1, q2;
+    Stage p0;
+    load_b(cur, 0, q0);
+    load_b(cur, 1, q1);
+    load_b(cur, 2, q2);
+    load_global(cur, 0, p0);
+
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int m0 = cur.m0, n0 = cur.n0;
         {
-            const float g = CH ? 1.0f : *gamma_p;
-            if (t < BM) row_scale[t] = (m0 + t < M) ? g / scale_x[m0 + t] : 0.0f;
+            const float gm = CH ? 1.0f : *gamma_p;
+            if (t < BM) row_scale[t] = (m0 + t < M) ? gm / scale_x[m0 + t] : 0.0f;
         }
         // per-channel scales of this lane's JN output columns, requested now
         // so their latency hides under the K loop (clamped index: the load is
         // unconditional; columns past N are not stored)
         float sc[CH ? JN : 1];
         if constexpr (CH) {
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < JN; ++j) sc[j] = gamma_p[min(n0 + (wave & 3) * 64 + (lane & 31) + j * 32, N - 1)];
         }
 
-        // Activations: thread tg stages chunks tg + 256 u (row c / 4, chunk c % 4)
-        // of the group's 128 rows; offsets relative to the step's base address.
-        const int mh = m0 + wm * HM;  // first row of the group's half
-        uint32_t aoff[kAPer];
-        int acol[kAPer];
-    #pragma unroll
-        for (int u = 0; u < kAPer; ++u) {
-            const int c = tg + u * kGroupThreads;
-            const int row = c >> 2;
-            acol[u] = (c & 3) * 16;
-            aoff[u] = mh + row < M ? (uint32_t)(row * K + acol[u]) : kBufOOB;
-        }
-        const int8_t* Xt = Xq + (int64_t)mh * K;
-        // Weights: in a quarter, thread tg stages slice bc = tg % 4 of row
-        // bq = tg / 4 (+ 64 per quarter), both 8-byte halves in slot order.
-        const int bq = tg >> 2, bc = tg & 3, bsw = half_swap(bq);
-        const uint32_t boff = (uint32_t)(bq * KB + 16 * bc);
-        const uint8_t* Wt = Wp + (int64_t)n0 * KB;
-
-        auto load_a = [&](int it, uint4 (&a)[kAPer]) {
-            const int k0 = it * BK;
-            const __amdgpu_buffer_rsrc_t ra = make_buf(Xt + k0);
-    #pragma unroll
-            for (int u = 0; u < kAPer; ++u) a[u] = buf_load16(ra, k0 + acol[u] < K ? aoff[u] : kBufOOB);
-        };
-        auto load_b = [&](int qi, uint4& b) {  // quarter qi: block qi / 4, rows 64 (qi % 4) + bq
-            const int blk = qi >> 2, part = qi & 3;
-            const int kb0 = blk * kStepsPerBlock * BK;  // first column of the block
-            const __amdgpu_buffer_rsrc_t rb = make_buf(Wt + (int64_t)part * kQuarterRows * KB + blk * ROW_BYTES);
-            const bool rv = n0 + part * kQuarterRows + bq < N;
-            const int kc = kb0 + bc * BK;  // first column of the slice
-            if constexpr (VECB) {
-                const bool v = rv && kc < K;
-                const uint2 lo = buf_load8(rb, v ? boff + 8 * bsw : kBufOOB);
-                const uint2 hi = buf_load8(rb, v ? boff + 8 * (bsw ^ 1) : kBufOOB);
-                b = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            } else {  // dword d of the slice covers columns kc + 16 d .. + 15
-                const int d0 = 2 * bsw, d1 = 2 * (bsw ^ 1);
-                b.x = buf_load4(rb, rv && kc + 16 * d0 < K ? boff + 4 * d0 : kBufOOB);
-                b.y = buf_load4(rb, rv && kc + 16 * d0 + 16 < K ? boff + 4 * d0 + 4 : kBufOOB);
-                b.z = buf_load4(rb, rv && kc + 16 * d1 < K ? boff + 4 * d1 : kBufOOB);
-                b.w = buf_load4(rb, rv && kc + 16 * d1 + 16 < K ? boff + 4 * d1 + 4 : kBufOOB);
-            }
-        };
-        // staged activation chunks are byte-transposed in registers (in a
-        // compute phase, where the VALU is otherwise idle) and stored as they are
-        auto transpose_a = [&](uint4 (&a)[kAPer]) {
-    #pragma unroll
-            for (int u = 0; u < kAPer; ++u) {
-                const uint32_t in[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
-                uint32_t o[4];
-                transpose4x4_bytes(in, o);
-                a[u] = make_uint4(o[0], o[1], o[2], o[3]);
-            }
-        };
-        auto store_a = [&](int buf, const uint4 (&a)[kAPer]) {
-            uint8_t* As = smem_a[wm][buf];
-    #pragma unroll
-            for (int u = 0; u < kAPer; ++u) {
-                const int c = tg + u * kGroupThreads;
-                *reinterpret_cast<uint4*>(As + row_slot(c >> 2, c & 3)) = a[u];
-            }
-        };
-        auto store_b = [&](int qi, const uint4& b) {
-            uint8_t* Bs = smem_b[wm][(qi >> 2) & 1];
-            *reinterpret_cast<uint4*>(Bs + row_slot((qi & 3) * kQuarterRows + bq, bc)) = b;
-        };
-        // tile t of the activations and quarter t + 3 of the weights
-        auto load_global = [&](int it, Stage& p) {
-            load_a(it, p.a);
-            load_b(it + 3, p.b);
-        };
-        auto store_lds = [&](int it, const Stage& p) {
-            store_a(it & 1, p.a);
-            store_b(it + 3, p.b);
-        };
-
         v16i acc[4][JN];
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; ++i)
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < JN; ++j)
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
-
-        const int g = lane >> 5;    // lane group: k chunks 2g, 2g+1 of the step
-        const int l32 = lane & 31;  // row (A) / column (B) inside a 32-block
-
-        // Operands of one step: MFMA half kh pairs activation chunk 2g+kh with
-        // the same chunk of the codes (one packed dword per half).
-        v4i a[2][4], b[2][JN];
-        uint2 bp[JN];
-        auto read_codes = [&](int it) {
-            const uint8_t* Bs = smem_b[wm][(it >> 2) & 1];
-            const int c = it & 3;
-    #pragma unroll
-            for (int j = 0; j < JN; ++j) {
-                const int r = wn * 64 + j * 32 + l32;
-                bp[j] = *reinterpret_cast<const uint2*>(Bs + row_slot(r, c) + 8 * (g ^ half_swap(r)));
-            }
-        };
-        auto read_acts = [&](int buf) {
-            const uint8_t* As = smem_a[wm][buf];
-    #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-    #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(As + row_slot(i * 32 + l32, 2 * g + kh));
-                    a[kh][i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-                }
-        };
-        auto unpack_codes = [&] {
-    #pragma unroll
-            for (int j = 0; j < JN; ++j) {
-                uint32_t u[4];
-                unpack16(bp[j].x, u);
-                b[0][j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
-                unpack16(bp[j].y, u);
-                b[1][j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
-            }
-        };
-        auto barrier = [] {
-            __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();
-            __builtin_amdgcn_sched_barrier(0);
-        };
 
         // One step.  Memory phase: operands of step it (packed codes first, then
         // activations); activation tile it + 1 and weight quarter it + 4 (loaded
@@ -280,41 +310,35 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
             read_codes(it);
             read_acts(it & 1);
             store_lds(it + 1, st);
-            load_global(it + 3, st);
+            load_global(cur, it + 3, st);
             __builtin_amdgcn_s_setprio(0);
             barrier();
             unpack_codes();
-    #pragma unroll
+#pragma unroll
             for (int kh = 0; kh < 2; ++kh)
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i)
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < JN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[kh][i], b[kh][j], acc[i][j], 0, 0, 0);
             transpose_a(nx.a);
             barrier();
         };
 
-        // Prologue: activation tile 0 and weight block 0 (quarters 0-3) in LDS;
-        // tiles 1, 2 and quarters 4, 5 loading.  Group 1 then waits one extra
-        // barrier, which puts it a phase behind group 0.
-        {
-            uint4 q0, q1, q2;
-            load_b(0, q0);
-            load_b(1, q1);
-            load_b(2, q2);
-            Stage p0;
-            load_global(0, p0);  // tile 0, quarter 3
-            transpose_a(p0.a);
-            store_a(0, p0.a);
-            store_b(0, q0);
-            store_b(1, q1);
-            store_b(2, q2);
-            store_b(3, p0.b);
-        }
+        // Prologue: activation tile 0 and weight block 0 (quarters 0-3) in LDS
+        // (their loads were issued before the previous tile's epilogue, or
+        // above for the first tile); tiles 1, 2 and quarters 4, 5 loading.
+        // Group 1 then waits one extra barrier, which puts it a phase behind
+        // group 0.
+        transpose_a(p0.a);
+        store_a(0, p0.a);
+        store_b(0, q0);
+        store_b(1, q1);
+        store_b(2, q2);
+        store_b(3, p0.b);
         Stage s0, s1;
-        load_global(1, s1);
-        load_global(2, s0);
+        load_global(cur, 1, s1);
+        load_global(cur, 2, s0);
         transpose_a(s1.a);
         barrier();
         if (wm == 1) barrier();
@@ -329,25 +353,41 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
         // Group 0 closes with the barrier group 1 took at the start: both
         // groups pass the same barriers in every tile.
         if (wm == 0) barrier();
+        // The next tile's prologue loads, ahead of this tile's stores (its
+        // LDS writes wait for the barrier at the end of this tile).  After
+        // the last tile they are issued too, all past the buffer: issued on
+        // every path, they leave nothing of this tile's prologue live across
+        // its K loop.
+        {
+            const int next = tile + (int)gridDim.x;
+            cur = geo_of(min(next, ntiles - 1), next < ntiles);
+        }
+        load_b(cur, 0, q0);
+        load_b(cur, 1, q1);
+        load_b(cur, 2, q2);
+        load_global(cur, 0, p0);
         // Epilogue.  32x32 block layout: lane holds column l32 and rows
         // 8*(r/4) + 4*g + r%4 for r = 0..15.  Stores address a uniform tile base
         // with 32-bit offsets (a tile spans < 2^31 bytes).
         float* Yt = Y + (int64_t)m0 * N + n0;
         const int mlim = M - m0, nlim = N - n0;
-        const int rbase = wm * 128 + 4 * g, cbase = wn * 64 + l32;
+        int rbase = wm * 128 + 4 * g, cbase = wn * 64 + l32;
+        // opaque per tile, so the 128 store offsets built from them are not
+        // hoisted out of the tile loop (they would stay live across it)
+        asm volatile("" : "+v"(rbase), "+v"(cbase));
         // Interior tiles store without per-element conditions: a branch per
         // store would let the compiler pull all 256 accumulators into VGPRs at
         // once.  Edge tiles take the guarded loop.
         auto store_tile = [&](auto guarded_tag, auto out, auto value) {
             constexpr bool GUARD = decltype(guarded_tag)::value;
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int rloc = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
                     const int roff = rloc * N;
                     const float rs = row_scale[rloc];
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < JN; ++j) {
                         const int cloc = cbase + j * 32;
                         // streaming (non-temporal) stores: the output is not read again here
