@@ -139,7 +139,7 @@ def test_linear_bwd_token_split(M, N, K):
 # copy's zero padding), ragged tile edges in N and K, a workspace that starts
 # as 0xff bytes, repeat calls (identical bits), and the range-gated variant
 # whose gate rides in the product's epilogue.
-XT_SHAPES = [(300, 8200, 2000), (1029, 8192, 2064), (40, 8448, 1936)]
+XT_SHAPES = [(300, 8200, 2000), (1029, 8192, 2064), (40, 8448, 1936), (1, 8192, 2048), (7, 8200, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", XT_SHAPES)
