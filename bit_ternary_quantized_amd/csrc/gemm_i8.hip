@@ -11,7 +11,8 @@
 //
 // Tiling: a 256 x 256 output tile per 512-thread workgroup; 8 waves as
 // 2 (M) x 4 (N), each owning 128 x 64 (4 x 2 MFMA blocks of 32 x 32, 128
-// int32 accumulators).  K advances 64 per step.  Activation chunks are
+// int32 accumulators).  For outputs with few such tiles, 128 x 256 tiles
+// (64 x 64 a wave) at two workgroups a CU.  K advances 64 per step.  Activation chunks are
 // staged in LDS byte-transposed 4 x 4; the weight tile stays 2-bit packed in
 // LDS (256 x 16 B, a quarter of the int8 bytes) and each wave unpacks its
 // operands in registers (unpack16 yields the same transposed column order,
@@ -41,21 +42,26 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BN = 256, BK = 64;
 constexpr int kThreads = 512;
 constexpr int kGroupThreads = 256;  // one wave group: 4 waves, one per SIMD
-constexpr int HM = BM / 2;          // tile rows per group
 constexpr int JN = 2;               // 32-column blocks per wave
 // Activation tile of one group and step: 128 rows x 64 B.  Weight codes come
 // in blocks of 4 steps: 256 rows x 64 B (4 slices of 16 B = 64 codes), so a
 // row's load is one 64-byte piece taken by 4 adjacent lanes; each step loads
 // a quarter (64 rows) of the block after next.
 constexpr int ROW_BYTES = 64;
-constexpr int A_BYTES = HM * ROW_BYTES;
 constexpr int B_BYTES = BN * ROW_BYTES;
 constexpr int kStepsPerBlock = 4;
 constexpr int kQuarterRows = BN / kStepsPerBlock;
-constexpr int kAPer = HM * (ROW_BYTES / 16) / kGroupThreads;  // 16-byte activation chunks per thread
+// IM: 32-row blocks per wave.  Tile rows: 32 IM per group, 64 IM in all.
+template <int IM>
+struct MTile {
+    static constexpr int HM = 32 * IM;  // tile rows per group
+    static constexpr int BM = 2 * HM;
+    static constexpr int A_BYTES = HM * ROW_BYTES;
+    static constexpr int kAPer = HM * (ROW_BYTES / 16) / kGroupThreads;  // 16-byte activation chunks per thread
+};
 // LDS rows are unpadded and XOR-swizzled so that the 16-byte writes of the
 // staging threads and the operand reads of the waves both hit distinct banks
 // in every 16-lane group: 16-byte chunk c of row r sits at slot
@@ -80,9 +86,10 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& t
     tn = __builtin_amdgcn_readfirstlane(id % tiles_n);
 }
 
+template <int KA>
 struct Stage {
-    uint4 a[kAPer];  // 16-byte activation chunks of the group's half (tile t)
-    uint4 b;         // one 16-byte weight slice (quarter t + 3), halves in slot order
+    uint4 a[KA];  // 16-byte activation chunks of the group's half (tile t)
+    uint4 b;      // one 16-byte weight slice (quarter t + 3), halves in slot order
 };
 
 }  // namespace
@@ -91,14 +98,23 @@ struct Stage {
 // or all out of range (else dword granularity).  CH: one scale per output
 // channel, gamma_p[n] (y = acc * (1/scale_x[m]) * gamma_p[n]); else the one
 // gamma of the matrix (y = acc * (gamma/scale_x[m])).
-template <bool VECB, bool CH = false>
-__global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
+template <bool VECB, bool CH = false, int IM = 4>
+__global__ __launch_bounds__(kThreads, IM == 4 ? 1 : 4) void gemm_i8t2_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ scale_x,
     const uint8_t* __restrict__ Wp, const float* __restrict__ gamma_p, int M, int N, int K,
     float* __restrict__ Y, int32_t* __restrict__ acc_out) {
-    __shared__ __align__(16) uint8_t smem_a[2][2][A_BYTES];  // [group][buffer]
-    __shared__ __align__(16) uint8_t smem_b[2][2][B_BYTES];  // [group][block buffer]
-    __shared__ float row_scale[BM];
+    constexpr int HM = MTile<IM>::HM, BM = MTile<IM>::BM, A_BYTES = MTile<IM>::A_BYTES;
+    constexpr int kAPer = MTile<IM>::kAPer;
+    using Stage = bitnet::Stage<kAPer>;
+    // LDS: activation tiles [group][buffer], weight tiles [group][block
+    // buffer], then (256-row tiles) the row scale table.  128-row tiles keep
+    // the table in the first activation buffer instead, written after the K
+    // loop, so that two workgroups fit in a CU's 160 KB.
+    constexpr int kLdsBytes = 4 * A_BYTES + 4 * B_BYTES + (IM == 4 ? 4 * BM : 0);
+    __shared__ __align__(16) uint8_t lds[kLdsBytes];
+    auto smem_a = reinterpret_cast<uint8_t(*)[2][A_BYTES]>(lds);
+    auto smem_b = reinterpret_cast<uint8_t(*)[2][B_BYTES]>(lds + 4 * A_BYTES);
+    float* const row_scale = reinterpret_cast<float*>(IM == 4 ? lds + 4 * A_BYTES + 4 * B_BYTES : lds);
 
     // Persistent: workgroup b takes tiles b, b + grid, ...  (the grid is at
     // most one workgroup per CU), so the y stores of one tile drain while
@@ -219,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
 
     // Operands of one step: MFMA half kh pairs activation chunk 2g+kh with
     // the same chunk of the codes (one packed dword per half).
-    v4i a[2][4], b[2][JN];
+    v4i a[2][IM], b[2][JN];
     uint2 bp[JN];
     auto read_codes = [&](int it) {
         const uint8_t* Bs = smem_b[wm][(it >> 2) & 1];
@@ -235,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < IM; ++i) {
                 const uint4 v = *reinterpret_cast<const uint4*>(As + row_slot(i * 32 + l32, 2 * g + kh));
                 a[kh][i] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
             }
@@ -268,9 +284,11 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
 
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const int m0 = cur.m0, n0 = cur.n0;
+        float rs_t;  // this thread's entry of the row scale table (t < BM)
         {
             const float gm = CH ? 1.0f : *gamma_p;
-            if (t < BM) row_scale[t] = (m0 + t < M) ? gm / scale_x[m0 + t] : 0.0f;
+            rs_t = (t < BM && m0 + t < M) ? gm / scale_x[m0 + t] : 0.0f;
+            if (IM == 4 && t < BM) row_scale[t] = rs_t;
         }
         // per-channel scales of this lane's JN output columns, requested now
         // so their latency hides under the K loop (clamped index: the load is
@@ -281,9 +299,9 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
             for (int j = 0; j < JN; ++j) sc[j] = gamma_p[min(n0 + (wave & 3) * 64 + (lane & 31) + j * 32, N - 1)];
         }
 
-        v16i acc[4][JN];
+        v16i acc[IM][JN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < IM; ++i)
 #pragma unroll
             for (int j = 0; j < JN; ++j)
 #pragma unroll
@@ -317,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < IM; ++i)
 #pragma unroll
                     for (int j = 0; j < JN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[kh][i], b[kh][j], acc[i][j], 0, 0, 0);
@@ -353,6 +371,10 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
         // Group 0 closes with the barrier group 1 took at the start: both
         // groups pass the same barriers in every tile.
         if (wm == 0) barrier();
+        if constexpr (IM != 4) {  // the table into the now unread first activation buffer
+            if (t < BM) row_scale[t] = rs_t;
+            barrier();
+        }
         // The next tile's prologue loads, ahead of this tile's stores (its
         // LDS writes wait for the barrier at the end of this tile).  After
         // the last tile they are issued too, all past the buffer: issued on
@@ -371,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
         // with 32-bit offsets (a tile spans < 2^31 bytes).
         float* Yt = Y + (int64_t)m0 * N + n0;
         const int mlim = M - m0, nlim = N - n0;
-        int rbase = wm * 128 + 4 * g, cbase = wn * 64 + l32;
+        int rbase = wm * HM + 4 * g, cbase = wn * 64 + l32;
         // opaque per tile, so the 128 store offsets built from them are not
         // hoisted out of the tile loop (they would stay live across it)
         asm volatile("" : "+v"(rbase), "+v"(cbase));
@@ -381,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
         auto store_tile = [&](auto guarded_tag, auto out, auto value) {
             constexpr bool GUARD = decltype(guarded_tag)::value;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < IM; ++i) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int rloc = rbase + i * 32 + 8 * (r >> 2) + (r & 3);
@@ -419,23 +441,39 @@ __global__ __launch_bounds__(kThreads) void gemm_i8t2_kernel(
 hipError_t launch_gemm_i8t2(const int8_t* Xq, const float* scale_x, const uint8_t* Wp,
                             const float* gamma, int64_t M, int64_t N, int64_t K, float* Y,
                             int32_t* acc, hipStream_t s, bool channel) {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    if (tiles > INT32_MAX) return hipErrorInvalidValue;
-    // one workgroup per CU at most (its LDS allows one), each walking tiles
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)std::min<int64_t>(tiles, std::max(cus, 1));
-#define BITNET_GEMM_LAUNCH(V_, C_)                                                                  \
-    gemm_i8t2_kernel<V_, C_><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, (int)K, Y, \
-                                                       acc)
-    if (K % BK == 0) {
-        if (channel) BITNET_GEMM_LAUNCH(true, true);
-        else BITNET_GEMM_LAUNCH(true, false);
+    cus = std::max(cus, 1);
+    const int64_t tiles_n = (N + BN - 1) / BN;
+    const int64_t tiles4 = ((M + MTile<4>::BM - 1) / MTile<4>::BM) * tiles_n;
+    if (tiles4 > INT32_MAX) return hipErrorInvalidValue;
+    // At most half as many 256-row tiles as CUs (and K % 64 == 0): 128-row
+    // tiles, two workgroups a CU (their LDS and registers allow two), so
+    // more CUs work and each one's two workgroups overlap their prologues and
+    // y stores with the other's K loop.  Otherwise 256-row tiles, one
+    // workgroup a CU at most, each walking tiles.  Measured (graphs of 10
+    // launches, bit-identical): 512 x 4096 x 4096 43.4 -> 31.6 us, 4096 x
+    // 1024 x 4096 44.0 -> 33.1 us, 2048 x 4096 x 4096 46.4 -> 39-41 us,
+    // 4096 x 1376 x 512 15.8 -> 12-14 us; with 192 tiles (8192 x 1376 x
+    // 512) slower, 16.3 -> 17.0-18.0 us; with K % 64 != 0 the 128-register
+    // budget spills inside the K loop.
+    const bool half = K % BK == 0 && 2 * tiles4 <= cus;
+    const int64_t tiles = half ? ((M + MTile<2>::BM - 1) / MTile<2>::BM) * tiles_n : tiles4;
+    const unsigned grid = (unsigned)std::min<int64_t>(tiles, half ? 2 * (int64_t)cus : cus);
+#define BITNET_GEMM_LAUNCH(V_, C_, IM_)                                                                  \
+    gemm_i8t2_kernel<V_, C_, IM_><<<grid, kThreads, 0, s>>>(Xq, scale_x, Wp, gamma, (int)M, (int)N, (int)K, Y, \
+                                                            acc)
+    if (half) {
+        if (channel) BITNET_GEMM_LAUNCH(true, true, 2);
+        else BITNET_GEMM_LAUNCH(true, false, 2);
+    } else if (K % BK == 0) {
+        if (channel) BITNET_GEMM_LAUNCH(true, true, 4);
+        else BITNET_GEMM_LAUNCH(true, false, 4);
     } else {
-        if (channel) BITNET_GEMM_LAUNCH(false, true);
-        else BITNET_GEMM_LAUNCH(false, false);
+        if (channel) BITNET_GEMM_LAUNCH(false, true, 4);
+        else BITNET_GEMM_LAUNCH(false, false, 4);
     }
 #undef BITNET_GEMM_LAUNCH
     return hipGetLastError();
