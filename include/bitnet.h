@@ -170,7 +170,8 @@ int bitnet_quant_operands(const void *X, int x_dtype, int64_t M, int64_t K, floa
  *   Y[m][n]   = acc[m][n] * gamma / scale_x[m]   (fp32)
  * M <= 16 (with K <= 16384) takes the bandwidth-bound packed GEMV (one
  * token with K % 64 == 0 and K <= 8192: a VALU row GEMV, lanes across K),
- * other shapes the int8 MFMA GEMM.  Every path gives the same bits.
+ * 17 <= M <= 64 the same GEMV once per block of 16 tokens, other shapes
+ * the int8 MFMA GEMM.  Every path gives the same bits.
  *   Xq       [M][K] int8;  scale_x [M] fp32;  W_packed [N][K/4];  gamma 1 fp32
  *   Y        [M][N] fp32, written
  *   acc      [M][N] int32, written when non-NULL (for exact checks)

@@ -33,6 +33,9 @@ FWD_SHAPES = [
     # one token with K % 64 == 0 (the row GEMV): one chunk per lane, two, a
     # ragged second chunk, a single chunk for the whole row
     (1, 4099, 64), (1, 33, 8192), (1, 17, 4160), (1, 1000, 4096),
+    # 17 to 64 tokens: blocks of 16 through the GEMV (the last block 1 to 16
+    # tokens, one token taking the row GEMV)
+    (17, 300, 256), (33, 1000, 4096), (64, 257, 1040), (48, 4099, 64), (49, 33, 8192),
     # GEMM path: several tiles plus ragged edges in M, N and K
     (17, 16, 16), (100, 300, 256), (256, 256, 64), (300, 513, 1040),
     (513, 257, 4096), (1000, 40, 48),
