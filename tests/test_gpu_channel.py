@@ -39,7 +39,9 @@ def _operands(M, N, K, seed):
 
 
 # GEMV (M <= 16), GEMM with ragged edges, many tiles per workgroup
-FWD_SHAPES = [(1, 300, 256), (1, 70, 8192), (16, 1000, 512), (300, 513, 1040), (4200, 4100, 64)]
+# (the last two: 17-64 tokens as GEMV blocks; 200 tokens on 128-row GEMM tiles)
+FWD_SHAPES = [(1, 300, 256), (1, 70, 8192), (16, 1000, 512), (300, 513, 1040), (4200, 4100, 64), (40, 300, 1024),
+              (200, 1000, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", FWD_SHAPES)

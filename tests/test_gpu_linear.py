@@ -36,6 +36,8 @@ FWD_SHAPES = [
     # 17 to 64 tokens: blocks of 16 through the GEMV (the last block 1 to 16
     # tokens, one token taking the row GEMV)
     (17, 300, 256), (33, 1000, 4096), (64, 257, 1040), (48, 4099, 64), (49, 33, 8192),
+    # 65 tokens and more with few tiles (128-row tiles, two workgroups a CU)
+    (65, 4100, 1024), (200, 1000, 4096), (129, 257, 2048), (300, 11008, 4096),
     # GEMM path: several tiles plus ragged edges in M, N and K
     (17, 16, 16), (100, 300, 256), (256, 256, 64), (300, 513, 1040),
     (513, 257, 4096), (1000, 40, 48),
