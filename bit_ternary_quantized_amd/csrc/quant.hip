@@ -701,14 +701,16 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const T* __restrict__ W, i
 // after issuing its weight loads (workgroup 0: all four waves evaluate).
 template <bool POLLER>
 constexpr int pub_threads() { return POLLER ? 5 * kWave : 4 * kWave; }
-// The four-wave form, as a body of the workgroup index.
+// The four-wave form, as a body of the workgroup index `bid` (its role:
+// workgroup 0 evaluates the threshold; its count slot) and of the block of
+// groups `dbid` it packs.
 template <typename T, int U, bool COUNT>
 __device__ __forceinline__ void wq_pack_pub4_body(const T* __restrict__ W, int64_t total4,
                                                   uint64_t* __restrict__ gate, const float* __restrict__ nodes,
                                                   int64_t N, int64_t K, float* __restrict__ gamma,
                                                   uint8_t* __restrict__ out, int polls,
-                                                  uint32_t* __restrict__ count_partial, int bid) {
-    const int64_t g0 = (int64_t)bid * (256 * U);
+                                                  uint32_t* __restrict__ count_partial, int bid, int dbid) {
+    const int64_t g0 = (int64_t)dbid * (256 * U);
     __shared__ float pub_thr;
     __shared__ int pub_ok;
     __shared__ float part[4];
@@ -762,7 +764,11 @@ __global__ __launch_bounds__(pub_threads<POLLER>()) void wq_pack_pub_kernel(
     int64_t N, int64_t K, float* __restrict__ gamma, uint8_t* __restrict__ out, int polls,
     uint32_t* __restrict__ count_partial = nullptr) {
     if constexpr (!POLLER) {
-        wq_pack_pub4_body<T, U, COUNT>(W, total4, gate, nodes, N, K, gamma, out, polls, count_partial, blockIdx.x);
+        // the groups in reverse order: the first workgroups read the end of W,
+        // which the row-sum pass read last (the part of a matrix larger than
+        // the Infinity Cache that it may still hold)
+        wq_pack_pub4_body<T, U, COUNT>(W, total4, gate, nodes, N, K, gamma, out, polls, count_partial, blockIdx.x,
+                                       (int)gridDim.x - 1 - (int)blockIdx.x);
     } else {
         const int64_t g0 = (int64_t)blockIdx.x * (256 * U);
         __shared__ float pub_thr;
@@ -1272,7 +1278,7 @@ __global__ __launch_bounds__(kAqWaves * kWave) void act_pack_kernel(
         act_quant_rows_body<TX, NB>(X, M, K, eps, Q, S, b, act_blocks);
     } else {
         wq_pack_pub4_body<TW, pack_u_pub<TW, false>(), false>(W, total4, gate, nodes, N, K, gamma, out, polls,
-                                                              nullptr, b - act_blocks);
+                                                              nullptr, b - act_blocks, b - act_blocks);
     }
 }
 
