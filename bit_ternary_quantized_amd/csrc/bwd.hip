@@ -259,6 +259,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     constexpr int BK = T::BK, GROWS = T::GROWS, IM = T::IM, JN = T::JN, KQ = T::KQ;
     constexpr int NA = T::NA, NB = T::NB;
     constexpr bool KS = T::KSPLIT;
+    // persistent tile loop (without it the registers the ragged element-wise
+    // loads need push the big tile over the register file)
+    constexpr bool PERS = !KS && VEC;
     constexpr bool GW = MODE != kGradX;   // a grad_W product
     constexpr bool BT = MODE == kGradWT;  // its B operand from X_deq^T rows
     constexpr int PB = T::pitch(T::BN);  // B tile ("cols")
@@ -288,8 +291,15 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     const int R = GW ? N : M;  // output rows
     const int C = K;           // output columns
     const int KC = GW ? M : N; // contraction length
+    // Persistent without a contraction split between the wave groups and
+    // with 16-byte rows of the contraction operand: the grid is at most one
+    // workgroup per CU and workgroup b takes tiles b, b + grid, ... (tile v
+    // on the XCD a one-tile-per-workgroup launch gives it when the grid is a
+    // multiple of 8).  Otherwise one tile a workgroup.
+    const int nwg = ((R + T::BM - 1) / T::BM) * ((C + T::BN - 1) / T::BN) * splits;
+    for (int wgi = blockIdx.x; wgi < nwg; wgi += gridDim.x) {
     int tm, tn, sp;
-    tile_of(blockIdx.x, (R + T::BM - 1) / T::BM, (C + T::BN - 1) / T::BN, splits, tm, tn, sp);
+    tile_of(wgi, (R + T::BM - 1) / T::BM, (C + T::BN - 1) / T::BN, splits, tm, tn, sp);
     const int r0 = tm * T::BM, c0 = tn * T::BN;
     const int klo = sp * kper, khi = min(KC, klo + kper);
     const int nsteps = (khi - klo + BK - 1) / BK;
@@ -600,6 +610,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     // 8*(r/4) + 4*g + r%4
     const float scale = MODE == kGradX && !CH ? *aux : 1.0f;
     float* outf = static_cast<float*>(out);
+    // this lane's row and column offsets inside the tile, opaque per tile so
+    // that the stores' offsets built from them are not hoisted out of the
+    // tile loop (they would stay live across it)
+    int lrow = wr + 4 * g, lcol = wc + l32;
+    if constexpr (PERS) asm volatile("" : "+v"(lrow), "+v"(lcol));
     if constexpr (GW) outf += (int64_t)sp * N * K;
 #pragma unroll
     for (int ii = 0; ii < IM; ++ii) {
@@ -609,10 +624,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
         if constexpr (GATED) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = min(rg + wr + ii * 32 + 8 * (r >> 2) + 4 * g + (r & 3), R - 1);
+                const int row = min(rg + lrow + ii * 32 + 8 * (r >> 2) + (r & 3), R - 1);
 #pragma unroll
                 for (int j = 0; j < JN; ++j) {
-                    const int64_t idx = (int64_t)row * C + min(c0 + wc + j * 32 + l32, C - 1);
+                    const int64_t idx = (int64_t)row * C + min(c0 + lcol + j * 32, C - 1);
                     wv[r][j] = gate.bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(gate.w)[idx])
                                          : static_cast<const float*>(gate.w)[idx];
                 }
@@ -620,11 +635,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = rg + wr + ii * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const int row = rg + lrow + ii * 32 + 8 * (r >> 2) + (r & 3);
             if (row < R) {
 #pragma unroll
                 for (int j = 0; j < JN; ++j) {
-                    const int col = c0 + wc + j * 32 + l32;
+                    const int col = c0 + lcol + j * 32;
                     if (col < C) {
                         const int64_t idx = (int64_t)row * C + col;
                         float v = acc[ii][j][r] * scale;
@@ -639,6 +654,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (!PERS) break;  // one tile a workgroup: no back edge
+    __syncthreads();  // the next tile rewrites the LDS tiles
     }
 }
 
@@ -800,7 +818,14 @@ template <int MODE, class T, bool OUT_BF16>
 hipError_t launch_one(const uint16_t* gy, const void* second, const float* aux, int M, int N, int K,
                       const Plan& p, void* out, hipStream_t s, const SteGate& gate = SteGate{},
                       bool channel = false) {
-    const unsigned grid = (unsigned)(p.tiles * p.splits);
+    unsigned grid = (unsigned)(p.tiles * p.splits);
+    if (!T::KSPLIT && N % 8 == 0) {  // persistent: at most one workgroup a CU
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        grid = (unsigned)std::min<int64_t>(grid, std::max(cus, 1));
+    }
     // the gate rides in the tile epilogue only without a token split (with
     // one, split_reduce_kernel applies it)
     const bool gated = MODE != kGradX && gate.w != nullptr && p.splits == 1;
