@@ -105,6 +105,30 @@ def test_linear_bwd_ste(M, N, K, gx_dtype):
     assert_grad_close(gw.cpu().numpy(), gw_ref, "grad_W")
 
 
+# More output tiles than the chip has CUs, so the persistent workgroups take
+# a second tile (ragged tile edges on every side): grad_x on the 128 x 128
+# tiles (289 of them), grad_x on the 256 x 256 tiles (289), the same with a
+# contraction length N % 8 != 0 (one tile a workgroup, element-wise loads),
+# and grad_W on the 256 x 256 tiles of a short output (N < 8192: X_deq
+# converted in the loop).
+LOOP_SHAPES = [(2100, 264, 2096), (4100, 264, 4208), (4100, 261, 4208), (300, 4200, 4208)]
+
+
+@pytest.mark.parametrize("M,N,K", LOOP_SHAPES)
+def test_linear_bwd_more_tiles_than_cus(M, N, K):
+    print(f"linear_bwd loop M={M} N={N} K={K}", flush=True)
+    q, codes, scale_x, gamma = _quantized_operands(M, N, K, seed=7 * M + N + K)
+    gy = workloads.normal((M, N), 1e-3, seed=M + 2 * N, dtype="bf16")
+    wp = oracle.pack(codes.numpy())
+    gx, gw = bt.bitnet_linear_bwd_ste(to_dev(gy), to_dev(q), to_dev(scale_x), to_dev(torch.from_numpy(wp)),
+                                      to_dev(gamma))
+    torch.cuda.synchronize()
+    gx_ref = oracle.ste_grad_x(host(gy), codes.numpy(), float(gamma[0]))
+    gw_ref = oracle.ste_grad_w(host(gy), q.numpy(), scale_x.numpy())
+    assert_grad_close(gx.cpu().numpy(), gx_ref, "grad_x")
+    assert_grad_close(gw.cpu().numpy(), gw_ref, "grad_W")
+
+
 # grad_W of these splits its token range over workgroups (fewer than 256
 # output tiles, at least 1024 tokens): 4 even splits, 2 with a ragged last
 # split and ragged tile edges, 5 with a short last split.  The workspace
